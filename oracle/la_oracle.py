@@ -1,0 +1,268 @@
+"""Plain fp64 CPU oracle for kernelized linear attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links
+this module: only the test suite, the smoke check and the CPU-baseline leg of
+the benchmark use it. It shares no code with the HIP library; the two meet only
+through the seeded inputs produced by ``workloads``.
+
+Everything is computed in float64 from the exact values the GPU sees (bf16 or
+fp32 inputs upcast without change). Each function follows one passage of the
+pages it cites; nothing is blocked, fused or reordered beyond what that passage
+states. Array layout everywhere: ``[B, H, n, d]``; the state ``S`` is
+``[B, H, r, d_v]`` and the normaliser ``z`` is ``[B, H, r]``.
+
+Pages cited (title, site):
+  * "Linear Attention Mechanisms" (sadullah.online)          -- [LAM-s]
+  * "Linear Attention Mechanisms" (dileepadev.github.io)     -- [LAM-d]
+  * "Attention-Free / Sub-Quadratic Architectures"
+    (blog.vguerra.net)                                       -- [AFA]
+
+Readings taken where the pages are silent or garbled are listed with each
+function; every one of them is pinned by a test in ``tests/test_oracle_pins.py``
+except where a docstring says "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+FMAPS = ("elu1", "favor")
+GATES = ("none", "decay", "gla")
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Feature maps
+# ---------------------------------------------------------------------------
+
+def phi_elu1(x):
+    """phi(x) = elu(x) + 1, elementwise, with the ELU slope parameter 1.
+
+    [LAM-d] "Choosing the Feature Map phi", ELU-based features (Linear
+    Transformer); [AFA] "Feature maps phi (must keep similarities >= 0)".
+    elu(x) is x for x > 0 and exp(x) - 1 otherwise, so elu(x) + 1 is x + 1 for
+    x > 0 and exp(x) for x <= 0 (the exp branch is written directly, which is
+    the same number without the cancellation of (exp(x) - 1) + 1).
+    """
+    x = _f64(x)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def phi_favor(x, omega):
+    """FAVOR+ positive random features phi(x)_m = exp(w_m.x - |x|^2/2) / sqrt(r).
+
+    [LAM-d] "Choosing the Feature Map phi": positive (and orthogonal) random
+    features whose inner product is an unbiased estimate of exp(q.k); [AFA]
+    "Feature maps phi": phi(q).phi(k) approximates exp(q.k).
+    Reading: the page prints exp(w.x)/sqrt(r) without the -|x|^2/2 term; only
+    the form with that term has expectation exp(q.k) for w ~ N(0, I), which is
+    the property both pages state, so that form is used. ``omega`` is [r, d]
+    (the random frequencies are an input, drawn outside this module).
+    """
+    x = _f64(x)
+    om = _f64(omega)
+    r = om.shape[0]
+    proj = np.einsum("...d,md->...m", x, om)
+    half_sq = 0.5 * np.sum(x * x, axis=-1, keepdims=True)
+    return np.exp(proj - half_sq) / np.sqrt(r)
+
+
+def feature_map(x, fmap="elu1", omega=None):
+    """Apply the named feature map phi over the last axis."""
+    if fmap == "elu1":
+        return phi_elu1(x)
+    if fmap == "favor":
+        if omega is None:
+            raise ValueError("favor feature map needs omega")
+        return phi_favor(x, omega)
+    raise ValueError(f"unknown feature map {fmap!r}")
+
+
+# ---------------------------------------------------------------------------
+# Gates
+# ---------------------------------------------------------------------------
+
+def gla_alpha(g, tau):
+    """Per-step diagonal GLA gate alpha_t = sigmoid(g_t) ** (1 / tau).
+
+    [LAM-d] "Gating and Selective State Updates", Gated Linear Attention: a
+    data-dependent gate in (0, 1) multiplies the previous state. Reading: the
+    gate is diagonal on the key (feature) axis, G_t = alpha_t 1^T, i.e. row k
+    of S is scaled by alpha_{t,k}; alpha comes from a raw input g through a
+    sigmoid raised to 1/tau.
+    """
+    g = _f64(g)
+    with np.errstate(over="ignore"):  # exp(-g) -> inf gives sigmoid 0 exactly
+        sig = 1.0 / (1.0 + np.exp(-g))
+    return sig ** (1.0 / float(tau))
+
+
+def _gate_factor(gate, t, B, H):
+    """Multiplier applied to the previous state before step t.
+
+    Returns an array broadcastable to S [B, H, r, 1] rows (shape [B, H, r] or
+    [1, H, 1]), or None when there is no gate.
+    """
+    if gate is None or gate[0] == "none":
+        return None
+    kind = gate[0]
+    if kind == "decay":
+        gamma = _f64(gate[1]).reshape(1, H, 1)
+        return gamma
+    if kind == "gla":
+        g, tau = gate[1], gate[2]
+        return gla_alpha(np.asarray(g)[:, :, t, :], tau)
+    raise ValueError(f"unknown gate {kind!r}")
+
+
+# ---------------------------------------------------------------------------
+# Non-causal form (reassociated)
+# ---------------------------------------------------------------------------
+
+def noncausal(Q, K, V, fmap="elu1", omega=None, eps=1e-6):
+    """o_i = phi(q_i)^T S / (phi(q_i)^T z + eps), S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j).
+
+    [LAM-s] "The linear attention trick: drop or approximate the softmax" (the
+    reassociated routine with eps = 1e-6 added to the normaliser); [LAM-d]
+    "The Kernel Trick for Attention" (the S, z formula); [AFA] "Linear
+    Attention (the core trick)".
+    """
+    V = _f64(V)
+    pq = feature_map(Q, fmap, omega)
+    pk = feature_map(K, fmap, omega)
+    S = np.einsum("bhjr,bhje->bhre", pk, V)
+    z = pk.sum(axis=2)
+    num = np.einsum("bhir,bhre->bhie", pq, S)
+    den = np.einsum("bhir,bhr->bhi", pq, z) + eps
+    return num / den[..., None]
+
+
+# ---------------------------------------------------------------------------
+# Explicit n x n kernel-matrix form (quadratic; tiny inputs only)
+# ---------------------------------------------------------------------------
+
+def kernel_weights(Q, K, fmap="elu1", omega=None, causal=False, gate=None):
+    """Explicit weights W_ij = sum_k phi(q_i)_k phi(k_j)_k D_ijk, shape [B, H, n, n].
+
+    [LAM-d] "The Kernel Trick for Attention": the similarity of query i and key
+    j is phi(q_i)^T phi(k_j). Causal: only j <= i contributes ([LAM-d]
+    "Recurrent Reformulation"; [AFA] "The recurrent form (causal)"). RetNet:
+    key j is discounted by gamma^(i-j) ([LAM-d] "Gating and Selective State
+    Updates"). GLA: key j is multiplied, per feature k, by the product of the
+    gates of the steps after j up to i, which is what unrolling
+    S_t = G_t * S_{t-1} + phi(k_t) v_t^T gives.
+    """
+    pq = feature_map(Q, fmap, omega)
+    pk = feature_map(K, fmap, omega)
+    B, H, n, r = pq.shape
+    kind = "none" if gate is None else gate[0]
+    if kind != "none" and not causal:
+        raise ValueError("gates are defined for the causal form only")
+    W = np.zeros((B, H, n, n))
+    if kind == "gla":
+        alpha = gla_alpha(gate[1], gate[2])  # [B, H, n, r]
+    for i in range(n):
+        for j in range(n):
+            if causal and j > i:
+                continue
+            if kind == "none":
+                D = 1.0
+            elif kind == "decay":
+                D = (_f64(gate[1]) ** (i - j)).reshape(1, H, 1)
+            else:
+                D = np.prod(alpha[:, :, j + 1:i + 1, :], axis=2)  # empty product = 1
+            W[:, :, i, j] = np.sum(pq[:, :, i, :] * pk[:, :, j, :] * D, axis=-1)
+    return W
+
+
+def attention_from_weights(W, V, eps=1e-6):
+    """o_i = sum_j W_ij v_j / (sum_j W_ij + eps).
+
+    [LAM-d] "The Kernel Trick for Attention" (the ratio form of o_i) with the
+    eps of [LAM-s] "The linear attention trick".
+    """
+    V = _f64(V)
+    num = np.einsum("bhij,bhje->bhie", W, V)
+    den = W.sum(axis=-1) + eps
+    return num / den[..., None]
+
+
+def brute(Q, K, V, fmap="elu1", omega=None, causal=False, gate=None, eps=1e-6):
+    """Quadratic reference: explicit weight matrix, then the normalised mix."""
+    W = kernel_weights(Q, K, fmap, omega, causal, gate)
+    return attention_from_weights(W, V, eps)
+
+
+# ---------------------------------------------------------------------------
+# Causal recurrent form (the matrix-state RNN)
+# ---------------------------------------------------------------------------
+
+def causal_recurrent(Q, K, V, fmap="elu1", omega=None, gate=None, eps=1e-6,
+                     S0=None, z0=None):
+    """Token-by-token recurrence; returns (o, S_final, z_final).
+
+    [LAM-d] "Recurrent Reformulation": S_t = S_{t-1} + phi(k_t) v_t^T,
+    z_t = z_{t-1} + phi(k_t), o_t = phi(q_t)^T S_t / (phi(q_t)^T z_t); [AFA]
+    "The recurrent form (causal)". Gated variants ([LAM-d] "Gating and
+    Selective State Updates"; [AFA] "Evolution: add decay/gating"):
+    S_t = G_t * S_{t-1} + phi(k_t) v_t^T with G_t = gamma_h (RetNet) or
+    alpha_t scaling row k by alpha_{t,k} (GLA).
+    Readings: the gate multiplies the previous state only (the current token
+    enters with weight 1); z is gated exactly like S (z is S's column for a
+    value of constant 1), which keeps the weights of each output summing to
+    one; eps is added to the denominator as in [LAM-s]'s routine; the page
+    calls z's update "scalar" but z has r entries (it is summed elementwise).
+    ``gate`` is None, ("decay", gamma[H]) or ("gla", g[B,H,n,r], tau).
+    """
+    V = _f64(V)
+    pq = feature_map(Q, fmap, omega)
+    pk = feature_map(K, fmap, omega)
+    B, H, n, r = pq.shape
+    dv = V.shape[-1]
+    S = np.zeros((B, H, r, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros((B, H, r)) if z0 is None else _f64(z0).copy()
+    out = np.empty((B, H, n, dv))
+    for t in range(n):
+        G = _gate_factor(gate, t, B, H)
+        if G is not None:
+            S = S * G[..., None]
+            z = z * G
+        S = S + pk[:, :, t, :, None] * V[:, :, t, None, :]
+        z = z + pk[:, :, t, :]
+        num = np.einsum("bhr,bhre->bhe", pq[:, :, t, :], S)
+        den = np.einsum("bhr,bhr->bh", pq[:, :, t, :], z) + eps
+        out[:, :, t, :] = num / den[..., None]
+    return out, S, z
+
+
+def decode_step(S, z, q, k, v, fmap="elu1", omega=None, gate=None, eps=1e-6):
+    """One step of the recurrence from a given state: returns (o, S', z').
+
+    [LAM-d] "Recurrent Reformulation" (rank-1 update of S, update of z, then
+    the read-out); [AFA] "The recurrent form (causal)" (constant cost per
+    token). q, k, v (and g for GLA) are [B, H, d] for the single new token;
+    ``gate`` is None, ("decay", gamma[H]) or ("gla", g[B,H,r], tau).
+    """
+    q4 = _f64(q)[:, :, None, :]
+    k4 = _f64(k)[:, :, None, :]
+    v4 = _f64(v)[:, :, None, :]
+    g4 = gate
+    if gate is not None and gate[0] == "gla":
+        g4 = ("gla", _f64(gate[1])[:, :, None, :], gate[2])
+    o, S1, z1 = causal_recurrent(q4, k4, v4, fmap, omega, g4, eps, S0=S, z0=z)
+    return o[:, :, 0, :], S1, z1
+
+
+# ---------------------------------------------------------------------------
+# Softmax attention (what the method replaces) -- used by the FAVOR+ pins
+# ---------------------------------------------------------------------------
+
+def softmax_score_matrix_bytes(n, bytes_per_entry):
+    """Bytes to hold one n x n score matrix.
+
+    [LAM-d] "Standard Self-Attention: The Quadratic Baseline" quotes the size of
+    this matrix at n = 16384 in float16.
+    """
+    return int(n) * int(n) * int(bytes_per_entry)

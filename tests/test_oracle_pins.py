@@ -1,0 +1,356 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test names the passage of the pages (or the mathematical fact) it checks,
+and is chosen so that a plausible slip in the oracle (a dropped term, a wrong
+sign or index, an off-by-one mask, a transposed operand, a gate applied at the
+wrong time, an ungated normaliser) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+import scipy.special
+import torch
+
+import oracle as orc
+
+RNG = np.random.default_rng(1234)
+
+
+def _rand(*shape, scale=1.0, rng=RNG):
+    return rng.standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- feature maps
+
+def test_elu1_closed_form_points():
+    # elu(x)+1 at hand-computed points: x+1 above zero, exp(x) at and below
+    x = np.array([2.5, 1.0, 1e-3, 0.0, -1.0, -30.0])
+    want = np.array([3.5, 2.0, 1.001, 1.0, math.exp(-1.0), math.exp(-30.0)])
+    np.testing.assert_allclose(orc.phi_elu1(x), want, rtol=1e-15, atol=0)
+
+
+def test_elu1_matches_library_elu():
+    x = _rand(1000, scale=3.0)
+    lib = torch.nn.functional.elu(torch.from_numpy(x), alpha=1.0).numpy() + 1.0
+    np.testing.assert_allclose(orc.phi_elu1(x), lib, rtol=1e-14, atol=1e-15)
+    assert np.all(orc.phi_elu1(x) > 0)
+
+
+def test_favor_unbiased_for_exp_kernel():
+    """E[phi(q).phi(k)] = exp(q.k) for w ~ N(0, I): the FAVOR+ property
+    ("Choosing the Feature Map phi"). A flipped sign of |x|^2/2, a missing
+    1/sqrt(r) or a transposed omega all move the mean by many sigmas."""
+    rng = np.random.default_rng(7)
+    d, r, draws = 4, 64, 4000
+    q = np.array([0.3, -0.2, 0.4, 0.1])
+    k = np.array([-0.1, 0.5, 0.2, -0.3])
+    est = np.empty(draws)
+    for t in range(draws):
+        om = rng.standard_normal((r, d))
+        est[t] = orc.phi_favor(q, om) @ orc.phi_favor(k, om)
+    mean, sem = est.mean(), est.std(ddof=1) / math.sqrt(draws)
+    assert abs(mean - math.exp(q @ k)) < 6 * sem
+    assert sem < 0.01 * math.exp(q @ k)
+
+
+def test_favor_features_positive():
+    om = _rand(256, 64)
+    x = _rand(10, 64, scale=64 ** -0.25)
+    assert np.all(orc.phi_favor(x, om) > 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_favor_converges_to_softmax_attention(causal):
+    """With many random features the FAVOR+ output approaches softmax attention
+    with weights exp(q.k) (library SDPA with scale 1)."""
+    rng = np.random.default_rng(11)
+    n, d, r = 6, 4, 1 << 16
+    Q = rng.standard_normal((1, 1, n, d)) * 0.5
+    K = rng.standard_normal((1, 1, n, d)) * 0.5
+    V = rng.standard_normal((1, 1, n, 3))
+    om = rng.standard_normal((r, d))
+    if causal:
+        o = orc.causal_recurrent(Q, K, V, "favor", om, None, eps=0.0)[0]
+    else:
+        o = orc.noncausal(Q, K, V, "favor", om, eps=0.0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V),
+        is_causal=causal, scale=1.0).numpy()
+    assert orc.rowwise_rel_err(o, ref) < 3e-2
+
+
+# ---------------------------------------------------------------- non-causal
+
+def _nc_inputs(n=256, d=32, dv=32, seed=0, scale=None):
+    rng = np.random.default_rng(seed)
+    s = d ** -0.5 if scale is None else scale
+    return (rng.standard_normal((1, 1, n, d)) * s, rng.standard_normal((1, 1, n, d)) * s,
+            rng.standard_normal((1, 1, n, dv)) * s)
+
+
+def test_noncausal_reassociation_equals_explicit_matrix():
+    """(phiQ phiK^T) V == phiQ (phiK^T V): the reassociation identity, at the
+    non-causal workload's full size (explicit 256 x 256 weight matrix)."""
+    Q, K, V = _nc_inputs()
+    a = orc.noncausal(Q, K, V, eps=1e-6)
+    b = orc.brute(Q, K, V, causal=False, eps=1e-6)
+    assert orc.rowwise_rel_err(a, b) < 1e-12
+
+
+def test_noncausal_rectangular_favor_reassociation():
+    # r != d_k != d_v: a transposed operand anywhere breaks the shapes or values
+    rng = np.random.default_rng(3)
+    Q = rng.standard_normal((2, 3, 9, 5)) * 0.4
+    K = rng.standard_normal((2, 3, 9, 5)) * 0.4
+    V = rng.standard_normal((2, 3, 9, 7))
+    om = rng.standard_normal((16, 5))
+    a = orc.noncausal(Q, K, V, "favor", om, eps=1e-6)
+    b = orc.brute(Q, K, V, "favor", om, causal=False, eps=1e-6)
+    assert a.shape == (2, 3, 9, 7)
+    assert orc.rowwise_rel_err(a, b) < 1e-12
+
+
+def test_noncausal_permutation_invariant():
+    Q, K, V = _nc_inputs(n=64, scale=1.0)
+    p = np.random.default_rng(5).permutation(64)
+    a = orc.noncausal(Q, K, V)
+    b = orc.noncausal(Q, K[:, :, p], V[:, :, p])
+    assert orc.rowwise_rel_err(a, b) < 1e-13
+
+
+def test_uniform_weights_give_plain_mean():
+    """Q = K = 0 makes every elu+1 feature exactly 1: non-causal output is the
+    mean of V, causal output is the running (prefix) mean."""
+    rng = np.random.default_rng(9)
+    n, d = 50, 8
+    Z = np.zeros((1, 1, n, d))
+    V = rng.standard_normal((1, 1, n, 3))
+    nc = orc.noncausal(Z, Z, V, eps=0.0)
+    np.testing.assert_allclose(nc, np.broadcast_to(V.mean(axis=2, keepdims=True), nc.shape), rtol=1e-13)
+    c = orc.causal_recurrent(Z, Z, V, eps=0.0)[0]
+    prefix = np.cumsum(V, axis=2) / np.arange(1, n + 1)[None, None, :, None]
+    np.testing.assert_allclose(c, prefix, rtol=1e-12, atol=1e-15)
+
+
+def test_constant_values_and_eps():
+    # V == c everywhere: o = c * den / (den + eps), den = phi(q).sum(phi(k))
+    Q, K, _ = _nc_inputs(n=40, scale=1.0)
+    V = np.full((1, 1, 40, 4), 2.5)
+    eps = 1e-2
+    pq, pk = orc.phi_elu1(Q), orc.phi_elu1(K)
+    den = np.einsum("bhir,bhjr->bhi", pq, pk)
+    want = 2.5 * den / (den + eps)
+    np.testing.assert_allclose(orc.noncausal(Q, K, V, eps=eps), np.broadcast_to(want[..., None], (1, 1, 40, 4)), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- causal forms
+
+CASES = [("elu1", "none"), ("elu1", "decay"), ("elu1", "gla"),
+         ("favor", "none"), ("favor", "decay"), ("favor", "gla")]
+
+
+def _causal_case(fmap, gate, B=2, H=3, n=23, d=6, dv=5, r=12, seed=0):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((B, H, n, d)) * 0.7
+    K = rng.standard_normal((B, H, n, d)) * 0.7
+    V = rng.standard_normal((B, H, n, dv))
+    om = rng.standard_normal((r, d)) if fmap == "favor" else None
+    rr = r if fmap == "favor" else d
+    if gate == "none":
+        gt = None
+    elif gate == "decay":
+        gt = ("decay", 1.0 - 2.0 ** (-1.0 - np.arange(H)))
+    else:
+        gt = ("gla", rng.standard_normal((B, H, n, rr)) * 2.0, 4.0)
+    return Q, K, V, om, gt
+
+
+@pytest.mark.parametrize("fmap,gate", CASES)
+def test_parallel_equals_recurrent(fmap, gate):
+    """The parallel (masked weight matrix) and recurrent forms agree: the
+    duality of "Recurrent Reformulation" / "The recurrent form (causal)"."""
+    Q, K, V, om, gt = _causal_case(fmap, gate)
+    a = orc.brute(Q, K, V, fmap, om, causal=True, gate=gt, eps=1e-6)
+    b = orc.causal_recurrent(Q, K, V, fmap, om, gt, eps=1e-6)[0]
+    assert orc.rowwise_rel_err(b, a) < 1e-12
+
+
+@pytest.mark.parametrize("fmap,gate", CASES)
+def test_split_sequence_resumes(fmap, gate):
+    """Carrying (S, z) out of a prefix and into the rest equals one pass."""
+    Q, K, V, om, gt = _causal_case(fmap, gate, n=30)
+    full, Sf, zf = orc.causal_recurrent(Q, K, V, fmap, om, gt)
+    m = 11
+
+    def cut(gg, sl):
+        if gg is None or gg[0] != "gla":
+            return gg
+        return ("gla", gg[1][:, :, sl], gg[2])
+    a, S1, z1 = orc.causal_recurrent(Q[:, :, :m], K[:, :, :m], V[:, :, :m], fmap, om, cut(gt, slice(0, m)))
+    b, S2, z2 = orc.causal_recurrent(Q[:, :, m:], K[:, :, m:], V[:, :, m:], fmap, om, cut(gt, slice(m, None)),
+                                     S0=S1, z0=z1)
+    assert orc.rowwise_rel_err(np.concatenate([a, b], axis=2), full) < 1e-12
+    np.testing.assert_allclose(S2, Sf, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z2, zf, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("fmap,gate", CASES)
+def test_decode_step_is_one_recurrence_step(fmap, gate):
+    Q, K, V, om, gt = _causal_case(fmap, gate, n=8)
+    full, _, _ = orc.causal_recurrent(Q, K, V, fmap, om, gt)
+    pre = gt
+    if gt is not None and gt[0] == "gla":
+        pre = ("gla", gt[1][:, :, :7], gt[2])
+    _, S7, z7 = orc.causal_recurrent(Q[:, :, :7], K[:, :, :7], V[:, :, :7], fmap, om, pre)
+    step_gate = gt if gt is None or gt[0] != "gla" else ("gla", gt[1][:, :, 7], gt[2])
+    o, _, _ = orc.decode_step(S7, z7, Q[:, :, 7], K[:, :, 7], V[:, :, 7], fmap, om, step_gate)
+    np.testing.assert_allclose(o, full[:, :, 7], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("gate", ["none", "decay", "gla"])
+def test_first_token_state_is_outer_product(gate):
+    """From a zero state, one token leaves S = phi(k) v^T and z = phi(k) under
+    any gate (the gate multiplies the previous state, not the new token), and
+    o_0 = v_0 * w / (w + eps) with w = phi(q).phi(k)."""
+    Q, K, V, om, gt = _causal_case("elu1", gate, n=1)
+    eps = 0.3
+    o, S, z = orc.causal_recurrent(Q, K, V, "elu1", None, gt, eps=eps)
+    pk, pq = orc.phi_elu1(K[:, :, 0]), orc.phi_elu1(Q[:, :, 0])
+    np.testing.assert_allclose(S, pk[..., :, None] * V[:, :, 0, None, :], rtol=1e-15)
+    np.testing.assert_allclose(z, pk, rtol=1e-15)
+    w = np.sum(pq * pk, axis=-1)
+    np.testing.assert_allclose(o[:, :, 0], V[:, :, 0] * (w / (w + eps))[..., None], rtol=1e-14)
+
+
+def test_decay_geometric_closed_form():
+    """RetNet weights gamma^(i-j) ("Gating and Selective State Updates"): with
+    all features 1 and a single unit value at t = 0, the output is
+    gamma^i (1 - gamma) / (1 - gamma^(i+1)). An undecayed normaliser or a
+    wrong exponent fails this."""
+    n, H = 40, 3
+    gam = np.array([0.5, 0.9, 1.0 - 2.0 ** -12])
+    Z = np.zeros((1, H, n, 4))
+    V = np.zeros((1, H, n, 1))
+    V[:, :, 0, 0] = 1.0
+    o = orc.causal_recurrent(Z, Z, V, gate=("decay", gam), eps=0.0)[0][0, :, :, 0]
+    i = np.arange(n)[None, :]
+    g = gam[:, None]
+    want = g ** i * (1 - g) / (1 - g ** (i + 1))
+    np.testing.assert_allclose(o, want, rtol=1e-10)
+
+
+def test_decay_matches_iir_filter():
+    """With all features 1, numerator and denominator are first-order IIR
+    filters y_i = gamma y_{i-1} + x_i (scipy.signal.lfilter)."""
+    rng = np.random.default_rng(21)
+    n, gam = 64, 0.8
+    Z = np.zeros((1, 1, n, 4))
+    V = rng.standard_normal((1, 1, n, 2))
+    o = orc.causal_recurrent(Z, Z, V, gate=("decay", np.array([gam])), eps=0.0)[0][0, 0]
+    num = scipy.signal.lfilter([1.0], [1.0, -gam], V[0, 0] * 4.0, axis=0)
+    den = scipy.signal.lfilter([1.0], [1.0, -gam], np.full(n, 4.0))
+    np.testing.assert_allclose(o, num / den[:, None], rtol=1e-12)
+
+
+@pytest.mark.parametrize("fmap", ["elu1", "favor"])
+def test_unit_gates_reduce_to_ungated(fmap):
+    """gamma = 1 and alpha = 1 (g -> +inf) give plain causal linear attention
+    ("When G_t = 1 everywhere, the model behaves like standard linear
+    attention")."""
+    Q, K, V, om, _ = _causal_case(fmap, "none")
+    base = orc.causal_recurrent(Q, K, V, fmap, om, None)[0]
+    d1 = orc.causal_recurrent(Q, K, V, fmap, om, ("decay", np.ones(3)))[0]
+    rr = om.shape[0] if om is not None else Q.shape[-1]
+    g1 = orc.causal_recurrent(Q, K, V, fmap, om, ("gla", np.full(Q.shape[:3] + (rr,), 1e4), 16.0))[0]
+    assert orc.rowwise_rel_err(d1, base) == 0.0
+    assert orc.rowwise_rel_err(g1, base) == 0.0
+
+
+def test_zero_gate_overwrites_state():
+    """alpha = 0 (g -> -inf) fully overwrites the state ("When G_t = 0, the
+    state is fully overwritten"): o_t = v_t * w_t / (w_t + eps)."""
+    Q, K, V, _, _ = _causal_case("elu1", "none")
+    eps = 0.05
+    o = orc.causal_recurrent(Q, K, V, gate=("gla", np.full(Q.shape, -1e4), 16.0), eps=eps)[0]
+    w = np.sum(orc.phi_elu1(Q) * orc.phi_elu1(K), axis=-1)
+    np.testing.assert_allclose(o, V * (w / (w + eps))[..., None], rtol=1e-13)
+
+
+def test_constant_gla_equals_decay():
+    """A GLA gate that is constant over time and features is a fixed decay with
+    gamma = sigmoid(g)^(1/tau)."""
+    Q, K, V, _, _ = _causal_case("elu1", "none")
+    gval, tau = 0.7, 16.0
+    gam = scipy.special.expit(gval) ** (1.0 / tau)
+    a = orc.causal_recurrent(Q, K, V, gate=("gla", np.full(Q.shape, gval), tau))[0]
+    b = orc.causal_recurrent(Q, K, V, gate=("decay", np.full(3, gam)))[0]
+    assert orc.rowwise_rel_err(a, b) < 1e-13
+    assert abs(orc.gla_alpha(0.0, 16.0) - 2.0 ** (-1.0 / 16.0)) < 1e-15
+
+
+@pytest.mark.parametrize("fmap,gate", CASES)
+def test_normaliser_positive_and_outputs_convex(fmap, gate):
+    """Similarities are non-negative ("must keep similarities >= 0"), so the
+    denominator is at least eps and each output coordinate, rescaled by
+    (den + eps) / den, lies between the min and max of the values it mixes."""
+    Q, K, V, om, gt = _causal_case(fmap, gate, n=20)
+    W = orc.kernel_weights(Q, K, fmap, om, True, gt)
+    assert np.all(W >= 0)
+    eps = 1e-6
+    o = orc.attention_from_weights(W, V, eps)
+    den = W.sum(-1)
+    assert np.all(den + eps >= eps)
+    scaled = o * ((den + eps) / den)[..., None]
+    for i in range(Q.shape[2]):
+        lo = V[:, :, :i + 1].min(axis=2)
+        hi = V[:, :, :i + 1].max(axis=2)
+        assert np.all(scaled[:, :, i] >= lo - 1e-12) and np.all(scaled[:, :, i] <= hi + 1e-12)
+
+
+@pytest.mark.parametrize("gate", ["none", "decay", "gla"])
+def test_exact_zero_probe_causal_mask(gate):
+    """A single unit value at position p: every output before p is exactly
+    zero (no future leak), and o_p is positive in the marked column."""
+    Q, K, _, _, gt = _causal_case("elu1", gate, n=30)
+    V = np.zeros(Q.shape[:3] + (5,))
+    p, col = 17, 2
+    V[:, :, p, col] = 1.0
+    o = orc.causal_recurrent(Q, K, V, gate=gt)[0]
+    assert np.all(o[:, :, :p] == 0.0)
+    assert np.all(o[:, :, p, col] > 0)
+    others = np.delete(o, col, axis=-1)
+    assert np.all(others == 0.0)
+
+
+# ---------------------------------------------------------------- the one printed figure
+
+def test_quadratic_baseline_figure(repo_root):
+    """Golden: the page's size of one n = 16384 float16 score matrix."""
+    vals = {}
+    with open(os.path.join(repo_root, "tests", "golden", "quadratic_baseline.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = (s.strip() for s in line.split("="))
+                vals[k] = float(v)
+    n = int(vals["n"])
+    assert abs(orc.softmax_score_matrix_bytes(n, 1) - vals["entries_approx"]) / vals["entries_approx"] < 0.005
+    assert abs(orc.softmax_score_matrix_bytes(n, 2) - vals["bytes_fp16_approx"]) / vals["bytes_fp16_approx"] < 0.005
+    assert orc.softmax_score_matrix_bytes(n, 2) == 536_870_912
+
+
+# ---------------------------------------------------------------- metric
+
+def test_rowwise_metric():
+    ref = np.array([[1.0, -2.0, 0.5], [0.0, 0.0, 0.0], [3.0, 0.0, 0.0]])
+    got = ref.copy()
+    assert orc.rowwise_rel_err(got, ref) == 0.0
+    got[0, 2] += 0.02  # 0.02 / 2.0
+    assert abs(orc.rowwise_rel_err(got, ref) - 0.01) < 1e-15
+    got[1, 0] = 1e-9  # a nonzero where the reference row is all zero
+    assert orc.rowwise_rel_err(got, ref) == math.inf
+    got[1, 0] = np.nan
+    assert orc.rowwise_rel_err(got, ref) == math.inf
