@@ -1,0 +1,174 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) kernelized linear attention library.
+ *
+ * The library computes, for every (batch b, head h) independently,
+ *
+ *     o_i = phi(q_i)^T S / (phi(q_i)^T z + eps),
+ *     S   = sum_j phi(k_j) v_j^T   (r x d_v),   z = sum_j phi(k_j)   (r),
+ *
+ * ("Linear Attention Mechanisms" (dileepadev.github.io), section "The Kernel
+ * Trick for Attention"; the eps added to the denominator follows the routine in
+ * "Linear Attention Mechanisms" (sadullah.online), section "The linear
+ * attention trick: drop or approximate the softmax").
+ *
+ * Non-causal: the sums run over all j. Causal: over j <= i, optionally with a
+ * per-head fixed decay (S_i = gamma_h S_{i-1} + phi(k_i) v_i^T) or a per-step
+ * diagonal gate on the feature axis (S_t = diag(alpha_t) S_{t-1} + phi(k_t)
+ * v_t^T), where z is decayed or gated exactly like S ("Gating and Selective
+ * State Updates" on the dileepadev page; "Evolution: add decay/gating" on
+ * "Attention-Free / Sub-Quadratic Architectures" (blog.vguerra.net)).
+ *
+ * Conventions shared by every entry point:
+ *   * Tensors are dense, row-major, contiguous: Q, K [B][H][n][d_k];
+ *     V [B][H][n][d_v]; out [B][H][n][d_v]; state S [B][H][r][d_v] fp32;
+ *     normaliser z [B][H][r] fp32; GLA gate input g [B][H][n][r].
+ *   * Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte
+ *     aligned. The library allocates no memory and keeps no state between
+ *     calls; scratch memory is passed in as `workspace`.
+ *   * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream). Argument errors are returned synchronously before anything is
+ *     launched; LA_ERR_HIP means the HIP runtime refused a launch. Faults of
+ *     the device surface at the caller's next synchronisation.
+ *   * NaN or Inf in the inputs propagate to the outputs; they are not checked.
+ *   * Results are deterministic: no atomics, fixed reduction orders.
+ *   * Functions are re-entrant; concurrent calls on different streams are
+ *     safe when their output and workspace buffers do not overlap.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+typedef enum la_status {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, bad size or enum, eps < 0, tau <= 0 */
+  LA_ERR_UNSUPPORTED = 2, /* well-formed but outside the built set (dims, dtype mix) */
+  LA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than la_forward_workspace_size */
+  LA_ERR_ALIAS = 4,       /* an output overlaps an input or another output */
+  LA_ERR_HIP = 5          /* the HIP runtime reported an error for a launch */
+} la_status;
+
+typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* Feature maps ("Choosing the Feature Map phi", dileepadev page):
+ *   ELU1  : phi(x) = elu(x) + 1 elementwise (r == d_k).
+ *   FAVOR : phi(x)_m = exp(w_m . x - |x|^2 / 2) / sqrt(r), m = 0..r-1, the
+ *           positive random features whose inner product estimates exp(q.k);
+ *           omega holds the r rows w_m. */
+typedef enum la_fmap_kind { LA_FMAP_ELU1 = 0, LA_FMAP_FAVOR = 1 } la_fmap_kind;
+
+/* State gates for the causal form ("Gating and Selective State Updates"):
+ *   NONE  : S_t = S_{t-1} + phi(k_t) v_t^T.
+ *   DECAY : S_t = gamma_h S_{t-1} + phi(k_t) v_t^T (RetNet fixed decay).
+ *   GLA   : S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T with
+ *           alpha_t = sigmoid(g_t)^(1/tau) per feature row (diagonal GLA gate). */
+typedef enum la_gate_kind { LA_GATE_NONE = 0, LA_GATE_DECAY = 1, LA_GATE_GLA = 2 } la_gate_kind;
+
+typedef struct la_problem {
+  int32_t B, H;      /* batch, heads: >= 1 */
+  int32_t n;         /* sequence length: >= 1 (== 1 for la_decode_step) */
+  int32_t d_k, d_v;  /* key/query and value widths */
+  int32_t in_dtype;  /* la_dtype of Q, K, V, g and omega */
+  int32_t out_dtype; /* la_dtype of out */
+  float eps;         /* added to every denominator; finite and >= 0 */
+} la_problem;
+
+typedef struct la_feature_map {
+  int32_t kind;      /* la_fmap_kind */
+  int32_t r;         /* feature dimension; must equal d_k for ELU1 */
+  const void* omega; /* FAVOR: device [r][d_k] in in_dtype. ELU1: must be NULL */
+} la_feature_map;
+
+typedef struct la_gate {
+  int32_t kind;       /* la_gate_kind */
+  float tau;          /* GLA temperature, > 0 (ignored otherwise) */
+  const float* gamma; /* DECAY: device [H] fp32, each in (0, 1] -- a documented
+                         precondition, not checked (the values live on the device) */
+  const void* g;      /* GLA: device [B][H][n][r] in in_dtype (decode: [B][H][r]) */
+} la_gate;
+
+/* ABI version of the loaded library (LA_ABI_VERSION at build time). */
+int32_t la_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* la_status_str(int32_t status);
+
+/*
+ * Bytes of device workspace la_forward needs for this problem (0 if none).
+ * Pure host computation: no HIP call is made. Same validation as la_forward
+ * (pointer fields of fmap/gate are not inspected).
+ */
+la_status la_forward_workspace_size(const la_problem* p, const la_feature_map* fmap,
+                                    int32_t causal, const la_gate* gate, size_t* bytes);
+
+/*
+ * How la_forward splits each head's sequence for the causal form: *segments
+ * contiguous pieces of *segment_len tokens (the last may be shorter), each a
+ * multiple of the 64-token chunk. Pure host computation; 1 for non-causal.
+ */
+la_status la_forward_segments(const la_problem* p, const la_feature_map* fmap,
+                              int32_t causal, const la_gate* gate,
+                              int32_t* segments, int32_t* segment_len);
+
+/*
+ * Full-sequence forward pass.
+ *   Q, K, V       inputs (in_dtype), layouts above.
+ *   fmap          feature map; gate: may be NULL (= NONE); must be NONE when causal == 0.
+ *   causal        0: sums over all j ("The linear attention trick", sadullah page);
+ *                 1: sums over j <= i ("Recurrent Reformulation", dileepadev page).
+ *   S0, z0        optional initial state carried in (causal only; both or neither;
+ *                 NULL = zero), fp32 [B][H][r][d_v] and [B][H][r].
+ *   S_final, z_final  optional (both or neither): the state after the last
+ *                 token (for non-causal, the full sums S and z), fp32.
+ *   out           [B][H][n][d_v] in out_dtype; must not overlap any input.
+ *   workspace     device scratch of at least la_forward_workspace_size bytes
+ *                 (may be NULL when that size is 0), 256-byte aligned.
+ * Supported (else LA_ERR_UNSUPPORTED):
+ *   causal: in_dtype BF16, out_dtype BF16; ELU1 with d_k in {32,64,128};
+ *           FAVOR with d_k in {32,64,128}, r in {64,128,256}, gate NONE or DECAY;
+ *           d_v in {32,64,128}; r * d_v <= 16384.
+ *   non-causal: in/out dtype F32 or BF16 (any mix); same d_k, d_v, r sets.
+ * Numerics: bf16 MFMA products with fp32 accumulation; the state, normaliser,
+ * gate factors and every denominator are fp32; the division is IEEE fp32.
+ */
+la_status la_forward(const la_problem* p, const void* Q, const void* K, const void* V,
+                     const la_feature_map* fmap, int32_t causal, const la_gate* gate,
+                     const float* S0, const float* z0, float* S_final, float* z_final,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent step for a batch of carried states, updated IN PLACE
+ * ("Recurrent Reformulation", dileepadev page: rank-1 update of S, update of
+ * z, then the read-out):
+ *   S' = G S + phi(k) v^T,  z' = G z + phi(k),  out = phi(q)^T S' / (phi(q)^T z' + eps)
+ * with G = 1, gamma_h or diag(alpha).
+ *   p->n must be 1; q, k [B][H][d_k], v [B][H][d_v], gate->g [B][H][r] (in_dtype);
+ *   S [B][H][r][d_v] fp32 and z [B][H][r] fp32 are read and overwritten;
+ *   out [B][H][d_v] in out_dtype.
+ * Supported: in_dtype F32 or BF16, out_dtype F32 or BF16; ELU1 d_k in {32,64,128};
+ * FAVOR d_k in {32,64,128}, r in {64,128,256}; any gate; d_v in {32,64,128}.
+ */
+la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
+                         const void* k, const void* v, const la_feature_map* fmap,
+                         const la_gate* gate, void* out, void* stream);
+
+/*
+ * The feature map alone: out[i][m] = phi(X[i])_m in fp32 for `rows` rows of
+ * width d_k ("Choosing the Feature Map phi", dileepadev page).
+ *   X [rows][d_k] in in_dtype; out [rows][r] fp32. Same d_k / r sets as above.
+ */
+la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t d_k,
+                               int32_t in_dtype, const void* X, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,201 @@
+"""Python entry points over the C ABI (argument marshalling only).
+
+Torch supplies device memory and the current stream; every step of the
+computation runs in the HIP kernels of liblinattn.so. Shapes are read from the
+tensors and cross-checked here, because the C ABI receives only pointers and
+sizes.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native as N
+
+_DT = {torch.float32: N.LA_F32, torch.bfloat16: N.LA_BF16}
+_FMAP = {"elu1": N.LA_FMAP_ELU1, "favor": N.LA_FMAP_FAVOR}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor, stream=None):
+    s = torch.cuda.current_stream(t.device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _fmap_struct(fmap: str, omega, d_k: int):
+    if fmap not in _FMAP:
+        raise ValueError(f"unknown feature map {fmap!r}")
+    if fmap == "favor":
+        if omega is None:
+            raise ValueError("favor needs omega [r, d_k]")
+        _dev(omega, "omega")
+        if omega.dim() != 2 or omega.shape[1] != d_k:
+            raise ValueError(f"omega must be [r, {d_k}], got {tuple(omega.shape)}")
+        return N.LaFeatureMap(N.LA_FMAP_FAVOR, omega.shape[0], omega.data_ptr()), omega.shape[0]
+    if omega is not None:
+        raise ValueError("elu1 takes no omega")
+    return N.LaFeatureMap(N.LA_FMAP_ELU1, d_k, None), d_k
+
+
+def _gate_struct(gate, expect_g_shape):
+    """gate: None | ("decay", gamma[H] fp32) | ("gla", g, tau)."""
+    if gate is None or gate == "none" or (isinstance(gate, tuple) and gate[0] == "none"):
+        return N.LaGate(N.LA_GATE_NONE, 1.0, None, None)
+    kind = gate[0]
+    if kind == "decay":
+        gam = _dev(gate[1], "gamma")
+        if gam.dtype != torch.float32 or gam.shape != (expect_g_shape[1],):
+            raise ValueError("gamma must be float32 [H]")
+        return N.LaGate(N.LA_GATE_DECAY, 1.0, gam.data_ptr(), None)
+    if kind == "gla":
+        g = _dev(gate[1], "g")
+        if tuple(g.shape) != tuple(expect_g_shape):
+            raise ValueError(f"g must be {tuple(expect_g_shape)}, got {tuple(g.shape)}")
+        return N.LaGate(N.LA_GATE_GLA, float(gate[2]), None, g.data_ptr())
+    raise ValueError(f"unknown gate {kind!r}")
+
+
+def _problem(B, H, n, d_k, d_v, in_dt, out_dt, eps):
+    return N.LaProblem(B, H, n, d_k, d_v, in_dt, out_dt, float(eps))
+
+
+def workspace_size(B, H, n, d_k, d_v, *, fmap="elu1", r=None, causal=True, gate_kind="none",
+                   dtype=torch.bfloat16, out_dtype=None) -> int:
+    """Workspace bytes la_forward needs (host arithmetic only)."""
+    r = d_k if r is None else r
+    out_dtype = dtype if out_dtype is None else out_dtype
+    p = _problem(B, H, n, d_k, d_v, _DT[dtype], _DT[out_dtype], 1e-6)
+    f = N.LaFeatureMap(_FMAP[fmap], r, 16 if fmap == "favor" else None)
+    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA}[gate_kind]
+    g = N.LaGate(gk, 16.0, None, None)
+    out = ctypes.c_size_t(0)
+    N.check(N.lib().la_forward_workspace_size(ctypes.byref(p), ctypes.byref(f), int(causal), ctypes.byref(g),
+                                              ctypes.byref(out)), "la_forward_workspace_size")
+    return out.value
+
+
+def segments(B, H, n, d_k, d_v, *, fmap="elu1", r=None, causal=True, gate_kind="none",
+             dtype=torch.bfloat16):
+    """(segments, segment_len) of the causal sequence split (host arithmetic only)."""
+    r = d_k if r is None else r
+    p = _problem(B, H, n, d_k, d_v, _DT[dtype], _DT[dtype], 1e-6)
+    f = N.LaFeatureMap(_FMAP[fmap], r, 16 if fmap == "favor" else None)
+    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA}[gate_kind]
+    g = N.LaGate(gk, 16.0, None, None)
+    P, L = ctypes.c_int32(0), ctypes.c_int32(0)
+    N.check(N.lib().la_forward_segments(ctypes.byref(p), ctypes.byref(f), int(causal), ctypes.byref(g),
+                                        ctypes.byref(P), ctypes.byref(L)), "la_forward_segments")
+    return P.value, L.value
+
+
+def forward(Q, K, V, *, fmap="elu1", omega=None, causal=True, gate=None, eps=1e-6, S0=None, z0=None,
+            return_state=False, out_dtype=None, out=None, workspace=None, stream=None):
+    """o = phi(Q) S / (phi(Q) z + eps) through la_forward.
+
+    Q, K [B, H, n, d_k]; V [B, H, n, d_v]; gate None | ("decay", gamma[H]) |
+    ("gla", g[B, H, n, r], tau). Returns out, or (out, S_final, z_final).
+    """
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
+        _dev(t, nm)
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
+        raise ValueError(f"shapes Q{tuple(Q.shape)} K{tuple(K.shape)} V{tuple(V.shape)} do not match")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K, V must share a dtype")
+    B, H, n, d_k = Q.shape
+    d_v = V.shape[3]
+    in_dt = _dt(Q)
+    out_dtype = Q.dtype if out_dtype is None else out_dtype
+    f, r = _fmap_struct(fmap, omega, d_k)
+    if omega is not None and omega.dtype != Q.dtype:
+        raise TypeError("omega must have the input dtype")
+    g = _gate_struct(gate, (B, H, n, r))
+    if g.kind == N.LA_GATE_GLA and gate[1].dtype != Q.dtype:
+        raise TypeError("g must have the input dtype")
+    p = _problem(B, H, n, d_k, d_v, in_dt, _DT[out_dtype], eps)
+    if out is None:
+        out = torch.empty((B, H, n, d_v), dtype=out_dtype, device=Q.device)
+    else:
+        _dev(out, "out")
+        if tuple(out.shape) != (B, H, n, d_v) or out.dtype != out_dtype:
+            raise ValueError("out has the wrong shape or dtype")
+    for t, nm, shp in ((S0, "S0", (B, H, r, d_v)), (z0, "z0", (B, H, r))):
+        if t is not None:
+            _dev(t, nm)
+            if tuple(t.shape) != shp or t.dtype != torch.float32:
+                raise ValueError(f"{nm} must be float32 {shp}")
+    Sf = zf = None
+    if return_state:
+        Sf = torch.empty((B, H, r, d_v), dtype=torch.float32, device=Q.device)
+        zf = torch.empty((B, H, r), dtype=torch.float32, device=Q.device)
+    ws_bytes = ctypes.c_size_t(0)
+    N.check(N.lib().la_forward_workspace_size(ctypes.byref(p), ctypes.byref(f), int(bool(causal)), ctypes.byref(g),
+                                              ctypes.byref(ws_bytes)), "la_forward_workspace_size")
+    need = ws_bytes.value
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    st = N.lib().la_forward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(f), int(bool(causal)),
+                            ctypes.byref(g), _ptr(S0), _ptr(z0), _ptr(Sf), _ptr(zf), _ptr(out),
+                            _ptr(workspace) if need else None, need, _stream(Q, stream))
+    N.check(st, "la_forward")
+    return (out, Sf, zf) if return_state else out
+
+
+def decode_step(S, z, q, k, v, *, fmap="elu1", omega=None, gate=None, eps=1e-6, out_dtype=torch.float32,
+                out=None, stream=None):
+    """One recurrent step; S [B, H, r, d_v] and z [B, H, r] (fp32) are updated in place.
+
+    q, k [B, H, d_k]; v [B, H, d_v]; gate None | ("decay", gamma[H]) |
+    ("gla", g[B, H, r], tau). Returns out [B, H, d_v].
+    """
+    for t, nm in ((S, "S"), (z, "z"), (q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [B, H, d_k] and v [B, H, d_v]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    B, H, d_k = q.shape
+    d_v = v.shape[2]
+    f, r = _fmap_struct(fmap, omega, d_k)
+    if tuple(S.shape) != (B, H, r, d_v) or S.dtype != torch.float32:
+        raise ValueError(f"S must be float32 {(B, H, r, d_v)}")
+    if tuple(z.shape) != (B, H, r) or z.dtype != torch.float32:
+        raise ValueError(f"z must be float32 {(B, H, r)}")
+    g = _gate_struct(gate, (B, H, r))
+    p = _problem(B, H, 1, d_k, d_v, _dt(q), _DT[out_dtype], eps)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
+    N.check(N.lib().la_decode_step(ctypes.byref(p), _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(f),
+                                   ctypes.byref(g), _ptr(out), _stream(q, stream)), "la_decode_step")
+    return out
+
+
+def feature_map(X, *, fmap="elu1", omega=None, stream=None):
+    """phi(X) over the last axis in fp32 through la_feature_map_apply."""
+    _dev(X, "X")
+    d_k = X.shape[-1]
+    f, r = _fmap_struct(fmap, omega, d_k)
+    rows = X.numel() // d_k
+    out = torch.empty(X.shape[:-1] + (r,), dtype=torch.float32, device=X.device)
+    N.check(N.lib().la_feature_map_apply(ctypes.byref(f), rows, d_k, _dt(X), _ptr(X), _ptr(out),
+                                         _stream(X, stream)), "la_feature_map_apply")
+    return out

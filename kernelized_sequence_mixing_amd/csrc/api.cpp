@@ -1,0 +1,345 @@
+// C ABI of the library: argument validation (all of it before any HIP call),
+// workspace sizing and segment planning (pure host arithmetic), and dispatch
+// to the kernel launchers on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "plan.hpp"
+
+namespace la {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_size(int dt) { return dt == LA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dt) { return dt == LA_F32 || dt == LA_BF16; }
+
+bool in_set(int x, std::initializer_list<int> s) {
+  for (int v : s)
+    if (x == v) return true;
+  return false;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + bytes};
+}
+
+bool overlaps(Range a, Range b) { return a.lo != 0 && b.lo != 0 && a.lo < b.hi && b.lo < a.hi; }
+
+la_status check_problem(const la_problem* p) {
+  if (p == nullptr) return LA_ERR_INVALID_ARG;
+  if (p->B < 1 || p->H < 1 || p->n < 1 || p->d_k < 1 || p->d_v < 1) return LA_ERR_INVALID_ARG;
+  if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype)) return LA_ERR_INVALID_ARG;
+  if (!(p->eps >= 0.f) || !isfinite(p->eps)) return LA_ERR_INVALID_ARG;
+  if ((long long)p->B * p->H > 65535) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+la_status check_fmap(const la_feature_map* f, int dk) {
+  if (f == nullptr) return LA_ERR_INVALID_ARG;
+  if (f->kind == LA_FMAP_ELU1) {
+    if (f->r != dk || f->omega != nullptr) return LA_ERR_INVALID_ARG;
+  } else if (f->kind == LA_FMAP_FAVOR) {
+    if (f->r < 1 || f->omega == nullptr) return LA_ERR_INVALID_ARG;
+    if (!aligned16(f->omega)) return LA_ERR_INVALID_ARG;
+  } else {
+    return LA_ERR_INVALID_ARG;
+  }
+  return LA_OK;
+}
+
+// gate may be NULL (= NONE). `check_ptrs` is false for the size queries.
+la_status check_gate(const la_gate* g, bool check_ptrs) {
+  if (g == nullptr || g->kind == LA_GATE_NONE) return LA_OK;
+  if (g->kind == LA_GATE_DECAY) {
+    if (check_ptrs && (g->gamma == nullptr || !aligned16(g->gamma))) return LA_ERR_INVALID_ARG;
+    return LA_OK;
+  }
+  if (g->kind == LA_GATE_GLA) {
+    if (!(g->tau > 0.f) || !isfinite(g->tau)) return LA_ERR_INVALID_ARG;
+    if (check_ptrs && (g->g == nullptr || !aligned16(g->g))) return LA_ERR_INVALID_ARG;
+    return LA_OK;
+  }
+  return LA_ERR_INVALID_ARG;
+}
+
+int gate_kind(const la_gate* g) { return g == nullptr ? LA_GATE_NONE : g->kind; }
+
+// The built set of (d_k, r, d_v) shapes; see the header.
+bool shapes_built(const la_feature_map* f, int dk, int dv, bool causal) {
+  if (!in_set(dk, {32, 64, 128})) return false;
+  if (causal ? !in_set(dv, {64, 128}) : !in_set(dv, {32, 64, 128})) return false;
+  if (f->kind == LA_FMAP_FAVOR && !in_set(f->r, {64, 128, 256})) return false;
+  return (long long)f->r * dv <= 16384;
+}
+
+void plan_segments(int B, int H, int n, int* P, int* seg_len) {
+  const int nchunks = (n + kChunk - 1) / kChunk;
+  const long long BH = (long long)B * H;
+  long long want = (kTargetGroups + BH - 1) / BH;
+  if (want < 1) want = 1;
+  if (want > nchunks) want = nchunks;
+  const int seg_chunks = int((nchunks + want - 1) / want);
+  *P = (nchunks + seg_chunks - 1) / seg_chunks;
+  *seg_len = seg_chunks * kChunk;
+}
+
+void plan_splits(int B, int H, int n, int* splits, int* split_len) {
+  const int tiles = (n + 31) / 32;
+  const long long BH = (long long)B * H;
+  long long want = (kTargetGroups + BH - 1) / BH;
+  if (want < 1) want = 1;
+  if (want > tiles) want = tiles;
+  const int per = int((tiles + want - 1) / want);
+  *split_len = per * 32;
+  *splits = (n + *split_len - 1) / *split_len;
+}
+
+struct WsLayout {
+  size_t S_off, z_off, logG_off, bytes;
+};
+
+WsLayout workspace_layout(const la_problem* p, const la_feature_map* f, int causal, int gate) {
+  WsLayout w{0, 0, 0, 0};
+  const size_t BH = (size_t)p->B * p->H;
+  size_t pieces;
+  if (causal) {
+    int P, L;
+    plan_segments(p->B, p->H, p->n, &P, &L);
+    if (P <= 1) return w;
+    pieces = (size_t)P;
+  } else {
+    int sp, L;
+    plan_splits(p->B, p->H, p->n, &sp, &L);
+    pieces = (size_t)sp;
+  }
+  const size_t r = (size_t)f->r;
+  w.S_off = 0;
+  w.z_off = round_up(BH * pieces * r * p->d_v * 4, kAlign);
+  w.logG_off = round_up(w.z_off + BH * pieces * r * 4, kAlign);
+  w.bytes = (causal && gate == LA_GATE_GLA) ? round_up(w.logG_off + BH * pieces * r * 4, kAlign) : w.logG_off;
+  return w;
+}
+
+// Validation shared by la_forward and its size queries (no pointers inspected).
+la_status check_forward_shape(const la_problem* p, const la_feature_map* f, int causal, const la_gate* g) {
+  la_status st = check_problem(p);
+  if (st != LA_OK) return st;
+  if ((st = check_fmap(f, p->d_k)) != LA_OK) return st;
+  if ((st = check_gate(g, false)) != LA_OK) return st;
+  if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
+  const int gk = gate_kind(g);
+  if (!causal && gk != LA_GATE_NONE) return LA_ERR_INVALID_ARG;
+  if (!shapes_built(f, p->d_k, p->d_v, causal != 0)) return LA_ERR_UNSUPPORTED;
+  if (causal) {
+    if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+    if (f->kind == LA_FMAP_FAVOR && gk == LA_GATE_GLA) return LA_ERR_UNSUPPORTED;
+  }
+  return LA_OK;
+}
+
+}  // namespace
+}  // namespace la
+
+using namespace la;
+
+extern "C" {
+
+int32_t la_abi_version(void) { return LA_ABI_VERSION; }
+
+const char* la_status_str(int32_t s) {
+  switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+    case LA_ERR_ALIAS: return "LA_ERR_ALIAS";
+    case LA_ERR_HIP: return "LA_ERR_HIP";
+  }
+  return "LA_ERR_UNKNOWN";
+}
+
+la_status la_forward_workspace_size(const la_problem* p, const la_feature_map* fmap, int32_t causal,
+                                    const la_gate* gate, size_t* bytes) {
+  if (bytes == nullptr) return LA_ERR_INVALID_ARG;
+  la_status st = check_forward_shape(p, fmap, causal, gate);
+  if (st != LA_OK) return st;
+  *bytes = workspace_layout(p, fmap, causal, gate_kind(gate)).bytes;
+  return LA_OK;
+}
+
+la_status la_forward_segments(const la_problem* p, const la_feature_map* fmap, int32_t causal,
+                              const la_gate* gate, int32_t* segments, int32_t* segment_len) {
+  if (segments == nullptr || segment_len == nullptr) return LA_ERR_INVALID_ARG;
+  la_status st = check_forward_shape(p, fmap, causal, gate);
+  if (st != LA_OK) return st;
+  if (!causal) {
+    *segments = 1;
+    *segment_len = p->n;
+    return LA_OK;
+  }
+  int P, L;
+  plan_segments(p->B, p->H, p->n, &P, &L);
+  *segments = P;
+  *segment_len = L;
+  return LA_OK;
+}
+
+la_status la_forward(const la_problem* p, const void* Q, const void* K, const void* V,
+                     const la_feature_map* fmap, int32_t causal, const la_gate* gate, const float* S0,
+                     const float* z0, float* S_final, float* z_final, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  la_status st = check_forward_shape(p, fmap, causal, gate);
+  if (st != LA_OK) return st;
+  if ((st = check_gate(gate, true)) != LA_OK) return st;
+  const int gk = gate_kind(gate);
+  if (Q == nullptr || K == nullptr || V == nullptr || out == nullptr) return LA_ERR_INVALID_ARG;
+  if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_INVALID_ARG;
+  if ((S_final == nullptr) != (z_final == nullptr)) return LA_ERR_INVALID_ARG;
+  if (!causal && S0 != nullptr) return LA_ERR_INVALID_ARG;
+  for (const void* ptr : {Q, K, V, (const void*)out, (const void*)S0, (const void*)z0, (const void*)S_final,
+                          (const void*)z_final})
+    if (ptr != nullptr && !aligned16(ptr)) return LA_ERR_INVALID_ARG;
+
+  const size_t BH = (size_t)p->B * p->H, n = (size_t)p->n, r = (size_t)fmap->r;
+  const size_t isz = dtype_size(p->in_dtype);
+  const Range rq = range_of(Q, BH * n * p->d_k * isz), rk = range_of(K, BH * n * p->d_k * isz),
+              rv = range_of(V, BH * n * p->d_v * isz);
+  const Range rg = range_of(gk == LA_GATE_GLA ? gate->g : nullptr, BH * n * r * isz);
+  const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
+  const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
+  const Range rs0 = range_of(S0, BH * r * p->d_v * 4), rz0 = range_of(z0, BH * r * 4);
+  const Range ro = range_of(out, BH * n * p->d_v * dtype_size(p->out_dtype));
+  const Range rsf = range_of(S_final, BH * r * p->d_v * 4), rzf = range_of(z_final, BH * r * 4);
+  const WsLayout wl = workspace_layout(p, fmap, causal, gk);
+  const Range rws = range_of(wl.bytes ? workspace : nullptr, wl.bytes);
+  for (Range o : {ro, rsf, rzf, rws}) {
+    for (Range i : {rq, rk, rv, rg, rgam, rom, rs0, rz0})
+      if (overlaps(o, i)) return LA_ERR_ALIAS;
+  }
+  if (overlaps(ro, rsf) || overlaps(ro, rzf) || overlaps(rsf, rzf) || overlaps(rws, ro) || overlaps(rws, rsf) ||
+      overlaps(rws, rzf))
+    return LA_ERR_ALIAS;
+  if (wl.bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < wl.bytes) return LA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return LA_ERR_WORKSPACE;
+  }
+
+  FwdPlan plan{};
+  plan.B = p->B;
+  plan.H = p->H;
+  plan.n = p->n;
+  plan.dk = p->d_k;
+  plan.dv = p->d_v;
+  plan.r = fmap->r;
+  plan.in_dtype = p->in_dtype;
+  plan.out_dtype = p->out_dtype;
+  plan.eps = p->eps;
+  plan.fmap = fmap->kind;
+  plan.gate = gk;
+  plan.causal = causal;
+  plan.tau = gk == LA_GATE_GLA ? gate->tau : 1.f;
+  plan.Q = Q;
+  plan.K = K;
+  plan.V = V;
+  plan.g = gk == LA_GATE_GLA ? gate->g : nullptr;
+  plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
+  plan.omega = fmap->omega;
+  plan.S0 = S0;
+  plan.z0 = z0;
+  plan.S_final = S_final;
+  plan.z_final = z_final;
+  plan.out = out;
+  plan.stream = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  plan.ws_S = wl.bytes ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
+  plan.ws_z = wl.bytes ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
+  plan.ws_logG = (wl.bytes && causal && gk == LA_GATE_GLA) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
+  if (causal) {
+    plan_segments(p->B, p->H, p->n, &plan.P, &plan.seg_len);
+    return fmap->kind == LA_FMAP_ELU1 ? launch_causal_elu1(plan) : launch_causal_favor(plan);
+  }
+  plan_splits(p->B, p->H, p->n, &plan.splits, &plan.split_len);
+  return launch_noncausal(plan);
+}
+
+la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q, const void* k, const void* v,
+                         const la_feature_map* fmap, const la_gate* gate, void* out, void* stream) {
+  la_status st = check_problem(p);
+  if (st != LA_OK) return st;
+  if (p->n != 1) return LA_ERR_INVALID_ARG;
+  if ((st = check_fmap(fmap, p->d_k)) != LA_OK) return st;
+  if ((st = check_gate(gate, true)) != LA_OK) return st;
+  if (S == nullptr || z == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return LA_ERR_INVALID_ARG;
+  for (const void* ptr : {(const void*)S, (const void*)z, q, k, v, (const void*)out})
+    if (!aligned16(ptr)) return LA_ERR_INVALID_ARG;
+  if (!shapes_built(fmap, p->d_k, p->d_v, false)) return LA_ERR_UNSUPPORTED;
+  const int gk = gate_kind(gate);
+  const size_t BH = (size_t)p->B * p->H, r = (size_t)fmap->r, isz = dtype_size(p->in_dtype);
+  const Range rS = range_of(S, BH * r * p->d_v * 4), rz = range_of(z, BH * r * 4);
+  const Range rq = range_of(q, BH * p->d_k * isz), rk = range_of(k, BH * p->d_k * isz),
+              rv = range_of(v, BH * p->d_v * isz);
+  const Range rg = range_of(gk == LA_GATE_GLA ? gate->g : nullptr, BH * r * isz);
+  const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
+  const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
+  const Range ro = range_of(out, BH * p->d_v * dtype_size(p->out_dtype));
+  for (Range o : {rS, rz, ro})
+    for (Range i : {rq, rk, rv, rg, rgam, rom})
+      if (overlaps(o, i)) return LA_ERR_ALIAS;
+  if (overlaps(rS, rz) || overlaps(ro, rS) || overlaps(ro, rz)) return LA_ERR_ALIAS;
+
+  DecodePlan plan{};
+  plan.B = p->B;
+  plan.H = p->H;
+  plan.dk = p->d_k;
+  plan.dv = p->d_v;
+  plan.r = fmap->r;
+  plan.in_dtype = p->in_dtype;
+  plan.out_dtype = p->out_dtype;
+  plan.eps = p->eps;
+  plan.fmap = fmap->kind;
+  plan.gate = gk;
+  plan.tau = gk == LA_GATE_GLA ? gate->tau : 1.f;
+  plan.S = S;
+  plan.z = z;
+  plan.q = q;
+  plan.k = k;
+  plan.v = v;
+  plan.g = gk == LA_GATE_GLA ? gate->g : nullptr;
+  plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
+  plan.omega = fmap->omega;
+  plan.out = out;
+  plan.stream = static_cast<hipStream_t>(stream);
+  return launch_decode(plan);
+}
+
+la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t d_k, int32_t in_dtype,
+                               const void* X, float* out, void* stream) {
+  if (rows < 1 || d_k < 1 || !valid_dtype(in_dtype)) return LA_ERR_INVALID_ARG;
+  la_status st = check_fmap(fmap, d_k);
+  if (st != LA_OK) return st;
+  if (X == nullptr || out == nullptr || !aligned16(X) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+  if (!in_set(d_k, {32, 64, 128})) return LA_ERR_UNSUPPORTED;
+  if (fmap->kind == LA_FMAP_FAVOR && !in_set(fmap->r, {64, 128, 256})) return LA_ERR_UNSUPPORTED;
+  if ((rows + 63) / 64 > 0x7fffffffLL) return LA_ERR_UNSUPPORTED;
+  const size_t isz = dtype_size(in_dtype);
+  const Range rx = range_of(X, (size_t)rows * d_k * isz), ro = range_of(out, (size_t)rows * fmap->r * 4);
+  const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, (size_t)fmap->r * d_k * isz);
+  if (overlaps(ro, rx) || overlaps(ro, rom)) return LA_ERR_ALIAS;
+  FmapPlan plan{rows, d_k, fmap->r, in_dtype, fmap->kind, X, fmap->omega, out, static_cast<hipStream_t>(stream)};
+  return launch_feature_map(plan);
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// One recurrent step of kernelized linear attention for a batch of carried
+// states, in place ("Recurrent Reformulation", "Linear Attention Mechanisms"
+// (dileepadev.github.io): a rank-1 update of S, an update of z, then the
+// read-out; gates per "Gating and Selective State Updates"):
+//
+//   S' = G S + phi(k) v^T,  z' = G z + phi(k),  o = phi(q)^T S' / (phi(q)^T z' + eps)
+//
+// The step streams each head's r x d_v fp32 state through once (read + write),
+// so it is bound by HBM bandwidth. One workgroup per (batch, head): thread
+// (row group, column quad) owns float4 column quads of R/(256/(E/4)) rows, all
+// loads issued before the prologue so the whole state is in flight while the
+// features are computed; the read-out reduction over rows goes through LDS.
+#include "vec_common.hpp"
+
+namespace la {
+
+struct DecodeArgs {
+  float* S;
+  float* z;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* omega;
+  const float* gamma;
+  void* out;
+  int H, in_dt, out_dt, gate;
+  float eps, inv_tau;
+};
+
+template <int R, int E, int DK, int FMAP>
+__global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
+  constexpr int CG = E / 4;          // float4 column quads per row
+  constexpr int RPP = 256 / CG;      // rows per pass
+  constexpr int PASSES = R / RPP;
+  __shared__ float sxq[DK], sxk[DK];
+  __shared__ float spq[R], spk[R], sal[R];
+  __shared__ __attribute__((aligned(16))) float sv[E];
+  __shared__ __attribute__((aligned(16))) float sred[RPP * E];
+  __shared__ float shalf[2], sden;
+  const int tid = threadIdx.x;
+  const long long bh = blockIdx.x;
+  const int col4 = tid % CG, r0 = tid / CG;
+  float4* Sh = reinterpret_cast<float4*>(a.S + bh * R * E);
+
+  // the whole state slice in flight first
+  float4 st[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) st[p] = Sh[(r0 + RPP * p) * CG + col4];
+
+  // features and gate of this token
+  for (int d = tid; d < DK; d += 256) {
+    sxq[d] = ld_elem(a.q, bh * DK + d, a.in_dt);
+    sxk[d] = ld_elem(a.k, bh * DK + d, a.in_dt);
+  }
+  for (int e = tid; e < E; e += 256) sv[e] = ld_elem(a.v, bh * E + e, a.in_dt);
+  __syncthreads();
+  if constexpr (FMAP == 1) {
+    if (tid < 2) {
+      const float* x = tid == 0 ? sxq : sxk;
+      float s = 0.f;
+      for (int d = 0; d < DK; ++d) s += x[d] * x[d];
+      shalf[tid] = 0.5f * s;
+    }
+    __syncthreads();
+  }
+  float zdot = 0.f;
+  if (tid < R) {
+    float pq, pk;
+    if constexpr (FMAP == 0) {
+      pq = elu1(sxq[tid]);
+      pk = elu1(sxk[tid]);
+    } else {
+      float aq = 0.f, ak = 0.f;
+      for (int d = 0; d < DK; ++d) {
+        const float w = ld_elem(a.omega, (long long)tid * DK + d, a.in_dt);
+        aq += w * sxq[d];
+        ak += w * sxk[d];
+      }
+      const float isr = rsqrtf(float(R));
+      pq = __expf(aq - shalf[0]) * isr;
+      pk = __expf(ak - shalf[1]) * isr;
+    }
+    float al = 1.f;
+    if (a.gate == LA_GATE_DECAY) al = a.gamma[bh % a.H];
+    if (a.gate == LA_GATE_GLA) al = __expf(gla_log_alpha(ld_elem(a.g, bh * R + tid, a.in_dt), a.inv_tau));
+    spq[tid] = pq;
+    spk[tid] = pk;
+    sal[tid] = al;
+    const float zn = al * a.z[bh * R + tid] + pk;
+    a.z[bh * R + tid] = zn;
+    zdot = pq * zn;
+  }
+  // denominator: block reduction of phi(q) . z'
+  zdot += __shfl_xor(zdot, 1);
+  zdot += __shfl_xor(zdot, 2);
+  zdot += __shfl_xor(zdot, 4);
+  zdot += __shfl_xor(zdot, 8);
+  zdot += __shfl_xor(zdot, 16);
+  zdot += __shfl_xor(zdot, 32);
+  if ((tid & 63) == 0) sred[tid >> 6] = zdot;
+  __syncthreads();
+  if (tid == 0) {
+    float d = 0.f;
+    for (int w = 0; w < 4; ++w) d += sred[w];
+    sden = d + a.eps;
+  }
+  __syncthreads();
+
+  // rank-1 update in place and partial read-out over this thread's rows
+  const float4 vv = reinterpret_cast<const float4*>(sv)[col4];
+  float4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = r0 + RPP * p;
+    const float al = sal[r], pk = spk[r], pq = spq[r];
+    float4 s = st[p];
+    s.x = al * s.x + pk * vv.x;
+    s.y = al * s.y + pk * vv.y;
+    s.z = al * s.z + pk * vv.z;
+    s.w = al * s.w + pk * vv.w;
+    Sh[r * CG + col4] = s;
+    o.x += pq * s.x;
+    o.y += pq * s.y;
+    o.z += pq * s.z;
+    o.w += pq * s.w;
+  }
+  reinterpret_cast<float4*>(sred)[r0 * CG + col4] = o;
+  __syncthreads();
+  if (tid < E) {
+    float acc = 0.f;
+    for (int rg = 0; rg < RPP; ++rg) acc += sred[rg * E + tid];
+    st_elem(a.out, bh * E + tid, a.out_dt, acc / sden);
+  }
+}
+
+template <int R, int E, int DK, int FMAP>
+static la_status run_decode(const DecodePlan& p) {
+  DecodeArgs a{p.S, p.z, p.q, p.k, p.v, p.g, p.omega, p.gamma, p.out, p.H, p.in_dtype, p.out_dtype, p.gate,
+               p.eps, p.gate == LA_GATE_GLA ? 1.f / p.tau : 0.f};
+  hipLaunchKernelGGL((decode_step_kernel<R, E, DK, FMAP>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256), 0,
+                     p.stream, a);
+  return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+template <int R, int DK, int FMAP>
+static la_status dec_by_dv(const DecodePlan& p) {
+  switch (p.dv) {
+    case 32: return run_decode<R, 32, DK, FMAP>(p);
+    case 64: return run_decode<R, 64, DK, FMAP>(p);
+    case 128:
+      if constexpr (R * 128 <= 16384) return run_decode<R, 128, DK, FMAP>(p);
+      break;
+  }
+  return LA_ERR_UNSUPPORTED;
+}
+
+template <int R>
+static la_status dec_favor_by_dk(const DecodePlan& p) {
+  switch (p.dk) {
+    case 32: return dec_by_dv<R, 32, 1>(p);
+    case 64: return dec_by_dv<R, 64, 1>(p);
+    case 128: return dec_by_dv<R, 128, 1>(p);
+  }
+  return LA_ERR_UNSUPPORTED;
+}
+
+la_status launch_decode(const DecodePlan& p) {
+  if (p.fmap == LA_FMAP_ELU1) {
+    switch (p.dk) {
+      case 32: return dec_by_dv<32, 32, 0>(p);
+      case 64: return dec_by_dv<64, 64, 0>(p);
+      case 128: return dec_by_dv<128, 128, 0>(p);
+    }
+    return LA_ERR_UNSUPPORTED;
+  }
+  switch (p.r) {
+    case 64: return dec_favor_by_dk<64>(p);
+    case 128: return dec_favor_by_dk<128>(p);
+    case 256: return dec_favor_by_dk<256>(p);
+  }
+  return LA_ERR_UNSUPPORTED;
+}
+
+}  // namespace la

@@ -1,0 +1,80 @@
+// Host-side description of one validated call, shared by the C ABI layer and
+// the kernel launchers. Everything here is plain data; no HIP types leak into
+// the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/linattn.h"
+
+namespace la {
+
+constexpr int kChunk = 64;        // tokens per chunk of the causal kernel (= wave64)
+constexpr int kTargetGroups = 512; // workgroups per causal launch the segment split aims at
+
+struct FwdPlan {
+  int B, H, n, dk, dv, r;
+  int in_dtype, out_dtype;
+  float eps;
+  int fmap, gate, causal;
+  float tau;
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* g;
+  const void* omega;
+  const float* gamma;
+  const float* S0;
+  const float* z0;
+  float* S_final;
+  float* z_final;
+  void* out;
+  // causal segmentation: P segments of seg_len tokens (multiple of kChunk)
+  int P, seg_len;
+  // non-causal split of the sequence into partial sums
+  int splits, split_len;
+  // workspace carve (device)
+  float* ws_S;     // [BH][P or splits][r][dv]
+  float* ws_z;     // [BH][P or splits][r]
+  float* ws_logG;  // [BH][P][r]  (GLA only)
+  hipStream_t stream;
+};
+
+struct DecodePlan {
+  int B, H, dk, dv, r;
+  int in_dtype, out_dtype;
+  float eps;
+  int fmap, gate;
+  float tau;
+  float* S;
+  float* z;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* omega;
+  const float* gamma;
+  void* out;
+  hipStream_t stream;
+};
+
+struct FmapPlan {
+  int64_t rows;
+  int dk, r, in_dtype, fmap;
+  const void* X;
+  const void* omega;
+  float* out;
+  hipStream_t stream;
+};
+
+// Launchers (each returns LA_OK or LA_ERR_HIP / LA_ERR_UNSUPPORTED).
+la_status launch_causal_elu1(const FwdPlan& p);
+la_status launch_causal_favor(const FwdPlan& p);
+la_status launch_segment_scan(const FwdPlan& p);
+la_status launch_noncausal(const FwdPlan& p);
+la_status launch_decode(const DecodePlan& p);
+la_status launch_feature_map(const FmapPlan& p);
+
+}  // namespace la

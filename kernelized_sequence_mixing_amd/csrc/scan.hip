@@ -1,0 +1,48 @@
+// Chaining of per-segment states across one head's sequence (fp32):
+//   S_in(0) = S0 (or 0),  S_in(s+1) = Gamma_s S_in(s) + dS_s,
+// the associativity of the prefix state (the recurrence S_t = G_t S_{t-1} +
+// phi(k_t) v_t^T of "Recurrent Reformulation", "Linear Attention Mechanisms",
+// dileepadev.github.io, applied one segment at a time). Slot s of the workspace
+// holds dS_s on entry and S_in(s) on exit; z is chained the same way.
+#include "chunked.hpp"
+
+namespace la {
+
+__global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S, float* __restrict__ z,
+                                                           const float* __restrict__ logG,
+                                                           const float* __restrict__ S0,
+                                                           const float* __restrict__ z0,
+                                                           const float* __restrict__ gamma, int H, int P,
+                                                           int R, int E, int seg_len, int gate) {
+  const long long bh = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int RE = R * E;
+  if (idx >= RE + R) return;
+  const bool is_z = idx >= RE;
+  const int row = is_z ? idx - RE : idx / E;
+  float* base = is_z ? z + bh * P * R + row : S + bh * P * RE + idx;
+  const long long stride = is_z ? R : RE;
+  float cur = 0.f;
+  if (S0 != nullptr) cur = is_z ? z0[bh * R + row] : S0[bh * RE + idx];
+  float seg_decay = 1.f;
+  if (gate == GT_DECAY) seg_decay = exp2f(float(seg_len) * log2f(gamma[bh % H]));
+  for (int s = 0; s < P; ++s) {
+    const float d = base[s * stride];
+    base[s * stride] = cur;
+    if (s + 1 < P) {
+      float G = seg_decay;
+      if (gate == GT_GLA) G = __expf(logG[(bh * P + s) * R + row]);
+      cur = G * cur + d;
+    }
+  }
+}
+
+la_status launch_segment_scan(const FwdPlan& p) {
+  const int items = p.r * p.dv + p.r;
+  dim3 grid((items + 255) / 256, unsigned(p.B) * unsigned(p.H));
+  hipLaunchKernelGGL(segment_scan_kernel, grid, dim3(256), 0, p.stream, p.ws_S, p.ws_z, p.ws_logG, p.S0, p.z0,
+                     p.gamma, p.H, p.P, p.r, p.dv, p.seg_len, p.gate);
+  return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // namespace la

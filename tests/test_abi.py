@@ -1,0 +1,211 @@
+"""The C ABI on the host: exports, struct layouts, planning and argument checks.
+
+No test here launches a kernel. The validation tests pass fake device pointers
+that are only compared and never dereferenced; each case breaks exactly one
+rule that the library checks before any HIP call. They are skipped where a GPU
+is visible, so a validation bug can never turn into a launch on fake pointers.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from kernelized_sequence_mixing_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(N.LIB_PATH), reason="liblinattn.so not built")
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer checks run only without a GPU")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(N.EXPORTED)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", N.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+    lib = N.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name)
+
+
+@needs_lib
+def test_version_and_status_strings():
+    lib = N.lib()
+    assert lib.la_abi_version() == 1
+    names = [lib.la_status_str(i).decode() for i in range(6)]
+    assert names == ["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_ALIAS",
+                     "LA_ERR_HIP"]
+    assert lib.la_status_str(99).decode() == "LA_ERR_UNKNOWN"
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(f"""
+#include <stdio.h>
+#include <stddef.h>
+#include "{HEADER}"
+int main(void) {{
+  printf("%zu %zu %zu\\n", sizeof(la_problem), offsetof(la_problem, eps), offsetof(la_problem, out_dtype));
+  printf("%zu %zu %zu\\n", sizeof(la_feature_map), offsetof(la_feature_map, r), offsetof(la_feature_map, omega));
+  printf("%zu %zu %zu %zu\\n", sizeof(la_gate), offsetof(la_gate, tau), offsetof(la_gate, gamma), offsetof(la_gate, g));
+  return 0;
+}}""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    c = [list(map(int, ln.split())) for ln in lines if ln.strip()]
+    assert c[0] == [ctypes.sizeof(N.LaProblem), N.LaProblem.eps.offset, N.LaProblem.out_dtype.offset]
+    assert c[1] == [ctypes.sizeof(N.LaFeatureMap), N.LaFeatureMap.r.offset, N.LaFeatureMap.omega.offset]
+    assert c[2] == [ctypes.sizeof(N.LaGate), N.LaGate.tau.offset, N.LaGate.gamma.offset, N.LaGate.g.offset]
+
+
+# ------------------------------------------------------------------ planning (host arithmetic)
+
+@needs_lib
+@pytest.mark.parametrize("B,H,n,expect_P,expect_len", [
+    (4, 16, 4096, 8, 512),      # causal elu+1 workload
+    (2, 8, 8192, 32, 256),      # RetNet workload
+    (2, 16, 16384, 16, 1024),   # GLA workload
+    (1, 8, 32768, 64, 512),     # FAVOR+ workload
+    (1, 1, 1, 1, 64),
+    (1, 1, 65, 2, 64),
+    (600, 1, 100, 1, 128),
+])
+def test_segment_plan(B, H, n, expect_P, expect_len):
+    from kernelized_sequence_mixing_amd import segments
+    P, L = segments(B, H, n, 64, 64)
+    assert (P, L) == (expect_P, expect_len)
+    assert L % 64 == 0 and (P - 1) * L < n <= P * L
+
+
+@needs_lib
+def test_workspace_sizes():
+    from kernelized_sequence_mixing_amd import workspace_size
+    # one segment: nothing to chain
+    assert workspace_size(600, 1, 100, 64, 64) == 0
+    # 8 segments x 64 heads of 64x64 fp32 states + normalisers, each region 256-aligned
+    assert workspace_size(4, 16, 4096, 64, 64) == 64 * 8 * 64 * 64 * 4 + 64 * 8 * 64 * 4
+    gla = workspace_size(2, 16, 16384, 128, 128, gate_kind="gla")
+    plain = workspace_size(2, 16, 16384, 128, 128)
+    assert gla == plain + 32 * 16 * 128 * 4
+    # non-causal partial sums always need workspace
+    assert workspace_size(1, 1, 256, 32, 32, causal=False, dtype=torch.float32) > 0
+
+
+# ------------------------------------------------------------------ validation (no launch)
+
+FAKE = 0x7f0000000000  # a 256-aligned fake device address; never dereferenced
+SP = 1 << 32           # spacing of the fake buffers: far apart, so only planted overlaps exist
+
+
+def _args(**over):
+    d = dict(B=2, H=3, n=100, d_k=64, d_v=64, in_dt=N.LA_BF16, out_dt=N.LA_BF16, eps=1e-6,
+             fkind=N.LA_FMAP_ELU1, r=64, omega=None, causal=1, gkind=N.LA_GATE_NONE, tau=16.0, gamma=None, g=None,
+             Q=FAKE, K=FAKE + SP, V=FAKE + 2 * SP, S0=None, z0=None, Sf=None, zf=None,
+             out=FAKE + 3 * SP, ws=FAKE + 4 * SP, ws_bytes=1 << 30)
+    d.update(over)
+    return d
+
+
+def _forward(a):
+    p = N.LaProblem(a["B"], a["H"], a["n"], a["d_k"], a["d_v"], a["in_dt"], a["out_dt"], a["eps"])
+    f = N.LaFeatureMap(a["fkind"], a["r"], a["omega"])
+    g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"])
+    return N.lib().la_forward(ctypes.byref(p), a["Q"], a["K"], a["V"], ctypes.byref(f), a["causal"],
+                              ctypes.byref(g), a["S0"], a["z0"], a["Sf"], a["zf"], a["out"], a["ws"],
+                              a["ws_bytes"], None)
+
+
+BAD_FORWARD = [
+    ("B=0", dict(B=0), N.LA_ERR_INVALID_ARG),
+    ("n=0", dict(n=0), N.LA_ERR_INVALID_ARG),
+    ("d_v<0", dict(d_v=-64), N.LA_ERR_INVALID_ARG),
+    ("dtype 7", dict(in_dt=7), N.LA_ERR_INVALID_ARG),
+    ("eps<0", dict(eps=-1.0), N.LA_ERR_INVALID_ARG),
+    ("eps nan", dict(eps=float("nan")), N.LA_ERR_INVALID_ARG),
+    ("fmap kind", dict(fkind=5), N.LA_ERR_INVALID_ARG),
+    ("elu r != d_k", dict(r=32), N.LA_ERR_INVALID_ARG),
+    ("elu with omega", dict(omega=FAKE + 5 * SP), N.LA_ERR_INVALID_ARG),
+    ("favor no omega", dict(fkind=N.LA_FMAP_FAVOR, r=256), N.LA_ERR_INVALID_ARG),
+    ("favor odd r", dict(fkind=N.LA_FMAP_FAVOR, r=100, omega=FAKE + 5 * SP), N.LA_ERR_UNSUPPORTED),
+    ("favor+gla", dict(fkind=N.LA_FMAP_FAVOR, r=128, omega=FAKE + 5 * SP, gkind=N.LA_GATE_GLA,
+                       g=FAKE + 6 * SP), N.LA_ERR_UNSUPPORTED),
+    ("gate kind", dict(gkind=9), N.LA_ERR_INVALID_ARG),
+    ("tau<=0", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP, tau=0.0), N.LA_ERR_INVALID_ARG),
+    ("gla no g", dict(gkind=N.LA_GATE_GLA), N.LA_ERR_INVALID_ARG),
+    ("decay no gamma", dict(gkind=N.LA_GATE_DECAY), N.LA_ERR_INVALID_ARG),
+    ("noncausal gated", dict(causal=0, gkind=N.LA_GATE_DECAY, gamma=FAKE + 6 * SP), N.LA_ERR_INVALID_ARG),
+    ("causal flag 2", dict(causal=2), N.LA_ERR_INVALID_ARG),
+    ("d_k 48", dict(d_k=48, r=48), N.LA_ERR_UNSUPPORTED),
+    ("causal d_v 32", dict(d_v=32), N.LA_ERR_UNSUPPORTED),
+    ("causal fp32", dict(in_dt=N.LA_F32, out_dt=N.LA_F32), N.LA_ERR_UNSUPPORTED),
+    ("causal fp32 out", dict(out_dt=N.LA_F32), N.LA_ERR_UNSUPPORTED),
+    ("r*d_v too big", dict(fkind=N.LA_FMAP_FAVOR, r=256, d_v=128, omega=FAKE + 5 * SP), N.LA_ERR_UNSUPPORTED),
+    ("BH too big", dict(B=70000, H=1), N.LA_ERR_UNSUPPORTED),
+    ("Q null", dict(Q=None), N.LA_ERR_INVALID_ARG),
+    ("out null", dict(out=None), N.LA_ERR_INVALID_ARG),
+    ("Q misaligned", dict(Q=FAKE + 8), N.LA_ERR_INVALID_ARG),
+    ("S0 without z0", dict(S0=FAKE + 7 * SP), N.LA_ERR_INVALID_ARG),
+    ("Sf without zf", dict(Sf=FAKE + 7 * SP), N.LA_ERR_INVALID_ARG),
+    ("noncausal S0", dict(causal=0, S0=FAKE + 7 * SP, z0=FAKE + 8 * SP), N.LA_ERR_INVALID_ARG),
+    ("out aliases V", dict(out=FAKE + 2 * SP + 64), N.LA_ERR_ALIAS),
+    ("Sf aliases K", dict(Sf=FAKE + SP, zf=FAKE + 9 * SP), N.LA_ERR_ALIAS),
+    ("ws overlaps out", dict(B=4, H=16, n=4096, ws=FAKE + 3 * SP + 256), N.LA_ERR_ALIAS),
+    ("ws null", dict(B=4, H=16, n=4096, ws=None), N.LA_ERR_WORKSPACE),
+    ("ws small", dict(B=4, H=16, n=4096, ws_bytes=1024), N.LA_ERR_WORKSPACE),
+    ("ws misaligned", dict(B=4, H=16, n=4096, ws=FAKE + 4 * SP + 16), N.LA_ERR_WORKSPACE),
+]
+
+
+@needs_lib
+@no_gpu
+@pytest.mark.parametrize("name,over,want", BAD_FORWARD, ids=[b[0] for b in BAD_FORWARD])
+def test_forward_rejects(name, over, want):
+    assert _forward(_args(**over)) == want
+
+
+@needs_lib
+@no_gpu
+def test_decode_rejects():
+    lib = N.lib()
+
+    def call(n=1, S=FAKE, z=FAKE + 0x1000000, q=FAKE + 0x2000000, out=FAKE + 0x3000000, d_v=128, gk=0, tau=16.0):
+        p = N.LaProblem(4, 2, n, 128, d_v, N.LA_BF16, N.LA_F32, 1e-6)
+        f = N.LaFeatureMap(N.LA_FMAP_ELU1, 128, None)
+        g = N.LaGate(gk, tau, None, None)
+        return lib.la_decode_step(ctypes.byref(p), S, z, q, FAKE + 0x4000000, FAKE + 5 * SP, ctypes.byref(f),
+                                  ctypes.byref(g), out, None)
+    assert call(n=2) == N.LA_ERR_INVALID_ARG
+    assert call(S=None) == N.LA_ERR_INVALID_ARG
+    assert call(q=FAKE + 0x2000000 + 4) == N.LA_ERR_INVALID_ARG
+    assert call(d_v=96) == N.LA_ERR_UNSUPPORTED
+    assert call(gk=N.LA_GATE_GLA) == N.LA_ERR_INVALID_ARG  # no g pointer
+    assert call(gk=N.LA_GATE_GLA, tau=-1.0) == N.LA_ERR_INVALID_ARG
+    assert call(out=FAKE + 0x2000000) == N.LA_ERR_ALIAS   # out over q
+    assert call(z=FAKE + 0x100) == N.LA_ERR_ALIAS         # z inside S
+
+
+@needs_lib
+@no_gpu
+def test_feature_map_rejects():
+    lib = N.lib()
+    f = N.LaFeatureMap(N.LA_FMAP_ELU1, 64, None)
+    assert lib.la_feature_map_apply(ctypes.byref(f), 0, 64, N.LA_BF16, FAKE, FAKE + 0x100000, None) == N.LA_ERR_INVALID_ARG
+    assert lib.la_feature_map_apply(ctypes.byref(f), 10, 64, N.LA_BF16, FAKE, FAKE + 64, None) == N.LA_ERR_ALIAS
+    f2 = N.LaFeatureMap(N.LA_FMAP_ELU1, 48, None)
+    assert lib.la_feature_map_apply(ctypes.byref(f2), 10, 48, N.LA_BF16, FAKE, FAKE + 0x100000, None) == N.LA_ERR_UNSUPPORTED
