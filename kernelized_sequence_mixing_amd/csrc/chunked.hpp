@@ -163,68 +163,20 @@ struct RawChunk {
   }
 };
 
-// FAVOR+ features of one side of a chunk: P^T = omega X^T on the matrix cores
-// (wave w: features [w R/4, (w+1) R/4), all 64 tokens), then
-// phi = exp(P - |x|^2/2 - ln(r)/2). Queries go to the row-major tile at
-// row_off; keys go to the row-major tile (when ROWS) and, with the decay
-// weight of the state update, to the transposed tile at kt_off.
-template <int R, int DK, int GATE, bool IS_K, bool ROWS>
-__device__ __forceinline__ void favor_side(const bf16x8 (&x)[4 * (DK / 32)], const bf16x8 (*om)[DK / 32], int L,
-                                           float lg2gam, char* sm, int row_off, int kt_off, int lane, int w) {
-  constexpr int KS = DK / 32, MT = R / 64, RP = R + 8;
-  const int g4 = lane >> 4, c16 = lane & 15;
-  const float half_log_r = 0.5f * __logf(float(R));
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    float ss = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float xv = to_f32(x[tt * KS + ks][u]);
-        ss += xv * xv;
-      }
-    const float shift = 0.5f * sum_over_groups(ss) + half_log_r;
-    const int t = 16 * tt + c16;
-    const bool tok_ok = t < L;
-    float decay_k = 1.f;
-    if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(L - 1 - t) * lg2gam);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16(om[mt][ks], x[tt * KS + ks], acc);
-      // acc[i] = P[token t][feature m0 + i]
-      const int m0 = w * (R / 4) + 16 * mt + 4 * g4;
-      float f[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[i] = __expf(acc[i] - shift);
-        if (IS_K) f[i] = tok_ok ? f[i] : 0.f;
-      }
-      if constexpr (!IS_K || ROWS) lds<bf16x4>(sm, row_off + 2 * (t * RP + m0)) = pack4(f[0], f[1], f[2], f[3]);
-      if constexpr (IS_K) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lds<bf16>(sm, kt_off + 2 * ((m0 + i) * CP + t)) = (bf16)(f[i] * decay_k);
-      }
-    }
-  }
-}
-
-// Feature map, gate factors and transposes of one chunk into LDS.
+// elu+1 features, gate factors and transposes of one chunk into LDS.
 //   WITH_Q: pass 3 (writes q, k, kt, vt, gam); else pass 1 (kt, vt, gam, logg).
 // L = valid tokens in the chunk. Rows t >= L get phi(k) = 0 and v = 0, and a
 // zero log-gate, so they add nothing to the state.
 template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q>
-__device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q>& raw,
-                                              const bf16x8 (*om)[DK / 32], const CausalArgs& a,
+__device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q>& raw, const CausalArgs& a,
                                               int L, float lg2gam, char* sm, int q_off, int k_off,
                                               int kt_off, int vt_off, int gam_off, int logg_off,
                                               int lane, int w) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q>;
   constexpr int RP = R + 8;
   const bool valid = lane < L;
-  if constexpr (FMAP == FM_ELU1) {
+  static_assert(FMAP == FM_ELU1, "FAVOR+ chunks use the kernels of chunked_favor.hpp");
+  {
     const int t = lane;
     float decay_k = 1.f;
     if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(L - 1 - t) * lg2gam);
@@ -263,9 +215,6 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
 #pragma unroll
       for (int u = 0; u < 8; ++u) lds<bf16>(sm, kt_off + 2 * ((f0 + u) * CP + t)) = (bf16)vkh[u];
     }
-  } else {
-    if constexpr (WITH_Q) favor_side<R, DK, GATE, false, false>(raw.xq, om, L, lg2gam, sm, q_off, 0, lane, w);
-    favor_side<R, DK, GATE, true, WITH_Q>(raw.xk, om, L, lg2gam, sm, k_off, kt_off, lane, w);
   }
   // values, transposed
   {
@@ -328,19 +277,6 @@ __device__ __forceinline__ float z_update(float zr, char* sm, int kt_off, int ga
   return G * zr + acc;
 }
 
-template <int R, int DK, int FMAP>
-__device__ __forceinline__ void load_omega(bf16x8 (*om)[DK / 32], const bf16* omega, int lane, int w) {
-  if constexpr (FMAP == FM_FAVOR) {
-    const int g4 = lane >> 4, c16 = lane & 15;
-#pragma unroll
-    for (int mt = 0; mt < R / 64; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks)
-        om[mt][ks] = *reinterpret_cast<const bf16x8*>(omega + (long long)(w * (R / 4) + 16 * mt + c16) * DK +
-                                                      32 * ks + 8 * g4);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Pass 1: each segment's own state contribution (segments 0 .. P-2).
 // ---------------------------------------------------------------------------
@@ -367,15 +303,13 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
     for (int eb = 0; eb < E / 64; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float zr = 0.f;
   if (tid < R) lds<float>(sm, LY::logg_off + 4 * tid) = 0.f;
-  bf16x8 om[FMAP == FM_FAVOR ? R / 64 : 1][DK / 32];
-  load_omega<R, DK, FMAP>(om, a.omega, lane, w);
   lds_barrier();
 
   RawChunk<R, E, DK, FMAP, GATE, false> raw;
   raw.load(a, tok0, t_begin, lane, w);
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int L = min(kChunk, a.n - t0);
-    chunk_prelude<R, E, DK, FMAP, GATE, false>(raw, om, a, L, lg2gam, sm, 0, 0, LY::kt_off, LY::vt_off,
+    chunk_prelude<R, E, DK, FMAP, GATE, false>(raw, a, L, lg2gam, sm, 0, 0, LY::kt_off, LY::vt_off,
                                                LY::gam_off, LY::logg_off, lane, w);
     lds_barrier();
     if (t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
@@ -449,14 +383,12 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
                           pack4(S[2 * p + 1][eb][0], S[2 * p + 1][eb][1], S[2 * p + 1][eb][2], S[2 * p + 1][eb][3]));
   };
   rebuild_sop();
-  bf16x8 om[FMAP == FM_FAVOR ? R / 64 : 1][DK / 32];
-  load_omega<R, DK, FMAP>(om, a.omega, lane, w);
 
   RawChunk<R, E, DK, FMAP, GATE, true> raw;
   raw.load(a, tok0, t_begin, lane, w);
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int L = min(kChunk, a.n - t0);
-    chunk_prelude<R, E, DK, FMAP, GATE, true>(raw, om, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kt_off,
+    chunk_prelude<R, E, DK, FMAP, GATE, true>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kt_off,
                                               LY::vt_off, LY::gam_off, 0, lane, w);
     lds_barrier();
 

@@ -1,13 +1,14 @@
-// FAVOR+ instances of the chunkwise causal kernels (projection on the matrix cores).
-#include "chunked.hpp"
+// FAVOR+ instances of the chunkwise causal kernels (projection on the matrix cores,
+// hi/lo bf16 operand pairs).
+#include "chunked_favor.hpp"
 
 namespace la {
 
 template <int R, int E, int DK>
 static la_status by_gate(const FwdPlan& p) {
   switch (p.gate) {
-    case GT_NONE: return run_causal<R, E, DK, FM_FAVOR, GT_NONE>(p);
-    case GT_DECAY: return run_causal<R, E, DK, FM_FAVOR, GT_DECAY>(p);
+    case GT_NONE: return run_causal_favor<R, E, DK, GT_NONE>(p);
+    case GT_DECAY: return run_causal_favor<R, E, DK, GT_DECAY>(p);
   }
   return LA_ERR_UNSUPPORTED;
 }
