@@ -112,51 +112,35 @@ struct RawChunk {
   bf16x8 xk[!ELU ? 4 * KS : 1];
   bf16x8 v[EV / 8];
 
+  // Rows past the end of the sequence are read from the last valid row (always
+  // in bounds) and masked by the consumer, so no instruction here touches the
+  // loaded values and the loads stay in flight until the next chunk needs them.
   __device__ __forceinline__ void load(const CausalArgs& a, long long tok0, int t0, int lane, int w) {
-    const bf16x8 zero = {};
     const int g4 = lane >> 4, c16 = lane & 15;
     {
-      const int t = t0 + lane;
-      const bool ok = t < a.n;
-      const long long row = tok0 + (ok ? t : a.n - 1);
+      const long long row = tok0 + min(t0 + lane, a.n - 1);
       if constexpr (ELU) {
 #pragma unroll
         for (int j = 0; j < FR / 8; ++j) {
-          if constexpr (WITH_Q) {
-            bf16x8 x = *reinterpret_cast<const bf16x8*>(a.Q + row * R + w * FR + 8 * j);
-            q[j] = ok ? x : zero;
-          }
-          bf16x8 y = *reinterpret_cast<const bf16x8*>(a.K + row * R + w * FR + 8 * j);
-          k[j] = ok ? y : zero;
+          if constexpr (WITH_Q) q[j] = *reinterpret_cast<const bf16x8*>(a.Q + row * R + w * FR + 8 * j);
+          k[j] = *reinterpret_cast<const bf16x8*>(a.K + row * R + w * FR + 8 * j);
         }
       }
       if constexpr (GATE == GT_GLA) {
 #pragma unroll
-        for (int j = 0; j < FR / 8; ++j) {
-          bf16x8 x = *reinterpret_cast<const bf16x8*>(a.g + row * R + w * FR + 8 * j);
-          g[j] = ok ? x : zero;
-        }
+        for (int j = 0; j < FR / 8; ++j) g[j] = *reinterpret_cast<const bf16x8*>(a.g + row * R + w * FR + 8 * j);
       }
 #pragma unroll
-      for (int j = 0; j < EV / 8; ++j) {
-        bf16x8 x = *reinterpret_cast<const bf16x8*>(a.V + row * E + w * EV + 8 * j);
-        v[j] = ok ? x : zero;
-      }
+      for (int j = 0; j < EV / 8; ++j) v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * E + w * EV + 8 * j);
     }
     if constexpr (!ELU) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const int t = t0 + 16 * tt + c16;
-        const bool ok = t < a.n;
-        const long long row = tok0 + (ok ? t : a.n - 1);
+        const long long row = tok0 + min(t0 + 16 * tt + c16, a.n - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (WITH_Q) {
-            bf16x8 x = *reinterpret_cast<const bf16x8*>(a.Q + row * DK + 32 * ks + 8 * g4);
-            xq[tt * KS + ks] = ok ? x : zero;
-          }
-          bf16x8 y = *reinterpret_cast<const bf16x8*>(a.K + row * DK + 32 * ks + 8 * g4);
-          xk[tt * KS + ks] = ok ? y : zero;
+          if constexpr (WITH_Q) xq[tt * KS + ks] = *reinterpret_cast<const bf16x8*>(a.Q + row * DK + 32 * ks + 8 * g4);
+          xk[tt * KS + ks] = *reinterpret_cast<const bf16x8*>(a.K + row * DK + 32 * ks + 8 * g4);
         }
       }
     }
@@ -216,13 +200,15 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       for (int u = 0; u < 8; ++u) lds<bf16>(sm, kt_off + 2 * ((f0 + u) * CP + t)) = (bf16)vkh[u];
     }
   }
-  // values, transposed
+  // values, transposed (rows past the end are zero)
   {
     constexpr int EV = Raw::EV;
+    const bf16 zero = (bf16)0.f;
 #pragma unroll
     for (int j = 0; j < EV / 8; ++j)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = raw.v[j][u];
+      for (int u = 0; u < 8; ++u)
+        lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = valid ? raw.v[j][u] : zero;
   }
 }
 

@@ -152,13 +152,17 @@ __device__ __forceinline__ void favor_block_side(const bf16x8 (&x)[4 * (DK / 32)
   }
 }
 
+// V transposed into LDS; rows at or past L (the chunk's valid tokens) are zero.
 template <int E>
-__device__ __forceinline__ void write_vt(const bf16x8 (&v)[E / 32], char* sm, int vt_off, int lane, int w) {
+__device__ __forceinline__ void write_vt(const bf16x8 (&v)[E / 32], int L, char* sm, int vt_off, int lane, int w) {
   constexpr int EV = E / 4;
+  const bool valid = lane < L;
+  const bf16 zero = (bf16)0.f;
 #pragma unroll
   for (int j = 0; j < EV / 8; ++j)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = v[j][u];
+    for (int u = 0; u < 8; ++u)
+      lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = valid ? v[j][u] : zero;
 }
 
 // S rows of feature block fb (all of them, wave's value columns) <- g S + K^^T V
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
     for (int fb = 0; fb < F::NFB; ++fb) {
       favor_block_side<R, DK, GATE, true, false>(raw.xk, a.omega, fb, L, lg2gam, sm, 0, 0, LY::kth_off, LY::ktl_off,
                                                  lane, w);
-      if (fb == 0) write_vt<E>(raw.v, sm, LY::vt_off, lane, w);
+      if (fb == 0) write_vt<E>(raw.v, L, sm, LY::vt_off, lane, w);
       lds_barrier();
       if (fb == F::NFB - 1 && t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
       favor_state_block<R, E>(S, fb, sm, LY::kth_off, LY::ktl_off, LY::vt_off, gsc, lane, w);
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
                                                   lane, w);
       favor_block_side<R, DK, GATE, true, true>(raw.xk, a.omega, fb, L, lg2gam, sm, LY::kh_off, LY::kl_off,
                                                 LY::kth_off, LY::ktl_off, lane, w);
-      if (fb == 0) write_vt<E>(raw.v, sm, LY::vt_off, lane, w);
+      if (fb == 0) write_vt<E>(raw.v, L, sm, LY::vt_off, lane, w);
       lds_barrier();
 
       // ---- scores over this block's features: A^T tiles = K~_c Q~_w^T

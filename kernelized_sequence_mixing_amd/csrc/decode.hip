@@ -28,7 +28,7 @@ struct DecodeArgs {
   float eps, inv_tau;
 };
 
-template <int R, int E, int DK, int FMAP>
+template <int R, int E, int DK, int FMAP, typename InT>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   constexpr int CG = E / 4;          // float4 column quads per row
   constexpr int RPP = 256 / CG;      // rows per pass
@@ -41,19 +41,31 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const long long bh = blockIdx.x;
   const int col4 = tid % CG, r0 = tid / CG;
-  float4* Sh = reinterpret_cast<float4*>(a.S + bh * R * E);
+  const InT* q = static_cast<const InT*>(a.q);
+  const InT* k = static_cast<const InT*>(a.k);
+  const InT* v = static_cast<const InT*>(a.v);
 
-  // the whole state slice in flight first
+  // Small per-head inputs first, then the state stream, all issued back to
+  // back from one basic block (clamped indices, no branches): the prologue
+  // below then waits only for the small loads while the whole state slice is
+  // in flight.
+  const bool gla = a.gate == LA_GATE_GLA;
+  const int iq = min(tid, DK - 1), iv = min(tid, E - 1), ir = min(tid, R - 1);
+  const InT* gp = gla ? static_cast<const InT*>(a.g) + bh * R + ir : q + bh * DK + iq;
+  const InT rq = q[bh * DK + iq], rk = k[bh * DK + iq], rv = v[bh * E + iv], rg = *gp;
+  const float rz = a.z[bh * R + ir];
+  float4* Sh = reinterpret_cast<float4*>(a.S + bh * R * E);
   float4 st[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) st[p] = Sh[(r0 + RPP * p) * CG + col4];
+  const float xq = to_f32(rq), xk = to_f32(rk), xv = to_f32(rv), xg = gla ? to_f32(rg) : 0.f, xz = rz;
 
   // features and gate of this token
-  for (int d = tid; d < DK; d += 256) {
-    sxq[d] = ld_elem(a.q, bh * DK + d, a.in_dt);
-    sxk[d] = ld_elem(a.k, bh * DK + d, a.in_dt);
-  }
-  for (int e = tid; e < E; e += 256) sv[e] = ld_elem(a.v, bh * E + e, a.in_dt);
+  // unconditional (clamped) writes keep the loads above out of branches;
+  // threads past the end rewrite the last element with the same value
+  sxq[iq] = xq;
+  sxk[iq] = xk;
+  sv[iv] = xv;
   __syncthreads();
   if constexpr (FMAP == 1) {
     if (tid < 2) {
@@ -68,12 +80,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   if (tid < R) {
     float pq, pk;
     if constexpr (FMAP == 0) {
-      pq = elu1(sxq[tid]);
-      pk = elu1(sxk[tid]);
+      pq = elu1(xq);
+      pk = elu1(xk);
     } else {
       float aq = 0.f, ak = 0.f;
+      const InT* om = static_cast<const InT*>(a.omega) + (long long)tid * DK;
       for (int d = 0; d < DK; ++d) {
-        const float w = ld_elem(a.omega, (long long)tid * DK + d, a.in_dt);
+        const float w = to_f32(om[d]);
         aq += w * sxq[d];
         ak += w * sxk[d];
       }
@@ -83,11 +96,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     }
     float al = 1.f;
     if (a.gate == LA_GATE_DECAY) al = a.gamma[bh % a.H];
-    if (a.gate == LA_GATE_GLA) al = __expf(gla_log_alpha(ld_elem(a.g, bh * R + tid, a.in_dt), a.inv_tau));
+    if (a.gate == LA_GATE_GLA) al = __expf(gla_log_alpha(xg, a.inv_tau));
     spq[tid] = pq;
     spk[tid] = pk;
     sal[tid] = al;
-    const float zn = al * a.z[bh * R + tid] + pk;
+    const float zn = al * xz + pk;
     a.z[bh * R + tid] = zn;
     zdot = pq * zn;
   }
@@ -138,8 +151,12 @@ template <int R, int E, int DK, int FMAP>
 static la_status run_decode(const DecodePlan& p) {
   DecodeArgs a{p.S, p.z, p.q, p.k, p.v, p.g, p.omega, p.gamma, p.out, p.H, p.in_dtype, p.out_dtype, p.gate,
                p.eps, p.gate == LA_GATE_GLA ? 1.f / p.tau : 0.f};
-  hipLaunchKernelGGL((decode_step_kernel<R, E, DK, FMAP>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256), 0,
-                     p.stream, a);
+  if (p.in_dtype == LA_BF16)
+    hipLaunchKernelGGL((decode_step_kernel<R, E, DK, FMAP, bf16>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256), 0,
+                       p.stream, a);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<R, E, DK, FMAP, float>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256),
+                       0, p.stream, a);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 

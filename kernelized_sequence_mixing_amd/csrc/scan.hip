@@ -26,13 +26,25 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S
   if (S0 != nullptr) cur = is_z ? z0[bh * R + row] : S0[bh * RE + idx];
   float seg_decay = 1.f;
   if (gate == GT_DECAY) seg_decay = exp2f(float(seg_len) * log2f(gamma[bh % H]));
-  for (int s = 0; s < P; ++s) {
-    const float d = base[s * stride];
-    base[s * stride] = cur;
-    if (s + 1 < P) {
-      float G = seg_decay;
-      if (gate == GT_GLA) G = __expf(logG[(bh * P + s) * R + row]);
-      cur = G * cur + d;
+  // Batches of 8 segments: all loads of a batch are issued before the chain
+  // that consumes them, so their latencies overlap.
+  constexpr int BATCH = 8;
+  for (int s0 = 0; s0 < P; s0 += BATCH) {
+    float d[BATCH], G[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int s = min(s0 + j, P - 1);
+      d[j] = base[s * stride];
+      G[j] = gate == GT_GLA ? logG[(bh * P + s) * R + row] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int s = s0 + j;
+      if (s < P) {
+        base[s * stride] = cur;
+        const float g = gate == GT_GLA ? __expf(G[j]) : seg_decay;
+        cur = g * cur + d[j];
+      }
     }
   }
 }
