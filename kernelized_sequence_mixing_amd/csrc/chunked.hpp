@@ -99,12 +99,21 @@ __device__ __forceinline__ T& lds(char* base, int byte_off) {
 
 // Raw inputs of one chunk, held in registers from the global load to the LDS
 // write so the next chunk's loads overlap the current chunk's math.
+//
+// Two register layouts of a chunk:
+//  * row-major (elu+1 without the GLA gate): wave w holds tokens [16w, 16w+16),
+//    four lanes per token; lane l holds 8-feature blocks (l % 4) + 4 j of token
+//    16 w + l / 4, so each load instruction reads 16 rows, 64 contiguous bytes
+//    of each, and every row is consumed whole by two instructions;
+//  * lane-per-token (GLA gate, whose scan runs across the 64 lanes): lane l
+//    holds token l, wave w holds features [w R/4, (w+1) R/4).
 template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q>
 struct RawChunk {
   static constexpr int FR = R / 4;       // features per wave (elu+1 lane-per-token layout)
   static constexpr int EV = E / 4;       // value columns per wave
   static constexpr int KS = DK / 32;     // projection k-steps (FAVOR)
   static constexpr bool ELU = FMAP == FM_ELU1;
+  static constexpr bool ROWMAJOR = ELU && GATE != GT_GLA;
   bf16x8 q[ELU && WITH_Q ? FR / 8 : 1];
   bf16x8 k[ELU ? FR / 8 : 1];
   bf16x8 g[GATE == GT_GLA ? FR / 8 : 1];
@@ -117,6 +126,19 @@ struct RawChunk {
   // loaded values and the loads stay in flight until the next chunk needs them.
   __device__ __forceinline__ void load(const CausalArgs& a, long long tok0, int t0, int lane, int w) {
     const int g4 = lane >> 4, c16 = lane & 15;
+    if constexpr (ROWMAJOR) {
+      const long long row = tok0 + min(t0 + 16 * w + (lane >> 2), a.n - 1);
+#pragma unroll
+      for (int j = 0; j < R / 32; ++j) {
+        const int f0 = 8 * ((lane & 3) + 4 * j);
+        if constexpr (WITH_Q) q[j] = *reinterpret_cast<const bf16x8*>(a.Q + row * R + f0);
+        k[j] = *reinterpret_cast<const bf16x8*>(a.K + row * R + f0);
+      }
+#pragma unroll
+      for (int j = 0; j < E / 32; ++j)
+        v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * E + 8 * ((lane & 3) + 4 * j));
+      return;
+    }
     {
       const long long row = tok0 + min(t0 + lane, a.n - 1);
       if constexpr (ELU) {
@@ -158,12 +180,48 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
                                               int lane, int w) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q>;
   constexpr int RP = R + 8;
-  const bool valid = lane < L;
   static_assert(FMAP == FM_ELU1, "FAVOR+ chunks use the kernels of chunked_favor.hpp");
+  if constexpr (Raw::ROWMAJOR) {
+    const int t = 16 * w + (lane >> 2);
+    const bool valid = t < L;
+    float decay_k = 1.f;
+    if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(L - 1 - t) * lg2gam);
+#pragma unroll
+    for (int j = 0; j < R / 32; ++j) {
+      const int f0 = 8 * ((lane & 3) + 4 * j);
+      float vq[8], vk[8], vkh[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        vq[u] = WITH_Q ? elu1(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
+        vk[u] = keep_if(valid, elu1(to_f32(raw.k[j][u])));
+        vkh[u] = vk[u] * decay_k;
+      }
+      if constexpr (WITH_Q) {
+        lds<bf16x8>(sm, q_off + 2 * (t * RP + f0)) =
+            cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
+        lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) =
+            cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7]));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lds<bf16>(sm, kt_off + 2 * ((f0 + u) * CP + t)) = (bf16)vkh[u];
+    }
+#pragma unroll
+    for (int j = 0; j < E / 32; ++j) {
+      const int e0 = 8 * ((lane & 3) + 4 * j);
+      const bf16x8 vv = keep_if(valid, raw.v[j]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lds<bf16>(sm, vt_off + 2 * ((e0 + u) * CP + t)) = vv[u];
+    }
+    return;
+  }
+  const bool valid = lane < L;
   {
     const int t = lane;
     float decay_k = 1.f;
     if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(L - 1 - t) * lg2gam);
+    // GLA: lane f (< FR) collects the chunk's summed log-gate of this wave's
+    // feature f; one store per lane after the feature loop.
+    float my_bend = 0.f;
 #pragma unroll
     for (int j = 0; j < Raw::FR / 8; ++j) {
       const int f0 = w * Raw::FR + 8 * j;
@@ -171,20 +229,18 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         float pq = WITH_Q ? elu1(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
-        float pk = valid ? elu1(to_f32(raw.k[j][u])) : 0.f;
+        float pk = keep_if(valid, elu1(to_f32(raw.k[j][u])));
         float kh = pk;
         if constexpr (GATE == GT_DECAY) kh = pk * decay_k;
         if constexpr (GATE == GT_GLA) {
-          float la = valid ? gla_log_alpha(to_f32(raw.g[j][u]), a.inv_tau) : 0.f;
+          float la = keep_if(valid, gla_log_alpha(to_f32(raw.g[j][u]), a.inv_tau));
           float b = wave_inclusive_scan(la);
-          float bend = __shfl(b, 63);
+          // the chunk total is uniform across the wave: a scalar read of lane 63
+          const float bend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
           pq *= __expf(b);
           kh = pk * __expf(bend - b);
           pk *= __expf(-b);
-          if (lane == 0) {
-            lds<float>(sm, gam_off + 4 * (f0 + u)) = __expf(bend);
-            if constexpr (!WITH_Q) lds<float>(sm, logg_off + 4 * (f0 + u)) += bend;
-          }
+          my_bend = lane == 8 * j + u ? bend : my_bend;
         }
         vq[u] = pq;
         vk[u] = pk;
@@ -199,25 +255,46 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
 #pragma unroll
       for (int u = 0; u < 8; ++u) lds<bf16>(sm, kt_off + 2 * ((f0 + u) * CP + t)) = (bf16)vkh[u];
     }
+    if constexpr (GATE == GT_GLA) {
+      if (lane < Raw::FR) {
+        lds<float>(sm, gam_off + 4 * (w * Raw::FR + lane)) = __expf(my_bend);
+        if constexpr (!WITH_Q) lds<float>(sm, logg_off + 4 * (w * Raw::FR + lane)) += my_bend;
+      }
+    }
   }
   // values, transposed (rows past the end are zero)
   {
     constexpr int EV = Raw::EV;
-    const bf16 zero = (bf16)0.f;
 #pragma unroll
-    for (int j = 0; j < EV / 8; ++j)
+    for (int j = 0; j < EV / 8; ++j) {
+      const bf16x8 vv = keep_if(valid, raw.v[j]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = valid ? raw.v[j][u] : zero;
+      for (int u = 0; u < 8; ++u) lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = vv[u];
+    }
   }
 }
 
-// S (wave slab: rows all R, value columns [w E/4, (w+1) E/4)) <- Gamma S + K^^T V.
+// z is carried on the matrix cores as the state column of a constant-1 value:
+// z <- Gamma z + K^^T 1. Wave w owns the z tiles rt = w ZT .. w ZT + ZT - 1
+// (16 rows each); lane (g, c) holds z[16 rt + 4 g + i] in Z[rt - w ZT][i]
+// (the same in every column lane c).
+template <int R>
+struct ZTiles {
+  static constexpr int ZT = R >= 64 ? R / 64 : 1;   // tiles per owning wave
+  static constexpr int OWNERS = R / (16 * ZT);      // waves that own z tiles
+};
+
+// S (wave slab: rows all R, value columns [w E/4, (w+1) E/4)) <- Gamma S + K^^T V,
+// and this wave's z tiles <- Gamma z + K^^T 1.
 template <int R, int E, int GATE>
-__device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], char* sm, int kt_off,
-                                             int vt_off, int gam_off, float gscale, int lane, int w) {
+__device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (&Z)[ZTiles<R>::ZT], char* sm,
+                                             int kt_off, int vt_off, int gam_off, float gscale, int lane, int w) {
+  constexpr int ZT = ZTiles<R>::ZT;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int ebase = w * (E / 4);
+  bf16x8 ones;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ones[u] = (bf16)1.f;
   bf16x8 vb[E / 64][2];
 #pragma unroll
   for (int eb = 0; eb < E / 64; ++eb)
@@ -245,22 +322,39 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], char* s
       for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vb[eb][ks], st);
       S[rt][eb] = st;
     }
+    if (rt / ZT == w) {
+      f32x4 zt = Z[rt % ZT];
+      if constexpr (GATE != GT_NONE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) zt = mfma16(ka[ks], ones, zt);
+      Z[rt % ZT] = zt;
+    }
   }
 }
 
-// z[row] <- Gamma z[row] + sum_t K^[t][row]   (thread `row` < R owns z[row])
-template <int R, int GATE>
-__device__ __forceinline__ float z_update(float zr, char* sm, int kt_off, int gam_off, float gscale, int row) {
-  float acc = 0.f;
+// z tiles of wave w to / from a flat [R] fp32 array (lanes with c == 0 write).
+template <int R>
+__device__ __forceinline__ void z_store(const f32x4 (&Z)[ZTiles<R>::ZT], float* dst, int lane, int w) {
+  constexpr int ZT = ZTiles<R>::ZT;
+  if (w < ZTiles<R>::OWNERS && (lane & 15) == 0) {
 #pragma unroll
-  for (int j = 0; j < kChunk / 8; ++j) {
-    bf16x8 x = lds<bf16x8>(sm, kt_off + 2 * (row * CP + 8 * j));
+    for (int j = 0; j < ZT; ++j)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += to_f32(x[u]);
+      for (int i = 0; i < 4; ++i) dst[16 * (w * ZT + j) + 4 * (lane >> 4) + i] = Z[j][i];
   }
-  float G = gscale;
-  if constexpr (GATE == GT_GLA) G = lds<float>(sm, gam_off + 4 * row);
-  return G * zr + acc;
+}
+
+template <int R>
+__device__ __forceinline__ void z_load(f32x4 (&Z)[ZTiles<R>::ZT], const float* src, int lane, int w) {
+  constexpr int ZT = ZTiles<R>::ZT;
+#pragma unroll
+  for (int j = 0; j < ZT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      Z[j][i] = (src != nullptr && w < ZTiles<R>::OWNERS) ? src[16 * (w * ZT + j) + 4 * (lane >> 4) + i] : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -287,22 +381,30 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
   for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
     for (int eb = 0; eb < E / 64; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float zr = 0.f;
+  f32x4 Z[ZTiles<R>::ZT];
+  z_load<R>(Z, nullptr, lane, w);
   if (tid < R) lds<float>(sm, LY::logg_off + 4 * tid) = 0.f;
   lds_barrier();
 
-  RawChunk<R, E, DK, FMAP, GATE, false> raw;
-  raw.load(a, tok0, t_begin, lane, w);
-  for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
+  // Two chunks of loads in flight: buffer b holds chunk (2 i + b); after its
+  // prelude consumes it, it is refilled with the chunk two ahead.
+  using Raw = RawChunk<R, E, DK, FMAP, GATE, false>;
+  Raw raw0, raw1;
+  raw0.load(a, tok0, t_begin, lane, w);
+  if (t_begin + kChunk < t_end) raw1.load(a, tok0, t_begin + kChunk, lane, w);
+  auto chunk = [&](Raw& raw, int t0) {
     const int L = min(kChunk, a.n - t0);
     chunk_prelude<R, E, DK, FMAP, GATE, false>(raw, a, L, lg2gam, sm, 0, 0, LY::kt_off, LY::vt_off,
                                                LY::gam_off, LY::logg_off, lane, w);
+    if (t0 + 2 * kChunk < t_end) raw.load(a, tok0, t0 + 2 * kChunk, lane, w);
     lds_barrier();
-    if (t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE>(S, sm, LY::kt_off, LY::vt_off, LY::gam_off, gsc, lane, w);
-    if (tid < R) zr = z_update<R, GATE>(zr, sm, LY::kt_off, LY::gam_off, gsc, tid);
+    state_update<R, E, GATE>(S, Z, sm, LY::kt_off, LY::vt_off, LY::gam_off, gsc, lane, w);
     lds_barrier();
+  };
+  for (int t0 = t_begin; t0 < t_end; t0 += 2 * kChunk) {
+    chunk(raw0, t0);
+    if (t0 + kChunk < t_end) chunk(raw1, t0 + kChunk);
   }
   const long long slot = bh * a.P + s;
   float* So = a.S_out + slot * R * E;
@@ -312,9 +414,9 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
     for (int eb = 0; eb < E / 64; ++eb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
-  if (tid < R) {
-    a.z_out[slot * R + tid] = zr;
-    if constexpr (GATE == GT_GLA) a.logG_out[slot * R + tid] = lds<float>(sm, LY::logg_off + 4 * tid);
+  z_store<R>(Z, a.z_out + slot * R, lane, w);
+  if constexpr (GATE == GT_GLA) {
+    if (tid < R) a.logG_out[slot * R + tid] = lds<float>(sm, LY::logg_off + 4 * tid);
   }
 }
 
@@ -340,7 +442,7 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
 
   // ---- state carried in
   f32x4 S[R / 16][NEB];
-  float zr = 0.f;
+  f32x4 Z[ZTiles<R>::ZT];
   if (a.S_in != nullptr) {
     const float* Sp = a.S_in + bh * a.in_head + s * a.in_seg;
 #pragma unroll
@@ -349,14 +451,14 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[rt][eb][i] = Sp[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16];
-    if (tid < R) zr = a.z_in[(bh * a.in_head + s * a.in_seg) / E + tid];
   } else {
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (tid < R) lds<float>(sm, LY::z_off + 4 * tid) = zr;
+  z_load<R>(Z, a.S_in != nullptr ? a.z_in + (bh * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
+  z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
   // bf16 image of the state as the A operand of O^T += S^T Q^^T: k-slot j of
   // lane (g, c) is feature 32p + 4g + j (j < 4) or 32p + 16 + 4g + (j - 4).
   bf16x8 Sop[KP][NEB];
@@ -376,6 +478,8 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
     const int L = min(kChunk, a.n - t0);
     chunk_prelude<R, E, DK, FMAP, GATE, true>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kt_off,
                                               LY::vt_off, LY::gam_off, 0, lane, w);
+    // the raw registers are free again: the next chunk's loads fly during this one
+    if (t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
     lds_barrier();
 
     // ---- scores for query rows [16w, 16w+16): A^T tiles = K~_c Q~_w^T
@@ -385,6 +489,11 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
       for (int ks = 0; ks < KP; ++ks) qop[ks] = lds<bf16x8>(sm, LY::q_off + 2 * ((16 * w + c16) * RP + 32 * ks + 8 * g4));
       const int q = 16 * w + c16;
       float rs = 0.f;
+      float ginv[4] = {1.f, 1.f, 1.f, 1.f};  // gamma^(-i), i = 0..3
+      if constexpr (GATE == GT_DECAY) {
+#pragma unroll
+        for (int i = 1; i < 4; ++i) ginv[i] = exp2f(-float(i) * lg2gam);
+      }
       for (int c = 0; c <= w; ++c) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -392,12 +501,14 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
           acc = mfma16(lds<bf16x8>(sm, LY::k_off + 2 * ((16 * c + c16) * RP + 32 * ks + 8 * g4)), qop[ks], acc);
         // acc[i] = A[q][key], key = 16c + 4g + i
         bf16x4 ab;
+        float gbase = 1.f;
+        if constexpr (GATE == GT_DECAY) gbase = exp2f(float(q - 16 * c - 4 * g4) * lg2gam);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = 16 * c + 4 * g4 + i;
           float v = acc[i];
-          if (key > q) v = 0.f;
-          if constexpr (GATE == GT_DECAY) v *= exp2f(float(q - key) * lg2gam);
+          if (c == w && key > q) v = 0.f;  // only the diagonal tile straddles the mask
+          if constexpr (GATE == GT_DECAY) v *= gbase * ginv[i];
           ab[i] = (bf16)v;
           rs += to_f32(ab[i]);
         }
@@ -415,7 +526,6 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
       if (g4 == 0) lds<float>(sm, LY::den_off + 4 * q) = rs + zd + a.eps;
     }
     lds_barrier();
-    if (t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
 
     // ---- outputs for value columns [w E/4, (w+1) E/4): O^T = S^T Q^^T + V^T A^T
 #pragma unroll
@@ -426,7 +536,8 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
       for (int p = 0; p < KP; ++p)
         qb[p] = cat8(lds<bf16x4>(sm, LY::q_off + 2 * (q * RP + 32 * p + 4 * g4)),
                      lds<bf16x4>(sm, LY::q_off + 2 * (q * RP + 32 * p + 16 + 4 * g4)));
-      const float den = lds<float>(sm, LY::den_off + 4 * q);
+      // one correctly rounded reciprocal per row; outputs are fl(O * fl(1 / den))
+      const float inv_den = 1.f / lds<float>(sm, LY::den_off + 4 * q);
       float isc = 1.f;
       if constexpr (GATE == GT_DECAY) isc = exp2f(float(q + 1) * lg2gam);
 #pragma unroll
@@ -444,7 +555,7 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
           acc = mfma16(lds<bf16x8>(sm, LY::vt_off + 2 * ((e + c16) * CP + 32 * p2 + 8 * g4)),
                        lds<bf16x8>(sm, LY::a_off + 2 * (q * CP + 32 * p2 + 8 * g4)), acc);
         if (q < L) {
-          bf16x4 o = pack4(acc[0] / den, acc[1] / den, acc[2] / den, acc[3] / den);
+          bf16x4 o = pack4(acc[0] * inv_den, acc[1] * inv_den, acc[2] * inv_den, acc[3] * inv_den);
           *reinterpret_cast<bf16x4*>(a.out + (tok0 + t0 + q) * E + e + 4 * g4) = o;
         }
       }
@@ -452,12 +563,9 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
 
     // ---- carry the state past this chunk
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE>(S, sm, LY::kt_off, LY::vt_off, LY::gam_off, gsc, lane, w);
+    state_update<R, E, GATE>(S, Z, sm, LY::kt_off, LY::vt_off, LY::gam_off, gsc, lane, w);
     rebuild_sop();
-    if (tid < R) {
-      zr = z_update<R, GATE>(zr, sm, LY::kt_off, LY::gam_off, gsc, tid);
-      lds<float>(sm, LY::z_off + 4 * tid) = zr;
-    }
+    z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
     lds_barrier();
   }
 
@@ -469,7 +577,7 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
-    if (tid < R) a.z_out[bh * R + tid] = zr;
+    z_store<R>(Z, a.z_out + bh * R, lane, w);
   }
 }
 

@@ -34,6 +34,37 @@ static la_status by_dv(const FwdPlan& p) {
   return LA_ERR_UNSUPPORTED;
 }
 
+template <int R>
+static int favor_lds(int dv) {
+  if (dv == 64) return FavorFwdLayout<R, 64>::bytes;
+  if (dv == 128 && R * 128 <= 16384) return FavorFwdLayout<R, 128>::bytes;
+  return 0;
+}
+
+template <int R>
+static int elu_lds(int dv) {
+  if (dv == 64) return FwdLayout<R, 64>::bytes;
+  if (dv == 128) return FwdLayout<R, 128>::bytes;
+  return 0;
+}
+
+int causal_output_lds_bytes(int fmap, int r, int dv) {
+  if (fmap == LA_FMAP_FAVOR) {
+    switch (r) {
+      case 64: return favor_lds<64>(dv);
+      case 128: return favor_lds<128>(dv);
+      case 256: return favor_lds<256>(dv);
+    }
+    return 0;
+  }
+  switch (r) {
+    case 32: return elu_lds<32>(dv);
+    case 64: return elu_lds<64>(dv);
+    case 128: return elu_lds<128>(dv);
+  }
+  return 0;
+}
+
 la_status launch_causal_favor(const FwdPlan& p) {
   switch (p.r) {
     case 64: return by_dv<64>(p);

@@ -131,7 +131,7 @@ __device__ __forceinline__ void favor_block_side(const bf16x8 (&x)[4 * (DK / 32)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f[i] = __expf(acc[i] - shift);
-        if (IS_K) f[i] = tok_ok ? f[i] : 0.f;
+        if (IS_K) f[i] = keep_if(tok_ok, f[i]);
       }
       if constexpr (!IS_K || ROWS) {
         bf16x4 h, l;
@@ -157,22 +157,29 @@ template <int E>
 __device__ __forceinline__ void write_vt(const bf16x8 (&v)[E / 32], int L, char* sm, int vt_off, int lane, int w) {
   constexpr int EV = E / 4;
   const bool valid = lane < L;
-  const bf16 zero = (bf16)0.f;
 #pragma unroll
-  for (int j = 0; j < EV / 8; ++j)
+  for (int j = 0; j < EV / 8; ++j) {
+    const bf16x8 vv = keep_if(valid, v[j]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = valid ? v[j][u] : zero;
+    for (int u = 0; u < 8; ++u) lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = vv[u];
+  }
 }
 
 // S rows of feature block fb (all of them, wave's value columns) <- g S + K^^T V
-// with K^ as a hi/lo pair.
+// with K^ as a hi/lo pair, and this wave's z tiles of the block <- g z + K^^T 1
+// (z is the state column of a constant-1 value). Wave w owns block-local z
+// tiles rt = w ZT .. w ZT + ZT - 1; lane (g, c) holds z[16 rt + 4 g + i].
 template <int R, int E>
-__device__ __forceinline__ void favor_state_block(f32x4 (&S)[R / 16][E / 64], int fb, char* sm, int kth_off,
-                                                  int ktl_off, int vt_off, float gscale, int lane, int w) {
+__device__ __forceinline__ void favor_state_block(f32x4 (&S)[R / 16][E / 64], f32x4 (&Zb)[FavorBlock<R>::FB / 64],
+                                                  int fb, char* sm, int kth_off, int ktl_off, int vt_off,
+                                                  float gscale, int lane, int w) {
   using F = FavorBlock<R>;
+  constexpr int ZT = F::FB / 64;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int ebase = w * (E / 4);
+  bf16x8 ones;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ones[u] = (bf16)1.f;
   bf16x8 vb[E / 64][2];
 #pragma unroll
   for (int eb = 0; eb < E / 64; ++eb)
@@ -199,20 +206,48 @@ __device__ __forceinline__ void favor_state_block(f32x4 (&S)[R / 16][E / 64], in
       }
       S[fb * (F::FB / 16) + rt][eb] = st;
     }
+    if (rt / ZT == w) {
+      f32x4 zt = Zb[rt % ZT];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zt[i] *= gscale;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        zt = mfma16(kh[ks], ones, zt);
+        zt = mfma16(kl[ks], ones, zt);
+      }
+      Zb[rt % ZT] = zt;
+    }
   }
 }
 
-// sum_t K^[t][row] over the chunk, from the hi/lo transposed tiles.
-__device__ __forceinline__ float favor_key_colsum(char* sm, int kth_off, int ktl_off, int row) {
-  float acc = 0.f;
+// z tiles (all blocks) of wave w to / from a flat [R] fp32 array.
+template <int R>
+__device__ __forceinline__ void favor_z_store(const f32x4 (&Z)[FavorBlock<R>::NFB][FavorBlock<R>::FB / 64],
+                                              float* dst, int lane, int w) {
+  using F = FavorBlock<R>;
+  constexpr int ZT = F::FB / 64;
+  if ((lane & 15) == 0) {
 #pragma unroll
-  for (int j = 0; j < kChunk / 8; ++j) {
-    const bf16x8 h = lds<bf16x8>(sm, kth_off + 2 * (row * CP + 8 * j));
-    const bf16x8 l = lds<bf16x8>(sm, ktl_off + 2 * (row * CP + 8 * j));
+    for (int fb = 0; fb < F::NFB; ++fb)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += to_f32(h[u]) + to_f32(l[u]);
+      for (int j = 0; j < ZT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[fb * F::FB + 16 * (w * ZT + j) + 4 * (lane >> 4) + i] = Z[fb][j][i];
   }
-  return acc;
+}
+
+template <int R>
+__device__ __forceinline__ void favor_z_load(f32x4 (&Z)[FavorBlock<R>::NFB][FavorBlock<R>::FB / 64],
+                                             const float* src, int lane, int w) {
+  using F = FavorBlock<R>;
+  constexpr int ZT = F::FB / 64;
+#pragma unroll
+  for (int fb = 0; fb < F::NFB; ++fb)
+#pragma unroll
+    for (int j = 0; j < ZT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Z[fb][j][i] = src != nullptr ? src[fb * F::FB + 16 * (w * ZT + j) + 4 * (lane >> 4) + i] : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -240,9 +275,8 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
     for (int eb = 0; eb < E / 64; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float zr[F::NFB];
-#pragma unroll
-  for (int fb = 0; fb < F::NFB; ++fb) zr[fb] = 0.f;
+  f32x4 Z[F::NFB][F::FB / 64];
+  favor_z_load<R>(Z, nullptr, lane, w);
 
   RawChunk<R, E, DK, FM_FAVOR, GT_NONE, false> raw;
   raw.load(a, tok0, t_begin, lane, w);
@@ -254,10 +288,9 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
       favor_block_side<R, DK, GATE, true, false>(raw.xk, a.omega, fb, L, lg2gam, sm, 0, 0, LY::kth_off, LY::ktl_off,
                                                  lane, w);
       if (fb == 0) write_vt<E>(raw.v, L, sm, LY::vt_off, lane, w);
-      lds_barrier();
       if (fb == F::NFB - 1 && t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
-      favor_state_block<R, E>(S, fb, sm, LY::kth_off, LY::ktl_off, LY::vt_off, gsc, lane, w);
-      if (tid < F::FB) zr[fb] = gsc * zr[fb] + favor_key_colsum(sm, LY::kth_off, LY::ktl_off, tid);
+      lds_barrier();
+      favor_state_block<R, E>(S, Z[fb], fb, sm, LY::kth_off, LY::ktl_off, LY::vt_off, gsc, lane, w);
       lds_barrier();
     }
   }
@@ -269,10 +302,7 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
     for (int eb = 0; eb < E / 64; ++eb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
-  if (tid < F::FB) {
-#pragma unroll
-    for (int fb = 0; fb < F::NFB; ++fb) a.z_out[slot * R + fb * F::FB + tid] = zr[fb];
-  }
+  favor_z_store<R>(Z, a.z_out + slot * R, lane, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -297,7 +327,7 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
   if constexpr (GATE == GT_DECAY) lg2gam = log2f(a.gamma[h]);
 
   f32x4 S[R / 16][NEB];
-  float zr[F::NFB];
+  f32x4 Z[F::NFB][F::FB / 64];
   if (a.S_in != nullptr) {
     const float* Sp = a.S_in + bh * a.in_head + s * a.in_seg;
 #pragma unroll
@@ -312,12 +342,8 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-#pragma unroll
-  for (int fb = 0; fb < F::NFB; ++fb) {
-    zr[fb] = 0.f;
-    if (a.S_in != nullptr && tid < F::FB) zr[fb] = a.z_in[(bh * a.in_head + s * a.in_seg) / E + fb * F::FB + tid];
-    if (tid < F::FB) lds<float>(sm, LY::z_off + 4 * (fb * F::FB + tid)) = zr[fb];
-  }
+  favor_z_load<R>(Z, a.S_in != nullptr ? a.z_in + (bh * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
+  favor_z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
 
   RawChunk<R, E, DK, FM_FAVOR, GT_NONE, true> raw;
   raw.load(a, tok0, t_begin, lane, w);
@@ -342,6 +368,7 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
       favor_block_side<R, DK, GATE, true, true>(raw.xk, a.omega, fb, L, lg2gam, sm, LY::kh_off, LY::kl_off,
                                                 LY::kth_off, LY::ktl_off, lane, w);
       if (fb == 0) write_vt<E>(raw.v, L, sm, LY::vt_off, lane, w);
+      if (last && t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
       lds_barrier();
 
       // ---- scores over this block's features: A^T tiles = K~_c Q~_w^T
@@ -380,7 +407,7 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
             for (int i = 0; i < 4; ++i) {
               const int key = 16 * c + 4 * g4 + i;
               float v = sacc[c][i];
-              if (key > q_own) v = 0.f;
+              if (c == w && key > q_own) v = 0.f;  // only the diagonal tile straddles the mask
               if constexpr (GATE == GT_DECAY) v *= exp2f(float(q_own - key) * lg2gam);
               ab[i] = (bf16)v;
               rs += to_f32(ab[i]);
@@ -394,7 +421,6 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
         if constexpr (GATE == GT_DECAY) zdt *= exp2f(float(q_own + 1) * lg2gam);
         if (g4 == 0) lds<float>(sm, LY::den_off + 4 * q_own) = rs + zdt + a.eps;
         lds_barrier();
-        if (t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
       }
 
       // ---- inter-chunk product over this block's features: O^T += S^T Q^^T
@@ -421,17 +447,17 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
 
       // ---- carry the state rows of this block past the chunk
       const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-      favor_state_block<R, E>(S, fb, sm, LY::kth_off, LY::ktl_off, LY::vt_off, gsc, lane, w);
       // z of this block is published after the chunk's last barrier: other
       // waves may still be reading the old values in this block's score phase.
-      if (tid < F::FB) zr[fb] = gsc * zr[fb] + favor_key_colsum(sm, LY::kth_off, LY::ktl_off, tid);
+      favor_state_block<R, E>(S, Z[fb], fb, sm, LY::kth_off, LY::ktl_off, LY::vt_off, gsc, lane, w);
 
       if (last) {
         // ---- intra-chunk part and normalisation: O^T += V^T A^T, o = O / den
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt) {
           const int q = 16 * qt + c16;
-          const float den = lds<float>(sm, LY::den_off + 4 * q);
+          // one correctly rounded reciprocal per row; outputs are fl(O * fl(1 / den))
+          const float inv_den = 1.f / lds<float>(sm, LY::den_off + 4 * q);
           float isc = 1.f;
           if constexpr (GATE == GT_DECAY) isc = exp2f(float(q + 1) * lg2gam);
 #pragma unroll
@@ -447,7 +473,7 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
               acc = mfma16(lds<bf16x8>(sm, LY::vt_off + 2 * ((e + c16) * CP + 32 * p2 + 8 * g4)),
                            lds<bf16x8>(sm, LY::a_off + 2 * (q * CP + 32 * p2 + 8 * g4)), acc);
             if (q < L) {
-              bf16x4 o = pack4(acc[0] / den, acc[1] / den, acc[2] / den, acc[3] / den);
+              bf16x4 o = pack4(acc[0] * inv_den, acc[1] * inv_den, acc[2] * inv_den, acc[3] * inv_den);
               *reinterpret_cast<bf16x4*>(a.out + (tok0 + t0 + q) * E + e + 4 * g4) = o;
             }
           }
@@ -455,10 +481,7 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
       }
       lds_barrier();
     }
-    if (tid < F::FB) {
-#pragma unroll
-      for (int fb = 0; fb < F::NFB; ++fb) lds<float>(sm, LY::z_off + 4 * (fb * F::FB + tid)) = zr[fb];
-    }
+    favor_z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
   }
 
   if (a.S_out != nullptr && s == a.P - 1) {
@@ -469,10 +492,7 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
-    if (tid < F::FB) {
-#pragma unroll
-      for (int fb = 0; fb < F::NFB; ++fb) a.z_out[bh * R + fb * F::FB + tid] = zr[fb];
-    }
+    favor_z_store<R>(Z, a.z_out + bh * R, lane, w);
   }
 }
 

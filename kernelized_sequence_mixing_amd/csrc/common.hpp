@@ -76,6 +76,20 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   return x;
 }
 
+// ---------------------------------------------------------------- masking
+
+// x if ok else +0, without a branch (a select around an expensive expression
+// would otherwise be compiled as a divergent branch per element).
+__device__ __forceinline__ float keep_if(bool ok, float x) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(unsigned, x) & (ok ? 0xffffffffu : 0u));
+}
+
+__device__ __forceinline__ bf16x8 keep_if(bool ok, bf16x8 x) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const unsigned m = ok ? 0xffffffffu : 0u;
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) & m);
+}
+
 // ---------------------------------------------------------------- feature maps
 
 // elu(x) + 1 = x + 1 for x > 0, exp(x) for x <= 0.

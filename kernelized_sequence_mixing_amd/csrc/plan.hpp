@@ -11,8 +11,15 @@
 
 namespace la {
 
-constexpr int kChunk = 64;        // tokens per chunk of the causal kernel (= wave64)
-constexpr int kTargetGroups = 512; // workgroups per causal launch the segment split aims at
+constexpr int kChunk = 64;          // tokens per chunk of the causal kernel (= wave64)
+constexpr int kComputeUnits = 256;  // MI355X
+constexpr int kLdsPerCU = 160 * 1024;
+constexpr int kMaxGroupsPerCU = 3;  // register budget of the chunked output pass
+constexpr int kNonCausalGroups = 512;
+
+// LDS bytes of the causal output-pass workgroup for this shape (0 if not built);
+// pure host arithmetic over the kernels' own layout definitions.
+int causal_output_lds_bytes(int fmap, int r, int dv);
 
 struct FwdPlan {
   int B, H, n, dk, dv, r;

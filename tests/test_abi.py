@@ -77,18 +77,22 @@ int main(void) {{
 # ------------------------------------------------------------------ planning (host arithmetic)
 
 @needs_lib
-@pytest.mark.parametrize("B,H,n,expect_P,expect_len", [
-    (4, 16, 4096, 8, 512),      # causal elu+1 workload
-    (2, 8, 8192, 32, 256),      # RetNet workload
-    (2, 16, 16384, 16, 1024),   # GLA workload
-    (1, 8, 32768, 64, 512),     # FAVOR+ workload
-    (1, 1, 1, 1, 64),
-    (1, 1, 65, 2, 64),
-    (600, 1, 100, 1, 128),
+@pytest.mark.parametrize("B,H,n,d,dv,fmap,r,expect_P,expect_len", [
+    # output-pass LDS 46.6 KB -> 3 workgroups per CU -> 768 (head, segment) groups
+    (4, 16, 4096, 64, 64, "elu1", 64, 11, 384),      # causal elu+1 workload
+    # 82 KB -> 1 per CU -> 256 groups
+    (2, 8, 8192, 128, 128, "elu1", 128, 16, 512),    # RetNet workload
+    (2, 16, 16384, 128, 128, "elu1", 128, 8, 2048),  # GLA workload
+    # FAVOR+ r=256: 126 KB -> 1 per CU
+    (1, 8, 32768, 64, 64, "favor", 256, 32, 1024),   # FAVOR+ workload
+    (1, 1, 1, 64, 64, "elu1", 64, 1, 64),
+    (1, 1, 65, 64, 64, "elu1", 64, 2, 64),
+    (600, 1, 100, 64, 64, "elu1", 64, 2, 64),
+    (800, 1, 100, 64, 64, "elu1", 64, 1, 128),
 ])
-def test_segment_plan(B, H, n, expect_P, expect_len):
+def test_segment_plan(B, H, n, d, dv, fmap, r, expect_P, expect_len):
     from kernelized_sequence_mixing_amd import segments
-    P, L = segments(B, H, n, 64, 64)
+    P, L = segments(B, H, n, d, dv, fmap=fmap, r=r)
     assert (P, L) == (expect_P, expect_len)
     assert L % 64 == 0 and (P - 1) * L < n <= P * L
 
@@ -97,12 +101,12 @@ def test_segment_plan(B, H, n, expect_P, expect_len):
 def test_workspace_sizes():
     from kernelized_sequence_mixing_amd import workspace_size
     # one segment: nothing to chain
-    assert workspace_size(600, 1, 100, 64, 64) == 0
-    # 8 segments x 64 heads of 64x64 fp32 states + normalisers, each region 256-aligned
-    assert workspace_size(4, 16, 4096, 64, 64) == 64 * 8 * 64 * 64 * 4 + 64 * 8 * 64 * 4
+    assert workspace_size(800, 1, 100, 64, 64) == 0
+    # 11 segments x 64 heads of 64x64 fp32 states + normalisers, each region 256-aligned
+    assert workspace_size(4, 16, 4096, 64, 64) == 64 * 11 * 64 * 64 * 4 + 64 * 11 * 64 * 4
     gla = workspace_size(2, 16, 16384, 128, 128, gate_kind="gla")
     plain = workspace_size(2, 16, 16384, 128, 128)
-    assert gla == plain + 32 * 16 * 128 * 4
+    assert gla == plain + 32 * 8 * 128 * 4  # 8 segments: one summed log-gate row per (head, segment)
     # non-causal partial sums always need workspace
     assert workspace_size(1, 1, 256, 32, 32, causal=False, dtype=torch.float32) > 0
 

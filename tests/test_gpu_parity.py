@@ -142,8 +142,9 @@ def test_integer_exact_probe():
     """Q = K = 0 makes every elu+1 feature exactly 1, so scores are exactly d and
     the denominators exactly (i+1) d. Integer values whose running sums stay
     small keep every partial sum exact in bf16/fp32; with eps = 0 each output
-    must equal the IEEE fp32 quotient num/den rounded to bf16, bit for bit,
-    across chunk and segment boundaries and the ragged tail."""
+    must equal fl(num * fl(1 / den)) in IEEE fp32 (one correctly rounded
+    reciprocal per row, then a product) rounded to bf16, bit for bit, across
+    chunk and segment boundaries and the ragged tail."""
     wl = WORKLOADS["causal_elu1"]
     B, H, n = 4, 16, 1285
     inp = make_inputs(wl, seed=0, B=B, H=H, n=n)
@@ -158,7 +159,8 @@ def test_integer_exact_probe():
     num = np.cumsum(np.broadcast_to(Vint, (B, H, n, wl.d_v)).astype(np.float64), axis=2) * wl.d_k
     den = (np.arange(1, n + 1, dtype=np.float64) * wl.d_k)[None, None, :, None]
     assert np.all(np.abs(num) < 2 ** 24) and np.all(np.abs(num / wl.d_k) <= 256)
-    q32 = (num.astype(np.float32) / den.astype(np.float32)).astype(np.float32)
+    inv = (np.float32(1.0) / den.astype(np.float32)).astype(np.float32)
+    q32 = (num.astype(np.float32) * inv).astype(np.float32)
     want = torch.from_numpy(q32).to(torch.bfloat16)
     assert torch.equal(out.view(torch.int16), want.view(torch.int16))
 
