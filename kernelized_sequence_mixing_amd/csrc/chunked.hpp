@@ -26,10 +26,14 @@
 // the chunk for the scores, and value columns [w E/4, (w+1) E/4) of the state
 // and the outputs. The fp32 state lives in MFMA accumulators for the whole
 // sequence; its bf16 image feeds the inter-chunk product straight from
-// registers. LDS holds the chunk's operands (bf16):
-//   q  [64][R+8]   Q~ (also Q^), row-major          k  [64][R+8]  K~
-//   kt [R][64+8]   K^ transposed                    vt [E][64+8]  V transposed
-//   a  [64][64+8]  masked scores, row-major
+// registers. LDS holds the chunk's operands (bf16), all row-major:
+//   q  [64][R+8]   Q~ (also Q^)      k [64][R+8]   K~      v [64][E+8]   V
+//   a  [64][64+8]  masked scores     kh [64][R+8]  K^ (RetNet only)
+// Operands that contract over tokens (the state update, V^T A^T) are read
+// from the row-major tiles with the LDS transpose read (ds_read_b64_tr_b16).
+// Without a gate K^ = K~; with the GLA gate K^ = Gamma K~ feature by feature,
+// so the state update is S <- Gamma (S + K~^T V); RetNet weights each key row
+// and keeps K^ in a tile of its own (pass 1 stores only K^, in the k tile).
 #pragma once
 
 #include "common.hpp"
@@ -61,25 +65,26 @@ struct CausalArgs {
 
 constexpr int CP = kChunk + 8;  // row stride (elements) of the [x][t] tiles
 
-template <int R, int E>
+template <int R, int E, int GATE>
 struct FwdLayout {
-  static constexpr int RP = R + 8;
+  static constexpr int RP = R + 8, EP = E + 8;
   static constexpr int q_off = 0;
   static constexpr int k_off = q_off + kChunk * RP * 2;
-  static constexpr int kt_off = k_off + kChunk * RP * 2;
-  static constexpr int vt_off = kt_off + R * CP * 2;
-  static constexpr int a_off = vt_off + E * CP * 2;
+  static constexpr int v_off = k_off + kChunk * RP * 2;
+  static constexpr int kh_off = v_off + kChunk * EP * 2;
+  static constexpr int a_off = kh_off + (GATE == GT_DECAY ? kChunk * RP * 2 : 0);
   static constexpr int z_off = a_off + kChunk * CP * 2;
   static constexpr int gam_off = z_off + R * 4;
   static constexpr int den_off = gam_off + R * 4;
   static constexpr int bytes = den_off + kChunk * 4;
 };
 
-template <int R, int E>
+template <int R, int E, int GATE>
 struct SegLayout {
-  static constexpr int kt_off = 0;
-  static constexpr int vt_off = kt_off + R * CP * 2;
-  static constexpr int gam_off = vt_off + E * CP * 2;
+  static constexpr int RP = R + 8, EP = E + 8;
+  static constexpr int k_off = 0;  // K^ rows
+  static constexpr int v_off = k_off + kChunk * RP * 2;
+  static constexpr int gam_off = v_off + kChunk * EP * 2;
   static constexpr int logg_off = gam_off + R * 4;
   static constexpr int bytes = logg_off + R * 4;
 };
@@ -95,6 +100,23 @@ __device__ __forceinline__ void lds_barrier() {
 template <typename T>
 __device__ __forceinline__ T& lds(char* base, int byte_off) {
   return *reinterpret_cast<T*>(base + byte_off);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA operand from a row-major bf16 LDS tile by transpose reads: lane (g, c)
+// receives tile[k0 + 8 g + jj][col0 + c] for jj = 0..7 (eight consecutive
+// contraction rows of column col0 + c). Within each 16-lane group the
+// transpose read hands lane i element j of the 4-element chunk addressed by
+// lane 4 j + i / 4, so lane m = 4 j + q addresses row k0 + 8 g + j (+4 for the
+// second read), columns col0 + 4 q .. col0 + 4 q + 3.
+__device__ __forceinline__ bf16x8 tr_operand(char* sm, int tile_off, int stride, int k0, int col0, int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int base = tile_off + 2 * ((k0 + 8 * g4 + (c16 >> 2)) * stride + col0 + 4 * (c16 & 3));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + base));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + base + 2 * 4 * stride));
+  return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
 }
 
 // Raw inputs of one chunk, held in registers from the global load to the LDS
@@ -169,17 +191,18 @@ struct RawChunk {
   }
 };
 
-// elu+1 features, gate factors and transposes of one chunk into LDS.
-//   WITH_Q: pass 3 (writes q, k, kt, vt, gam); else pass 1 (kt, vt, gam, logg).
+// elu+1 features and gate factors of one chunk into LDS, all tiles row-major.
+//   WITH_Q: pass 3 (writes q, k, v, gam; kh for RetNet); else pass 1 (k holding
+//   K^, v, gam, logg).
 // L = valid tokens in the chunk. Rows t >= L get phi(k) = 0 and v = 0, and a
 // zero log-gate, so they add nothing to the state.
 template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q>
 __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q>& raw, const CausalArgs& a,
                                               int L, float lg2gam, char* sm, int q_off, int k_off,
-                                              int kt_off, int vt_off, int gam_off, int logg_off,
+                                              int kh_off, int v_off, int gam_off, int logg_off,
                                               int lane, int w) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q>;
-  constexpr int RP = R + 8;
+  constexpr int RP = R + 8, EP = E + 8;
   static_assert(FMAP == FM_ELU1, "FAVOR+ chunks use the kernels of chunked_favor.hpp");
   if constexpr (Raw::ROWMAJOR) {
     const int t = 16 * w + (lane >> 2);
@@ -196,64 +219,56 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         vk[u] = keep_if(valid, elu1(to_f32(raw.k[j][u])));
         vkh[u] = vk[u] * decay_k;
       }
-      if constexpr (WITH_Q) {
+      if constexpr (WITH_Q)
         lds<bf16x8>(sm, q_off + 2 * (t * RP + f0)) =
             cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
-        lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) =
-            cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7]));
+      const bf16x8 kr = cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7]));
+      const bf16x8 khr = cat8(pack4(vkh[0], vkh[1], vkh[2], vkh[3]), pack4(vkh[4], vkh[5], vkh[6], vkh[7]));
+      if constexpr (GATE != GT_DECAY) {
+        lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) = kr;
+      } else if constexpr (WITH_Q) {
+        lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) = kr;
+        lds<bf16x8>(sm, kh_off + 2 * (t * RP + f0)) = khr;
+      } else {
+        lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) = khr;
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) lds<bf16>(sm, kt_off + 2 * ((f0 + u) * CP + t)) = (bf16)vkh[u];
     }
 #pragma unroll
-    for (int j = 0; j < E / 32; ++j) {
-      const int e0 = 8 * ((lane & 3) + 4 * j);
-      const bf16x8 vv = keep_if(valid, raw.v[j]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) lds<bf16>(sm, vt_off + 2 * ((e0 + u) * CP + t)) = vv[u];
-    }
+    for (int j = 0; j < E / 32; ++j)
+      lds<bf16x8>(sm, v_off + 2 * (t * EP + 8 * ((lane & 3) + 4 * j))) = keep_if(valid, raw.v[j]);
     return;
   }
   const bool valid = lane < L;
   {
     const int t = lane;
-    float decay_k = 1.f;
-    if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(L - 1 - t) * lg2gam);
     // GLA: lane f (< FR) collects the chunk's summed log-gate of this wave's
     // feature f; one store per lane after the feature loop.
     float my_bend = 0.f;
 #pragma unroll
     for (int j = 0; j < Raw::FR / 8; ++j) {
       const int f0 = w * Raw::FR + 8 * j;
-      float vq[8], vk[8], vkh[8];
+      float vq[8], vk[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         float pq = WITH_Q ? elu1(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
         float pk = keep_if(valid, elu1(to_f32(raw.k[j][u])));
-        float kh = pk;
-        if constexpr (GATE == GT_DECAY) kh = pk * decay_k;
         if constexpr (GATE == GT_GLA) {
           float la = keep_if(valid, gla_log_alpha(to_f32(raw.g[j][u]), a.inv_tau));
           float b = wave_inclusive_scan(la);
           // the chunk total is uniform across the wave: a scalar read of lane 63
           const float bend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
           pq *= __expf(b);
-          kh = pk * __expf(bend - b);
-          pk *= __expf(-b);
+          pk *= __expf(-b);  // K^ = e^{b_end} K~: applied to the state row after the update
           my_bend = lane == 8 * j + u ? bend : my_bend;
         }
         vq[u] = pq;
         vk[u] = pk;
-        vkh[u] = kh;
       }
-      if constexpr (WITH_Q) {
+      if constexpr (WITH_Q)
         lds<bf16x8>(sm, q_off + 2 * (t * RP + f0)) =
             cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
-        lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) =
-            cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7]));
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) lds<bf16>(sm, kt_off + 2 * ((f0 + u) * CP + t)) = (bf16)vkh[u];
+      lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) =
+          cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7]));
     }
     if constexpr (GATE == GT_GLA) {
       if (lane < Raw::FR) {
@@ -262,15 +277,12 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       }
     }
   }
-  // values, transposed (rows past the end are zero)
+  // values, row-major (rows past the end are zero)
   {
     constexpr int EV = Raw::EV;
 #pragma unroll
-    for (int j = 0; j < EV / 8; ++j) {
-      const bf16x8 vv = keep_if(valid, raw.v[j]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = vv[u];
-    }
+    for (int j = 0; j < EV / 8; ++j)
+      lds<bf16x8>(sm, v_off + 2 * (lane * EP + w * EV + 8 * j)) = keep_if(valid, raw.v[j]);
   }
 }
 
@@ -284,13 +296,17 @@ struct ZTiles {
   static constexpr int OWNERS = R / (16 * ZT);      // waves that own z tiles
 };
 
-// S (wave slab: rows all R, value columns [w E/4, (w+1) E/4)) <- Gamma S + K^^T V,
-// and this wave's z tiles <- Gamma z + K^^T 1.
+// S (wave slab: rows all R, value columns [w E/4, (w+1) E/4)) and this wave's
+// z tiles, past one chunk:
+//   no gate   S <- S + K~^T V                    z <- z + K~^T 1
+//   RetNet    S <- gamma^L S + K^^T V            (kh_off holds K^ rows)
+//   GLA       S <- Gamma (S + K~^T V)            Gamma = diag(e^{b_end}) from gam_off
+// Both operands come from row-major [token][column] tiles by transpose reads.
 template <int R, int E, int GATE>
 __device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (&Z)[ZTiles<R>::ZT], char* sm,
-                                             int kt_off, int vt_off, int gam_off, float gscale, int lane, int w) {
-  constexpr int ZT = ZTiles<R>::ZT;
-  const int g4 = lane >> 4, c16 = lane & 15;
+                                             int kh_off, int v_off, int gam_off, float gscale, int lane, int w) {
+  constexpr int ZT = ZTiles<R>::ZT, RP = R + 8, EP = E + 8;
+  const int g4 = lane >> 4;
   const int ebase = w * (E / 4);
   bf16x8 ones;
 #pragma unroll
@@ -299,13 +315,12 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (
 #pragma unroll
   for (int eb = 0; eb < E / 64; ++eb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      vb[eb][ks] = lds<bf16x8>(sm, vt_off + 2 * ((ebase + 16 * eb + c16) * CP + 32 * ks + 8 * g4));
+    for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_operand(sm, v_off, EP, 32 * ks, ebase + 16 * eb, lane);
 #pragma unroll
   for (int rt = 0; rt < R / 16; ++rt) {
     bf16x8 ka[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) ka[ks] = lds<bf16x8>(sm, kt_off + 2 * ((16 * rt + c16) * CP + 32 * ks + 8 * g4));
+    for (int ks = 0; ks < 2; ++ks) ka[ks] = tr_operand(sm, kh_off, RP, 32 * ks, 16 * rt, lane);
     float gr[4] = {gscale, gscale, gscale, gscale};
     if constexpr (GATE == GT_GLA) {
 #pragma unroll
@@ -314,22 +329,30 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (
 #pragma unroll
     for (int eb = 0; eb < E / 64; ++eb) {
       f32x4 st = S[rt][eb];
-      if constexpr (GATE != GT_NONE) {
+      if constexpr (GATE == GT_DECAY) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[i] *= gr[i];
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vb[eb][ks], st);
+      if constexpr (GATE == GT_GLA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[i] *= gr[i];
+      }
       S[rt][eb] = st;
     }
     if (rt / ZT == w) {
       f32x4 zt = Z[rt % ZT];
-      if constexpr (GATE != GT_NONE) {
+      if constexpr (GATE == GT_DECAY) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) zt = mfma16(ka[ks], ones, zt);
+      if constexpr (GATE == GT_GLA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
+      }
       Z[rt % ZT] = zt;
     }
   }
@@ -363,7 +386,7 @@ __device__ __forceinline__ void z_load(f32x4 (&Z)[ZTiles<R>::ZT], const float* s
 template <int R, int E, int DK, int FMAP, int GATE>
 __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  using LY = SegLayout<R, E>;
+  using LY = SegLayout<R, E, GATE>;
   const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
@@ -394,12 +417,12 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
   if (t_begin + kChunk < t_end) raw1.load(a, tok0, t_begin + kChunk, lane, w);
   auto chunk = [&](Raw& raw, int t0) {
     const int L = min(kChunk, a.n - t0);
-    chunk_prelude<R, E, DK, FMAP, GATE, false>(raw, a, L, lg2gam, sm, 0, 0, LY::kt_off, LY::vt_off,
+    chunk_prelude<R, E, DK, FMAP, GATE, false>(raw, a, L, lg2gam, sm, 0, LY::k_off, 0, LY::v_off,
                                                LY::gam_off, LY::logg_off, lane, w);
     if (t0 + 2 * kChunk < t_end) raw.load(a, tok0, t0 + 2 * kChunk, lane, w);
     lds_barrier();
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE>(S, Z, sm, LY::kt_off, LY::vt_off, LY::gam_off, gsc, lane, w);
+    state_update<R, E, GATE>(S, Z, sm, LY::k_off, LY::v_off, LY::gam_off, gsc, lane, w);
     lds_barrier();
   };
   for (int t0 = t_begin; t0 < t_end; t0 += 2 * kChunk) {
@@ -426,8 +449,8 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
 template <int R, int E, int DK, int FMAP, int GATE>
 __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  using LY = FwdLayout<R, E>;
-  constexpr int RP = LY::RP, NEB = E / 64, KP = R / 32;
+  using LY = FwdLayout<R, E, GATE>;
+  constexpr int RP = LY::RP, EP = LY::EP, NEB = E / 64, KP = R / 32;
   const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
@@ -470,14 +493,13 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
         Sop[p][eb] = cat8(pack4(S[2 * p][eb][0], S[2 * p][eb][1], S[2 * p][eb][2], S[2 * p][eb][3]),
                           pack4(S[2 * p + 1][eb][0], S[2 * p + 1][eb][1], S[2 * p + 1][eb][2], S[2 * p + 1][eb][3]));
   };
-  rebuild_sop();
 
   RawChunk<R, E, DK, FMAP, GATE, true> raw;
   raw.load(a, tok0, t_begin, lane, w);
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int L = min(kChunk, a.n - t0);
-    chunk_prelude<R, E, DK, FMAP, GATE, true>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kt_off,
-                                              LY::vt_off, LY::gam_off, 0, lane, w);
+    chunk_prelude<R, E, DK, FMAP, GATE, true>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
+                                              LY::v_off, LY::gam_off, 0, lane, w);
     // the raw registers are free again: the next chunk's loads fly during this one
     if (t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
     lds_barrier();
@@ -528,6 +550,7 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
     lds_barrier();
 
     // ---- outputs for value columns [w E/4, (w+1) E/4): O^T = S^T Q^^T + V^T A^T
+    rebuild_sop();  // built here so it is not live across the prelude and the scores
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
       const int q = 16 * qt + c16;
@@ -552,7 +575,7 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
         }
 #pragma unroll
         for (int p2 = 0; p2 <= qt / 2; ++p2)
-          acc = mfma16(lds<bf16x8>(sm, LY::vt_off + 2 * ((e + c16) * CP + 32 * p2 + 8 * g4)),
+          acc = mfma16(tr_operand(sm, LY::v_off, EP, 32 * p2, e, lane),
                        lds<bf16x8>(sm, LY::a_off + 2 * (q * CP + 32 * p2 + 8 * g4)), acc);
         if (q < L) {
           bf16x4 o = pack4(acc[0] * inv_den, acc[1] * inv_den, acc[2] * inv_den, acc[3] * inv_den);
@@ -563,8 +586,8 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
 
     // ---- carry the state past this chunk
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE>(S, Z, sm, LY::kt_off, LY::vt_off, LY::gam_off, gsc, lane, w);
-    rebuild_sop();
+    state_update<R, E, GATE>(S, Z, sm, GATE == GT_DECAY ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off, gsc,
+                             lane, w);
     z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
     lds_barrier();
   }
@@ -606,7 +629,7 @@ la_status run_causal(const FwdPlan& p) {
     a1.z_out = p.ws_z;
     a1.logG_out = p.ws_logG;
     auto k1 = causal_segment_state<R, E, DK, FMAP, GATE>;
-    constexpr int lds1 = SegLayout<R, E>::bytes;
+    constexpr int lds1 = SegLayout<R, E, GATE>::bytes;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
         hipSuccess)
       return LA_ERR_HIP;
@@ -627,7 +650,7 @@ la_status run_causal(const FwdPlan& p) {
   a.S_out = p.S_final;
   a.z_out = p.z_final;
   auto k3 = causal_chunk_forward<R, E, DK, FMAP, GATE>;
-  constexpr int lds3 = FwdLayout<R, E>::bytes;
+  constexpr int lds3 = FwdLayout<R, E, GATE>::bytes;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k3), hipFuncAttributeMaxDynamicSharedMemorySize, lds3) !=
       hipSuccess)
     return LA_ERR_HIP;

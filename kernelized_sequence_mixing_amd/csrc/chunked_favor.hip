@@ -41,14 +41,26 @@ static int favor_lds(int dv) {
   return 0;
 }
 
-template <int R>
-static int elu_lds(int dv) {
-  if (dv == 64) return FwdLayout<R, 64>::bytes;
-  if (dv == 128) return FwdLayout<R, 128>::bytes;
+template <int R, int GATE>
+static int elu_lds_gate(int dv) {
+  if (dv == 64) return FwdLayout<R, 64, GATE>::bytes;
+  if (dv == 128) return FwdLayout<R, 128, GATE>::bytes;
   return 0;
 }
 
-int causal_output_lds_bytes(int fmap, int r, int dv) {
+template <int R>
+static int elu_lds(int dv, int gate) {
+  switch (gate) {
+    case GT_NONE: return elu_lds_gate<R, GT_NONE>(dv);
+    case GT_DECAY: return elu_lds_gate<R, GT_DECAY>(dv);
+    case GT_GLA: return elu_lds_gate<R, GT_GLA>(dv);
+  }
+  return 0;
+}
+
+static_assert(GT_NONE == LA_GATE_NONE && GT_DECAY == LA_GATE_DECAY && GT_GLA == LA_GATE_GLA, "gate codes");
+
+int causal_output_lds_bytes(int fmap, int r, int dv, int gate) {
   if (fmap == LA_FMAP_FAVOR) {
     switch (r) {
       case 64: return favor_lds<64>(dv);
@@ -58,9 +70,9 @@ int causal_output_lds_bytes(int fmap, int r, int dv) {
     return 0;
   }
   switch (r) {
-    case 32: return elu_lds<32>(dv);
-    case 64: return elu_lds<64>(dv);
-    case 128: return elu_lds<128>(dv);
+    case 32: return elu_lds<32>(dv, gate);
+    case 64: return elu_lds<64>(dv, gate);
+    case 128: return elu_lds<128>(dv, gate);
   }
   return 0;
 }

@@ -77,22 +77,22 @@ int main(void) {{
 # ------------------------------------------------------------------ planning (host arithmetic)
 
 @needs_lib
-@pytest.mark.parametrize("B,H,n,d,dv,fmap,r,expect_P,expect_len", [
-    # output-pass LDS 46.6 KB -> 3 workgroups per CU -> 768 (head, segment) groups
-    (4, 16, 4096, 64, 64, "elu1", 64, 11, 384),      # causal elu+1 workload
-    # 82 KB -> 1 per CU -> 256 groups
-    (2, 8, 8192, 128, 128, "elu1", 128, 16, 512),    # RetNet workload
-    (2, 16, 16384, 128, 128, "elu1", 128, 8, 2048),  # GLA workload
+@pytest.mark.parametrize("B,H,n,d,dv,fmap,r,gate,expect_P,expect_len", [
+    # output-pass LDS 37.6 KB -> 4 workgroups per CU by LDS, capped at 3 -> 768 (head, segment) groups
+    (4, 16, 4096, 64, 64, "elu1", 64, "none", 11, 384),       # causal elu+1 workload
+    # 78.3 KB (RetNet keeps a weighted key tile) / 61.3 KB -> 2 per CU -> 512 groups
+    (2, 8, 8192, 128, 128, "elu1", 128, "decay", 32, 256),    # RetNet workload
+    (2, 16, 16384, 128, 128, "elu1", 128, "gla", 16, 1024),   # GLA workload
     # FAVOR+ r=256: 126 KB -> 1 per CU
-    (1, 8, 32768, 64, 64, "favor", 256, 32, 1024),   # FAVOR+ workload
-    (1, 1, 1, 64, 64, "elu1", 64, 1, 64),
-    (1, 1, 65, 64, 64, "elu1", 64, 2, 64),
-    (600, 1, 100, 64, 64, "elu1", 64, 2, 64),
-    (800, 1, 100, 64, 64, "elu1", 64, 1, 128),
+    (1, 8, 32768, 64, 64, "favor", 256, "none", 32, 1024),    # FAVOR+ workload
+    (1, 1, 1, 64, 64, "elu1", 64, "none", 1, 64),
+    (1, 1, 65, 64, 64, "elu1", 64, "none", 2, 64),
+    (600, 1, 100, 64, 64, "elu1", 64, "none", 2, 64),
+    (800, 1, 100, 64, 64, "elu1", 64, "none", 1, 128),
 ])
-def test_segment_plan(B, H, n, d, dv, fmap, r, expect_P, expect_len):
+def test_segment_plan(B, H, n, d, dv, fmap, r, gate, expect_P, expect_len):
     from kernelized_sequence_mixing_amd import segments
-    P, L = segments(B, H, n, d, dv, fmap=fmap, r=r)
+    P, L = segments(B, H, n, d, dv, fmap=fmap, r=r, gate_kind=gate)
     assert (P, L) == (expect_P, expect_len)
     assert L % 64 == 0 and (P - 1) * L < n <= P * L
 
@@ -106,7 +106,7 @@ def test_workspace_sizes():
     assert workspace_size(4, 16, 4096, 64, 64) == 64 * 11 * 64 * 64 * 4 + 64 * 11 * 64 * 4
     gla = workspace_size(2, 16, 16384, 128, 128, gate_kind="gla")
     plain = workspace_size(2, 16, 16384, 128, 128)
-    assert gla == plain + 32 * 8 * 128 * 4  # 8 segments: one summed log-gate row per (head, segment)
+    assert gla == plain + 32 * 16 * 128 * 4  # 16 segments: one summed log-gate row per (head, segment)
     # non-causal partial sums always need workspace
     assert workspace_size(1, 1, 256, 32, 32, causal=False, dtype=torch.float32) > 0
 
