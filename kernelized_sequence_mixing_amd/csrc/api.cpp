@@ -87,10 +87,10 @@ bool shapes_built(const la_feature_map* f, int dk, int dv, bool causal) {
 // Segments per head for the causal form: enough (head, segment) workgroups to
 // fill every CU with as many output-pass workgroups as its LDS holds (at most
 // kMaxGroupsPerCU), each segment a whole number of chunks.
-void plan_segments(int B, int H, int n, int fmap, int r, int dv, int gate, int* P, int* seg_len) {
+void plan_segments(int B, int H, int n, int fmap, int r, int dv, int dk, int gate, int* P, int* seg_len) {
   const int nchunks = (n + kChunk - 1) / kChunk;
   const long long BH = (long long)B * H;
-  const int lds = causal_output_lds_bytes(fmap, r, dv, gate);
+  const int lds = causal_output_lds_bytes(fmap, r, dv, dk, gate);
   int per_cu = lds > 0 ? kLdsPerCU / lds : 1;
   if (per_cu < 1) per_cu = 1;
   if (per_cu > kMaxGroupsPerCU) per_cu = kMaxGroupsPerCU;
@@ -124,7 +124,7 @@ WsLayout workspace_layout(const la_problem* p, const la_feature_map* f, int caus
   size_t pieces;
   if (causal) {
     int P, L;
-    plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, gate, &P, &L);
+    plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate, &P, &L);
     if (P <= 1) return w;
     pieces = (size_t)P;
   } else {
@@ -198,7 +198,7 @@ la_status la_forward_segments(const la_problem* p, const la_feature_map* fmap, i
     return LA_OK;
   }
   int P, L;
-  plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, p->d_v, gate_kind(gate), &P, &L);
+  plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, p->d_v, p->d_k, gate_kind(gate), &P, &L);
   *segments = P;
   *segment_len = L;
   return LA_OK;
@@ -275,7 +275,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   plan.ws_z = wl.bytes ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
   plan.ws_logG = (wl.bytes && causal && gk == LA_GATE_GLA) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
   if (causal) {
-    plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, p->d_v, gk, &plan.P, &plan.seg_len);
+    plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, p->d_v, p->d_k, gk, &plan.P, &plan.seg_len);
     return fmap->kind == LA_FMAP_ELU1 ? launch_causal_elu1(plan) : launch_causal_favor(plan);
   }
   plan_splits(p->B, p->H, p->n, &plan.splits, &plan.split_len);

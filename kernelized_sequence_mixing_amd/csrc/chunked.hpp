@@ -128,7 +128,10 @@ __device__ __forceinline__ bf16x8 tr_operand(char* sm, int tile_off, int stride,
 //    16 w + l / 4, so each load instruction reads 16 rows, 64 contiguous bytes
 //    of each, and every row is consumed whole by two instructions;
 //  * lane-per-token (GLA gate, whose scan runs across the 64 lanes): lane l
-//    holds token l, wave w holds features [w R/4, (w+1) R/4).
+//    holds token l, wave w holds features [w R/4, (w+1) R/4); V uses this
+//    layout for FAVOR+ too.
+// FAVOR+ inputs X (projected inside the kernel): wave w holds tokens
+// [16w, 16w+16), lane l token 16 w + l % 16, columns 32 ks + 8 (l / 16) .. + 7.
 template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q>
 struct RawChunk {
   static constexpr int FR = R / 4;       // features per wave (elu+1 lane-per-token layout)
@@ -139,17 +142,20 @@ struct RawChunk {
   bf16x8 q[ELU && WITH_Q ? FR / 8 : 1];
   bf16x8 k[ELU ? FR / 8 : 1];
   bf16x8 g[GATE == GT_GLA ? FR / 8 : 1];
-  bf16x8 xq[!ELU && WITH_Q ? 4 * KS : 1];
-  bf16x8 xk[!ELU ? 4 * KS : 1];
+  bf16x8 xq[!ELU && WITH_Q ? KS : 1];   // FAVOR+: token 16 w + l % 16, columns 32 ks + 8 (l / 16)
+  bf16x8 xk[!ELU ? KS : 1];
   bf16x8 v[EV / 8];
 
-  // Rows past the end of the sequence are read from the last valid row (always
-  // in bounds) and masked by the consumer, so no instruction here touches the
-  // loaded values and the loads stay in flight until the next chunk needs them.
-  __device__ __forceinline__ void load(const CausalArgs& a, long long tok0, int t0, int lane, int w) {
+  // Rows at or past row_end (the end of the segment, at most n) are read from
+  // row row_end - 1 (always in bounds) and masked by the consumer, so no
+  // instruction here touches the loaded values and the loads stay in flight
+  // until the next chunk needs them. A load for a chunk past the segment is
+  // therefore harmless, which lets the loops issue every refill
+  // unconditionally.
+  __device__ __forceinline__ void load(const CausalArgs& a, long long tok0, int t0, int row_end, int lane, int w) {
     const int g4 = lane >> 4, c16 = lane & 15;
     if constexpr (ROWMAJOR) {
-      const long long row = tok0 + min(t0 + 16 * w + (lane >> 2), a.n - 1);
+      const long long row = tok0 + min(t0 + 16 * w + (lane >> 2), row_end - 1);
 #pragma unroll
       for (int j = 0; j < R / 32; ++j) {
         const int f0 = 8 * ((lane & 3) + 4 * j);
@@ -162,7 +168,7 @@ struct RawChunk {
       return;
     }
     {
-      const long long row = tok0 + min(t0 + lane, a.n - 1);
+      const long long row = tok0 + min(t0 + lane, row_end - 1);
       if constexpr (ELU) {
 #pragma unroll
         for (int j = 0; j < FR / 8; ++j) {
@@ -178,14 +184,11 @@ struct RawChunk {
       for (int j = 0; j < EV / 8; ++j) v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * E + w * EV + 8 * j);
     }
     if constexpr (!ELU) {
+      const long long row = tok0 + min(t0 + 16 * w + c16, row_end - 1);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const long long row = tok0 + min(t0 + 16 * tt + c16, a.n - 1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (WITH_Q) xq[tt * KS + ks] = *reinterpret_cast<const bf16x8*>(a.Q + row * DK + 32 * ks + 8 * g4);
-          xk[tt * KS + ks] = *reinterpret_cast<const bf16x8*>(a.K + row * DK + 32 * ks + 8 * g4);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (WITH_Q) xq[ks] = *reinterpret_cast<const bf16x8*>(a.Q + row * DK + 32 * ks + 8 * g4);
+        xk[ks] = *reinterpret_cast<const bf16x8*>(a.K + row * DK + 32 * ks + 8 * g4);
       }
     }
   }
@@ -216,14 +219,16 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         vq[u] = WITH_Q ? elu1(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
-        vk[u] = keep_if(valid, elu1(to_f32(raw.k[j][u])));
+        vk[u] = elu1(to_f32(raw.k[j][u]));
         vkh[u] = vk[u] * decay_k;
       }
       if constexpr (WITH_Q)
         lds<bf16x8>(sm, q_off + 2 * (t * RP + f0)) =
             cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
-      const bf16x8 kr = cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7]));
-      const bf16x8 khr = cat8(pack4(vkh[0], vkh[1], vkh[2], vkh[3]), pack4(vkh[4], vkh[5], vkh[6], vkh[7]));
+      // keys past the end are zeroed after packing (four masks per eight features)
+      const bf16x8 kr = keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
+      const bf16x8 khr =
+          keep_if(valid, cat8(pack4(vkh[0], vkh[1], vkh[2], vkh[3]), pack4(vkh[4], vkh[5], vkh[6], vkh[7])));
       if constexpr (GATE != GT_DECAY) {
         lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) = kr;
       } else if constexpr (WITH_Q) {
@@ -251,7 +256,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         float pq = WITH_Q ? elu1(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
-        float pk = keep_if(valid, elu1(to_f32(raw.k[j][u])));
+        float pk = elu1(to_f32(raw.k[j][u]));
         if constexpr (GATE == GT_GLA) {
           float la = keep_if(valid, gla_log_alpha(to_f32(raw.g[j][u]), a.inv_tau));
           float b = wave_inclusive_scan(la);
@@ -268,7 +273,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         lds<bf16x8>(sm, q_off + 2 * (t * RP + f0)) =
             cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
       lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) =
-          cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7]));
+          keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
     }
     if constexpr (GATE == GT_GLA) {
       if (lane < Raw::FR) {
@@ -409,25 +414,39 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
   if (tid < R) lds<float>(sm, LY::logg_off + 4 * tid) = 0.f;
   lds_barrier();
 
-  // Two chunks of loads in flight: buffer b holds chunk (2 i + b); after its
-  // prelude consumes it, it is refilled with the chunk two ahead.
+  // DEPTH chunks of loads in flight: buffer b holds chunk DEPTH i + b; after
+  // its prelude consumes it, it is refilled with the chunk DEPTH ahead.
+  // Refills are unconditional (past the segment they re-read its last row),
+  // so every path into a prelude has the same loads outstanding and the wait
+  // before it covers only that buffer. A step past the last chunk does
+  // nothing but its refill.
   using Raw = RawChunk<R, E, DK, FMAP, GATE, false>;
-  Raw raw0, raw1;
-  raw0.load(a, tok0, t_begin, lane, w);
-  if (t_begin + kChunk < t_end) raw1.load(a, tok0, t_begin + kChunk, lane, w);
-  auto chunk = [&](Raw& raw, int t0) {
+  constexpr int DEPTH = 2;
+  const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+  Raw raw[DEPTH];
+#pragma unroll
+  for (int b = 0; b < DEPTH; ++b) {
+    raw[b].load(a, tok0, t_begin + b * kChunk, t_end, lane, w);
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: lower buffers complete first
+  }
+  auto step = [&](Raw& rw, int ci) {
+    const int t0 = t_begin + ci * kChunk;
+    const bool live = ci < nch;
     const int L = min(kChunk, a.n - t0);
-    chunk_prelude<R, E, DK, FMAP, GATE, false>(raw, a, L, lg2gam, sm, 0, LY::k_off, 0, LY::v_off,
-                                               LY::gam_off, LY::logg_off, lane, w);
-    if (t0 + 2 * kChunk < t_end) raw.load(a, tok0, t0 + 2 * kChunk, lane, w);
-    lds_barrier();
-    const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE>(S, Z, sm, LY::k_off, LY::v_off, LY::gam_off, gsc, lane, w);
-    lds_barrier();
+    if (live)
+      chunk_prelude<R, E, DK, FMAP, GATE, false>(rw, a, L, lg2gam, sm, 0, LY::k_off, 0, LY::v_off,
+                                                 LY::gam_off, LY::logg_off, lane, w);
+    rw.load(a, tok0, t0 + DEPTH * kChunk, t_end, lane, w);
+    if (live) {
+      lds_barrier();
+      const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+      state_update<R, E, GATE>(S, Z, sm, LY::k_off, LY::v_off, LY::gam_off, gsc, lane, w);
+      lds_barrier();
+    }
   };
-  for (int t0 = t_begin; t0 < t_end; t0 += 2 * kChunk) {
-    chunk(raw0, t0);
-    if (t0 + kChunk < t_end) chunk(raw1, t0 + kChunk);
+  for (int ci = 0; ci < nch; ci += DEPTH) {
+#pragma unroll
+    for (int b = 0; b < DEPTH; ++b) step(raw[b], ci + b);
   }
   const long long slot = bh * a.P + s;
   float* So = a.S_out + slot * R * E;
@@ -494,14 +513,25 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
                           pack4(S[2 * p + 1][eb][0], S[2 * p + 1][eb][1], S[2 * p + 1][eb][2], S[2 * p + 1][eb][3]));
   };
 
-  RawChunk<R, E, DK, FMAP, GATE, true> raw;
-  raw.load(a, tok0, t_begin, lane, w);
-  for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
+  // Loads run DEPTH chunks ahead (two buffers when the registers allow),
+  // refilled unconditionally as in pass 1.
+  using Raw = RawChunk<R, E, DK, FMAP, GATE, true>;
+  constexpr int DEPTH = 1;
+  const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+  Raw raw0, raw1;
+  raw0.load(a, tok0, t_begin, t_end, lane, w);
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order: buffer 0's loads complete first
+  if constexpr (DEPTH == 2) raw1.load(a, tok0, t_begin + kChunk, t_end, lane, w);
+  auto step = [&](Raw& raw, int ci) {
+    const int t0 = t_begin + ci * kChunk;
+    const bool live = ci < nch;
     const int L = min(kChunk, a.n - t0);
-    chunk_prelude<R, E, DK, FMAP, GATE, true>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
-                                              LY::v_off, LY::gam_off, 0, lane, w);
-    // the raw registers are free again: the next chunk's loads fly during this one
-    if (t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
+    if (live)
+      chunk_prelude<R, E, DK, FMAP, GATE, true>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
+                                                LY::v_off, LY::gam_off, 0, lane, w);
+    // the raw registers are free again: this refill flies during the next DEPTH chunks
+    raw.load(a, tok0, t0 + DEPTH * kChunk, t_end, lane, w);
+    if (!live) return;
     lds_barrier();
 
     // ---- scores for query rows [16w, 16w+16): A^T tiles = K~_c Q~_w^T
@@ -522,19 +552,21 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
         for (int ks = 0; ks < KP; ++ks)
           acc = mfma16(lds<bf16x8>(sm, LY::k_off + 2 * ((16 * c + c16) * RP + 32 * ks + 8 * g4)), qop[ks], acc);
         // acc[i] = A[q][key], key = 16c + 4g + i
-        bf16x4 ab;
         float gbase = 1.f;
         if constexpr (GATE == GT_DECAY) gbase = exp2f(float(q - 16 * c - 4 * g4) * lg2gam);
+        float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = 16 * c + 4 * g4 + i;
-          float v = acc[i];
-          if (c == w && key > q) v = 0.f;  // only the diagonal tile straddles the mask
-          if constexpr (GATE == GT_DECAY) v *= gbase * ginv[i];
-          ab[i] = (bf16)v;
-          rs += to_f32(ab[i]);
+          v[i] = acc[i];
+          if (c == w && key > q) v[i] = 0.f;  // only the diagonal tile straddles the mask
+          if constexpr (GATE == GT_DECAY) v[i] *= gbase * ginv[i];
         }
-        lds<bf16x4>(sm, LY::a_off + 2 * (q * CP + 16 * c + 4 * g4)) = ab;
+        // bf16 scores, and the row sum of exactly those rounded values
+        const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
+        rs += (lo_bf16_f32(p01) + hi_bf16_f32(p01)) + (lo_bf16_f32(p23) + hi_bf16_f32(p23));
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        lds<u32x2>(sm, LY::a_off + 2 * (q * CP + 16 * c + 4 * g4)) = u32x2{p01, p23};
       }
       if ((w & 1) == 0) lds<bf16x4>(sm, LY::a_off + 2 * (q * CP + 16 * (w + 1) + 4 * g4)) = bf16x4{};
       float zd = 0.f;
@@ -590,6 +622,14 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
                              lane, w);
     z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
     lds_barrier();
+  };
+  if constexpr (DEPTH == 2) {
+    for (int ci = 0; ci < nch; ci += 2) {
+      step(raw0, ci);
+      step(raw1, ci + 1);
+    }
+  } else {
+    for (int ci = 0; ci < nch; ++ci) step(raw0, ci);
   }
 
   if (a.S_out != nullptr && s == a.P - 1) {

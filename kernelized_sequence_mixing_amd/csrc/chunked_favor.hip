@@ -34,11 +34,27 @@ static la_status by_dv(const FwdPlan& p) {
   return LA_ERR_UNSUPPORTED;
 }
 
-template <int R>
-static int favor_lds(int dv) {
-  if (dv == 64) return FavorFwdLayout<R, 64>::bytes;
-  if (dv == 128 && R * 128 <= 16384) return FavorFwdLayout<R, 128>::bytes;
+template <int R, int GATE, int E>
+static int favor_lds_dk(int dk) {
+  using LY = FavorFwdLayout<R, E, GATE>;
+  switch (dk) {
+    case 32: return LY::template bytes_dk<32>;
+    case 64: return LY::template bytes_dk<64>;
+    case 128: return LY::template bytes_dk<128>;
+  }
   return 0;
+}
+
+template <int R, int GATE>
+static int favor_lds_gate(int dv, int dk) {
+  if (dv == 64) return favor_lds_dk<R, GATE, 64>(dk);
+  if (dv == 128 && R * 128 <= 16384) return favor_lds_dk<R, GATE, 128>(dk);
+  return 0;
+}
+
+template <int R>
+static int favor_lds(int dv, int dk, int gate) {
+  return gate == GT_DECAY ? favor_lds_gate<R, GT_DECAY>(dv, dk) : favor_lds_gate<R, GT_NONE>(dv, dk);
 }
 
 template <int R, int GATE>
@@ -60,12 +76,12 @@ static int elu_lds(int dv, int gate) {
 
 static_assert(GT_NONE == LA_GATE_NONE && GT_DECAY == LA_GATE_DECAY && GT_GLA == LA_GATE_GLA, "gate codes");
 
-int causal_output_lds_bytes(int fmap, int r, int dv, int gate) {
+int causal_output_lds_bytes(int fmap, int r, int dv, int dk, int gate) {
   if (fmap == LA_FMAP_FAVOR) {
     switch (r) {
-      case 64: return favor_lds<64>(dv);
-      case 128: return favor_lds<128>(dv);
-      case 256: return favor_lds<256>(dv);
+      case 64: return favor_lds<64>(dv, dk, gate);
+      case 128: return favor_lds<128>(dv, dk, gate);
+      case 256: return favor_lds<256>(dv, dk, gate);
     }
     return 0;
   }

@@ -8,11 +8,19 @@
 //     (x = hi + lo, hi = bf16(x), lo = bf16(x - hi)), and products take the
 //     three significant terms hi*hi + lo*hi + hi*lo, so scores, inter-chunk
 //     reads and state updates keep ~16 significant bits on the matrix cores;
-//   * the feature axis is processed in blocks of up to 128 features, so the
-//     hi/lo tiles of one block fit in LDS; everything that contracts over the
-//     features accumulates across blocks in registers.
+//   * the feature axis is processed in blocks of 64 features: the hi/lo tiles
+//     of one block are the only per-block LDS, which keeps a workgroup near
+//     57 KB so two of them share a CU. Everything that contracts over the
+//     features (scores, inter-chunk product, z . phi(q)) accumulates across
+//     blocks in registers.
 // The projection X w^T runs on the matrix cores (exact bf16 products, fp32
 // accumulation); |x|^2/2 and ln(r)/2 are subtracted before the exponential.
+//
+// LDS tiles are row-major [token][column]. Operands that contract over tokens
+// (phi(k)^T in the state update, V^T in the intra-chunk product) come from
+// them by transpose reads (tr_operand). The chunk's raw X rows are staged in
+// LDS once (each wave loads a quarter of them) with the per-token shift
+// |x|^2/2 + ln(r)/2, so the register prefetch of the next chunk stays small.
 #pragma once
 
 #include "chunked.hpp"
@@ -21,57 +29,92 @@ namespace la {
 
 template <int R>
 struct FavorBlock {
-  static constexpr int FB = R < 128 ? R : 128;  // features per block
-  static constexpr int NFB = R / FB;            // blocks
-  static constexpr int RPB = FB + 8;            // row stride of [t][feature] tiles
-  static constexpr int MT = FB / 64;            // 16-feature tiles per wave per block
+  static constexpr int FB = 64;        // features per block
+  static constexpr int NFB = R / FB;   // blocks
+  static constexpr int FP = FB + 8;    // row stride of the [token][feature] tiles
+  static constexpr int FT = FB / 16;   // 16-feature tiles per block
 };
 
-template <int R, int E>
+// Staged raw rows of one side: X [64][DK + 8] bf16 and the shift [64] fp32.
+template <int DK>
+struct XStage {
+  static constexpr int XP = DK + 8;
+  static constexpr int bytes = kChunk * XP * 2 + kChunk * 4;
+  static constexpr int sh = kChunk * XP * 2;  // offset of the shifts
+};
+
+// Output pass. kwh/kwl (RetNet only) hold the decay-weighted key features of
+// the state update; kh/kl hold the unweighted ones of the scores.
+template <int R, int E, int GATE>
 struct FavorFwdLayout {
   using F = FavorBlock<R>;
+  static constexpr int EP = E + 8;
+  static constexpr int TILE = kChunk * F::FP * 2;
   static constexpr int qh_off = 0;
-  static constexpr int ql_off = qh_off + kChunk * F::RPB * 2;
-  static constexpr int kh_off = ql_off + kChunk * F::RPB * 2;
-  static constexpr int kl_off = kh_off + kChunk * F::RPB * 2;
-  static constexpr int kth_off = kl_off + kChunk * F::RPB * 2;
-  static constexpr int ktl_off = kth_off + F::FB * CP * 2;
-  static constexpr int vt_off = ktl_off + F::FB * CP * 2;
-  static constexpr int a_off = vt_off + E * CP * 2;
+  static constexpr int ql_off = qh_off + TILE;
+  static constexpr int kh_off = ql_off + TILE;
+  static constexpr int kl_off = kh_off + TILE;
+  static constexpr int kwh_off = kl_off + TILE;
+  static constexpr int kwl_off = kwh_off + (GATE == GT_DECAY ? TILE : 0);
+  static constexpr int v_off = kwl_off + (GATE == GT_DECAY ? TILE : 0);
+  static constexpr int a_off = v_off + kChunk * EP * 2;
   static constexpr int z_off = a_off + kChunk * CP * 2;
-  static constexpr int den_off = z_off + R * 4;
-  static constexpr int bytes = den_off + kChunk * 4;
+  static constexpr int rsp_off = z_off + R * 4;     // [4][64] partial score row sums
+  static constexpr int zdp_off = rsp_off + 4 * kChunk * 4;  // [64] phi(q) . z
+  static constexpr int xq_off = zdp_off + kChunk * 4;       // XStage<DK> of the queries
+  template <int DK>
+  static constexpr int bytes_dk = xq_off + 2 * XStage<DK>::bytes;
 };
 
+// Segment-state pass: kh/kl hold the (decay-weighted) key features.
 template <int R, int E>
 struct FavorSegLayout {
   using F = FavorBlock<R>;
-  static constexpr int kth_off = 0;
-  static constexpr int ktl_off = kth_off + F::FB * CP * 2;
-  static constexpr int vt_off = ktl_off + F::FB * CP * 2;
-  static constexpr int bytes = vt_off + E * CP * 2;
+  static constexpr int EP = E + 8;
+  static constexpr int kh_off = 0;
+  static constexpr int kl_off = kh_off + kChunk * F::FP * 2;
+  static constexpr int v_off = kl_off + kChunk * F::FP * 2;
+  static constexpr int xk_off = v_off + kChunk * EP * 2;  // XStage<DK> of the keys
+  template <int DK>
+  static constexpr int bytes_dk = xk_off + XStage<DK>::bytes;
 };
 
-__device__ __forceinline__ void split2(float x, bf16& hi, bf16& lo) {
-  hi = (bf16)x;
-  lo = (bf16)(x - to_f32(hi));
+// Stage this wave's quarter of the raw rows (tokens 16 w .. 16 w + 15) and
+// their shifts |x|^2/2 + ln(r)/2.
+template <int R, int DK>
+__device__ __forceinline__ void favor_stage_x(const bf16x8 (&x)[DK / 32], char* sm, int x_off, int lane, int w) {
+  using X = XStage<DK>;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int t = 16 * w + c16;
+  float ss = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks) {
+    lds<bf16x8>(sm, x_off + 2 * (t * X::XP + 32 * ks + 8 * g4)) = x[ks];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float xv = to_f32(x[ks][u]);
+      ss += xv * xv;
+    }
+  }
+  ss = sum_over_groups(ss);
+  if (g4 == 0) lds<float>(sm, x_off + X::sh + 4 * t) = 0.5f * ss + 0.5f * __logf(float(R));
 }
 
+// hi/lo bf16 pairs of four floats (packed two per dword).
 __device__ __forceinline__ void split4(const float (&f)[4], bf16x4& hi, bf16x4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bf16 h, l;
-    split2(f[i], h, l);
-    hi[i] = h;
-    lo[i] = l;
-  }
+  const unsigned h01 = pack2_bits(f[0], f[1]), h23 = pack2_bits(f[2], f[3]);
+  const unsigned l01 = pack2_bits(f[0] - lo_bf16_f32(h01), f[1] - hi_bf16_f32(h01));
+  const unsigned l23 = pack2_bits(f[2] - lo_bf16_f32(h23), f[3] - hi_bf16_f32(h23));
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  hi = __builtin_bit_cast(bf16x4, u32x2{h01, h23});
+  lo = __builtin_bit_cast(bf16x4, u32x2{l01, l23});
 }
 
 // hi/lo bf16 image of 8 state rows (two 4-row halves of adjacent 16-row tiles)
 // in the k-slot order of the inter-chunk product.
 __device__ __forceinline__ void split_state_op(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
   bf16x4 ha, la, hb, lb;
-  float fa[4] = {a[0], a[1], a[2], a[3]}, fb[4] = {b[0], b[1], b[2], b[3]};
+  const float fa[4] = {a[0], a[1], a[2], a[3]}, fb[4] = {b[0], b[1], b[2], b[3]};
   split4(fa, ha, la);
   split4(fb, hb, lb);
   hi = cat8(ha, hb);
@@ -86,96 +129,82 @@ __device__ __forceinline__ f32x4 mfma3(const bf16x8& ah, const bf16x8& al, const
   return c;
 }
 
-// FAVOR+ features of one block of one side of a chunk, as hi/lo pairs.
-// Queries: row-major tiles (qh, ql). Keys: row-major tiles (kh, kl) when ROWS,
-// and transposed tiles (kth, ktl) carrying the RetNet weight gamma^(L-1-t).
-template <int R, int DK, int GATE, bool IS_K, bool ROWS>
-__device__ __forceinline__ void favor_block_side(const bf16x8 (&x)[4 * (DK / 32)], const bf16* omega, int fb, int L,
-                                                 float lg2gam, char* sm, int hi_off, int lo_off, int kth_off,
-                                                 int ktl_off, int lane, int w) {
+__device__ __forceinline__ bf16x4 keep_if(bool ok, bf16x4 x) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const unsigned m = ok ? 0xffffffffu : 0u;
+  return __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, x) & m);
+}
+
+// FAVOR+ features of one side of a chunk for this wave's 16 features of block
+// fb (block features 16 w .. 16 w + 15), as hi/lo pairs in row-major
+// [token][feature] tiles. Keys past the chunk's valid rows are zero. With
+// WEIGHTED, keys are also written multiplied by gamma^(L-1-t) (RetNet state
+// update) into (wh_off, wl_off); with ONLY_WEIGHTED that is the only copy.
+template <int R, int DK, bool IS_K, bool WEIGHTED, bool ONLY_WEIGHTED>
+__device__ __forceinline__ void favor_project(int x_off, const bf16* omega, int fb, int L, float lg2gam, char* sm,
+                                              int hi_off, int lo_off, int wh_off, int wl_off, int lane, int w) {
   using F = FavorBlock<R>;
-  constexpr int KS = DK / 32, RPB = F::RPB;
+  using X = XStage<DK>;
+  constexpr int KS = DK / 32, FP = F::FP;
   const int g4 = lane >> 4, c16 = lane & 15;
-  // omega fragments of this wave's features in block fb (32 KB total: cache-resident)
-  bf16x8 om[F::MT][KS];
+  // omega rows of this wave's features (the whole omega is 32 KB or less: cache-resident)
+  bf16x8 om[KS];
 #pragma unroll
-  for (int mt = 0; mt < F::MT; ++mt)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      om[mt][ks] = *reinterpret_cast<const bf16x8*>(
-          omega + (long long)(fb * F::FB + w * (F::FB / 4) + 16 * mt + c16) * DK + 32 * ks + 8 * g4);
-  const float half_log_r = 0.5f * __logf(float(R));
+  for (int ks = 0; ks < KS; ++ks)
+    om[ks] = *reinterpret_cast<const bf16x8*>(omega + (long long)(fb * F::FB + 16 * w + c16) * DK + 32 * ks + 8 * g4);
+  const int f0 = 16 * w + 4 * g4;  // block-local features f0 .. f0 + 3 of this lane
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    float ss = 0.f;
+    const int t = 16 * tt + c16;
+    const float shift = lds<float>(sm, x_off + X::sh + 4 * t);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
+      acc = mfma16(om[ks], lds<bf16x8>(sm, x_off + 2 * (t * X::XP + 32 * ks + 8 * g4)), acc);
+    // acc[i] = P[token t][block feature f0 + i]
+    float f[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float xv = to_f32(x[tt * KS + ks][u]);
-        ss += xv * xv;
-      }
-    const float shift = 0.5f * sum_over_groups(ss) + half_log_r;
-    const int t = 16 * tt + c16;
-    const bool tok_ok = t < L;
-    float decay_k = 1.f;
-    if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(L - 1 - t) * lg2gam);
-#pragma unroll
-    for (int mt = 0; mt < F::MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16(om[mt][ks], x[tt * KS + ks], acc);
-      // acc[i] = P[token t][block feature ml + i]
-      const int ml = w * (F::FB / 4) + 16 * mt + 4 * g4;
-      float f[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[i] = __expf(acc[i] - shift);
-        if (IS_K) f[i] = keep_if(tok_ok, f[i]);
-      }
-      if constexpr (!IS_K || ROWS) {
-        bf16x4 h, l;
-        split4(f, h, l);
-        lds<bf16x4>(sm, hi_off + 2 * (t * RPB + ml)) = h;
-        lds<bf16x4>(sm, lo_off + 2 * (t * RPB + ml)) = l;
-      }
-      if constexpr (IS_K) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16 h, l;
-          split2(f[i] * decay_k, h, l);
-          lds<bf16>(sm, kth_off + 2 * ((ml + i) * CP + t)) = h;
-          lds<bf16>(sm, ktl_off + 2 * ((ml + i) * CP + t)) = l;
-        }
-      }
+    for (int i = 0; i < 4; ++i) f[i] = __expf(acc[i] - shift);
+    const bool ok = !IS_K || t < L;
+    if constexpr (!ONLY_WEIGHTED) {
+      bf16x4 h, l;
+      split4(f, h, l);
+      lds<bf16x4>(sm, hi_off + 2 * (t * FP + f0)) = keep_if(ok, h);
+      lds<bf16x4>(sm, lo_off + 2 * (t * FP + f0)) = keep_if(ok, l);
     }
+    if constexpr (WEIGHTED) {
+      const float wt = exp2f(float(L - 1 - t) * lg2gam);
+      float fw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fw[i] = f[i] * wt;
+      bf16x4 h, l;
+      split4(fw, h, l);
+      lds<bf16x4>(sm, wh_off + 2 * (t * FP + f0)) = keep_if(ok, h);
+      lds<bf16x4>(sm, wl_off + 2 * (t * FP + f0)) = keep_if(ok, l);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one token tile at a time: bounded live registers
   }
 }
 
-// V transposed into LDS; rows at or past L (the chunk's valid tokens) are zero.
+// V rows of the chunk into a row-major [token][E + 8] tile (lane = token,
+// wave w holds columns [w E/4, (w+1) E/4)). Rows past the end need no mask:
+// their key features are zero and their scores are masked.
 template <int E>
-__device__ __forceinline__ void write_vt(const bf16x8 (&v)[E / 32], int L, char* sm, int vt_off, int lane, int w) {
-  constexpr int EV = E / 4;
-  const bool valid = lane < L;
+__device__ __forceinline__ void favor_write_v(const bf16x8 (&v)[E / 32], char* sm, int v_off, int lane, int w) {
+  constexpr int EV = E / 4, EP = E + 8;
 #pragma unroll
-  for (int j = 0; j < EV / 8; ++j) {
-    const bf16x8 vv = keep_if(valid, v[j]);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) lds<bf16>(sm, vt_off + 2 * ((w * EV + 8 * j + u) * CP + lane)) = vv[u];
-  }
+  for (int j = 0; j < EV / 8; ++j) lds<bf16x8>(sm, v_off + 2 * (lane * EP + w * EV + 8 * j)) = v[j];
 }
 
-// S rows of feature block fb (all of them, wave's value columns) <- g S + K^^T V
-// with K^ as a hi/lo pair, and this wave's z tiles of the block <- g z + K^^T 1
-// (z is the state column of a constant-1 value). Wave w owns block-local z
-// tiles rt = w ZT .. w ZT + ZT - 1; lane (g, c) holds z[16 rt + 4 g + i].
+// S rows of feature block fb (the wave's value columns) <- g S + K^^T V with
+// K^ as a hi/lo pair, and the wave's z tile of the block <- g z + K^^T 1 (z
+// is the state column of a constant-1 value). Wave w owns block-local z tile
+// w: lane (g, c) holds z[64 fb + 16 w + 4 g + i] in Zb.
 template <int R, int E>
-__device__ __forceinline__ void favor_state_block(f32x4 (&S)[R / 16][E / 64], f32x4 (&Zb)[FavorBlock<R>::FB / 64],
-                                                  int fb, char* sm, int kth_off, int ktl_off, int vt_off,
-                                                  float gscale, int lane, int w) {
+__device__ __forceinline__ void favor_state_block(f32x4 (&S)[R / 16][E / 64], f32x4& Zb, int fb, char* sm, int kh_off,
+                                                  int kl_off, int v_off, float gscale, int lane, int w) {
   using F = FavorBlock<R>;
-  constexpr int ZT = F::FB / 64;
-  const int g4 = lane >> 4, c16 = lane & 15;
+  constexpr int FP = F::FP, EP = E + 8;
   const int ebase = w * (E / 4);
   bf16x8 ones;
 #pragma unroll
@@ -184,19 +213,18 @@ __device__ __forceinline__ void favor_state_block(f32x4 (&S)[R / 16][E / 64], f3
 #pragma unroll
   for (int eb = 0; eb < E / 64; ++eb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      vb[eb][ks] = lds<bf16x8>(sm, vt_off + 2 * ((ebase + 16 * eb + c16) * CP + 32 * ks + 8 * g4));
+    for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_operand(sm, v_off, EP, 32 * ks, ebase + 16 * eb, lane);
 #pragma unroll
-  for (int rt = 0; rt < F::FB / 16; ++rt) {
+  for (int rt = 0; rt < F::FT; ++rt) {
     bf16x8 kh[2], kl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      kh[ks] = lds<bf16x8>(sm, kth_off + 2 * ((16 * rt + c16) * CP + 32 * ks + 8 * g4));
-      kl[ks] = lds<bf16x8>(sm, ktl_off + 2 * ((16 * rt + c16) * CP + 32 * ks + 8 * g4));
+      kh[ks] = tr_operand(sm, kh_off, FP, 32 * ks, 16 * rt, lane);
+      kl[ks] = tr_operand(sm, kl_off, FP, 32 * ks, 16 * rt, lane);
     }
 #pragma unroll
     for (int eb = 0; eb < E / 64; ++eb) {
-      f32x4 st = S[fb * (F::FB / 16) + rt][eb];
+      f32x4 st = S[fb * F::FT + rt][eb];
 #pragma unroll
       for (int i = 0; i < 4; ++i) st[i] *= gscale;
 #pragma unroll
@@ -204,10 +232,10 @@ __device__ __forceinline__ void favor_state_block(f32x4 (&S)[R / 16][E / 64], f3
         st = mfma16(kh[ks], vb[eb][ks], st);
         st = mfma16(kl[ks], vb[eb][ks], st);
       }
-      S[fb * (F::FB / 16) + rt][eb] = st;
+      S[fb * F::FT + rt][eb] = st;
     }
-    if (rt / ZT == w) {
-      f32x4 zt = Zb[rt % ZT];
+    if (rt == w) {
+      f32x4 zt = Zb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) zt[i] *= gscale;
 #pragma unroll
@@ -215,39 +243,38 @@ __device__ __forceinline__ void favor_state_block(f32x4 (&S)[R / 16][E / 64], f3
         zt = mfma16(kh[ks], ones, zt);
         zt = mfma16(kl[ks], ones, zt);
       }
-      Zb[rt % ZT] = zt;
+      Zb = zt;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // z tiles (all blocks) of wave w to / from a flat [R] fp32 array.
 template <int R>
-__device__ __forceinline__ void favor_z_store(const f32x4 (&Z)[FavorBlock<R>::NFB][FavorBlock<R>::FB / 64],
-                                              float* dst, int lane, int w) {
-  using F = FavorBlock<R>;
-  constexpr int ZT = F::FB / 64;
+__device__ __forceinline__ void favor_z_store(const f32x4 (&Z)[FavorBlock<R>::NFB], float* dst, int lane, int w) {
   if ((lane & 15) == 0) {
 #pragma unroll
-    for (int fb = 0; fb < F::NFB; ++fb)
+    for (int fb = 0; fb < FavorBlock<R>::NFB; ++fb)
 #pragma unroll
-      for (int j = 0; j < ZT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[fb * F::FB + 16 * (w * ZT + j) + 4 * (lane >> 4) + i] = Z[fb][j][i];
+      for (int i = 0; i < 4; ++i) dst[64 * fb + 16 * w + 4 * (lane >> 4) + i] = Z[fb][i];
   }
 }
 
 template <int R>
-__device__ __forceinline__ void favor_z_load(f32x4 (&Z)[FavorBlock<R>::NFB][FavorBlock<R>::FB / 64],
-                                             const float* src, int lane, int w) {
-  using F = FavorBlock<R>;
-  constexpr int ZT = F::FB / 64;
+__device__ __forceinline__ void favor_z_load(f32x4 (&Z)[FavorBlock<R>::NFB], const float* src, int lane, int w) {
 #pragma unroll
-  for (int fb = 0; fb < F::NFB; ++fb)
+  for (int fb = 0; fb < FavorBlock<R>::NFB; ++fb)
 #pragma unroll
-    for (int j = 0; j < ZT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Z[fb][j][i] = src != nullptr ? src[fb * F::FB + 16 * (w * ZT + j) + 4 * (lane >> 4) + i] : 0.f;
+    for (int i = 0; i < 4; ++i) Z[fb][i] = src != nullptr ? src[64 * fb + 16 * w + 4 * (lane >> 4) + i] : 0.f;
+}
+
+// The ten lower-triangle 16x16 score tiles (query tile qi, key tile kj <= qi)
+// dealt to the four waves as 3, 3, 2, 2 tiles, no wave holding two tiles of
+// the same query rows: slot s of wave w is tile s * 4 + w of the row-major
+// enumeration (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3).
+__device__ __forceinline__ int score_tile_qi(int idx) { return idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3; }
+__device__ __forceinline__ int score_tile_kj(int idx) {
+  return idx - (idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 3 : 6);
 }
 
 // ---------------------------------------------------------------------------
@@ -258,8 +285,8 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FavorSegLayout<R, E>;
   using F = FavorBlock<R>;
-  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
-  const int g4 = lane >> 4, c16 = lane & 15;
+  const int lane0 = lane_id(), w = wave_id();
+  const int lane = lane0, g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
@@ -275,22 +302,28 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
     for (int eb = 0; eb < E / 64; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 Z[F::NFB][F::FB / 64];
+  f32x4 Z[F::NFB];
   favor_z_load<R>(Z, nullptr, lane, w);
 
   RawChunk<R, E, DK, FM_FAVOR, GT_NONE, false> raw;
-  raw.load(a, tok0, t_begin, lane, w);
+  raw.load(a, tok0, t_begin, t_end, lane, w);
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int L = min(kChunk, a.n - t0);
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+    favor_stage_x<R, DK>(raw.xk, sm, LY::xk_off, lane, w);
+    favor_write_v<E>(raw.v, sm, LY::v_off, lane, w);
+    // the raw registers are free: the next chunk's loads fly during this one
+    raw.load(a, tok0, t0 + kChunk, t_end, lane, w);
+    lds_barrier();
 #pragma unroll
     for (int fb = 0; fb < F::NFB; ++fb) {
-      favor_block_side<R, DK, GATE, true, false>(raw.xk, a.omega, fb, L, lg2gam, sm, 0, 0, LY::kth_off, LY::ktl_off,
-                                                 lane, w);
-      if (fb == 0) write_vt<E>(raw.v, L, sm, LY::vt_off, lane, w);
-      if (fb == F::NFB - 1 && t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
+      const int lane = opaque_lane(lane0);
+      // pass 1 keeps only the keys of the state update (decay-weighted for RetNet)
+      favor_project<R, DK, true, GATE == GT_DECAY, GATE == GT_DECAY>(LY::xk_off, a.omega, fb, L, lg2gam, sm,
+                                                                     LY::kh_off, LY::kl_off, LY::kh_off, LY::kl_off,
+                                                                     lane, w);
       lds_barrier();
-      favor_state_block<R, E>(S, Z[fb], fb, sm, LY::kth_off, LY::ktl_off, LY::vt_off, gsc, lane, w);
+      favor_state_block<R, E>(S, Z[fb], fb, sm, LY::kh_off, LY::kl_off, LY::v_off, gsc, lane, w);
       lds_barrier();
     }
   }
@@ -309,13 +342,13 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
 // Pass 3 (FAVOR+): outputs of one segment from its chained state.
 // ---------------------------------------------------------------------------
 template <int R, int E, int DK, int GATE>
-__global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
+__global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  using LY = FavorFwdLayout<R, E>;
+  using LY = FavorFwdLayout<R, E, GATE>;
   using F = FavorBlock<R>;
-  constexpr int RPB = F::RPB, NEB = E / 64, KPB = F::FB / 32;
-  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
-  const int g4 = lane >> 4, c16 = lane & 15;
+  constexpr int FP = F::FP, EP = LY::EP, NEB = E / 64, KPB = F::FB / 32;
+  const int lane0 = lane_id(), w = wave_id(), tid = threadIdx.x;
+  const int lane = lane0, g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
@@ -327,7 +360,7 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
   if constexpr (GATE == GT_DECAY) lg2gam = log2f(a.gamma[h]);
 
   f32x4 S[R / 16][NEB];
-  f32x4 Z[F::NFB][F::FB / 64];
+  f32x4 Z[F::NFB];
   if (a.S_in != nullptr) {
     const float* Sp = a.S_in + bh * a.in_head + s * a.in_seg;
 #pragma unroll
@@ -344,120 +377,154 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
   }
   favor_z_load<R>(Z, a.S_in != nullptr ? a.z_in + (bh * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
   favor_z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
+  // partial row sums of query tiles this wave holds no score tile of stay zero
+  lds<float>(sm, LY::rsp_off + 4 * tid) = 0.f;
 
+  // this wave's score tiles
+  const int nslot = w < 2 ? 3 : 2;
+  int sqi[3], skj[3];
+#pragma unroll
+  for (int sl = 0; sl < 3; ++sl) {
+    const int idx = min(4 * sl + w, 9);
+    sqi[sl] = score_tile_qi(idx);
+    skj[sl] = score_tile_kj(idx);
+  }
+
+  constexpr int xq_off = LY::xq_off, xk_off = LY::xq_off + XStage<DK>::bytes;
   RawChunk<R, E, DK, FM_FAVOR, GT_NONE, true> raw;
-  raw.load(a, tok0, t_begin, lane, w);
+  raw.load(a, tok0, t_begin, t_end, lane, w);
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int L = min(kChunk, a.n - t0);
-    const int q_own = 16 * w + c16;  // this lane's query row in the score phase
-    f32x4 sacc[4];
+    favor_stage_x<R, DK>(raw.xq, sm, xq_off, lane, w);
+    favor_stage_x<R, DK>(raw.xk, sm, xk_off, lane, w);
+    favor_write_v<E>(raw.v, sm, LY::v_off, lane, w);
+    // the raw registers are free: the next chunk's loads fly during this one
+    raw.load(a, tok0, t0 + kChunk, t_end, lane, w);
+    lds_barrier();
+    f32x4 sacc[3];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < 3; ++sl) sacc[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 oacc[4][NEB];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) oacc[qt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float zd = 0.f;
+    float zd = 0.f;  // phi(q) . z_prev for query 16 w + c over this lane's k-slots
 
 #pragma unroll
     for (int fb = 0; fb < F::NFB; ++fb) {
+      const int lane = opaque_lane(lane0);
+      const int g4 = lane >> 4, c16 = lane & 15;
       const bool last = fb == F::NFB - 1;
-      favor_block_side<R, DK, GATE, false, false>(raw.xq, a.omega, fb, L, lg2gam, sm, LY::qh_off, LY::ql_off, 0, 0,
-                                                  lane, w);
-      favor_block_side<R, DK, GATE, true, true>(raw.xk, a.omega, fb, L, lg2gam, sm, LY::kh_off, LY::kl_off,
-                                                LY::kth_off, LY::ktl_off, lane, w);
-      if (fb == 0) write_vt<E>(raw.v, L, sm, LY::vt_off, lane, w);
-      if (last && t0 + kChunk < t_end) raw.load(a, tok0, t0 + kChunk, lane, w);
+      favor_project<R, DK, false, false, false>(xq_off, a.omega, fb, L, lg2gam, sm, LY::qh_off, LY::ql_off, 0, 0,
+                                                lane, w);
+      favor_project<R, DK, true, GATE == GT_DECAY, false>(xk_off, a.omega, fb, L, lg2gam, sm, LY::kh_off, LY::kl_off,
+                                                          LY::kwh_off, LY::kwl_off, lane, w);
       lds_barrier();
 
-      // ---- scores over this block's features: A^T tiles = K~_c Q~_w^T
-      {
-        bf16x8 qh[KPB], ql[KPB];
+      // ---- scores over this block's features: A^T tiles = K~_kj Q~_qi^T
 #pragma unroll
-        for (int ks = 0; ks < KPB; ++ks) {
-          qh[ks] = lds<bf16x8>(sm, LY::qh_off + 2 * (q_own * RPB + 32 * ks + 8 * g4));
-          ql[ks] = lds<bf16x8>(sm, LY::ql_off + 2 * (q_own * RPB + 32 * ks + 8 * g4));
-        }
+      for (int sl = 0; sl < 3; ++sl) {
+        if (sl < nslot) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (c <= w) {
-#pragma unroll
-            for (int ks = 0; ks < KPB; ++ks) {
-              const int ko = 2 * ((16 * c + c16) * RPB + 32 * ks + 8 * g4);
-              sacc[c] = mfma3(lds<bf16x8>(sm, LY::kh_off + ko), lds<bf16x8>(sm, LY::kl_off + ko), qh[ks], ql[ks],
-                              sacc[c]);
-            }
+          for (int ks = 0; ks < KPB; ++ks) {
+            const int ko = 2 * ((16 * skj[sl] + c16) * FP + 32 * ks + 8 * g4);
+            const int qo = 2 * ((16 * sqi[sl] + c16) * FP + 32 * ks + 8 * g4);
+            sacc[sl] = mfma3(lds<bf16x8>(sm, LY::kh_off + ko), lds<bf16x8>(sm, LY::kl_off + ko),
+                             lds<bf16x8>(sm, LY::qh_off + qo), lds<bf16x8>(sm, LY::ql_off + qo), sacc[sl]);
           }
         }
-#pragma unroll
-        for (int ks = 0; ks < KPB; ++ks)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            zd += (to_f32(qh[ks][j]) + to_f32(ql[ks][j])) *
-                  lds<float>(sm, LY::z_off + 4 * (fb * F::FB + 32 * ks + 8 * g4 + j));
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (last) {
-        float rs = 0.f;
+      __builtin_amdgcn_sched_barrier(0);  // phases stay apart: bounded register live ranges
+      // ---- phi(q) . z_prev for query tile w
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (c <= w) {
-            bf16x4 ab;
+      for (int ks = 0; ks < KPB; ++ks) {
+        const int qo = 2 * ((16 * w + c16) * FP + 32 * ks + 8 * g4);
+        const bf16x8 qh = lds<bf16x8>(sm, LY::qh_off + qo), ql = lds<bf16x8>(sm, LY::ql_off + qo);
+        const f32x4 z0 = lds<f32x4>(sm, LY::z_off + 4 * (64 * fb + 32 * ks + 8 * g4));
+        const f32x4 z1 = lds<f32x4>(sm, LY::z_off + 4 * (64 * fb + 32 * ks + 8 * g4 + 4));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = 16 * c + 4 * g4 + i;
-              float v = sacc[c][i];
-              if (c == w && key > q_own) v = 0.f;  // only the diagonal tile straddles the mask
-              if constexpr (GATE == GT_DECAY) v *= exp2f(float(q_own - key) * lg2gam);
-              ab[i] = (bf16)v;
-              rs += to_f32(ab[i]);
-            }
-            lds<bf16x4>(sm, LY::a_off + 2 * (q_own * CP + 16 * c + 4 * g4)) = ab;
-          }
-        }
-        if ((w & 1) == 0) lds<bf16x4>(sm, LY::a_off + 2 * (q_own * CP + 16 * (w + 1) + 4 * g4)) = bf16x4{};
-        rs = sum_over_groups(rs);
-        float zdt = sum_over_groups(zd);
-        if constexpr (GATE == GT_DECAY) zdt *= exp2f(float(q_own + 1) * lg2gam);
-        if (g4 == 0) lds<float>(sm, LY::den_off + 4 * q_own) = rs + zdt + a.eps;
-        lds_barrier();
+        for (int j = 0; j < 8; ++j) zd += (to_f32(qh[j]) + to_f32(ql[j])) * (j < 4 ? z0[j] : z1[j - 4]);
       }
 
+      __builtin_amdgcn_sched_barrier(0);
       // ---- inter-chunk product over this block's features: O^T += S^T Q^^T
+      {
+        bf16x8 sh[KPB][NEB], slo[KPB][NEB];
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        const int q = 16 * qt + c16;
-        bf16x8 qbh[KPB], qbl[KPB];
+        for (int p = 0; p < KPB; ++p)
 #pragma unroll
-        for (int p = 0; p < KPB; ++p) {
-          const int o0 = 2 * (q * RPB + 32 * p + 4 * g4), o1 = 2 * (q * RPB + 32 * p + 16 + 4 * g4);
-          qbh[p] = cat8(lds<bf16x4>(sm, LY::qh_off + o0), lds<bf16x4>(sm, LY::qh_off + o1));
-          qbl[p] = cat8(lds<bf16x4>(sm, LY::ql_off + o0), lds<bf16x4>(sm, LY::ql_off + o1));
-        }
+          for (int eb = 0; eb < NEB; ++eb)
+            split_state_op(S[fb * F::FT + 2 * p][eb], S[fb * F::FT + 2 * p + 1][eb], sh[p][eb], slo[p][eb]);
 #pragma unroll
-        for (int eb = 0; eb < NEB; ++eb)
+        for (int qt = 0; qt < 4; ++qt) {
+          const int q = 16 * qt + c16;
 #pragma unroll
           for (int p = 0; p < KPB; ++p) {
-            bf16x8 sh, sl;
-            const int rt = fb * (F::FB / 16) + 2 * p;
-            split_state_op(S[rt][eb], S[rt + 1][eb], sh, sl);
-            oacc[qt][eb] = mfma3(sh, sl, qbh[p], qbl[p], oacc[qt][eb]);
+            const int o0 = 2 * (q * FP + 32 * p + 4 * g4), o1 = 2 * (q * FP + 32 * p + 16 + 4 * g4);
+            const bf16x8 qbh = cat8(lds<bf16x4>(sm, LY::qh_off + o0), lds<bf16x4>(sm, LY::qh_off + o1));
+            const bf16x8 qbl = cat8(lds<bf16x4>(sm, LY::ql_off + o0), lds<bf16x4>(sm, LY::ql_off + o1));
+#pragma unroll
+            for (int eb = 0; eb < NEB; ++eb) oacc[qt][eb] = mfma3(sh[p][eb], slo[p][eb], qbh, qbl, oacc[qt][eb]);
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 
-      // ---- carry the state rows of this block past the chunk
+      // ---- carry the state rows of this block past the chunk (z is
+      // published after the chunk's last barrier: other waves still read the
+      // old values in later blocks)
+      __builtin_amdgcn_sched_barrier(0);
       const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-      // z of this block is published after the chunk's last barrier: other
-      // waves may still be reading the old values in this block's score phase.
-      favor_state_block<R, E>(S, Z[fb], fb, sm, LY::kth_off, LY::ktl_off, LY::vt_off, gsc, lane, w);
+      favor_state_block<R, E>(S, Z[fb], fb, sm, GATE == GT_DECAY ? LY::kwh_off : LY::kh_off,
+                              GATE == GT_DECAY ? LY::kwl_off : LY::kl_off, LY::v_off, gsc, lane, w);
 
+      __builtin_amdgcn_sched_barrier(0);
       if (last) {
+        // ---- masked bf16 scores, their partial row sums, phi(q) . z
+#pragma unroll
+        for (int sl = 0; sl < 3; ++sl) {
+          if (sl < nslot) {
+            const int q = 16 * sqi[sl] + c16;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = 16 * skj[sl] + 4 * g4 + i;
+              v[i] = sacc[sl][i];
+              if (key > q) v[i] = 0.f;  // only the diagonal tiles straddle the mask
+              if constexpr (GATE == GT_DECAY) v[i] *= exp2f(float(q - key) * lg2gam);
+            }
+            const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            lds<u32x2>(sm, LY::a_off + 2 * (q * CP + 16 * skj[sl] + 4 * g4)) = u32x2{p01, p23};
+            const float rs =
+                sum_over_groups((lo_bf16_f32(p01) + hi_bf16_f32(p01)) + (lo_bf16_f32(p23) + hi_bf16_f32(p23)));
+            if (g4 == 0) lds<float>(sm, LY::rsp_off + 4 * (w * kChunk + q)) = rs;
+          }
+        }
+        // upper-triangle tiles read by the intra-chunk product: (0,1) and (2,3)
+        if (w >= 2) {
+          const int q = 16 * (2 * w - 4) + c16;
+          lds<bf16x4>(sm, LY::a_off + 2 * (q * CP + 16 * (2 * w - 3) + 4 * g4)) = bf16x4{};
+        }
+        {
+          float zdt = sum_over_groups(zd);
+          if constexpr (GATE == GT_DECAY) zdt *= exp2f(float(16 * w + c16 + 1) * lg2gam);
+          if (g4 == 0) lds<float>(sm, LY::zdp_off + 4 * (16 * w + c16)) = zdt;
+        }
+        lds_barrier();
+
         // ---- intra-chunk part and normalisation: O^T += V^T A^T, o = O / den
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt) {
           const int q = 16 * qt + c16;
+          const float den = (((lds<float>(sm, LY::rsp_off + 4 * q) + lds<float>(sm, LY::rsp_off + 4 * (64 + q))) +
+                              lds<float>(sm, LY::rsp_off + 4 * (128 + q))) +
+                             lds<float>(sm, LY::rsp_off + 4 * (192 + q))) +
+                            lds<float>(sm, LY::zdp_off + 4 * q) + a.eps;
           // one correctly rounded reciprocal per row; outputs are fl(O * fl(1 / den))
-          const float inv_den = 1.f / lds<float>(sm, LY::den_off + 4 * q);
+          const float inv_den = 1.f / den;
           float isc = 1.f;
           if constexpr (GATE == GT_DECAY) isc = exp2f(float(q + 1) * lg2gam);
 #pragma unroll
@@ -470,7 +537,7 @@ __global__ __launch_bounds__(256) void favor_chunk_forward(CausalArgs a) {
             }
 #pragma unroll
             for (int p2 = 0; p2 <= qt / 2; ++p2)
-              acc = mfma16(lds<bf16x8>(sm, LY::vt_off + 2 * ((e + c16) * CP + 32 * p2 + 8 * g4)),
+              acc = mfma16(tr_operand(sm, LY::v_off, EP, 32 * p2, e, lane),
                            lds<bf16x8>(sm, LY::a_off + 2 * (q * CP + 32 * p2 + 8 * g4)), acc);
             if (q < L) {
               bf16x4 o = pack4(acc[0] * inv_den, acc[1] * inv_den, acc[2] * inv_den, acc[3] * inv_den);
@@ -516,7 +583,7 @@ la_status run_causal_favor(const FwdPlan& p) {
     a1.S_out = p.ws_S;
     a1.z_out = p.ws_z;
     auto k1 = favor_segment_state<R, E, DK, GATE>;
-    constexpr int lds1 = FavorSegLayout<R, E>::bytes;
+    constexpr int lds1 = FavorSegLayout<R, E>::template bytes_dk<DK>;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
         hipSuccess)
       return LA_ERR_HIP;
@@ -537,7 +604,7 @@ la_status run_causal_favor(const FwdPlan& p) {
   a.S_out = p.S_final;
   a.z_out = p.z_final;
   auto k3 = favor_chunk_forward<R, E, DK, GATE>;
-  constexpr int lds3 = FavorFwdLayout<R, E>::bytes;
+  constexpr int lds3 = FavorFwdLayout<R, E, GATE>::template bytes_dk<DK>;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k3), hipFuncAttributeMaxDynamicSharedMemorySize, lds3) !=
       hipSuccess)
     return LA_ERR_HIP;

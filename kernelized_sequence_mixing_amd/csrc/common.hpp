@@ -33,6 +33,15 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Two floats rounded to bf16 and packed (a in the low half): one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned pack2_bits(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+// The two halves of a packed bf16 pair, widened exactly to float.
+__device__ __forceinline__ float lo_bf16_f32(unsigned p) { return __builtin_bit_cast(float, p << 16); }
+__device__ __forceinline__ float hi_bf16_f32(unsigned p) { return __builtin_bit_cast(float, p & 0xffff0000u); }
+
 // ---------------------------------------------------------------- matrix core
 
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16) on one wave.
@@ -47,7 +56,19 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 // ---------------------------------------------------------------- wave64 lanes
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// The lane index, opaque to the optimizer. Addresses derived from it inside a
+// loop body are rebuilt there (a few integer ops) instead of being hoisted out
+// of the loop and kept live in registers for its whole duration; the mask
+// restores the 0..63 range that lets constant offsets fold into instructions.
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane & 63;
+}
+// Wave index in a 256-thread workgroup. The mask gives the compiler its range
+// (readfirstlane alone hides it), so LDS addresses built from it keep their
+// constant parts in the instruction's offset field instead of in registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3; }
 
 // Sum over the four lanes {c, c+16, c+32, c+48} that share c = lane % 16.
 __device__ __forceinline__ float sum_over_groups(float x) {

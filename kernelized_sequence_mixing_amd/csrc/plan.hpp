@@ -19,7 +19,7 @@ constexpr int kNonCausalGroups = 512;
 
 // LDS bytes of the causal output-pass workgroup for this shape (0 if not built);
 // pure host arithmetic over the kernels' own layout definitions.
-int causal_output_lds_bytes(int fmap, int r, int dv, int gate);
+int causal_output_lds_bytes(int fmap, int r, int dv, int dk, int gate);
 
 struct FwdPlan {
   int B, H, n, dk, dv, r;

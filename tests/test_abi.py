@@ -83,8 +83,8 @@ int main(void) {{
     # 78.3 KB (RetNet keeps a weighted key tile) / 61.3 KB -> 2 per CU -> 512 groups
     (2, 8, 8192, 128, 128, "elu1", 128, "decay", 32, 256),    # RetNet workload
     (2, 16, 16384, 128, 128, "elu1", 128, "gla", 16, 1024),   # GLA workload
-    # FAVOR+ r=256: 126 KB -> 1 per CU
-    (1, 8, 32768, 64, 64, "favor", 256, "none", 32, 1024),    # FAVOR+ workload
+    # FAVOR+ r=256: 74.8 KB (64-feature blocks, staged inputs) -> 2 per CU -> 512 groups
+    (1, 8, 32768, 64, 64, "favor", 256, "none", 64, 512),     # FAVOR+ workload
     (1, 1, 1, 64, 64, "elu1", 64, "none", 1, 64),
     (1, 1, 65, 64, 64, "elu1", 64, "none", 2, 64),
     (600, 1, 100, 64, 64, "elu1", 64, "none", 2, 64),
