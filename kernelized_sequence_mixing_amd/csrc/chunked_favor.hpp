@@ -44,12 +44,16 @@ struct XStage {
 };
 
 // Output pass. kwh/kwl (RetNet only) hold the decay-weighted key features of
-// the state update; kh/kl hold the unweighted ones of the scores.
+// the state update; kh/kl hold the unweighted ones of the scores. zh/zl are
+// the bf16 hi/lo image of z_prev (B operand of phi(q) . z on the matrix cores).
 template <int R, int E, int GATE>
 struct FavorFwdLayout {
   using F = FavorBlock<R>;
   static constexpr int EP = E + 8;
-  static constexpr int TILE = kChunk * F::FP * 2;
+  // 16 bytes between tiles: the hi and lo halves of one row are never a
+  // multiple of 512 B apart, so their reads are not fused into one two-address
+  // load whose halves would then have to be moved into operand order
+  static constexpr int TILE = kChunk * F::FP * 2 + 16;
   static constexpr int qh_off = 0;
   static constexpr int ql_off = qh_off + TILE;
   static constexpr int kh_off = ql_off + TILE;
@@ -58,8 +62,9 @@ struct FavorFwdLayout {
   static constexpr int kwl_off = kwh_off + (GATE == GT_DECAY ? TILE : 0);
   static constexpr int v_off = kwl_off + (GATE == GT_DECAY ? TILE : 0);
   static constexpr int a_off = v_off + kChunk * EP * 2;
-  static constexpr int z_off = a_off + kChunk * CP * 2;
-  static constexpr int rsp_off = z_off + R * 4;     // [4][64] partial score row sums
+  static constexpr int zh_off = a_off + kChunk * CP * 2;
+  static constexpr int zl_off = zh_off + R * 2 + 16;
+  static constexpr int rsp_off = zl_off + R * 2 + 16;       // [4][64] partial score row sums
   static constexpr int zdp_off = rsp_off + 4 * kChunk * 4;  // [64] phi(q) . z
   static constexpr int xq_off = zdp_off + kChunk * 4;       // XStage<DK> of the queries
   template <int DK>
@@ -72,15 +77,53 @@ struct FavorSegLayout {
   using F = FavorBlock<R>;
   static constexpr int EP = E + 8;
   static constexpr int kh_off = 0;
-  static constexpr int kl_off = kh_off + kChunk * F::FP * 2;
-  static constexpr int v_off = kl_off + kChunk * F::FP * 2;
+  static constexpr int kl_off = kh_off + kChunk * F::FP * 2 + 16;
+  static constexpr int v_off = kl_off + kChunk * F::FP * 2 + 16;
   static constexpr int xk_off = v_off + kChunk * EP * 2;  // XStage<DK> of the keys
   template <int DK>
   static constexpr int bytes_dk = xk_off + XStage<DK>::bytes;
 };
 
+// Per-lane byte offsets of every LDS access pattern, built once per feature
+// block from an opaque lane index (opaque_lane): each access then adds only
+// compile-time or wave-uniform constants, which fold into the instruction.
+template <int FP, int EP, int XP>
+struct FavorLane {
+  int g4, c16;
+  int frag;   // row c, 8 columns at 8 g of an FP-stride tile (row-fragment operands)
+  int half;   // row c, 4 columns at 4 g of an FP-stride tile (inter-chunk B operand)
+  int put;    // row c, 4 columns at 16 w + 4 g of an FP-stride tile (feature writes)
+  int trf;    // transpose reads of FP-stride tiles
+  int tre;    // transpose reads of the EP-stride V tile
+  int xfrag;  // row c, 8 columns at 8 g of an X stage
+  int afrag;  // row c, 8 columns at 8 g of the score tile
+  int a4;     // row c, 4 columns at 4 g of the score tile
+  int l4;     // 4 c (per-row floats)
+  __device__ __forceinline__ FavorLane(int lane, int w) {
+    g4 = lane >> 4;
+    c16 = lane & 15;
+    frag = 2 * (c16 * FP + 8 * g4);
+    half = 2 * (c16 * FP + 4 * g4);
+    put = 2 * (c16 * FP + 4 * g4) + 32 * w;
+    trf = 2 * ((8 * g4 + (c16 >> 2)) * FP + 4 * (c16 & 3));
+    tre = 2 * ((8 * g4 + (c16 >> 2)) * EP + 4 * (c16 & 3));
+    xfrag = 2 * (c16 * XP + 8 * g4);
+    afrag = 2 * (c16 * CP + 8 * g4);
+    a4 = 2 * (c16 * CP + 4 * g4);
+    l4 = 4 * c16;
+  }
+};
+
+// MFMA operand by two transpose reads at a lane's transpose-read base plus a
+// constant (see tr_operand): rows r0 + 8 g + 0..7 of one column per lane.
+__device__ __forceinline__ bf16x8 tr_at(char* sm, int addr, int stride_bytes) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + addr));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + addr + 4 * stride_bytes));
+  return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
+}
+
 // Stage this wave's quarter of the raw rows (tokens 16 w .. 16 w + 15) and
-// their shifts |x|^2/2 + ln(r)/2.
+// their shifts in base 2, (|x|^2/2 + ln(r)/2) log2(e).
 template <int R, int DK>
 __device__ __forceinline__ void favor_stage_x(const bf16x8 (&x)[DK / 32], char* sm, int x_off, int lane, int w) {
   using X = XStage<DK>;
@@ -97,7 +140,7 @@ __device__ __forceinline__ void favor_stage_x(const bf16x8 (&x)[DK / 32], char* 
     }
   }
   ss = sum_over_groups(ss);
-  if (g4 == 0) lds<float>(sm, x_off + X::sh + 4 * t) = 0.5f * ss + 0.5f * __logf(float(R));
+  if (g4 == 0) lds<float>(sm, x_off + X::sh + 4 * t) = (0.5f * ss + 0.5f * __logf(float(R))) * 1.44269504f;
 }
 
 // hi/lo bf16 pairs of four floats (packed two per dword).
@@ -137,40 +180,40 @@ __device__ __forceinline__ bf16x4 keep_if(bool ok, bf16x4 x) {
 
 // FAVOR+ features of one side of a chunk for this wave's 16 features of block
 // fb (block features 16 w .. 16 w + 15), as hi/lo pairs in row-major
-// [token][feature] tiles. Keys past the chunk's valid rows are zero. With
-// WEIGHTED, keys are also written multiplied by gamma^(L-1-t) (RetNet state
-// update) into (wh_off, wl_off); with ONLY_WEIGHTED that is the only copy.
-template <int R, int DK, bool IS_K, bool WEIGHTED, bool ONLY_WEIGHTED>
-__device__ __forceinline__ void favor_project(int x_off, const bf16* omega, int fb, int L, float lg2gam, char* sm,
-                                              int hi_off, int lo_off, int wh_off, int wl_off, int lane, int w) {
+// [token][feature] tiles: phi = 2^(P log2(e) - shift2) with P = x . w on the
+// matrix cores. Keys past the chunk's valid rows are zero. With WEIGHTED,
+// keys are also written multiplied by gamma^(L-1-t) (RetNet state update)
+// into (wh_off, wl_off); with ONLY_WEIGHTED that is the only copy.
+template <int R, int DK, bool IS_K, bool WEIGHTED, bool ONLY_WEIGHTED, class LN>
+__device__ __forceinline__ void favor_project(const LN& ln, int x_off, const bf16* omega, int fb, int L, float lg2gam,
+                                              char* sm, int hi_off, int lo_off, int wh_off, int wl_off, int w) {
   using F = FavorBlock<R>;
   using X = XStage<DK>;
   constexpr int KS = DK / 32, FP = F::FP;
-  const int g4 = lane >> 4, c16 = lane & 15;
   // omega rows of this wave's features (the whole omega is 32 KB or less: cache-resident)
   bf16x8 om[KS];
+  const bf16* orow = omega + (long long)(fb * F::FB + 16 * w + ln.c16) * DK + 8 * ln.g4;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    om[ks] = *reinterpret_cast<const bf16x8*>(omega + (long long)(fb * F::FB + 16 * w + c16) * DK + 32 * ks + 8 * g4);
-  const int f0 = 16 * w + 4 * g4;  // block-local features f0 .. f0 + 3 of this lane
+  for (int ks = 0; ks < KS; ++ks) om[ks] = *reinterpret_cast<const bf16x8*>(orow + 32 * ks);
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    const int t = 16 * tt + c16;
-    const float shift = lds<float>(sm, x_off + X::sh + 4 * t);
+    const float shift2 = lds<float>(sm, x_off + X::sh + 64 * tt + ln.l4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      acc = mfma16(om[ks], lds<bf16x8>(sm, x_off + 2 * (t * X::XP + 32 * ks + 8 * g4)), acc);
-    // acc[i] = P[token t][block feature f0 + i]
+      acc = mfma16(om[ks], lds<bf16x8>(sm, x_off + 32 * tt * X::XP + 64 * ks + ln.xfrag), acc);
+    // acc[i] = P[token 16 tt + c][block feature 16 w + 4 g + i]
     float f[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __expf(acc[i] - shift);
+    for (int i = 0; i < 4; ++i) f[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], 1.44269504f, -shift2));
+    const int t = 16 * tt + ln.c16;
     const bool ok = !IS_K || t < L;
+    const int at = 32 * tt * FP + ln.put;
     if constexpr (!ONLY_WEIGHTED) {
       bf16x4 h, l;
       split4(f, h, l);
-      lds<bf16x4>(sm, hi_off + 2 * (t * FP + f0)) = keep_if(ok, h);
-      lds<bf16x4>(sm, lo_off + 2 * (t * FP + f0)) = keep_if(ok, l);
+      lds<bf16x4>(sm, hi_off + at) = keep_if(ok, h);
+      lds<bf16x4>(sm, lo_off + at) = keep_if(ok, l);
     }
     if constexpr (WEIGHTED) {
       const float wt = exp2f(float(L - 1 - t) * lg2gam);
@@ -179,8 +222,8 @@ __device__ __forceinline__ void favor_project(int x_off, const bf16* omega, int 
       for (int i = 0; i < 4; ++i) fw[i] = f[i] * wt;
       bf16x4 h, l;
       split4(fw, h, l);
-      lds<bf16x4>(sm, wh_off + 2 * (t * FP + f0)) = keep_if(ok, h);
-      lds<bf16x4>(sm, wl_off + 2 * (t * FP + f0)) = keep_if(ok, l);
+      lds<bf16x4>(sm, wh_off + at) = keep_if(ok, h);
+      lds<bf16x4>(sm, wl_off + at) = keep_if(ok, l);
     }
     __builtin_amdgcn_sched_barrier(0);  // one token tile at a time: bounded live registers
   }
@@ -200,27 +243,27 @@ __device__ __forceinline__ void favor_write_v(const bf16x8 (&v)[E / 32], char* s
 // K^ as a hi/lo pair, and the wave's z tile of the block <- g z + K^^T 1 (z
 // is the state column of a constant-1 value). Wave w owns block-local z tile
 // w: lane (g, c) holds z[64 fb + 16 w + 4 g + i] in Zb.
-template <int R, int E>
-__device__ __forceinline__ void favor_state_block(f32x4 (&S)[R / 16][E / 64], f32x4& Zb, int fb, char* sm, int kh_off,
-                                                  int kl_off, int v_off, float gscale, int lane, int w) {
+template <int R, int E, class LN>
+__device__ __forceinline__ void favor_state_block(const LN& ln, f32x4 (&S)[R / 16][E / 64], f32x4& Zb, int fb,
+                                                  char* sm, int kh_off, int kl_off, int v_off, float gscale, int w) {
   using F = FavorBlock<R>;
   constexpr int FP = F::FP, EP = E + 8;
-  const int ebase = w * (E / 4);
   bf16x8 ones;
 #pragma unroll
   for (int u = 0; u < 8; ++u) ones[u] = (bf16)1.f;
   bf16x8 vb[E / 64][2];
+  const int vbase = v_off + 2 * w * (E / 4) + ln.tre;
 #pragma unroll
   for (int eb = 0; eb < E / 64; ++eb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_operand(sm, v_off, EP, 32 * ks, ebase + 16 * eb, lane);
+    for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_at(sm, vbase + 2 * (32 * ks * EP + 16 * eb), 2 * EP);
 #pragma unroll
   for (int rt = 0; rt < F::FT; ++rt) {
     bf16x8 kh[2], kl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      kh[ks] = tr_operand(sm, kh_off, FP, 32 * ks, 16 * rt, lane);
-      kl[ks] = tr_operand(sm, kl_off, FP, 32 * ks, 16 * rt, lane);
+      kh[ks] = tr_at(sm, kh_off + 2 * (32 * ks * FP + 16 * rt) + ln.trf, 2 * FP);
+      kl[ks] = tr_at(sm, kl_off + 2 * (32 * ks * FP + 16 * rt) + ln.trf, 2 * FP);
     }
 #pragma unroll
     for (int eb = 0; eb < E / 64; ++eb) {
@@ -260,6 +303,23 @@ __device__ __forceinline__ void favor_z_store(const f32x4 (&Z)[FavorBlock<R>::NF
   }
 }
 
+// bf16 hi/lo image of the wave's z tiles into LDS (zh, zl: [R] bf16 each).
+template <int R>
+__device__ __forceinline__ void favor_z_publish(const f32x4 (&Z)[FavorBlock<R>::NFB], char* sm, int zh_off,
+                                                int zl_off, int lane, int w) {
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int fb = 0; fb < FavorBlock<R>::NFB; ++fb) {
+      const float f[4] = {Z[fb][0], Z[fb][1], Z[fb][2], Z[fb][3]};
+      bf16x4 h, l;
+      split4(f, h, l);
+      const int o = 2 * (64 * fb + 16 * w + 4 * (lane >> 4));
+      lds<bf16x4>(sm, zh_off + o) = h;
+      lds<bf16x4>(sm, zl_off + o) = l;
+    }
+  }
+}
+
 template <int R>
 __device__ __forceinline__ void favor_z_load(f32x4 (&Z)[FavorBlock<R>::NFB], const float* src, int lane, int w) {
 #pragma unroll
@@ -285,8 +345,9 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FavorSegLayout<R, E>;
   using F = FavorBlock<R>;
-  const int lane0 = lane_id(), w = wave_id();
-  const int lane = lane0, g4 = lane >> 4, c16 = lane & 15;
+  using LN = FavorLane<F::FP, E + 8, DK + 8>;
+  const int lane = lane_id(), w = wave_id();
+  const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
@@ -317,13 +378,13 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
     lds_barrier();
 #pragma unroll
     for (int fb = 0; fb < F::NFB; ++fb) {
-      const int lane = opaque_lane(lane0);
+      const LN ln(opaque_lane(lane), w);
       // pass 1 keeps only the keys of the state update (decay-weighted for RetNet)
-      favor_project<R, DK, true, GATE == GT_DECAY, GATE == GT_DECAY>(LY::xk_off, a.omega, fb, L, lg2gam, sm,
+      favor_project<R, DK, true, GATE == GT_DECAY, GATE == GT_DECAY>(ln, LY::xk_off, a.omega, fb, L, lg2gam, sm,
                                                                      LY::kh_off, LY::kl_off, LY::kh_off, LY::kl_off,
-                                                                     lane, w);
+                                                                     w);
       lds_barrier();
-      favor_state_block<R, E>(S, Z[fb], fb, sm, LY::kh_off, LY::kl_off, LY::v_off, gsc, lane, w);
+      favor_state_block<R, E>(ln, S, Z[fb], fb, sm, LY::kh_off, LY::kl_off, LY::v_off, gsc, w);
       lds_barrier();
     }
   }
@@ -346,9 +407,10 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FavorFwdLayout<R, E, GATE>;
   using F = FavorBlock<R>;
+  using LN = FavorLane<F::FP, E + 8, DK + 8>;
   constexpr int FP = F::FP, EP = LY::EP, NEB = E / 64, KPB = F::FB / 32;
-  const int lane0 = lane_id(), w = wave_id(), tid = threadIdx.x;
-  const int lane = lane0, g4 = lane >> 4, c16 = lane & 15;
+  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+  const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
@@ -376,7 +438,7 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
       for (int eb = 0; eb < NEB; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   favor_z_load<R>(Z, a.S_in != nullptr ? a.z_in + (bh * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
-  favor_z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
+  favor_z_publish<R>(Z, sm, LY::zh_off, LY::zl_off, lane, w);
   // partial row sums of query tiles this wave holds no score tile of stay zero
   lds<float>(sm, LY::rsp_off + 4 * tid) = 0.f;
 
@@ -409,46 +471,44 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
     for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) oacc[qt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float zd = 0.f;  // phi(q) . z_prev for query 16 w + c over this lane's k-slots
+    f32x4 zacc = {0.f, 0.f, 0.f, 0.f};  // phi(q) . z_prev for queries 16 w + 4 g + i
 
 #pragma unroll
     for (int fb = 0; fb < F::NFB; ++fb) {
-      const int lane = opaque_lane(lane0);
-      const int g4 = lane >> 4, c16 = lane & 15;
+      const LN ln(opaque_lane(lane), w);
       const bool last = fb == F::NFB - 1;
-      favor_project<R, DK, false, false, false>(xq_off, a.omega, fb, L, lg2gam, sm, LY::qh_off, LY::ql_off, 0, 0,
-                                                lane, w);
-      favor_project<R, DK, true, GATE == GT_DECAY, false>(xk_off, a.omega, fb, L, lg2gam, sm, LY::kh_off, LY::kl_off,
-                                                          LY::kwh_off, LY::kwl_off, lane, w);
+      favor_project<R, DK, false, false, false>(ln, xq_off, a.omega, fb, L, lg2gam, sm, LY::qh_off, LY::ql_off, 0, 0,
+                                                w);
+      favor_project<R, DK, true, GATE == GT_DECAY, false>(ln, xk_off, a.omega, fb, L, lg2gam, sm, LY::kh_off,
+                                                          LY::kl_off, LY::kwh_off, LY::kwl_off, w);
       lds_barrier();
 
       // ---- scores over this block's features: A^T tiles = K~_kj Q~_qi^T
 #pragma unroll
       for (int sl = 0; sl < 3; ++sl) {
         if (sl < nslot) {
+          const int ko = 32 * skj[sl] * FP + ln.frag, qo = 32 * sqi[sl] * FP + ln.frag;
 #pragma unroll
-          for (int ks = 0; ks < KPB; ++ks) {
-            const int ko = 2 * ((16 * skj[sl] + c16) * FP + 32 * ks + 8 * g4);
-            const int qo = 2 * ((16 * sqi[sl] + c16) * FP + 32 * ks + 8 * g4);
-            sacc[sl] = mfma3(lds<bf16x8>(sm, LY::kh_off + ko), lds<bf16x8>(sm, LY::kl_off + ko),
-                             lds<bf16x8>(sm, LY::qh_off + qo), lds<bf16x8>(sm, LY::ql_off + qo), sacc[sl]);
-          }
+          for (int ks = 0; ks < KPB; ++ks)
+            sacc[sl] = mfma3(lds<bf16x8>(sm, LY::kh_off + 64 * ks + ko), lds<bf16x8>(sm, LY::kl_off + 64 * ks + ko),
+                             lds<bf16x8>(sm, LY::qh_off + 64 * ks + qo), lds<bf16x8>(sm, LY::ql_off + 64 * ks + qo),
+                             sacc[sl]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);  // phases stay apart: bounded register live ranges
-      // ---- phi(q) . z_prev for query tile w
+      // ---- phi(q) . z_prev for query tile w on the matrix cores (z as a
+      // hi/lo column replicated over the 16 output columns)
+      {
+        const int qo = 32 * w * FP + ln.frag;
 #pragma unroll
-      for (int ks = 0; ks < KPB; ++ks) {
-        const int qo = 2 * ((16 * w + c16) * FP + 32 * ks + 8 * g4);
-        const bf16x8 qh = lds<bf16x8>(sm, LY::qh_off + qo), ql = lds<bf16x8>(sm, LY::ql_off + qo);
-        const f32x4 z0 = lds<f32x4>(sm, LY::z_off + 4 * (64 * fb + 32 * ks + 8 * g4));
-        const f32x4 z1 = lds<f32x4>(sm, LY::z_off + 4 * (64 * fb + 32 * ks + 8 * g4 + 4));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) zd += (to_f32(qh[j]) + to_f32(ql[j])) * (j < 4 ? z0[j] : z1[j - 4]);
+        for (int ks = 0; ks < KPB; ++ks) {
+          const int zo = 2 * (64 * fb + 32 * ks + 8 * ln.g4);
+          zacc = mfma3(lds<bf16x8>(sm, LY::qh_off + 64 * ks + qo), lds<bf16x8>(sm, LY::ql_off + 64 * ks + qo),
+                       lds<bf16x8>(sm, LY::zh_off + zo), lds<bf16x8>(sm, LY::zl_off + zo), zacc);
+        }
       }
 
-      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);  // phases stay apart: bounded register live ranges
       // ---- inter-chunk product over this block's features: O^T += S^T Q^^T
       {
         bf16x8 sh[KPB][NEB], slo[KPB][NEB];
@@ -459,12 +519,11 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
             split_state_op(S[fb * F::FT + 2 * p][eb], S[fb * F::FT + 2 * p + 1][eb], sh[p][eb], slo[p][eb]);
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt) {
-          const int q = 16 * qt + c16;
 #pragma unroll
           for (int p = 0; p < KPB; ++p) {
-            const int o0 = 2 * (q * FP + 32 * p + 4 * g4), o1 = 2 * (q * FP + 32 * p + 16 + 4 * g4);
-            const bf16x8 qbh = cat8(lds<bf16x4>(sm, LY::qh_off + o0), lds<bf16x4>(sm, LY::qh_off + o1));
-            const bf16x8 qbl = cat8(lds<bf16x4>(sm, LY::ql_off + o0), lds<bf16x4>(sm, LY::ql_off + o1));
+            const int o0 = 32 * qt * FP + 64 * p + ln.half;
+            const bf16x8 qbh = cat8(lds<bf16x4>(sm, LY::qh_off + o0), lds<bf16x4>(sm, LY::qh_off + o0 + 32));
+            const bf16x8 qbl = cat8(lds<bf16x4>(sm, LY::ql_off + o0), lds<bf16x4>(sm, LY::ql_off + o0 + 32));
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb) oacc[qt][eb] = mfma3(sh[p][eb], slo[p][eb], qbh, qbl, oacc[qt][eb]);
           }
@@ -477,8 +536,8 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
       // old values in later blocks)
       __builtin_amdgcn_sched_barrier(0);
       const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-      favor_state_block<R, E>(S, Z[fb], fb, sm, GATE == GT_DECAY ? LY::kwh_off : LY::kh_off,
-                              GATE == GT_DECAY ? LY::kwl_off : LY::kl_off, LY::v_off, gsc, lane, w);
+      favor_state_block<R, E>(ln, S, Z[fb], fb, sm, GATE == GT_DECAY ? LY::kwh_off : LY::kh_off,
+                              GATE == GT_DECAY ? LY::kwl_off : LY::kl_off, LY::v_off, gsc, w);
 
       __builtin_amdgcn_sched_barrier(0);
       if (last) {
@@ -486,43 +545,44 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
 #pragma unroll
         for (int sl = 0; sl < 3; ++sl) {
           if (sl < nslot) {
-            const int q = 16 * sqi[sl] + c16;
+            const int q = 16 * sqi[sl] + ln.c16;
             float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int key = 16 * skj[sl] + 4 * g4 + i;
+              const int key = 16 * skj[sl] + 4 * ln.g4 + i;
               v[i] = sacc[sl][i];
               if (key > q) v[i] = 0.f;  // only the diagonal tiles straddle the mask
               if constexpr (GATE == GT_DECAY) v[i] *= exp2f(float(q - key) * lg2gam);
             }
             const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
             typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-            lds<u32x2>(sm, LY::a_off + 2 * (q * CP + 16 * skj[sl] + 4 * g4)) = u32x2{p01, p23};
+            lds<u32x2>(sm, LY::a_off + 32 * sqi[sl] * CP + 32 * skj[sl] + ln.a4) = u32x2{p01, p23};
             const float rs =
                 sum_over_groups((lo_bf16_f32(p01) + hi_bf16_f32(p01)) + (lo_bf16_f32(p23) + hi_bf16_f32(p23)));
-            if (g4 == 0) lds<float>(sm, LY::rsp_off + 4 * (w * kChunk + q)) = rs;
+            if (ln.g4 == 0) lds<float>(sm, LY::rsp_off + 256 * w + 64 * sqi[sl] + ln.l4) = rs;
           }
         }
         // upper-triangle tiles read by the intra-chunk product: (0,1) and (2,3)
-        if (w >= 2) {
-          const int q = 16 * (2 * w - 4) + c16;
-          lds<bf16x4>(sm, LY::a_off + 2 * (q * CP + 16 * (2 * w - 3) + 4 * g4)) = bf16x4{};
-        }
+        if (w >= 2) lds<bf16x4>(sm, LY::a_off + 32 * (2 * w - 4) * CP + 32 * (2 * w - 3) + ln.a4) = bf16x4{};
         {
-          float zdt = sum_over_groups(zd);
-          if constexpr (GATE == GT_DECAY) zdt *= exp2f(float(16 * w + c16 + 1) * lg2gam);
-          if (g4 == 0) lds<float>(sm, LY::zdp_off + 4 * (16 * w + c16)) = zdt;
+          // zacc[i] = phi(q) . z for q = 16 w + 4 g + i (every column c alike)
+          f32x4 zd = zacc;
+          if constexpr (GATE == GT_DECAY) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zd[i] *= exp2f(float(16 * w + 4 * ln.g4 + i + 1) * lg2gam);
+          }
+          if (ln.c16 == 0) lds<f32x4>(sm, LY::zdp_off + 4 * (16 * w + 4 * ln.g4)) = zd;
         }
         lds_barrier();
 
         // ---- intra-chunk part and normalisation: O^T += V^T A^T, o = O / den
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt) {
-          const int q = 16 * qt + c16;
-          const float den = (((lds<float>(sm, LY::rsp_off + 4 * q) + lds<float>(sm, LY::rsp_off + 4 * (64 + q))) +
-                              lds<float>(sm, LY::rsp_off + 4 * (128 + q))) +
-                             lds<float>(sm, LY::rsp_off + 4 * (192 + q))) +
-                            lds<float>(sm, LY::zdp_off + 4 * q) + a.eps;
+          const int q = 16 * qt + ln.c16;
+          const int ro = LY::rsp_off + 64 * qt + ln.l4;
+          const float den = (((lds<float>(sm, ro) + lds<float>(sm, ro + 256)) + lds<float>(sm, ro + 512)) +
+                             lds<float>(sm, ro + 768)) +
+                            lds<float>(sm, LY::zdp_off + 64 * qt + ln.l4) + a.eps;
           // one correctly rounded reciprocal per row; outputs are fl(O * fl(1 / den))
           const float inv_den = 1.f / den;
           float isc = 1.f;
@@ -537,18 +597,18 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
             }
 #pragma unroll
             for (int p2 = 0; p2 <= qt / 2; ++p2)
-              acc = mfma16(tr_operand(sm, LY::v_off, EP, 32 * p2, e, lane),
-                           lds<bf16x8>(sm, LY::a_off + 2 * (q * CP + 32 * p2 + 8 * g4)), acc);
+              acc = mfma16(tr_at(sm, LY::v_off + 2 * (32 * p2 * EP + e) + ln.tre, 2 * EP),
+                           lds<bf16x8>(sm, LY::a_off + 32 * qt * CP + 64 * p2 + ln.afrag), acc);
             if (q < L) {
               bf16x4 o = pack4(acc[0] * inv_den, acc[1] * inv_den, acc[2] * inv_den, acc[3] * inv_den);
-              *reinterpret_cast<bf16x4*>(a.out + (tok0 + t0 + q) * E + e + 4 * g4) = o;
+              *reinterpret_cast<bf16x4*>(a.out + (tok0 + t0 + q) * E + e + 4 * ln.g4) = o;
             }
           }
         }
       }
       lds_barrier();
     }
-    favor_z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
+    favor_z_publish<R>(Z, sm, LY::zh_off, LY::zl_off, lane, w);
   }
 
   if (a.S_out != nullptr && s == a.P - 1) {
