@@ -94,6 +94,10 @@ void plan_segments(int B, int H, int n, int fmap, int r, int dv, int dk, int gat
   int per_cu = lds > 0 ? kLdsPerCU / lds : 1;
   if (per_cu < 1) per_cu = 1;
   if (per_cu > kMaxGroupsPerCU) per_cu = kMaxGroupsPerCU;
+  // elu+1 with a 128 x 128 state: the fp32 state and its bf16 image alone take
+  // a third of a lane's 512 registers, and the output pass runs one
+  // workgroup per CU
+  if (fmap == LA_FMAP_ELU1 && (long long)r * dv >= 128 * 128) per_cu = 1;
   const long long target = (long long)kComputeUnits * per_cu;
   long long want = (target + BH - 1) / BH;
   if (want < 1) want = 1;

@@ -63,11 +63,17 @@ struct CausalArgs {
   float eps, inv_tau;
 };
 
-constexpr int CP = kChunk + 8;  // row stride (elements) of the [x][t] tiles
+// Row padding (bf16 elements) of the LDS tiles: rows of 32, 64 or 128
+// elements plus 8 start 4 dwords apart modulo the banks. Of the paddings
+// measured on these kernels (8 and 16) this one gives the faster chunk loops
+// for the 64-wide tiles, whose mix of 8-byte, 16-byte and transpose reads no
+// single padding makes conflict-free.
+constexpr int kPad = 8;
+constexpr int CP = kChunk + kPad;  // row stride (elements) of the score tile
 
 template <int R, int E, int GATE>
 struct FwdLayout {
-  static constexpr int RP = R + 8, EP = E + 8;
+  static constexpr int RP = R + kPad, EP = E + kPad;
   static constexpr int q_off = 0;
   static constexpr int k_off = q_off + kChunk * RP * 2;
   static constexpr int v_off = k_off + kChunk * RP * 2;
@@ -81,7 +87,7 @@ struct FwdLayout {
 
 template <int R, int E, int GATE>
 struct SegLayout {
-  static constexpr int RP = R + 8, EP = E + 8;
+  static constexpr int RP = R + kPad, EP = E + kPad;
   static constexpr int k_off = 0;  // K^ rows
   static constexpr int v_off = k_off + kChunk * RP * 2;
   static constexpr int gam_off = v_off + kChunk * EP * 2;
@@ -205,7 +211,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
                                               int kh_off, int v_off, int gam_off, int logg_off,
                                               int lane, int w) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q>;
-  constexpr int RP = R + 8, EP = E + 8;
+  constexpr int RP = R + kPad, EP = E + kPad;
   static_assert(FMAP == FM_ELU1, "FAVOR+ chunks use the kernels of chunked_favor.hpp");
   if constexpr (Raw::ROWMAJOR) {
     const int t = 16 * w + (lane >> 2);
@@ -310,7 +316,7 @@ struct ZTiles {
 template <int R, int E, int GATE>
 __device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (&Z)[ZTiles<R>::ZT], char* sm,
                                              int kh_off, int v_off, int gam_off, float gscale, int lane, int w) {
-  constexpr int ZT = ZTiles<R>::ZT, RP = R + 8, EP = E + 8;
+  constexpr int ZT = ZTiles<R>::ZT, RP = R + kPad, EP = E + kPad;
   const int g4 = lane >> 4;
   const int ebase = w * (E / 4);
   bf16x8 ones;

@@ -31,14 +31,14 @@ template <int R>
 struct FavorBlock {
   static constexpr int FB = 64;        // features per block
   static constexpr int NFB = R / FB;   // blocks
-  static constexpr int FP = FB + 8;    // row stride of the [token][feature] tiles
+  static constexpr int FP = FB + kPad;  // row stride of the [token][feature] tiles
   static constexpr int FT = FB / 16;   // 16-feature tiles per block
 };
 
-// Staged raw rows of one side: X [64][DK + 8] bf16 and the shift [64] fp32.
+// Staged raw rows of one side: X [64][DK + kPad] bf16 and the shift [64] fp32.
 template <int DK>
 struct XStage {
-  static constexpr int XP = DK + 8;
+  static constexpr int XP = DK + kPad;
   static constexpr int bytes = kChunk * XP * 2 + kChunk * 4;
   static constexpr int sh = kChunk * XP * 2;  // offset of the shifts
 };
@@ -49,7 +49,7 @@ struct XStage {
 template <int R, int E, int GATE>
 struct FavorFwdLayout {
   using F = FavorBlock<R>;
-  static constexpr int EP = E + 8;
+  static constexpr int EP = E + kPad;
   // 16 bytes between tiles: the hi and lo halves of one row are never a
   // multiple of 512 B apart, so their reads are not fused into one two-address
   // load whose halves would then have to be moved into operand order
@@ -61,21 +61,26 @@ struct FavorFwdLayout {
   static constexpr int kwh_off = kl_off + TILE;
   static constexpr int kwl_off = kwh_off + (GATE == GT_DECAY ? TILE : 0);
   static constexpr int v_off = kwl_off + (GATE == GT_DECAY ? TILE : 0);
-  static constexpr int a_off = v_off + kChunk * EP * 2;
-  static constexpr int zh_off = a_off + kChunk * CP * 2;
+  static constexpr int zh_off = v_off + kChunk * EP * 2;
   static constexpr int zl_off = zh_off + R * 2 + 16;
   static constexpr int rsp_off = zl_off + R * 2 + 16;       // [4][64] partial score row sums
   static constexpr int zdp_off = rsp_off + 4 * kChunk * 4;  // [64] phi(q) . z
   static constexpr int xq_off = zdp_off + kChunk * 4;       // XStage<DK> of the queries
+  // The score tile [64][CP] shares the query stage: it is written after the
+  // chunk's last projection and read before the next chunk is staged.
+  static constexpr int a_off = xq_off;
   template <int DK>
-  static constexpr int bytes_dk = xq_off + 2 * XStage<DK>::bytes;
+  static constexpr int xk_off_dk =
+      xq_off + (XStage<DK>::bytes > kChunk * CP * 2 ? XStage<DK>::bytes : kChunk * CP * 2);
+  template <int DK>
+  static constexpr int bytes_dk = xk_off_dk<DK> + XStage<DK>::bytes;
 };
 
 // Segment-state pass: kh/kl hold the (decay-weighted) key features.
 template <int R, int E>
 struct FavorSegLayout {
   using F = FavorBlock<R>;
-  static constexpr int EP = E + 8;
+  static constexpr int EP = E + kPad;
   static constexpr int kh_off = 0;
   static constexpr int kl_off = kh_off + kChunk * F::FP * 2 + 16;
   static constexpr int v_off = kl_off + kChunk * F::FP * 2 + 16;
@@ -229,12 +234,12 @@ __device__ __forceinline__ void favor_project(const LN& ln, int x_off, const bf1
   }
 }
 
-// V rows of the chunk into a row-major [token][E + 8] tile (lane = token,
+// V rows of the chunk into a row-major [token][E + kPad] tile (lane = token,
 // wave w holds columns [w E/4, (w+1) E/4)). Rows past the end need no mask:
 // their key features are zero and their scores are masked.
 template <int E>
 __device__ __forceinline__ void favor_write_v(const bf16x8 (&v)[E / 32], char* sm, int v_off, int lane, int w) {
-  constexpr int EV = E / 4, EP = E + 8;
+  constexpr int EV = E / 4, EP = E + kPad;
 #pragma unroll
   for (int j = 0; j < EV / 8; ++j) lds<bf16x8>(sm, v_off + 2 * (lane * EP + w * EV + 8 * j)) = v[j];
 }
@@ -247,7 +252,7 @@ template <int R, int E, class LN>
 __device__ __forceinline__ void favor_state_block(const LN& ln, f32x4 (&S)[R / 16][E / 64], f32x4& Zb, int fb,
                                                   char* sm, int kh_off, int kl_off, int v_off, float gscale, int w) {
   using F = FavorBlock<R>;
-  constexpr int FP = F::FP, EP = E + 8;
+  constexpr int FP = F::FP, EP = E + kPad;
   bf16x8 ones;
 #pragma unroll
   for (int u = 0; u < 8; ++u) ones[u] = (bf16)1.f;
@@ -345,7 +350,7 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FavorSegLayout<R, E>;
   using F = FavorBlock<R>;
-  using LN = FavorLane<F::FP, E + 8, DK + 8>;
+  using LN = FavorLane<F::FP, E + kPad, DK + kPad>;
   const int lane = lane_id(), w = wave_id();
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FavorFwdLayout<R, E, GATE>;
   using F = FavorBlock<R>;
-  using LN = FavorLane<F::FP, E + 8, DK + 8>;
+  using LN = FavorLane<F::FP, E + kPad, DK + kPad>;
   constexpr int FP = F::FP, EP = LY::EP, NEB = E / 64, KPB = F::FB / 32;
   const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
     skj[sl] = score_tile_kj(idx);
   }
 
-  constexpr int xq_off = LY::xq_off, xk_off = LY::xq_off + XStage<DK>::bytes;
+  constexpr int xq_off = LY::xq_off, xk_off = LY::template xk_off_dk<DK>;
   RawChunk<R, E, DK, FM_FAVOR, GT_NONE, true> raw;
   raw.load(a, tok0, t_begin, t_end, lane, w);
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
