@@ -108,13 +108,8 @@ def segments(B, H, n, d_k, d_v, *, fmap="elu1", r=None, causal=True, gate_kind="
     return P.value, L.value
 
 
-def forward(Q, K, V, *, fmap="elu1", omega=None, causal=True, gate=None, eps=1e-6, S0=None, z0=None,
-            return_state=False, out_dtype=None, out=None, workspace=None, stream=None):
-    """o = phi(Q) S / (phi(Q) z + eps) through la_forward.
-
-    Q, K [B, H, n, d_k]; V [B, H, n, d_v]; gate None | ("decay", gamma[H]) |
-    ("gla", g[B, H, n, r], tau). Returns out, or (out, S_final, z_final).
-    """
+def _forward_args(Q, K, V, fmap, omega, causal, gate, eps, S0, z0, return_state, out_dtype, out, workspace, stream):
+    """Validate and marshal one la_forward call: (ctypes argument tuple, keep-alive objects, out, S_final, z_final)."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
         _dev(t, nm)
     if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
@@ -153,20 +148,47 @@ def forward(Q, K, V, *, fmap="elu1", omega=None, causal=True, gate=None, eps=1e-
     need = ws_bytes.value
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    st = N.lib().la_forward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(f), int(bool(causal)),
-                            ctypes.byref(g), _ptr(S0), _ptr(z0), _ptr(Sf), _ptr(zf), _ptr(out),
-                            _ptr(workspace) if need else None, need, _stream(Q, stream))
-    N.check(st, "la_forward")
+    args = (ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(f), int(bool(causal)), ctypes.byref(g),
+            _ptr(S0), _ptr(z0), _ptr(Sf), _ptr(zf), _ptr(out), _ptr(workspace) if need else None, need,
+            _stream(Q, stream))
+    keep = (p, f, g, Q, K, V, omega, gate, S0, z0, workspace)
+    return args, keep, out, Sf, zf
+
+
+def forward(Q, K, V, *, fmap="elu1", omega=None, causal=True, gate=None, eps=1e-6, S0=None, z0=None,
+            return_state=False, out_dtype=None, out=None, workspace=None, stream=None):
+    """o = phi(Q) S / (phi(Q) z + eps) through la_forward.
+
+    Q, K [B, H, n, d_k]; V [B, H, n, d_v]; gate None | ("decay", gamma[H]) |
+    ("gla", g[B, H, n, r], tau). Returns out, or (out, S_final, z_final).
+    """
+    args, _keep, out, Sf, zf = _forward_args(Q, K, V, fmap, omega, causal, gate, eps, S0, z0, return_state,
+                                             out_dtype, out, workspace, stream)
+    N.check(N.lib().la_forward(*args), "la_forward")
     return (out, Sf, zf) if return_state else out
 
 
-def decode_step(S, z, q, k, v, *, fmap="elu1", omega=None, gate=None, eps=1e-6, out_dtype=torch.float32,
-                out=None, stream=None):
-    """One recurrent step; S [B, H, r, d_v] and z [B, H, r] (fp32) are updated in place.
+class PreparedForward:
+    """One la_forward call validated and marshalled once (same arguments as
+    forward). Calling the object launches it again on the same buffers and
+    stream, with no per-call Python work beyond the foreign call: for loops
+    that repeat a call, such as timing runs. The tensors passed in must stay
+    alive and unchanged in shape while the object is used."""
 
-    q, k [B, H, d_k]; v [B, H, d_v]; gate None | ("decay", gamma[H]) |
-    ("gla", g[B, H, r], tau). Returns out [B, H, d_v].
-    """
+    def __init__(self, Q, K, V, *, fmap="elu1", omega=None, causal=True, gate=None, eps=1e-6, S0=None, z0=None,
+                 return_state=False, out_dtype=None, out=None, workspace=None, stream=None):
+        self._args, self._keep, self.out, self.S_final, self.z_final = _forward_args(
+            Q, K, V, fmap, omega, causal, gate, eps, S0, z0, return_state, out_dtype, out, workspace, stream)
+        self._fn = N.lib().la_forward
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            N.check(st, "la_forward")
+        return self.out
+
+
+def _decode_args(S, z, q, k, v, fmap, omega, gate, eps, out_dtype, out, stream):
     for t, nm in ((S, "S"), (z, "z"), (q, "q"), (k, "k"), (v, "v")):
         _dev(t, nm)
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
@@ -184,9 +206,38 @@ def decode_step(S, z, q, k, v, *, fmap="elu1", omega=None, gate=None, eps=1e-6, 
     p = _problem(B, H, 1, d_k, d_v, _dt(q), _DT[out_dtype], eps)
     if out is None:
         out = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
-    N.check(N.lib().la_decode_step(ctypes.byref(p), _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(f),
-                                   ctypes.byref(g), _ptr(out), _stream(q, stream)), "la_decode_step")
+    args = (ctypes.byref(p), _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(f), ctypes.byref(g),
+            _ptr(out), _stream(q, stream))
+    return args, (p, f, g, S, z, q, k, v, omega, gate), out
+
+
+def decode_step(S, z, q, k, v, *, fmap="elu1", omega=None, gate=None, eps=1e-6, out_dtype=torch.float32,
+                out=None, stream=None):
+    """One recurrent step; S [B, H, r, d_v] and z [B, H, r] (fp32) are updated in place.
+
+    q, k [B, H, d_k]; v [B, H, d_v]; gate None | ("decay", gamma[H]) |
+    ("gla", g[B, H, r], tau). Returns out [B, H, d_v].
+    """
+    args, _keep, out = _decode_args(S, z, q, k, v, fmap, omega, gate, eps, out_dtype, out, stream)
+    N.check(N.lib().la_decode_step(*args), "la_decode_step")
     return out
+
+
+class PreparedDecode:
+    """One la_decode_step call validated and marshalled once (same arguments
+    as decode_step); calling the object launches it again on the same buffers."""
+
+    def __init__(self, S, z, q, k, v, *, fmap="elu1", omega=None, gate=None, eps=1e-6, out_dtype=torch.float32,
+                 out=None, stream=None):
+        self._args, self._keep, self.out = _decode_args(S, z, q, k, v, fmap, omega, gate, eps, out_dtype, out,
+                                                        stream)
+        self._fn = N.lib().la_decode_step
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            N.check(st, "la_decode_step")
+        return self.out
 
 
 def feature_map(X, *, fmap="elu1", omega=None, stream=None):

@@ -12,7 +12,7 @@ import torch
 
 import oracle as orc
 from workloads import WORKLOADS, make_inputs, to_f64
-from _helpers import (TOL_BF16, TOL_F32, check_close, dev, oracle_forward, run_forward, tol_for)
+from _helpers import (TOL_BF16, TOL_F32, check_close, dev, gpu_gate, oracle_forward, run_forward, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -274,3 +274,41 @@ def test_feature_map(fmap, dtype, d, r):
     phi = ksm.feature_map(dev(X), fmap=fmap, omega=dev(om)).cpu()
     ref = orc.feature_map(to_f64(X), fmap, None if om is None else to_f64(om))
     check_close(phi, ref, TOL_F32, f"phi {fmap} {dtype}")
+
+
+# ------------------------------------------------------------------ prepared calls
+
+@pytest.mark.parametrize("name", ["causal_elu1", "gla_gate", "favor_causal"])
+def test_prepared_forward_matches_forward(name):
+    """PreparedForward launches the same la_forward call: bitwise the output of
+    forward(), on every repeat, and after the inputs are overwritten in place."""
+    import kernelized_sequence_mixing_amd as ksm
+    inp = make_inputs(WORKLOADS[name], seed=12, B=2, H=4, n=777)
+    Q, K, V = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"])
+    kw = dict(fmap=inp["fmap"], omega=dev(inp.get("omega")), causal=True, gate=gpu_gate(inp), eps=inp["eps"])
+    ref = ksm.forward(Q, K, V, **kw)
+    call = ksm.PreparedForward(Q, K, V, **kw)
+    for _ in range(3):
+        got = call()
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    Q.mul_(0.5)
+    ref2 = ksm.forward(Q, K, V, **kw)
+    got2 = call()
+    torch.cuda.synchronize()
+    assert torch.equal(got2.view(torch.int16), ref2.view(torch.int16))
+
+
+def test_prepared_decode_matches_decode_step():
+    import kernelized_sequence_mixing_amd as ksm
+    wl = WORKLOADS["gla_decode"]
+    inp = make_inputs(wl, seed=13, B=4, H=3)
+    q, k, v, g = (dev(inp[x]) for x in ("q", "k", "v", "g"))
+    S1, z1 = dev(inp["S0"]), dev(inp["z0"])
+    S2, z2 = S1.clone(), z1.clone()
+    call = ksm.PreparedDecode(S2, z2, q, k, v, gate=("gla", g, wl.tau), eps=wl.eps)
+    for _ in range(2):  # two steps: the state advances in place both ways
+        ref = ksm.decode_step(S1, z1, q, k, v, gate=("gla", g, wl.tau), eps=wl.eps)
+        got = call()
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref) and torch.equal(S2, S1) and torch.equal(z2, z1)
