@@ -352,19 +352,29 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (
       }
       S[rt][eb] = st;
     }
-    if (rt / ZT == w) {
-      f32x4 zt = Z[rt % ZT];
+  }
+  // this wave's z tiles, outside the tile loop so no branch on the wave index splits it
+  if (w < ZTiles<R>::OWNERS) {
+#pragma unroll
+    for (int j = 0; j < ZT; ++j) {
+      const int rt = w * ZT + j;
+      f32x4 zt = Z[j];
+      float gr[4] = {gscale, gscale, gscale, gscale};
+      if constexpr (GATE == GT_GLA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gr[i] = lds<float>(sm, gam_off + 4 * (16 * rt + 4 * g4 + i));
+      }
       if constexpr (GATE == GT_DECAY) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) zt = mfma16(ka[ks], ones, zt);
+      for (int ks = 0; ks < 2; ++ks) zt = mfma16(tr_operand(sm, kh_off, RP, 32 * ks, 16 * rt, lane), ones, zt);
       if constexpr (GATE == GT_GLA) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
-      Z[rt % ZT] = zt;
+      Z[j] = zt;
     }
   }
 }

@@ -282,19 +282,20 @@ __device__ __forceinline__ void favor_state_block(const LN& ln, f32x4 (&S)[R / 1
       }
       S[fb * F::FT + rt][eb] = st;
     }
-    if (rt == w) {
-      f32x4 zt = Zb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) zt[i] *= gscale;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        zt = mfma16(kh[ks], ones, zt);
-        zt = mfma16(kl[ks], ones, zt);
-      }
-      Zb = zt;
-    }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // this wave's z tile (block rows 16 w .. 16 w + 15), outside the tile loop
+  // so no branch on the wave index splits it
+  f32x4 zt = Zb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) zt[i] *= gscale;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int o = 2 * (32 * ks * FP) + 32 * w + ln.trf;
+    zt = mfma16(tr_at(sm, kh_off + o, 2 * FP), ones, zt);
+    zt = mfma16(tr_at(sm, kl_off + o, 2 * FP), ones, zt);
+  }
+  Zb = zt;
 }
 
 // z tiles (all blocks) of wave w to / from a flat [R] fp32 array.

@@ -14,7 +14,7 @@ namespace la {
 constexpr int kChunk = 64;          // tokens per chunk of the causal kernel (= wave64)
 constexpr int kComputeUnits = 256;  // MI355X
 constexpr int kLdsPerCU = 160 * 1024;
-constexpr int kMaxGroupsPerCU = 3;  // register budget of the chunked output pass
+constexpr int kMaxGroupsPerCU = 2;  // measured: 2 beats 1 and 3 on the chunked passes (fewer segments, less state traffic)
 constexpr int kNonCausalGroups = 512;
 
 // LDS bytes of the causal output-pass workgroup for this shape (0 if not built);

@@ -78,8 +78,8 @@ int main(void) {{
 
 @needs_lib
 @pytest.mark.parametrize("B,H,n,d,dv,fmap,r,gate,expect_P,expect_len", [
-    # output-pass LDS 36.8 KB -> 4 workgroups per CU by LDS, capped at 3 -> 768 (head, segment) groups
-    (4, 16, 4096, 64, 64, "elu1", 64, "none", 11, 384),       # causal elu+1 workload
+    # output-pass LDS 36.8 KB -> 4 workgroups per CU by LDS, capped at 2 -> 512 (head, segment) groups
+    (4, 16, 4096, 64, 64, "elu1", 64, "none", 8, 512),        # causal elu+1 workload
     # 128 x 128 states: one output-pass workgroup per CU (registers) -> 256 groups
     (2, 8, 8192, 128, 128, "elu1", 128, "decay", 16, 512),    # RetNet workload
     (2, 16, 16384, 128, 128, "elu1", 128, "gla", 8, 2048),    # GLA workload
@@ -87,7 +87,8 @@ int main(void) {{
     (1, 8, 32768, 64, 64, "favor", 256, "none", 64, 512),     # FAVOR+ workload
     (1, 1, 1, 64, 64, "elu1", 64, "none", 1, 64),
     (1, 1, 65, 64, 64, "elu1", 64, "none", 2, 64),
-    (600, 1, 100, 64, 64, "elu1", 64, "none", 2, 64),
+    (300, 1, 100, 64, 64, "elu1", 64, "none", 2, 64),
+    (600, 1, 100, 64, 64, "elu1", 64, "none", 1, 128),
     (800, 1, 100, 64, 64, "elu1", 64, "none", 1, 128),
 ])
 def test_segment_plan(B, H, n, d, dv, fmap, r, gate, expect_P, expect_len):
@@ -102,8 +103,8 @@ def test_workspace_sizes():
     from kernelized_sequence_mixing_amd import workspace_size
     # one segment: nothing to chain
     assert workspace_size(800, 1, 100, 64, 64) == 0
-    # 11 segments x 64 heads of 64x64 fp32 states + normalisers, each region 256-aligned
-    assert workspace_size(4, 16, 4096, 64, 64) == 64 * 11 * 64 * 64 * 4 + 64 * 11 * 64 * 4
+    # 8 segments x 64 heads of 64x64 fp32 states + normalisers, each region 256-aligned
+    assert workspace_size(4, 16, 4096, 64, 64) == 64 * 8 * 64 * 64 * 4 + 64 * 8 * 64 * 4
     gla = workspace_size(2, 16, 16384, 128, 128, gate_kind="gla")
     plain = workspace_size(2, 16, 16384, 128, 128)
     assert gla == plain + 32 * 8 * 128 * 4  # 8 segments: one summed log-gate row per (head, segment)
