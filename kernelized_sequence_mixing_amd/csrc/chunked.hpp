@@ -22,9 +22,11 @@
 // contribution, a scan chains them, and pass 3 recomputes every segment's
 // outputs starting from its chained state.
 //
-// Workgroup = 256 threads = 4 waves. Wave w owns query rows [16w, 16w+16) of
-// the chunk for the scores, and value columns [w E/4, (w+1) E/4) of the state
-// and the outputs. The fp32 state lives in MFMA accumulators for the whole
+// Workgroup = NW waves: 4, or 8 for 128 x 128 states (so the per-wave share of
+// the state and of the chunk's registers fits two waves per SIMD). Waves 0..3
+// own query rows [16w, 16w+16) of the chunk for the scores (with 8 waves,
+// waves 4..7 compute phi(q) . z for those rows), and wave w owns value columns
+// [w E/NW, (w+1) E/NW) of the state and the outputs. The fp32 state lives in MFMA accumulators for the whole
 // sequence; its bf16 image feeds the inter-chunk product straight from
 // registers. LDS holds the chunk's operands (bf16), all row-major:
 //   q  [64][R+8]   Q~ (also Q^)      k [64][R+8]   K~      v [64][E+8]   V
@@ -71,6 +73,12 @@ struct CausalArgs {
 constexpr int kPad = 8;
 constexpr int CP = kChunk + kPad;  // row stride (elements) of the score tile
 
+// Waves per workgroup of the elu+1 chunk kernels.
+template <int R, int E>
+struct Waves {
+  static constexpr int NW = R * E >= 128 * 128 ? 8 : 4;
+};
+
 template <int R, int E, int GATE>
 struct FwdLayout {
   static constexpr int RP = R + kPad, EP = E + kPad;
@@ -81,8 +89,9 @@ struct FwdLayout {
   static constexpr int a_off = kh_off + (GATE == GT_DECAY ? kChunk * RP * 2 : 0);
   static constexpr int z_off = a_off + kChunk * CP * 2;
   static constexpr int gam_off = z_off + R * 4;
-  static constexpr int den_off = gam_off + R * 4;
-  static constexpr int bytes = den_off + kChunk * 4;
+  static constexpr int rs_off = gam_off + R * 4;   // [64] score row sums
+  static constexpr int zd_off = rs_off + kChunk * 4;  // [64] Q^ . z_prev
+  static constexpr int bytes = zd_off + kChunk * 4;
 };
 
 template <int R, int E, int GATE>
@@ -129,22 +138,25 @@ __device__ __forceinline__ bf16x8 tr_operand(char* sm, int tile_off, int stride,
 // write so the next chunk's loads overlap the current chunk's math.
 //
 // Two register layouts of a chunk:
-//  * row-major (elu+1 without the GLA gate): wave w holds tokens [16w, 16w+16),
-//    four lanes per token; lane l holds 8-feature blocks (l % 4) + 4 j of token
-//    16 w + l / 4, so each load instruction reads 16 rows, 64 contiguous bytes
-//    of each, and every row is consumed whole by two instructions;
+//  * row-major (elu+1 without the GLA gate): wave w holds TPW = 64 / NW tokens
+//    [TPW w, TPW (w+1)), LPT = NW lanes per token; lane l holds 8-feature
+//    blocks (l % LPT) + LPT j of token TPW w + l / LPT, so each load
+//    instruction reads TPW rows, 16 LPT contiguous bytes of each;
 //  * lane-per-token (GLA gate, whose scan runs across the 64 lanes): lane l
-//    holds token l, wave w holds features [w R/4, (w+1) R/4); V uses this
+//    holds token l, wave w holds features [w R/NW, (w+1) R/NW); V uses this
 //    layout for FAVOR+ too.
 // FAVOR+ inputs X (projected inside the kernel): wave w holds tokens
 // [16w, 16w+16), lane l token 16 w + l % 16, columns 32 ks + 8 (l / 16) .. + 7.
-template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q>
+template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW = 4>
 struct RawChunk {
-  static constexpr int FR = R / 4;       // features per wave (elu+1 lane-per-token layout)
-  static constexpr int EV = E / 4;       // value columns per wave
+  static constexpr int FR = R / NW;      // features per wave (lane-per-token layout)
+  static constexpr int EV = E / NW;      // value columns per wave
   static constexpr int KS = DK / 32;     // projection k-steps (FAVOR)
+  static constexpr int TPW = kChunk / NW;  // tokens per wave (row-major layout)
+  static constexpr int LPT = NW;           // lanes per token (row-major layout)
   static constexpr bool ELU = FMAP == FM_ELU1;
   static constexpr bool ROWMAJOR = ELU && GATE != GT_GLA;
+  // row-major: R / (8 LPT) blocks of 8 features per lane per row (= FR / 8)
   bf16x8 q[ELU && WITH_Q ? FR / 8 : 1];
   bf16x8 k[ELU ? FR / 8 : 1];
   bf16x8 g[GATE == GT_GLA ? FR / 8 : 1];
@@ -161,16 +173,16 @@ struct RawChunk {
   __device__ __forceinline__ void load(const CausalArgs& a, long long tok0, int t0, int row_end, int lane, int w) {
     const int g4 = lane >> 4, c16 = lane & 15;
     if constexpr (ROWMAJOR) {
-      const long long row = tok0 + min(t0 + 16 * w + (lane >> 2), row_end - 1);
+      const long long row = tok0 + min(t0 + TPW * w + lane / LPT, row_end - 1);
 #pragma unroll
-      for (int j = 0; j < R / 32; ++j) {
-        const int f0 = 8 * ((lane & 3) + 4 * j);
+      for (int j = 0; j < R / (8 * LPT); ++j) {
+        const int f0 = 8 * (lane % LPT + LPT * j);
         if constexpr (WITH_Q) q[j] = *reinterpret_cast<const bf16x8*>(a.Q + row * R + f0);
         k[j] = *reinterpret_cast<const bf16x8*>(a.K + row * R + f0);
       }
 #pragma unroll
-      for (int j = 0; j < E / 32; ++j)
-        v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * E + 8 * ((lane & 3) + 4 * j));
+      for (int j = 0; j < E / (8 * LPT); ++j)
+        v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * E + 8 * (lane % LPT + LPT * j));
       return;
     }
     {
@@ -205,22 +217,23 @@ struct RawChunk {
 //   K^, v, gam, logg).
 // L = valid tokens in the chunk. Rows t >= L get phi(k) = 0 and v = 0, and a
 // zero log-gate, so they add nothing to the state.
-template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q>
-__device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q>& raw, const CausalArgs& a,
-                                              int L, float lg2gam, char* sm, int q_off, int k_off,
-                                              int kh_off, int v_off, int gam_off, int logg_off,
+template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW>
+__device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>& raw,
+                                              const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
+                                              int k_off, int kh_off, int v_off, int gam_off, int logg_off,
                                               int lane, int w) {
-  using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q>;
+  using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
+  constexpr int LPT = Raw::LPT;
   constexpr int RP = R + kPad, EP = E + kPad;
   static_assert(FMAP == FM_ELU1, "FAVOR+ chunks use the kernels of chunked_favor.hpp");
   if constexpr (Raw::ROWMAJOR) {
-    const int t = 16 * w + (lane >> 2);
+    const int t = Raw::TPW * w + lane / LPT;
     const bool valid = t < L;
     float decay_k = 1.f;
     if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(L - 1 - t) * lg2gam);
 #pragma unroll
-    for (int j = 0; j < R / 32; ++j) {
-      const int f0 = 8 * ((lane & 3) + 4 * j);
+    for (int j = 0; j < R / (8 * LPT); ++j) {
+      const int f0 = 8 * (lane % LPT + LPT * j);
       float vq[8], vk[8], vkh[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -245,8 +258,8 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       }
     }
 #pragma unroll
-    for (int j = 0; j < E / 32; ++j)
-      lds<bf16x8>(sm, v_off + 2 * (t * EP + 8 * ((lane & 3) + 4 * j))) = keep_if(valid, raw.v[j]);
+    for (int j = 0; j < E / (8 * LPT); ++j)
+      lds<bf16x8>(sm, v_off + 2 * (t * EP + 8 * (lane % LPT + LPT * j))) = keep_if(valid, raw.v[j]);
     return;
   }
   const bool valid = lane < L;
@@ -301,30 +314,31 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
 // z <- Gamma z + K^^T 1. Wave w owns the z tiles rt = w ZT .. w ZT + ZT - 1
 // (16 rows each); lane (g, c) holds z[16 rt + 4 g + i] in Z[rt - w ZT][i]
 // (the same in every column lane c).
-template <int R>
+template <int R, int NW = 4>
 struct ZTiles {
-  static constexpr int ZT = R >= 64 ? R / 64 : 1;   // tiles per owning wave
-  static constexpr int OWNERS = R / (16 * ZT);      // waves that own z tiles
+  static constexpr int ZT = R >= 16 * NW ? R / (16 * NW) : 1;  // tiles per owning wave
+  static constexpr int OWNERS = R / (16 * ZT);                 // waves that own z tiles
 };
 
-// S (wave slab: rows all R, value columns [w E/4, (w+1) E/4)) and this wave's
+// S (wave slab: rows all R, value columns [w E/NW, (w+1) E/NW)) and this wave's
 // z tiles, past one chunk:
 //   no gate   S <- S + K~^T V                    z <- z + K~^T 1
 //   RetNet    S <- gamma^L S + K^^T V            (kh_off holds K^ rows)
 //   GLA       S <- Gamma (S + K~^T V)            Gamma = diag(e^{b_end}) from gam_off
 // Both operands come from row-major [token][column] tiles by transpose reads.
-template <int R, int E, int GATE>
-__device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (&Z)[ZTiles<R>::ZT], char* sm,
-                                             int kh_off, int v_off, int gam_off, float gscale, int lane, int w) {
-  constexpr int ZT = ZTiles<R>::ZT, RP = R + kPad, EP = E + kPad;
+// S is f32x4[R / 16][E / (16 NW)], Z is f32x4[ZTiles<R, NW>::ZT].
+template <int R, int E, int GATE, int NW, class SArr, class ZArr>
+__device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_off, int v_off, int gam_off,
+                                             float gscale, int lane, int w) {
+  constexpr int ZT = ZTiles<R, NW>::ZT, RP = R + kPad, EP = E + kPad, NEB = E / (16 * NW);
   const int g4 = lane >> 4;
-  const int ebase = w * (E / 4);
+  const int ebase = w * (E / NW);
   bf16x8 ones;
 #pragma unroll
   for (int u = 0; u < 8; ++u) ones[u] = (bf16)1.f;
-  bf16x8 vb[E / 64][2];
+  bf16x8 vb[NEB][2];
 #pragma unroll
-  for (int eb = 0; eb < E / 64; ++eb)
+  for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_operand(sm, v_off, EP, 32 * ks, ebase + 16 * eb, lane);
 #pragma unroll
@@ -338,7 +352,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (
       for (int i = 0; i < 4; ++i) gr[i] = lds<float>(sm, gam_off + 4 * (16 * rt + 4 * g4 + i));
     }
 #pragma unroll
-    for (int eb = 0; eb < E / 64; ++eb) {
+    for (int eb = 0; eb < NEB; ++eb) {
       f32x4 st = S[rt][eb];
       if constexpr (GATE == GT_DECAY) {
 #pragma unroll
@@ -354,7 +368,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (
     }
   }
   // this wave's z tiles, outside the tile loop so no branch on the wave index splits it
-  if (w < ZTiles<R>::OWNERS) {
+  if (w < ZTiles<R, NW>::OWNERS) {
 #pragma unroll
     for (int j = 0; j < ZT; ++j) {
       const int rt = w * ZT + j;
@@ -380,10 +394,10 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[R / 16][E / 64], f32x4 (
 }
 
 // z tiles of wave w to / from a flat [R] fp32 array (lanes with c == 0 write).
-template <int R>
-__device__ __forceinline__ void z_store(const f32x4 (&Z)[ZTiles<R>::ZT], float* dst, int lane, int w) {
-  constexpr int ZT = ZTiles<R>::ZT;
-  if (w < ZTiles<R>::OWNERS && (lane & 15) == 0) {
+template <int R, int NW, class ZArr>
+__device__ __forceinline__ void z_store(const ZArr& Z, float* dst, int lane, int w) {
+  constexpr int ZT = ZTiles<R, NW>::ZT;
+  if (w < ZTiles<R, NW>::OWNERS && (lane & 15) == 0) {
 #pragma unroll
     for (int j = 0; j < ZT; ++j)
 #pragma unroll
@@ -391,24 +405,25 @@ __device__ __forceinline__ void z_store(const f32x4 (&Z)[ZTiles<R>::ZT], float* 
   }
 }
 
-template <int R>
-__device__ __forceinline__ void z_load(f32x4 (&Z)[ZTiles<R>::ZT], const float* src, int lane, int w) {
-  constexpr int ZT = ZTiles<R>::ZT;
+template <int R, int NW, class ZArr>
+__device__ __forceinline__ void z_load(ZArr& Z, const float* src, int lane, int w) {
+  constexpr int ZT = ZTiles<R, NW>::ZT;
 #pragma unroll
   for (int j = 0; j < ZT; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      Z[j][i] = (src != nullptr && w < ZTiles<R>::OWNERS) ? src[16 * (w * ZT + j) + 4 * (lane >> 4) + i] : 0.f;
+      Z[j][i] = (src != nullptr && w < ZTiles<R, NW>::OWNERS) ? src[16 * (w * ZT + j) + 4 * (lane >> 4) + i] : 0.f;
 }
 
 // ---------------------------------------------------------------------------
 // Pass 1: each segment's own state contribution (segments 0 .. P-2).
 // ---------------------------------------------------------------------------
 template <int R, int E, int DK, int FMAP, int GATE>
-__global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
+__global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = SegLayout<R, E, GATE>;
-  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+  constexpr int NW = Waves<R, E>::NW, NEB = E / (16 * NW);
+  const int lane = lane_id(), w = wave_id<NW>(), tid = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
@@ -416,17 +431,17 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
   const int t_begin = s * a.seg_len;
   const int t_end = min(a.n, t_begin + a.seg_len);
   const long long tok0 = bh * a.n;
-  const int ebase = w * (E / 4);
+  const int ebase = w * (E / NW);
   float lg2gam = 0.f;
   if constexpr (GATE == GT_DECAY) lg2gam = log2f(a.gamma[h]);
 
-  f32x4 S[R / 16][E / 64];
+  f32x4 S[R / 16][NEB];
 #pragma unroll
   for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
-    for (int eb = 0; eb < E / 64; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 Z[ZTiles<R>::ZT];
-  z_load<R>(Z, nullptr, lane, w);
+    for (int eb = 0; eb < NEB; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 Z[ZTiles<R, NW>::ZT];
+  z_load<R, NW>(Z, nullptr, lane, w);
   if (tid < R) lds<float>(sm, LY::logg_off + 4 * tid) = 0.f;
   lds_barrier();
 
@@ -436,7 +451,7 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
   // so every path into a prelude has the same loads outstanding and the wait
   // before it covers only that buffer. A step past the last chunk does
   // nothing but its refill.
-  using Raw = RawChunk<R, E, DK, FMAP, GATE, false>;
+  using Raw = RawChunk<R, E, DK, FMAP, GATE, false, NW>;
   constexpr int DEPTH = 2;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw[DEPTH];
@@ -450,13 +465,13 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
     const bool live = ci < nch;
     const int L = min(kChunk, a.n - t0);
     if (live)
-      chunk_prelude<R, E, DK, FMAP, GATE, false>(rw, a, L, lg2gam, sm, 0, LY::k_off, 0, LY::v_off,
-                                                 LY::gam_off, LY::logg_off, lane, w);
+      chunk_prelude<R, E, DK, FMAP, GATE, false, NW>(rw, a, L, lg2gam, sm, 0, LY::k_off, 0, LY::v_off,
+                                                     LY::gam_off, LY::logg_off, lane, w);
     rw.load(a, tok0, t0 + DEPTH * kChunk, t_end, lane, w);
     if (live) {
       lds_barrier();
       const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-      state_update<R, E, GATE>(S, Z, sm, LY::k_off, LY::v_off, LY::gam_off, gsc, lane, w);
+      state_update<R, E, GATE, NW>(S, Z, sm, LY::k_off, LY::v_off, LY::gam_off, gsc, lane, w);
       lds_barrier();
     }
   };
@@ -469,10 +484,10 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
 #pragma unroll
   for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
-    for (int eb = 0; eb < E / 64; ++eb)
+    for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
-  z_store<R>(Z, a.z_out + slot * R, lane, w);
+  z_store<R, NW>(Z, a.z_out + slot * R, lane, w);
   if constexpr (GATE == GT_GLA) {
     if (tid < R) a.logG_out[slot * R + tid] = lds<float>(sm, LY::logg_off + 4 * tid);
   }
@@ -482,11 +497,12 @@ __global__ __launch_bounds__(256) void causal_segment_state(CausalArgs a) {
 // Pass 3: outputs of one segment, starting from its chained state.
 // ---------------------------------------------------------------------------
 template <int R, int E, int DK, int FMAP, int GATE>
-__global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
+__global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FwdLayout<R, E, GATE>;
-  constexpr int RP = LY::RP, EP = LY::EP, NEB = E / 64, KP = R / 32;
-  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+  constexpr int NW = Waves<R, E>::NW;
+  constexpr int RP = LY::RP, EP = LY::EP, NEB = E / (16 * NW), KP = R / 32;
+  const int lane = lane_id(), w = wave_id<NW>(), tid = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
@@ -494,13 +510,13 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
   const int t_begin = s * a.seg_len;
   const int t_end = min(a.n, t_begin + a.seg_len);
   const long long tok0 = bh * a.n;
-  const int ebase = w * (E / 4);
+  const int ebase = w * (E / NW);
   float lg2gam = 0.f;
   if constexpr (GATE == GT_DECAY) lg2gam = log2f(a.gamma[h]);
 
   // ---- state carried in
   f32x4 S[R / 16][NEB];
-  f32x4 Z[ZTiles<R>::ZT];
+  f32x4 Z[ZTiles<R, NW>::ZT];
   if (a.S_in != nullptr) {
     const float* Sp = a.S_in + bh * a.in_head + s * a.in_seg;
 #pragma unroll
@@ -515,8 +531,8 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  z_load<R>(Z, a.S_in != nullptr ? a.z_in + (bh * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
-  z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
+  z_load<R, NW>(Z, a.S_in != nullptr ? a.z_in + (bh * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
+  z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
   // bf16 image of the state as the A operand of O^T += S^T Q^^T: k-slot j of
   // lane (g, c) is feature 32p + 4g + j (j < 4) or 32p + 16 + 4g + (j - 4).
   bf16x8 Sop[KP][NEB];
@@ -531,7 +547,7 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
 
   // Loads run DEPTH chunks ahead (two buffers when the registers allow),
   // refilled unconditionally as in pass 1.
-  using Raw = RawChunk<R, E, DK, FMAP, GATE, true>;
+  using Raw = RawChunk<R, E, DK, FMAP, GATE, true, NW>;
   constexpr int DEPTH = 1;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw0, raw1;
@@ -543,61 +559,70 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
     const bool live = ci < nch;
     const int L = min(kChunk, a.n - t0);
     if (live)
-      chunk_prelude<R, E, DK, FMAP, GATE, true>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
-                                                LY::v_off, LY::gam_off, 0, lane, w);
+      chunk_prelude<R, E, DK, FMAP, GATE, true, NW>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
+                                                    LY::v_off, LY::gam_off, 0, lane, w);
     // the raw registers are free again: this refill flies during the next DEPTH chunks
     raw.load(a, tok0, t0 + DEPTH * kChunk, t_end, lane, w);
     if (!live) return;
     lds_barrier();
 
-    // ---- scores for query rows [16w, 16w+16): A^T tiles = K~_c Q~_w^T
+    // ---- scores for query rows [16 qw, 16 qw + 16): A^T tiles = K~_c Q~_qw^T
+    // (waves 0..3), and Q^ . z_prev for the same rows (with 8 waves, by waves 4..7)
     {
+      const int qw = w & 3;
+      const bool scores = NW == 4 || w < 4, zdot = NW == 4 || w >= 4;
       bf16x8 qop[KP];
 #pragma unroll
-      for (int ks = 0; ks < KP; ++ks) qop[ks] = lds<bf16x8>(sm, LY::q_off + 2 * ((16 * w + c16) * RP + 32 * ks + 8 * g4));
-      const int q = 16 * w + c16;
-      float rs = 0.f;
-      float ginv[4] = {1.f, 1.f, 1.f, 1.f};  // gamma^(-i), i = 0..3
-      if constexpr (GATE == GT_DECAY) {
+      for (int ks = 0; ks < KP; ++ks) qop[ks] = lds<bf16x8>(sm, LY::q_off + 2 * ((16 * qw + c16) * RP + 32 * ks + 8 * g4));
+      const int q = 16 * qw + c16;
+      if (scores) {
+        float rs = 0.f;
+        float ginv[4] = {1.f, 1.f, 1.f, 1.f};  // gamma^(-i), i = 0..3
+        if constexpr (GATE == GT_DECAY) {
 #pragma unroll
-        for (int i = 1; i < 4; ++i) ginv[i] = exp2f(-float(i) * lg2gam);
+          for (int i = 1; i < 4; ++i) ginv[i] = exp2f(-float(i) * lg2gam);
+        }
+        for (int c = 0; c <= qw; ++c) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KP; ++ks)
+            acc = mfma16(lds<bf16x8>(sm, LY::k_off + 2 * ((16 * c + c16) * RP + 32 * ks + 8 * g4)), qop[ks], acc);
+          // acc[i] = A[q][key], key = 16c + 4g + i
+          float gbase = 1.f;
+          if constexpr (GATE == GT_DECAY) gbase = exp2f(float(q - 16 * c - 4 * g4) * lg2gam);
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = 16 * c + 4 * g4 + i;
+            v[i] = acc[i];
+            if (c == qw && key > q) v[i] = 0.f;  // only the diagonal tile straddles the mask
+            if constexpr (GATE == GT_DECAY) v[i] *= gbase * ginv[i];
+          }
+          // bf16 scores, and the row sum of exactly those rounded values
+          const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
+          rs += (lo_bf16_f32(p01) + hi_bf16_f32(p01)) + (lo_bf16_f32(p23) + hi_bf16_f32(p23));
+          typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+          lds<u32x2>(sm, LY::a_off + 2 * (q * CP + 16 * c + 4 * g4)) = u32x2{p01, p23};
+        }
+        if ((qw & 1) == 0) lds<bf16x4>(sm, LY::a_off + 2 * (q * CP + 16 * (qw + 1) + 4 * g4)) = bf16x4{};
+        rs = sum_over_groups(rs);
+        if (g4 == 0) lds<float>(sm, LY::rs_off + 4 * q) = rs;
       }
-      for (int c = 0; c <= w; ++c) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (zdot) {
+        float zd = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KP; ++ks)
-          acc = mfma16(lds<bf16x8>(sm, LY::k_off + 2 * ((16 * c + c16) * RP + 32 * ks + 8 * g4)), qop[ks], acc);
-        // acc[i] = A[q][key], key = 16c + 4g + i
-        float gbase = 1.f;
-        if constexpr (GATE == GT_DECAY) gbase = exp2f(float(q - 16 * c - 4 * g4) * lg2gam);
-        float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * c + 4 * g4 + i;
-          v[i] = acc[i];
-          if (c == w && key > q) v[i] = 0.f;  // only the diagonal tile straddles the mask
-          if constexpr (GATE == GT_DECAY) v[i] *= gbase * ginv[i];
-        }
-        // bf16 scores, and the row sum of exactly those rounded values
-        const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
-        rs += (lo_bf16_f32(p01) + hi_bf16_f32(p01)) + (lo_bf16_f32(p23) + hi_bf16_f32(p23));
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        lds<u32x2>(sm, LY::a_off + 2 * (q * CP + 16 * c + 4 * g4)) = u32x2{p01, p23};
+          for (int j = 0; j < 8; ++j)
+            zd += to_f32(qop[ks][j]) * lds<float>(sm, LY::z_off + 4 * (32 * ks + 8 * g4 + j));
+        zd = sum_over_groups(zd);
+        if constexpr (GATE == GT_DECAY) zd *= exp2f(float(q + 1) * lg2gam);
+        if (g4 == 0) lds<float>(sm, LY::zd_off + 4 * q) = zd;
       }
-      if ((w & 1) == 0) lds<bf16x4>(sm, LY::a_off + 2 * (q * CP + 16 * (w + 1) + 4 * g4)) = bf16x4{};
-      float zd = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KP; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) zd += to_f32(qop[ks][j]) * lds<float>(sm, LY::z_off + 4 * (32 * ks + 8 * g4 + j));
-      rs = sum_over_groups(rs);
-      zd = sum_over_groups(zd);
-      if constexpr (GATE == GT_DECAY) zd *= exp2f(float(q + 1) * lg2gam);
-      if (g4 == 0) lds<float>(sm, LY::den_off + 4 * q) = rs + zd + a.eps;
     }
     lds_barrier();
 
-    // ---- outputs for value columns [w E/4, (w+1) E/4): O^T = S^T Q^^T + V^T A^T
+    // ---- outputs for value columns [w E/NW, (w+1) E/NW): O^T = S^T Q^^T + V^T A^T
     rebuild_sop();  // built here so it is not live across the prelude and the scores
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
@@ -608,7 +633,7 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
         qb[p] = cat8(lds<bf16x4>(sm, LY::q_off + 2 * (q * RP + 32 * p + 4 * g4)),
                      lds<bf16x4>(sm, LY::q_off + 2 * (q * RP + 32 * p + 16 + 4 * g4)));
       // one correctly rounded reciprocal per row; outputs are fl(O * fl(1 / den))
-      const float inv_den = 1.f / lds<float>(sm, LY::den_off + 4 * q);
+      const float inv_den = 1.f / (lds<float>(sm, LY::rs_off + 4 * q) + lds<float>(sm, LY::zd_off + 4 * q) + a.eps);
       float isc = 1.f;
       if constexpr (GATE == GT_DECAY) isc = exp2f(float(q + 1) * lg2gam);
 #pragma unroll
@@ -634,9 +659,9 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
 
     // ---- carry the state past this chunk
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE>(S, Z, sm, GATE == GT_DECAY ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off, gsc,
-                             lane, w);
-    z_store<R>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
+    state_update<R, E, GATE, NW>(S, Z, sm, GATE == GT_DECAY ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
+                                 gsc, lane, w);
+    z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
     lds_barrier();
   };
   if constexpr (DEPTH == 2) {
@@ -656,7 +681,7 @@ __global__ __launch_bounds__(256) void causal_chunk_forward(CausalArgs a) {
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
-    z_store<R>(Z, a.z_out + bh * R, lane, w);
+    z_store<R, NW>(Z, a.z_out + bh * R, lane, w);
   }
 }
 
@@ -689,7 +714,7 @@ la_status run_causal(const FwdPlan& p) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
         hipSuccess)
       return LA_ERR_HIP;
-    hipLaunchKernelGGL(k1, dim3(p.P - 1, BH), dim3(256), lds1, p.stream, a1);
+    hipLaunchKernelGGL(k1, dim3(p.P - 1, BH), dim3(64 * Waves<R, E>::NW), lds1, p.stream, a1);
     if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     la_status st = launch_segment_scan(p);
     if (st != LA_OK) return st;
@@ -710,7 +735,7 @@ la_status run_causal(const FwdPlan& p) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k3), hipFuncAttributeMaxDynamicSharedMemorySize, lds3) !=
       hipSuccess)
     return LA_ERR_HIP;
-  hipLaunchKernelGGL(k3, dim3(p.P, BH), dim3(256), lds3, p.stream, a);
+  hipLaunchKernelGGL(k3, dim3(p.P, BH), dim3(64 * Waves<R, E>::NW), lds3, p.stream, a);
   if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
   return LA_OK;
 }

@@ -65,10 +65,11 @@ __device__ __forceinline__ int opaque_lane(int lane) {
   asm volatile("" : "+v"(lane));
   return lane & 63;
 }
-// Wave index in a 256-thread workgroup. The mask gives the compiler its range
+// Wave index in a workgroup of NW waves. The mask gives the compiler its range
 // (readfirstlane alone hides it), so LDS addresses built from it keep their
 // constant parts in the instruction's offset field instead of in registers.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3; }
+template <int NW = 4>
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1); }
 
 // Sum over the four lanes {c, c+16, c+32, c+48} that share c = lane % 16.
 __device__ __forceinline__ float sum_over_groups(float x) {
