@@ -18,9 +18,9 @@
 //
 // LDS tiles are row-major [token][column]. Operands that contract over tokens
 // (phi(k)^T in the state update, V^T in the intra-chunk product) come from
-// them by transpose reads (tr_operand). The chunk's raw X rows are staged in
-// LDS once (each wave loads a quarter of them) with the per-token shift
-// |x|^2/2 + ln(r)/2, so the register prefetch of the next chunk stays small.
+// them by transpose reads (tr_operand). Each wave projects its own 16 tokens
+// (whose raw rows it loaded) onto all features of a block, so the raw rows
+// never pass through LDS; omega comes from the cache.
 #pragma once
 
 #include "chunked.hpp"
@@ -33,14 +33,6 @@ struct FavorBlock {
   static constexpr int NFB = R / FB;   // blocks
   static constexpr int FP = FB + kPad;  // row stride of the [token][feature] tiles
   static constexpr int FT = FB / 16;   // 16-feature tiles per block
-};
-
-// Staged raw rows of one side: X [64][DK + kPad] bf16 and the shift [64] fp32.
-template <int DK>
-struct XStage {
-  static constexpr int XP = DK + kPad;
-  static constexpr int bytes = kChunk * XP * 2 + kChunk * 4;
-  static constexpr int sh = kChunk * XP * 2;  // offset of the shifts
 };
 
 // Output pass. kwh/kwl (RetNet only) hold the decay-weighted key features of
@@ -65,15 +57,10 @@ struct FavorFwdLayout {
   static constexpr int zl_off = zh_off + R * 2 + 16;
   static constexpr int rsp_off = zl_off + R * 2 + 16;       // [4][64] partial score row sums
   static constexpr int zdp_off = rsp_off + 4 * kChunk * 4;  // [64] phi(q) . z
-  static constexpr int xq_off = zdp_off + kChunk * 4;       // XStage<DK> of the queries
-  // The score tile [64][CP] shares the query stage: it is written after the
-  // chunk's last projection and read before the next chunk is staged.
-  static constexpr int a_off = xq_off;
+  static constexpr int a_off = zdp_off + kChunk * 4;       // [64][CP] masked scores
+  static constexpr int bytes = a_off + kChunk * CP * 2;
   template <int DK>
-  static constexpr int xk_off_dk =
-      xq_off + (XStage<DK>::bytes > kChunk * CP * 2 ? XStage<DK>::bytes : kChunk * CP * 2);
-  template <int DK>
-  static constexpr int bytes_dk = xk_off_dk<DK> + XStage<DK>::bytes;
+  static constexpr int bytes_dk = bytes;
 };
 
 // Segment-state pass: kh/kl hold the (decay-weighted) key features.
@@ -84,35 +71,31 @@ struct FavorSegLayout {
   static constexpr int kh_off = 0;
   static constexpr int kl_off = kh_off + kChunk * F::FP * 2 + 16;
   static constexpr int v_off = kl_off + kChunk * F::FP * 2 + 16;
-  static constexpr int xk_off = v_off + kChunk * EP * 2;  // XStage<DK> of the keys
+  static constexpr int bytes = v_off + kChunk * EP * 2;
   template <int DK>
-  static constexpr int bytes_dk = xk_off + XStage<DK>::bytes;
+  static constexpr int bytes_dk = bytes;
 };
 
 // Per-lane byte offsets of every LDS access pattern, built once per feature
 // block from an opaque lane index (opaque_lane): each access then adds only
 // compile-time or wave-uniform constants, which fold into the instruction.
-template <int FP, int EP, int XP>
+template <int FP, int EP>
 struct FavorLane {
   int g4, c16;
   int frag;   // row c, 8 columns at 8 g of an FP-stride tile (row-fragment operands)
-  int half;   // row c, 4 columns at 4 g of an FP-stride tile (inter-chunk B operand)
-  int put;    // row c, 4 columns at 16 w + 4 g of an FP-stride tile (feature writes)
+  int half;   // row c, 4 columns at 4 g of an FP-stride tile (inter-chunk B operand, feature writes)
   int trf;    // transpose reads of FP-stride tiles
   int tre;    // transpose reads of the EP-stride V tile
-  int xfrag;  // row c, 8 columns at 8 g of an X stage
   int afrag;  // row c, 8 columns at 8 g of the score tile
   int a4;     // row c, 4 columns at 4 g of the score tile
   int l4;     // 4 c (per-row floats)
-  __device__ __forceinline__ FavorLane(int lane, int w) {
+  __device__ __forceinline__ FavorLane(int lane) {
     g4 = lane >> 4;
     c16 = lane & 15;
     frag = 2 * (c16 * FP + 8 * g4);
     half = 2 * (c16 * FP + 4 * g4);
-    put = 2 * (c16 * FP + 4 * g4) + 32 * w;
     trf = 2 * ((8 * g4 + (c16 >> 2)) * FP + 4 * (c16 & 3));
     tre = 2 * ((8 * g4 + (c16 >> 2)) * EP + 4 * (c16 & 3));
-    xfrag = 2 * (c16 * XP + 8 * g4);
     afrag = 2 * (c16 * CP + 8 * g4);
     a4 = 2 * (c16 * CP + 4 * g4);
     l4 = 4 * c16;
@@ -127,25 +110,22 @@ __device__ __forceinline__ bf16x8 tr_at(char* sm, int addr, int stride_bytes) {
   return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
 }
 
-// Stage this wave's quarter of the raw rows (tokens 16 w .. 16 w + 15) and
-// their shifts in base 2, (|x|^2/2 + ln(r)/2) log2(e).
+// The raw rows of this wave's tokens (16 w + c) as projection B operands,
+// copied out of the prefetch registers, and each token's shift in base 2,
+// (|x|^2/2 + ln(r)/2) log2(e).
 template <int R, int DK>
-__device__ __forceinline__ void favor_stage_x(const bf16x8 (&x)[DK / 32], char* sm, int x_off, int lane, int w) {
-  using X = XStage<DK>;
-  const int g4 = lane >> 4, c16 = lane & 15;
-  const int t = 16 * w + c16;
+__device__ __forceinline__ float favor_take_x(const bf16x8 (&raw)[DK / 32], bf16x8 (&x)[DK / 32]) {
   float ss = 0.f;
 #pragma unroll
   for (int ks = 0; ks < DK / 32; ++ks) {
-    lds<bf16x8>(sm, x_off + 2 * (t * X::XP + 32 * ks + 8 * g4)) = x[ks];
+    x[ks] = raw[ks];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float xv = to_f32(x[ks][u]);
+      const float xv = to_f32(raw[ks][u]);
       ss += xv * xv;
     }
   }
-  ss = sum_over_groups(ss);
-  if (g4 == 0) lds<float>(sm, x_off + X::sh + 4 * t) = (0.5f * ss + 0.5f * __logf(float(R))) * 1.44269504f;
+  return (0.5f * sum_over_groups(ss) + 0.5f * __logf(float(R))) * 1.44269504f;
 }
 
 // hi/lo bf16 pairs of four floats (packed two per dword).
@@ -183,37 +163,46 @@ __device__ __forceinline__ bf16x4 keep_if(bool ok, bf16x4 x) {
   return __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, x) & m);
 }
 
-// FAVOR+ features of one side of a chunk for this wave's 16 features of block
-// fb (block features 16 w .. 16 w + 15), as hi/lo pairs in row-major
+// omega rows of feature block fb as projection A operands: om[ft][ks] holds
+// row 64 fb + 16 ft + c, columns 32 ks + 8 g .. + 7 (the whole omega is 32 KB
+// or less: cache-resident). Loaded one block ahead of its use.
+template <int R, int DK, class LN>
+__device__ __forceinline__ void favor_load_omega(bf16x8 (&om)[FavorBlock<R>::FT][DK / 32], const bf16* omega, int fb,
+                                                 const LN& ln) {
+  const bf16* orow = omega + (long long)(fb * FavorBlock<R>::FB + ln.c16) * DK + 8 * ln.g4;
+#pragma unroll
+  for (int ft = 0; ft < FavorBlock<R>::FT; ++ft)
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) om[ft][ks] = *reinterpret_cast<const bf16x8*>(orow + 16 * ft * DK + 32 * ks);
+}
+
+// FAVOR+ features of one side of a chunk for this wave's 16 tokens (16 w + c)
+// and all 64 features of block fb, as hi/lo pairs in row-major
 // [token][feature] tiles: phi = 2^(P log2(e) - shift2) with P = x . w on the
-// matrix cores. Keys past the chunk's valid rows are zero. With WEIGHTED,
-// keys are also written multiplied by gamma^(L-1-t) (RetNet state update)
-// into (wh_off, wl_off); with ONLY_WEIGHTED that is the only copy.
+// matrix cores (x: this wave's raw rows, omega rows from the cache). Keys past
+// the chunk's valid rows are zero. With WEIGHTED, keys are also written
+// multiplied by gamma^(L-1-t) (RetNet state update) into (wh_off, wl_off);
+// with ONLY_WEIGHTED that is the only copy.
 template <int R, int DK, bool IS_K, bool WEIGHTED, bool ONLY_WEIGHTED, class LN>
-__device__ __forceinline__ void favor_project(const LN& ln, int x_off, const bf16* omega, int fb, int L, float lg2gam,
+__device__ __forceinline__ void favor_project(const LN& ln, const bf16x8 (&x)[DK / 32], float shift2,
+                                              const bf16x8 (&om)[FavorBlock<R>::FT][DK / 32], int L, float lg2gam,
                                               char* sm, int hi_off, int lo_off, int wh_off, int wl_off, int w) {
   using F = FavorBlock<R>;
-  using X = XStage<DK>;
   constexpr int KS = DK / 32, FP = F::FP;
-  // omega rows of this wave's features (the whole omega is 32 KB or less: cache-resident)
-  bf16x8 om[KS];
-  const bf16* orow = omega + (long long)(fb * F::FB + 16 * w + ln.c16) * DK + 8 * ln.g4;
+  const int t = 16 * w + ln.c16;
+  const bool ok = !IS_K || t < L;
+  float wt = 1.f;
+  if constexpr (WEIGHTED) wt = exp2f(float(L - 1 - t) * lg2gam);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) om[ks] = *reinterpret_cast<const bf16x8*>(orow + 32 * ks);
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const float shift2 = lds<float>(sm, x_off + X::sh + 64 * tt + ln.l4);
+  for (int ft = 0; ft < F::FT; ++ft) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc = mfma16(om[ks], lds<bf16x8>(sm, x_off + 32 * tt * X::XP + 64 * ks + ln.xfrag), acc);
-    // acc[i] = P[token 16 tt + c][block feature 16 w + 4 g + i]
+    for (int ks = 0; ks < KS; ++ks) acc = mfma16(om[ft][ks], x[ks], acc);
+    // acc[i] = P[token t][block feature 16 ft + 4 g + i]
     float f[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], 1.44269504f, -shift2));
-    const int t = 16 * tt + ln.c16;
-    const bool ok = !IS_K || t < L;
-    const int at = 32 * tt * FP + ln.put;
+    const int at = 32 * w * FP + 32 * ft + ln.half;
     if constexpr (!ONLY_WEIGHTED) {
       bf16x4 h, l;
       split4(f, h, l);
@@ -221,7 +210,6 @@ __device__ __forceinline__ void favor_project(const LN& ln, int x_off, const bf1
       lds<bf16x4>(sm, lo_off + at) = keep_if(ok, l);
     }
     if constexpr (WEIGHTED) {
-      const float wt = exp2f(float(L - 1 - t) * lg2gam);
       float fw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) fw[i] = f[i] * wt;
@@ -230,7 +218,7 @@ __device__ __forceinline__ void favor_project(const LN& ln, int x_off, const bf1
       lds<bf16x4>(sm, wh_off + at) = keep_if(ok, h);
       lds<bf16x4>(sm, wl_off + at) = keep_if(ok, l);
     }
-    __builtin_amdgcn_sched_barrier(0);  // one token tile at a time: bounded live registers
+    __builtin_amdgcn_sched_barrier(0);  // one feature tile at a time: bounded live registers
   }
 }
 
@@ -336,11 +324,17 @@ __device__ __forceinline__ void favor_z_load(f32x4 (&Z)[FavorBlock<R>::NFB], con
 
 // The ten lower-triangle 16x16 score tiles (query tile qi, key tile kj <= qi)
 // dealt to the four waves as 3, 3, 2, 2 tiles, no wave holding two tiles of
-// the same query rows: slot s of wave w is tile s * 4 + w of the row-major
-// enumeration (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3).
-__device__ __forceinline__ int score_tile_qi(int idx) { return idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3; }
-__device__ __forceinline__ int score_tile_kj(int idx) {
-  return idx - (idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 3 : 6);
+// the same query rows, and slot 0 of wave w on query tile w (whose features
+// phi(q) . z also reads):
+//   wave 0: (0,0) (3,0) (2,0)   wave 1: (1,0) (3,1) (2,1)
+//   wave 2: (2,2) (3,2)         wave 3: (3,3) (1,1)
+__device__ __forceinline__ void score_tiles(int w, int (&qi)[3], int (&kj)[3]) {
+  qi[0] = w;
+  kj[0] = w < 2 ? 0 : w;
+  qi[1] = w == 3 ? 1 : 3;
+  kj[1] = w == 3 ? 1 : w;
+  qi[2] = 2;  // waves 0 and 1 only
+  kj[2] = w;
 }
 
 // ---------------------------------------------------------------------------
@@ -351,7 +345,7 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FavorSegLayout<R, E>;
   using F = FavorBlock<R>;
-  using LN = FavorLane<F::FP, E + kPad, DK + kPad>;
+  using LN = FavorLane<F::FP, E + kPad>;
   const int lane = lane_id(), w = wave_id();
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
@@ -374,21 +368,23 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
 
   RawChunk<R, E, DK, FM_FAVOR, GT_NONE, false> raw;
   raw.load(a, tok0, t_begin, t_end, lane, w);
+  bf16x8 om[F::FT][DK / 32];
+  favor_load_omega<R, DK>(om, a.omega, 0, LN(lane));
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int L = min(kChunk, a.n - t0);
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    favor_stage_x<R, DK>(raw.xk, sm, LY::xk_off, lane, w);
+    bf16x8 xk[DK / 32];
+    const float shk = favor_take_x<R, DK>(raw.xk, xk);
     favor_write_v<E>(raw.v, sm, LY::v_off, lane, w);
     // the raw registers are free: the next chunk's loads fly during this one
     raw.load(a, tok0, t0 + kChunk, t_end, lane, w);
-    lds_barrier();
 #pragma unroll
     for (int fb = 0; fb < F::NFB; ++fb) {
-      const LN ln(opaque_lane(lane), w);
+      const LN ln(opaque_lane(lane));
       // pass 1 keeps only the keys of the state update (decay-weighted for RetNet)
-      favor_project<R, DK, true, GATE == GT_DECAY, GATE == GT_DECAY>(ln, LY::xk_off, a.omega, fb, L, lg2gam, sm,
-                                                                     LY::kh_off, LY::kl_off, LY::kh_off, LY::kl_off,
-                                                                     w);
+      favor_project<R, DK, true, GATE == GT_DECAY, GATE == GT_DECAY>(ln, xk, shk, om, L, lg2gam, sm, LY::kh_off,
+                                                                     LY::kl_off, LY::kh_off, LY::kl_off, w);
+      favor_load_omega<R, DK>(om, a.omega, fb + 1 < F::NFB ? fb + 1 : 0, ln);  // next block (block 0 of the next chunk)
       lds_barrier();
       favor_state_block<R, E>(ln, S, Z[fb], fb, sm, LY::kh_off, LY::kl_off, LY::v_off, gsc, w);
       lds_barrier();
@@ -413,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FavorFwdLayout<R, E, GATE>;
   using F = FavorBlock<R>;
-  using LN = FavorLane<F::FP, E + kPad, DK + kPad>;
+  using LN = FavorLane<F::FP, E + kPad>;
   constexpr int FP = F::FP, EP = LY::EP, NEB = E / 64, KPB = F::FB / 32;
   const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -451,24 +447,19 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   // this wave's score tiles
   const int nslot = w < 2 ? 3 : 2;
   int sqi[3], skj[3];
-#pragma unroll
-  for (int sl = 0; sl < 3; ++sl) {
-    const int idx = min(4 * sl + w, 9);
-    sqi[sl] = score_tile_qi(idx);
-    skj[sl] = score_tile_kj(idx);
-  }
+  score_tiles(w, sqi, skj);
 
-  constexpr int xq_off = LY::xq_off, xk_off = LY::template xk_off_dk<DK>;
   RawChunk<R, E, DK, FM_FAVOR, GT_NONE, true> raw;
   raw.load(a, tok0, t_begin, t_end, lane, w);
+  bf16x8 om[F::FT][DK / 32];
+  favor_load_omega<R, DK>(om, a.omega, 0, LN(lane));
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int L = min(kChunk, a.n - t0);
-    favor_stage_x<R, DK>(raw.xq, sm, xq_off, lane, w);
-    favor_stage_x<R, DK>(raw.xk, sm, xk_off, lane, w);
+    bf16x8 xq[DK / 32], xk[DK / 32];
+    const float shq = favor_take_x<R, DK>(raw.xq, xq), shk = favor_take_x<R, DK>(raw.xk, xk);
     favor_write_v<E>(raw.v, sm, LY::v_off, lane, w);
     // the raw registers are free: the next chunk's loads fly during this one
     raw.load(a, tok0, t0 + kChunk, t_end, lane, w);
-    lds_barrier();
     f32x4 sacc[3];
 #pragma unroll
     for (int sl = 0; sl < 3; ++sl) sacc[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -481,37 +472,33 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
 
 #pragma unroll
     for (int fb = 0; fb < F::NFB; ++fb) {
-      const LN ln(opaque_lane(lane), w);
+      const LN ln(opaque_lane(lane));
       const bool last = fb == F::NFB - 1;
-      favor_project<R, DK, false, false, false>(ln, xq_off, a.omega, fb, L, lg2gam, sm, LY::qh_off, LY::ql_off, 0, 0,
-                                                w);
-      favor_project<R, DK, true, GATE == GT_DECAY, false>(ln, xk_off, a.omega, fb, L, lg2gam, sm, LY::kh_off,
-                                                          LY::kl_off, LY::kwh_off, LY::kwl_off, w);
+      favor_project<R, DK, false, false, false>(ln, xq, shq, om, L, lg2gam, sm, LY::qh_off, LY::ql_off, 0, 0, w);
+      favor_project<R, DK, true, GATE == GT_DECAY, false>(ln, xk, shk, om, L, lg2gam, sm, LY::kh_off, LY::kl_off,
+                                                          LY::kwh_off, LY::kwl_off, w);
+      favor_load_omega<R, DK>(om, a.omega, fb + 1 < F::NFB ? fb + 1 : 0, ln);  // next block (block 0 of the next chunk)
       lds_barrier();
 
-      // ---- scores over this block's features: A^T tiles = K~_kj Q~_qi^T
+      // ---- scores over this block's features: A^T tiles = K~_kj Q~_qi^T, and
+      // phi(q) . z_prev for query tile w (slot 0) on the matrix cores, z as a
+      // hi/lo column replicated over the 16 output columns
 #pragma unroll
       for (int sl = 0; sl < 3; ++sl) {
         if (sl < nslot) {
           const int ko = 32 * skj[sl] * FP + ln.frag, qo = 32 * sqi[sl] * FP + ln.frag;
 #pragma unroll
-          for (int ks = 0; ks < KPB; ++ks)
-            sacc[sl] = mfma3(lds<bf16x8>(sm, LY::kh_off + 64 * ks + ko), lds<bf16x8>(sm, LY::kl_off + 64 * ks + ko),
-                             lds<bf16x8>(sm, LY::qh_off + 64 * ks + qo), lds<bf16x8>(sm, LY::ql_off + 64 * ks + qo),
-                             sacc[sl]);
+          for (int ks = 0; ks < KPB; ++ks) {
+            const bf16x8 qh = lds<bf16x8>(sm, LY::qh_off + 64 * ks + qo), ql = lds<bf16x8>(sm, LY::ql_off + 64 * ks + qo);
+            sacc[sl] = mfma3(lds<bf16x8>(sm, LY::kh_off + 64 * ks + ko), lds<bf16x8>(sm, LY::kl_off + 64 * ks + ko), qh,
+                             ql, sacc[sl]);
+            if (sl == 0) {
+              const int zo = 2 * (64 * fb + 32 * ks + 8 * ln.g4);
+              zacc = mfma3(qh, ql, lds<bf16x8>(sm, LY::zh_off + zo), lds<bf16x8>(sm, LY::zl_off + zo), zacc);
+            }
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
-      }
-      // ---- phi(q) . z_prev for query tile w on the matrix cores (z as a
-      // hi/lo column replicated over the 16 output columns)
-      {
-        const int qo = 32 * w * FP + ln.frag;
-#pragma unroll
-        for (int ks = 0; ks < KPB; ++ks) {
-          const int zo = 2 * (64 * fb + 32 * ks + 8 * ln.g4);
-          zacc = mfma3(lds<bf16x8>(sm, LY::qh_off + 64 * ks + qo), lds<bf16x8>(sm, LY::ql_off + 64 * ks + qo),
-                       lds<bf16x8>(sm, LY::zh_off + zo), lds<bf16x8>(sm, LY::zl_off + zo), zacc);
-        }
       }
 
       __builtin_amdgcn_sched_barrier(0);  // phases stay apart: bounded register live ranges

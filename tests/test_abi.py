@@ -83,7 +83,7 @@ int main(void) {{
     # 128 x 128 states: one output-pass workgroup per CU (registers) -> 256 groups
     (2, 8, 8192, 128, 128, "elu1", 128, "decay", 16, 512),    # RetNet workload
     (2, 16, 16384, 128, 128, "elu1", 128, "gla", 8, 2048),    # GLA workload
-    # FAVOR+ r=256: 65.8 KB (64-feature blocks, staged inputs) -> 2 per CU -> 512 groups
+    # FAVOR+ r=256: 56.3 KB (64-feature blocks) -> 2 per CU -> 512 groups
     (1, 8, 32768, 64, 64, "favor", 256, "none", 64, 512),     # FAVOR+ workload
     (1, 1, 1, 64, 64, "elu1", 64, "none", 1, 64),
     (1, 1, 65, 64, 64, "elu1", 64, "none", 2, 64),
