@@ -10,17 +10,19 @@
 //     reads and state updates keep ~16 significant bits on the matrix cores;
 //   * the feature axis is processed in blocks of 64 features: the hi/lo tiles
 //     of one block are the only per-block LDS, which keeps a workgroup near
-//     57 KB so two of them share a CU. Everything that contracts over the
+//     54 KB so two of them share a CU. Everything that contracts over the
 //     features (scores, inter-chunk product, z . phi(q)) accumulates across
 //     blocks in registers.
 // The projection X w^T runs on the matrix cores (exact bf16 products, fp32
 // accumulation); |x|^2/2 and ln(r)/2 are subtracted before the exponential.
 //
-// LDS tiles are row-major [token][column]. Operands that contract over tokens
-// (phi(k)^T in the state update, V^T in the intra-chunk product) come from
-// them by transpose reads (tr_operand). Each wave projects its own 16 tokens
-// (whose raw rows it loaded) onto all features of a block, so the raw rows
-// never pass through LDS; omega comes from the cache.
+// LDS tiles are [token][column]. Operands that contract over tokens (phi(k)^T
+// in the state update, V^T in the intra-chunk product) come from them by
+// transpose reads. The feature tiles have unpadded 128-byte rows whose 16-byte
+// chunks are permuted per row (favor_swz), so that every access pattern on
+// them spreads over all LDS banks. Each wave projects its own 16 tokens (whose
+// raw rows it loaded) onto all features of a block, so the raw rows never pass
+// through LDS; omega comes from the cache.
 #pragma once
 
 #include "chunked.hpp"
@@ -29,11 +31,23 @@ namespace la {
 
 template <int R>
 struct FavorBlock {
-  static constexpr int FB = 64;        // features per block
-  static constexpr int NFB = R / FB;   // blocks
-  static constexpr int FP = FB + kPad;  // row stride of the [token][feature] tiles
-  static constexpr int FT = FB / 16;   // 16-feature tiles per block
+  static constexpr int FB = 64;       // features per block
+  static constexpr int NFB = R / FB;  // blocks
+  static constexpr int FT = FB / 16;  // 16-feature tiles per block
+  static constexpr int ROW = 2 * FB;  // bytes per token row of a feature tile
+  static constexpr int TILE16 = 16 * ROW;  // bytes per 16 token rows
 };
+
+// Feature tiles. Block-local feature f = 16 t + 4 g + i is stored at logical
+// column 32 (t >> 1) + 8 g + 4 (t & 1) + i of its token's row: the eight
+// features one lane needs as an inter-chunk B operand (S tiles 2p and 2p + 1
+// give the k-slots of the matrix-core product), or that it projects for two
+// adjacent 16-feature tiles, form one 16-byte chunk. Logical chunk k of row r
+// is stored at chunk k ^ favor_swz(r). Measured on gfx950, 16-byte row
+// accesses (rows c, chunks g + const) and transpose reads of rows 4 g + j
+// (j < 4) then reach all banks without conflicts, where a plain padded stride
+// serves one of the two patterns at a time.
+__device__ __forceinline__ int favor_swz(int r) { return 4 * ((r >> 1) & 1) | 2 * ((r >> 2) & 1); }
 
 // Output pass. kwh/kwl (RetNet only) hold the decay-weighted key features of
 // the state update; kh/kl hold the unweighted ones of the scores. zh/zl are
@@ -45,7 +59,7 @@ struct FavorFwdLayout {
   // 16 bytes between tiles: the hi and lo halves of one row are never a
   // multiple of 512 B apart, so their reads are not fused into one two-address
   // load whose halves would then have to be moved into operand order
-  static constexpr int TILE = kChunk * F::FP * 2 + 16;
+  static constexpr int TILE = kChunk * F::ROW + 16;
   static constexpr int qh_off = 0;
   static constexpr int ql_off = qh_off + TILE;
   static constexpr int kh_off = ql_off + TILE;
@@ -69,8 +83,8 @@ struct FavorSegLayout {
   using F = FavorBlock<R>;
   static constexpr int EP = E + kPad;
   static constexpr int kh_off = 0;
-  static constexpr int kl_off = kh_off + kChunk * F::FP * 2 + 16;
-  static constexpr int v_off = kl_off + kChunk * F::FP * 2 + 16;
+  static constexpr int kl_off = kh_off + kChunk * F::ROW + 16;
+  static constexpr int v_off = kl_off + kChunk * F::ROW + 16;
   static constexpr int bytes = v_off + kChunk * EP * 2;
   template <int DK>
   static constexpr int bytes_dk = bytes;
@@ -79,34 +93,38 @@ struct FavorSegLayout {
 // Per-lane byte offsets of every LDS access pattern, built once per feature
 // block from an opaque lane index (opaque_lane): each access then adds only
 // compile-time or wave-uniform constants, which fold into the instruction.
-template <int FP, int EP>
+template <int EP>
 struct FavorLane {
   int g4, c16;
-  int frag;   // row c, 8 columns at 8 g of an FP-stride tile (row-fragment operands)
-  int half;   // row c, 4 columns at 4 g of an FP-stride tile (inter-chunk B operand, feature writes)
-  int trf;    // transpose reads of FP-stride tiles
-  int tre;    // transpose reads of the EP-stride V tile
-  int afrag;  // row c, 8 columns at 8 g of the score tile
-  int a4;     // row c, 4 columns at 4 g of the score tile
-  int l4;     // 4 c (per-row floats)
+  int row[2];  // feature tile: row c, logical chunk g + 4 h (h = 0, 1)
+  int tr[2];   // feature tile transpose reads: row 4 g + (c >> 2), logical chunk 4 h + (c & 3)
+  int tre;     // V tile transpose reads, rows 8 g + (c >> 2) (+4): intra-chunk product
+  int tre2;    // V tile transpose reads, rows 4 g + (c >> 2) (+16): state update
+  int afrag;   // row c, 8 columns at 8 g of the score tile
+  int a4;      // row c, 4 columns at 4 g of the score tile
+  int l4;      // 4 c (per-row floats)
   __device__ __forceinline__ FavorLane(int lane) {
     g4 = lane >> 4;
     c16 = lane & 15;
-    frag = 2 * (c16 * FP + 8 * g4);
-    half = 2 * (c16 * FP + 4 * g4);
-    trf = 2 * ((8 * g4 + (c16 >> 2)) * FP + 4 * (c16 & 3));
+    const int rs = favor_swz(c16);
+    row[0] = 128 * c16 + 16 * (g4 ^ rs);
+    row[1] = 128 * c16 + 16 * ((g4 + 4) ^ rs);
+    const int rt = 4 * g4 + (c16 >> 2), ts = favor_swz(rt);
+    tr[0] = 128 * rt + 16 * ((c16 & 3) ^ ts);
+    tr[1] = 128 * rt + 16 * ((4 + (c16 & 3)) ^ ts);
     tre = 2 * ((8 * g4 + (c16 >> 2)) * EP + 4 * (c16 & 3));
+    tre2 = 2 * ((4 * g4 + (c16 >> 2)) * EP + 4 * (c16 & 3));
     afrag = 2 * (c16 * CP + 8 * g4);
     a4 = 2 * (c16 * CP + 4 * g4);
     l4 = 4 * c16;
   }
 };
 
-// MFMA operand by two transpose reads at a lane's transpose-read base plus a
-// constant (see tr_operand): rows r0 + 8 g + 0..7 of one column per lane.
-__device__ __forceinline__ bf16x8 tr_at(char* sm, int addr, int stride_bytes) {
+// MFMA operand by two transpose reads (see tr_operand), the second `gap`
+// bytes after the first: k-slots 0..3 and 4..7 of the lane's group.
+__device__ __forceinline__ bf16x8 tr_pair(char* sm, int addr, int gap) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + addr));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + addr + 4 * stride_bytes));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + addr + gap));
   return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
 }
 
@@ -176,49 +194,57 @@ __device__ __forceinline__ void favor_load_omega(bf16x8 (&om)[FavorBlock<R>::FT]
     for (int ks = 0; ks < DK / 32; ++ks) om[ft][ks] = *reinterpret_cast<const bf16x8*>(orow + 16 * ft * DK + 32 * ks);
 }
 
+// hi/lo tile chunks of eight features (two adjacent 16-feature tiles), zero
+// unless ok.
+__device__ __forceinline__ void favor_store_pair(char* sm, int hi_at, int lo_at, const float (&f0)[4],
+                                                 const float (&f1)[4], bool ok) {
+  bf16x4 h0, l0, h1, l1;
+  split4(f0, h0, l0);
+  split4(f1, h1, l1);
+  lds<bf16x8>(sm, hi_at) = cat8(keep_if(ok, h0), keep_if(ok, h1));
+  lds<bf16x8>(sm, lo_at) = cat8(keep_if(ok, l0), keep_if(ok, l1));
+}
+
 // FAVOR+ features of one side of a chunk for this wave's 16 tokens (16 w + c)
-// and all 64 features of block fb, as hi/lo pairs in row-major
-// [token][feature] tiles: phi = 2^(P log2(e) - shift2) with P = x . w on the
-// matrix cores (x: this wave's raw rows, omega rows from the cache). Keys past
-// the chunk's valid rows are zero. With WEIGHTED, keys are also written
-// multiplied by gamma^(L-1-t) (RetNet state update) into (wh_off, wl_off);
-// with ONLY_WEIGHTED that is the only copy.
+// and all 64 features of block fb, as hi/lo pairs in feature tiles: phi =
+// 2^(P log2(e) - shift2) with P = x . w on the matrix cores (x: this wave's raw
+// rows, omega rows from the cache). Keys past the chunk's valid rows are zero.
+// With WEIGHTED, keys are also written multiplied by gamma^(L-1-t) (RetNet
+// state update) into (wh_off, wl_off); with ONLY_WEIGHTED that is the only copy.
 template <int R, int DK, bool IS_K, bool WEIGHTED, bool ONLY_WEIGHTED, class LN>
 __device__ __forceinline__ void favor_project(const LN& ln, const bf16x8 (&x)[DK / 32], float shift2,
                                               const bf16x8 (&om)[FavorBlock<R>::FT][DK / 32], int L, float lg2gam,
                                               char* sm, int hi_off, int lo_off, int wh_off, int wl_off, int w) {
   using F = FavorBlock<R>;
-  constexpr int KS = DK / 32, FP = F::FP;
+  constexpr int KS = DK / 32;
   const int t = 16 * w + ln.c16;
   const bool ok = !IS_K || t < L;
   float wt = 1.f;
   if constexpr (WEIGHTED) wt = exp2f(float(L - 1 - t) * lg2gam);
 #pragma unroll
-  for (int ft = 0; ft < F::FT; ++ft) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < F::FT / 2; ++h) {
+    float f[2][4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = mfma16(om[ft][ks], x[ks], acc);
-    // acc[i] = P[token t][block feature 16 ft + 4 g + i]
-    float f[4];
+    for (int u = 0; u < 2; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], 1.44269504f, -shift2));
-    const int at = 32 * w * FP + 32 * ft + ln.half;
-    if constexpr (!ONLY_WEIGHTED) {
-      bf16x4 h, l;
-      split4(f, h, l);
-      lds<bf16x4>(sm, hi_off + at) = keep_if(ok, h);
-      lds<bf16x4>(sm, lo_off + at) = keep_if(ok, l);
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16(om[2 * h + u][ks], x[ks], acc);
+      // acc[i] = P[token t][block feature 16 (2 h + u) + 4 g + i]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[u][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], 1.44269504f, -shift2));
     }
+    // logical chunk 4 h + g of row t
+    const int at = F::TILE16 * w + ln.row[h];
+    if constexpr (!ONLY_WEIGHTED) favor_store_pair(sm, hi_off + at, lo_off + at, f[0], f[1], ok);
     if constexpr (WEIGHTED) {
-      float fw[4];
+      float fw[2][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fw[i] = f[i] * wt;
-      bf16x4 h, l;
-      split4(fw, h, l);
-      lds<bf16x4>(sm, wh_off + at) = keep_if(ok, h);
-      lds<bf16x4>(sm, wl_off + at) = keep_if(ok, l);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fw[u][i] = f[u][i] * wt;
+      favor_store_pair(sm, wh_off + at, wl_off + at, fw[0], fw[1], ok);
     }
-    __builtin_amdgcn_sched_barrier(0);  // one feature tile at a time: bounded live registers
+    __builtin_amdgcn_sched_barrier(0);  // two feature tiles at a time: bounded live registers
   }
 }
 
@@ -235,28 +261,32 @@ __device__ __forceinline__ void favor_write_v(const bf16x8 (&v)[E / 32], char* s
 // S rows of feature block fb (the wave's value columns) <- g S + K^^T V with
 // K^ as a hi/lo pair, and the wave's z tile of the block <- g z + K^^T 1 (z
 // is the state column of a constant-1 value). Wave w owns block-local z tile
-// w: lane (g, c) holds z[64 fb + 16 w + 4 g + i] in Zb.
+// w: lane (g, c) holds z[64 fb + 16 w + 4 g + i] in Zb. The contraction runs
+// over the chunk's tokens in the order 32 ks + 16 (s >> 2) + 4 g + (s & 3) for
+// k-slot s of lane group g, the same for K^ and V.
 template <int R, int E, class LN>
 __device__ __forceinline__ void favor_state_block(const LN& ln, f32x4 (&S)[R / 16][E / 64], f32x4& Zb, int fb,
                                                   char* sm, int kh_off, int kl_off, int v_off, float gscale, int w) {
   using F = FavorBlock<R>;
-  constexpr int FP = F::FP, EP = E + kPad;
+  constexpr int EP = E + kPad;
   bf16x8 ones;
 #pragma unroll
   for (int u = 0; u < 8; ++u) ones[u] = (bf16)1.f;
   bf16x8 vb[E / 64][2];
-  const int vbase = v_off + 2 * w * (E / 4) + ln.tre;
+  const int vbase = v_off + 2 * w * (E / 4) + ln.tre2;
 #pragma unroll
   for (int eb = 0; eb < E / 64; ++eb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_at(sm, vbase + 2 * (32 * ks * EP + 16 * eb), 2 * EP);
+    for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_pair(sm, vbase + 2 * (32 * ks * EP + 16 * eb), 2 * 16 * EP);
 #pragma unroll
   for (int rt = 0; rt < F::FT; ++rt) {
+    // features 16 rt + c: logical chunk 4 (rt >> 1) + (c >> 2), half rt & 1
     bf16x8 kh[2], kl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      kh[ks] = tr_at(sm, kh_off + 2 * (32 * ks * FP + 16 * rt) + ln.trf, 2 * FP);
-      kl[ks] = tr_at(sm, kl_off + 2 * (32 * ks * FP + 16 * rt) + ln.trf, 2 * FP);
+      const int o = 2 * F::TILE16 * ks + ln.tr[rt >> 1] + 8 * (rt & 1);
+      kh[ks] = tr_pair(sm, kh_off + o, F::TILE16);
+      kl[ks] = tr_pair(sm, kl_off + o, F::TILE16);
     }
 #pragma unroll
     for (int eb = 0; eb < E / 64; ++eb) {
@@ -277,11 +307,12 @@ __device__ __forceinline__ void favor_state_block(const LN& ln, f32x4 (&S)[R / 1
   f32x4 zt = Zb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) zt[i] *= gscale;
+  const int zb = (w >= 2 ? ln.tr[1] : ln.tr[0]) + 8 * (w & 1);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const int o = 2 * (32 * ks * FP) + 32 * w + ln.trf;
-    zt = mfma16(tr_at(sm, kh_off + o, 2 * FP), ones, zt);
-    zt = mfma16(tr_at(sm, kl_off + o, 2 * FP), ones, zt);
+    const int o = 2 * F::TILE16 * ks + zb;
+    zt = mfma16(tr_pair(sm, kh_off + o, F::TILE16), ones, zt);
+    zt = mfma16(tr_pair(sm, kl_off + o, F::TILE16), ones, zt);
   }
   Zb = zt;
 }
@@ -297,7 +328,8 @@ __device__ __forceinline__ void favor_z_store(const f32x4 (&Z)[FavorBlock<R>::NF
   }
 }
 
-// bf16 hi/lo image of the wave's z tiles into LDS (zh, zl: [R] bf16 each).
+// bf16 hi/lo image of the wave's z tiles into LDS (zh, zl: [R] bf16 each, in
+// the logical column order of the feature tiles).
 template <int R>
 __device__ __forceinline__ void favor_z_publish(const f32x4 (&Z)[FavorBlock<R>::NFB], char* sm, int zh_off,
                                                 int zl_off, int lane, int w) {
@@ -307,7 +339,7 @@ __device__ __forceinline__ void favor_z_publish(const f32x4 (&Z)[FavorBlock<R>::
       const float f[4] = {Z[fb][0], Z[fb][1], Z[fb][2], Z[fb][3]};
       bf16x4 h, l;
       split4(f, h, l);
-      const int o = 2 * (64 * fb + 16 * w + 4 * (lane >> 4));
+      const int o = 2 * (64 * fb + 32 * (w >> 1) + 8 * (lane >> 4) + 4 * (w & 1));
       lds<bf16x4>(sm, zh_off + o) = h;
       lds<bf16x4>(sm, zl_off + o) = l;
     }
@@ -345,7 +377,7 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FavorSegLayout<R, E>;
   using F = FavorBlock<R>;
-  using LN = FavorLane<F::FP, E + kPad>;
+  using LN = FavorLane<E + kPad>;
   const int lane = lane_id(), w = wave_id();
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
@@ -409,8 +441,8 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FavorFwdLayout<R, E, GATE>;
   using F = FavorBlock<R>;
-  using LN = FavorLane<F::FP, E + kPad>;
-  constexpr int FP = F::FP, EP = LY::EP, NEB = E / 64, KPB = F::FB / 32;
+  using LN = FavorLane<E + kPad>;
+  constexpr int EP = LY::EP, NEB = E / 64, KPB = F::FB / 32;
   const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
@@ -486,12 +518,14 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
 #pragma unroll
       for (int sl = 0; sl < 3; ++sl) {
         if (sl < nslot) {
-          const int ko = 32 * skj[sl] * FP + ln.frag, qo = 32 * sqi[sl] * FP + ln.frag;
+          const int ko = F::TILE16 * skj[sl], qo = F::TILE16 * sqi[sl];
 #pragma unroll
           for (int ks = 0; ks < KPB; ++ks) {
-            const bf16x8 qh = lds<bf16x8>(sm, LY::qh_off + 64 * ks + qo), ql = lds<bf16x8>(sm, LY::ql_off + 64 * ks + qo);
-            sacc[sl] = mfma3(lds<bf16x8>(sm, LY::kh_off + 64 * ks + ko), lds<bf16x8>(sm, LY::kl_off + 64 * ks + ko), qh,
-                             ql, sacc[sl]);
+            // logical columns 32 ks + 8 g .. + 7 of both sides
+            const int r = ln.row[ks];
+            const bf16x8 qh = lds<bf16x8>(sm, LY::qh_off + qo + r), ql = lds<bf16x8>(sm, LY::ql_off + qo + r);
+            sacc[sl] = mfma3(lds<bf16x8>(sm, LY::kh_off + ko + r), lds<bf16x8>(sm, LY::kl_off + ko + r), qh, ql,
+                             sacc[sl]);
             if (sl == 0) {
               const int zo = 2 * (64 * fb + 32 * ks + 8 * ln.g4);
               zacc = mfma3(qh, ql, lds<bf16x8>(sm, LY::zh_off + zo), lds<bf16x8>(sm, LY::zl_off + zo), zacc);
@@ -514,9 +548,9 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
         for (int qt = 0; qt < 4; ++qt) {
 #pragma unroll
           for (int p = 0; p < KPB; ++p) {
-            const int o0 = 32 * qt * FP + 64 * p + ln.half;
-            const bf16x8 qbh = cat8(lds<bf16x4>(sm, LY::qh_off + o0), lds<bf16x4>(sm, LY::qh_off + o0 + 32));
-            const bf16x8 qbl = cat8(lds<bf16x4>(sm, LY::ql_off + o0), lds<bf16x4>(sm, LY::ql_off + o0 + 32));
+            // features 32 p + 4 g + (0..3) and 32 p + 16 + 4 g + (0..3): logical chunk 4 p + g
+            const int o = F::TILE16 * qt + ln.row[p];
+            const bf16x8 qbh = lds<bf16x8>(sm, LY::qh_off + o), qbl = lds<bf16x8>(sm, LY::ql_off + o);
 #pragma unroll
             for (int eb = 0; eb < NEB; ++eb) oacc[qt][eb] = mfma3(sh[p][eb], slo[p][eb], qbh, qbl, oacc[qt][eb]);
           }
@@ -590,7 +624,7 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
             }
 #pragma unroll
             for (int p2 = 0; p2 <= qt / 2; ++p2)
-              acc = mfma16(tr_at(sm, LY::v_off + 2 * (32 * p2 * EP + e) + ln.tre, 2 * EP),
+              acc = mfma16(tr_pair(sm, LY::v_off + 2 * (32 * p2 * EP + e) + ln.tre, 8 * EP),
                            lds<bf16x8>(sm, LY::a_off + 32 * qt * CP + 64 * p2 + ln.afrag), acc);
             if (q < L) {
               bf16x4 o = pack4(acc[0] * inv_den, acc[1] * inv_den, acc[2] * inv_den, acc[3] * inv_den);
