@@ -193,6 +193,32 @@ def test_initial_state_resumes(name):
     check_close(out, full[:, :, m:], TOL_BF16, f"{name} resumed")
 
 
+@pytest.mark.parametrize("gate,d,dv,B,H,n", [("decay", 64, 64, 4, 16, 700), ("gla", 64, 64, 4, 16, 700),
+                                              ("gla", 32, 64, 2, 16, 1100), ("decay", 32, 64, 2, 16, 1100)])
+def test_small_state_gates_resume(gate, d, dv, B, H, n):
+    """Gated forms with small states over several segments with a ragged last
+    one, resumed from a carried-in state, against the oracle over the whole
+    history (outputs and final state)."""
+    import kernelized_sequence_mixing_amd as ksm
+    wl = WORKLOADS["causal_elu1"].resized(d_k=d, d_v=dv, r=d, gate=gate)
+    P, L = ksm.segments(B, H, n, d, dv, fmap="elu1", r=d, gate_kind=gate)
+    assert P > 1 and n % L != 0, (P, L)
+    m = 130
+    inp = make_inputs(wl, seed=11, B=B, H=H, n=m + n)
+    full, Sr, zr = oracle_forward(inp)
+    first = {k: (v[:, :, :m] if isinstance(v, torch.Tensor) and v.dim() == 4 else v) for k, v in inp.items()}
+    _, S1, z1 = oracle_forward(first)
+    second = {k: (v[:, :, m:].contiguous() if isinstance(v, torch.Tensor) and v.dim() == 4 else v)
+              for k, v in inp.items()}
+    second["n"] = n
+    out, S, z = run_forward(second, return_state=True, S0=torch.from_numpy(S1.astype(np.float32)),
+                            z0=torch.from_numpy(z1.astype(np.float32)))
+    check_close(out, full[:, :, m:], TOL_BF16, f"{gate} d{d}x{dv} resumed")
+    scale = np.max(np.abs(Sr)) + 1e-30
+    assert np.max(np.abs(to_f64(S) - Sr)) / scale < 2e-2
+    np.testing.assert_allclose(to_f64(z), zr, rtol=2e-2)
+
+
 def test_decode_workload_full():
     """Decode step at batch 256 x 16 heads with 128 x 128 fp32 states (GLA)."""
     import kernelized_sequence_mixing_amd as ksm
