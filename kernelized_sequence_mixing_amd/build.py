@@ -4,7 +4,11 @@
 
 Every source is compiled to an object under ``_build/`` (in parallel), then
 linked into ``kernelized_sequence_mixing_amd/liblinattn.so``. All device code
-is compiled with packed-fp32 instruction selection disabled.
+is compiled with packed-fp32 instruction selection disabled, and with matrix-core
+accumulators in ordinary VGPRs (``-amdgpu-mfma-vgpr-form``): gfx950 MFMAs read and
+write either register file, and the accumulation-register form made the compiler
+copy every accumulator the VALU touches (the state's bf16 image, scores, outputs)
+with v_accvgpr_read/write, ~11% of the elu+1 output pass's VALU instructions.
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ SOURCES = ["api.cpp", "chunked_elu1.hip", "chunked_favor.hip", "scan.hip", "nonc
 
 HIPCC_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form",
                f"-I{os.path.join(ROOT, 'include')}"]
 
 

@@ -28,9 +28,11 @@
 // waves 4..7 compute phi(q) . z for those rows), and wave w owns value columns
 // [w E/NW, (w+1) E/NW) of the state and the outputs. The fp32 state lives in MFMA accumulators for the whole
 // sequence; its bf16 image feeds the inter-chunk product straight from
-// registers. LDS holds the chunk's operands (bf16), all row-major:
-//   q  [64][R+8]   Q~ (also Q^)      k [64][R+8]   K~      v [64][E+8]   V
-//   a  [64][64+8]  masked scores     kh [64][R+8]  K^ (RetNet only)
+// registers. LDS holds the chunk's operands (bf16), all [token][column]:
+//   q  [64][R]     Q~ (also Q^)      k [64][R]     K~      v [64][E+8]   V
+//   a  [64][64+8]  masked scores     kh [64][R]    K^ (RetNet only)
+// The feature tiles (q, k, kh) have unpadded rows whose 16-byte chunks are
+// permuted per row (FeatTile), the others padded rows.
 // Operands that contract over tokens (the state update, V^T A^T) are read
 // from the row-major tiles with the LDS transpose read (ds_read_b64_tr_b16).
 // Without a gate K^ = K~; with the GLA gate K^ = Gamma K~ feature by feature,
@@ -65,13 +67,36 @@ struct CausalArgs {
   float eps, inv_tau;
 };
 
-// Row padding (bf16 elements) of the LDS tiles: rows of 32, 64 or 128
-// elements plus 8 start 4 dwords apart modulo the banks. Of the paddings
-// measured on these kernels (8 and 16) this one gives the faster chunk loops
-// for the 64-wide tiles, whose mix of 8-byte, 16-byte and transpose reads no
-// single padding makes conflict-free.
+// Row padding (bf16 elements) of the value and score tiles: rows of 32, 64 or
+// 128 elements plus 8 start 4 dwords apart modulo the banks.
 constexpr int kPad = 8;
 constexpr int CP = kChunk + kPad;  // row stride (elements) of the score tile
+
+// Feature tiles ([token][feature] bf16, R features, rows of 2R bytes without
+// padding). The 16-byte chunk k of row t is stored at chunk k ^ swz(t), where
+// swz maps the row bits that alias LDS banks for each row width onto chunk
+// bits. The chunk kernels access these tiles as 16-byte row fragments (rows c,
+// chunks g + const, c < 16, g < 4), 8-byte row fragments (16 rows, one chunk
+// half) and transpose reads (rows 8 g + j and + 4, j < 4; 8-byte column
+// groups), each spread over all 64 banks by this permutation, which no row
+// padding achieves for all three at once (measured on gfx950: 16-byte rows are
+// 2-way conflicted at a 144-byte stride, 8-byte rows at 160).
+// With SWZ false the rows are instead padded by kPad elements (the segment
+// pass, which reads these tiles only by transpose reads, conflict-free at that
+// stride, and runs with fewer registers without the per-row permutation).
+template <int R, bool SWZ = true>
+struct FeatTile {
+  static constexpr int ROW = 2 * R + (SWZ ? 0 : 2 * kPad);  // bytes per token row
+  static constexpr int BYTES = kChunk * ROW;
+  __device__ static __forceinline__ int swz(int t) {
+    if constexpr (!SWZ) return 0;
+    else if constexpr (R == 32) return 2 * ((t >> 2) & 1) | ((t >> 3) & 1);
+    else if constexpr (R == 64) return 4 * ((t >> 1) & 1) | 2 * ((t >> 2) & 1) | ((t >> 3) & 1);
+    else return 8 * ((t >> 2) & 1) | 4 * ((t >> 1) & 1) | 2 * (t & 1) | ((t >> 3) & 1);
+  }
+  // byte offset of byte b of 16-byte chunk k of row t
+  __device__ static __forceinline__ int at(int t, int k, int b = 0) { return t * ROW + 16 * (k ^ swz(t)) + b; }
+};
 
 // Waves per workgroup of the elu+1 chunk kernels.
 template <int R, int E>
@@ -81,12 +106,13 @@ struct Waves {
 
 template <int R, int E, int GATE>
 struct FwdLayout {
-  static constexpr int RP = R + kPad, EP = E + kPad;
+  static constexpr bool SWZ = true;  // feature tiles permuted per row (FeatTile)
+  static constexpr int EP = E + kPad, FTB = FeatTile<R, SWZ>::BYTES;
   static constexpr int q_off = 0;
-  static constexpr int k_off = q_off + kChunk * RP * 2;
-  static constexpr int v_off = k_off + kChunk * RP * 2;
+  static constexpr int k_off = q_off + FTB;
+  static constexpr int v_off = k_off + FTB;
   static constexpr int kh_off = v_off + kChunk * EP * 2;
-  static constexpr int a_off = kh_off + (GATE == GT_DECAY ? kChunk * RP * 2 : 0);
+  static constexpr int a_off = kh_off + (GATE == GT_DECAY ? FTB : 0);
   static constexpr int z_off = a_off + kChunk * CP * 2;
   static constexpr int gam_off = z_off + R * 4;
   static constexpr int rs_off = gam_off + R * 4;   // [64] score row sums
@@ -101,9 +127,10 @@ struct FwdLayout {
 template <int R, int E, int GATE>
 struct SegLayout {
   static constexpr bool PIPELINED = GATE == GT_GLA;
-  static constexpr int RP = R + kPad, EP = E + kPad;
-  static constexpr int k_off = 0;  // K^ rows
-  static constexpr int v_off = k_off + kChunk * RP * 2;
+  static constexpr bool SWZ = false;  // padded feature tile (FeatTile)
+  static constexpr int EP = E + kPad;
+  static constexpr int k_off = 0;  // K^ rows (feature tile)
+  static constexpr int v_off = k_off + FeatTile<R, SWZ>::BYTES;
   static constexpr int gam_off = v_off + kChunk * EP * 2;
   static constexpr int HALF = gam_off + R * 4;
   static constexpr int logg_off = (PIPELINED ? 2 : 1) * HALF;
@@ -137,6 +164,20 @@ __device__ __forceinline__ bf16x8 tr_operand(char* sm, int tile_off, int stride,
   const int base = tile_off + 2 * ((k0 + 8 * g4 + (c16 >> 2)) * stride + col0 + 4 * (c16 & 3));
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + base));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + base + 2 * 4 * stride));
+  return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
+}
+
+// The same operand from a feature tile (FeatTile): column col0 + c (col0 a
+// multiple of 16) of rows k0 + 8 g + 0..7 (k0 a multiple of 8). Lane m = 4 j + q
+// of each 16-lane group addresses row k0 + 8 g + j (+4 for the second read),
+// columns col0 + 4 q .. + 3: half q & 1 of chunk col0 / 8 + q / 2.
+template <int R, bool SWZ>
+__device__ __forceinline__ bf16x8 tr_feat(char* sm, int tile_off, int k0, int col0, int lane) {
+  using FT = FeatTile<R, SWZ>;
+  const int g4 = lane >> 4, c16 = lane & 15, q = c16 & 3;
+  const int t = k0 + 8 * g4 + (c16 >> 2), k = col0 / 8 + (q >> 1), b = 8 * (q & 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + tile_off + FT::at(t, k, b)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + tile_off + FT::at(t + 4, k, b)));
   return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
 }
 
@@ -223,14 +264,15 @@ struct RawChunk {
 //   K^, v, gam, logg).
 // L = valid tokens in the chunk. Rows t >= L get phi(k) = 0 and v = 0, and a
 // zero log-gate, so they add nothing to the state.
-template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW>
+template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SWZ>
 __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>& raw,
                                               const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
                                               int k_off, int kh_off, int v_off, int gam_off, int logg_off,
                                               int lane, int w) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
   constexpr int LPT = Raw::LPT;
-  constexpr int RP = R + kPad, EP = E + kPad;
+  constexpr int EP = E + kPad;
+  using FT = FeatTile<R, SWZ>;
   static_assert(FMAP == FM_ELU1, "FAVOR+ chunks use the kernels of chunked_favor.hpp");
   if constexpr (Raw::ROWMAJOR) {
     const int t = Raw::TPW * w + lane / LPT;
@@ -247,20 +289,20 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         vk[u] = elu1(to_f32(raw.k[j][u]));
         vkh[u] = vk[u] * decay_k;
       }
+      const int fo = FT::at(t, f0 / 8);
       if constexpr (WITH_Q)
-        lds<bf16x8>(sm, q_off + 2 * (t * RP + f0)) =
-            cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
+        lds<bf16x8>(sm, q_off + fo) = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
       // keys past the end are zeroed after packing (four masks per eight features)
       const bf16x8 kr = keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
       const bf16x8 khr =
           keep_if(valid, cat8(pack4(vkh[0], vkh[1], vkh[2], vkh[3]), pack4(vkh[4], vkh[5], vkh[6], vkh[7])));
       if constexpr (GATE != GT_DECAY) {
-        lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) = kr;
+        lds<bf16x8>(sm, k_off + fo) = kr;
       } else if constexpr (WITH_Q) {
-        lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) = kr;
-        lds<bf16x8>(sm, kh_off + 2 * (t * RP + f0)) = khr;
+        lds<bf16x8>(sm, k_off + fo) = kr;
+        lds<bf16x8>(sm, kh_off + fo) = khr;
       } else {
-        lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) = khr;
+        lds<bf16x8>(sm, k_off + fo) = khr;
       }
     }
 #pragma unroll
@@ -294,10 +336,10 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         vq[u] = pq;
         vk[u] = pk;
       }
+      const int fo = FT::at(t, f0 / 8);
       if constexpr (WITH_Q)
-        lds<bf16x8>(sm, q_off + 2 * (t * RP + f0)) =
-            cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
-      lds<bf16x8>(sm, k_off + 2 * (t * RP + f0)) =
+        lds<bf16x8>(sm, q_off + fo) = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
+      lds<bf16x8>(sm, k_off + fo) =
           keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
     }
     if constexpr (GATE == GT_GLA) {
@@ -331,12 +373,12 @@ struct ZTiles {
 //   no gate   S <- S + K~^T V                    z <- z + K~^T 1
 //   RetNet    S <- gamma^L S + K^^T V            (kh_off holds K^ rows)
 //   GLA       S <- Gamma (S + K~^T V)            Gamma = diag(e^{b_end}) from gam_off
-// Both operands come from row-major [token][column] tiles by transpose reads.
+// Both operands come from [token][column] tiles by transpose reads.
 // S is f32x4[R / 16][E / (16 NW)], Z is f32x4[ZTiles<R, NW>::ZT].
-template <int R, int E, int GATE, int NW, class SArr, class ZArr>
+template <int R, int E, int GATE, int NW, bool SWZ, class SArr, class ZArr>
 __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_off, int v_off, int gam_off,
                                              float gscale, int lane, int w) {
-  constexpr int ZT = ZTiles<R, NW>::ZT, RP = R + kPad, EP = E + kPad, NEB = E / (16 * NW);
+  constexpr int ZT = ZTiles<R, NW>::ZT, EP = E + kPad, NEB = E / (16 * NW);
   const int g4 = lane >> 4;
   const int ebase = w * (E / NW);
   bf16x8 ones;
@@ -351,7 +393,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
   for (int rt = 0; rt < R / 16; ++rt) {
     bf16x8 ka[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) ka[ks] = tr_operand(sm, kh_off, RP, 32 * ks, 16 * rt, lane);
+    for (int ks = 0; ks < 2; ++ks) ka[ks] = tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane);
     float gr[4] = {gscale, gscale, gscale, gscale};
     if constexpr (GATE == GT_GLA) {
 #pragma unroll
@@ -389,7 +431,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) zt = mfma16(tr_operand(sm, kh_off, RP, 32 * ks, 16 * rt, lane), ones, zt);
+      for (int ks = 0; ks < 2; ++ks) zt = mfma16(tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane), ones, zt);
       if constexpr (GATE == GT_GLA) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
@@ -465,14 +507,14 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
   __builtin_amdgcn_sched_barrier(0);
   auto prelude = [&](Raw& rw, int ci, int half) {
     const int L = min(kChunk, a.n - (t_begin + ci * kChunk));
-    chunk_prelude<R, E, DK, FMAP, GATE, false, NW>(rw, a, L, lg2gam, sm, 0, half * LY::HALF + LY::k_off, 0,
+    chunk_prelude<R, E, DK, FMAP, GATE, false, NW, LY::SWZ>(rw, a, L, lg2gam, sm, 0, half * LY::HALF + LY::k_off, 0,
                                                    half * LY::HALF + LY::v_off, half * LY::HALF + LY::gam_off,
                                                    LY::logg_off, lane, w);
   };
   auto update = [&](int ci, int half) {
     const int L = min(kChunk, a.n - (t_begin + ci * kChunk));
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE, NW>(S, Z, sm, half * LY::HALF + LY::k_off, half * LY::HALF + LY::v_off,
+    state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, half * LY::HALF + LY::k_off, half * LY::HALF + LY::v_off,
                                  half * LY::HALF + LY::gam_off, gsc, lane, w);
   };
   if constexpr (LY::PIPELINED) {
@@ -531,7 +573,8 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FwdLayout<R, E, GATE>;
   constexpr int NW = Waves<R, E>::NW;
-  constexpr int RP = LY::RP, EP = LY::EP, NEB = E / (16 * NW), KP = R / 32;
+  constexpr int EP = LY::EP, NEB = E / (16 * NW), KP = R / 32;
+  using FT = FeatTile<R, LY::SWZ>;
   const int lane = lane_id(), w = wave_id<NW>(), tid = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
@@ -589,7 +632,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
     const bool live = ci < nch;
     const int L = min(kChunk, a.n - t0);
     if (live)
-      chunk_prelude<R, E, DK, FMAP, GATE, true, NW>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
+      chunk_prelude<R, E, DK, FMAP, GATE, true, NW, LY::SWZ>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
                                                     LY::v_off, LY::gam_off, 0, lane, w);
     // the raw registers are free again: this refill flies during the next DEPTH chunks
     raw.load(a, tok0, t0 + DEPTH * kChunk, t_end, lane, w);
@@ -603,7 +646,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
       const bool scores = NW == 4 || w < 4, zdot = NW == 4 || w >= 4;
       bf16x8 qop[KP];
 #pragma unroll
-      for (int ks = 0; ks < KP; ++ks) qop[ks] = lds<bf16x8>(sm, LY::q_off + 2 * ((16 * qw + c16) * RP + 32 * ks + 8 * g4));
+      for (int ks = 0; ks < KP; ++ks) qop[ks] = lds<bf16x8>(sm, LY::q_off + FT::at(16 * qw + c16, 4 * ks + g4));
       const int q = 16 * qw + c16;
       if (scores) {
         float rs = 0.f;
@@ -616,7 +659,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KP; ++ks)
-            acc = mfma16(lds<bf16x8>(sm, LY::k_off + 2 * ((16 * c + c16) * RP + 32 * ks + 8 * g4)), qop[ks], acc);
+            acc = mfma16(lds<bf16x8>(sm, LY::k_off + FT::at(16 * c + c16, 4 * ks + g4)), qop[ks], acc);
           // acc[i] = A[q][key], key = 16c + 4g + i
           float gbase = 1.f;
           if constexpr (GATE == GT_DECAY) gbase = exp2f(float(q - 16 * c - 4 * g4) * lg2gam);
@@ -660,8 +703,8 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
       bf16x8 qb[KP];
 #pragma unroll
       for (int p = 0; p < KP; ++p)
-        qb[p] = cat8(lds<bf16x4>(sm, LY::q_off + 2 * (q * RP + 32 * p + 4 * g4)),
-                     lds<bf16x4>(sm, LY::q_off + 2 * (q * RP + 32 * p + 16 + 4 * g4)));
+        qb[p] = cat8(lds<bf16x4>(sm, LY::q_off + FT::at(q, 4 * p + (g4 >> 1), 8 * (g4 & 1))),
+                     lds<bf16x4>(sm, LY::q_off + FT::at(q, 4 * p + 2 + (g4 >> 1), 8 * (g4 & 1))));
       // one correctly rounded reciprocal per row; outputs are fl(O * fl(1 / den))
       const float inv_den = 1.f / (lds<float>(sm, LY::rs_off + 4 * q) + lds<float>(sm, LY::zd_off + 4 * q) + a.eps);
       float isc = 1.f;
@@ -689,7 +732,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
 
     // ---- carry the state past this chunk
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE, NW>(S, Z, sm, GATE == GT_DECAY ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
+    state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, GATE == GT_DECAY ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
                                  gsc, lane, w);
     z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
     lds_barrier();
