@@ -28,13 +28,13 @@
 // waves 4..7 compute phi(q) . z for those rows), and wave w owns value columns
 // [w E/NW, (w+1) E/NW) of the state and the outputs. The fp32 state lives in MFMA accumulators for the whole
 // sequence; its bf16 image feeds the inter-chunk product straight from
-// registers. LDS holds the chunk's operands (bf16), all [token][column]:
-//   q  [64][R]     Q~ (also Q^)      k [64][R]     K~      v [64][E+8]   V
-//   a  [64][64+8]  masked scores     kh [64][R]    K^ (RetNet only)
-// The feature tiles (q, k, kh) have unpadded rows whose 16-byte chunks are
-// permuted per row (FeatTile), the others padded rows.
+// registers. LDS holds the chunk's operands (bf16), all [row][column]:
+//   q  [64][R]     Q~ (also Q^)      k [64][R]     K~      v [64][E]   V
+//   a  [64][64]    masked scores     kh [64][R]    K^ (RetNet only)
+// In the output pass every tile has unpadded rows whose 16-byte chunks are
+// permuted per row (FeatTile); the segment pass pads its rows instead.
 // Operands that contract over tokens (the state update, V^T A^T) are read
-// from the row-major tiles with the LDS transpose read (ds_read_b64_tr_b16).
+// with the LDS transpose read (ds_read_b64_tr_b16).
 // Without a gate K^ = K~; with the GLA gate K^ = Gamma K~ feature by feature,
 // so the state update is S <- Gamma (S + K~^T V); RetNet weights each key row
 // and keeps K^ in a tile of its own (pass 1 stores only K^, in the k tile).
@@ -67,20 +67,21 @@ struct CausalArgs {
   float eps, inv_tau;
 };
 
-// Row padding (bf16 elements) of the value and score tiles: rows of 32, 64 or
-// 128 elements plus 8 start 4 dwords apart modulo the banks.
+// Row padding (bf16 elements) of padded tiles: rows of 32, 64 or 128
+// elements plus 8 start 4 dwords apart modulo the banks.
 constexpr int kPad = 8;
 constexpr int CP = kChunk + kPad;  // row stride (elements) of the score tile
 
-// Feature tiles ([token][feature] bf16, R features, rows of 2R bytes without
-// padding). The 16-byte chunk k of row t is stored at chunk k ^ swz(t), where
-// swz maps the row bits that alias LDS banks for each row width onto chunk
-// bits. The chunk kernels access these tiles as 16-byte row fragments (rows c,
-// chunks g + const, c < 16, g < 4), 8-byte row fragments (16 rows, one chunk
-// half) and transpose reads (rows 8 g + j and + 4, j < 4; 8-byte column
-// groups), each spread over all 64 banks by this permutation, which no row
-// padding achieves for all three at once (measured on gfx950: 16-byte rows are
-// 2-way conflicted at a 144-byte stride, 8-byte rows at 160).
+// LDS tiles of 64 rows ([token][feature], [token][value column] or
+// [query][key] bf16) of R columns, rows of 2R bytes without padding. The
+// 16-byte chunk k of row t is stored at chunk k ^ swz(t), where swz maps the
+// row bits that alias LDS banks for each row width onto chunk bits. The chunk
+// kernels access these tiles as 16-byte row fragments (rows c, chunks g +
+// const, c < 16, g < 4), 8-byte row fragments (16 rows, one chunk half) and
+// transpose reads (rows 8 g + j and + 4, j < 4; 8-byte column groups), each
+// spread over all 64 banks by this permutation, which no row padding achieves
+// for all three at once (measured on gfx950: 16-byte rows are 2-way conflicted
+// at a 144-byte stride, 8-byte rows at 160).
 // With SWZ false the rows are instead padded by kPad elements (the segment
 // pass, which reads these tiles only by transpose reads, conflict-free at that
 // stride, and runs with fewer registers without the per-row permutation).
@@ -106,14 +107,16 @@ struct Waves {
 
 template <int R, int E, int GATE>
 struct FwdLayout {
-  static constexpr bool SWZ = true;  // feature tiles permuted per row (FeatTile)
-  static constexpr int EP = E + kPad, FTB = FeatTile<R, SWZ>::BYTES;
+  // every [token][column] tile (q, k, kh, v, and the [query][key] scores) is
+  // stored with the per-row chunk permutation of FeatTile
+  static constexpr bool SWZ = true;
+  static constexpr int FTB = FeatTile<R, SWZ>::BYTES;
   static constexpr int q_off = 0;
   static constexpr int k_off = q_off + FTB;
   static constexpr int v_off = k_off + FTB;
-  static constexpr int kh_off = v_off + kChunk * EP * 2;
+  static constexpr int kh_off = v_off + FeatTile<E, SWZ>::BYTES;
   static constexpr int a_off = kh_off + (GATE == GT_DECAY ? FTB : 0);
-  static constexpr int z_off = a_off + kChunk * CP * 2;
+  static constexpr int z_off = a_off + FeatTile<kChunk, SWZ>::BYTES;
   static constexpr int gam_off = z_off + R * 4;
   static constexpr int rs_off = gam_off + R * 4;   // [64] score row sums
   static constexpr int zd_off = rs_off + kChunk * 4;  // [64] Q^ . z_prev
@@ -127,11 +130,10 @@ struct FwdLayout {
 template <int R, int E, int GATE>
 struct SegLayout {
   static constexpr bool PIPELINED = GATE == GT_GLA;
-  static constexpr bool SWZ = false;  // padded feature tile (FeatTile)
-  static constexpr int EP = E + kPad;
-  static constexpr int k_off = 0;  // K^ rows (feature tile)
+  static constexpr bool SWZ = false;  // padded tiles (FeatTile)
+  static constexpr int k_off = 0;     // K^ rows
   static constexpr int v_off = k_off + FeatTile<R, SWZ>::BYTES;
-  static constexpr int gam_off = v_off + kChunk * EP * 2;
+  static constexpr int gam_off = v_off + FeatTile<E, SWZ>::BYTES;
   static constexpr int HALF = gam_off + R * 4;
   static constexpr int logg_off = (PIPELINED ? 2 : 1) * HALF;
   static constexpr int bytes = logg_off + R * 4;
@@ -153,24 +155,12 @@ __device__ __forceinline__ T& lds(char* base, int byte_off) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// MFMA operand from a row-major bf16 LDS tile by transpose reads: lane (g, c)
-// receives tile[k0 + 8 g + jj][col0 + c] for jj = 0..7 (eight consecutive
-// contraction rows of column col0 + c). Within each 16-lane group the
-// transpose read hands lane i element j of the 4-element chunk addressed by
+// MFMA operand from a [token][column] tile (FeatTile) by transpose reads
+// (ds_read_b64_tr_b16): lane (g, c) receives column col0 + c (col0 a multiple of
+// 16) of rows k0 + 8 g + 0..7 (k0 a multiple of 8). Within each 16-lane group
+// the transpose read hands lane i element j of the 4-element piece addressed by
 // lane 4 j + i / 4, so lane m = 4 j + q addresses row k0 + 8 g + j (+4 for the
-// second read), columns col0 + 4 q .. col0 + 4 q + 3.
-__device__ __forceinline__ bf16x8 tr_operand(char* sm, int tile_off, int stride, int k0, int col0, int lane) {
-  const int g4 = lane >> 4, c16 = lane & 15;
-  const int base = tile_off + 2 * ((k0 + 8 * g4 + (c16 >> 2)) * stride + col0 + 4 * (c16 & 3));
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + base));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + base + 2 * 4 * stride));
-  return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
-}
-
-// The same operand from a feature tile (FeatTile): column col0 + c (col0 a
-// multiple of 16) of rows k0 + 8 g + 0..7 (k0 a multiple of 8). Lane m = 4 j + q
-// of each 16-lane group addresses row k0 + 8 g + j (+4 for the second read),
-// columns col0 + 4 q .. + 3: half q & 1 of chunk col0 / 8 + q / 2.
+// second read), columns col0 + 4 q .. + 3: half q & 1 of chunk col0 / 8 + q / 2.
 template <int R, bool SWZ>
 __device__ __forceinline__ bf16x8 tr_feat(char* sm, int tile_off, int k0, int col0, int lane) {
   using FT = FeatTile<R, SWZ>;
@@ -259,7 +249,7 @@ struct RawChunk {
   }
 };
 
-// elu+1 features and gate factors of one chunk into LDS, all tiles row-major.
+// elu+1 features and gate factors of one chunk into LDS ([token][column] tiles).
 //   WITH_Q: pass 3 (writes q, k, v, gam; kh for RetNet); else pass 1 (k holding
 //   K^, v, gam, logg).
 // L = valid tokens in the chunk. Rows t >= L get phi(k) = 0 and v = 0, and a
@@ -271,8 +261,8 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
                                               int lane, int w) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
   constexpr int LPT = Raw::LPT;
-  constexpr int EP = E + kPad;
   using FT = FeatTile<R, SWZ>;
+  using VT = FeatTile<E, SWZ>;
   static_assert(FMAP == FM_ELU1, "FAVOR+ chunks use the kernels of chunked_favor.hpp");
   if constexpr (Raw::ROWMAJOR) {
     const int t = Raw::TPW * w + lane / LPT;
@@ -307,7 +297,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
     }
 #pragma unroll
     for (int j = 0; j < E / (8 * LPT); ++j)
-      lds<bf16x8>(sm, v_off + 2 * (t * EP + 8 * (lane % LPT + LPT * j))) = keep_if(valid, raw.v[j]);
+      lds<bf16x8>(sm, v_off + VT::at(t, lane % LPT + LPT * j)) = keep_if(valid, raw.v[j]);
     return;
   }
   const bool valid = lane < L;
@@ -349,12 +339,12 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       }
     }
   }
-  // values, row-major (rows past the end are zero)
+  // values (rows past the end are zero)
   {
     constexpr int EV = Raw::EV;
 #pragma unroll
     for (int j = 0; j < EV / 8; ++j)
-      lds<bf16x8>(sm, v_off + 2 * (lane * EP + w * EV + 8 * j)) = keep_if(valid, raw.v[j]);
+      lds<bf16x8>(sm, v_off + VT::at(lane, w * EV / 8 + j)) = keep_if(valid, raw.v[j]);
   }
 }
 
@@ -378,7 +368,7 @@ struct ZTiles {
 template <int R, int E, int GATE, int NW, bool SWZ, class SArr, class ZArr>
 __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_off, int v_off, int gam_off,
                                              float gscale, int lane, int w) {
-  constexpr int ZT = ZTiles<R, NW>::ZT, EP = E + kPad, NEB = E / (16 * NW);
+  constexpr int ZT = ZTiles<R, NW>::ZT, NEB = E / (16 * NW);
   const int g4 = lane >> 4;
   const int ebase = w * (E / NW);
   bf16x8 ones;
@@ -388,7 +378,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_operand(sm, v_off, EP, 32 * ks, ebase + 16 * eb, lane);
+    for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_feat<E, SWZ>(sm, v_off, 32 * ks, ebase + 16 * eb, lane);
 #pragma unroll
   for (int rt = 0; rt < R / 16; ++rt) {
     bf16x8 ka[2];
@@ -573,8 +563,9 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = FwdLayout<R, E, GATE>;
   constexpr int NW = Waves<R, E>::NW;
-  constexpr int EP = LY::EP, NEB = E / (16 * NW), KP = R / 32;
+  constexpr int NEB = E / (16 * NW), KP = R / 32;
   using FT = FeatTile<R, LY::SWZ>;
+  using AT = FeatTile<kChunk, LY::SWZ>;
   const int lane = lane_id(), w = wave_id<NW>(), tid = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x;
@@ -675,9 +666,9 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
           const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
           rs += (lo_bf16_f32(p01) + hi_bf16_f32(p01)) + (lo_bf16_f32(p23) + hi_bf16_f32(p23));
           typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-          lds<u32x2>(sm, LY::a_off + 2 * (q * CP + 16 * c + 4 * g4)) = u32x2{p01, p23};
+          lds<u32x2>(sm, LY::a_off + AT::at(q, 2 * c + (g4 >> 1), 8 * (g4 & 1))) = u32x2{p01, p23};
         }
-        if ((qw & 1) == 0) lds<bf16x4>(sm, LY::a_off + 2 * (q * CP + 16 * (qw + 1) + 4 * g4)) = bf16x4{};
+        if ((qw & 1) == 0) lds<bf16x4>(sm, LY::a_off + AT::at(q, 2 * (qw + 1) + (g4 >> 1), 8 * (g4 & 1))) = bf16x4{};
         rs = sum_over_groups(rs);
         if (g4 == 0) lds<float>(sm, LY::rs_off + 4 * q) = rs;
       }
@@ -721,8 +712,8 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
         }
 #pragma unroll
         for (int p2 = 0; p2 <= qt / 2; ++p2)
-          acc = mfma16(tr_operand(sm, LY::v_off, EP, 32 * p2, e, lane),
-                       lds<bf16x8>(sm, LY::a_off + 2 * (q * CP + 32 * p2 + 8 * g4)), acc);
+          acc = mfma16(tr_feat<E, LY::SWZ>(sm, LY::v_off, 32 * p2, e, lane),
+                       lds<bf16x8>(sm, LY::a_off + AT::at(q, 4 * p2 + g4)), acc);
         if (q < L) {
           bf16x4 o = pack4(acc[0] * inv_den, acc[1] * inv_den, acc[2] * inv_den, acc[3] * inv_den);
           *reinterpret_cast<bf16x4*>(a.out + (tok0 + t0 + q) * E + e + 4 * g4) = o;

@@ -120,7 +120,7 @@ struct FavorLane {
   }
 };
 
-// MFMA operand by two transpose reads (see tr_operand), the second `gap`
+// MFMA operand by two transpose reads (see tr_feat), the second `gap`
 // bytes after the first: k-slots 0..3 and 4..7 of the lane's group.
 __device__ __forceinline__ bf16x8 tr_pair(char* sm, int addr, int gap) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + addr));
