@@ -10,3 +10,4 @@ from .la_oracle import (  # noqa: F401
     decode_step, softmax_score_matrix_bytes,
 )
 from .metrics import rowwise_rel_err, elementwise_max_rel_err  # noqa: F401
+from . import la_backward  # noqa: F401

@@ -1,0 +1,95 @@
+"""Pins of the fp64 gradient oracle (oracle/la_backward.py).
+
+The gradients are checked against central finite differences of the forward
+oracle (itself pinned in test_oracle_pins.py), against closed forms for
+uniform features, and against the scale invariance of the normalised output,
+so a dropped term, a wrong sign of the normaliser's gradient, a transposed
+weight matrix or a wrong feature-map derivative fails at least one of them.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+from oracle import la_backward as bwd
+
+RNG = np.random.default_rng(4321)
+
+
+def _loss(Q, K, V, dO, fmap, omega, causal, gate, eps, S0=None, z0=None):
+    if causal:
+        o, _, _ = orc.causal_recurrent(Q, K, V, fmap, omega, gate, eps, S0=S0, z0=z0)
+    else:
+        o = orc.noncausal(Q, K, V, fmap, omega, eps)
+    return float(np.sum(o * dO))
+
+
+CASES = [("elu1", False, "none", False), ("elu1", True, "none", False), ("elu1", True, "decay", False),
+         ("elu1", True, "decay", True), ("elu1", True, "none", True), ("favor", False, "none", False),
+         ("favor", True, "none", True), ("favor", True, "decay", False)]
+
+
+@pytest.mark.parametrize("fmap,causal,gate_kind,with_state", CASES)
+def test_gradients_match_finite_differences(fmap, causal, gate_kind, with_state):
+    """Directional derivatives of L = sum dO . o along random directions equal
+    <grad, direction> (central differences, step 1e-6, fp64)."""
+    B, H, n, d, e = 1, 2, 9, 5, 3
+    r = 8 if fmap == "favor" else d
+    Q = RNG.standard_normal((B, H, n, d)) * 0.7
+    K = RNG.standard_normal((B, H, n, d)) * 0.7
+    V = RNG.standard_normal((B, H, n, e))
+    dO = RNG.standard_normal((B, H, n, e))
+    omega = RNG.standard_normal((r, d)) if fmap == "favor" else None
+    gate = ("decay", np.array([0.9, 0.6])) if gate_kind == "decay" else None
+    S0 = z0 = None
+    if with_state:
+        S0 = np.abs(RNG.standard_normal((B, H, r, e)))
+        z0 = np.abs(RNG.standard_normal((B, H, r))) + 0.5
+    eps = 1e-3
+    dQ, dK, dV = bwd.backward(Q, K, V, dO, fmap, omega, causal, gate, eps, S0, z0)
+    step = 1e-6
+    for name, X, G in (("Q", Q, dQ), ("K", K, dK), ("V", V, dV)):
+        U = RNG.standard_normal(X.shape)
+        args = {"Q": Q, "K": K, "V": V}
+        args[name] = X + step * U
+        lp = _loss(args["Q"], args["K"], args["V"], dO, fmap, omega, causal, gate, eps, S0, z0)
+        args[name] = X - step * U
+        lm = _loss(args["Q"], args["K"], args["V"], dO, fmap, omega, causal, gate, eps, S0, z0)
+        fd = (lp - lm) / (2 * step)
+        an = float(np.sum(G * U))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_uniform_features_closed_form():
+    """Q = K = 0 gives phi = 1 (elu+1), so W_ij = d for j <= i and causal
+    o_i = d sum_{j<=i} v_j / (d (i + 1) + eps). Then dV_j = d sum_{i>=j} dO_i / den_i,
+    and every entry of dQ_i is eps (dO_i . o_i) / (d den_i): the output depends
+    on the scale of phi(q_i) only through eps."""
+    B, H, n, d, e = 1, 1, 12, 4, 3
+    Q = np.zeros((B, H, n, d))
+    K = np.zeros((B, H, n, d))
+    V = RNG.standard_normal((B, H, n, e))
+    dO = RNG.standard_normal((B, H, n, e))
+    eps = 0.25
+    dQ, dK, dV = bwd.backward(Q, K, V, dO, "elu1", None, True, None, eps)
+    den = d * np.arange(1, n + 1) + eps
+    o = d * np.cumsum(V[0, 0], axis=0) / den[:, None]
+    want_dV = np.array([d * np.sum(dO[0, 0, j:] / den[j:, None], axis=0) for j in range(n)])
+    np.testing.assert_allclose(dV[0, 0], want_dV, rtol=1e-13, atol=1e-13)
+    want_dQ = eps * np.sum(dO[0, 0] * o, axis=1) / (d * den)
+    np.testing.assert_allclose(dQ[0, 0], np.repeat(want_dQ[:, None], d, axis=1), rtol=1e-11, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal,gate_kind", [(False, "none"), (True, "none"), (True, "decay")])
+def test_output_invariant_to_query_feature_scale(causal, gate_kind):
+    """With eps = 0, o_i depends on phi(q_i) only through its direction, so
+    sum_f dL/dphi(q_i)_f phi(q_i)_f = 0. With all q > 0, elu+1 has phi' = 1 and
+    phi(q) = q + 1, so this reads sum_f dQ_if (q_if + 1) = 0."""
+    B, H, n, d, e = 1, 2, 10, 6, 4
+    Q = np.abs(RNG.standard_normal((B, H, n, d))) + 0.1
+    K = RNG.standard_normal((B, H, n, d))
+    V = RNG.standard_normal((B, H, n, e))
+    dO = RNG.standard_normal((B, H, n, e))
+    gate = ("decay", np.array([0.8, 0.95])) if gate_kind == "decay" else None
+    dQ, _, _ = bwd.backward(Q, K, V, dO, "elu1", None, causal, gate, 0.0)
+    s = np.sum(dQ * (Q + 1.0), axis=-1)
+    assert np.max(np.abs(s)) < 1e-12 * np.max(np.abs(dQ))
