@@ -144,6 +144,40 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
                      void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace la_backward needs for this problem. Pure host
+ * computation, same validation as la_backward (pointer fields not inspected).
+ */
+la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* fmap,
+                                     int32_t causal, const la_gate* gate, size_t* bytes);
+
+/*
+ * Gradients of the causal forward pass, for training with the parallel form
+ * ("Recurrent Reformulation", dileepadev page: trained in parallel, run as an
+ * RNN). For a loss L with dL/dout = dO, writes dQ = dL/dQ, dK = dL/dK and
+ * dV = dL/dV of la_forward(p, Q, K, V, fmap, 1, gate, S0, z0, ...):
+ *   g_i = dO_i / den_i,  h_i = -(dO_i . o_i) / den_i,  dW_ij = g_i . v_j + h_i,
+ *   dphi(q_i) = sum_{j<=i} dW_ij G_ij phi(k_j) (+ the carried state's share),
+ *   dphi(k_j) = sum_{i>=j} dW_ij G_ij phi(q_i),  dv_j = sum_{i>=j} w_ij g_i,
+ * with G_ij = 1 or gamma_h^(i-j) and w_ij = phi(q_i).phi(k_j) G_ij, then the
+ * feature map's derivative (elu+1: 1 for x > 0, exp(x) below).
+ *   Q, K, dQ, dK [B][H][n][d_k]; V, dO, dV [B][H][n][d_v]; all BF16 (in_dtype and
+ *   out_dtype must be BF16). S0, z0: the optional carried-in state of the forward
+ *   (both or neither; fp32). gamma is a constant: no gradient is returned for it,
+ *   nor for S0, z0.
+ *   workspace: device scratch of at least la_backward_workspace_size bytes,
+ *   256-byte aligned (segment states of both directions, g and h per token).
+ * Supported (else LA_ERR_UNSUPPORTED): causal == 1, ELU1, gate NONE or DECAY,
+ * (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
+ * inputs, each other or the workspace (LA_ERR_ALIAS). Numerics as la_forward:
+ * bf16 MFMA operands (phi, values, g, the scores and dW), fp32 accumulation,
+ * states and denominators.
+ */
+la_status la_backward(const la_problem* p, const void* Q, const void* K, const void* V,
+                      const void* dO, const la_feature_map* fmap, int32_t causal,
+                      const la_gate* gate, const float* S0, const float* z0, void* dQ,
+                      void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent step for a batch of carried states, updated IN PLACE
  * ("Recurrent Reformulation", dileepadev page: rank-1 update of S, update of
  * z, then the read-out):

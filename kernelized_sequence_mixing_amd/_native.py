@@ -18,7 +18,7 @@ LA_FMAP_ELU1, LA_FMAP_FAVOR = 0, 1
 LA_GATE_NONE, LA_GATE_DECAY, LA_GATE_GLA = 0, 1, 2
 
 EXPORTED = ("la_abi_version", "la_status_str", "la_forward_workspace_size", "la_forward_segments",
-            "la_forward", "la_decode_step", "la_feature_map_apply")
+            "la_forward", "la_backward_workspace_size", "la_backward", "la_decode_step", "la_feature_map_apply")
 
 
 class LaProblem(ctypes.Structure):
@@ -66,6 +66,13 @@ def lib():
     L.la_forward.argtypes = [POINTER(LaProblem), c_void_p, c_void_p, c_void_p, POINTER(LaFeatureMap), c_int32,
                              POINTER(LaGate), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_size_t, c_void_p]
+    L.la_backward_workspace_size.restype = c_int32
+    L.la_backward_workspace_size.argtypes = [POINTER(LaProblem), POINTER(LaFeatureMap), c_int32, POINTER(LaGate),
+                                             POINTER(c_size_t)]
+    L.la_backward.restype = c_int32
+    L.la_backward.argtypes = [POINTER(LaProblem), c_void_p, c_void_p, c_void_p, c_void_p, POINTER(LaFeatureMap),
+                              c_int32, POINTER(LaGate), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_size_t, c_void_p]
     L.la_decode_step.restype = c_int32
     L.la_decode_step.argtypes = [POINTER(LaProblem), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  POINTER(LaFeatureMap), POINTER(LaGate), c_void_p, c_void_p]

@@ -188,6 +188,72 @@ class PreparedForward:
         return self.out
 
 
+def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream):
+    """Validate and marshal one la_backward call: (ctypes arguments, keep-alive objects, (dQ, dK, dV))."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (dO, "dO")):
+        _dev(t, nm)
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3] or dO.shape != V.shape:
+        raise ValueError(f"shapes Q{tuple(Q.shape)} K{tuple(K.shape)} V{tuple(V.shape)} dO{tuple(dO.shape)} "
+                         "do not match")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype or dO.dtype != Q.dtype:
+        raise TypeError("Q, K, V, dO must share a dtype")
+    B, H, n, d_k = Q.shape
+    d_v = V.shape[3]
+    f, r = _fmap_struct(fmap, None, d_k)
+    g = _gate_struct(gate, (B, H, n, r))
+    p = _problem(B, H, n, d_k, d_v, _dt(Q), _dt(Q), eps)
+    for t, nm, shp in ((S0, "S0", (B, H, r, d_v)), (z0, "z0", (B, H, r))):
+        if t is not None:
+            _dev(t, nm)
+            if tuple(t.shape) != shp or t.dtype != torch.float32:
+                raise ValueError(f"{nm} must be float32 {shp}")
+    if grads is None:
+        grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    dQ, dK, dV = grads
+    for t, ref, nm in ((dQ, Q, "dQ"), (dK, K, "dK"), (dV, V, "dV")):
+        _dev(t, nm)
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{nm} has the wrong shape or dtype")
+    ws_bytes = ctypes.c_size_t(0)
+    N.check(N.lib().la_backward_workspace_size(ctypes.byref(p), ctypes.byref(f), 1, ctypes.byref(g),
+                                               ctypes.byref(ws_bytes)), "la_backward_workspace_size")
+    need = ws_bytes.value
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    args = (ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), ctypes.byref(f), 1, ctypes.byref(g), _ptr(S0),
+            _ptr(z0), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace), need, _stream(Q, stream))
+    keep = (p, f, g, Q, K, V, dO, gate, S0, z0, workspace)
+    return args, keep, (dQ, dK, dV)
+
+
+def backward(Q, K, V, dO, *, fmap="elu1", gate=None, eps=1e-6, S0=None, z0=None, grads=None, workspace=None,
+             stream=None):
+    """(dQ, dK, dV) of the causal forward for an incoming gradient dO, through la_backward.
+
+    Q, K [B, H, n, d_k]; V, dO [B, H, n, d_v] (bf16); gate None | ("decay", gamma[H]);
+    S0, z0: the forward's carried-in state, if any."""
+    args, _keep, grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream)
+    N.check(N.lib().la_backward(*args), "la_backward")
+    return grads
+
+
+class PreparedBackward:
+    """One la_backward call marshalled once (same arguments as backward);
+    calling the object launches it again on the same buffers and stream."""
+
+    def __init__(self, Q, K, V, dO, *, fmap="elu1", gate=None, eps=1e-6, S0=None, z0=None, grads=None,
+                 workspace=None, stream=None):
+        self._args, self._keep, self.grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace,
+                                                            stream)
+        self._fn = N.lib().la_backward
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            N.check(st, "la_backward")
+        return self.grads
+
+
 def _decode_args(S, z, q, k, v, fmap, omega, gate, eps, out_dtype, out, stream):
     for t, nm in ((S, "S"), (z, "z"), (q, "q"), (k, "k"), (v, "v")):
         _dev(t, nm)

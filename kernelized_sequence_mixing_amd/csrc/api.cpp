@@ -161,6 +161,44 @@ la_status check_forward_shape(const la_problem* p, const la_feature_map* f, int 
   return LA_OK;
 }
 
+// The backward pass: causal elu+1, bf16 in and out, no gate or RetNet decay,
+// (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}.
+la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int causal, const la_gate* g) {
+  la_status st = check_problem(p);
+  if (st != LA_OK) return st;
+  if ((st = check_fmap(f, p->d_k)) != LA_OK) return st;
+  if ((st = check_gate(g, false)) != LA_OK) return st;
+  if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
+  const int gk = gate_kind(g);
+  if (!causal && gk != LA_GATE_NONE) return LA_ERR_INVALID_ARG;
+  if (!causal || f->kind != LA_FMAP_ELU1 || gk == LA_GATE_GLA) return LA_ERR_UNSUPPORTED;
+  if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  const int key = p->d_k * 1000 + p->d_v;
+  if (key != 64064 && key != 64128 && key != 128064) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+struct BwdWsLayout {
+  size_t S_off, z_off, R_off, rh_off, G_off, h_off, bytes;
+  int P, L;
+};
+
+// Forward segment states, reverse segment states, g (bf16) and h per token.
+BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, int gate) {
+  BwdWsLayout w{};
+  plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate, &w.P, &w.L);
+  const size_t BH = (size_t)p->B * p->H, r = (size_t)f->r, dv = (size_t)p->d_v, n = (size_t)p->n;
+  const size_t states = BH * w.P * r * dv * 4, zs = BH * w.P * r * 4;
+  w.S_off = 0;
+  w.z_off = round_up(w.S_off + states, kAlign);
+  w.R_off = round_up(w.z_off + zs, kAlign);
+  w.rh_off = round_up(w.R_off + states, kAlign);
+  w.G_off = round_up(w.rh_off + zs, kAlign);
+  w.h_off = round_up(w.G_off + BH * n * dv * 2, kAlign);
+  w.bytes = round_up(w.h_off + BH * n * 4, kAlign);
+  return w;
+}
+
 }  // namespace
 }  // namespace la
 
@@ -335,6 +373,83 @@ la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
   plan.out = out;
   plan.stream = static_cast<hipStream_t>(stream);
   return launch_decode(plan);
+}
+
+la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* fmap, int32_t causal,
+                                     const la_gate* gate, size_t* bytes) {
+  if (bytes == nullptr) return LA_ERR_INVALID_ARG;
+  la_status st = check_backward_shape(p, fmap, causal, gate);
+  if (st != LA_OK) return st;
+  *bytes = bwd_workspace_layout(p, fmap, gate_kind(gate)).bytes;
+  return LA_OK;
+}
+
+la_status la_backward(const la_problem* p, const void* Q, const void* K, const void* V, const void* dO,
+                      const la_feature_map* fmap, int32_t causal, const la_gate* gate, const float* S0,
+                      const float* z0, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  la_status st = check_backward_shape(p, fmap, causal, gate);
+  if (st != LA_OK) return st;
+  if ((st = check_gate(gate, true)) != LA_OK) return st;
+  const int gk = gate_kind(gate);
+  if (Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || dQ == nullptr || dK == nullptr ||
+      dV == nullptr)
+    return LA_ERR_INVALID_ARG;
+  if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_INVALID_ARG;
+  for (const void* ptr : {Q, K, V, dO, (const void*)S0, (const void*)z0, (const void*)dQ, (const void*)dK,
+                          (const void*)dV})
+    if (ptr != nullptr && !aligned16(ptr)) return LA_ERR_INVALID_ARG;
+  const size_t BH = (size_t)p->B * p->H, n = (size_t)p->n, r = (size_t)fmap->r;
+  const size_t qk = BH * n * p->d_k * 2, vv = BH * n * p->d_v * 2;
+  const Range rq = range_of(Q, qk), rk = range_of(K, qk), rv = range_of(V, vv), rdo = range_of(dO, vv);
+  const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
+  const Range rs0 = range_of(S0, BH * r * p->d_v * 4), rz0 = range_of(z0, BH * r * 4);
+  const Range rdq = range_of(dQ, qk), rdk = range_of(dK, qk), rdv = range_of(dV, vv);
+  const BwdWsLayout wl = bwd_workspace_layout(p, fmap, gk);
+  const Range rws = range_of(workspace, wl.bytes);
+  for (Range o : {rdq, rdk, rdv, rws})
+    for (Range i : {rq, rk, rv, rdo, rgam, rs0, rz0})
+      if (overlaps(o, i)) return LA_ERR_ALIAS;
+  if (overlaps(rdq, rdk) || overlaps(rdq, rdv) || overlaps(rdk, rdv) || overlaps(rws, rdq) || overlaps(rws, rdk) ||
+      overlaps(rws, rdv))
+    return LA_ERR_ALIAS;
+  if (workspace == nullptr || workspace_bytes < wl.bytes) return LA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return LA_ERR_WORKSPACE;
+
+  BwdPlan plan{};
+  plan.B = p->B;
+  plan.H = p->H;
+  plan.n = p->n;
+  plan.dk = p->d_k;
+  plan.dv = p->d_v;
+  plan.r = fmap->r;
+  plan.in_dtype = p->in_dtype;
+  plan.out_dtype = p->out_dtype;
+  plan.eps = p->eps;
+  plan.fmap = fmap->kind;
+  plan.gate = gk;
+  plan.causal = 1;
+  plan.Q = Q;
+  plan.K = K;
+  plan.V = V;
+  plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
+  plan.S0 = S0;
+  plan.z0 = z0;
+  plan.P = wl.P;
+  plan.seg_len = wl.L;
+  plan.stream = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  plan.ws_S = reinterpret_cast<float*>(ws + wl.S_off);
+  plan.ws_z = reinterpret_cast<float*>(ws + wl.z_off);
+  plan.ws_R = reinterpret_cast<float*>(ws + wl.R_off);
+  plan.ws_rh = reinterpret_cast<float*>(ws + wl.rh_off);
+  plan.ws_G = ws + wl.G_off;
+  plan.ws_h = reinterpret_cast<float*>(ws + wl.h_off);
+  plan.dO = dO;
+  plan.dQ = dQ;
+  plan.dK = dK;
+  plan.dV = dV;
+  return launch_backward(plan);
 }
 
 la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t d_k, int32_t in_dtype,

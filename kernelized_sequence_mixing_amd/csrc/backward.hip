@@ -1,0 +1,94 @@
+// Launchers of the causal backward pass (backward.hpp) and its built shapes.
+#include "backward.hpp"
+
+namespace la {
+
+template <class K>
+static la_status launch_with_lds(K kernel, dim3 grid, int lds, hipStream_t st, const BwdArgs& b) {
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
+      hipSuccess)
+    return LA_ERR_HIP;
+  hipLaunchKernelGGL(kernel, grid, dim3(256), lds, st, b);
+  return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+template <int R, int E, int GATE>
+static la_status run_backward(const BwdPlan& p) {
+  static_assert(Waves<R, E>::NW == 4, "the backward kernels use four-wave workgroups");
+  const unsigned BH = unsigned(p.B) * unsigned(p.H);
+  BwdArgs b{};
+  b.Q = static_cast<const bf16*>(p.Q);
+  b.K = static_cast<const bf16*>(p.K);
+  b.V = static_cast<const bf16*>(p.V);
+  b.dO = static_cast<const bf16*>(p.dO);
+  b.gamma = p.gamma;
+  b.G = static_cast<bf16*>(p.ws_G);
+  b.h = p.ws_h;
+  b.R_ws = p.ws_R;
+  b.rh_ws = p.ws_rh;
+  b.dQ = static_cast<bf16*>(p.dQ);
+  b.dK = static_cast<bf16*>(p.dK);
+  b.dV = static_cast<bf16*>(p.dV);
+  b.H = p.H;
+  b.n = p.n;
+  b.P = p.P;
+  b.seg_len = p.seg_len;
+  b.eps = p.eps;
+  la_status st;
+  // forward state entering each segment: the forward's segment pass and scan
+  if (p.P > 1) {
+    CausalArgs a1{};
+    a1.Q = b.Q;
+    a1.K = b.K;
+    a1.V = b.V;
+    a1.gamma = p.gamma;
+    a1.H = p.H;
+    a1.n = p.n;
+    a1.P = p.P;
+    a1.seg_len = p.seg_len;
+    a1.eps = p.eps;
+    a1.S_out = p.ws_S;
+    a1.z_out = p.ws_z;
+    auto k1 = causal_segment_state<R, E, R, FM_ELU1, GATE>;
+    constexpr int lds1 = SegLayout<R, E, GATE>::bytes;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
+        hipSuccess)
+      return LA_ERR_HIP;
+    hipLaunchKernelGGL(k1, dim3(p.P - 1, BH), dim3(256), lds1, p.stream, a1);
+    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    if ((st = launch_segment_scan(p)) != LA_OK) return st;
+    b.S_in = p.ws_S;
+    b.z_in = p.ws_z;
+    b.in_head = (long long)p.P * R * E;
+    b.in_seg = (long long)R * E;
+  } else {
+    b.S_in = p.S0;
+    b.z_in = p.z0;
+    b.in_head = (long long)R * E;
+    b.in_seg = 0;
+  }
+  if ((st = launch_with_lds(bwd_pass_a<R, E, GATE>, dim3(p.P, BH), BwdALayout<R, E, GATE>::bytes, p.stream, b)) !=
+      LA_OK)
+    return st;
+  if (p.P > 1) {
+    if ((st = launch_with_lds(bwd_rstate<R, E, GATE>, dim3(p.P - 1, BH), BwdRLayout<R, E, GATE>::bytes, p.stream,
+                              b)) != LA_OK)
+      return st;
+    if ((st = launch_segment_scan_reverse(p, p.ws_R, p.ws_rh)) != LA_OK) return st;
+  }
+  return launch_with_lds(bwd_pass_b<R, E, GATE>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b);
+}
+
+// Built shapes: elu+1 with (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}, no gate or RetNet decay.
+la_status launch_backward(const BwdPlan& p) {
+  const int key = p.r * 1000 + p.dv;
+  const bool decay = p.gate == LA_GATE_DECAY;
+  switch (key) {
+    case 64064: return decay ? run_backward<64, 64, GT_DECAY>(p) : run_backward<64, 64, GT_NONE>(p);
+    case 64128: return decay ? run_backward<64, 128, GT_DECAY>(p) : run_backward<64, 128, GT_NONE>(p);
+    case 128064: return decay ? run_backward<128, 64, GT_DECAY>(p) : run_backward<128, 64, GT_NONE>(p);
+    default: return LA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace la

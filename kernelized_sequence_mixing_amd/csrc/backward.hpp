@@ -1,0 +1,660 @@
+// Backward pass of the chunkwise causal kernel (elu+1 features; no gate or
+// the RetNet decay), for training with the parallel form ("Recurrent
+// Reformulation", "Linear Attention Mechanisms" (dileepadev.github.io): the
+// layer is trained in parallel and served as an RNN).
+//
+// For a loss with dL/do_i = dO_i, write the forward output o_i = num_i / den_i
+// with num_i = sum_{j<=i} w_ij v_j, den_i = sum_{j<=i} w_ij + eps,
+// w_ij = phi(q_i).phi(k_j) gamma^(i-j). Then
+//   g_i = dO_i / den_i,  h_i = -(dO_i . o_i) / den_i,  dW_ij = g_i . v_j + h_i,
+//   dphi(q_i) = sum_{j<=i} dW_ij gamma^(i-j) phi(k_j)   (+ the carried state's share)
+//   dphi(k_j) = sum_{i>=j} dW_ij gamma^(i-j) phi(q_i),  dv_j = sum_{i>=j} w_ij g_i,
+// and dq = dphi(q) phi'(q), dk = dphi(k) phi'(k) with phi'(x) = min(phi(x), 1)
+// for elu+1 (1 for x > 0, exp(x) = phi(x) below). The sums over j <= i run
+// chunkwise exactly like the forward: intra-chunk masked products plus the
+// forward state (S, z) entering the chunk. The sums over i >= j run the other
+// way: intra-chunk products plus the reverse state R = sum_{later i}
+// gamma^(..) phi(q_i) [g_i, h_i]^T entering the chunk from its end.
+//
+// Kernels (one workgroup of four waves per (head, segment), as the forward):
+//   forward segment pass + scan  -> S, z entering each segment (forward code)
+//   bwd_pass_a   chunks in order: recompute den, o; g, h (to the workspace);
+//                dW; dq = (Phi_k^T dW^T + gamma^(t+1) (S^T g + z h))^T phi'(q)
+//   bwd_rstate   each segment's own reverse state, rows read back to front
+//   scan (reverse)                -> R entering each segment from its end
+//   bwd_pass_b   chunks back to front: W, dW; dv = W^T g + Phi_k R'^T-part;
+//                dk = (Phi_q^T dW + R [v; 1])^T phi'(k); then R <- gamma^L R + ...
+// All LDS tiles use the per-row chunk permutation of FeatTile.
+#pragma once
+
+#include "chunked.hpp"
+
+namespace la {
+
+struct BwdArgs {
+  const bf16* Q;
+  const bf16* K;
+  const bf16* V;
+  const bf16* dO;
+  const float* gamma;
+  const float* S_in;  // pass A: forward state entering each segment (nullable)
+  const float* z_in;
+  long long in_head, in_seg;  // S_in element strides between heads and segments
+  bf16* G;                    // [B H n E] g_i (pass A writes, passes R / B read)
+  float* h;                   // [B H n] h_i
+  float* R_ws;                // [B H P R E] reverse state deltas (bwd_rstate), then R entering (scan)
+  float* rh_ws;               // [B H P R]
+  bf16* dQ;
+  bf16* dK;
+  bf16* dV;
+  int H, n, P, seg_len;
+  float eps;
+};
+
+// One chunk of an E-wide bf16 array in the row-major layout of RawChunk with
+// four waves: wave w holds tokens 16 w .. 16 w + 15, lane l token 16 w + l / 4
+// and 8-column blocks l % 4 + 4 j.
+template <int E>
+struct RowsE {
+  bf16x8 v[E / 32];
+  __device__ __forceinline__ void load(const bf16* X, long long tok0, int t0, int row_end, int lane, int w) {
+    const long long row = tok0 + min(t0 + 16 * w + lane / 4, row_end - 1);
+#pragma unroll
+    for (int j = 0; j < E / 32; ++j) v[j] = *reinterpret_cast<const bf16x8*>(X + row * E + 8 * (lane % 4 + 4 * j));
+  }
+  // into a FeatTile<E> tile; rows >= L are zero
+  __device__ __forceinline__ void store(char* sm, int off, int L, int lane, int w) const {
+    const int t = 16 * w + lane / 4;
+#pragma unroll
+    for (int j = 0; j < E / 32; ++j) lds<bf16x8>(sm, off + FeatTile<E>::at(t, lane % 4 + 4 * j)) = keep_if(t < L, v[j]);
+  }
+};
+
+// bf16 image of a wave's state slab (rows all R, value columns [w E/4, (w+1) E/4))
+// into an [R][E] tile (FeatTile<E> rows), for products that contract over E.
+template <int R, int E, class SArr>
+__device__ __forceinline__ void state_image(const SArr& S, char* sm, int off, int lane, int w) {
+  constexpr int NEB = E / 64;
+  const int g4 = lane >> 4, c16 = lane & 15, ebase = w * (E / 4);
+#pragma unroll
+  for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) {
+      const int e = ebase + 16 * eb + c16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lds<bf16>(sm, off + FeatTile<E>::at(16 * rt + 4 * g4 + i, e / 8, 2 * (e % 8))) = (bf16)S[rt][eb][i];
+    }
+}
+
+// The state slab as the A operand of a product over the state rows (features):
+// k-slot j of lane (g, c) is feature 32 p + 4 g + j (j < 4) or 32 p + 16 + 4 g +
+// (j - 4), the order of the forward's inter-chunk product.
+template <int R, int E, class SArr, class OArr>
+__device__ __forceinline__ void state_operand(const SArr& S, OArr& op) {
+#pragma unroll
+  for (int p = 0; p < R / 32; ++p)
+#pragma unroll
+    for (int eb = 0; eb < E / 64; ++eb)
+      op[p][eb] = cat8(pack4(S[2 * p][eb][0], S[2 * p][eb][1], S[2 * p][eb][2], S[2 * p][eb][3]),
+                       pack4(S[2 * p + 1][eb][0], S[2 * p + 1][eb][1], S[2 * p + 1][eb][2], S[2 * p + 1][eb][3]));
+}
+
+// B operand of that product from a feature tile: row t, the same eight features.
+template <int R>
+__device__ __forceinline__ bf16x8 feature_pairs(char* sm, int off, int t, int p, int g4) {
+  using FT = FeatTile<R>;
+  return cat8(lds<bf16x4>(sm, off + FT::at(t, 4 * p + (g4 >> 1), 8 * (g4 & 1))),
+              lds<bf16x4>(sm, off + FT::at(t, 4 * p + 2 + (g4 >> 1), 8 * (g4 & 1))));
+}
+
+// ---------------------------------------------------------------------------
+// Pass A: g, h and dq, chunks in order from the forward state.
+// ---------------------------------------------------------------------------
+template <int R, int E, int GATE>
+struct BwdALayout {
+  static constexpr int FTB = FeatTile<R>::BYTES, VTB = FeatTile<E>::BYTES, ATB = FeatTile<kChunk>::BYTES;
+  static constexpr int q_off = 0;                      // phi(q)
+  static constexpr int k_off = q_off + FTB;            // phi(k)
+  static constexpr int v_off = k_off + FTB;            // v
+  static constexpr int g_off = v_off + VTB;            // dO, then g = dO / den
+  static constexpr int kh_off = g_off + VTB;           // RetNet: gamma^(L-1-t) phi(k)
+  static constexpr int a_off = kh_off + (GATE == GT_DECAY ? FTB : 0);  // scores A, then dW
+  static constexpr int sb_off = a_off + ATB;           // bf16 [R][E] image of S entering the chunk
+  static constexpr int z_off = sb_off + R * 2 * E;     // [R] z entering the chunk
+  static constexpr int rs_off = z_off + R * 4;         // [64] score row sums
+  static constexpr int zd_off = rs_off + kChunk * 4;   // [64] phi(q) . z
+  static constexpr int inv_off = zd_off + kChunk * 4;  // [64] 1 / den
+  static constexpr int hp_off = inv_off + kChunk * 4;  // [4][64] partial g . o per wave
+  static constexpr int gam_off = hp_off + 4 * kChunk * 4;
+  static constexpr int bytes = gam_off + R * 4;
+};
+
+// h_i = -g_i . o_i from the four waves' partial dot products (fixed order).
+// h is taken against the bf16-rounded g that every product uses, so that
+// g_i . v_j + h_i = g_i . (v_j - o_i) holds for the rounded g: the two terms
+// cancel to a difference of the size of v_j - o_i, and an error in g that is
+// the same for every key would otherwise survive that cancellation (measured
+// on a CPU model of these rounding points: dq error 2.2% of the head's largest
+// entry with h = -(dO . o) / den, 0.3% with this h, all else exact).
+__device__ __forceinline__ float bwd_h(char* sm, int hp_off, int i) {
+  const float s = ((lds<float>(sm, hp_off + 4 * i) + lds<float>(sm, hp_off + 256 + 4 * i)) +
+                   lds<float>(sm, hp_off + 512 + 4 * i)) +
+                  lds<float>(sm, hp_off + 768 + 4 * i);
+  return -s;
+}
+
+template <int R, int E, int GATE>
+__global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
+  extern __shared__ __attribute__((aligned(16))) char sm[];
+  using LY = BwdALayout<R, E, GATE>;
+  using FT = FeatTile<R>;
+  using VT = FeatTile<E>;
+  using AT = FeatTile<kChunk>;
+  constexpr int NW = 4, NEB = E / 64, KP = R / 32, KE = E / 32, FPW = R / 64;
+  static_assert(R * E < 128 * 128, "four-wave layout");
+  const int lane = lane_id(), w = wave_id<NW>();
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int s = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int hd = int(bh % b.H);
+  const int t_begin = s * b.seg_len;
+  const int t_end = min(b.n, t_begin + b.seg_len);
+  const long long tok0 = bh * b.n;
+  const int ebase = w * (E / NW);
+  float lg2gam = 0.f;
+  if constexpr (GATE == GT_DECAY) lg2gam = log2f(b.gamma[hd]);
+  CausalArgs ca{};
+  ca.Q = b.Q;
+  ca.K = b.K;
+  ca.V = b.V;
+
+  using Raw = RawChunk<R, E, R, FM_ELU1, GATE, true, NW>;
+  const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+  Raw raw;
+  RowsE<E> rdo;
+  raw.load(ca, tok0, t_begin, t_end, lane, w);
+  rdo.load(b.dO, tok0, t_begin, t_end, lane, w);
+
+  // ---- forward state entering the segment
+  f32x4 S[R / 16][NEB];
+  f32x4 Z[ZTiles<R, NW>::ZT];
+  if (b.S_in != nullptr) {
+    const float* Sp = b.S_in + bh * b.in_head + s * b.in_seg;
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[rt][eb][i] = Sp[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16];
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  z_load<R, NW>(Z, b.S_in != nullptr ? b.z_in + (bh * b.in_head + s * b.in_seg) / E : nullptr, lane, w);
+  z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
+
+  for (int ci = 0; ci < nch; ++ci) {
+    const int t0 = t_begin + ci * kChunk;
+    const int L = min(kChunk, b.n - t0);
+    // ---- prelude: features, values, dO, and the bf16 image of S
+    chunk_prelude<R, E, R, FM_ELU1, GATE, true, NW, true>(raw, ca, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
+                                                          LY::v_off, LY::gam_off, 0, lane, w);
+    rdo.store(sm, LY::g_off, L, lane, w);
+    state_image<R, E>(S, sm, LY::sb_off, lane, w);
+    raw.load(ca, tok0, t0 + kChunk, t_end, lane, w);
+    rdo.load(b.dO, tok0, t0 + kChunk, t_end, lane, w);
+    lds_barrier();
+
+    // ---- scores A (masked, RetNet-weighted) and their row sums; phi(q) . z
+    {
+      const int qw = w;
+      const int q = 16 * qw + c16;
+      bf16x8 qop[KP];
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks) qop[ks] = lds<bf16x8>(sm, LY::q_off + FT::at(q, 4 * ks + g4));
+      float rs = 0.f;
+      for (int c = 0; c <= qw; ++c) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KP; ++ks)
+          acc = mfma16(lds<bf16x8>(sm, LY::k_off + FT::at(16 * c + c16, 4 * ks + g4)), qop[ks], acc);
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * c + 4 * g4 + i;
+          v[i] = key > q ? 0.f : acc[i];
+          if constexpr (GATE == GT_DECAY) v[i] *= exp2f(float(q - key) * lg2gam);
+        }
+        const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
+        rs += (lo_bf16_f32(p01) + hi_bf16_f32(p01)) + (lo_bf16_f32(p23) + hi_bf16_f32(p23));
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        lds<u32x2>(sm, LY::a_off + AT::at(q, 2 * c + (g4 >> 1), 8 * (g4 & 1))) = u32x2{p01, p23};
+      }
+      if ((qw & 1) == 0) lds<bf16x4>(sm, LY::a_off + AT::at(q, 2 * (qw + 1) + (g4 >> 1), 8 * (g4 & 1))) = bf16x4{};
+      rs = sum_over_groups(rs);
+      float zd = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zd += to_f32(qop[ks][j]) * lds<float>(sm, LY::z_off + 4 * (32 * ks + 8 * g4 + j));
+      zd = sum_over_groups(zd);
+      if constexpr (GATE == GT_DECAY) zd *= exp2f(float(q + 1) * lg2gam);
+      if (g4 == 0) {
+        lds<float>(sm, LY::rs_off + 4 * q) = rs;
+        lds<float>(sm, LY::zd_off + 4 * q) = zd;
+        lds<float>(sm, LY::inv_off + 4 * q) = 1.f / (rs + zd + b.eps);
+      }
+    }
+    lds_barrier();
+
+    // ---- o (fp32, not stored), g = dO / den (bf16) and the wave's share of g . o
+    {
+      bf16x8 Sop[KP][NEB];
+      state_operand<R, E>(S, Sop);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const int q = 16 * qt + c16;
+        bf16x8 qb[KP];
+#pragma unroll
+        for (int p = 0; p < KP; ++p) qb[p] = feature_pairs<R>(sm, LY::q_off, q, p, g4);
+        const float inv_den = lds<float>(sm, LY::inv_off + 4 * q);
+        float isc = 1.f;
+        if constexpr (GATE == GT_DECAY) isc = exp2f(float(q + 1) * lg2gam);
+        float hp = 0.f;
+#pragma unroll
+        for (int eb = 0; eb < NEB; ++eb) {
+          const int e = ebase + 16 * eb;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < KP; ++p) acc = mfma16(Sop[p][eb], qb[p], acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] *= isc;
+#pragma unroll
+          for (int p2 = 0; p2 <= qt / 2; ++p2)
+            acc = mfma16(tr_feat<E, true>(sm, LY::v_off, 32 * p2, e, lane),
+                         lds<bf16x8>(sm, LY::a_off + AT::at(q, 4 * p2 + g4)), acc);
+          // acc[i] = num[q][e + 4 g + i]
+          const int go = LY::g_off + VT::at(q, (e + 4 * g4) / 8, 2 * ((e + 4 * g4) % 8));
+          const bf16x4 dov = lds<bf16x4>(sm, go);
+          const bf16x4 gb = pack4(to_f32(dov[0]) * inv_den, to_f32(dov[1]) * inv_den, to_f32(dov[2]) * inv_den,
+                                  to_f32(dov[3]) * inv_den);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hp += to_f32(gb[i]) * (acc[i] * inv_den);
+          lds<bf16x4>(sm, go) = gb;
+        }
+        hp = sum_over_groups(hp);
+        if (g4 == 0) lds<float>(sm, LY::hp_off + 256 * w + 4 * q) = hp;
+      }
+    }
+    lds_barrier();
+
+    // ---- dW (masked, RetNet-weighted) over the score tile: dW^T tiles = V G^T, + h
+    {
+      const int it = w;
+      const int i = 16 * it + c16;
+      const float hi = bwd_h(sm, LY::hp_off, i);
+      for (int jt = 0; jt <= it; ++jt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KE; ++ks)
+          acc = mfma16(lds<bf16x8>(sm, LY::v_off + VT::at(16 * jt + c16, 4 * ks + g4)),
+                       lds<bf16x8>(sm, LY::g_off + VT::at(i, 4 * ks + g4)), acc);
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = 16 * jt + 4 * g4 + u;
+          v[u] = j > i ? 0.f : acc[u] + hi;
+          if constexpr (GATE == GT_DECAY) v[u] *= exp2f(float(i - j) * lg2gam);
+        }
+        lds<bf16x4>(sm, LY::a_off + AT::at(i, 2 * jt + (g4 >> 1), 8 * (g4 & 1))) = pack4(v[0], v[1], v[2], v[3]);
+      }
+      if ((it & 1) == 0) lds<bf16x4>(sm, LY::a_off + AT::at(i, 2 * (it + 1) + (g4 >> 1), 8 * (g4 & 1))) = bf16x4{};
+    }
+    lds_barrier();
+
+    // ---- dphi(q)^T = Phi_k^T dW^T + gamma^(t+1) (S G^T + z h^T); dq = dphi(q) phi'(q)
+#pragma unroll
+    for (int u = 0; u < FPW; ++u) {
+      const int ft = w * FPW + u;
+      const int f0 = 16 * ft + 4 * g4;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int i = 16 * it + c16;
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p <= it / 2; ++p)
+          a1 = mfma16(tr_feat<R, true>(sm, LY::k_off, 32 * p, 16 * ft, lane),
+                      lds<bf16x8>(sm, LY::a_off + AT::at(i, 4 * p + g4)), a1);
+#pragma unroll
+        for (int ks = 0; ks < KE; ++ks)
+          a2 = mfma16(lds<bf16x8>(sm, LY::sb_off + VT::at(16 * ft + c16, 4 * ks + g4)),
+                      lds<bf16x8>(sm, LY::g_off + VT::at(i, 4 * ks + g4)), a2);
+        const float hi = bwd_h(sm, LY::hp_off, i);
+        float sc = 1.f;
+        if constexpr (GATE == GT_DECAY) sc = exp2f(float(i + 1) * lg2gam);
+        const bf16x4 ph = lds<bf16x4>(sm, LY::q_off + FT::at(i, f0 / 8, 2 * (f0 % 8)));
+        float dq[4];
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const float dphi = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::z_off + 4 * (f0 + u2)) * hi);
+          dq[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
+        }
+        if (i < L) *reinterpret_cast<bf16x4*>(b.dQ + (tok0 + t0 + i) * R + f0) = pack4(dq[0], dq[1], dq[2], dq[3]);
+      }
+    }
+
+    // ---- g and h for the reverse passes
+    {
+      const int t = 16 * w + lane / 4;
+      if (t < L) {
+#pragma unroll
+        for (int j = 0; j < E / 32; ++j)
+          *reinterpret_cast<bf16x8*>(b.G + (tok0 + t0 + t) * E + 8 * (lane % 4 + 4 * j)) =
+              lds<bf16x8>(sm, LY::g_off + VT::at(t, lane % 4 + 4 * j));
+      }
+      if (w == 0 && lane < L) b.h[tok0 + t0 + lane] = bwd_h(sm, LY::hp_off, lane);
+    }
+    lds_barrier();  // z, the S image and the tiles are read above; the update below rewrites z
+
+    // ---- carry the forward state past this chunk
+    const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+    state_update<R, E, GATE, NW, true>(S, Z, sm, GATE == GT_DECAY ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
+                                       gsc, lane, w);
+    z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
+    lds_barrier();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse state of each segment (segments 1 .. P-1):
+//   dR_s = sum_{i in s} gamma^(i - start_s) phi(q_i) g_i^T,  dr_s = the same with h_i,
+// chunks from the segment's end, rows of each chunk back to front, so that
+// with t the row index of the reversed chunk, gamma^(i - chunk start) =
+// gamma^(L-1-t): the weighting and update of the forward segment pass.
+// ---------------------------------------------------------------------------
+template <int R, int E, int GATE>
+struct BwdRLayout {
+  static constexpr int k_off = 0;  // gamma^(L-1-t) phi(q) (reversed rows)
+  static constexpr int v_off = k_off + FeatTile<R>::BYTES;  // g (reversed rows)
+  static constexpr int hw_off = v_off + FeatTile<E>::BYTES;  // [64] h (reversed rows)
+  static constexpr int gam_off = hw_off + kChunk * 4;
+  static constexpr int logg_off = gam_off + R * 4;
+  static constexpr int bytes = logg_off + R * 4;
+};
+
+template <int R, int E, int GATE>
+__global__ __launch_bounds__(256) void bwd_rstate(BwdArgs b) {
+  extern __shared__ __attribute__((aligned(16))) char sm[];
+  using LY = BwdRLayout<R, E, GATE>;
+  constexpr int NW = 4, NEB = E / 64;
+  const int lane = lane_id(), w = wave_id<NW>();
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int s = blockIdx.x + 1;
+  const long long bh = blockIdx.y;
+  const int hd = int(bh % b.H);
+  const int t_begin = s * b.seg_len;
+  const int t_end = min(b.n, t_begin + b.seg_len);
+  const long long tok0 = bh * b.n;
+  const int ebase = w * (E / NW);
+  float lg2gam = 0.f;
+  if constexpr (GATE == GT_DECAY) lg2gam = log2f(b.gamma[hd]);
+  CausalArgs ca{};
+
+  f32x4 Rs[R / 16][NEB];
+#pragma unroll
+  for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) Rs[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 Rz[ZTiles<R, NW>::ZT];
+  z_load<R, NW>(Rz, nullptr, lane, w);
+
+  using Raw = RawChunk<R, E, R, FM_ELU1, GATE, false, NW>;
+  // reversed chunk u0: row t holds token t_end - 1 - (u0 + t) (clamped into the segment)
+  auto load_rev = [&](Raw& rw, float& hv, int u0) {
+    const int tt = t_end - 1 - (u0 + 16 * w + lane / 4);
+    const long long row = tok0 + max(tt, t_begin);
+#pragma unroll
+    for (int j = 0; j < R / 32; ++j) rw.k[j] = *reinterpret_cast<const bf16x8*>(b.Q + row * R + 8 * (lane % 4 + 4 * j));
+#pragma unroll
+    for (int j = 0; j < E / 32; ++j) rw.v[j] = *reinterpret_cast<const bf16x8*>(b.G + row * E + 8 * (lane % 4 + 4 * j));
+    hv = b.h[row];
+  };
+  const int seg = t_end - t_begin;
+  Raw raw;
+  float hv;
+  load_rev(raw, hv, 0);
+  for (int u0 = 0; u0 < seg; u0 += kChunk) {
+    const int L = min(kChunk, seg - u0);
+    chunk_prelude<R, E, R, FM_ELU1, GATE, false, NW, true>(raw, ca, L, lg2gam, sm, 0, LY::k_off, 0, LY::v_off,
+                                                           LY::gam_off, LY::logg_off, lane, w);
+    {
+      const int t = 16 * w + lane / 4;
+      if ((lane & 3) == 0) lds<float>(sm, LY::hw_off + 4 * t) = t < L ? hv : 0.f;
+    }
+    load_rev(raw, hv, u0 + kChunk);
+    lds_barrier();
+    const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+    state_update<R, E, GATE, NW, true, true>(Rs, Rz, sm, LY::k_off, LY::v_off, LY::gam_off, gsc, lane, w,
+                                             LY::hw_off);
+    lds_barrier();
+  }
+  const long long slot = bh * b.P + s;
+  float* Ro = b.R_ws + slot * R * E;
+#pragma unroll
+  for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ro[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = Rs[rt][eb][i];
+  z_store<R, NW>(Rz, b.rh_ws + slot * R, lane, w);
+}
+
+// ---------------------------------------------------------------------------
+// Pass B: dk and dv, chunks from the segment's end, from the reverse state R
+// entering each chunk from its end.
+// ---------------------------------------------------------------------------
+template <int R, int E, int GATE>
+struct BwdBLayout {
+  static constexpr int FTB = FeatTile<R>::BYTES, VTB = FeatTile<E>::BYTES, ATB = FeatTile<kChunk>::BYTES;
+  static constexpr int q_off = 0;                      // phi(q)
+  static constexpr int k_off = q_off + FTB;            // phi(k)
+  static constexpr int v_off = k_off + FTB;            // v
+  static constexpr int g_off = v_off + VTB;            // g
+  static constexpr int qw_off = g_off + VTB;           // RetNet: gamma^t phi(q)
+  static constexpr int w_off = qw_off + (GATE == GT_DECAY ? FTB : 0);  // W^T [key][query]
+  static constexpr int dw_off = w_off + ATB;           // dW^T [key][query]
+  static constexpr int rb_off = dw_off + ATB;          // bf16 [R][E] image of R entering the chunk
+  static constexpr int rh_off = rb_off + R * 2 * E;    // [R] r_h entering the chunk
+  static constexpr int hw_off = rh_off + R * 4;        // [64] h
+  static constexpr int gam_off = hw_off + kChunk * 4;
+  static constexpr int bytes = gam_off + R * 4;
+};
+
+template <int R, int E, int GATE>
+__global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
+  extern __shared__ __attribute__((aligned(16))) char sm[];
+  using LY = BwdBLayout<R, E, GATE>;
+  using FT = FeatTile<R>;
+  using VT = FeatTile<E>;
+  using AT = FeatTile<kChunk>;
+  constexpr int NW = 4, NEB = E / 64, KP = R / 32, KE = E / 32, FPW = R / 64;
+  static_assert(R * E < 128 * 128, "four-wave layout");
+  const int lane = lane_id(), w = wave_id<NW>();
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int s = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int hd = int(bh % b.H);
+  const int t_begin = s * b.seg_len;
+  const int t_end = min(b.n, t_begin + b.seg_len);
+  const long long tok0 = bh * b.n;
+  const int ebase = w * (E / NW);
+  float lg2gam = 0.f;
+  if constexpr (GATE == GT_DECAY) lg2gam = log2f(b.gamma[hd]);
+  CausalArgs ca{};
+  ca.Q = b.Q;
+  ca.K = b.K;
+  ca.V = b.V;
+
+  // ---- reverse state entering the segment from its end
+  f32x4 Rs[R / 16][NEB];
+  f32x4 Rz[ZTiles<R, NW>::ZT];
+  const bool has_in = b.P > 1;
+  {
+    const long long slot = bh * b.P + s;
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Rs[rt][eb][i] = has_in ? b.R_ws[slot * R * E + (16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] : 0.f;
+    z_load<R, NW>(Rz, has_in ? b.rh_ws + slot * R : nullptr, lane, w);
+  }
+
+  using Raw = RawChunk<R, E, R, FM_ELU1, GT_NONE, true, NW>;
+  const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+  Raw raw;
+  RowsE<E> rg;
+  float hv = 0.f;
+  auto load = [&](int ci) {
+    const int t0 = t_begin + ci * kChunk;
+    raw.load(ca, tok0, t0, t_end, lane, w);
+    rg.load(b.G, tok0, t0, t_end, lane, w);
+    hv = b.h[tok0 + min(t0 + lane, t_end - 1)];
+  };
+  load(nch - 1);
+  for (int ci = nch - 1; ci >= 0; --ci) {
+    const int t0 = t_begin + ci * kChunk;
+    const int L = min(kChunk, b.n - t0);
+    // ---- prelude
+    chunk_prelude<R, E, R, FM_ELU1, GT_NONE, true, NW, true>(raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0, LY::v_off,
+                                                             LY::gam_off, 0, lane, w);
+    if constexpr (GATE == GT_DECAY) {
+      // gamma^t phi(q) for the reverse-state update
+      const int t = 16 * w + lane / 4;
+      const float wt = exp2f(float(t) * lg2gam);
+#pragma unroll
+      for (int j = 0; j < R / 32; ++j) {
+        float f[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) f[u] = elu1(to_f32(raw.q[j][u])) * wt;
+        lds<bf16x8>(sm, LY::qw_off + FT::at(t, lane % 4 + 4 * j)) =
+            keep_if(t < L, cat8(pack4(f[0], f[1], f[2], f[3]), pack4(f[4], f[5], f[6], f[7])));
+      }
+    }
+    rg.store(sm, LY::g_off, L, lane, w);
+    if (w == 0) lds<float>(sm, LY::hw_off + 4 * lane) = lane < L ? hv : 0.f;
+    state_image<R, E>(Rs, sm, LY::rb_off, lane, w);
+    z_store<R, NW>(Rz, reinterpret_cast<float*>(sm + LY::rh_off), lane, w);
+    if (ci > 0) load(ci - 1);
+    lds_barrier();
+
+    // ---- W^T and dW^T tiles [key j][query i], i >= j: wave w owns key tile w
+    {
+      const int jt = w;
+      const int j = 16 * jt + c16;
+      for (int it = jt; it < 4; ++it) {
+        f32x4 aw = {0.f, 0.f, 0.f, 0.f}, ad = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KP; ++ks)
+          aw = mfma16(lds<bf16x8>(sm, LY::q_off + FT::at(16 * it + c16, 4 * ks + g4)),
+                      lds<bf16x8>(sm, LY::k_off + FT::at(j, 4 * ks + g4)), aw);
+#pragma unroll
+        for (int ks = 0; ks < KE; ++ks)
+          ad = mfma16(lds<bf16x8>(sm, LY::g_off + VT::at(16 * it + c16, 4 * ks + g4)),
+                      lds<bf16x8>(sm, LY::v_off + VT::at(j, 4 * ks + g4)), ad);
+        // aw[u] = phi(q_i) . phi(k_j), ad[u] = g_i . v_j with i = 16 it + 4 g + u
+        float vw[4], vd[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 16 * it + 4 * g4 + u;
+          const bool ok = i >= j;
+          float dec = 1.f;
+          if constexpr (GATE == GT_DECAY) dec = exp2f(float(i - j) * lg2gam);
+          vw[u] = ok ? aw[u] * dec : 0.f;
+          vd[u] = ok ? (ad[u] + lds<float>(sm, LY::hw_off + 4 * i)) * dec : 0.f;
+        }
+        const int o = AT::at(j, 2 * it + (g4 >> 1), 8 * (g4 & 1));
+        lds<bf16x4>(sm, LY::w_off + o) = pack4(vw[0], vw[1], vw[2], vw[3]);
+        lds<bf16x4>(sm, LY::dw_off + o) = pack4(vd[0], vd[1], vd[2], vd[3]);
+      }
+      if (jt & 1) {
+        const int o = AT::at(j, 2 * (jt - 1) + (g4 >> 1), 8 * (g4 & 1));
+        lds<bf16x4>(sm, LY::w_off + o) = bf16x4{};
+        lds<bf16x4>(sm, LY::dw_off + o) = bf16x4{};
+      }
+    }
+    lds_barrier();
+
+    // ---- dv^T = G^T W (intra) + gamma^(L-t) R'^T phi(k)^T (inter): the wave's value columns
+    {
+      bf16x8 Rop[KP][NEB];
+      state_operand<R, E>(Rs, Rop);
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = 16 * jt + c16;
+        bf16x8 kb[KP];
+#pragma unroll
+        for (int p = 0; p < KP; ++p) kb[p] = feature_pairs<R>(sm, LY::k_off, j, p, g4);
+        float sc = 1.f;
+        if constexpr (GATE == GT_DECAY) sc = exp2f(float(L - j) * lg2gam);
+#pragma unroll
+        for (int eb = 0; eb < NEB; ++eb) {
+          const int e = ebase + 16 * eb;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < KP; ++p) acc = mfma16(Rop[p][eb], kb[p], acc);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] *= sc;
+#pragma unroll
+          for (int p = jt / 2; p < 2; ++p)
+            acc = mfma16(tr_feat<E, true>(sm, LY::g_off, 32 * p, e, lane),
+                         lds<bf16x8>(sm, LY::w_off + AT::at(j, 4 * p + g4)), acc);
+          if (j < L)
+            *reinterpret_cast<bf16x4*>(b.dV + (tok0 + t0 + j) * E + e + 4 * g4) = pack4(acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
+    }
+
+    // ---- dphi(k)^T = Phi_q^T dW (intra) + gamma^(L-t) (R v + r_h) (inter); dk = dphi(k) phi'(k)
+#pragma unroll
+    for (int u = 0; u < FPW; ++u) {
+      const int ft = w * FPW + u;
+      const int f0 = 16 * ft + 4 * g4;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = 16 * jt + c16;
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = jt / 2; p < 2; ++p)
+          a1 = mfma16(tr_feat<R, true>(sm, LY::q_off, 32 * p, 16 * ft, lane),
+                      lds<bf16x8>(sm, LY::dw_off + AT::at(j, 4 * p + g4)), a1);
+#pragma unroll
+        for (int ks = 0; ks < KE; ++ks)
+          a2 = mfma16(lds<bf16x8>(sm, LY::rb_off + VT::at(16 * ft + c16, 4 * ks + g4)),
+                      lds<bf16x8>(sm, LY::v_off + VT::at(j, 4 * ks + g4)), a2);
+        float sc = 1.f;
+        if constexpr (GATE == GT_DECAY) sc = exp2f(float(L - j) * lg2gam);
+        const bf16x4 ph = lds<bf16x4>(sm, LY::k_off + FT::at(j, f0 / 8, 2 * (f0 % 8)));
+        float dk[4];
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const float dphi = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::rh_off + 4 * (f0 + u2)));
+          dk[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
+        }
+        if (j < L) *reinterpret_cast<bf16x4*>(b.dK + (tok0 + t0 + j) * R + f0) = pack4(dk[0], dk[1], dk[2], dk[3]);
+      }
+    }
+
+    // ---- R <- gamma^L R + (gamma^t phi(q))^T [g, h]: the state entering the previous chunk
+    const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+    state_update<R, E, GATE, NW, true, true>(Rs, Rz, sm, GATE == GT_DECAY ? LY::qw_off : LY::q_off, LY::g_off,
+                                             LY::gam_off, gsc, lane, w, LY::hw_off);
+    lds_barrier();
+  }
+}
+
+}  // namespace la

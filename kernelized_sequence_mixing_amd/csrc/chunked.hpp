@@ -365,9 +365,11 @@ struct ZTiles {
 //   GLA       S <- Gamma (S + K~^T V)            Gamma = diag(e^{b_end}) from gam_off
 // Both operands come from [token][column] tiles by transpose reads.
 // S is f32x4[R / 16][E / (16 NW)], Z is f32x4[ZTiles<R, NW>::ZT].
-template <int R, int E, int GATE, int NW, bool SWZ, class SArr, class ZArr>
+// With ZW the z column uses per-token weights (fp32 [64] at zw_off) instead of
+// the constant-1 value: z <- Gamma z + K^^T w.
+template <int R, int E, int GATE, int NW, bool SWZ, bool ZW = false, class SArr, class ZArr>
 __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_off, int v_off, int gam_off,
-                                             float gscale, int lane, int w) {
+                                             float gscale, int lane, int w, int zw_off = 0) {
   constexpr int ZT = ZTiles<R, NW>::ZT, NEB = E / (16 * NW);
   const int g4 = lane >> 4;
   const int ebase = w * (E / NW);
@@ -421,7 +423,15 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) zt = mfma16(tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane), ones, zt);
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 zb = ones;
+        if constexpr (ZW) {
+          // k-slot jj of lane group g is token 32 ks + 8 g + jj (see tr_feat)
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) zb[jj] = (bf16)lds<float>(sm, zw_off + 4 * (32 * ks + 8 * g4 + jj));
+        }
+        zt = mfma16(tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane), zb, zt);
+      }
       if constexpr (GATE == GT_GLA) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];

@@ -49,6 +49,20 @@ struct FwdPlan {
   hipStream_t stream;
 };
 
+// The backward pass of the causal form: the forward plan (segments, state
+// workspace) plus the incoming gradient, the gradient outputs and the
+// workspace of the reverse passes.
+struct BwdPlan : FwdPlan {
+  const void* dO;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* ws_R;   // [BH][P][r][dv]
+  float* ws_rh;  // [BH][P][r]
+  void* ws_G;    // [BH][n][dv] bf16
+  float* ws_h;   // [BH][n]
+};
+
 struct DecodePlan {
   int B, H, dk, dv, r;
   int in_dtype, out_dtype;
@@ -80,6 +94,8 @@ struct FmapPlan {
 la_status launch_causal_elu1(const FwdPlan& p);
 la_status launch_causal_favor(const FwdPlan& p);
 la_status launch_segment_scan(const FwdPlan& p);
+la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z);
+la_status launch_backward(const BwdPlan& p);
 la_status launch_noncausal(const FwdPlan& p);
 la_status launch_decode(const DecodePlan& p);
 la_status launch_feature_map(const FmapPlan& p);

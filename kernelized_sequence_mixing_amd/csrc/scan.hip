@@ -4,6 +4,8 @@
 // phi(k_t) v_t^T of "Recurrent Reformulation", "Linear Attention Mechanisms",
 // dileepadev.github.io, applied one segment at a time). Slot s of the workspace
 // holds dS_s on entry and S_in(s) on exit; z is chained the same way.
+// Reverse mode (the backward pass's state over later tokens) chains from the
+// last segment: R_in(P-1) = 0, R_in(s) = dR_{s+1} + Gamma R_in(s+1).
 #include "chunked.hpp"
 
 namespace la {
@@ -13,7 +15,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S
                                                            const float* __restrict__ S0,
                                                            const float* __restrict__ z0,
                                                            const float* __restrict__ gamma, int H, int P,
-                                                           int R, int E, int seg_len, int gate) {
+                                                           int R, int E, int seg_len, int gate, int reverse) {
   const long long bh = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int RE = R * E;
@@ -23,7 +25,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S
   float* base = is_z ? z + bh * P * R + row : S + bh * P * RE + idx;
   const long long stride = is_z ? R : RE;
   float cur = 0.f;
-  if (S0 != nullptr) cur = is_z ? z0[bh * R + row] : S0[bh * RE + idx];
+  if (S0 != nullptr && !reverse) cur = is_z ? z0[bh * R + row] : S0[bh * RE + idx];
   float seg_decay = 1.f;
   if (gate == GT_DECAY) seg_decay = exp2f(float(seg_len) * log2f(gamma[bh % H]));
   // Batches of 8 segments: all loads of a batch are issued before the chain
@@ -34,14 +36,15 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int s = min(s0 + j, P - 1);
-      d[j] = base[s * stride];
-      G[j] = gate == GT_GLA ? logG[(bh * P + s) * R + row] : 0.f;
+      const int si = reverse ? P - 1 - s : s;
+      d[j] = base[si * stride];
+      G[j] = gate == GT_GLA ? logG[(bh * P + si) * R + row] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int s = s0 + j;
       if (s < P) {
-        base[s * stride] = cur;
+        base[(reverse ? P - 1 - s : s) * stride] = cur;
         const float g = gate == GT_GLA ? __expf(G[j]) : seg_decay;
         cur = g * cur + d[j];
       }
@@ -53,7 +56,15 @@ la_status launch_segment_scan(const FwdPlan& p) {
   const int items = p.r * p.dv + p.r;
   dim3 grid((items + 255) / 256, unsigned(p.B) * unsigned(p.H));
   hipLaunchKernelGGL(segment_scan_kernel, grid, dim3(256), 0, p.stream, p.ws_S, p.ws_z, p.ws_logG, p.S0, p.z0,
-                     p.gamma, p.H, p.P, p.r, p.dv, p.seg_len, p.gate);
+                     p.gamma, p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 0);
+  return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z) {
+  const int items = p.r * p.dv + p.r;
+  dim3 grid((items + 255) / 256, unsigned(p.B) * unsigned(p.H));
+  hipLaunchKernelGGL(segment_scan_kernel, grid, dim3(256), 0, p.stream, S, z, nullptr, nullptr, nullptr, p.gamma,
+                     p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 1);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 

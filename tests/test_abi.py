@@ -214,3 +214,62 @@ def test_feature_map_rejects():
     assert lib.la_feature_map_apply(ctypes.byref(f), 10, 64, N.LA_BF16, FAKE, FAKE + 64, None) == N.LA_ERR_ALIAS
     f2 = N.LaFeatureMap(N.LA_FMAP_ELU1, 48, None)
     assert lib.la_feature_map_apply(ctypes.byref(f2), 10, 48, N.LA_BF16, FAKE, FAKE + 0x100000, None) == N.LA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------ backward (validation, no launch)
+
+def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAKE + 13 * SP):
+    p = N.LaProblem(a["B"], a["H"], a["n"], a["d_k"], a["d_v"], a["in_dt"], a["out_dt"], a["eps"])
+    f = N.LaFeatureMap(a["fkind"], a["r"], a["omega"])
+    g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"])
+    return N.lib().la_backward(ctypes.byref(p), a["Q"], a["K"], a["V"], dO, ctypes.byref(f), a["causal"],
+                               ctypes.byref(g), a["S0"], a["z0"], dQ, dK, dV, a["ws"], a["ws_bytes"], None)
+
+
+BAD_BACKWARD = [
+    ("n=0", dict(n=0), {}, N.LA_ERR_INVALID_ARG),
+    ("noncausal", dict(causal=0), {}, N.LA_ERR_UNSUPPORTED),
+    ("favor", dict(fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
+    ("gla", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), {}, N.LA_ERR_UNSUPPORTED),
+    ("d 128x128", dict(d_k=128, r=128, d_v=128), {}, N.LA_ERR_UNSUPPORTED),
+    ("d_k 32", dict(d_k=32, r=32), {}, N.LA_ERR_UNSUPPORTED),
+    ("fp32", dict(in_dt=N.LA_F32, out_dt=N.LA_F32), {}, N.LA_ERR_UNSUPPORTED),
+    ("decay no gamma", dict(gkind=N.LA_GATE_DECAY), {}, N.LA_ERR_INVALID_ARG),
+    ("dO null", {}, dict(dO=None), N.LA_ERR_INVALID_ARG),
+    ("dK null", {}, dict(dK=None), N.LA_ERR_INVALID_ARG),
+    ("dQ misaligned", {}, dict(dQ=FAKE + 11 * SP + 8), N.LA_ERR_INVALID_ARG),
+    ("S0 without z0", dict(S0=FAKE + 7 * SP), {}, N.LA_ERR_INVALID_ARG),
+    ("dQ aliases K", {}, dict(dQ=FAKE + SP + 256), N.LA_ERR_ALIAS),
+    ("dV aliases dO", {}, dict(dV=FAKE + 10 * SP), N.LA_ERR_ALIAS),
+    ("dK aliases dQ", {}, dict(dK=FAKE + 11 * SP + 512), N.LA_ERR_ALIAS),
+    ("ws null", dict(ws=None), {}, N.LA_ERR_WORKSPACE),
+    ("ws small", dict(ws_bytes=1024), {}, N.LA_ERR_WORKSPACE),
+    ("ws misaligned", dict(ws=FAKE + 4 * SP + 16), {}, N.LA_ERR_WORKSPACE),
+]
+
+
+@needs_lib
+@no_gpu
+@pytest.mark.parametrize("name,over,ptrs,want", BAD_BACKWARD, ids=[b[0] for b in BAD_BACKWARD])
+def test_backward_rejects(name, over, ptrs, want):
+    assert _backward(_args(**over), **ptrs) == want
+
+
+@needs_lib
+def test_backward_workspace_size():
+    lib = N.lib()
+
+    def size(B, H, n, d, dv, gk=N.LA_GATE_NONE):
+        p = N.LaProblem(B, H, n, d, dv, N.LA_BF16, N.LA_BF16, 1e-6)
+        f = N.LaFeatureMap(N.LA_FMAP_ELU1, d, None)
+        g = N.LaGate(gk, 16.0, None, None)
+        out = ctypes.c_size_t(0)
+        assert lib.la_backward_workspace_size(ctypes.byref(p), ctypes.byref(f), 1, ctypes.byref(g),
+                                              ctypes.byref(out)) == N.LA_OK
+        return out.value
+    # headline shape: 8 segments; forward and reverse states, g (bf16) and h per token, 256-aligned regions
+    BH, P, n = 64, 8, 4096
+    states = BH * P * 64 * 64 * 4
+    zs = BH * P * 64 * 4
+    assert size(4, 16, n, 64, 64) == 2 * states + 2 * zs + BH * n * 64 * 2 + BH * n * 4
+    assert size(4, 16, n, 64, 64, N.LA_GATE_DECAY) == size(4, 16, n, 64, 64)

@@ -1,0 +1,169 @@
+"""GPU parity of the causal backward pass (la_backward) against the fp64
+gradient oracle (oracle/la_backward.py) on the same seeded inputs.
+
+Each gradient entry is a sum of terms (dphi(q_i) = sum_j dW_ij phi(k_j) with
+dW_ij = g_i . v_j + h_i, and so on), and its bf16-operand, fp32-accumulated
+evaluation has an error bounded by a small multiple of 2^-8 times the sum of
+the terms' magnitudes. The gradient itself can be far smaller than that sum:
+o_i does not change when phi(q_i) is scaled (up to eps), so dphi(q_i) is
+nearly orthogonal to phi(q_i) and g_i . v_j cancels against h_i. The gated
+metric is therefore the entrywise error over that magnitude sum (the
+forward-error bound of a sum). Each term carries up to five bf16 roundings
+(phi(q), phi(k), the rounded score or dW, g, and den inside g), at most
+5 * 2^-9 ~ 1e-2 of its magnitude; the tolerance is twice that. The error over
+the head's largest reference entry is printed beside it.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import la_backward as obwd
+from workloads import WORKLOADS, make_inputs, to_f64, incoming_gradient
+from _helpers import dev, gpu_gate, oracle_gate
+
+pytestmark = pytest.mark.gpu
+
+TOL_GRAD = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from kernelized_sequence_mixing_amd import _native
+    _native.lib()
+
+
+def head_err(got, ref):
+    """max over (b, h) of max|got - ref| / max|ref| within the head."""
+    g = to_f64(got)
+    num = np.max(np.abs(g - ref), axis=(2, 3))
+    den = np.max(np.abs(ref), axis=(2, 3)) + 1e-30
+    return float(np.max(num / den))
+
+
+def term_scales(inp, dO, S0=None, z0=None, head=None):
+    """Per entry of dQ, dK, dV: the sum of the magnitudes of the terms it sums
+    (with the feature map's derivative for dQ, dK), from the oracle's forward
+    quantities."""
+    Q, K, V = (to_f64(inp[k]) for k in ("Q", "K", "V"))
+    d = to_f64(dO)
+    gate = oracle_gate(inp)
+    S0 = None if S0 is None else to_f64(S0)
+    z0 = None if z0 is None else to_f64(z0)
+    if head is not None:
+        b, h = head
+        Q, K, V, d = (x[b:b + 1, h:h + 1] for x in (Q, K, V, d))
+        if gate is not None:
+            gate = ("decay", gate[1][h:h + 1])
+    pq, pk, D, c, W, num, den, o = obwd.forward_terms(Q, K, V, "elu1", None, True, gate, inp["eps"], S0, z0)
+    g = d / den[..., None]
+    hh = -np.sum(d * o, axis=-1) / den
+    T = (np.einsum("bhie,bhje->bhij", np.abs(g), np.abs(V)) + np.abs(hh)[..., None]) * D[None]
+    sq = np.einsum("bhij,bhjf->bhif", T, pk)
+    if S0 is not None:
+        sq = sq + c[None, :, :, None] * (np.einsum("bhre,bhie->bhir", np.abs(S0), np.abs(g)) +
+                                         np.abs(hh)[..., None] * z0[:, :, None, :])
+    sk = np.einsum("bhij,bhif->bhjf", T, pq)
+    sv = np.einsum("bhij,bhie->bhje", W, np.abs(g))
+    dphi = lambda x: np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+    return sq * dphi(Q), sk * dphi(K), sv
+
+
+def term_err(got, ref, scale):
+    return float(np.max(np.abs(to_f64(got) - ref) / (scale + 1e-30)))
+
+
+def check_grads(got, ref, scales, what):
+    errs = [term_err(g, r, sc) for g, r, sc in zip(got, ref, scales)]
+    heads = [head_err(g, r) for g, r in zip(got, ref)]
+    print(f"  {what}: term-relative dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}; "
+          f"of the head max dQ {heads[0]:.2e} dK {heads[1]:.2e} dV {heads[2]:.2e}", flush=True)
+    for nm, e in zip(("dQ", "dK", "dV"), errs):
+        assert e < TOL_GRAD, (what, nm, e)
+
+
+def run_backward(inp, dO, S0=None, z0=None):
+    import kernelized_sequence_mixing_amd as ksm
+    res = ksm.backward(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(dO), fmap="elu1", gate=gpu_gate(inp),
+                       eps=inp["eps"], S0=dev(S0), z0=dev(z0))
+    torch.cuda.synchronize()
+    return tuple(x.cpu() for x in res)
+
+
+def oracle_backward(inp, dO, S0=None, z0=None, head=None):
+    Q, K, V = (to_f64(inp[k]) for k in ("Q", "K", "V"))
+    d = to_f64(dO)
+    gate = oracle_gate(inp)
+    if head is not None:
+        b, h = head
+        Q, K, V, d = (x[b:b + 1, h:h + 1] for x in (Q, K, V, d))
+        if gate is not None:
+            gate = ("decay", gate[1][h:h + 1])
+    return obwd.backward(Q, K, V, d, "elu1", None, True, gate, inp["eps"],
+                         None if S0 is None else to_f64(S0), None if z0 is None else to_f64(z0))
+
+
+def _case(gate, d, dv, B, H, n, seed=3):
+    wl = WORKLOADS["causal_elu1"].resized(d_k=d, d_v=dv, r=d, gate=gate)
+    inp = make_inputs(wl, seed=seed, B=B, H=H, n=n)
+    dO = incoming_gradient((B, H, n, dv), seed + 100)
+    return wl, inp, dO
+
+
+CASES = [("none", 64, 64, 2, 4, 200), ("none", 64, 64, 2, 4, 777), ("decay", 64, 64, 2, 4, 777),
+         ("none", 64, 64, 4, 16, 1285), ("decay", 64, 64, 4, 16, 1285), ("none", 128, 64, 2, 4, 300),
+         ("decay", 64, 128, 2, 4, 300), ("none", 64, 64, 1, 1, 1), ("none", 64, 64, 2, 1, 63),
+         ("decay", 64, 64, 2, 1, 65)]
+
+
+@pytest.mark.parametrize("gate,d,dv,B,H,n", CASES)
+def test_backward_parity_small(gate, d, dv, B, H, n):
+    """Several segments with a ragged last chunk (n 777, 1285), one segment
+    (n 200), tiny n, each built shape and both gates."""
+    wl, inp, dO = _case(gate, d, dv, B, H, n)
+    got = run_backward(inp, dO)
+    check_grads(got, oracle_backward(inp, dO), term_scales(inp, dO), f"{gate} d{d}x{dv} B{B} H{H} n{n}")
+
+
+@pytest.mark.parametrize("gate", ["none", "decay"])
+def test_backward_with_carried_state(gate):
+    """The forward's carried-in state enters dQ (and g, h, hence every gradient)."""
+    wl, inp, dO = _case(gate, 64, 64, 4, 16, 700, seed=9)
+    rng = np.random.default_rng(77)
+    S0 = torch.from_numpy((rng.standard_normal((4, 16, 64, 64)) * 2.0).astype(np.float32))
+    z0 = torch.from_numpy((20.0 + 2.0 * np.abs(rng.standard_normal((4, 16, 64)))).astype(np.float32))
+    got = run_backward(inp, dO, S0, z0)
+    check_grads(got, oracle_backward(inp, dO, S0, z0), term_scales(inp, dO, S0, z0), f"carried state {gate}")
+
+
+def test_backward_headline_full_size():
+    """The benchmark's shape (B4 H16 n4096 d64, 8 segments), two sampled heads."""
+    wl = WORKLOADS["causal_elu1"]
+    inp = make_inputs(wl, seed=0)
+    dO = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1)
+    got = run_backward(inp, dO)
+    for x in got:
+        assert torch.isfinite(x.float()).all()
+    for head in [(0, 0), (wl.B - 1, wl.H - 1)]:
+        b, h = head
+        check_grads([g[b:b + 1, h:h + 1] for g in got], oracle_backward(inp, dO, head=head),
+                    term_scales(inp, dO, head=head), f"head {head}")
+
+
+def test_backward_deterministic():
+    wl, inp, dO = _case("decay", 64, 64, 4, 16, 1285, seed=4)
+    a = run_backward(inp, dO)
+    b = run_backward(inp, dO)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_prepared_backward_matches_backward():
+    import kernelized_sequence_mixing_amd as ksm
+    wl, inp, dO = _case("none", 64, 64, 2, 4, 500, seed=5)
+    ref = run_backward(inp, dO)
+    pb = ksm.PreparedBackward(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(dO), eps=inp["eps"])
+    got = pb()
+    torch.cuda.synchronize()
+    for x, y in zip(got, ref):
+        assert torch.equal(x.cpu(), y)

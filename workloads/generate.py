@@ -90,6 +90,13 @@ def make_inputs(wl, seed: int = 0, *, B=None, H=None, n=None, qk_scale=None,
     return out
 
 
+def incoming_gradient(shape, seed: int, dtype: str = "bf16", scale: float = 1.0) -> torch.Tensor:
+    """A seeded dL/d(out) for the backward pass: N(0,1) * scale, cast like the inputs."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal(tuple(shape), dtype=np.float32) * np.float32(scale)
+    return _cast(g, dtype)
+
+
 def _decode_inputs(wl: Workload, rng, B, H, qs, vs) -> dict:
     """A carried state standing in for a short prefill, plus one new token.
 
