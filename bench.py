@@ -11,8 +11,9 @@ find their inputs in the 256 MB last-level (MALL) cache. Timing uses HIP events
 on the stream the library launches on. Rank 0 prints one JSON line.
 
 The same line carries, under "extra", the other workloads (non-causal fp32,
-RetNet decay, GLA gate, FAVOR+, and the GLA decode step), and the fp64 CPU
-oracle timed on the host on a bounded sample of the headline workload.
+RetNet decay, GLA gate, FAVOR+, the GLA decode step, and the backward pass on
+the headline shape), and the fp64 CPU oracle timed on the host on a bounded
+sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -186,6 +187,49 @@ def bench_decode(wl, steps, warmup):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def backward_algorithmic_per_token(wl):
+    """(bytes, matrix-core flops) per head-token of the causal backward pass.
+
+    Bytes: read q, k, v, dO once, write dq, dk, dv once. Flops (chunk C, masked
+    upper triangle excluded): the scores, the numerator of o, dW, and the
+    intra-chunk parts of dq, dk, dv ((C+1)/2 * 2 r or 2 d_v each), plus six
+    r x d_v products per token (o's inter-chunk read, dq's S g, dk's R v, dv's
+    R phi(k), and the forward and reverse state updates).
+    """
+    nbytes = 2 * (2 * wl.d_k + 2 * wl.d_v) + 2 * (2 * wl.d_k + wl.d_v)
+    half = (CHUNK + 1) / 2
+    flops = half * 2 * wl.r * 3 + half * 2 * wl.d_v * 3 + 6 * 2 * wl.r * wl.d_v
+    return nbytes, flops
+
+
+def bench_backward(wl, steps, warmup):
+    """la_backward on workload wl (causal elu+1): one step is one full backward pass."""
+    import kernelized_sequence_mixing_amd as ksm
+    from workloads import incoming_gradient
+    inp = make_inputs(wl, seed=0)
+    inp["dO"] = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1)
+    nb_tok, fl_tok = backward_algorithmic_per_token(wl)
+    per_set = wl.head_tokens * nb_tok
+    sets = _device_sets(inp, ["Q", "K", "V", "dO", "gamma"], per_set)
+    gate_of = {"none": lambda s: None, "decay": lambda s: ("decay", s["gamma"])}[wl.gate]
+    grads = [(torch.empty_like(s["Q"]), torch.empty_like(s["K"]), torch.empty_like(s["V"])) for s in sets]
+    stream = torch.cuda.current_stream()
+    calls = [ksm.PreparedBackward(s["Q"], s["K"], s["V"], s["dO"], gate=gate_of(s), eps=wl.eps, grads=grads[i],
+                                  stream=stream) for i, s in enumerate(sets)]
+
+    def step(i):
+        calls[i]()
+
+    ms, med = time_steps(step, len(sets), steps, warmup, stream)
+    gbs = per_set / (ms * 1e-3) / 1e9
+    tfl = wl.head_tokens * fl_tok / (ms * 1e-3) / 1e12
+    return {"workload": wl.name + "_backward", "ms_per_step": round(ms, 5), "median_ms": round(med, 5),
+            "value": wl.head_tokens / (ms * 1e-3), "unit": "head-tokens/s", "input_sets_rotated": len(sets),
+            "hbm_alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_alg_TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4),
+            "alg_bytes_per_token": nb_tok, "alg_flops_per_token": fl_tok}
+
+
 def cpu_baseline(wl, min_seconds=10.0):
     """The fp64 oracle (recurrent form, numpy) on the host: whole passes over
     all heads of the headline workload, repeated until about `min_seconds` of
@@ -275,6 +319,7 @@ def main():
         for name in ("noncausal_elu1_f32", "retnet_decay", "gla_gate", "favor_causal"):
             extra.append(bench_forward(WORKLOADS[name], args.steps, args.warmup))
         extra.append(bench_decode(WORKLOADS["gla_decode"], args.steps, args.warmup))
+        extra.append(bench_backward(WORKLOADS["causal_elu1"], args.steps, args.warmup))
         line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
