@@ -514,6 +514,10 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     z_load<R, NW>(Rz, has_in ? b.rh_ws + slot * R : nullptr, lane, w);
   }
 
+  const int nslot = w < 2 ? 3 : 2;
+  int sqi[3], skj[3];
+  score_tiles(w, sqi, skj);
+
   using Raw = RawChunk<R, E, R, FM_ELU1, GT_NONE, true, NW>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
@@ -552,11 +556,12 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     if (ci > 0) load(ci - 1);
     lds_barrier();
 
-    // ---- W^T and dW^T tiles [key j][query i], i >= j: wave w owns key tile w
-    {
-      const int jt = w;
-      const int j = 16 * jt + c16;
-      for (int it = jt; it < 4; ++it) {
+    // ---- W^T and dW^T tiles [key j][query i], i >= j, dealt 3, 3, 2, 2 over the waves
+#pragma unroll
+    for (int sl = 0; sl < 3; ++sl) {
+      if (sl < nslot) {
+        const int it = sqi[sl], jt = skj[sl];
+        const int j = 16 * jt + c16;
         f32x4 aw = {0.f, 0.f, 0.f, 0.f}, ad = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KP; ++ks)
@@ -581,11 +586,12 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
         lds<bf16x4>(sm, LY::w_off + o) = pack4(vw[0], vw[1], vw[2], vw[3]);
         lds<bf16x4>(sm, LY::dw_off + o) = pack4(vd[0], vd[1], vd[2], vd[3]);
       }
-      if (jt & 1) {
-        const int o = AT::at(j, 2 * (jt - 1) + (g4 >> 1), 8 * (g4 & 1));
-        lds<bf16x4>(sm, LY::w_off + o) = bf16x4{};
-        lds<bf16x4>(sm, LY::dw_off + o) = bf16x4{};
-      }
+    }
+    // tiles below the diagonal read by the products over 32 queries: (key 1, query 0) and (3, 2)
+    if (w >= 2) {
+      const int o = AT::at(16 * (2 * w - 3) + c16, 2 * (2 * w - 4) + (g4 >> 1), 8 * (g4 & 1));
+      lds<bf16x4>(sm, LY::w_off + o) = bf16x4{};
+      lds<bf16x4>(sm, LY::dw_off + o) = bf16x4{};
     }
     lds_barrier();
 

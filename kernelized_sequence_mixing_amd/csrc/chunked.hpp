@@ -348,6 +348,21 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
   }
 }
 
+// The ten lower-triangle 16x16 score tiles (query tile qi, key tile kj <= qi)
+// dealt to the four waves as 3, 3, 2, 2 tiles, no wave holding two tiles of
+// the same query rows, and slot 0 of wave w on query tile w (whose features
+// phi(q) . z also reads):
+//   wave 0: (0,0) (3,0) (2,0)   wave 1: (1,0) (3,1) (2,1)
+//   wave 2: (2,2) (3,2)         wave 3: (3,3) (1,1)
+__device__ __forceinline__ void score_tiles(int w, int (&qi)[3], int (&kj)[3]) {
+  qi[0] = w;
+  kj[0] = w < 2 ? 0 : w;
+  qi[1] = w == 3 ? 1 : 3;
+  kj[1] = w == 3 ? 1 : w;
+  qi[2] = 2;  // waves 0 and 1 only
+  kj[2] = w;
+}
+
 // z is carried on the matrix cores as the state column of a constant-1 value:
 // z <- Gamma z + K^^T 1. Wave w owns the z tiles rt = w ZT .. w ZT + ZT - 1
 // (16 rows each); lane (g, c) holds z[16 rt + 4 g + i] in Z[rt - w ZT][i]
