@@ -14,8 +14,9 @@ of ``la_oracle`` (W_ij = phi(q_i).phi(k_j) D_ij, o_i = sum_j W_ij v_j /
 (sum_j W_ij + eps), plus the read-out of a carried-in state S0, z0) by the
 chain rule written out step by step below; nothing is blocked or reordered.
 
-Gates covered: none and the RetNet decay (gamma is a fixed per-head constant,
-so it has no gradient). The diagonal GLA gate is not covered here.
+Gates covered: none, the RetNet decay (gamma is a fixed per-head constant, so
+it has no gradient) and the diagonal GLA gate, whose raw input g also gets a
+gradient (``backward_gla``).
 Pinned by ``tests/test_oracle_backward_pins.py`` against central finite differences of
 the pinned forward oracle and against closed forms.
 """
@@ -25,7 +26,7 @@ import numpy as np
 
 from .la_oracle import feature_map
 
-__all__ = ["feature_map_vjp", "forward_terms", "backward"]
+__all__ = ["feature_map_vjp", "forward_terms", "backward", "backward_gla"]
 
 
 def _f64(a):
@@ -134,3 +135,64 @@ def backward(Q, K, V, dO, fmap="elu1", omega=None, causal=True, gate=None, eps=1
     dQ = feature_map_vjp(Q, dpq, fmap, omega)
     dK = feature_map_vjp(K, dpk, fmap, omega)
     return dQ, dK, dV
+
+
+def backward_gla(Q, K, V, dO, g, tau, fmap="elu1", omega=None, eps=1e-6, S0=None, z0=None):
+    """(dQ, dK, dV, dg) of L = sum_i dO_i . o_i for the causal form with the
+    diagonal GLA gate, all float64.
+
+    Forward ("Gating and Selective State Updates", dileepadev page): with
+    alpha_t = sigmoid(g_t)^(1/tau) per feature and B_t = sum_{u<=t} log alpha_u,
+    W_ij = sum_k phi(q_i)_k phi(k_j)_k D_ijk with D_ijk = exp(B_ik - B_jk) =
+    prod_{u=j+1}^{i} alpha_uk for j <= i, and the carried-in state enters step i
+    with the factor c_ik = exp(B_ik) on row k (the gate of every step up to i).
+    Chain rule, as in ``backward`` with the per-feature factors inside the sums:
+      dphi_q_ik = sum_j dW_ij phi_k_jk D_ijk + c_ik (S0 g_i + h_i z0)_k
+      dphi_k_jk = sum_i dW_ij phi_q_ik D_ijk
+      dB_tk     = sum_{i,j} dW_ij phi_q_ik phi_k_jk D_ijk ([t = i] - [t = j])
+                  + c_tk phi_q_tk (S0 g_t + h_t z0)_k
+                = dphi_q_tk phi_q_tk - dphi_k_tk phi_k_tk
+      d log alpha_uk = sum_{t >= u} dB_tk     (B_t sums the log-gates up to t)
+      dg_uk = d log alpha_uk * sigmoid(-g_uk) / tau   (log alpha = -softplus(-g) / tau)
+    """
+    V = _f64(V)
+    dO = _f64(dO)
+    g = _f64(g)
+    pq = feature_map(Q, fmap, omega)
+    pk = feature_map(K, fmap, omega)
+    B, H, n, r = pq.shape
+    with np.errstate(over="ignore"):
+        logalpha = -np.logaddexp(0.0, -g) / float(tau)            # log sigmoid(g) / tau
+    Bc = np.cumsum(logalpha, axis=2)                             # [B, H, n, r]
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    mask = (j <= i)
+    # D[b, h, i, j, k] = exp(B_ik - B_jk) on and below the diagonal
+    D = np.where(mask[None, None, :, :, None], np.exp(np.minimum(Bc[:, :, :, None, :] - Bc[:, :, None, :, :], 0.0)),
+                 0.0)
+    W = np.einsum("bhik,bhjk,bhijk->bhij", pq, pk, D)
+    num = np.einsum("bhij,bhje->bhie", W, V)
+    den = W.sum(axis=-1) + eps
+    c = np.exp(Bc)
+    if S0 is not None:
+        S0 = _f64(S0)
+        z0 = _f64(z0)
+        num = num + np.einsum("bhik,bhke->bhie", pq * c, S0)
+        den = den + np.einsum("bhik,bhk->bhi", pq * c, z0)
+    o = num / den[..., None]
+    gg = dO / den[..., None]
+    h = -np.sum(dO * o, axis=-1) / den
+    dW = (np.einsum("bhie,bhje->bhij", gg, V) + h[..., None]) * mask[None, None]
+    dV = np.einsum("bhij,bhie->bhje", W, gg)
+    dpq = np.einsum("bhij,bhjk,bhijk->bhik", dW, pk, D)
+    dpk = np.einsum("bhij,bhik,bhijk->bhjk", dW, pq, D)
+    if S0 is not None:
+        dpq = dpq + c * (np.einsum("bhke,bhie->bhik", S0, gg) + h[..., None] * z0[:, :, None, :])
+    dB = dpq * pq - dpk * pk
+    dlogalpha = np.flip(np.cumsum(np.flip(dB, axis=2), axis=2), axis=2)
+    with np.errstate(over="ignore"):
+        sig_neg = 1.0 / (1.0 + np.exp(g))                        # sigmoid(-g)
+    dg = dlogalpha * sig_neg / float(tau)
+    dQ = feature_map_vjp(Q, dpq, fmap, omega)
+    dK = feature_map_vjp(K, dpk, fmap, omega)
+    return dQ, dK, dV, dg

@@ -93,3 +93,54 @@ def test_output_invariant_to_query_feature_scale(causal, gate_kind):
     dQ, _, _ = bwd.backward(Q, K, V, dO, "elu1", None, causal, gate, 0.0)
     s = np.sum(dQ * (Q + 1.0), axis=-1)
     assert np.max(np.abs(s)) < 1e-12 * np.max(np.abs(dQ))
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_gla_gradients_match_finite_differences(with_state):
+    """dQ, dK, dV and the gradient of the raw gate input g of the GLA form,
+    against central differences of the recurrent oracle (which applies the gate
+    step by step and is pinned against the explicit weights)."""
+    B, H, n, d, e = 1, 2, 8, 4, 3
+    tau = 3.0
+    Q = RNG.standard_normal((B, H, n, d)) * 0.7
+    K = RNG.standard_normal((B, H, n, d)) * 0.7
+    V = RNG.standard_normal((B, H, n, e))
+    G = RNG.standard_normal((B, H, n, d))
+    dO = RNG.standard_normal((B, H, n, e))
+    S0 = z0 = None
+    if with_state:
+        S0 = np.abs(RNG.standard_normal((B, H, d, e)))
+        z0 = np.abs(RNG.standard_normal((B, H, d))) + 0.5
+    eps = 1e-3
+    dQ, dK, dV, dg = bwd.backward_gla(Q, K, V, dO, G, tau, "elu1", None, eps, S0, z0)
+
+    def loss(Q_, K_, V_, G_):
+        o, _, _ = orc.causal_recurrent(Q_, K_, V_, "elu1", None, ("gla", G_, tau), eps, S0=S0, z0=z0)
+        return float(np.sum(o * dO))
+    step = 1e-6
+    for idx, (X, Gr) in enumerate(((Q, dQ), (K, dK), (V, dV), (G, dg))):
+        U = RNG.standard_normal(X.shape)
+        args = [Q, K, V, G]
+        args[idx] = X + step * U
+        lp = loss(*args)
+        args[idx] = X - step * U
+        lm = loss(*args)
+        fd = (lp - lm) / (2 * step)
+        an = float(np.sum(Gr * U))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (idx, fd, an)
+
+
+def test_gla_unit_gates_reduce_to_ungated():
+    """Gates that are exactly 1 (g = +inf) leave dQ, dK, dV of the ungated form
+    and give dg = 0."""
+    B, H, n, d, e = 1, 1, 7, 4, 3
+    Q = RNG.standard_normal((B, H, n, d))
+    K = RNG.standard_normal((B, H, n, d))
+    V = RNG.standard_normal((B, H, n, e))
+    dO = RNG.standard_normal((B, H, n, e))
+    G = np.full((B, H, n, d), np.inf)
+    got = bwd.backward_gla(Q, K, V, dO, G, 16.0, "elu1", None, 1e-3)
+    want = bwd.backward(Q, K, V, dO, "elu1", None, True, None, 1e-3)
+    for a, b in zip(got[:3], want):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    assert np.all(got[3] == 0.0)
