@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 
 typedef enum la_status {
   LA_OK = 0,
@@ -159,23 +159,32 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  *   dphi(q_i) = sum_{j<=i} dW_ij G_ij phi(k_j) (+ the carried state's share),
  *   dphi(k_j) = sum_{i>=j} dW_ij G_ij phi(q_i),  dv_j = sum_{i>=j} w_ij g_i,
  * with G_ij = 1 or gamma_h^(i-j) and w_ij = phi(q_i).phi(k_j) G_ij, then the
- * feature map's derivative (elu+1: 1 for x > 0, exp(x) below).
+ * feature map's derivative (elu+1: 1 for x > 0, exp(x) below). With the GLA
+ * gate ("Gating and Selective State Updates", dileepadev page) the weights
+ * G_ij are per feature, prod_{u=j+1..i} alpha_u, and the gate's raw input g
+ * also gets its gradient: with B_t = sum_{u<=t} log alpha_u,
+ *   dB_t = dphi(q_t) * phi(q_t) - dphi(k_t) * phi(k_t)   (per feature),
+ *   dg_u = (sum_{t>=u} dB_t) * sigmoid(-g_u) / tau.
  *   Q, K, dQ, dK [B][H][n][d_k]; V, dO, dV [B][H][n][d_v]; all BF16 (in_dtype and
  *   out_dtype must be BF16). S0, z0: the optional carried-in state of the forward
- *   (both or neither; fp32). gamma is a constant: no gradient is returned for it,
- *   nor for S0, z0.
+ *   (both or neither; fp32). gamma and tau are constants: no gradient is returned
+ *   for them, nor for S0, z0.
+ *   dg: [B][H][n][r] BF16, the gradient of gate->g; required (non-NULL) with the
+ *   GLA gate and must be NULL otherwise (else LA_ERR_INVALID_ARG).
  *   workspace: device scratch of at least la_backward_workspace_size bytes,
- *   256-byte aligned (segment states of both directions, g and h per token).
- * Supported (else LA_ERR_UNSUPPORTED): causal == 1, ELU1, gate NONE or DECAY,
+ *   256-byte aligned (segment states of both directions, g and h per token;
+ *   GLA: also dB per token and feature and per-segment sums).
+ * Supported (else LA_ERR_UNSUPPORTED): causal == 1, ELU1, any gate,
  * (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
  * inputs, each other or the workspace (LA_ERR_ALIAS). Numerics as la_forward:
  * bf16 MFMA operands (phi, values, g, the scores and dW), fp32 accumulation,
- * states and denominators.
+ * states, denominators and the sums behind dg.
  */
 la_status la_backward(const la_problem* p, const void* Q, const void* K, const void* V,
                       const void* dO, const la_feature_map* fmap, int32_t causal,
                       const la_gate* gate, const float* S0, const float* z0, void* dQ,
-                      void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream);
+                      void* dK, void* dV, void* dg, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /*
  * One recurrent step for a batch of carried states, updated IN PLACE

@@ -189,7 +189,8 @@ class PreparedForward:
 
 
 def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream):
-    """Validate and marshal one la_backward call: (ctypes arguments, keep-alive objects, (dQ, dK, dV))."""
+    """Validate and marshal one la_backward call: (ctypes arguments, keep-alive objects, gradients), the
+    gradients being (dQ, dK, dV), plus dg with the GLA gate."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (dO, "dO")):
         _dev(t, nm)
     if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3] or dO.shape != V.shape:
@@ -207,10 +208,16 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
             _dev(t, nm)
             if tuple(t.shape) != shp or t.dtype != torch.float32:
                 raise ValueError(f"{nm} must be float32 {shp}")
+    gla = g.kind == N.LA_GATE_GLA
     if grads is None:
         grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
-    dQ, dK, dV = grads
-    for t, ref, nm in ((dQ, Q, "dQ"), (dK, K, "dK"), (dV, V, "dV")):
+        if gla:
+            grads = grads + (torch.empty_like(gate[1]),)
+    if len(grads) != (4 if gla else 3):
+        raise ValueError("grads must be (dQ, dK, dV)" + (" plus dg with the GLA gate" if gla else ""))
+    dQ, dK, dV = grads[:3]
+    dg = grads[3] if gla else None
+    for t, ref, nm in ((dQ, Q, "dQ"), (dK, K, "dK"), (dV, V, "dV")) + (((dg, gate[1], "dg"),) if gla else ()):
         _dev(t, nm)
         if t.shape != ref.shape or t.dtype != ref.dtype:
             raise ValueError(f"{nm} has the wrong shape or dtype")
@@ -221,17 +228,18 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     args = (ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), ctypes.byref(f), 1, ctypes.byref(g), _ptr(S0),
-            _ptr(z0), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace), need, _stream(Q, stream))
+            _ptr(z0), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dg), _ptr(workspace), need, _stream(Q, stream))
     keep = (p, f, g, Q, K, V, dO, gate, S0, z0, workspace)
-    return args, keep, (dQ, dK, dV)
+    return args, keep, tuple(grads)
 
 
 def backward(Q, K, V, dO, *, fmap="elu1", gate=None, eps=1e-6, S0=None, z0=None, grads=None, workspace=None,
              stream=None):
-    """(dQ, dK, dV) of the causal forward for an incoming gradient dO, through la_backward.
+    """(dQ, dK, dV) of the causal forward for an incoming gradient dO, through la_backward;
+    (dQ, dK, dV, dg) with the GLA gate, dg the gradient of its raw input g.
 
-    Q, K [B, H, n, d_k]; V, dO [B, H, n, d_v] (bf16); gate None | ("decay", gamma[H]);
-    S0, z0: the forward's carried-in state, if any."""
+    Q, K [B, H, n, d_k]; V, dO [B, H, n, d_v] (bf16); gate None | ("decay", gamma[H]) |
+    ("gla", g[B, H, n, d_k] bf16, tau); S0, z0: the forward's carried-in state, if any."""
     args, _keep, grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream)
     N.check(N.lib().la_backward(*args), "la_backward")
     return grads

@@ -161,7 +161,7 @@ la_status check_forward_shape(const la_problem* p, const la_feature_map* f, int 
   return LA_OK;
 }
 
-// The backward pass: causal elu+1, bf16 in and out, no gate or RetNet decay,
+// The backward pass: causal elu+1, bf16 in and out, any gate,
 // (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}.
 la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int causal, const la_gate* g) {
   la_status st = check_problem(p);
@@ -171,7 +171,7 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
   if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
   const int gk = gate_kind(g);
   if (!causal && gk != LA_GATE_NONE) return LA_ERR_INVALID_ARG;
-  if (!causal || f->kind != LA_FMAP_ELU1 || gk == LA_GATE_GLA) return LA_ERR_UNSUPPORTED;
+  if (!causal || f->kind != LA_FMAP_ELU1) return LA_ERR_UNSUPPORTED;
   if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   const int key = p->d_k * 1000 + p->d_v;
   if (key != 64064 && key != 64128 && key != 128064) return LA_ERR_UNSUPPORTED;
@@ -179,11 +179,13 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
 }
 
 struct BwdWsLayout {
-  size_t S_off, z_off, R_off, rh_off, G_off, h_off, bytes;
+  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, T_off, logG_off, bytes;
   int P, L;
 };
 
-// Forward segment states, reverse segment states, g (bf16) and h per token.
+// Forward segment states, reverse segment states, g (bf16) and h per token;
+// GLA adds the log-gate gradient per token and feature, its segment sums and
+// the segments' summed log-gates.
 BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, int gate) {
   BwdWsLayout w{};
   plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate, &w.P, &w.L);
@@ -195,7 +197,14 @@ BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, i
   w.rh_off = round_up(w.R_off + states, kAlign);
   w.G_off = round_up(w.rh_off + zs, kAlign);
   w.h_off = round_up(w.G_off + BH * n * dv * 2, kAlign);
-  w.bytes = round_up(w.h_off + BH * n * 4, kAlign);
+  w.dB_off = round_up(w.h_off + BH * n * 4, kAlign);
+  if (gate != LA_GATE_GLA) {
+    w.T_off = w.logG_off = w.bytes = w.dB_off;
+    return w;
+  }
+  w.T_off = round_up(w.dB_off + BH * n * r * 4, kAlign);
+  w.logG_off = round_up(w.T_off + BH * w.P * r * 4, kAlign);
+  w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
   return w;
 }
 
@@ -386,8 +395,8 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
 
 la_status la_backward(const la_problem* p, const void* Q, const void* K, const void* V, const void* dO,
                       const la_feature_map* fmap, int32_t causal, const la_gate* gate, const float* S0,
-                      const float* z0, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      const float* z0, void* dQ, void* dK, void* dV, void* dg, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   la_status st = check_backward_shape(p, fmap, causal, gate);
   if (st != LA_OK) return st;
   if ((st = check_gate(gate, true)) != LA_OK) return st;
@@ -395,23 +404,25 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   if (Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || dQ == nullptr || dK == nullptr ||
       dV == nullptr)
     return LA_ERR_INVALID_ARG;
+  if ((dg != nullptr) != (gk == LA_GATE_GLA)) return LA_ERR_INVALID_ARG;
   if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_INVALID_ARG;
   for (const void* ptr : {Q, K, V, dO, (const void*)S0, (const void*)z0, (const void*)dQ, (const void*)dK,
-                          (const void*)dV})
+                          (const void*)dV, (const void*)dg})
     if (ptr != nullptr && !aligned16(ptr)) return LA_ERR_INVALID_ARG;
   const size_t BH = (size_t)p->B * p->H, n = (size_t)p->n, r = (size_t)fmap->r;
-  const size_t qk = BH * n * p->d_k * 2, vv = BH * n * p->d_v * 2;
+  const size_t qk = BH * n * p->d_k * 2, vv = BH * n * p->d_v * 2, gg = BH * n * r * 2;
   const Range rq = range_of(Q, qk), rk = range_of(K, qk), rv = range_of(V, vv), rdo = range_of(dO, vv);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
+  const Range rgl = range_of(gk == LA_GATE_GLA ? gate->g : nullptr, gg);
   const Range rs0 = range_of(S0, BH * r * p->d_v * 4), rz0 = range_of(z0, BH * r * 4);
-  const Range rdq = range_of(dQ, qk), rdk = range_of(dK, qk), rdv = range_of(dV, vv);
+  const Range rdq = range_of(dQ, qk), rdk = range_of(dK, qk), rdv = range_of(dV, vv), rdg = range_of(dg, gg);
   const BwdWsLayout wl = bwd_workspace_layout(p, fmap, gk);
   const Range rws = range_of(workspace, wl.bytes);
-  for (Range o : {rdq, rdk, rdv, rws})
-    for (Range i : {rq, rk, rv, rdo, rgam, rs0, rz0})
+  for (Range o : {rdq, rdk, rdv, rdg, rws})
+    for (Range i : {rq, rk, rv, rdo, rgam, rgl, rs0, rz0})
       if (overlaps(o, i)) return LA_ERR_ALIAS;
   if (overlaps(rdq, rdk) || overlaps(rdq, rdv) || overlaps(rdk, rdv) || overlaps(rws, rdq) || overlaps(rws, rdk) ||
-      overlaps(rws, rdv))
+      overlaps(rws, rdv) || overlaps(rdg, rdq) || overlaps(rdg, rdk) || overlaps(rdg, rdv) || overlaps(rdg, rws))
     return LA_ERR_ALIAS;
   if (workspace == nullptr || workspace_bytes < wl.bytes) return LA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return LA_ERR_WORKSPACE;
@@ -433,6 +444,8 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.K = K;
   plan.V = V;
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
+  plan.g = gk == LA_GATE_GLA ? gate->g : nullptr;
+  plan.tau = gk == LA_GATE_GLA ? gate->tau : 1.f;
   plan.S0 = S0;
   plan.z0 = z0;
   plan.P = wl.P;
@@ -445,6 +458,12 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.ws_rh = reinterpret_cast<float*>(ws + wl.rh_off);
   plan.ws_G = ws + wl.G_off;
   plan.ws_h = reinterpret_cast<float*>(ws + wl.h_off);
+  if (gk == LA_GATE_GLA) {
+    plan.ws_dB = reinterpret_cast<float*>(ws + wl.dB_off);
+    plan.ws_T = reinterpret_cast<float*>(ws + wl.T_off);
+    plan.ws_logG = reinterpret_cast<float*>(ws + wl.logG_off);
+    plan.dg = dg;
+  }
   plan.dO = dO;
   plan.dQ = dQ;
   plan.dK = dK;

@@ -34,6 +34,14 @@ static la_status run_backward(const BwdPlan& p) {
   b.P = p.P;
   b.seg_len = p.seg_len;
   b.eps = p.eps;
+  if constexpr (GATE == GT_GLA) {
+    b.gl = static_cast<const bf16*>(p.g);
+    b.inv_tau = 1.f / p.tau;
+    b.dB = p.ws_dB;
+    b.logG = p.ws_logG;
+    b.T = p.ws_T;
+    b.dg = static_cast<bf16*>(p.dg);
+  }
   la_status st;
   // forward state entering each segment: the forward's segment pass and scan
   if (p.P > 1) {
@@ -49,6 +57,9 @@ static la_status run_backward(const BwdPlan& p) {
     a1.eps = p.eps;
     a1.S_out = p.ws_S;
     a1.z_out = p.ws_z;
+    a1.g = b.gl;
+    a1.inv_tau = b.inv_tau;
+    a1.logG_out = p.ws_logG;
     auto k1 = causal_segment_state<R, E, R, FM_ELU1, GATE>;
     constexpr int lds1 = SegLayout<R, E, GATE>::bytes;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
@@ -71,22 +82,42 @@ static la_status run_backward(const BwdPlan& p) {
       LA_OK)
     return st;
   if (p.P > 1) {
-    if ((st = launch_with_lds(bwd_rstate<R, E, GATE>, dim3(p.P - 1, BH), BwdRLayout<R, E, GATE>::bytes, p.stream,
-                              b)) != LA_OK)
+    if constexpr (GATE == GT_GLA)
+      st = launch_with_lds(bwd_rstate_gla<R, E>, dim3(p.P - 1, BH), BwdRGLayout<R, E>::bytes, p.stream, b);
+    else
+      st = launch_with_lds(bwd_rstate<R, E, GATE>, dim3(p.P - 1, BH), BwdRLayout<R, E, GATE>::bytes, p.stream, b);
+    if (st != LA_OK) return st;
+    if ((st = launch_segment_scan_reverse(p, p.ws_R, p.ws_rh, GATE == GT_GLA ? p.ws_logG : nullptr)) != LA_OK)
       return st;
-    if ((st = launch_segment_scan_reverse(p, p.ws_R, p.ws_rh)) != LA_OK) return st;
   }
-  return launch_with_lds(bwd_pass_b<R, E, GATE>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b);
+  if ((st = launch_with_lds(bwd_pass_b<R, E, GATE>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b)) !=
+      LA_OK)
+    return st;
+  if constexpr (GATE == GT_GLA) {
+    hipLaunchKernelGGL(bwd_dg_totals<R>, dim3(p.P, BH), dim3(256), 0, p.stream, b);
+    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    hipLaunchKernelGGL(bwd_dg<R>, dim3(p.P, BH), dim3(256), 0, p.stream, b);
+    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+  }
+  return LA_OK;
 }
 
-// Built shapes: elu+1 with (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}, no gate or RetNet decay.
+template <int R, int E>
+static la_status run_backward_gated(const BwdPlan& p) {
+  switch (p.gate) {
+    case LA_GATE_NONE: return run_backward<R, E, GT_NONE>(p);
+    case LA_GATE_DECAY: return run_backward<R, E, GT_DECAY>(p);
+    case LA_GATE_GLA: return run_backward<R, E, GT_GLA>(p);
+    default: return LA_ERR_UNSUPPORTED;
+  }
+}
+
+// Built shapes: elu+1 with (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}; no gate, RetNet decay or GLA.
 la_status launch_backward(const BwdPlan& p) {
-  const int key = p.r * 1000 + p.dv;
-  const bool decay = p.gate == LA_GATE_DECAY;
-  switch (key) {
-    case 64064: return decay ? run_backward<64, 64, GT_DECAY>(p) : run_backward<64, 64, GT_NONE>(p);
-    case 64128: return decay ? run_backward<64, 128, GT_DECAY>(p) : run_backward<64, 128, GT_NONE>(p);
-    case 128064: return decay ? run_backward<128, 64, GT_DECAY>(p) : run_backward<128, 64, GT_NONE>(p);
+  switch (p.r * 1000 + p.dv) {
+    case 64064: return run_backward_gated<64, 64>(p);
+    case 64128: return run_backward_gated<64, 128>(p);
+    case 128064: return run_backward_gated<128, 64>(p);
     default: return LA_ERR_UNSUPPORTED;
   }
 }

@@ -1,5 +1,5 @@
-// Backward pass of the chunkwise causal kernel (elu+1 features; no gate or
-// the RetNet decay), for training with the parallel form ("Recurrent
+// Backward pass of the chunkwise causal kernel (elu+1 features; no gate, the
+// RetNet decay or the diagonal GLA gate), for training with the parallel form ("Recurrent
 // Reformulation", "Linear Attention Mechanisms" (dileepadev.github.io): the
 // layer is trained in parallel and served as an RNN).
 //
@@ -24,6 +24,14 @@
 //   scan (reverse)                -> R entering each segment from its end
 //   bwd_pass_b   chunks back to front: W, dW; dv = W^T g + Phi_k R'^T-part;
 //                dk = (Phi_q^T dW + R [v; 1])^T phi'(k); then R <- gamma^L R + ...
+// With the diagonal GLA gate ("Gating and Selective State Updates",
+// dileepadev page) the chunk tiles hold Q~ = e^{b} phi(q), K~ = e^{-b} phi(k)
+// as in the forward (b the chunk's inclusive summed log-gate per feature), the
+// same passes give dQ~ and dK~, and the gate's gradient follows from
+// dB = dQ~ . Q~ - dK~ . K~ (the gradient of the cumulative log-gate; the
+// carried-in state, weighted by e^{B}, enters through dQ~) by a suffix sum
+// over the sequence (bwd_dg_totals, bwd_dg). The reverse state of a segment
+// then runs in natural row order (bwd_rstate_gla).
 // All LDS tiles use the per-row chunk permutation of FeatTile.
 #pragma once
 
@@ -47,8 +55,14 @@ struct BwdArgs {
   bf16* dQ;
   bf16* dK;
   bf16* dV;
+  // GLA gate (per feature: alpha = sigmoid(g)^(1/tau))
+  const bf16* gl;  // [B H n R] raw gate input
+  float* dB;       // [B H n R] dQ~ . Q~ (pass A), then that minus dK~ . K~ (pass B)
+  float* logG;     // [B H P R] summed log-gate of each segment (bwd_rstate_gla)
+  float* T;        // [B H P R] segment sums of dB
+  bf16* dg;        // [B H n R]
   int H, n, P, seg_len;
-  float eps;
+  float eps, inv_tau;
 };
 
 // One chunk of an E-wide bf16 array in the row-major layout of RawChunk with
@@ -119,7 +133,8 @@ struct BwdALayout {
   static constexpr int v_off = k_off + FTB;            // v
   static constexpr int g_off = v_off + VTB;            // dO, then g = dO / den
   static constexpr int kh_off = g_off + VTB;           // RetNet: gamma^(L-1-t) phi(k)
-  static constexpr int a_off = kh_off + (GATE == GT_DECAY ? FTB : 0);  // scores A, then dW
+  static constexpr int qd_off = kh_off + (GATE == GT_DECAY ? FTB : 0);  // GLA: e^{b} phi'(q)
+  static constexpr int a_off = qd_off + (GATE == GT_GLA ? FTB : 0);     // scores A, then dW
   static constexpr int sb_off = a_off + ATB;           // bf16 [R][E] image of S entering the chunk
   static constexpr int z_off = sb_off + R * 2 * E;     // [R] z entering the chunk
   static constexpr int rs_off = z_off + R * 4;         // [64] score row sums
@@ -168,6 +183,8 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   ca.Q = b.Q;
   ca.K = b.K;
   ca.V = b.V;
+  ca.g = b.gl;
+  ca.inv_tau = b.inv_tau;
 
   using Raw = RawChunk<R, E, R, FM_ELU1, GATE, true, NW>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
@@ -200,8 +217,8 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
     // ---- prelude: features, values, dO, and the bf16 image of S
-    chunk_prelude<R, E, R, FM_ELU1, GATE, true, NW, true>(raw, ca, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
-                                                          LY::v_off, LY::gam_off, 0, lane, w);
+    chunk_prelude<R, E, R, FM_ELU1, GATE, true, NW, true, GATE == GT_GLA ? kPreQD : 0>(
+        raw, ca, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off, LY::v_off, LY::gam_off, 0, lane, w, LY::qd_off);
     rdo.store(sm, LY::g_off, L, lane, w);
     state_image<R, E>(S, sm, LY::sb_off, lane, w);
     raw.load(ca, tok0, t0 + kChunk, t_end, lane, w);
@@ -315,7 +332,10 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     }
     lds_barrier();
 
-    // ---- dphi(q)^T = Phi_k^T dW^T + gamma^(t+1) (S G^T + z h^T); dq = dphi(q) phi'(q)
+    // ---- dphi(q)^T = Phi_k^T dW^T + gamma^(t+1) (S G^T + z h^T); dq = dphi(q) phi'(q).
+    // GLA: the tiles hold Q~ = e^{b} phi(q) and K~ = e^{-b} phi(k), so this is
+    // dQ~ (with the state terms unweighted); dq = dQ~ e^{b} phi'(q), and
+    // dQ~ . Q~ goes to dB (the log-gates' gradient, completed by pass B).
 #pragma unroll
     for (int u = 0; u < FPW; ++u) {
       const int ft = w * FPW + u;
@@ -336,13 +356,24 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
         float sc = 1.f;
         if constexpr (GATE == GT_DECAY) sc = exp2f(float(i + 1) * lg2gam);
         const bf16x4 ph = lds<bf16x4>(sm, LY::q_off + FT::at(i, f0 / 8, 2 * (f0 % 8)));
+        bf16x4 qd = ph;
+        if constexpr (GATE == GT_GLA) qd = lds<bf16x4>(sm, LY::qd_off + FT::at(i, f0 / 8, 2 * (f0 % 8)));
         float dq[4];
+        f32x4 db;
 #pragma unroll
         for (int u2 = 0; u2 < 4; ++u2) {
           const float dphi = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::z_off + 4 * (f0 + u2)) * hi);
-          dq[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
+          if constexpr (GATE == GT_GLA) {
+            dq[u2] = dphi * to_f32(qd[u2]);
+            db[u2] = dphi * to_f32(ph[u2]);
+          } else {
+            dq[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
+          }
         }
-        if (i < L) *reinterpret_cast<bf16x4*>(b.dQ + (tok0 + t0 + i) * R + f0) = pack4(dq[0], dq[1], dq[2], dq[3]);
+        if (i < L) {
+          *reinterpret_cast<bf16x4*>(b.dQ + (tok0 + t0 + i) * R + f0) = pack4(dq[0], dq[1], dq[2], dq[3]);
+          if constexpr (GATE == GT_GLA) *reinterpret_cast<f32x4*>(b.dB + (tok0 + t0 + i) * R + f0) = db;
+        }
       }
     }
 
@@ -464,12 +495,13 @@ struct BwdBLayout {
   static constexpr int v_off = k_off + FTB;            // v
   static constexpr int g_off = v_off + VTB;            // g
   static constexpr int qw_off = g_off + VTB;           // RetNet: gamma^t phi(q)
-  static constexpr int w_off = qw_off + (GATE == GT_DECAY ? FTB : 0);  // W^T [key][query]
+  static constexpr int kd_off = qw_off + (GATE == GT_DECAY ? FTB : 0);  // GLA: e^{-b} phi'(k)
+  static constexpr int w_off = kd_off + (GATE == GT_GLA ? FTB : 0);     // W^T [key][query]
   static constexpr int dw_off = w_off + ATB;           // dW^T [key][query]
   static constexpr int rb_off = dw_off + ATB;          // bf16 [R][E] image of R entering the chunk
   static constexpr int rh_off = rb_off + R * 2 * E;    // [R] r_h entering the chunk
   static constexpr int hw_off = rh_off + R * 4;        // [64] h
-  static constexpr int gam_off = hw_off + kChunk * 4;
+  static constexpr int gam_off = hw_off + kChunk * 4;  // GLA: e^{chunk's summed log-gate}
   static constexpr int bytes = gam_off + R * 4;
 };
 
@@ -497,6 +529,11 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   ca.Q = b.Q;
   ca.K = b.K;
   ca.V = b.V;
+  ca.g = b.gl;
+  ca.inv_tau = b.inv_tau;
+  // the chunk's tiles: plain features (RetNet weights are applied per product)
+  // or, with the GLA gate, Q~ and K~ as in the forward
+  constexpr int PG = GATE == GT_GLA ? GT_GLA : GT_NONE;
 
   // ---- reverse state entering the segment from its end
   f32x4 Rs[R / 16][NEB];
@@ -518,7 +555,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   int sqi[3], skj[3];
   score_tiles(w, sqi, skj);
 
-  using Raw = RawChunk<R, E, R, FM_ELU1, GT_NONE, true, NW>;
+  using Raw = RawChunk<R, E, R, FM_ELU1, PG, true, NW>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
   RowsE<E> rg;
@@ -534,8 +571,8 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
     // ---- prelude
-    chunk_prelude<R, E, R, FM_ELU1, GT_NONE, true, NW, true>(raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0, LY::v_off,
-                                                             LY::gam_off, 0, lane, w);
+    chunk_prelude<R, E, R, FM_ELU1, PG, true, NW, true, GATE == GT_GLA ? kPreKD : 0>(
+        raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0, LY::v_off, LY::gam_off, 0, lane, w, 0, LY::kd_off);
     if constexpr (GATE == GT_DECAY) {
       // gamma^t phi(q) for the reverse-state update
       const int t = 16 * w + lane / 4;
@@ -595,10 +632,26 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     }
     lds_barrier();
 
-    // ---- dv^T = G^T W (intra) + gamma^(L-t) R'^T phi(k)^T (inter): the wave's value columns
+    // ---- dv^T = G^T W (intra) + gamma^(L-t) R'^T phi(k)^T (inter): the wave's value columns.
+    // GLA: a key's share of the state reaches the chunk's end scaled by
+    // Gamma = e^{chunk's summed log-gate} per feature, so the inter term is
+    // (Gamma R)^T K~^T.
     {
       bf16x8 Rop[KP][NEB];
-      state_operand<R, E>(Rs, Rop);
+      if constexpr (GATE == GT_GLA) {
+        f32x4 Rg[R / 16][NEB];
+#pragma unroll
+        for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gm = lds<float>(sm, LY::gam_off + 4 * (16 * rt + 4 * g4 + i));
+#pragma unroll
+            for (int eb = 0; eb < NEB; ++eb) Rg[rt][eb][i] = Rs[rt][eb][i] * gm;
+          }
+        state_operand<R, E>(Rg, Rop);
+      } else {
+        state_operand<R, E>(Rs, Rop);
+      }
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
         const int j = 16 * jt + c16;
@@ -625,7 +678,9 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
       }
     }
 
-    // ---- dphi(k)^T = Phi_q^T dW (intra) + gamma^(L-t) (R v + r_h) (inter); dk = dphi(k) phi'(k)
+    // ---- dphi(k)^T = Phi_q^T dW (intra) + gamma^(L-t) (R v + r_h) (inter); dk = dphi(k) phi'(k).
+    // GLA: dK~ = Q~^T dW + Gamma (R v + r_h); dk = dK~ e^{-b} phi'(k), and dB
+    // becomes dQ~ . Q~ - dK~ . K~, the gradient of the cumulative log-gate.
 #pragma unroll
     for (int u = 0; u < FPW; ++u) {
       const int ft = w * FPW + u;
@@ -645,21 +700,212 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
         float sc = 1.f;
         if constexpr (GATE == GT_DECAY) sc = exp2f(float(L - j) * lg2gam);
         const bf16x4 ph = lds<bf16x4>(sm, LY::k_off + FT::at(j, f0 / 8, 2 * (f0 % 8)));
-        float dk[4];
+        bf16x4 kd = ph;
+        if constexpr (GATE == GT_GLA) kd = lds<bf16x4>(sm, LY::kd_off + FT::at(j, f0 / 8, 2 * (f0 % 8)));
+        float dk[4], bk[4];
 #pragma unroll
         for (int u2 = 0; u2 < 4; ++u2) {
+          if constexpr (GATE == GT_GLA) sc = lds<float>(sm, LY::gam_off + 4 * (f0 + u2));
           const float dphi = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::rh_off + 4 * (f0 + u2)));
-          dk[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
+          if constexpr (GATE == GT_GLA) {
+            dk[u2] = dphi * to_f32(kd[u2]);
+            bk[u2] = dphi * to_f32(ph[u2]);
+          } else {
+            dk[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
+          }
         }
-        if (j < L) *reinterpret_cast<bf16x4*>(b.dK + (tok0 + t0 + j) * R + f0) = pack4(dk[0], dk[1], dk[2], dk[3]);
+        if (j < L) {
+          *reinterpret_cast<bf16x4*>(b.dK + (tok0 + t0 + j) * R + f0) = pack4(dk[0], dk[1], dk[2], dk[3]);
+          if constexpr (GATE == GT_GLA) {
+            f32x4* pb = reinterpret_cast<f32x4*>(b.dB + (tok0 + t0 + j) * R + f0);
+            f32x4 db = *pb;
+#pragma unroll
+            for (int u2 = 0; u2 < 4; ++u2) db[u2] -= bk[u2];
+            *pb = db;
+          }
+        }
       }
     }
 
     // ---- R <- gamma^L R + (gamma^t phi(q))^T [g, h]: the state entering the previous chunk
-    const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE, NW, true, true>(Rs, Rz, sm, GATE == GT_DECAY ? LY::qw_off : LY::q_off, LY::g_off,
-                                             LY::gam_off, gsc, lane, w, LY::hw_off);
+    // (GLA: R <- Gamma R + Q~^T [g, h])
+    if constexpr (GATE == GT_GLA) {
+      state_update<R, E, GT_GLA, NW, true, true, true>(Rs, Rz, sm, LY::q_off, LY::g_off, LY::gam_off, 1.f, lane, w,
+                                                       LY::hw_off);
+    } else {
+      const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+      state_update<R, E, GATE, NW, true, true>(Rs, Rz, sm, GATE == GT_DECAY ? LY::qw_off : LY::q_off, LY::g_off,
+                                               LY::gam_off, gsc, lane, w, LY::hw_off);
+    }
     lds_barrier();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GLA: each segment's own reverse state (segments 1 .. P-1). With the
+// per-feature gate the reverse state entering chunk c from its end obeys
+// R_c = Gamma_c R_{c+1} + Q~_c^T [g, h] (Q~ = e^{b} phi(q), b the chunk's
+// inclusive summed log-gate), so the segment's share starts from zero at its
+// end and runs its chunks back to front in natural row order. The segment's
+// summed log-gate goes to logG for the reverse scan.
+// ---------------------------------------------------------------------------
+template <int R, int E>
+struct BwdRGLayout {
+  static constexpr int q_off = 0;                           // Q~
+  static constexpr int k_off = q_off + FeatTile<R>::BYTES;  // (written by the shared prelude, unused)
+  static constexpr int v_off = k_off + FeatTile<R>::BYTES;  // g
+  static constexpr int hw_off = v_off + FeatTile<E>::BYTES;  // [64] h
+  static constexpr int gam_off = hw_off + kChunk * 4;        // [R] e^{chunk's summed log-gate}
+  static constexpr int logg_off = gam_off + R * 4;           // [R] segment's summed log-gate
+  static constexpr int bytes = logg_off + R * 4;
+};
+
+template <int R, int E>
+__global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
+  extern __shared__ __attribute__((aligned(16))) char sm[];
+  using LY = BwdRGLayout<R, E>;
+  constexpr int NW = 4, NEB = E / 64, FR = R / NW;
+  const int lane = lane_id(), w = wave_id<NW>();
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int s = blockIdx.x + 1;
+  const long long bh = blockIdx.y;
+  const int t_begin = s * b.seg_len;
+  const int t_end = min(b.n, t_begin + b.seg_len);
+  const long long tok0 = bh * b.n;
+  const int ebase = w * (E / NW);
+  CausalArgs ca{};
+  ca.Q = b.Q;
+  ca.K = b.Q;  // the prelude's key slot is not used here
+  ca.V = b.G;
+  ca.g = b.gl;
+  ca.inv_tau = b.inv_tau;
+
+  f32x4 Rs[R / 16][NEB];
+#pragma unroll
+  for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) Rs[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 Rz[ZTiles<R, NW>::ZT];
+  z_load<R, NW>(Rz, nullptr, lane, w);
+  // the lane that accumulates feature w FR + lane in the prelude clears it
+  if (lane < FR) lds<float>(sm, LY::logg_off + 4 * (w * FR + lane)) = 0.f;
+
+  using Raw = RawChunk<R, E, R, FM_ELU1, GT_GLA, true, NW>;
+  const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+  Raw raw;
+  float hv = 0.f;
+  auto load = [&](int ci) {
+    const int t0 = t_begin + ci * kChunk;
+    raw.load(ca, tok0, t0, t_end, lane, w);
+    hv = b.h[tok0 + min(t0 + lane, t_end - 1)];
+  };
+  load(nch - 1);
+  for (int ci = nch - 1; ci >= 0; --ci) {
+    const int t0 = t_begin + ci * kChunk;
+    const int L = min(kChunk, t_end - t0);
+    chunk_prelude<R, E, R, FM_ELU1, GT_GLA, true, NW, true, kPreLogG>(raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0,
+                                                                      LY::v_off, LY::gam_off, LY::logg_off, lane, w);
+    if (w == 0) lds<float>(sm, LY::hw_off + 4 * lane) = lane < L ? hv : 0.f;
+    if (ci > 0) load(ci - 1);
+    lds_barrier();
+    state_update<R, E, GT_GLA, NW, true, true, true>(Rs, Rz, sm, LY::q_off, LY::v_off, LY::gam_off, 1.f, lane, w,
+                                                     LY::hw_off);
+    lds_barrier();
+  }
+  const long long slot = bh * b.P + s;
+  float* Ro = b.R_ws + slot * R * E;
+#pragma unroll
+  for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ro[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = Rs[rt][eb][i];
+  z_store<R, NW>(Rz, b.rh_ws + slot * R, lane, w);
+  if (lane < FR) b.logG[slot * R + w * FR + lane] = lds<float>(sm, LY::logg_off + 4 * (w * FR + lane));
+}
+
+// ---------------------------------------------------------------------------
+// GLA: the raw gate's gradient. B_t = sum_{u<=t} log alpha_u over the whole
+// sequence, so d log alpha_u = sum_{t>=u} dB_t, and
+// log alpha = -softplus(-g) / tau gives dg = d log alpha * sigmoid(-g) / tau.
+// Two launches over (segment, head) workgroups of 256 threads, thread
+// (phase p, feature f) with 256 / R phases: the segments' sums of dB, then each
+// segment's suffix sums from the later segments' sums (added last to first)
+// and its own tokens. Every sum runs in a fixed order.
+// ---------------------------------------------------------------------------
+template <int R>
+__global__ __launch_bounds__(256) void bwd_dg_totals(BwdArgs b) {
+  constexpr int NP = 256 / R, BATCH = 8;
+  __shared__ float part[256];
+  const int f = threadIdx.x % R, ph = threadIdx.x / R;
+  const int s = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int t_begin = s * b.seg_len;
+  const int t_end = min(b.n, t_begin + b.seg_len);
+  const float* src = b.dB + bh * b.n * R + f;
+  float acc = 0.f;
+  for (int t = t_begin + ph; t < t_end; t += BATCH * NP) {
+    float x[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int tt = t + j * NP;
+      x[j] = tt < t_end ? src[(long long)tt * R] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) acc += x[j];
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  if (ph == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) tot += part[p * R + f];
+    b.T[(bh * b.P + s) * R + f] = tot;
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void bwd_dg(BwdArgs b) {
+  constexpr int NP = 256 / R, BATCH = 8;
+  __shared__ float part[256];
+  const int f = threadIdx.x % R, ph = threadIdx.x / R;
+  const int s = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int t_begin = s * b.seg_len;
+  const int t_end = min(b.n, t_begin + b.seg_len);
+  const long long base = bh * b.n * R + f;
+  // the segment as NP runs of consecutive tokens, run p = [r0, r1)
+  const int run = (t_end - t_begin + NP - 1) / NP;
+  const int r0 = t_begin + ph * run, r1 = min(t_end, r0 + run);
+  float rsum = 0.f;
+  for (int t = r0; t < r1; t += BATCH) {
+    float x[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) x[j] = t + j < r1 ? b.dB[base + (long long)(t + j) * R] : 0.f;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) rsum += x[j];
+  }
+  part[threadIdx.x] = rsum;
+  float carry = 0.f;
+  for (int s2 = b.P - 1; s2 > s; --s2) carry += b.T[(bh * b.P + s2) * R + f];
+  __syncthreads();
+  for (int p = NP - 1; p > ph; --p) carry += part[p * R + f];
+  for (int t = r1 - 1; t >= r0; t -= BATCH) {
+    float x[BATCH], gv[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const bool ok = t - j >= r0;
+      x[j] = ok ? b.dB[base + (long long)(t - j) * R] : 0.f;
+      gv[j] = ok ? to_f32(b.gl[base + (long long)(t - j) * R]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      if (t - j >= r0) {
+        carry += x[j];
+        const float sig_neg = 1.f / (1.f + __expf(gv[j]));
+        b.dg[base + (long long)(t - j) * R] = (bf16)(carry * sig_neg * b.inv_tau);
+      }
+    }
   }
 }
 

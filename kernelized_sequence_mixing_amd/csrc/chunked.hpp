@@ -254,11 +254,17 @@ struct RawChunk {
 //   K^, v, gam, logg).
 // L = valid tokens in the chunk. Rows t >= L get phi(k) = 0 and v = 0, and a
 // zero log-gate, so they add nothing to the state.
-template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SWZ>
+// EXTRA (GLA, backward pass), a mask of: kPreQD also writes the tile
+// qd = e^{b} phi'(q), kPreKD the tile kd = e^{-b} phi'(k) (phi'(x) =
+// min(phi(x), 1) for elu+1), the factors that turn gradients with respect to
+// Q~ and K~ into gradients of q and k; kPreLogG adds the chunk's summed
+// log-gates to logg also when WITH_Q.
+constexpr int kPreQD = 1, kPreKD = 2, kPreLogG = 4;
+template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SWZ, int EXTRA = 0>
 __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>& raw,
                                               const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
                                               int k_off, int kh_off, int v_off, int gam_off, int logg_off,
-                                              int lane, int w) {
+                                              int lane, int w, int qd_off = 0, int kd_off = 0) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
   constexpr int LPT = Raw::LPT;
   using FT = FeatTile<R, SWZ>;
@@ -309,7 +315,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
 #pragma unroll
     for (int j = 0; j < Raw::FR / 8; ++j) {
       const int f0 = w * Raw::FR + 8 * j;
-      float vq[8], vk[8];
+      float vq[8], vk[8], dq[8], dk[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         float pq = WITH_Q ? elu1(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
@@ -319,8 +325,11 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
           float b = wave_inclusive_scan(la);
           // the chunk total is uniform across the wave: a scalar read of lane 63
           const float bend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
-          pq *= __expf(b);
-          pk *= __expf(-b);  // K^ = e^{b_end} K~: applied to the state row after the update
+          const float eb = __expf(b), emb = __expf(-b);
+          if constexpr ((EXTRA & kPreQD) != 0) dq[u] = eb * fminf(pq, 1.f);
+          if constexpr ((EXTRA & kPreKD) != 0) dk[u] = emb * fminf(pk, 1.f);
+          pq *= eb;
+          pk *= emb;  // K^ = e^{b_end} K~: applied to the state row after the update
           my_bend = lane == 8 * j + u ? bend : my_bend;
         }
         vq[u] = pq;
@@ -331,11 +340,15 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         lds<bf16x8>(sm, q_off + fo) = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
       lds<bf16x8>(sm, k_off + fo) =
           keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
+      if constexpr (GATE == GT_GLA && (EXTRA & kPreQD) != 0)
+        lds<bf16x8>(sm, qd_off + fo) = cat8(pack4(dq[0], dq[1], dq[2], dq[3]), pack4(dq[4], dq[5], dq[6], dq[7]));
+      if constexpr (GATE == GT_GLA && (EXTRA & kPreKD) != 0)
+        lds<bf16x8>(sm, kd_off + fo) = cat8(pack4(dk[0], dk[1], dk[2], dk[3]), pack4(dk[4], dk[5], dk[6], dk[7]));
     }
     if constexpr (GATE == GT_GLA) {
       if (lane < Raw::FR) {
         lds<float>(sm, gam_off + 4 * (w * Raw::FR + lane)) = __expf(my_bend);
-        if constexpr (!WITH_Q) lds<float>(sm, logg_off + 4 * (w * Raw::FR + lane)) += my_bend;
+        if constexpr (!WITH_Q || (EXTRA & kPreLogG) != 0) lds<float>(sm, logg_off + 4 * (w * Raw::FR + lane)) += my_bend;
       }
     }
   }
@@ -381,8 +394,10 @@ struct ZTiles {
 // Both operands come from [token][column] tiles by transpose reads.
 // S is f32x4[R / 16][E / (16 NW)], Z is f32x4[ZTiles<R, NW>::ZT].
 // With ZW the z column uses per-token weights (fp32 [64] at zw_off) instead of
-// the constant-1 value: z <- Gamma z + K^^T w.
-template <int R, int E, int GATE, int NW, bool SWZ, bool ZW = false, class SArr, class ZArr>
+// the constant-1 value: z <- Gamma z + K^^T w. With PRE the GLA gate scales
+// the old state only (S <- Gamma S + K~^T V), as the backward pass's reverse
+// state needs.
+template <int R, int E, int GATE, int NW, bool SWZ, bool ZW = false, bool PRE = false, class SArr, class ZArr>
 __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_off, int v_off, int gam_off,
                                              float gscale, int lane, int w, int zw_off = 0) {
   constexpr int ZT = ZTiles<R, NW>::ZT, NEB = E / (16 * NW);
@@ -409,13 +424,13 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
       f32x4 st = S[rt][eb];
-      if constexpr (GATE == GT_DECAY) {
+      if constexpr (GATE == GT_DECAY || (GATE == GT_GLA && PRE)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[i] *= gr[i];
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vb[eb][ks], st);
-      if constexpr (GATE == GT_GLA) {
+      if constexpr (GATE == GT_GLA && !PRE) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[i] *= gr[i];
       }
@@ -433,7 +448,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
 #pragma unroll
         for (int i = 0; i < 4; ++i) gr[i] = lds<float>(sm, gam_off + 4 * (16 * rt + 4 * g4 + i));
       }
-      if constexpr (GATE == GT_DECAY) {
+      if constexpr (GATE == GT_DECAY || (GATE == GT_GLA && PRE)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
@@ -447,7 +462,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
         }
         zt = mfma16(tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane), zb, zt);
       }
-      if constexpr (GATE == GT_GLA) {
+      if constexpr (GATE == GT_GLA && !PRE) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }

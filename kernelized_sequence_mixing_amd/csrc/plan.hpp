@@ -61,6 +61,10 @@ struct BwdPlan : FwdPlan {
   float* ws_rh;  // [BH][P][r]
   void* ws_G;    // [BH][n][dv] bf16
   float* ws_h;   // [BH][n]
+  // GLA gate
+  void* dg;      // [BH][n][r] out_dtype
+  float* ws_dB;  // [BH][n][r]
+  float* ws_T;   // [BH][P][r]
 };
 
 struct DecodePlan {
@@ -94,7 +98,7 @@ struct FmapPlan {
 la_status launch_causal_elu1(const FwdPlan& p);
 la_status launch_causal_favor(const FwdPlan& p);
 la_status launch_segment_scan(const FwdPlan& p);
-la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z);
+la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG);
 la_status launch_backward(const BwdPlan& p);
 la_status launch_noncausal(const FwdPlan& p);
 la_status launch_decode(const DecodePlan& p);

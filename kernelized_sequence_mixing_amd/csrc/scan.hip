@@ -5,7 +5,9 @@
 // dileepadev.github.io, applied one segment at a time). Slot s of the workspace
 // holds dS_s on entry and S_in(s) on exit; z is chained the same way.
 // Reverse mode (the backward pass's state over later tokens) chains from the
-// last segment: R_in(P-1) = 0, R_in(s) = dR_{s+1} + Gamma R_in(s+1).
+// last segment: R_in(P-1) = 0, R_in(s) = dR_{s+1} + Gamma_{s+1} R_in(s+1)
+// (GLA: logG slot s + 1 holds segment s + 1's summed log-gate; slot 0 and
+// dR_0 only feed a value that is never stored).
 #include "chunked.hpp"
 
 namespace la {
@@ -60,10 +62,10 @@ la_status launch_segment_scan(const FwdPlan& p) {
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
-la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z) {
+la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG) {
   const int items = p.r * p.dv + p.r;
   dim3 grid((items + 255) / 256, unsigned(p.B) * unsigned(p.H));
-  hipLaunchKernelGGL(segment_scan_kernel, grid, dim3(256), 0, p.stream, S, z, nullptr, nullptr, nullptr, p.gamma,
+  hipLaunchKernelGGL(segment_scan_kernel, grid, dim3(256), 0, p.stream, S, z, logG, nullptr, nullptr, p.gamma,
                      p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 1);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

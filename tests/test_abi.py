@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     lib = N.lib()
-    assert lib.la_abi_version() == 1
+    assert lib.la_abi_version() == 2
     names = [lib.la_status_str(i).decode() for i in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_ALIAS",
                      "LA_ERR_HIP"]
@@ -218,19 +218,33 @@ def test_feature_map_rejects():
 
 # ------------------------------------------------------------------ backward (validation, no launch)
 
-def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAKE + 13 * SP):
+def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAKE + 13 * SP, dg=None):
     p = N.LaProblem(a["B"], a["H"], a["n"], a["d_k"], a["d_v"], a["in_dt"], a["out_dt"], a["eps"])
     f = N.LaFeatureMap(a["fkind"], a["r"], a["omega"])
     g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"])
     return N.lib().la_backward(ctypes.byref(p), a["Q"], a["K"], a["V"], dO, ctypes.byref(f), a["causal"],
-                               ctypes.byref(g), a["S0"], a["z0"], dQ, dK, dV, a["ws"], a["ws_bytes"], None)
+                               ctypes.byref(g), a["S0"], a["z0"], dQ, dK, dV, dg, a["ws"], a["ws_bytes"], None)
 
 
 BAD_BACKWARD = [
     ("n=0", dict(n=0), {}, N.LA_ERR_INVALID_ARG),
     ("noncausal", dict(causal=0), {}, N.LA_ERR_UNSUPPORTED),
     ("favor", dict(fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
-    ("gla", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), {}, N.LA_ERR_UNSUPPORTED),
+    ("gla without dg", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),
+    ("dg without gla", {}, dict(dg=FAKE + 14 * SP), N.LA_ERR_INVALID_ARG),
+    ("gla no g", dict(gkind=N.LA_GATE_GLA), dict(dg=FAKE + 14 * SP), N.LA_ERR_INVALID_ARG),
+    ("gla tau 0", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP, tau=0.0), dict(dg=FAKE + 14 * SP), N.LA_ERR_INVALID_ARG),
+    ("gla dg misaligned", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), dict(dg=FAKE + 14 * SP + 8),
+     N.LA_ERR_INVALID_ARG),
+    ("gla dg aliases g", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), dict(dg=FAKE + 6 * SP + 256), N.LA_ERR_ALIAS),
+    ("gla dg aliases dK", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), dict(dg=FAKE + 12 * SP + 256),
+     N.LA_ERR_ALIAS),
+    ("gla dg in workspace", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), dict(dg=FAKE + 4 * SP + 4096),
+     N.LA_ERR_ALIAS),
+    ("gla dQ aliases g", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), dict(dQ=FAKE + 6 * SP, dg=FAKE + 14 * SP),
+     N.LA_ERR_ALIAS),
+    ("gla favor", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP, fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP),
+     dict(dg=FAKE + 14 * SP), N.LA_ERR_UNSUPPORTED),
     ("d 128x128", dict(d_k=128, r=128, d_v=128), {}, N.LA_ERR_UNSUPPORTED),
     ("d_k 32", dict(d_k=32, r=32), {}, N.LA_ERR_UNSUPPORTED),
     ("fp32", dict(in_dt=N.LA_F32, out_dt=N.LA_F32), {}, N.LA_ERR_UNSUPPORTED),
@@ -273,3 +287,5 @@ def test_backward_workspace_size():
     zs = BH * P * 64 * 4
     assert size(4, 16, n, 64, 64) == 2 * states + 2 * zs + BH * n * 64 * 2 + BH * n * 4
     assert size(4, 16, n, 64, 64, N.LA_GATE_DECAY) == size(4, 16, n, 64, 64)
+    # GLA adds dB per token and feature (fp32), the segments' sums of dB and their summed log-gates
+    assert size(4, 16, n, 64, 64, N.LA_GATE_GLA) == size(4, 16, n, 64, 64) + BH * n * 64 * 4 + 2 * zs
