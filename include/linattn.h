@@ -173,7 +173,7 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  *   GLA gate and must be NULL otherwise (else LA_ERR_INVALID_ARG).
  *   workspace: device scratch of at least la_backward_workspace_size bytes,
  *   256-byte aligned (segment states of both directions, g and h per token;
- *   GLA: also dB per token and feature and per-segment sums).
+ *   GLA: also dQ~ . Q~ per token and feature and per-segment summed log-gates).
  * Supported (else LA_ERR_UNSUPPORTED): causal == 1, ELU1, any gate,
  * (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
  * inputs, each other or the workspace (LA_ERR_ALIAS). Numerics as la_forward:

@@ -179,13 +179,12 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
 }
 
 struct BwdWsLayout {
-  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, T_off, logG_off, bytes;
+  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, bytes;
   int P, L;
 };
 
 // Forward segment states, reverse segment states, g (bf16) and h per token;
-// GLA adds the log-gate gradient per token and feature, its segment sums and
-// the segments' summed log-gates.
+// GLA adds dQ~ . Q~ per token and feature and the segments' summed log-gates.
 BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, int gate) {
   BwdWsLayout w{};
   plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate, &w.P, &w.L);
@@ -199,11 +198,10 @@ BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, i
   w.h_off = round_up(w.G_off + BH * n * dv * 2, kAlign);
   w.dB_off = round_up(w.h_off + BH * n * 4, kAlign);
   if (gate != LA_GATE_GLA) {
-    w.T_off = w.logG_off = w.bytes = w.dB_off;
+    w.logG_off = w.bytes = w.dB_off;
     return w;
   }
-  w.T_off = round_up(w.dB_off + BH * n * r * 4, kAlign);
-  w.logG_off = round_up(w.T_off + BH * w.P * r * 4, kAlign);
+  w.logG_off = round_up(w.dB_off + BH * n * r * 4, kAlign);
   w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
   return w;
 }
@@ -460,7 +458,6 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.ws_h = reinterpret_cast<float*>(ws + wl.h_off);
   if (gk == LA_GATE_GLA) {
     plan.ws_dB = reinterpret_cast<float*>(ws + wl.dB_off);
-    plan.ws_T = reinterpret_cast<float*>(ws + wl.T_off);
     plan.ws_logG = reinterpret_cast<float*>(ws + wl.logG_off);
     plan.dg = dg;
   }

@@ -39,7 +39,6 @@ static la_status run_backward(const BwdPlan& p) {
     b.inv_tau = 1.f / p.tau;
     b.dB = p.ws_dB;
     b.logG = p.ws_logG;
-    b.T = p.ws_T;
     b.dg = static_cast<bf16*>(p.dg);
   }
   la_status st;
@@ -90,16 +89,7 @@ static la_status run_backward(const BwdPlan& p) {
     if ((st = launch_segment_scan_reverse(p, p.ws_R, p.ws_rh, GATE == GT_GLA ? p.ws_logG : nullptr)) != LA_OK)
       return st;
   }
-  if ((st = launch_with_lds(bwd_pass_b<R, E, GATE>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b)) !=
-      LA_OK)
-    return st;
-  if constexpr (GATE == GT_GLA) {
-    hipLaunchKernelGGL(bwd_dg_totals<R>, dim3(p.P, BH), dim3(256), 0, p.stream, b);
-    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
-    hipLaunchKernelGGL(bwd_dg<R>, dim3(p.P, BH), dim3(256), 0, p.stream, b);
-    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
-  }
-  return LA_OK;
+  return launch_with_lds(bwd_pass_b<R, E, GATE>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b);
 }
 
 template <int R, int E>

@@ -30,8 +30,11 @@
 // same passes give dQ~ and dK~, and the gate's gradient follows from
 // dB = dQ~ . Q~ - dK~ . K~ (the gradient of the cumulative log-gate; the
 // carried-in state, weighted by e^{B}, enters through dQ~) by a suffix sum
-// over the sequence (bwd_dg_totals, bwd_dg). The reverse state of a segment
-// then runs in natural row order (bwd_rstate_gla).
+// over the sequence: pass B sums the segment's own tokens back to front and
+// starts from d log alpha at the next segment's first token, which is the
+// row-wise product of the forward and reverse states there (scaling the state
+// that crosses a boundary is scaling every pair weight across it). The
+// reverse state of a segment runs in natural row order (bwd_rstate_gla).
 // All LDS tiles use the per-row chunk permutation of FeatTile.
 #pragma once
 
@@ -57,9 +60,8 @@ struct BwdArgs {
   bf16* dV;
   // GLA gate (per feature: alpha = sigmoid(g)^(1/tau))
   const bf16* gl;  // [B H n R] raw gate input
-  float* dB;       // [B H n R] dQ~ . Q~ (pass A), then that minus dK~ . K~ (pass B)
+  float* dB;       // [B H n R] dQ~ . Q~ (pass A, read by pass B)
   float* logG;     // [B H P R] summed log-gate of each segment (bwd_rstate_gla)
-  float* T;        // [B H P R] segment sums of dB
   bf16* dg;        // [B H n R]
   int H, n, P, seg_len;
   float eps, inv_tau;
@@ -502,8 +504,20 @@ struct BwdBLayout {
   static constexpr int rh_off = rb_off + R * 2 * E;    // [R] r_h entering the chunk
   static constexpr int hw_off = rh_off + R * 4;        // [64] h
   static constexpr int gam_off = hw_off + kChunk * 4;  // GLA: e^{chunk's summed log-gate}
-  static constexpr int bytes = gam_off + R * 4;
+  // GLA: [4][R] the waves' partial products of the states at the next segment's start
+  static constexpr int cpart_off = gam_off + R * 4;
+  static constexpr int bytes = cpart_off + (GATE == GT_GLA ? 4 * R * 4 : 0);
 };
+
+// Inclusive prefix sum across each row of 16 lanes (lane c gets x_0 + ... + x_c
+// of its row).
+__device__ __forceinline__ float row_inclusive_scan(float x) {
+  x += dpp_or_zero<0x111, 0xf>(x);
+  x += dpp_or_zero<0x112, 0xf>(x);
+  x += dpp_or_zero<0x114, 0xf>(x);
+  x += dpp_or_zero<0x118, 0xf>(x);
+  return x;
+}
 
 template <int R, int E, int GATE>
 __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
@@ -550,10 +564,36 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           Rs[rt][eb][i] = has_in ? b.R_ws[slot * R * E + (16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] : 0.f;
     z_load<R, NW>(Rz, has_in ? b.rh_ws + slot * R : nullptr, lane, w);
   }
+  // GLA: d log alpha at the next segment's first token t1 is
+  // sum_e S(t1)[f][e] R(t1)[f][e] + z(t1)[f] r_h(t1)[f], S(t1) the forward
+  // state entering that segment and R(t1) the reverse state entering this one
+  // from its end: the waves' partial sums over their value columns here, the
+  // z share in the first chunk
+  const bool later = s + 1 < b.P;
+  if constexpr (GATE == GT_GLA) {
+    const float* Sn = later ? b.S_in + bh * b.in_head + (long long)(s + 1) * b.in_seg : nullptr;
+#pragma unroll
+    for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = 16 * rt + 4 * g4 + i;
+        float acc = 0.f;
+        if (later) {
+#pragma unroll
+          for (int eb = 0; eb < NEB; ++eb) acc += Rs[rt][eb][i] * Sn[f * E + ebase + 16 * eb + c16];
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        acc += __shfl_xor(acc, 4);
+        acc += __shfl_xor(acc, 8);
+        if (c16 == 0) lds<float>(sm, LY::cpart_off + 4 * (w * R + f)) = acc;
+      }
+  }
 
   const int nslot = w < 2 ? 3 : 2;
   int sqi[3], skj[3];
   score_tiles(w, sqi, skj);
+  float carry[FPW][4];  // GLA: d log alpha at the end of the chunk, for this lane's features
 
   using Raw = RawChunk<R, E, R, FM_ELU1, PG, true, NW>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
@@ -679,14 +719,34 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     }
 
     // ---- dphi(k)^T = Phi_q^T dW (intra) + gamma^(L-t) (R v + r_h) (inter); dk = dphi(k) phi'(k).
-    // GLA: dK~ = Q~^T dW + Gamma (R v + r_h); dk = dK~ e^{-b} phi'(k), and dB
-    // becomes dQ~ . Q~ - dK~ . K~, the gradient of the cumulative log-gate.
+    // GLA: dK~ = Q~^T dW + Gamma (R v + r_h); dk = dK~ e^{-b} phi'(k), and
+    // dB = dQ~ . Q~ - dK~ . K~, the gradient of the cumulative log-gate, whose
+    // suffix sums give dg (below). A lane keeps the same features in every
+    // chunk: 16 ft + 4 g + u2, tokens 16 jt + c.
 #pragma unroll
     for (int u = 0; u < FPW; ++u) {
       const int ft = w * FPW + u;
       const int f0 = 16 * ft + 4 * g4;
+      if constexpr (GATE == GT_GLA) {
+        if (ci == nch - 1) {
+          // d log alpha entering from the later segments (see above)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
+          for (int u2 = 0; u2 < 4; ++u2) {
+            const int f = f0 + u2;
+            carry[u][u2] =
+                later ? ((lds<float>(sm, LY::cpart_off + 4 * f) + lds<float>(sm, LY::cpart_off + 4 * (R + f))) +
+                         (lds<float>(sm, LY::cpart_off + 4 * (2 * R + f)) +
+                          lds<float>(sm, LY::cpart_off + 4 * (3 * R + f)))) +
+                            b.z_in[(bh * b.in_head + (long long)(s + 1) * b.in_seg) / E + f] *
+                                lds<float>(sm, LY::rh_off + 4 * f)
+                      : 0.f;
+          }
+        }
+      }
+      // GLA walks the key tiles back to front for the suffix sums of dB
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int jt = GATE == GT_GLA ? 3 - jj : jj;
         const int j = 16 * jt + c16;
         f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -714,15 +774,28 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
             dk[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
           }
         }
-        if (j < L) {
-          *reinterpret_cast<bf16x4*>(b.dK + (tok0 + t0 + j) * R + f0) = pack4(dk[0], dk[1], dk[2], dk[3]);
-          if constexpr (GATE == GT_GLA) {
-            f32x4* pb = reinterpret_cast<f32x4*>(b.dB + (tok0 + t0 + j) * R + f0);
-            f32x4 db = *pb;
-#pragma unroll
-            for (int u2 = 0; u2 < 4; ++u2) db[u2] -= bk[u2];
-            *pb = db;
+        if (j < L) *reinterpret_cast<bf16x4*>(b.dK + (tok0 + t0 + j) * R + f0) = pack4(dk[0], dk[1], dk[2], dk[3]);
+        if constexpr (GATE == GT_GLA) {
+          // ---- dg: d log alpha_t = (d log alpha after the tile) + sum of dB over
+          // the tile's tokens t' >= t (the row of 16 lanes holds tokens 16 jt + c
+          // of four features); dg = d log alpha sigmoid(-g) / tau
+          const long long at = (tok0 + t0 + j) * R + f0;
+          f32x4 db = {0.f, 0.f, 0.f, 0.f};
+          bf16x4 gv = {};
+          if (j < L) {
+            db = *reinterpret_cast<const f32x4*>(b.dB + at);
+            gv = *reinterpret_cast<const bf16x4*>(b.gl + at);
           }
+          float o[4];
+#pragma unroll
+          for (int u2 = 0; u2 < 4; ++u2) {
+            const float x = j < L ? db[u2] - bk[u2] : 0.f;
+            const float pre = row_inclusive_scan(x);
+            const float tot = __shfl(pre, (lane & 48) | 15);
+            o[u2] = (carry[u][u2] + ((tot - pre) + x)) * (b.inv_tau / (1.f + __expf(to_f32(gv[u2]))));
+            carry[u][u2] += tot;
+          }
+          if (j < L) *reinterpret_cast<bf16x4*>(b.dg + at) = pack4(o[0], o[1], o[2], o[3]);
         }
       }
     }
@@ -822,91 +895,6 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
       for (int i = 0; i < 4; ++i) Ro[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = Rs[rt][eb][i];
   z_store<R, NW>(Rz, b.rh_ws + slot * R, lane, w);
   if (lane < FR) b.logG[slot * R + w * FR + lane] = lds<float>(sm, LY::logg_off + 4 * (w * FR + lane));
-}
-
-// ---------------------------------------------------------------------------
-// GLA: the raw gate's gradient. B_t = sum_{u<=t} log alpha_u over the whole
-// sequence, so d log alpha_u = sum_{t>=u} dB_t, and
-// log alpha = -softplus(-g) / tau gives dg = d log alpha * sigmoid(-g) / tau.
-// Two launches over (segment, head) workgroups of 256 threads, thread
-// (phase p, feature f) with 256 / R phases: the segments' sums of dB, then each
-// segment's suffix sums from the later segments' sums (added last to first)
-// and its own tokens. Every sum runs in a fixed order.
-// ---------------------------------------------------------------------------
-template <int R>
-__global__ __launch_bounds__(256) void bwd_dg_totals(BwdArgs b) {
-  constexpr int NP = 256 / R, BATCH = 8;
-  __shared__ float part[256];
-  const int f = threadIdx.x % R, ph = threadIdx.x / R;
-  const int s = blockIdx.x;
-  const long long bh = blockIdx.y;
-  const int t_begin = s * b.seg_len;
-  const int t_end = min(b.n, t_begin + b.seg_len);
-  const float* src = b.dB + bh * b.n * R + f;
-  float acc = 0.f;
-  for (int t = t_begin + ph; t < t_end; t += BATCH * NP) {
-    float x[BATCH];
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int tt = t + j * NP;
-      x[j] = tt < t_end ? src[(long long)tt * R] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) acc += x[j];
-  }
-  part[threadIdx.x] = acc;
-  __syncthreads();
-  if (ph == 0) {
-    float tot = 0.f;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) tot += part[p * R + f];
-    b.T[(bh * b.P + s) * R + f] = tot;
-  }
-}
-
-template <int R>
-__global__ __launch_bounds__(256) void bwd_dg(BwdArgs b) {
-  constexpr int NP = 256 / R, BATCH = 8;
-  __shared__ float part[256];
-  const int f = threadIdx.x % R, ph = threadIdx.x / R;
-  const int s = blockIdx.x;
-  const long long bh = blockIdx.y;
-  const int t_begin = s * b.seg_len;
-  const int t_end = min(b.n, t_begin + b.seg_len);
-  const long long base = bh * b.n * R + f;
-  // the segment as NP runs of consecutive tokens, run p = [r0, r1)
-  const int run = (t_end - t_begin + NP - 1) / NP;
-  const int r0 = t_begin + ph * run, r1 = min(t_end, r0 + run);
-  float rsum = 0.f;
-  for (int t = r0; t < r1; t += BATCH) {
-    float x[BATCH];
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) x[j] = t + j < r1 ? b.dB[base + (long long)(t + j) * R] : 0.f;
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) rsum += x[j];
-  }
-  part[threadIdx.x] = rsum;
-  float carry = 0.f;
-  for (int s2 = b.P - 1; s2 > s; --s2) carry += b.T[(bh * b.P + s2) * R + f];
-  __syncthreads();
-  for (int p = NP - 1; p > ph; --p) carry += part[p * R + f];
-  for (int t = r1 - 1; t >= r0; t -= BATCH) {
-    float x[BATCH], gv[BATCH];
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const bool ok = t - j >= r0;
-      x[j] = ok ? b.dB[base + (long long)(t - j) * R] : 0.f;
-      gv[j] = ok ? to_f32(b.gl[base + (long long)(t - j) * R]) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      if (t - j >= r0) {
-        carry += x[j];
-        const float sig_neg = 1.f / (1.f + __expf(gv[j]));
-        b.dg[base + (long long)(t - j) * R] = (bf16)(carry * sig_neg * b.inv_tau);
-      }
-    }
-  }
 }
 
 }  // namespace la

@@ -64,7 +64,6 @@ struct BwdPlan : FwdPlan {
   // GLA gate
   void* dg;      // [BH][n][r] out_dtype
   float* ws_dB;  // [BH][n][r]
-  float* ws_T;   // [BH][P][r]
 };
 
 struct DecodePlan {

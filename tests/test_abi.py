@@ -287,5 +287,5 @@ def test_backward_workspace_size():
     zs = BH * P * 64 * 4
     assert size(4, 16, n, 64, 64) == 2 * states + 2 * zs + BH * n * 64 * 2 + BH * n * 4
     assert size(4, 16, n, 64, 64, N.LA_GATE_DECAY) == size(4, 16, n, 64, 64)
-    # GLA adds dB per token and feature (fp32), the segments' sums of dB and their summed log-gates
-    assert size(4, 16, n, 64, 64, N.LA_GATE_GLA) == size(4, 16, n, 64, 64) + BH * n * 64 * 4 + 2 * zs
+    # GLA adds dQ~ . Q~ per token and feature (fp32) and the segments' summed log-gates
+    assert size(4, 16, n, 64, 64, N.LA_GATE_GLA) == size(4, 16, n, 64, 64) + BH * n * 64 * 4 + zs
