@@ -201,7 +201,8 @@ BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, i
     w.logG_off = w.bytes = w.dB_off;
     return w;
   }
-  w.logG_off = round_up(w.dB_off + BH * n * r * 4, kAlign);
+  const size_t n64 = (n + 63) / 64 * 64;  // dQ~ . Q~ is stored by whole chunks
+  w.logG_off = round_up(w.dB_off + BH * n64 * r * 4, kAlign);
   w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
   return w;
 }

@@ -60,12 +60,23 @@ struct BwdArgs {
   bf16* dV;
   // GLA gate (per feature: alpha = sigmoid(g)^(1/tau))
   const bf16* gl;  // [B H n R] raw gate input
-  float* dB;       // [B H n R] dQ~ . Q~ (pass A, read by pass B)
+  float* dB;       // dQ~ . Q~ (pass A, read by pass B), in the order of dbq_at
   float* logG;     // [B H P R] summed log-gate of each segment (bwd_rstate_gla)
   bf16* dg;        // [B H n R]
   int H, n, P, seg_len;
   float eps, inv_tau;
 };
+
+// Index (floats) of the four features 16 ft + 4 g .. + 3 of token 16 it + c of
+// chunk ch (chunks counted from the head's first token) in the GLA workspace of
+// dQ~ . Q~: per head ceil(n / 64) chunks of R / 16 feature tiles of four token
+// tiles, 16 bytes per lane (g, c), so the lanes that write it in pass A and the
+// lanes that read it in pass B move 1 KB contiguous per instruction.
+template <int R>
+__device__ __forceinline__ long long dbq_at(long long bh, int n, int ch, int ft, int it, int lane) {
+  const long long nch = (n + kChunk - 1) / kChunk;
+  return ((((bh * nch + ch) * (R / 16) + ft) * 4 + it) * 64 + lane) * 4;
+}
 
 // One chunk of an E-wide bf16 array in the row-major layout of RawChunk with
 // four waves: wave w holds tokens 16 w .. 16 w + 15, lane l token 16 w + l / 4
@@ -372,10 +383,9 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
             dq[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
           }
         }
-        if (i < L) {
-          *reinterpret_cast<bf16x4*>(b.dQ + (tok0 + t0 + i) * R + f0) = pack4(dq[0], dq[1], dq[2], dq[3]);
-          if constexpr (GATE == GT_GLA) *reinterpret_cast<f32x4*>(b.dB + (tok0 + t0 + i) * R + f0) = db;
-        }
+        if (i < L) *reinterpret_cast<bf16x4*>(b.dQ + (tok0 + t0 + i) * R + f0) = pack4(dq[0], dq[1], dq[2], dq[3]);
+        if constexpr (GATE == GT_GLA)
+          *reinterpret_cast<f32x4*>(b.dB + dbq_at<R>(bh, b.n, t0 / kChunk, ft, it, lane)) = db;
       }
     }
 
@@ -498,7 +508,8 @@ struct BwdBLayout {
   static constexpr int g_off = v_off + VTB;            // g
   static constexpr int qw_off = g_off + VTB;           // RetNet: gamma^t phi(q)
   static constexpr int kd_off = qw_off + (GATE == GT_DECAY ? FTB : 0);  // GLA: e^{-b} phi'(k)
-  static constexpr int w_off = kd_off + (GATE == GT_GLA ? FTB : 0);     // W^T [key][query]
+  static constexpr int gr_off = kd_off + (GATE == GT_GLA ? FTB : 0);    // GLA: the raw gate input g
+  static constexpr int w_off = gr_off + (GATE == GT_GLA ? FTB : 0);     // W^T [key][query]
   static constexpr int dw_off = w_off + ATB;           // dW^T [key][query]
   static constexpr int rb_off = dw_off + ATB;          // bf16 [R][E] image of R entering the chunk
   static constexpr int rh_off = rb_off + R * 2 * E;    // [R] r_h entering the chunk
@@ -625,6 +636,12 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
         lds<bf16x8>(sm, LY::qw_off + FT::at(t, lane % 4 + 4 * j)) =
             keep_if(t < L, cat8(pack4(f[0], f[1], f[2], f[3]), pack4(f[4], f[5], f[6], f[7])));
       }
+    }
+    if constexpr (GATE == GT_GLA) {
+      // the raw gate of this lane's token and the wave's features, for dg
+#pragma unroll
+      for (int jg = 0; jg < R / 32; ++jg)
+        lds<bf16x8>(sm, LY::gr_off + FT::at(lane, (w * (R / 4) + 8 * jg) / 8)) = raw.g[jg];
     }
     rg.store(sm, LY::g_off, L, lane, w);
     if (w == 0) lds<float>(sm, LY::hw_off + 4 * lane) = lane < L ? hv : 0.f;
@@ -779,23 +796,18 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           // ---- dg: d log alpha_t = (d log alpha after the tile) + sum of dB over
           // the tile's tokens t' >= t (the row of 16 lanes holds tokens 16 jt + c
           // of four features); dg = d log alpha sigmoid(-g) / tau
-          const long long at = (tok0 + t0 + j) * R + f0;
-          f32x4 db = {0.f, 0.f, 0.f, 0.f};
-          bf16x4 gv = {};
-          if (j < L) {
-            db = *reinterpret_cast<const f32x4*>(b.dB + at);
-            gv = *reinterpret_cast<const bf16x4*>(b.gl + at);
-          }
+          const f32x4 db = *reinterpret_cast<const f32x4*>(b.dB + dbq_at<R>(bh, b.n, t0 / kChunk, ft, jt, lane));
+          const bf16x4 gv = lds<bf16x4>(sm, LY::gr_off + FT::at(j, f0 / 8, 2 * (f0 % 8)));
           float o[4];
 #pragma unroll
           for (int u2 = 0; u2 < 4; ++u2) {
             const float x = j < L ? db[u2] - bk[u2] : 0.f;
             const float pre = row_inclusive_scan(x);
             const float tot = __shfl(pre, (lane & 48) | 15);
-            o[u2] = (carry[u][u2] + ((tot - pre) + x)) * (b.inv_tau / (1.f + __expf(to_f32(gv[u2]))));
+            o[u2] = (carry[u][u2] + ((tot - pre) + x)) * b.inv_tau * __builtin_amdgcn_rcpf(1.f + __expf(to_f32(gv[u2])));
             carry[u][u2] += tot;
           }
-          if (j < L) *reinterpret_cast<bf16x4*>(b.dg + at) = pack4(o[0], o[1], o[2], o[3]);
+          if (j < L) *reinterpret_cast<bf16x4*>(b.dg + (tok0 + t0 + j) * R + f0) = pack4(o[0], o[1], o[2], o[3]);
         }
       }
     }
@@ -825,8 +837,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
 template <int R, int E>
 struct BwdRGLayout {
   static constexpr int q_off = 0;                           // Q~
-  static constexpr int k_off = q_off + FeatTile<R>::BYTES;  // (written by the shared prelude, unused)
-  static constexpr int v_off = k_off + FeatTile<R>::BYTES;  // g
+  static constexpr int v_off = q_off + FeatTile<R>::BYTES;  // g
   static constexpr int hw_off = v_off + FeatTile<E>::BYTES;  // [64] h
   static constexpr int gam_off = hw_off + kChunk * 4;        // [R] e^{chunk's summed log-gate}
   static constexpr int logg_off = gam_off + R * 4;           // [R] segment's summed log-gate
@@ -847,8 +858,7 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   const long long tok0 = bh * b.n;
   const int ebase = w * (E / NW);
   CausalArgs ca{};
-  ca.Q = b.Q;
-  ca.K = b.Q;  // the prelude's key slot is not used here
+  ca.K = b.Q;  // the queries in the prelude's key slot, scaled by e^{+b}: Q~
   ca.V = b.G;
   ca.g = b.gl;
   ca.inv_tau = b.inv_tau;
@@ -863,7 +873,7 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   // the lane that accumulates feature w FR + lane in the prelude clears it
   if (lane < FR) lds<float>(sm, LY::logg_off + 4 * (w * FR + lane)) = 0.f;
 
-  using Raw = RawChunk<R, E, R, FM_ELU1, GT_GLA, true, NW>;
+  using Raw = RawChunk<R, E, R, FM_ELU1, GT_GLA, false, NW>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
   float hv = 0.f;
@@ -876,8 +886,8 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, t_end - t0);
-    chunk_prelude<R, E, R, FM_ELU1, GT_GLA, true, NW, true, kPreLogG>(raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0,
-                                                                      LY::v_off, LY::gam_off, LY::logg_off, lane, w);
+    chunk_prelude<R, E, R, FM_ELU1, GT_GLA, false, NW, true, kPreKPos>(raw, ca, L, 0.f, sm, 0, LY::q_off, 0,
+                                                                       LY::v_off, LY::gam_off, LY::logg_off, lane, w);
     if (w == 0) lds<float>(sm, LY::hw_off + 4 * lane) = lane < L ? hv : 0.f;
     if (ci > 0) load(ci - 1);
     lds_barrier();

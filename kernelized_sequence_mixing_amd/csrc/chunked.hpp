@@ -258,8 +258,9 @@ struct RawChunk {
 // qd = e^{b} phi'(q), kPreKD the tile kd = e^{-b} phi'(k) (phi'(x) =
 // min(phi(x), 1) for elu+1), the factors that turn gradients with respect to
 // Q~ and K~ into gradients of q and k; kPreLogG adds the chunk's summed
-// log-gates to logg also when WITH_Q.
-constexpr int kPreQD = 1, kPreKD = 2, kPreLogG = 4;
+// log-gates to logg also when WITH_Q; kPreKPos scales the key slot by e^{+b}
+// (the Q~ of the reverse state, with the queries passed as keys).
+constexpr int kPreQD = 1, kPreKD = 2, kPreLogG = 4, kPreKPos = 8;
 template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SWZ, int EXTRA = 0>
 __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>& raw,
                                               const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
@@ -325,7 +326,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
           float b = wave_inclusive_scan(la);
           // the chunk total is uniform across the wave: a scalar read of lane 63
           const float bend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
-          const float eb = __expf(b), emb = __expf(-b);
+          const float eb = __expf(b), emb = __expf((EXTRA & kPreKPos) != 0 ? b : -b);
           if constexpr ((EXTRA & kPreQD) != 0) dq[u] = eb * fminf(pq, 1.f);
           if constexpr ((EXTRA & kPreKD) != 0) dk[u] = emb * fminf(pk, 1.f);
           pq *= eb;

@@ -63,7 +63,7 @@ struct BwdPlan : FwdPlan {
   float* ws_h;   // [BH][n]
   // GLA gate
   void* dg;      // [BH][n][r] out_dtype
-  float* ws_dB;  // [BH][n][r]
+  float* ws_dB;  // [BH][ceil(n / 64) * 64][r] in the kernels' own order
 };
 
 struct DecodePlan {
