@@ -190,29 +190,35 @@ def bench_decode(wl, steps, warmup):
 def backward_algorithmic_per_token(wl):
     """(bytes, matrix-core flops) per head-token of the causal backward pass.
 
-    Bytes: read q, k, v, dO once, write dq, dk, dv once. Flops (chunk C, masked
-    upper triangle excluded): the scores, the numerator of o, dW, and the
-    intra-chunk parts of dq, dk, dv ((C+1)/2 * 2 r or 2 d_v each), plus six
-    r x d_v products per token (o's inter-chunk read, dq's S g, dk's R v, dv's
-    R phi(k), and the forward and reverse state updates).
+    Bytes: read q, k, v, dO once, write dq, dk, dv once (GLA: also read g and
+    write dg). Flops (chunk C, masked upper triangle excluded): the scores, the
+    numerator of o, dW, and the intra-chunk parts of dq, dk, dv ((C+1)/2 * 2 r
+    or 2 d_v each), plus six r x d_v products per token (o's inter-chunk read,
+    dq's S g, dk's R v, dv's R phi(k), and the forward and reverse state
+    updates).
     """
     nbytes = 2 * (2 * wl.d_k + 2 * wl.d_v) + 2 * (2 * wl.d_k + wl.d_v)
+    if wl.gate == "gla":
+        nbytes += 2 * (2 * wl.r)
     half = (CHUNK + 1) / 2
     flops = half * 2 * wl.r * 3 + half * 2 * wl.d_v * 3 + 6 * 2 * wl.r * wl.d_v
     return nbytes, flops
 
 
 def bench_backward(wl, steps, warmup):
-    """la_backward on workload wl (causal elu+1): one step is one full backward pass."""
+    """la_backward on workload wl (causal elu+1): one step is one full backward pass
+    (with the GLA gate it includes dg)."""
     import kernelized_sequence_mixing_amd as ksm
     from workloads import incoming_gradient
     inp = make_inputs(wl, seed=0)
     inp["dO"] = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1)
     nb_tok, fl_tok = backward_algorithmic_per_token(wl)
     per_set = wl.head_tokens * nb_tok
-    sets = _device_sets(inp, ["Q", "K", "V", "dO", "gamma"], per_set)
-    gate_of = {"none": lambda s: None, "decay": lambda s: ("decay", s["gamma"])}[wl.gate]
-    grads = [(torch.empty_like(s["Q"]), torch.empty_like(s["K"]), torch.empty_like(s["V"])) for s in sets]
+    sets = _device_sets(inp, ["Q", "K", "V", "dO", "gamma", "g"], per_set)
+    gate_of = {"none": lambda s: None, "decay": lambda s: ("decay", s["gamma"]),
+               "gla": lambda s: ("gla", s["g"], wl.tau)}[wl.gate]
+    grads = [(torch.empty_like(s["Q"]), torch.empty_like(s["K"]), torch.empty_like(s["V"])) +
+             ((torch.empty_like(s["g"]),) if wl.gate == "gla" else ()) for s in sets]
     stream = torch.cuda.current_stream()
     calls = [ksm.PreparedBackward(s["Q"], s["K"], s["V"], s["dO"], gate=gate_of(s), eps=wl.eps, grads=grads[i],
                                   stream=stream) for i, s in enumerate(sets)]
@@ -227,7 +233,8 @@ def bench_backward(wl, steps, warmup):
             "value": wl.head_tokens / (ms * 1e-3), "unit": "head-tokens/s", "input_sets_rotated": len(sets),
             "hbm_alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "mfma_alg_TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4),
-            "alg_bytes_per_token": nb_tok, "alg_flops_per_token": fl_tok}
+            "alg_bytes_per_token": nb_tok, "alg_flops_per_token": fl_tok,
+            "shape": {"B": wl.B, "H": wl.H, "n": wl.n, "d_k": wl.d_k, "d_v": wl.d_v, "gate": wl.gate}}
 
 
 def cpu_baseline(wl, min_seconds=10.0):
@@ -320,6 +327,10 @@ def main():
             extra.append(bench_forward(WORKLOADS[name], args.steps, args.warmup))
         extra.append(bench_decode(WORKLOADS["gla_decode"], args.steps, args.warmup))
         extra.append(bench_backward(WORKLOADS["causal_elu1"], args.steps, args.warmup))
+        # the GLA workload's sequence shape at d_k = d_v = 64 (no backward build for 128 x 128 states)
+        extra.append(bench_backward(WORKLOADS["gla_gate"].resized(name="gla_gate_d64", d_k=64, d_v=64, r=64,
+                                                                  qk_scale=64 ** -0.5, v_scale=64 ** -0.5),
+                                    args.steps, args.warmup))
         line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
