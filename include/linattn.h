@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 2
+#define LA_ABI_VERSION 3
 
 typedef enum la_status {
   LA_OK = 0,
@@ -94,6 +94,32 @@ typedef struct la_gate {
   const void* g;      /* GLA: device [B][H][n][r] in in_dtype (decode: [B][H][r]) */
 } la_gate;
 
+/* Flags of la_batch.flags. */
+#define LA_SLOT_READ 1  /* each sequence starts from the state in its slot (else from zero) */
+#define LA_SLOT_WRITE 2 /* each sequence's state after its last token is stored in its slot */
+
+/*
+ * A serving batch for la_forward_batch: independent causal sequences, each
+ * bound to a slot of a caller-owned state pool (the recurrent state that
+ * replaces a growing KV cache: "Recurrent Reformulation", dileepadev page;
+ * inference throughput, "Linear Attention Mechanisms", sadullah page).
+ */
+typedef struct la_batch {
+  const int32_t* cu_seqlens; /* NULL: p->B sequences of p->n tokens ([B][H][n][.] layout).
+                                Else device [num_seqs + 1] token offsets along n, with
+                                p->B == 1: sequence b is tokens cu[b] .. cu[b+1] - 1 of
+                                the [1][H][n][.] tensors (packed, no padding). */
+  int32_t num_seqs;          /* number of sequences; must be p->B without cu_seqlens */
+  int32_t max_seqlen;        /* with cu_seqlens: an upper bound of every sequence's length,
+                                1 <= max_seqlen <= p->n (used for planning); without: p->n */
+  float* S;                  /* state pool: device fp32 [num_slots][H][r][d_v]; read and/or
+                                written in place; may be NULL when flags == 0 */
+  float* z;                  /* device fp32 [num_slots][H][r] */
+  const int32_t* slot_ids;   /* device [num_seqs]: the slot of each sequence */
+  int32_t num_slots;         /* >= 1 when flags != 0 */
+  int32_t flags;             /* LA_SLOT_READ | LA_SLOT_WRITE, or 0 */
+} la_batch;
+
 /* ABI version of the loaded library (LA_ABI_VERSION at build time). */
 int32_t la_abi_version(void);
 
@@ -142,6 +168,43 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
                      const la_feature_map* fmap, int32_t causal, const la_gate* gate,
                      const float* S0, const float* z0, float* S_final, float* z_final,
                      void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace la_forward_batch needs. Pure host computation,
+ * same validation as la_forward_batch (device pointers not inspected).
+ */
+la_status la_forward_batch_workspace_size(const la_problem* p, const la_batch* batch,
+                                          const la_feature_map* fmap, const la_gate* gate,
+                                          size_t* bytes);
+
+/*
+ * The causal forward pass over a serving batch of sequences (see la_batch):
+ * a ragged prefill (cu_seqlens) or a step of m tokens for each of B
+ * sequences (multi-token decode; m = p->n), each sequence continuing from
+ * and/or storing its state in its slot. Per sequence the result is that of
+ * la_forward(causal = 1) on that sequence alone with S0 = its slot's state
+ * (LA_SLOT_READ) and S_final = its slot (LA_SLOT_WRITE); the slots are updated
+ * in place, after every read of them.
+ *   Q, K, out, gate->g as la_forward on the [B][H][n][.] tensors (B = 1 with
+ *   cu_seqlens); fmap, gate as la_forward; out: tokens no sequence covers are
+ *   left untouched.
+ * Device-side contents are not validated on the host; the kernels clamp them
+ * so that no access leaves the buffers: each sequence's bounds are clamped
+ * into [0, n] (an end below its start gives an empty sequence), lengths
+ * above max_seqlen are cut to the planned capacity (tokens past it get no
+ * output), and a slot id outside [0, num_slots) means that sequence starts
+ * from zero and stores no state. Overlapping sequences give unspecified
+ * outputs for the shared tokens.
+ * Slot ids must be distinct within a call when LA_SLOT_WRITE is set (two
+ * sequences writing one slot race).
+ * Supported: as la_forward with causal == 1. Errors: LA_ERR_INVALID_ARG for a
+ * malformed batch (num_seqs, max_seqlen, flags, B != 1 with cu_seqlens, NULL
+ * pool pointers with flags set); LA_ERR_ALIAS when out, the pool or the
+ * workspace overlap an input or each other. The library allocates nothing.
+ */
+la_status la_forward_batch(const la_problem* p, const la_batch* batch, const void* Q, const void* K,
+                           const void* V, const la_feature_map* fmap, const la_gate* gate,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace la_backward needs for this problem. Pure host

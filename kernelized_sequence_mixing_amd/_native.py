@@ -16,9 +16,11 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_ALIAS, L
 LA_F32, LA_BF16 = 0, 1
 LA_FMAP_ELU1, LA_FMAP_FAVOR = 0, 1
 LA_GATE_NONE, LA_GATE_DECAY, LA_GATE_GLA = 0, 1, 2
+LA_SLOT_READ, LA_SLOT_WRITE = 1, 2
 
 EXPORTED = ("la_abi_version", "la_status_str", "la_forward_workspace_size", "la_forward_segments",
-            "la_forward", "la_backward_workspace_size", "la_backward", "la_decode_step", "la_feature_map_apply")
+            "la_forward", "la_forward_batch_workspace_size", "la_forward_batch", "la_backward_workspace_size",
+            "la_backward", "la_decode_step", "la_feature_map_apply")
 
 
 class LaProblem(ctypes.Structure):
@@ -32,6 +34,11 @@ class LaFeatureMap(ctypes.Structure):
 
 class LaGate(ctypes.Structure):
     _fields_ = [("kind", c_int32), ("tau", c_float), ("gamma", c_void_p), ("g", c_void_p)]
+
+
+class LaBatch(ctypes.Structure):
+    _fields_ = [("cu_seqlens", c_void_p), ("num_seqs", c_int32), ("max_seqlen", c_int32), ("S", c_void_p),
+                ("z", c_void_p), ("slot_ids", c_void_p), ("num_slots", c_int32), ("flags", c_int32)]
 
 
 class LinattnError(RuntimeError):
@@ -66,6 +73,12 @@ def lib():
     L.la_forward.argtypes = [POINTER(LaProblem), c_void_p, c_void_p, c_void_p, POINTER(LaFeatureMap), c_int32,
                              POINTER(LaGate), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_size_t, c_void_p]
+    L.la_forward_batch_workspace_size.restype = c_int32
+    L.la_forward_batch_workspace_size.argtypes = [POINTER(LaProblem), POINTER(LaBatch), POINTER(LaFeatureMap),
+                                                  POINTER(LaGate), POINTER(c_size_t)]
+    L.la_forward_batch.restype = c_int32
+    L.la_forward_batch.argtypes = [POINTER(LaProblem), POINTER(LaBatch), c_void_p, c_void_p, c_void_p,
+                                   POINTER(LaFeatureMap), POINTER(LaGate), c_void_p, c_void_p, c_size_t, c_void_p]
     L.la_backward_workspace_size.restype = c_int32
     L.la_backward_workspace_size.argtypes = [POINTER(LaProblem), POINTER(LaFeatureMap), c_int32, POINTER(LaGate),
                                              POINTER(c_size_t)]

@@ -188,6 +188,100 @@ class PreparedForward:
         return self.out
 
 
+def _batch_args(Q, K, V, cu_seqlens, max_seqlen, state, slot_ids, read, write, fmap, omega, gate, eps, out,
+                workspace, stream):
+    """Validate and marshal one la_forward_batch call: (ctypes arguments, keep-alive objects, out)."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
+        _dev(t, nm)
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
+        raise ValueError(f"shapes Q{tuple(Q.shape)} K{tuple(K.shape)} V{tuple(V.shape)} do not match")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K, V must share a dtype")
+    B, H, n, d_k = Q.shape
+    d_v = V.shape[3]
+    f, r = _fmap_struct(fmap, omega, d_k)
+    g = _gate_struct(gate, (B, H, n, r))
+    p = _problem(B, H, n, d_k, d_v, _dt(Q), _dt(Q), eps)
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+        num_seqs = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens (a host-side bound)")
+    else:
+        num_seqs, max_seqlen = B, n
+    flags = (N.LA_SLOT_READ if read else 0) | (N.LA_SLOT_WRITE if write else 0)
+    S = z = None
+    num_slots = 0
+    if flags:
+        if state is None or slot_ids is None:
+            raise ValueError("reading or writing slots needs state=(S, z) and slot_ids")
+        S, z = state
+        _dev(S, "S")
+        _dev(z, "z")
+        _dev(slot_ids, "slot_ids")
+        num_slots = S.shape[0]
+        if (S.dtype != torch.float32 or tuple(S.shape) != (num_slots, H, r, d_v) or z.dtype != torch.float32
+                or tuple(z.shape) != (num_slots, H, r)):
+            raise ValueError(f"state must be float32 S[slots, {H}, {r}, {d_v}] and z[slots, {H}, {r}]")
+        if slot_ids.dtype != torch.int32 or slot_ids.numel() != num_seqs:
+            raise ValueError("slot_ids must be int32 with one entry per sequence")
+    addr = lambda t: None if t is None else t.data_ptr()
+    batch = N.LaBatch(addr(cu_seqlens), num_seqs, int(max_seqlen), addr(S), addr(z), addr(slot_ids), num_slots,
+                      flags)
+    if out is None:
+        out = torch.empty((B, H, n, d_v), dtype=Q.dtype, device=Q.device)
+    ws_bytes = ctypes.c_size_t(0)
+    N.check(N.lib().la_forward_batch_workspace_size(ctypes.byref(p), ctypes.byref(batch), ctypes.byref(f),
+                                                    ctypes.byref(g), ctypes.byref(ws_bytes)),
+            "la_forward_batch_workspace_size")
+    need = ws_bytes.value
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    args = (ctypes.byref(p), ctypes.byref(batch), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(f), ctypes.byref(g),
+            _ptr(out), _ptr(workspace) if need else None, need, _stream(Q, stream))
+    keep = (p, batch, f, g, Q, K, V, omega, gate, cu_seqlens, S, z, slot_ids, workspace)
+    return args, keep, out
+
+
+def forward_batch(Q, K, V, *, cu_seqlens=None, max_seqlen=None, state=None, slot_ids=None, read=False,
+                  write=False, fmap="elu1", omega=None, gate=None, eps=1e-6, out=None, workspace=None, stream=None):
+    """Causal forward over a serving batch through la_forward_batch.
+
+    Without cu_seqlens: B sequences of n tokens (Q [B, H, n, d_k]), e.g. a step
+    of n new tokens for each of B running sequences. With cu_seqlens (int32
+    [num_seqs + 1] on the device) and max_seqlen (host int): the sequences lie
+    back to back along n of [1, H, n, d_k] tensors. state = (S, z), float32
+    [slots, H, r, d_v] and [slots, H, r], updated in place; slot_ids int32
+    [num_seqs]; read: start from the slots' states; write: store the final
+    states. Returns out."""
+    args, _keep, out = _batch_args(Q, K, V, cu_seqlens, max_seqlen, state, slot_ids, read, write, fmap, omega,
+                                   gate, eps, out, workspace, stream)
+    N.check(N.lib().la_forward_batch(*args), "la_forward_batch")
+    return out
+
+
+class PreparedForwardBatch:
+    """One la_forward_batch call marshalled once (same arguments as
+    forward_batch); calling the object launches it again on the same buffers."""
+
+    def __init__(self, Q, K, V, **kw):
+        keys = ("cu_seqlens", "max_seqlen", "state", "slot_ids", "read", "write", "fmap", "omega", "gate", "eps",
+                "out", "workspace", "stream")
+        d = dict(cu_seqlens=None, max_seqlen=None, state=None, slot_ids=None, read=False, write=False, fmap="elu1",
+                 omega=None, gate=None, eps=1e-6, out=None, workspace=None, stream=None)
+        d.update(kw)
+        self._args, self._keep, self.out = _batch_args(Q, K, V, *(d[k] for k in keys))
+        self._fn = N.lib().la_forward_batch
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            N.check(st, "la_forward_batch")
+        return self.out
+
+
 def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream):
     """Validate and marshal one la_backward call: (ctypes arguments, keep-alive objects, gradients), the
     gradients being (dQ, dK, dV), plus dg with the GLA gate."""

@@ -319,6 +319,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   plan.S_final = S_final;
   plan.z_final = z_final;
   plan.out = out;
+  plan.nseq = p->B;
   plan.stream = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   plan.ws_S = wl.bytes ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
@@ -330,6 +331,127 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   }
   plan_splits(p->B, p->H, p->n, &plan.splits, &plan.split_len);
   return launch_noncausal(plan);
+}
+
+// ---- serving batches
+
+namespace {
+// Validation of a batch description shared by la_forward_batch and its size
+// query; *eff gets the problem the segment planner sees (num_seqs sequences
+// of max_seqlen tokens).
+la_status check_batch(const la_problem* p, const la_batch* b, const la_feature_map* f, const la_gate* g,
+                      la_problem* eff) {
+  if (b == nullptr) return LA_ERR_INVALID_ARG;
+  la_status st = check_forward_shape(p, f, 1, g);
+  if (st != LA_OK) return st;
+  if ((b->flags & ~(LA_SLOT_READ | LA_SLOT_WRITE)) != 0) return LA_ERR_INVALID_ARG;
+  *eff = *p;
+  if (b->cu_seqlens != nullptr) {
+    if (p->B != 1 || b->num_seqs < 1 || b->max_seqlen < 1 || b->max_seqlen > p->n) return LA_ERR_INVALID_ARG;
+    eff->B = b->num_seqs;
+    eff->n = b->max_seqlen;
+  } else if (b->num_seqs != p->B || b->max_seqlen != p->n) {
+    return LA_ERR_INVALID_ARG;
+  }
+  if (b->flags != 0 && b->num_slots < 1) return LA_ERR_INVALID_ARG;
+  return LA_OK;
+}
+}  // namespace
+
+la_status la_forward_batch_workspace_size(const la_problem* p, const la_batch* batch, const la_feature_map* fmap,
+                                          const la_gate* gate, size_t* bytes) {
+  if (bytes == nullptr) return LA_ERR_INVALID_ARG;
+  la_problem eff;
+  la_status st = check_batch(p, batch, fmap, gate, &eff);
+  if (st != LA_OK) return st;
+  *bytes = workspace_layout(&eff, fmap, 1, gate_kind(gate)).bytes;
+  return LA_OK;
+}
+
+la_status la_forward_batch(const la_problem* p, const la_batch* batch, const void* Q, const void* K, const void* V,
+                           const la_feature_map* fmap, const la_gate* gate, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  la_problem eff;
+  la_status st = check_batch(p, batch, fmap, gate, &eff);
+  if (st != LA_OK) return st;
+  if ((st = check_gate(gate, true)) != LA_OK) return st;
+  const int gk = gate_kind(gate);
+  if (Q == nullptr || K == nullptr || V == nullptr || out == nullptr) return LA_ERR_INVALID_ARG;
+  const bool slots = batch->flags != 0;
+  if (slots && (batch->S == nullptr || batch->z == nullptr || batch->slot_ids == nullptr)) return LA_ERR_INVALID_ARG;
+  for (const void* ptr : {Q, K, V, (const void*)out, (const void*)(slots ? batch->S : nullptr),
+                          (const void*)(slots ? batch->z : nullptr)})
+    if (ptr != nullptr && !aligned16(ptr)) return LA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(batch->cu_seqlens) & 3) != 0 ||
+      (slots && (reinterpret_cast<uintptr_t>(batch->slot_ids) & 3) != 0))
+    return LA_ERR_INVALID_ARG;
+
+  const size_t BH = (size_t)p->B * p->H, n = (size_t)p->n, r = (size_t)fmap->r;
+  const size_t isz = dtype_size(p->in_dtype);
+  const Range rq = range_of(Q, BH * n * p->d_k * isz), rk = range_of(K, BH * n * p->d_k * isz),
+              rv = range_of(V, BH * n * p->d_v * isz);
+  const Range rg = range_of(gk == LA_GATE_GLA ? gate->g : nullptr, BH * n * r * isz);
+  const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
+  const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
+  const Range rcu = range_of(batch->cu_seqlens, ((size_t)batch->num_seqs + 1) * 4);
+  const Range rsl = range_of(slots ? batch->slot_ids : nullptr, (size_t)batch->num_seqs * 4);
+  const size_t pool = slots ? (size_t)batch->num_slots * p->H : 0;
+  const Range rS = range_of(slots ? batch->S : nullptr, pool * r * p->d_v * 4),
+              rz = range_of(slots ? batch->z : nullptr, pool * r * 4);
+  const Range ro = range_of(out, BH * n * p->d_v * dtype_size(p->out_dtype));
+  const WsLayout wl = workspace_layout(&eff, fmap, 1, gk);
+  const Range rws = range_of(wl.bytes ? workspace : nullptr, wl.bytes);
+  for (Range o : {ro, rS, rz, rws})
+    for (Range i : {rq, rk, rv, rg, rgam, rom, rcu, rsl})
+      if (overlaps(o, i)) return LA_ERR_ALIAS;
+  if (overlaps(ro, rS) || overlaps(ro, rz) || overlaps(rS, rz) || overlaps(rws, ro) || overlaps(rws, rS) ||
+      overlaps(rws, rz))
+    return LA_ERR_ALIAS;
+  if (wl.bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < wl.bytes) return LA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return LA_ERR_WORKSPACE;
+  }
+
+  FwdPlan plan{};
+  plan.B = p->B;
+  plan.H = p->H;
+  plan.n = p->n;
+  plan.dk = p->d_k;
+  plan.dv = p->d_v;
+  plan.r = fmap->r;
+  plan.in_dtype = p->in_dtype;
+  plan.out_dtype = p->out_dtype;
+  plan.eps = p->eps;
+  plan.fmap = fmap->kind;
+  plan.gate = gk;
+  plan.causal = 1;
+  plan.tau = gk == LA_GATE_GLA ? gate->tau : 1.f;
+  plan.Q = Q;
+  plan.K = K;
+  plan.V = V;
+  plan.g = gk == LA_GATE_GLA ? gate->g : nullptr;
+  plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
+  plan.omega = fmap->omega;
+  plan.nseq = eff.B;
+  plan.cu = batch->cu_seqlens;
+  plan.slot = slots ? batch->slot_ids : nullptr;
+  plan.nslot = slots ? batch->num_slots : 0;
+  if (batch->flags & LA_SLOT_READ) {
+    plan.S0 = batch->S;
+    plan.z0 = batch->z;
+  }
+  if (batch->flags & LA_SLOT_WRITE) {
+    plan.S_final = batch->S;
+    plan.z_final = batch->z;
+  }
+  plan.out = out;
+  plan.stream = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  plan.ws_S = wl.bytes ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
+  plan.ws_z = wl.bytes ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
+  plan.ws_logG = (wl.bytes && gk == LA_GATE_GLA) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
+  plan_segments(eff.B, eff.H, eff.n, fmap->kind, fmap->r, p->d_v, p->d_k, gk, &plan.P, &plan.seg_len);
+  return fmap->kind == LA_FMAP_ELU1 ? launch_causal_elu1(plan) : launch_causal_favor(plan);
 }
 
 la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q, const void* k, const void* v,
@@ -449,6 +571,7 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.z0 = z0;
   plan.P = wl.P;
   plan.seg_len = wl.L;
+  plan.nseq = p->B;
   plan.stream = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   plan.ws_S = reinterpret_cast<float*>(ws + wl.S_off);

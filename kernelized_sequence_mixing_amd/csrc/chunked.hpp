@@ -63,9 +63,46 @@ struct CausalArgs {
   float* z_out;
   float* logG_out;         // pass 1, GLA: per-segment summed log-gates
   bf16* out;
+  // A batch of independent sequences: with cu, blockIdx.y = b H + h and
+  // sequence b is tokens cu[b] .. cu[b+1] of head h's n rows ([H][n][.]
+  // layout); without it, sequence (b, h) is rows (b H + h) n .. + n. The
+  // carried state of sequence b, head h is [.][H] entry slot[b] H + h (or
+  // b H + h without slot); slots outside [0, nslot) mean no carried state.
+  const int* cu;
+  const int* slot;
+  int nslot;
+  int in_is_state;         // S_in is the caller's carried state (indexed like S_out), not the segment workspace
   int H, n, P, seg_len;
   float eps, inv_tau;
 };
+
+// Rows, length and carried-state index of the sequence of workgroup row bh.
+// Offsets are clamped into [0, n] and lengths to the planned P seg_len, so a
+// malformed table cannot address memory outside the inputs and outputs.
+struct SeqView {
+  long long tok0;  // row of the first token
+  int len;         // tokens
+  long long st;    // carried-state index, -1 for none
+};
+__device__ __forceinline__ SeqView seq_view(const CausalArgs& a, long long bh) {
+  SeqView v;
+  const int b = int(bh / a.H), h = int(bh % a.H);
+  if (a.cu == nullptr) {
+    v.tok0 = bh * a.n;
+    v.len = a.n;
+  } else {
+    const int lo = min(max(a.cu[b], 0), a.n);
+    const int hi = min(max(a.cu[b + 1], lo), a.n);
+    v.tok0 = (long long)h * a.n + lo;
+    v.len = min(hi - lo, a.P * a.seg_len);
+  }
+  v.st = bh;
+  if (a.slot != nullptr) {
+    const int sl = a.slot[b];
+    v.st = (sl >= 0 && sl < a.nslot) ? (long long)sl * a.H + h : -1;
+  }
+  return v;
+}
 
 // Row padding (bf16 elements) of padded tiles: rows of 32, 64 or 128
 // elements plus 8 start 4 dwords apart modulo the banks.
@@ -507,9 +544,12 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
+  const SeqView sv = seq_view(a, bh);
   const int t_begin = s * a.seg_len;
-  const int t_end = min(a.n, t_begin + a.seg_len);
-  const long long tok0 = bh * a.n;
+  // only segments that a later segment of the same sequence follows
+  if (t_begin + a.seg_len >= sv.len) return;
+  const int t_end = min(sv.len, t_begin + a.seg_len);
+  const long long tok0 = sv.tok0;
   const int ebase = w * (E / NW);
   float lg2gam = 0.f;
   if constexpr (GATE == GT_DECAY) lg2gam = log2f(a.gamma[h]);
@@ -537,13 +577,13 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
   raw[1].load(a, tok0, t_begin + kChunk, t_end, lane, w);
   __builtin_amdgcn_sched_barrier(0);
   auto prelude = [&](Raw& rw, int ci, int half) {
-    const int L = min(kChunk, a.n - (t_begin + ci * kChunk));
+    const int L = min(kChunk, sv.len - (t_begin + ci * kChunk));
     chunk_prelude<R, E, DK, FMAP, GATE, false, NW, LY::SWZ>(rw, a, L, lg2gam, sm, 0, half * LY::HALF + LY::k_off, 0,
                                                    half * LY::HALF + LY::v_off, half * LY::HALF + LY::gam_off,
                                                    LY::logg_off, lane, w);
   };
   auto update = [&](int ci, int half) {
-    const int L = min(kChunk, a.n - (t_begin + ci * kChunk));
+    const int L = min(kChunk, sv.len - (t_begin + ci * kChunk));
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
     state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, half * LY::HALF + LY::k_off, half * LY::HALF + LY::v_off,
                                  half * LY::HALF + LY::gam_off, gsc, lane, w);
@@ -612,9 +652,11 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
+  const SeqView sv = seq_view(a, bh);
   const int t_begin = s * a.seg_len;
-  const int t_end = min(a.n, t_begin + a.seg_len);
-  const long long tok0 = bh * a.n;
+  if (s > 0 && t_begin >= sv.len) return;  // past the end of this sequence
+  const int t_end = min(sv.len, t_begin + a.seg_len);
+  const long long tok0 = sv.tok0;
   const int ebase = w * (E / NW);
   float lg2gam = 0.f;
   if constexpr (GATE == GT_DECAY) lg2gam = log2f(a.gamma[h]);
@@ -622,8 +664,10 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
   // ---- state carried in
   f32x4 S[R / 16][NEB];
   f32x4 Z[ZTiles<R, NW>::ZT];
-  if (a.S_in != nullptr) {
-    const float* Sp = a.S_in + bh * a.in_head + s * a.in_seg;
+  const long long in_idx = a.in_is_state ? sv.st : bh;
+  const bool has_in = a.S_in != nullptr && in_idx >= 0;
+  if (has_in) {
+    const float* Sp = a.S_in + in_idx * a.in_head + s * a.in_seg;
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
@@ -636,7 +680,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  z_load<R, NW>(Z, a.S_in != nullptr ? a.z_in + (bh * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
+  z_load<R, NW>(Z, has_in ? a.z_in + (in_idx * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
   z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
   // bf16 image of the state as the A operand of O^T += S^T Q^^T: k-slot j of
   // lane (g, c) is feature 32p + 4g + j (j < 4) or 32p + 16 + 4g + (j - 4).
@@ -656,13 +700,13 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
   constexpr int DEPTH = 1;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw0, raw1;
-  raw0.load(a, tok0, t_begin, t_end, lane, w);
+  if (sv.len > 0) raw0.load(a, tok0, t_begin, t_end, lane, w);  // an empty sequence reads nothing
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order: buffer 0's loads complete first
   if constexpr (DEPTH == 2) raw1.load(a, tok0, t_begin + kChunk, t_end, lane, w);
   auto step = [&](Raw& raw, int ci) {
     const int t0 = t_begin + ci * kChunk;
     const bool live = ci < nch;
-    const int L = min(kChunk, a.n - t0);
+    const int L = min(kChunk, sv.len - t0);
     if (live)
       chunk_prelude<R, E, DK, FMAP, GATE, true, NW, LY::SWZ>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
                                                     LY::v_off, LY::gam_off, 0, lane, w);
@@ -778,15 +822,16 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
     for (int ci = 0; ci < nch; ++ci) step(raw0, ci);
   }
 
-  if (a.S_out != nullptr && s == a.P - 1) {
-    float* So = a.S_out + bh * R * E;
+  // the sequence's last segment stores its final state
+  if (a.S_out != nullptr && sv.st >= 0 && s == (sv.len > 0 ? (sv.len - 1) / a.seg_len : 0)) {
+    float* So = a.S_out + sv.st * R * E;
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
-    z_store<R, NW>(Z, a.z_out + bh * R, lane, w);
+    z_store<R, NW>(Z, a.z_out + sv.st * R, lane, w);
   }
 }
 
@@ -801,13 +846,16 @@ la_status run_causal(const FwdPlan& p) {
   a.omega = static_cast<const bf16*>(p.omega);
   a.gamma = p.gamma;
   a.out = static_cast<bf16*>(p.out);
+  a.cu = p.cu;
+  a.slot = p.slot;
+  a.nslot = p.nslot;
   a.H = p.H;
   a.n = p.n;
   a.P = p.P;
   a.seg_len = p.seg_len;
   a.eps = p.eps;
   a.inv_tau = GATE == GT_GLA ? 1.f / p.tau : 0.f;
-  const unsigned BH = unsigned(p.B) * unsigned(p.H);
+  const unsigned BH = unsigned(p.nseq) * unsigned(p.H);
 
   if (p.P > 1) {
     CausalArgs a1 = a;
@@ -832,6 +880,7 @@ la_status run_causal(const FwdPlan& p) {
     a.z_in = p.z0;
     a.in_head = (long long)R * E;
     a.in_seg = 0;
+    a.in_is_state = 1;
   }
   a.S_out = p.S_final;
   a.z_out = p.z_final;

@@ -368,9 +368,12 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
+  const SeqView sv = seq_view(a, bh);
   const int t_begin = s * a.seg_len;
-  const int t_end = min(a.n, t_begin + a.seg_len);
-  const long long tok0 = bh * a.n;
+  // only segments that a later segment of the same sequence follows
+  if (t_begin + a.seg_len >= sv.len) return;
+  const int t_end = min(sv.len, t_begin + a.seg_len);
+  const long long tok0 = sv.tok0;
   const int ebase = w * (E / 4);
   float lg2gam = 0.f;
   if constexpr (GATE == GT_DECAY) lg2gam = log2f(a.gamma[h]);
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   bf16x8 om[F::FT][DK / 32];
   favor_load_omega<R, DK>(om, a.omega, 0, LN(lane));
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const int L = min(kChunk, a.n - t0);
+    const int L = min(kChunk, sv.len - t0);
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
     bf16x8 xk[DK / 32];
     const float shk = favor_take_x<R, DK>(raw.xk, xk);
@@ -433,17 +436,21 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   const int s = blockIdx.x;
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
+  const SeqView sv = seq_view(a, bh);
   const int t_begin = s * a.seg_len;
-  const int t_end = min(a.n, t_begin + a.seg_len);
-  const long long tok0 = bh * a.n;
+  if (s > 0 && t_begin >= sv.len) return;  // past the end of this sequence
+  const int t_end = min(sv.len, t_begin + a.seg_len);
+  const long long tok0 = sv.tok0;
   const int ebase = w * (E / 4);
   float lg2gam = 0.f;
   if constexpr (GATE == GT_DECAY) lg2gam = log2f(a.gamma[h]);
 
   f32x4 S[R / 16][NEB];
   f32x4 Z[F::NFB];
-  if (a.S_in != nullptr) {
-    const float* Sp = a.S_in + bh * a.in_head + s * a.in_seg;
+  const long long in_idx = a.in_is_state ? sv.st : bh;
+  const bool has_in = a.S_in != nullptr && in_idx >= 0;
+  if (has_in) {
+    const float* Sp = a.S_in + in_idx * a.in_head + s * a.in_seg;
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
@@ -456,7 +463,7 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) S[rt][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  favor_z_load<R>(Z, a.S_in != nullptr ? a.z_in + (bh * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
+  favor_z_load<R>(Z, has_in ? a.z_in + (in_idx * a.in_head + s * a.in_seg) / E : nullptr, lane, w);
   favor_z_publish<R>(Z, sm, LY::zh_off, LY::zl_off, lane, w);
   // partial row sums of query tiles this wave holds no score tile of stay zero
   lds<float>(sm, LY::rsp_off + 4 * tid) = 0.f;
@@ -467,11 +474,11 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   score_tiles(w, sqi, skj);
 
   RawChunk<R, E, DK, FM_FAVOR, GT_NONE, true> raw;
-  raw.load(a, tok0, t_begin, t_end, lane, w);
+  if (sv.len > 0) raw.load(a, tok0, t_begin, t_end, lane, w);  // an empty sequence reads nothing
   bf16x8 om[F::FT][DK / 32];
   favor_load_omega<R, DK>(om, a.omega, 0, LN(lane));
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const int L = min(kChunk, a.n - t0);
+    const int L = min(kChunk, sv.len - t0);
     bf16x8 xq[DK / 32], xk[DK / 32];
     const float shq = favor_take_x<R, DK>(raw.xq, xq), shk = favor_take_x<R, DK>(raw.xk, xk);
     favor_write_v<E>(raw.v, sm, LY::v_off, lane, w);
@@ -623,15 +630,16 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
     favor_z_publish<R>(Z, sm, LY::zh_off, LY::zl_off, lane, w);
   }
 
-  if (a.S_out != nullptr && s == a.P - 1) {
-    float* So = a.S_out + bh * R * E;
+  // the sequence's last segment stores its final state
+  if (a.S_out != nullptr && sv.st >= 0 && s == (sv.len > 0 ? (sv.len - 1) / a.seg_len : 0)) {
+    float* So = a.S_out + sv.st * R * E;
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
-    favor_z_store<R>(Z, a.z_out + bh * R, lane, w);
+    favor_z_store<R>(Z, a.z_out + sv.st * R, lane, w);
   }
 }
 
@@ -644,12 +652,15 @@ la_status run_causal_favor(const FwdPlan& p) {
   a.omega = static_cast<const bf16*>(p.omega);
   a.gamma = p.gamma;
   a.out = static_cast<bf16*>(p.out);
+  a.cu = p.cu;
+  a.slot = p.slot;
+  a.nslot = p.nslot;
   a.H = p.H;
   a.n = p.n;
   a.P = p.P;
   a.seg_len = p.seg_len;
   a.eps = p.eps;
-  const unsigned BH = unsigned(p.B) * unsigned(p.H);
+  const unsigned BH = unsigned(p.nseq) * unsigned(p.H);
   if (p.P > 1) {
     CausalArgs a1 = a;
     a1.S_out = p.ws_S;
@@ -672,6 +683,7 @@ la_status run_causal_favor(const FwdPlan& p) {
     a.z_in = p.z0;
     a.in_head = (long long)R * E;
     a.in_seg = 0;
+    a.in_is_state = 1;
   }
   a.S_out = p.S_final;
   a.z_out = p.z_final;

@@ -40,6 +40,13 @@ struct FwdPlan {
   void* out;
   // causal segmentation: P segments of seg_len tokens (multiple of kChunk)
   int P, seg_len;
+  // a batch of sequences (la_forward_batch): nseq sequences (= B without cu);
+  // cu: device [nseq + 1] offsets along n (B == 1), slot: device [nseq] state
+  // slots of S0 / S_final ([nslot][H][r][d_v]); both null for la_forward
+  int nseq;
+  const int* cu;
+  const int* slot;
+  int nslot;
   // non-causal split of the sequence into partial sums
   int splits, split_len;
   // workspace carve (device)

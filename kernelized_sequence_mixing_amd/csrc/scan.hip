@@ -16,7 +16,8 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S
                                                            const float* __restrict__ logG,
                                                            const float* __restrict__ S0,
                                                            const float* __restrict__ z0,
-                                                           const float* __restrict__ gamma, int H, int P,
+                                                           const float* __restrict__ gamma,
+                                                           const int* __restrict__ slot, int nslot, int H, int P,
                                                            int R, int E, int seg_len, int gate, int reverse) {
   const long long bh = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -27,7 +28,13 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S
   float* base = is_z ? z + bh * P * R + row : S + bh * P * RE + idx;
   const long long stride = is_z ? R : RE;
   float cur = 0.f;
-  if (S0 != nullptr && !reverse) cur = is_z ? z0[bh * R + row] : S0[bh * RE + idx];
+  // the carried-in state of this (sequence, head): its slot's entry, if any
+  long long st = bh;
+  if (slot != nullptr) {
+    const int sl = slot[bh / H];
+    st = (sl >= 0 && sl < nslot) ? (long long)sl * H + bh % H : -1;
+  }
+  if (S0 != nullptr && !reverse && st >= 0) cur = is_z ? z0[st * R + row] : S0[st * RE + idx];
   float seg_decay = 1.f;
   if (gate == GT_DECAY) seg_decay = exp2f(float(seg_len) * log2f(gamma[bh % H]));
   // Batches of 8 segments: all loads of a batch are issued before the chain
@@ -56,17 +63,17 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S
 
 la_status launch_segment_scan(const FwdPlan& p) {
   const int items = p.r * p.dv + p.r;
-  dim3 grid((items + 255) / 256, unsigned(p.B) * unsigned(p.H));
+  dim3 grid((items + 255) / 256, unsigned(p.nseq) * unsigned(p.H));
   hipLaunchKernelGGL(segment_scan_kernel, grid, dim3(256), 0, p.stream, p.ws_S, p.ws_z, p.ws_logG, p.S0, p.z0,
-                     p.gamma, p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 0);
+                     p.gamma, p.slot, p.nslot, p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 0);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
 la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG) {
   const int items = p.r * p.dv + p.r;
-  dim3 grid((items + 255) / 256, unsigned(p.B) * unsigned(p.H));
+  dim3 grid((items + 255) / 256, unsigned(p.nseq) * unsigned(p.H));
   hipLaunchKernelGGL(segment_scan_kernel, grid, dim3(256), 0, p.stream, S, z, logG, nullptr, nullptr, p.gamma,
-                     p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 1);
+                     nullptr, 0, p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 1);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 

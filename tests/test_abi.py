@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     lib = N.lib()
-    assert lib.la_abi_version() == 2
+    assert lib.la_abi_version() == 3
     names = [lib.la_status_str(i).decode() for i in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_ALIAS",
                      "LA_ERR_HIP"]
@@ -63,6 +63,9 @@ int main(void) {{
   printf("%zu %zu %zu\\n", sizeof(la_problem), offsetof(la_problem, eps), offsetof(la_problem, out_dtype));
   printf("%zu %zu %zu\\n", sizeof(la_feature_map), offsetof(la_feature_map, r), offsetof(la_feature_map, omega));
   printf("%zu %zu %zu %zu\\n", sizeof(la_gate), offsetof(la_gate, tau), offsetof(la_gate, gamma), offsetof(la_gate, g));
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(la_batch), offsetof(la_batch, cu_seqlens),
+         offsetof(la_batch, num_seqs), offsetof(la_batch, max_seqlen), offsetof(la_batch, S), offsetof(la_batch, z),
+         offsetof(la_batch, slot_ids), offsetof(la_batch, num_slots), offsetof(la_batch, flags));
   return 0;
 }}""")
     exe = tmp_path / "layout"
@@ -72,6 +75,9 @@ int main(void) {{
     assert c[0] == [ctypes.sizeof(N.LaProblem), N.LaProblem.eps.offset, N.LaProblem.out_dtype.offset]
     assert c[1] == [ctypes.sizeof(N.LaFeatureMap), N.LaFeatureMap.r.offset, N.LaFeatureMap.omega.offset]
     assert c[2] == [ctypes.sizeof(N.LaGate), N.LaGate.tau.offset, N.LaGate.gamma.offset, N.LaGate.g.offset]
+    B = N.LaBatch
+    assert c[3] == [ctypes.sizeof(B), B.cu_seqlens.offset, B.num_seqs.offset, B.max_seqlen.offset, B.S.offset,
+                    B.z.offset, B.slot_ids.offset, B.num_slots.offset, B.flags.offset]
 
 
 # ------------------------------------------------------------------ planning (host arithmetic)
@@ -289,3 +295,74 @@ def test_backward_workspace_size():
     assert size(4, 16, n, 64, 64, N.LA_GATE_DECAY) == size(4, 16, n, 64, 64)
     # GLA adds dQ~ . Q~ per token and feature (fp32) and the segments' summed log-gates
     assert size(4, 16, n, 64, 64, N.LA_GATE_GLA) == size(4, 16, n, 64, 64) + BH * n * 64 * 4 + zs
+
+
+# ------------------------------------------------------------------ serving batch (validation, no launch)
+
+def _batch_call(a, cu=None, num_seqs=None, max_seqlen=None, S=FAKE + 20 * SP, z=FAKE + 21 * SP,
+                slot_ids=FAKE + 22 * SP, num_slots=8, flags=3, out=None):
+    p = N.LaProblem(a["B"], a["H"], a["n"], a["d_k"], a["d_v"], a["in_dt"], a["out_dt"], a["eps"])
+    f = N.LaFeatureMap(a["fkind"], a["r"], a["omega"])
+    g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"])
+    b = N.LaBatch(cu, a["B"] if num_seqs is None else num_seqs, a["n"] if max_seqlen is None else max_seqlen, S, z,
+                  slot_ids, num_slots, flags)
+    return N.lib().la_forward_batch(ctypes.byref(p), ctypes.byref(b), a["Q"], a["K"], a["V"], ctypes.byref(f),
+                                    ctypes.byref(g), a["out"] if out is None else out, a["ws"], a["ws_bytes"], None)
+
+
+BAD_BATCH = [
+    ("num_seqs != B", {}, dict(num_seqs=3), N.LA_ERR_INVALID_ARG),
+    ("max_seqlen != n", {}, dict(max_seqlen=50), N.LA_ERR_INVALID_ARG),
+    ("cu with B 2", {}, dict(cu=FAKE + 23 * SP, num_seqs=4, max_seqlen=50), N.LA_ERR_INVALID_ARG),
+    ("cu num_seqs 0", dict(B=1), dict(cu=FAKE + 23 * SP, num_seqs=0, max_seqlen=50), N.LA_ERR_INVALID_ARG),
+    ("cu max_seqlen 0", dict(B=1), dict(cu=FAKE + 23 * SP, num_seqs=4, max_seqlen=0), N.LA_ERR_INVALID_ARG),
+    ("cu max_seqlen > n", dict(B=1), dict(cu=FAKE + 23 * SP, num_seqs=4, max_seqlen=101), N.LA_ERR_INVALID_ARG),
+    ("cu misaligned", dict(B=1), dict(cu=FAKE + 23 * SP + 2, num_seqs=4, max_seqlen=50), N.LA_ERR_INVALID_ARG),
+    ("bad flags", {}, dict(flags=4), N.LA_ERR_INVALID_ARG),
+    ("no slots", {}, dict(num_slots=0), N.LA_ERR_INVALID_ARG),
+    ("S null", {}, dict(S=None), N.LA_ERR_INVALID_ARG),
+    ("slot_ids null", {}, dict(slot_ids=None), N.LA_ERR_INVALID_ARG),
+    ("S misaligned", {}, dict(S=FAKE + 20 * SP + 8), N.LA_ERR_INVALID_ARG),
+    ("noncausal-only dtype", dict(in_dt=N.LA_F32, out_dt=N.LA_F32), {}, N.LA_ERR_UNSUPPORTED),
+    ("pool over Q", {}, dict(S=FAKE + 256), N.LA_ERR_ALIAS),
+    ("pool over out", {}, dict(z=FAKE + 3 * SP + 256), N.LA_ERR_ALIAS),
+    ("out over cu", dict(B=1), dict(cu=FAKE + 3 * SP, num_seqs=4, max_seqlen=50), N.LA_ERR_ALIAS),
+    ("pool over slot ids", {}, dict(slot_ids=FAKE + 20 * SP + 64), N.LA_ERR_ALIAS),
+    ("ws small", dict(ws_bytes=16), {}, N.LA_ERR_WORKSPACE),
+]
+
+
+@needs_lib
+@no_gpu
+@pytest.mark.parametrize("name,over,kw,want", BAD_BATCH, ids=[b[0] for b in BAD_BATCH])
+def test_batch_rejects(name, over, kw, want):
+    assert _batch_call(_args(**over), **kw) == want
+
+
+@needs_lib
+def test_batch_workspace_size():
+    """A ragged batch is planned as num_seqs sequences of max_seqlen tokens;
+    without slots or cu_seqlens it needs what la_forward needs."""
+    lib = N.lib()
+
+    def size(B, n, cu, num_seqs, max_seqlen, flags=0):
+        p = N.LaProblem(B, 16, n, 64, 64, N.LA_BF16, N.LA_BF16, 1e-6)
+        f = N.LaFeatureMap(N.LA_FMAP_ELU1, 64, None)
+        g = N.LaGate(N.LA_GATE_NONE, 16.0, None, None)
+        b = N.LaBatch(cu, num_seqs, max_seqlen, None, None, None, 1, flags)
+        out = ctypes.c_size_t(0)
+        assert lib.la_forward_batch_workspace_size(ctypes.byref(p), ctypes.byref(b), ctypes.byref(f),
+                                                   ctypes.byref(g), ctypes.byref(out)) == N.LA_OK
+        return out.value
+
+    def fwd(B, n):
+        p = N.LaProblem(B, 16, n, 64, 64, N.LA_BF16, N.LA_BF16, 1e-6)
+        f = N.LaFeatureMap(N.LA_FMAP_ELU1, 64, None)
+        g = N.LaGate(N.LA_GATE_NONE, 16.0, None, None)
+        out = ctypes.c_size_t(0)
+        assert lib.la_forward_workspace_size(ctypes.byref(p), ctypes.byref(f), 1, ctypes.byref(g),
+                                             ctypes.byref(out)) == N.LA_OK
+        return out.value
+    assert size(4, 4096, None, 4, 4096) == fwd(4, 4096)
+    assert size(1, 40000, FAKE, 10, 4096) == fwd(10, 4096)
+    assert size(1, 40000, FAKE, 64, 128) == fwd(64, 128) == 0   # one segment per sequence: no workspace
