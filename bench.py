@@ -30,6 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 from workloads import WORKLOADS, HEADLINE, make_inputs  # noqa: E402
@@ -187,6 +188,64 @@ def bench_decode(wl, steps, warmup):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def bench_serve_prefill(steps, warmup, num_seqs=32, H=16, d=64):
+    """la_forward_batch over a ragged prefill: num_seqs sequences of a seeded
+    log-uniform length mix (64 .. 8192 tokens) packed along n, causal elu+1,
+    each storing its final state in its slot. Bytes per head-token as the
+    headline (q, k, v read, o written) plus each sequence's stored state."""
+    import kernelized_sequence_mixing_amd as ksm
+    from workloads import serving_lengths
+    lens = serving_lengths(num_seqs, seed=7)
+    T = int(lens.sum())
+    wl = WORKLOADS["causal_elu1"].resized(name="serve_prefill", B=1, H=H, n=T, d_k=d, d_v=d, r=d)
+    inp = make_inputs(wl, seed=0)
+    inp["cu"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    inp["ids"] = torch.arange(num_seqs, dtype=torch.int32)
+    state_bytes = num_seqs * H * (d * d + d) * 4
+    per_set = H * T * 4 * 2 * d + state_bytes
+    sets = _device_sets(inp, ["Q", "K", "V", "cu", "ids"], per_set)
+    stream = torch.cuda.current_stream()
+    pools = [(torch.empty((num_seqs, H, d, d), dtype=torch.float32, device="cuda"),
+              torch.empty((num_seqs, H, d), dtype=torch.float32, device="cuda")) for _ in sets]
+    calls = [ksm.PreparedForwardBatch(s["Q"], s["K"], s["V"], cu_seqlens=s["cu"], max_seqlen=int(lens.max()),
+                                      state=pools[i], slot_ids=s["ids"], write=True, eps=wl.eps, stream=stream)
+             for i, s in enumerate(sets)]
+    ms, med = time_steps(lambda i: calls[i](), len(sets), steps, warmup, stream)
+    gbs = per_set / (ms * 1e-3) / 1e9
+    return {"workload": "serve_prefill_ragged", "ms_per_step": round(ms, 5), "median_ms": round(med, 5),
+            "value": H * T / (ms * 1e-3), "unit": "head-tokens/s", "input_sets_rotated": len(sets),
+            "hbm_alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_step": per_set,
+            "shape": {"num_seqs": num_seqs, "tokens": T, "H": H, "d_k": d, "d_v": d, "min_len": int(lens.min()),
+                      "max_len": int(lens.max()), "gate": "none", "feature_map": "elu+1"}}
+
+
+def bench_serve_decode(wl, m, steps, warmup):
+    """la_forward_batch as a decode step of m tokens for each of B sequences
+    (the GLA decode configuration), every sequence reading and writing its
+    state slot in place. Bytes per step: each head's state read and written,
+    plus m tokens of q, k, v, g read and o written."""
+    import kernelized_sequence_mixing_amd as ksm
+    B, H, r, dv, dk = wl.B, wl.H, wl.r, wl.d_v, wl.d_k
+    base = WORKLOADS["gla_gate"].resized(name=f"serve_decode_m{m}", B=B, H=H, n=m)
+    inp = make_inputs(base, seed=0)
+    dec = make_inputs(wl, seed=0)
+    inp["S"], inp["z"] = dec["S0"], dec["z0"]
+    inp["ids"] = torch.arange(B, dtype=torch.int32)
+    per_head = 2 * (r * dv + r) * 4 + m * 2 * (2 * dk + dv + r) + m * 2 * dv
+    per_step = B * H * per_head
+    sets = _device_sets(inp, ["Q", "K", "V", "g", "S", "z", "ids"], per_step)
+    stream = torch.cuda.current_stream()
+    calls = [ksm.PreparedForwardBatch(s["Q"], s["K"], s["V"], state=(s["S"], s["z"]), slot_ids=s["ids"], read=True,
+                                      write=True, gate=("gla", s["g"], wl.tau), eps=wl.eps, stream=stream)
+             for s in sets]
+    ms, med = time_steps(lambda i: calls[i](), len(sets), steps, warmup, stream)
+    gbs = per_step / (ms * 1e-3) / 1e9
+    return {"workload": f"serve_decode_slots_m{m}", "ms_per_step": round(ms, 5), "median_ms": round(med, 5),
+            "value": B * H * m / (ms * 1e-3), "unit": "head-tokens/s", "input_sets_rotated": len(sets),
+            "alg_bytes_per_step": per_step, "hbm_alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "shape": {"B": B, "H": H, "m": m, "r": r, "d_v": dv, "gate": "gla"}}
+
+
 def backward_algorithmic_per_token(wl):
     """(bytes, matrix-core flops) per head-token of the causal backward pass.
 
@@ -326,6 +385,9 @@ def main():
         for name in ("noncausal_elu1_f32", "retnet_decay", "gla_gate", "favor_causal"):
             extra.append(bench_forward(WORKLOADS[name], args.steps, args.warmup))
         extra.append(bench_decode(WORKLOADS["gla_decode"], args.steps, args.warmup))
+        extra.append(bench_serve_prefill(args.steps, args.warmup))
+        for m in (1, 4):
+            extra.append(bench_serve_decode(WORKLOADS["gla_decode"], m, args.steps, args.warmup))
         extra.append(bench_backward(WORKLOADS["causal_elu1"], args.steps, args.warmup))
         # the GLA workload's sequence shape at d_k = d_v = 64 (no backward build for 128 x 128 states)
         extra.append(bench_backward(WORKLOADS["gla_gate"].resized(name="gla_gate_d64", d_k=64, d_v=64, r=64,

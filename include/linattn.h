@@ -197,6 +197,12 @@ la_status la_forward_batch_workspace_size(const la_problem* p, const la_batch* b
  * outputs for the shared tokens.
  * Slot ids must be distinct within a call when LA_SLOT_WRITE is set (two
  * sequences writing one slot race).
+ * A batch of one token per sequence (no cu_seqlens, p->n == 1) runs the
+ * recurrent step of la_decode_step (fp32 arithmetic, one read and one write of
+ * each state) on the slots; longer steps and prefills run the chunked kernels.
+ * A ragged batch is planned from p->n and max_seqlen (the lengths stay on the
+ * device): segments sized for about one round of workgroups over all
+ * sequences, as many as the longest sequence needs.
  * Supported: as la_forward with causal == 1. Errors: LA_ERR_INVALID_ARG for a
  * malformed batch (num_seqs, max_seqlen, flags, B != 1 with cu_seqlens, NULL
  * pool pointers with flags set); LA_ERR_ALIAS when out, the pool or the

@@ -84,12 +84,9 @@ bool shapes_built(const la_feature_map* f, int dk, int dv, bool causal) {
   return (long long)f->r * dv <= 16384;
 }
 
-// Segments per head for the causal form: enough (head, segment) workgroups to
-// fill every CU with as many output-pass workgroups as its LDS holds (at most
-// kMaxGroupsPerCU), each segment a whole number of chunks.
-void plan_segments(int B, int H, int n, int fmap, int r, int dv, int dk, int gate, int* P, int* seg_len) {
-  const int nchunks = (n + kChunk - 1) / kChunk;
-  const long long BH = (long long)B * H;
+// Output-pass workgroups the GPU holds at once: every CU with as many as its
+// LDS fits, at most kMaxGroupsPerCU.
+long long resident_groups(int fmap, int r, int dv, int dk, int gate) {
   const int lds = causal_output_lds_bytes(fmap, r, dv, dk, gate);
   int per_cu = lds > 0 ? kLdsPerCU / lds : 1;
   if (per_cu < 1) per_cu = 1;
@@ -98,13 +95,39 @@ void plan_segments(int B, int H, int n, int fmap, int r, int dv, int dk, int gat
   // a third of a lane's 512 registers, and the output pass runs one
   // workgroup per CU
   if (fmap == LA_FMAP_ELU1 && (long long)r * dv >= 128 * 128) per_cu = 1;
-  const long long target = (long long)kComputeUnits * per_cu;
+  return (long long)kComputeUnits * per_cu;
+}
+
+// Segments per head for the causal form: enough (head, segment) workgroups to
+// fill the resident workgroup slots, each segment a whole number of chunks.
+void plan_segments(int B, int H, int n, int fmap, int r, int dv, int dk, int gate, int* P, int* seg_len) {
+  const int nchunks = (n + kChunk - 1) / kChunk;
+  const long long BH = (long long)B * H;
+  const long long target = resident_groups(fmap, r, dv, dk, gate);
   long long want = (target + BH - 1) / BH;
   if (want < 1) want = 1;
   if (want > nchunks) want = nchunks;
   const int seg_chunks = int((nchunks + want - 1) / want);
   *P = (nchunks + seg_chunks - 1) / seg_chunks;
   *seg_len = seg_chunks * kChunk;
+}
+
+// Segments for a ragged batch (la_forward_batch with cu_seqlens): the lengths
+// live on the device, so the plan takes the total (at most total / 64 + nseq
+// chunks over all sequences) and the longest: segments of equal length sized
+// so that all sequences' segments give about one round of workgroups, and P
+// segments cover the longest sequence. Sequences shorter than P segments
+// leave the rest of their workgroups idle (they exit at once).
+void plan_segments_ragged(int nseq, int H, int total, int max_len, int fmap, int r, int dv, int dk, int gate, int* P,
+                          int* seg_len) {
+  const long long target = resident_groups(fmap, r, dv, dk, gate);
+  const long long chunks = ((long long)total + kChunk - 1) / kChunk + nseq;
+  const int max_chunks = (max_len + kChunk - 1) / kChunk;
+  long long seg_chunks = (chunks * H + target - 1) / target;
+  if (seg_chunks < 1) seg_chunks = 1;
+  if (seg_chunks > max_chunks) seg_chunks = max_chunks;
+  *P = int((max_chunks + seg_chunks - 1) / seg_chunks);
+  *seg_len = int(seg_chunks) * kChunk;
 }
 
 void plan_splits(int B, int H, int n, int* splits, int* split_len) {
@@ -122,26 +145,30 @@ struct WsLayout {
   size_t S_off, z_off, logG_off, bytes;
 };
 
-WsLayout workspace_layout(const la_problem* p, const la_feature_map* f, int causal, int gate) {
+// Segment states (and GLA log-gates) of BH sequences cut into `pieces`.
+WsLayout workspace_pieces(size_t BH, size_t pieces, size_t r, size_t dv, bool gla) {
   WsLayout w{0, 0, 0, 0};
+  w.S_off = 0;
+  w.z_off = round_up(BH * pieces * r * dv * 4, kAlign);
+  w.logG_off = round_up(w.z_off + BH * pieces * r * 4, kAlign);
+  w.bytes = gla ? round_up(w.logG_off + BH * pieces * r * 4, kAlign) : w.logG_off;
+  return w;
+}
+
+WsLayout workspace_layout(const la_problem* p, const la_feature_map* f, int causal, int gate) {
   const size_t BH = (size_t)p->B * p->H;
   size_t pieces;
   if (causal) {
     int P, L;
     plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate, &P, &L);
-    if (P <= 1) return w;
+    if (P <= 1) return WsLayout{0, 0, 0, 0};
     pieces = (size_t)P;
   } else {
     int sp, L;
     plan_splits(p->B, p->H, p->n, &sp, &L);
     pieces = (size_t)sp;
   }
-  const size_t r = (size_t)f->r;
-  w.S_off = 0;
-  w.z_off = round_up(BH * pieces * r * p->d_v * 4, kAlign);
-  w.logG_off = round_up(w.z_off + BH * pieces * r * 4, kAlign);
-  w.bytes = (causal && gate == LA_GATE_GLA) ? round_up(w.logG_off + BH * pieces * r * 4, kAlign) : w.logG_off;
-  return w;
+  return workspace_pieces(BH, pieces, f->r, p->d_v, causal && gate == LA_GATE_GLA);
 }
 
 // Validation shared by la_forward and its size queries (no pointers inspected).
@@ -337,8 +364,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
 
 namespace {
 // Validation of a batch description shared by la_forward_batch and its size
-// query; *eff gets the problem the segment planner sees (num_seqs sequences
-// of max_seqlen tokens).
+// query; *eff gets num_seqs sequences of max_seqlen tokens.
 la_status check_batch(const la_problem* p, const la_batch* b, const la_feature_map* f, const la_gate* g,
                       la_problem* eff) {
   if (b == nullptr) return LA_ERR_INVALID_ARG;
@@ -356,6 +382,17 @@ la_status check_batch(const la_problem* p, const la_batch* b, const la_feature_m
   if (b->flags != 0 && b->num_slots < 1) return LA_ERR_INVALID_ARG;
   return LA_OK;
 }
+
+// Segment plan and workspace of a validated batch.
+WsLayout batch_plan(const la_problem* p, const la_batch* b, const la_problem& eff, const la_feature_map* f, int gate,
+                    int* P, int* seg_len) {
+  if (b->cu_seqlens != nullptr)
+    plan_segments_ragged(eff.B, p->H, p->n, eff.n, f->kind, f->r, p->d_v, p->d_k, gate, P, seg_len);
+  else
+    plan_segments(eff.B, p->H, eff.n, f->kind, f->r, p->d_v, p->d_k, gate, P, seg_len);
+  if (*P <= 1) return WsLayout{0, 0, 0, 0};
+  return workspace_pieces((size_t)eff.B * p->H, (size_t)*P, f->r, p->d_v, gate == LA_GATE_GLA);
+}
 }  // namespace
 
 la_status la_forward_batch_workspace_size(const la_problem* p, const la_batch* batch, const la_feature_map* fmap,
@@ -364,7 +401,8 @@ la_status la_forward_batch_workspace_size(const la_problem* p, const la_batch* b
   la_problem eff;
   la_status st = check_batch(p, batch, fmap, gate, &eff);
   if (st != LA_OK) return st;
-  *bytes = workspace_layout(&eff, fmap, 1, gate_kind(gate)).bytes;
+  int P, L;
+  *bytes = batch_plan(p, batch, eff, fmap, gate_kind(gate), &P, &L).bytes;
   return LA_OK;
 }
 
@@ -399,7 +437,8 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   const Range rS = range_of(slots ? batch->S : nullptr, pool * r * p->d_v * 4),
               rz = range_of(slots ? batch->z : nullptr, pool * r * 4);
   const Range ro = range_of(out, BH * n * p->d_v * dtype_size(p->out_dtype));
-  const WsLayout wl = workspace_layout(&eff, fmap, 1, gk);
+  int P, seg_len;
+  const WsLayout wl = batch_plan(p, batch, eff, fmap, gk, &P, &seg_len);
   const Range rws = range_of(wl.bytes ? workspace : nullptr, wl.bytes);
   for (Range o : {ro, rS, rz, rws})
     for (Range i : {rq, rk, rv, rg, rgam, rom, rcu, rsl})
@@ -450,7 +489,38 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   plan.ws_S = wl.bytes ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
   plan.ws_z = wl.bytes ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
   plan.ws_logG = (wl.bytes && gk == LA_GATE_GLA) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
-  plan_segments(eff.B, eff.H, eff.n, fmap->kind, fmap->r, p->d_v, p->d_k, gk, &plan.P, &plan.seg_len);
+  plan.P = P;
+  plan.seg_len = seg_len;
+  if (batch->cu_seqlens == nullptr && p->n == 1) {
+    // one token per sequence: the recurrent step kernel streams each state once
+    DecodePlan dp{};
+    dp.B = p->B;
+    dp.H = p->H;
+    dp.dk = p->d_k;
+    dp.dv = p->d_v;
+    dp.r = fmap->r;
+    dp.in_dtype = p->in_dtype;
+    dp.out_dtype = p->out_dtype;
+    dp.eps = p->eps;
+    dp.fmap = fmap->kind;
+    dp.gate = gk;
+    dp.tau = plan.tau;
+    dp.S = batch->S;
+    dp.z = batch->z;
+    dp.q = Q;
+    dp.k = K;
+    dp.v = V;
+    dp.g = plan.g;
+    dp.gamma = plan.gamma;
+    dp.omega = fmap->omega;
+    dp.out = out;
+    dp.slot = plan.slot;
+    dp.nslot = plan.nslot;
+    dp.flags = batch->flags;
+    dp.stream = plan.stream;
+    const la_status ds = launch_decode(dp);
+    if (ds != LA_ERR_UNSUPPORTED) return ds;
+  }
   return fmap->kind == LA_FMAP_ELU1 ? launch_causal_elu1(plan) : launch_causal_favor(plan);
 }
 
@@ -501,6 +571,7 @@ la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
   plan.omega = fmap->omega;
   plan.out = out;
+  plan.flags = 3;
   plan.stream = static_cast<hipStream_t>(stream);
   return launch_decode(plan);
 }

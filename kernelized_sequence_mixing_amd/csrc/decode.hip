@@ -10,6 +10,9 @@
 // (row group, column quad) owns float4 column quads of R/(256/(E/4)) rows, all
 // loads issued before the prologue so the whole state is in flight while the
 // features are computed; the read-out reduction over rows goes through LDS.
+// The states may live in a pool of slots (la_forward_batch with one token per
+// sequence): then the head's state is slot[b] H + h, read and/or written as
+// the flags say, and a slot outside the pool means a zero state, not stored.
 #include "vec_common.hpp"
 
 namespace la {
@@ -26,6 +29,8 @@ struct DecodeArgs {
   void* out;
   int H, in_dt, out_dt, gate;
   float eps, inv_tau;
+  const int* slot;  // nullable: state index = b H + h
+  int nslot, flags;  // flags: 1 read the state, 2 write it back
 };
 
 template <int R, int E, int DK, int FMAP, typename InT>
@@ -53,11 +58,23 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const int iq = min(tid, DK - 1), iv = min(tid, E - 1), ir = min(tid, R - 1);
   const InT* gp = gla ? static_cast<const InT*>(a.g) + bh * R + ir : q + bh * DK + iq;
   const InT rq = q[bh * DK + iq], rk = k[bh * DK + iq], rv = v[bh * E + iv], rg = *gp;
-  const float rz = a.z[bh * R + ir];
-  float4* Sh = reinterpret_cast<float4*>(a.S + bh * R * E);
+  long long si = bh;  // this head's state
+  if (a.slot != nullptr) {
+    const int sl = a.slot[bh / a.H];
+    si = (sl >= 0 && sl < a.nslot) ? (long long)sl * a.H + bh % a.H : -1;
+  }
+  const bool rd = (a.flags & 1) && si >= 0, wr = (a.flags & 2) && si >= 0;
+  float4* Sh = reinterpret_cast<float4*>(a.S + (si >= 0 ? si : 0) * R * E);
+  float rz = 0.f;
   float4 st[PASSES];
+  if (rd) {  // uniform over the workgroup: the loads stay in one block
+    rz = a.z[si * R + ir];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) st[p] = Sh[(r0 + RPP * p) * CG + col4];
+    for (int p = 0; p < PASSES; ++p) st[p] = Sh[(r0 + RPP * p) * CG + col4];
+  } else {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) st[p] = float4{0.f, 0.f, 0.f, 0.f};
+  }
   const float xq = to_f32(rq), xk = to_f32(rk), xv = to_f32(rv), xg = gla ? to_f32(rg) : 0.f, xz = rz;
 
   // features and gate of this token
@@ -101,7 +118,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     spk[tid] = pk;
     sal[tid] = al;
     const float zn = al * xz + pk;
-    a.z[bh * R + tid] = zn;
+    if (wr) a.z[si * R + tid] = zn;
     zdot = pq * zn;
   }
   // denominator: block reduction of phi(q) . z'
@@ -132,7 +149,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     s.y = al * s.y + pk * vv.y;
     s.z = al * s.z + pk * vv.z;
     s.w = al * s.w + pk * vv.w;
-    Sh[r * CG + col4] = s;
+    if (wr) Sh[r * CG + col4] = s;
     o.x += pq * s.x;
     o.y += pq * s.y;
     o.z += pq * s.z;
@@ -149,8 +166,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
 
 template <int R, int E, int DK, int FMAP>
 static la_status run_decode(const DecodePlan& p) {
-  DecodeArgs a{p.S, p.z, p.q, p.k, p.v, p.g, p.omega, p.gamma, p.out, p.H, p.in_dtype, p.out_dtype, p.gate,
-               p.eps, p.gate == LA_GATE_GLA ? 1.f / p.tau : 0.f};
+  DecodeArgs a{p.S,         p.z,          p.q,    p.k,    p.v,         p.g,
+               p.omega,     p.gamma,      p.out,  p.H,    p.in_dtype,  p.out_dtype,
+               p.gate,      p.eps,        p.gate == LA_GATE_GLA ? 1.f / p.tau : 0.f,
+               p.slot,      p.nslot,      p.flags};
   if (p.in_dtype == LA_BF16)
     hipLaunchKernelGGL((decode_step_kernel<R, E, DK, FMAP, bf16>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256), 0,
                        p.stream, a);

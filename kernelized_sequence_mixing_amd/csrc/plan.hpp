@@ -88,6 +88,10 @@ struct DecodePlan {
   const void* omega;
   const float* gamma;
   void* out;
+  // state slots (la_forward_batch with one token per sequence): state index
+  // slot[b] H + h; flags 1 read, 2 write (la_decode_step: no slots, both)
+  const int* slot;
+  int nslot, flags;
   hipStream_t stream;
 };
 

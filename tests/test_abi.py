@@ -341,8 +341,11 @@ def test_batch_rejects(name, over, kw, want):
 
 @needs_lib
 def test_batch_workspace_size():
-    """A ragged batch is planned as num_seqs sequences of max_seqlen tokens;
-    without slots or cu_seqlens it needs what la_forward needs."""
+    """Without cu_seqlens a batch needs what la_forward needs. A ragged batch
+    is planned from its total and longest lengths: segments of
+    ceil((total / 64 + num_seqs) * H / 512) chunks (at most the longest
+    sequence's), P of them covering the longest sequence, fp32 segment states
+    for num_seqs * H * P (0 when P is 1)."""
     lib = N.lib()
 
     def size(B, n, cu, num_seqs, max_seqlen, flags=0):
@@ -364,5 +367,11 @@ def test_batch_workspace_size():
                                              ctypes.byref(out)) == N.LA_OK
         return out.value
     assert size(4, 4096, None, 4, 4096) == fwd(4, 4096)
-    assert size(1, 40000, FAKE, 10, 4096) == fwd(10, 4096)
-    assert size(1, 40000, FAKE, 64, 128) == fwd(64, 128) == 0   # one segment per sequence: no workspace
+
+    def ragged(total, nseq, max_len, H=16, r=64, dv=64):
+        seg = min(max(-(-((-(-total // 64) + nseq) * H) // 512), 1), -(-max_len // 64))
+        P = -(-(-(-max_len // 64)) // seg)
+        return 0 if P <= 1 else nseq * H * P * (r * dv + r) * 4
+    assert size(1, 40000, FAKE, 10, 4096) == ragged(40000, 10, 4096) == 10 * 16 * 4 * (64 * 64 + 64) * 4
+    assert size(1, 8192, FAKE, 64, 4096) == ragged(8192, 64, 4096) > 0 == fwd(64, 4096)
+    assert size(1, 40000, FAKE, 64, 128) == 0   # one segment per sequence: no workspace

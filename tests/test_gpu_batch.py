@@ -148,6 +148,44 @@ def test_uniform_batch_matches_forward(gate):
     assert torch.equal(S_pool[3], untouched)
 
 
+@pytest.mark.parametrize("gate", ["none", "gla"])
+def test_one_token_steps_with_slots(gate):
+    """One token per sequence runs the recurrent step kernel on the slots:
+    states equal la_decode_step's on the gathered states bit for bit, slots
+    of other sequences and the one with an id outside the pool stay as they
+    were, and outputs follow the oracle's recurrence."""
+    import kernelized_sequence_mixing_amd as ksm
+    wl = _wl("elu1", gate, 128, 128)
+    B, H = 6, 4
+    inp = make_inputs(wl, seed=8, B=B, H=H, n=1)
+    S_init, z_init = _slot_states(wl, 9, H, seed=6)
+    S = torch.from_numpy(S_init.astype(np.float32)).to("cuda")
+    z = torch.from_numpy(z_init.astype(np.float32)).to("cuda")
+    ids_np = np.array([4, 0, 8, 2, 11, 6], dtype=np.int32)   # 11 is outside the pool of 9
+    ids = torch.from_numpy(ids_np).to("cuda")
+    valid = torch.from_numpy(ids_np[ids_np < 9].astype(np.int64)).to("cuda")
+    rows = torch.from_numpy(np.nonzero(ids_np < 9)[0]).to("cuda")
+    S_ref, z_ref = S[valid].clone(), z[valid].clone()
+    before_S, before_z = S.clone(), z.clone()
+    out = ksm.forward_batch(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), state=(S, z), slot_ids=ids, read=True,
+                            write=True, gate=_gpu_gate(inp), eps=inp["eps"])
+    g1 = None
+    if gate == "gla":
+        g1 = ("gla", dev(inp["g"])[rows, :, 0].contiguous(), wl.tau)
+    ksm.decode_step(S_ref, z_ref, dev(inp["Q"])[rows, :, 0].contiguous(), dev(inp["K"])[rows, :, 0].contiguous(),
+                    dev(inp["V"])[rows, :, 0].contiguous(), gate=g1, eps=inp["eps"])
+    torch.cuda.synchronize()
+    assert torch.equal(S[valid], S_ref) and torch.equal(z[valid], z_ref)
+    for sl in (1, 3, 5, 7):
+        assert torch.equal(S[sl], before_S[sl]) and torch.equal(z[sl], before_z[sl])
+    out = out.cpu()
+    for b in range(B):
+        sl = int(ids_np[b])
+        ok = sl < 9
+        o, _, _ = _oracle(_slice(inp, 0, 1, b=b), S_init[sl:sl + 1] if ok else None, z_init[sl:sl + 1] if ok else None)
+        check_close(out[b:b + 1], o, TOL_BF16, f"{gate} one-token seq {b} slot {sl}")
+
+
 @pytest.mark.parametrize("gate", ["decay", "gla"])
 def test_prefill_then_multi_token_decode(gate):
     """A ragged prefill that stores states, then three steps of four new tokens

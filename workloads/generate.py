@@ -121,3 +121,11 @@ def _decode_inputs(wl: Workload, rng, B, H, qs, vs) -> dict:
     if wl.fmap == "favor":
         d["omega"] = _cast(orthogonal_gaussian_omega(rng, wl.r, wl.d_k), wl.dtype)
     return d
+
+
+def serving_lengths(num_seqs: int, seed: int, lo: int = 64, hi: int = 8192) -> np.ndarray:
+    """A seeded length mix for a serving batch: log-uniform integers in [lo, hi]
+    (many short requests, a few long ones), as int32."""
+    rng = np.random.default_rng(seed)
+    u = rng.random(num_seqs)
+    return np.clip(np.round(np.exp(np.log(lo) + u * (np.log(hi) - np.log(lo)))), lo, hi).astype(np.int32)
