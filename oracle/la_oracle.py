@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-FMAPS = ("elu1", "favor")
+FMAPS = ("elu1", "favor", "identity")
 GATES = ("none", "decay", "gla")
 
 
@@ -70,7 +70,16 @@ def phi_favor(x, omega):
 
 
 def feature_map(x, fmap="elu1", omega=None):
-    """Apply the named feature map phi over the last axis."""
+    """Apply the named feature map phi over the last axis.
+
+    "identity" is the state-space reading ([LAM-d] "State Space Models as
+    Linear Attention": h_t = A_t h_{t-1} + B_t x_t, y_t = C_t^T h_t; [AFA]
+    "Evolution: add decay/gating", the bridge to Mamba): the inputs C_t = q_t
+    and B_t = k_t enter as they are, and the read-out is not normalised (see
+    ``normalised``).
+    """
+    if fmap == "identity":
+        return _f64(x)
     if fmap == "elu1":
         return phi_elu1(x)
     if fmap == "favor":
@@ -78,6 +87,18 @@ def feature_map(x, fmap="elu1", omega=None):
             raise ValueError("favor feature map needs omega")
         return phi_favor(x, omega)
     raise ValueError(f"unknown feature map {fmap!r}")
+
+
+def normalised(fmap):
+    """Whether the read-out divides by phi(q).z + eps.
+
+    The attention forms are normalised ([LAM-d] "The Kernel Trick for
+    Attention"). The state-space form reads y_t = C_t^T h_t directly ([LAM-d]
+    "State Space Models as Linear Attention"); its inputs may be negative, so a
+    denominator phi(q).z would have no sign ([AFA] notes the normaliser's
+    fragility). Reading: the identity feature map means the SSM read-out.
+    """
+    return fmap != "identity"
 
 
 # ---------------------------------------------------------------------------
@@ -129,6 +150,8 @@ def noncausal(Q, K, V, fmap="elu1", omega=None, eps=1e-6):
     "The Kernel Trick for Attention" (the S, z formula); [AFA] "Linear
     Attention (the core trick)".
     """
+    if not normalised(fmap):
+        raise ValueError("the state-space read-out is defined for the causal form only")
     V = _f64(V)
     pq = feature_map(Q, fmap, omega)
     pk = feature_map(K, fmap, omega)
@@ -177,22 +200,26 @@ def kernel_weights(Q, K, fmap="elu1", omega=None, causal=False, gate=None):
     return W
 
 
-def attention_from_weights(W, V, eps=1e-6):
-    """o_i = sum_j W_ij v_j / (sum_j W_ij + eps).
+def attention_from_weights(W, V, eps=1e-6, normalise=True):
+    """o_i = sum_j W_ij v_j / (sum_j W_ij + eps), or sum_j W_ij v_j unnormalised.
 
     [LAM-d] "The Kernel Trick for Attention" (the ratio form of o_i) with the
-    eps of [LAM-s] "The linear attention trick".
+    eps of [LAM-s] "The linear attention trick"; the unnormalised sum is the
+    read-out of [LAM-d] "State Space Models as Linear Attention".
     """
     V = _f64(V)
     num = np.einsum("bhij,bhje->bhie", W, V)
+    if not normalise:
+        return num
     den = W.sum(axis=-1) + eps
     return num / den[..., None]
 
 
 def brute(Q, K, V, fmap="elu1", omega=None, causal=False, gate=None, eps=1e-6):
-    """Quadratic reference: explicit weight matrix, then the normalised mix."""
+    """Quadratic reference: explicit weight matrix, then the mix (normalised
+    unless ``fmap`` is the state-space "identity")."""
     W = kernel_weights(Q, K, fmap, omega, causal, gate)
-    return attention_from_weights(W, V, eps)
+    return attention_from_weights(W, V, eps, normalised(fmap))
 
 
 # ---------------------------------------------------------------------------
@@ -215,8 +242,11 @@ def causal_recurrent(Q, K, V, fmap="elu1", omega=None, gate=None, eps=1e-6,
     one; eps is added to the denominator as in [LAM-s]'s routine; the page
     calls z's update "scalar" but z has r entries (it is summed elementwise).
     ``gate`` is None, ("decay", gamma[H]) or ("gla", g[B,H,n,r], tau).
+    With the "identity" feature map the read-out is o_t = q_t^T S_t, the
+    state-space y_t = C_t^T h_t (z is still carried, unused).
     """
     V = _f64(V)
+    norm = normalised(fmap)
     pq = feature_map(Q, fmap, omega)
     pk = feature_map(K, fmap, omega)
     B, H, n, r = pq.shape
@@ -232,6 +262,9 @@ def causal_recurrent(Q, K, V, fmap="elu1", omega=None, gate=None, eps=1e-6,
         S = S + pk[:, :, t, :, None] * V[:, :, t, None, :]
         z = z + pk[:, :, t, :]
         num = np.einsum("bhr,bhre->bhe", pq[:, :, t, :], S)
+        if not norm:
+            out[:, :, t, :] = num
+            continue
         den = np.einsum("bhr,bhr->bh", pq[:, :, t, :], z) + eps
         out[:, :, t, :] = num / den[..., None]
     return out, S, z

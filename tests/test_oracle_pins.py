@@ -149,7 +149,8 @@ def test_constant_values_and_eps():
 # ---------------------------------------------------------------- causal forms
 
 CASES = [("elu1", "none"), ("elu1", "decay"), ("elu1", "gla"),
-         ("favor", "none"), ("favor", "decay"), ("favor", "gla")]
+         ("favor", "none"), ("favor", "decay"), ("favor", "gla"),
+         ("identity", "none"), ("identity", "decay"), ("identity", "gla")]
 
 
 def _causal_case(fmap, gate, B=2, H=3, n=23, d=6, dv=5, r=12, seed=0):
@@ -291,7 +292,10 @@ def test_constant_gla_equals_decay():
     assert abs(orc.gla_alpha(0.0, 16.0) - 2.0 ** (-1.0 / 16.0)) < 1e-15
 
 
-@pytest.mark.parametrize("fmap,gate", CASES)
+ATTN_CASES = [c for c in CASES if c[0] != "identity"]   # the normalised (positive-feature) forms
+
+
+@pytest.mark.parametrize("fmap,gate", ATTN_CASES)
 def test_normaliser_positive_and_outputs_convex(fmap, gate):
     """Similarities are non-negative ("must keep similarities >= 0"), so the
     denominator is at least eps and each output coordinate, rescaled by
@@ -354,3 +358,62 @@ def test_rowwise_metric():
     assert orc.rowwise_rel_err(got, ref) == math.inf
     got[1, 0] = np.nan
     assert orc.rowwise_rel_err(got, ref) == math.inf
+
+
+# ------------------------------------------------------- state-space read-out
+
+@pytest.mark.parametrize("gate", ["none", "decay", "gla"])
+def test_identity_is_masked_matrix_product(gate):
+    """The state-space form y_t = C_t^T h_t, h_t = A_t h_{t-1} + B_t x_t
+    ("State Space Models as Linear Attention") unrolls to y = (M o (C B^T)) X
+    with M the causal decay mask. The gate enters through the cumulative
+    log-gate c_t = sum_{u<=t} log a_u: the weight of key j at query i is
+    exp(c_i - c_j) per feature, so y = tril((C e^c)(B e^-c)^T) X, written here
+    with numpy matmuls (no loop over steps, no product of gates)."""
+    rng = np.random.default_rng(5)
+    B, H, n, d, dv = 2, 3, 29, 5, 4
+    C = rng.standard_normal((B, H, n, d))
+    Bk = rng.standard_normal((B, H, n, d))
+    X = rng.standard_normal((B, H, n, dv))
+    if gate == "none":
+        logs = np.zeros((B, H, n, d))
+        gt = None
+    elif gate == "decay":
+        gam = np.array([0.5, 0.8, 0.97])
+        logs = np.broadcast_to(np.log(gam)[None, :, None, None], (B, H, n, d))
+        gt = ("decay", gam)
+    else:
+        g = rng.standard_normal((B, H, n, d)) * 2.0
+        tau = 3.0
+        logs = np.log(scipy.special.expit(g)) / tau
+        gt = ("gla", g, tau)
+    c = np.cumsum(logs, axis=2)
+    W = np.tril((C * np.exp(c)) @ np.swapaxes(Bk * np.exp(-c), -1, -2))
+    want = W @ X
+    got = orc.causal_recurrent(C, Bk, X, "identity", None, gt)[0]
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_identity_decay_matches_iir_filter():
+    """One state feature with C = B = 1: y_t = gamma y_{t-1} + x_t, a
+    first-order IIR filter (scipy.signal.lfilter), with no normaliser."""
+    rng = np.random.default_rng(22)
+    n, gam = 50, 0.85
+    one = np.ones((1, 1, n, 1))
+    X = rng.standard_normal((1, 1, n, 3))
+    y = orc.causal_recurrent(one, one, X, "identity", None, ("decay", np.array([gam])))[0][0, 0]
+    np.testing.assert_allclose(y, scipy.signal.lfilter([1.0], [1.0, -gam], X[0, 0], axis=0), rtol=1e-12)
+
+
+def test_identity_is_linear_in_values():
+    """The unnormalised read-out is linear in the values (a normaliser or a
+    feature map applied to the inputs would break it: y(2x + x') = 2 y(x) + y(x'))."""
+    Q, K, V, om, gt = _causal_case("identity", "gla", seed=3)
+    V2 = np.random.default_rng(4).standard_normal(V.shape)
+    a = orc.causal_recurrent(Q, K, 2.0 * V + V2, "identity", None, gt)[0]
+    b = 2.0 * orc.causal_recurrent(Q, K, V, "identity", None, gt)[0] + orc.causal_recurrent(Q, K, V2, "identity",
+                                                                                               None, gt)[0]
+    np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+    # and also linear (odd) in the queries, which a positive feature map is not
+    c = orc.causal_recurrent(-Q, K, V, "identity", None, gt)[0]
+    np.testing.assert_allclose(c, -orc.causal_recurrent(Q, K, V, "identity", None, gt)[0], rtol=1e-12)
