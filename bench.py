@@ -382,7 +382,7 @@ def main():
     }
     if not args.no_extra:
         extra = []
-        for name in ("noncausal_elu1_f32", "retnet_decay", "gla_gate", "favor_causal"):
+        for name in ("noncausal_elu1_f32", "retnet_decay", "gla_gate", "ssm_selective", "favor_causal"):
             extra.append(bench_forward(WORKLOADS[name], args.steps, args.warmup))
         extra.append(bench_decode(WORKLOADS["gla_decode"], args.steps, args.warmup))
         extra.append(bench_serve_prefill(args.steps, args.warmup))

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 3
+#define LA_ABI_VERSION 4
 
 typedef enum la_status {
   LA_OK = 0,
@@ -62,7 +62,17 @@ typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
  *   FAVOR : phi(x)_m = exp(w_m . x - |x|^2 / 2) / sqrt(r), m = 0..r-1, the
  *           positive random features whose inner product estimates exp(q.k);
  *           omega holds the r rows w_m. */
-typedef enum la_fmap_kind { LA_FMAP_ELU1 = 0, LA_FMAP_FAVOR = 1 } la_fmap_kind;
+/*
+ * Feature maps. ELU1: phi(x) = elu(x) + 1; FAVOR: positive random features
+ * exp(w.x - |x|^2/2) / sqrt(r) with omega [r][d_k]. IDENTITY: the state-space
+ * form ("State Space Models as Linear Attention", dileepadev page: h_t =
+ * A_t h_{t-1} + B_t x_t, y_t = C_t^T h_t): q = C and k = B enter unchanged
+ * and the read-out is NOT normalised, o_i = q_i^T S_i (z is still carried as
+ * the state's column of a constant-1 value and returned in z_final, but not
+ * read); causal only, r = d_k, gates as for ELU1 (the GLA gate is the
+ * selective, input-dependent diagonal A_t).
+ */
+typedef enum la_fmap_kind { LA_FMAP_ELU1 = 0, LA_FMAP_FAVOR = 1, LA_FMAP_IDENTITY = 2 } la_fmap_kind;
 
 /* State gates for the causal form ("Gating and Selective State Updates"):
  *   NONE  : S_t = S_{t-1} + phi(k_t) v_t^T.
@@ -157,7 +167,7 @@ la_status la_forward_segments(const la_problem* p, const la_feature_map* fmap,
  *   workspace     device scratch of at least la_forward_workspace_size bytes
  *                 (may be NULL when that size is 0), 256-byte aligned.
  * Supported (else LA_ERR_UNSUPPORTED):
- *   causal: in_dtype BF16, out_dtype BF16; ELU1 with d_k in {32,64,128};
+ *   causal: in_dtype BF16, out_dtype BF16; ELU1 or IDENTITY with d_k in {32,64,128};
  *           FAVOR with d_k in {32,64,128}, r in {64,128,256}, gate NONE or DECAY;
  *           d_v in {32,64,128}; r * d_v <= 16384.
  *   non-causal: in/out dtype F32 or BF16 (any mix); same d_k, d_v, r sets.
@@ -274,7 +284,8 @@ la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
 /*
  * The feature map alone: out[i][m] = phi(X[i])_m in fp32 for `rows` rows of
  * width d_k ("Choosing the Feature Map phi", dileepadev page).
- *   X [rows][d_k] in in_dtype; out [rows][r] fp32. Same d_k / r sets as above.
+ *   X [rows][d_k] in in_dtype; out [rows][r] fp32. Same d_k / r sets as above;
+ *   IDENTITY gives LA_ERR_UNSUPPORTED (nothing to apply).
  */
 la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t d_k,
                                int32_t in_dtype, const void* X, float* out, void* stream);

@@ -14,7 +14,7 @@ import torch
 from . import _native as N
 
 _DT = {torch.float32: N.LA_F32, torch.bfloat16: N.LA_BF16}
-_FMAP = {"elu1": N.LA_FMAP_ELU1, "favor": N.LA_FMAP_FAVOR}
+_FMAP = {"elu1": N.LA_FMAP_ELU1, "favor": N.LA_FMAP_FAVOR, "identity": N.LA_FMAP_IDENTITY}
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -53,8 +53,8 @@ def _fmap_struct(fmap: str, omega, d_k: int):
             raise ValueError(f"omega must be [r, {d_k}], got {tuple(omega.shape)}")
         return N.LaFeatureMap(N.LA_FMAP_FAVOR, omega.shape[0], omega.data_ptr()), omega.shape[0]
     if omega is not None:
-        raise ValueError("elu1 takes no omega")
-    return N.LaFeatureMap(N.LA_FMAP_ELU1, d_k, None), d_k
+        raise ValueError(f"{fmap} takes no omega")
+    return N.LaFeatureMap(_FMAP[fmap], d_k, None), d_k
 
 
 def _gate_struct(gate, expect_g_shape):

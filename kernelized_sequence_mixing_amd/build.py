@@ -26,7 +26,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblinattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "chunked_elu1.hip", "chunked_favor.hip", "scan.hip", "noncausal.hip", "decode.hip",
+SOURCES = ["api.cpp", "chunked_elu1.hip", "chunked_ssm.hip", "chunked_favor.hip", "scan.hip", "noncausal.hip", "decode.hip",
            "featuremap.hip", "backward.hip"]
 
 HIPCC_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -48,7 +48,7 @@ la_status check_problem(const la_problem* p) {
 
 la_status check_fmap(const la_feature_map* f, int dk) {
   if (f == nullptr) return LA_ERR_INVALID_ARG;
-  if (f->kind == LA_FMAP_ELU1) {
+  if (f->kind == LA_FMAP_ELU1 || f->kind == LA_FMAP_IDENTITY) {
     if (f->r != dk || f->omega != nullptr) return LA_ERR_INVALID_ARG;
   } else if (f->kind == LA_FMAP_FAVOR) {
     if (f->r < 1 || f->omega == nullptr) return LA_ERR_INVALID_ARG;
@@ -94,7 +94,7 @@ long long resident_groups(int fmap, int r, int dv, int dk, int gate) {
   // elu+1 with a 128 x 128 state: the fp32 state and its bf16 image alone take
   // a third of a lane's 512 registers, and the output pass runs one
   // workgroup per CU
-  if (fmap == LA_FMAP_ELU1 && (long long)r * dv >= 128 * 128) per_cu = 1;
+  if (fmap != LA_FMAP_FAVOR && (long long)r * dv >= 128 * 128) per_cu = 1;
   return (long long)kComputeUnits * per_cu;
 }
 
@@ -171,6 +171,16 @@ WsLayout workspace_layout(const la_problem* p, const la_feature_map* f, int caus
   return workspace_pieces(BH, pieces, f->r, p->d_v, causal && gate == LA_GATE_GLA);
 }
 
+// The causal kernels of the plan's feature map.
+la_status launch_causal(const FwdPlan& p) {
+  switch (p.fmap) {
+    case LA_FMAP_ELU1: return launch_causal_elu1(p);
+    case LA_FMAP_IDENTITY: return launch_causal_ssm(p);
+    case LA_FMAP_FAVOR: return launch_causal_favor(p);
+  }
+  return LA_ERR_UNSUPPORTED;
+}
+
 // Validation shared by la_forward and its size queries (no pointers inspected).
 la_status check_forward_shape(const la_problem* p, const la_feature_map* f, int causal, const la_gate* g) {
   la_status st = check_problem(p);
@@ -181,6 +191,7 @@ la_status check_forward_shape(const la_problem* p, const la_feature_map* f, int 
   const int gk = gate_kind(g);
   if (!causal && gk != LA_GATE_NONE) return LA_ERR_INVALID_ARG;
   if (!shapes_built(f, p->d_k, p->d_v, causal != 0)) return LA_ERR_UNSUPPORTED;
+  if (!causal && f->kind == LA_FMAP_IDENTITY) return LA_ERR_UNSUPPORTED;  // the state-space form is causal
   if (causal) {
     if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
     if (f->kind == LA_FMAP_FAVOR && gk == LA_GATE_GLA) return LA_ERR_UNSUPPORTED;
@@ -354,7 +365,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   plan.ws_logG = (wl.bytes && causal && gk == LA_GATE_GLA) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
   if (causal) {
     plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, p->d_v, p->d_k, gk, &plan.P, &plan.seg_len);
-    return fmap->kind == LA_FMAP_ELU1 ? launch_causal_elu1(plan) : launch_causal_favor(plan);
+    return launch_causal(plan);
   }
   plan_splits(p->B, p->H, p->n, &plan.splits, &plan.split_len);
   return launch_noncausal(plan);
@@ -521,7 +532,7 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
     const la_status ds = launch_decode(dp);
     if (ds != LA_ERR_UNSUPPORTED) return ds;
   }
-  return fmap->kind == LA_FMAP_ELU1 ? launch_causal_elu1(plan) : launch_causal_favor(plan);
+  return launch_causal(plan);
 }
 
 la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q, const void* k, const void* v,
@@ -669,6 +680,7 @@ la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t
   la_status st = check_fmap(fmap, d_k);
   if (st != LA_OK) return st;
   if (X == nullptr || out == nullptr || !aligned16(X) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+  if (fmap->kind == LA_FMAP_IDENTITY) return LA_ERR_UNSUPPORTED;  // nothing to apply
   if (!in_set(d_k, {32, 64, 128})) return LA_ERR_UNSUPPORTED;
   if (fmap->kind == LA_FMAP_FAVOR && !in_set(fmap->r, {64, 128, 256})) return LA_ERR_UNSUPPORTED;
   if ((rows + 63) / 64 > 0x7fffffffLL) return LA_ERR_UNSUPPORTED;

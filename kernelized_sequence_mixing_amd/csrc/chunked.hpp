@@ -45,7 +45,15 @@
 
 namespace la {
 
-enum FmapKind { FM_ELU1 = 0, FM_FAVOR = 1 };
+enum FmapKind { FM_ELU1 = 0, FM_FAVOR = 1, FM_IDENT = 2 };
+
+// Elementwise feature maps of the chunk prelude: elu+1, or the identity of the
+// state-space form (whose read-out is not normalised).
+template <int FMAP>
+__device__ __forceinline__ float phi_ew(float x) {
+  if constexpr (FMAP == FM_IDENT) return x;
+  else return elu1(x);
+}
 enum GateKind { GT_NONE = 0, GT_DECAY = 1, GT_GLA = 2 };
 
 struct CausalArgs {
@@ -228,7 +236,7 @@ struct RawChunk {
   static constexpr int KS = DK / 32;     // projection k-steps (FAVOR)
   static constexpr int TPW = kChunk / NW;  // tokens per wave (row-major layout)
   static constexpr int LPT = NW;           // lanes per token (row-major layout)
-  static constexpr bool ELU = FMAP == FM_ELU1;
+  static constexpr bool ELU = FMAP != FM_FAVOR;  // elementwise feature maps
   static constexpr bool ROWMAJOR = ELU && GATE != GT_GLA;
   // row-major: R / (8 LPT) blocks of 8 features per lane per row (= FR / 8)
   bf16x8 q[ELU && WITH_Q ? FR / 8 : 1];
@@ -307,7 +315,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
   constexpr int LPT = Raw::LPT;
   using FT = FeatTile<R, SWZ>;
   using VT = FeatTile<E, SWZ>;
-  static_assert(FMAP == FM_ELU1, "FAVOR+ chunks use the kernels of chunked_favor.hpp");
+  static_assert(FMAP != FM_FAVOR, "FAVOR+ chunks use the kernels of chunked_favor.hpp");
   if constexpr (Raw::ROWMAJOR) {
     const int t = Raw::TPW * w + lane / LPT;
     const bool valid = t < L;
@@ -319,8 +327,8 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       float vq[8], vk[8], vkh[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        vq[u] = WITH_Q ? elu1(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
-        vk[u] = elu1(to_f32(raw.k[j][u]));
+        vq[u] = WITH_Q ? phi_ew<FMAP>(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
+        vk[u] = phi_ew<FMAP>(to_f32(raw.k[j][u]));
         vkh[u] = vk[u] * decay_k;
       }
       const int fo = FT::at(t, f0 / 8);
@@ -356,8 +364,8 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       float vq[8], vk[8], dq[8], dk[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        float pq = WITH_Q ? elu1(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
-        float pk = elu1(to_f32(raw.k[j][u]));
+        float pq = WITH_Q ? phi_ew<FMAP>(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
+        float pk = phi_ew<FMAP>(to_f32(raw.k[j][u]));
         if constexpr (GATE == GT_GLA) {
           float la = keep_if(valid, gla_log_alpha(to_f32(raw.g[j][u]), a.inv_tau));
           float b = wave_inclusive_scan(la);
@@ -781,8 +789,11 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
       for (int p = 0; p < KP; ++p)
         qb[p] = cat8(lds<bf16x4>(sm, LY::q_off + FT::at(q, 4 * p + (g4 >> 1), 8 * (g4 & 1))),
                      lds<bf16x4>(sm, LY::q_off + FT::at(q, 4 * p + 2 + (g4 >> 1), 8 * (g4 & 1))));
-      // one correctly rounded reciprocal per row; outputs are fl(O * fl(1 / den))
-      const float inv_den = 1.f / (lds<float>(sm, LY::rs_off + 4 * q) + lds<float>(sm, LY::zd_off + 4 * q) + a.eps);
+      // one correctly rounded reciprocal per row; outputs are fl(O * fl(1 / den));
+      // the state-space read-out is the numerator itself
+      float inv_den = 1.f;
+      if constexpr (FMAP != FM_IDENT)
+        inv_den = 1.f / (lds<float>(sm, LY::rs_off + 4 * q) + lds<float>(sm, LY::zd_off + 4 * q) + a.eps);
       float isc = 1.f;
       if constexpr (GATE == GT_DECAY) isc = exp2f(float(q + 1) * lg2gam);
 #pragma unroll

@@ -99,6 +99,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     if constexpr (FMAP == 0) {
       pq = elu1(xq);
       pk = elu1(xk);
+    } else if constexpr (FMAP == 2) {  // the state-space form: C = q, B = k as they are
+      pq = xq;
+      pk = xk;
     } else {
       float aq = 0.f, ak = 0.f;
       const InT* om = static_cast<const InT*>(a.omega) + (long long)tid * DK;
@@ -160,7 +163,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   if (tid < E) {
     float acc = 0.f;
     for (int rg = 0; rg < RPP; ++rg) acc += sred[rg * E + tid];
-    st_elem(a.out, bh * E + tid, a.out_dt, acc / sden);
+    // the state-space read-out y = C^T h is not normalised
+    st_elem(a.out, bh * E + tid, a.out_dt, FMAP == 2 ? acc : acc / sden);
   }
 }
 
@@ -207,6 +211,14 @@ la_status launch_decode(const DecodePlan& p) {
       case 32: return dec_by_dv<32, 32, 0>(p);
       case 64: return dec_by_dv<64, 64, 0>(p);
       case 128: return dec_by_dv<128, 128, 0>(p);
+    }
+    return LA_ERR_UNSUPPORTED;
+  }
+  if (p.fmap == LA_FMAP_IDENTITY) {
+    switch (p.dk) {
+      case 32: return dec_by_dv<32, 32, 2>(p);
+      case 64: return dec_by_dv<64, 64, 2>(p);
+      case 128: return dec_by_dv<128, 128, 2>(p);
     }
     return LA_ERR_UNSUPPORTED;
   }

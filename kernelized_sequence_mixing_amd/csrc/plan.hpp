@@ -106,6 +106,7 @@ struct FmapPlan {
 
 // Launchers (each returns LA_OK or LA_ERR_HIP / LA_ERR_UNSUPPORTED).
 la_status launch_causal_elu1(const FwdPlan& p);
+la_status launch_causal_ssm(const FwdPlan& p);
 la_status launch_causal_favor(const FwdPlan& p);
 la_status launch_segment_scan(const FwdPlan& p);
 la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG);

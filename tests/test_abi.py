@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     lib = N.lib()
-    assert lib.la_abi_version() == 3
+    assert lib.la_abi_version() == 4
     names = [lib.la_status_str(i).decode() for i in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_ALIAS",
                      "LA_ERR_HIP"]
@@ -143,6 +143,11 @@ def _forward(a):
 
 
 BAD_FORWARD = [
+    ("identity noncausal", dict(fkind=N.LA_FMAP_IDENTITY, causal=0, in_dt=N.LA_F32, out_dt=N.LA_F32),
+     N.LA_ERR_UNSUPPORTED),
+    ("identity r != d_k", dict(fkind=N.LA_FMAP_IDENTITY, r=32), N.LA_ERR_INVALID_ARG),
+    ("identity with omega", dict(fkind=N.LA_FMAP_IDENTITY, omega=FAKE + 5 * SP), N.LA_ERR_INVALID_ARG),
+    ("fmap kind 3", dict(fkind=3), N.LA_ERR_INVALID_ARG),
     ("B=0", dict(B=0), N.LA_ERR_INVALID_ARG),
     ("n=0", dict(n=0), N.LA_ERR_INVALID_ARG),
     ("d_v<0", dict(d_v=-64), N.LA_ERR_INVALID_ARG),
@@ -234,6 +239,7 @@ def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAK
 
 BAD_BACKWARD = [
     ("n=0", dict(n=0), {}, N.LA_ERR_INVALID_ARG),
+    ("identity", dict(fkind=N.LA_FMAP_IDENTITY), {}, N.LA_ERR_UNSUPPORTED),
     ("noncausal", dict(causal=0), {}, N.LA_ERR_UNSUPPORTED),
     ("favor", dict(fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
     ("gla without dg", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),

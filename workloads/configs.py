@@ -17,7 +17,7 @@ class Workload:
     d_k: int
     d_v: int
     r: int                 # feature dimension (d_k for elu1)
-    fmap: str              # "elu1" | "favor"
+    fmap: str              # "elu1" | "favor" | "identity" (the state-space read-out)
     causal: bool
     gate: str              # "none" | "decay" | "gla"
     dtype: str             # input dtype: "f32" | "bf16"
@@ -57,6 +57,9 @@ WORKLOADS = {
         "gla_decode", B=256, H=16, n=1, d_k=128, d_v=128, r=128, fmap="elu1",
         causal=True, gate="gla", dtype="bf16", qk_scale=128 ** -0.5, v_scale=128 ** -0.5,
         decode=True),
+    "ssm_selective": Workload(
+        "ssm_selective", B=2, H=16, n=16384, d_k=64, d_v=64, r=64, fmap="identity",
+        causal=True, gate="gla", dtype="bf16", qk_scale=64 ** -0.5, v_scale=1.0),
     "favor_causal": Workload(
         "favor_causal", B=1, H=8, n=32768, d_k=64, d_v=64, r=256, fmap="favor",
         causal=True, gate="none", dtype="bf16", qk_scale=64 ** -0.25, v_scale=1.0),
