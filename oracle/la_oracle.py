@@ -26,7 +26,7 @@ from __future__ import annotations
 import numpy as np
 
 FMAPS = ("elu1", "favor", "identity")
-GATES = ("none", "decay", "gla")
+GATES = ("none", "decay", "gla", "sel")
 
 
 def _f64(a):
@@ -120,11 +120,25 @@ def gla_alpha(g, tau):
     return sig ** (1.0 / float(tau))
 
 
+def sel_alpha(g, tau):
+    """Per-step scalar selective gate a_t = sigmoid(g_t) ** (1 / tau) per head.
+
+    [LAM-d] "State Space Models as Linear Attention": Mamba makes A_t depend
+    on the input; [AFA] "Evolution: add decay/gating": Mamba is the
+    content-dependent (selective) version of the gated recurrence
+    S_i = gamma S_{i-1} + phi(k_i) v_i^T. Reading: the selective A_t is one
+    number per step and head (A_t = a_t I, the RetNet decay made
+    input-dependent), from a raw input g [B, H, n] through the same sigmoid
+    and 1/tau as the GLA gate; the per-feature A_t is the GLA gate itself.
+    """
+    return gla_alpha(g, tau)
+
+
 def _gate_factor(gate, t, B, H):
     """Multiplier applied to the previous state before step t.
 
-    Returns an array broadcastable to S [B, H, r, 1] rows (shape [B, H, r] or
-    [1, H, 1]), or None when there is no gate.
+    Returns an array broadcastable to S [B, H, r, 1] rows (shape [B, H, r],
+    [B, H, 1] or [1, H, 1]), or None when there is no gate.
     """
     if gate is None or gate[0] == "none":
         return None
@@ -135,6 +149,9 @@ def _gate_factor(gate, t, B, H):
     if kind == "gla":
         g, tau = gate[1], gate[2]
         return gla_alpha(np.asarray(g)[:, :, t, :], tau)
+    if kind == "sel":
+        g, tau = gate[1], gate[2]
+        return sel_alpha(np.asarray(g)[:, :, t], tau)[:, :, None]
     raise ValueError(f"unknown gate {kind!r}")
 
 
@@ -175,7 +192,8 @@ def kernel_weights(Q, K, fmap="elu1", omega=None, causal=False, gate=None):
     key j is discounted by gamma^(i-j) ([LAM-d] "Gating and Selective State
     Updates"). GLA: key j is multiplied, per feature k, by the product of the
     gates of the steps after j up to i, which is what unrolling
-    S_t = G_t * S_{t-1} + phi(k_t) v_t^T gives.
+    S_t = G_t * S_{t-1} + phi(k_t) v_t^T gives; the scalar selective gate the
+    same with one factor per step shared by all features.
     """
     pq = feature_map(Q, fmap, omega)
     pk = feature_map(K, fmap, omega)
@@ -186,6 +204,8 @@ def kernel_weights(Q, K, fmap="elu1", omega=None, causal=False, gate=None):
     W = np.zeros((B, H, n, n))
     if kind == "gla":
         alpha = gla_alpha(gate[1], gate[2])  # [B, H, n, r]
+    if kind == "sel":
+        alpha = sel_alpha(gate[1], gate[2])[..., None]  # [B, H, n, 1]
     for i in range(n):
         for j in range(n):
             if causal and j > i:
@@ -241,8 +261,8 @@ def causal_recurrent(Q, K, V, fmap="elu1", omega=None, gate=None, eps=1e-6,
     value of constant 1), which keeps the weights of each output summing to
     one; eps is added to the denominator as in [LAM-s]'s routine; the page
     calls z's update "scalar" but z has r entries (it is summed elementwise).
-    ``gate`` is None, ("decay", gamma[H]) or ("gla", g[B,H,n,r], tau).
-    With the "identity" feature map the read-out is o_t = q_t^T S_t, the
+    ``gate`` is None, ("decay", gamma[H]), ("gla", g[B,H,n,r], tau) or
+    ("sel", g[B,H,n], tau). With the "identity" feature map the read-out is o_t = q_t^T S_t, the
     state-space y_t = C_t^T h_t (z is still carried, unused).
     """
     V = _f64(V)
@@ -276,7 +296,8 @@ def decode_step(S, z, q, k, v, fmap="elu1", omega=None, gate=None, eps=1e-6):
     [LAM-d] "Recurrent Reformulation" (rank-1 update of S, update of z, then
     the read-out); [AFA] "The recurrent form (causal)" (constant cost per
     token). q, k, v (and g for GLA) are [B, H, d] for the single new token;
-    ``gate`` is None, ("decay", gamma[H]) or ("gla", g[B,H,r], tau).
+    ``gate`` is None, ("decay", gamma[H]), ("gla", g[B,H,r], tau) or
+    ("sel", g[B,H], tau).
     """
     q4 = _f64(q)[:, :, None, :]
     k4 = _f64(k)[:, :, None, :]
@@ -284,6 +305,8 @@ def decode_step(S, z, q, k, v, fmap="elu1", omega=None, gate=None, eps=1e-6):
     g4 = gate
     if gate is not None and gate[0] == "gla":
         g4 = ("gla", _f64(gate[1])[:, :, None, :], gate[2])
+    if gate is not None and gate[0] == "sel":
+        g4 = ("sel", _f64(gate[1])[:, :, None], gate[2])
     o, S1, z1 = causal_recurrent(q4, k4, v4, fmap, omega, g4, eps, S0=S, z0=z)
     return o[:, :, 0, :], S1, z1
 

@@ -148,9 +148,9 @@ def test_constant_values_and_eps():
 
 # ---------------------------------------------------------------- causal forms
 
-CASES = [("elu1", "none"), ("elu1", "decay"), ("elu1", "gla"),
+CASES = [("elu1", "none"), ("elu1", "decay"), ("elu1", "gla"), ("elu1", "sel"),
          ("favor", "none"), ("favor", "decay"), ("favor", "gla"),
-         ("identity", "none"), ("identity", "decay"), ("identity", "gla")]
+         ("identity", "none"), ("identity", "decay"), ("identity", "gla"), ("identity", "sel")]
 
 
 def _causal_case(fmap, gate, B=2, H=3, n=23, d=6, dv=5, r=12, seed=0):
@@ -164,6 +164,8 @@ def _causal_case(fmap, gate, B=2, H=3, n=23, d=6, dv=5, r=12, seed=0):
         gt = None
     elif gate == "decay":
         gt = ("decay", 1.0 - 2.0 ** (-1.0 - np.arange(H)))
+    elif gate == "sel":
+        gt = ("sel", rng.standard_normal((B, H, n)) * 2.0, 4.0)
     else:
         gt = ("gla", rng.standard_normal((B, H, n, rr)) * 2.0, 4.0)
     return Q, K, V, om, gt
@@ -187,9 +189,9 @@ def test_split_sequence_resumes(fmap, gate):
     m = 11
 
     def cut(gg, sl):
-        if gg is None or gg[0] != "gla":
+        if gg is None or gg[0] not in ("gla", "sel"):
             return gg
-        return ("gla", gg[1][:, :, sl], gg[2])
+        return (gg[0], gg[1][:, :, sl], gg[2])
     a, S1, z1 = orc.causal_recurrent(Q[:, :, :m], K[:, :, :m], V[:, :, :m], fmap, om, cut(gt, slice(0, m)))
     b, S2, z2 = orc.causal_recurrent(Q[:, :, m:], K[:, :, m:], V[:, :, m:], fmap, om, cut(gt, slice(m, None)),
                                      S0=S1, z0=z1)
@@ -203,10 +205,10 @@ def test_decode_step_is_one_recurrence_step(fmap, gate):
     Q, K, V, om, gt = _causal_case(fmap, gate, n=8)
     full, _, _ = orc.causal_recurrent(Q, K, V, fmap, om, gt)
     pre = gt
-    if gt is not None and gt[0] == "gla":
-        pre = ("gla", gt[1][:, :, :7], gt[2])
+    if gt is not None and gt[0] in ("gla", "sel"):
+        pre = (gt[0], gt[1][:, :, :7], gt[2])
     _, S7, z7 = orc.causal_recurrent(Q[:, :, :7], K[:, :, :7], V[:, :, :7], fmap, om, pre)
-    step_gate = gt if gt is None or gt[0] != "gla" else ("gla", gt[1][:, :, 7], gt[2])
+    step_gate = gt if gt is None or gt[0] not in ("gla", "sel") else (gt[0], gt[1][:, :, 7], gt[2])
     o, _, _ = orc.decode_step(S7, z7, Q[:, :, 7], K[:, :, 7], V[:, :, 7], fmap, om, step_gate)
     np.testing.assert_allclose(o, full[:, :, 7], rtol=1e-12, atol=1e-14)
 
@@ -362,7 +364,7 @@ def test_rowwise_metric():
 
 # ------------------------------------------------------- state-space read-out
 
-@pytest.mark.parametrize("gate", ["none", "decay", "gla"])
+@pytest.mark.parametrize("gate", ["none", "decay", "gla", "sel"])
 def test_identity_is_masked_matrix_product(gate):
     """The state-space form y_t = C_t^T h_t, h_t = A_t h_{t-1} + B_t x_t
     ("State Space Models as Linear Attention") unrolls to y = (M o (C B^T)) X
@@ -382,6 +384,11 @@ def test_identity_is_masked_matrix_product(gate):
         gam = np.array([0.5, 0.8, 0.97])
         logs = np.broadcast_to(np.log(gam)[None, :, None, None], (B, H, n, d))
         gt = ("decay", gam)
+    elif gate == "sel":
+        g = rng.standard_normal((B, H, n)) * 2.0
+        tau = 3.0
+        logs = np.broadcast_to((np.log(scipy.special.expit(g)) / tau)[..., None], (B, H, n, d))
+        gt = ("sel", g, tau)
     else:
         g = rng.standard_normal((B, H, n, d)) * 2.0
         tau = 3.0
@@ -417,3 +424,33 @@ def test_identity_is_linear_in_values():
     # and also linear (odd) in the queries, which a positive feature map is not
     c = orc.causal_recurrent(-Q, K, V, "identity", None, gt)[0]
     np.testing.assert_allclose(c, -orc.causal_recurrent(Q, K, V, "identity", None, gt)[0], rtol=1e-12)
+
+
+# ------------------------------------------------------- scalar selective gate
+
+def test_constant_selective_gate_equals_decay():
+    """A selective gate whose input is constant in time is a fixed decay:
+    a = sigmoid(g)^(1/tau) per head reproduces the RetNet form."""
+    rng = np.random.default_rng(31)
+    B, H, n = 2, 3, 19
+    Q, K, V = rng.standard_normal((B, H, n, 5)), rng.standard_normal((B, H, n, 5)), rng.standard_normal((B, H, n, 4))
+    gh = np.array([-1.0, 0.5, 3.0])
+    tau = 2.0
+    g = np.broadcast_to(gh[None, :, None], (B, H, n)).copy()
+    gam = scipy.special.expit(gh) ** (1.0 / tau)
+    for fmap in ("elu1", "identity"):
+        a = orc.causal_recurrent(Q, K, V, fmap, None, ("sel", g, tau))[0]
+        b = orc.causal_recurrent(Q, K, V, fmap, None, ("decay", gam))[0]
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def test_selective_gate_is_gla_shared_by_features():
+    """The scalar selective gate is the diagonal GLA gate with the same input
+    on every feature (A_t = a_t I)."""
+    rng = np.random.default_rng(32)
+    B, H, n, d = 2, 2, 17, 6
+    Q, K, V = rng.standard_normal((B, H, n, d)), rng.standard_normal((B, H, n, d)), rng.standard_normal((B, H, n, 3))
+    g = rng.standard_normal((B, H, n)) * 2.0
+    a = orc.causal_recurrent(Q, K, V, "elu1", None, ("sel", g, 3.0))[0]
+    b = orc.causal_recurrent(Q, K, V, "elu1", None, ("gla", np.repeat(g[..., None], d, axis=-1), 3.0))[0]
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
