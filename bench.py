@@ -53,6 +53,8 @@ def algorithmic_per_token(wl):
     nbytes = isz * (2 * wl.d_k + wl.d_v) + isz * wl.d_v
     if wl.gate == "gla":
         nbytes += isz * wl.r
+    if wl.gate == "sel":
+        nbytes += isz
     half = (CHUNK + 1) / 2
     flops = half * 2 * wl.r + half * 2 * wl.d_v + 4 * wl.r * wl.d_v
     if wl.fmap == "favor":
@@ -133,6 +135,7 @@ def bench_forward(wl, steps, warmup):
         "none": lambda s: None,
         "decay": lambda s: ("decay", s["gamma"]),
         "gla": lambda s: ("gla", s["g"], wl.tau),
+        "sel": lambda s: ("sel", s["g"], wl.tau),
     }[wl.gate]
     outs = [torch.empty((wl.B, wl.H, wl.n, wl.d_v), dtype=sets[0]["V"].dtype, device="cuda") for _ in sets]
     nws = ksm.workspace_size(wl.B, wl.H, wl.n, wl.d_k, wl.d_v, fmap=wl.fmap, r=wl.r, causal=wl.causal,
@@ -382,7 +385,7 @@ def main():
     }
     if not args.no_extra:
         extra = []
-        for name in ("noncausal_elu1_f32", "retnet_decay", "gla_gate", "ssm_selective", "favor_causal"):
+        for name in ("noncausal_elu1_f32", "retnet_decay", "gla_gate", "ssm_selective", "ssm_scalar", "favor_causal"):
             extra.append(bench_forward(WORKLOADS[name], args.steps, args.warmup))
         extra.append(bench_decode(WORKLOADS["gla_decode"], args.steps, args.warmup))
         extra.append(bench_serve_prefill(args.steps, args.warmup))

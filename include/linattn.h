@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 4
+#define LA_ABI_VERSION 5
 
 typedef enum la_status {
   LA_OK = 0,
@@ -79,7 +79,18 @@ typedef enum la_fmap_kind { LA_FMAP_ELU1 = 0, LA_FMAP_FAVOR = 1, LA_FMAP_IDENTIT
  *   DECAY : S_t = gamma_h S_{t-1} + phi(k_t) v_t^T (RetNet fixed decay).
  *   GLA   : S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T with
  *           alpha_t = sigmoid(g_t)^(1/tau) per feature row (diagonal GLA gate). */
-typedef enum la_gate_kind { LA_GATE_NONE = 0, LA_GATE_DECAY = 1, LA_GATE_GLA = 2 } la_gate_kind;
+/*
+ * Gates of the causal forms (the multiplier of the previous state at each
+ * step). DECAY: RetNet's fixed gamma_h. GLA: a per-feature, input-dependent
+ * alpha_t = sigmoid(g_t)^(1/tau), g [B][H][n][r] ("Gating and Selective State
+ * Updates", dileepadev page). SEL: the scalar selective gate, one
+ * input-dependent a_t = sigmoid(g_t)^(1/tau) per step and head shared by all
+ * features, g [B][H][n] (decode: [B][H]); the RetNet decay made
+ * input-dependent, the selective recurrence of Mamba's kind ("State Space
+ * Models as Linear Attention", dileepadev page; "Evolution: add
+ * decay/gating", vguerra page). GLA and SEL: elementwise feature maps only.
+ */
+typedef enum la_gate_kind { LA_GATE_NONE = 0, LA_GATE_DECAY = 1, LA_GATE_GLA = 2, LA_GATE_SEL = 3 } la_gate_kind;
 
 typedef struct la_problem {
   int32_t B, H;      /* batch, heads: >= 1 */
@@ -101,7 +112,8 @@ typedef struct la_gate {
   float tau;          /* GLA temperature, > 0 (ignored otherwise) */
   const float* gamma; /* DECAY: device [H] fp32, each in (0, 1] -- a documented
                          precondition, not checked (the values live on the device) */
-  const void* g;      /* GLA: device [B][H][n][r] in in_dtype (decode: [B][H][r]) */
+  const void* g;      /* GLA: device [B][H][n][r] in in_dtype (decode: [B][H][r]);
+                         SEL: [B][H][n] (decode: [B][H]) */
 } la_gate;
 
 /* Flags of la_batch.flags. */

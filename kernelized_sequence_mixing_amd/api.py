@@ -58,7 +58,9 @@ def _fmap_struct(fmap: str, omega, d_k: int):
 
 
 def _gate_struct(gate, expect_g_shape):
-    """gate: None | ("decay", gamma[H] fp32) | ("gla", g, tau)."""
+    """gate: None | ("decay", gamma[H] fp32) | ("gla", g, tau) | ("sel", g, tau); g has shape
+    expect_g_shape for GLA and expect_g_shape without its last (feature) axis for the
+    selective scalar gate."""
     if gate is None or gate == "none" or (isinstance(gate, tuple) and gate[0] == "none"):
         return N.LaGate(N.LA_GATE_NONE, 1.0, None, None)
     kind = gate[0]
@@ -72,6 +74,11 @@ def _gate_struct(gate, expect_g_shape):
         if tuple(g.shape) != tuple(expect_g_shape):
             raise ValueError(f"g must be {tuple(expect_g_shape)}, got {tuple(g.shape)}")
         return N.LaGate(N.LA_GATE_GLA, float(gate[2]), None, g.data_ptr())
+    if kind == "sel":
+        g = _dev(gate[1], "g")
+        if tuple(g.shape) != tuple(expect_g_shape[:-1]):
+            raise ValueError(f"g must be {tuple(expect_g_shape[:-1])}, got {tuple(g.shape)}")
+        return N.LaGate(N.LA_GATE_SEL, float(gate[2]), None, g.data_ptr())
     raise ValueError(f"unknown gate {kind!r}")
 
 
@@ -86,7 +93,7 @@ def workspace_size(B, H, n, d_k, d_v, *, fmap="elu1", r=None, causal=True, gate_
     out_dtype = dtype if out_dtype is None else out_dtype
     p = _problem(B, H, n, d_k, d_v, _DT[dtype], _DT[out_dtype], 1e-6)
     f = N.LaFeatureMap(_FMAP[fmap], r, 16 if fmap == "favor" else None)
-    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA}[gate_kind]
+    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA, "sel": N.LA_GATE_SEL}[gate_kind]
     g = N.LaGate(gk, 16.0, None, None)
     out = ctypes.c_size_t(0)
     N.check(N.lib().la_forward_workspace_size(ctypes.byref(p), ctypes.byref(f), int(causal), ctypes.byref(g),
@@ -100,7 +107,7 @@ def segments(B, H, n, d_k, d_v, *, fmap="elu1", r=None, causal=True, gate_kind="
     r = d_k if r is None else r
     p = _problem(B, H, n, d_k, d_v, _DT[dtype], _DT[dtype], 1e-6)
     f = N.LaFeatureMap(_FMAP[fmap], r, 16 if fmap == "favor" else None)
-    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA}[gate_kind]
+    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA, "sel": N.LA_GATE_SEL}[gate_kind]
     g = N.LaGate(gk, 16.0, None, None)
     P, L = ctypes.c_int32(0), ctypes.c_int32(0)
     N.check(N.lib().la_forward_segments(ctypes.byref(p), ctypes.byref(f), int(causal), ctypes.byref(g),

@@ -66,7 +66,7 @@ la_status check_gate(const la_gate* g, bool check_ptrs) {
     if (check_ptrs && (g->gamma == nullptr || !aligned16(g->gamma))) return LA_ERR_INVALID_ARG;
     return LA_OK;
   }
-  if (g->kind == LA_GATE_GLA) {
+  if (g->kind == LA_GATE_GLA || g->kind == LA_GATE_SEL) {
     if (!(g->tau > 0.f) || !isfinite(g->tau)) return LA_ERR_INVALID_ARG;
     if (check_ptrs && (g->g == nullptr || !aligned16(g->g))) return LA_ERR_INVALID_ARG;
     return LA_OK;
@@ -75,6 +75,11 @@ la_status check_gate(const la_gate* g, bool check_ptrs) {
 }
 
 int gate_kind(const la_gate* g) { return g == nullptr ? LA_GATE_NONE : g->kind; }
+
+// Gates driven by a raw input g (GLA: one value per feature and token; the
+// selective scalar gate: one per token), and that input's elements per token.
+bool gate_has_input(int gk) { return gk == LA_GATE_GLA || gk == LA_GATE_SEL; }
+size_t gate_input_per_token(int gk, size_t r) { return gk == LA_GATE_GLA ? r : (gk == LA_GATE_SEL ? 1 : 0); }
 
 // The built set of (d_k, r, d_v) shapes; see the header.
 bool shapes_built(const la_feature_map* f, int dk, int dv, bool causal) {
@@ -168,7 +173,7 @@ WsLayout workspace_layout(const la_problem* p, const la_feature_map* f, int caus
     plan_splits(p->B, p->H, p->n, &sp, &L);
     pieces = (size_t)sp;
   }
-  return workspace_pieces(BH, pieces, f->r, p->d_v, causal && gate == LA_GATE_GLA);
+  return workspace_pieces(BH, pieces, f->r, p->d_v, causal && gate_has_input(gate));
 }
 
 // The causal kernels of the plan's feature map.
@@ -194,7 +199,7 @@ la_status check_forward_shape(const la_problem* p, const la_feature_map* f, int 
   if (!causal && f->kind == LA_FMAP_IDENTITY) return LA_ERR_UNSUPPORTED;  // the state-space form is causal
   if (causal) {
     if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
-    if (f->kind == LA_FMAP_FAVOR && gk == LA_GATE_GLA) return LA_ERR_UNSUPPORTED;
+    if (f->kind == LA_FMAP_FAVOR && gate_has_input(gk)) return LA_ERR_UNSUPPORTED;
   }
   return LA_OK;
 }
@@ -209,7 +214,7 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
   if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
   const int gk = gate_kind(g);
   if (!causal && gk != LA_GATE_NONE) return LA_ERR_INVALID_ARG;
-  if (!causal || f->kind != LA_FMAP_ELU1) return LA_ERR_UNSUPPORTED;
+  if (!causal || f->kind != LA_FMAP_ELU1 || gk == LA_GATE_SEL) return LA_ERR_UNSUPPORTED;
   if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   const int key = p->d_k * 1000 + p->d_v;
   if (key != 64064 && key != 64128 && key != 128064) return LA_ERR_UNSUPPORTED;
@@ -312,7 +317,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   const size_t isz = dtype_size(p->in_dtype);
   const Range rq = range_of(Q, BH * n * p->d_k * isz), rk = range_of(K, BH * n * p->d_k * isz),
               rv = range_of(V, BH * n * p->d_v * isz);
-  const Range rg = range_of(gk == LA_GATE_GLA ? gate->g : nullptr, BH * n * r * isz);
+  const Range rg = range_of(gate_has_input(gk) ? gate->g : nullptr, BH * n * gate_input_per_token(gk, r) * isz);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
   const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
   const Range rs0 = range_of(S0, BH * r * p->d_v * 4), rz0 = range_of(z0, BH * r * 4);
@@ -345,11 +350,11 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   plan.fmap = fmap->kind;
   plan.gate = gk;
   plan.causal = causal;
-  plan.tau = gk == LA_GATE_GLA ? gate->tau : 1.f;
+  plan.tau = gate_has_input(gk) ? gate->tau : 1.f;
   plan.Q = Q;
   plan.K = K;
   plan.V = V;
-  plan.g = gk == LA_GATE_GLA ? gate->g : nullptr;
+  plan.g = gate_has_input(gk) ? gate->g : nullptr;
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
   plan.omega = fmap->omega;
   plan.S0 = S0;
@@ -362,7 +367,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   char* ws = static_cast<char*>(workspace);
   plan.ws_S = wl.bytes ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
   plan.ws_z = wl.bytes ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
-  plan.ws_logG = (wl.bytes && causal && gk == LA_GATE_GLA) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
+  plan.ws_logG = (wl.bytes && causal && gate_has_input(gk)) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
   if (causal) {
     plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, p->d_v, p->d_k, gk, &plan.P, &plan.seg_len);
     return launch_causal(plan);
@@ -402,7 +407,7 @@ WsLayout batch_plan(const la_problem* p, const la_batch* b, const la_problem& ef
   else
     plan_segments(eff.B, p->H, eff.n, f->kind, f->r, p->d_v, p->d_k, gate, P, seg_len);
   if (*P <= 1) return WsLayout{0, 0, 0, 0};
-  return workspace_pieces((size_t)eff.B * p->H, (size_t)*P, f->r, p->d_v, gate == LA_GATE_GLA);
+  return workspace_pieces((size_t)eff.B * p->H, (size_t)*P, f->r, p->d_v, gate_has_input(gate));
 }
 }  // namespace
 
@@ -439,7 +444,7 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   const size_t isz = dtype_size(p->in_dtype);
   const Range rq = range_of(Q, BH * n * p->d_k * isz), rk = range_of(K, BH * n * p->d_k * isz),
               rv = range_of(V, BH * n * p->d_v * isz);
-  const Range rg = range_of(gk == LA_GATE_GLA ? gate->g : nullptr, BH * n * r * isz);
+  const Range rg = range_of(gate_has_input(gk) ? gate->g : nullptr, BH * n * gate_input_per_token(gk, r) * isz);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
   const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
   const Range rcu = range_of(batch->cu_seqlens, ((size_t)batch->num_seqs + 1) * 4);
@@ -475,11 +480,11 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   plan.fmap = fmap->kind;
   plan.gate = gk;
   plan.causal = 1;
-  plan.tau = gk == LA_GATE_GLA ? gate->tau : 1.f;
+  plan.tau = gate_has_input(gk) ? gate->tau : 1.f;
   plan.Q = Q;
   plan.K = K;
   plan.V = V;
-  plan.g = gk == LA_GATE_GLA ? gate->g : nullptr;
+  plan.g = gate_has_input(gk) ? gate->g : nullptr;
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
   plan.omega = fmap->omega;
   plan.nseq = eff.B;
@@ -499,7 +504,7 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   char* ws = static_cast<char*>(workspace);
   plan.ws_S = wl.bytes ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
   plan.ws_z = wl.bytes ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
-  plan.ws_logG = (wl.bytes && gk == LA_GATE_GLA) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
+  plan.ws_logG = (wl.bytes && gate_has_input(gk)) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
   plan.P = P;
   plan.seg_len = seg_len;
   if (batch->cu_seqlens == nullptr && p->n == 1) {
@@ -552,7 +557,7 @@ la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
   const Range rS = range_of(S, BH * r * p->d_v * 4), rz = range_of(z, BH * r * 4);
   const Range rq = range_of(q, BH * p->d_k * isz), rk = range_of(k, BH * p->d_k * isz),
               rv = range_of(v, BH * p->d_v * isz);
-  const Range rg = range_of(gk == LA_GATE_GLA ? gate->g : nullptr, BH * r * isz);
+  const Range rg = range_of(gate_has_input(gk) ? gate->g : nullptr, BH * gate_input_per_token(gk, r) * isz);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
   const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
   const Range ro = range_of(out, BH * p->d_v * dtype_size(p->out_dtype));
@@ -572,13 +577,13 @@ la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
   plan.eps = p->eps;
   plan.fmap = fmap->kind;
   plan.gate = gk;
-  plan.tau = gk == LA_GATE_GLA ? gate->tau : 1.f;
+  plan.tau = gate_has_input(gk) ? gate->tau : 1.f;
   plan.S = S;
   plan.z = z;
   plan.q = q;
   plan.k = k;
   plan.v = v;
-  plan.g = gk == LA_GATE_GLA ? gate->g : nullptr;
+  plan.g = gate_has_input(gk) ? gate->g : nullptr;
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
   plan.omega = fmap->omega;
   plan.out = out;
@@ -647,8 +652,8 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.K = K;
   plan.V = V;
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
-  plan.g = gk == LA_GATE_GLA ? gate->g : nullptr;
-  plan.tau = gk == LA_GATE_GLA ? gate->tau : 1.f;
+  plan.g = gate_has_input(gk) ? gate->g : nullptr;
+  plan.tau = gate_has_input(gk) ? gate->tau : 1.f;
   plan.S0 = S0;
   plan.z0 = z0;
   plan.P = wl.P;

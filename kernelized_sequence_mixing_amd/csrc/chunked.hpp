@@ -54,7 +54,11 @@ __device__ __forceinline__ float phi_ew(float x) {
   if constexpr (FMAP == FM_IDENT) return x;
   else return elu1(x);
 }
-enum GateKind { GT_NONE = 0, GT_DECAY = 1, GT_GLA = 2 };
+enum GateKind { GT_NONE = 0, GT_DECAY = 1, GT_GLA = 2, GT_SEL = 3 };
+// Gates that scale every feature of a step alike (RetNet's fixed gamma, the
+// selective scalar a_t): keys are weighted per token, one factor per step.
+template <int GATE>
+constexpr bool kScalarDecay = GATE == GT_DECAY || GATE == GT_SEL;
 
 struct CausalArgs {
   const bf16* Q;
@@ -160,12 +164,13 @@ struct FwdLayout {
   static constexpr int k_off = q_off + FTB;
   static constexpr int v_off = k_off + FTB;
   static constexpr int kh_off = v_off + FeatTile<E, SWZ>::BYTES;
-  static constexpr int a_off = kh_off + (GATE == GT_DECAY ? FTB : 0);
+  static constexpr int a_off = kh_off + (kScalarDecay<GATE> ? FTB : 0);
   static constexpr int z_off = a_off + FeatTile<kChunk, SWZ>::BYTES;
   static constexpr int gam_off = z_off + R * 4;
   static constexpr int rs_off = gam_off + R * 4;   // [64] score row sums
   static constexpr int zd_off = rs_off + kChunk * 4;  // [64] Q^ . z_prev
-  static constexpr int bytes = zd_off + kChunk * 4;
+  static constexpr int bs_off = zd_off + kChunk * 4;  // selective gate: [64] cumulative log-gate
+  static constexpr int bytes = bs_off + (GATE == GT_SEL ? kChunk * 4 : 0);
 };
 
 // Pass 1: one chunk (K^ rows, V rows, gate factors) per half, then the
@@ -181,7 +186,8 @@ struct SegLayout {
   static constexpr int gam_off = v_off + FeatTile<E, SWZ>::BYTES;
   static constexpr int HALF = gam_off + R * 4;
   static constexpr int logg_off = (PIPELINED ? 2 : 1) * HALF;
-  static constexpr int bytes = logg_off + R * 4;
+  static constexpr int bs_off = logg_off + R * 4;  // selective gate: [64] cumulative log-gate
+  static constexpr int bytes = bs_off + (GATE == GT_SEL ? kChunk * 4 : 0);
 };
 
 // Wave barrier for LDS traffic only: every LDS access issued before it is
@@ -242,6 +248,7 @@ struct RawChunk {
   bf16x8 q[ELU && WITH_Q ? FR / 8 : 1];
   bf16x8 k[ELU ? FR / 8 : 1];
   bf16x8 g[GATE == GT_GLA ? FR / 8 : 1];
+  bf16 sg;  // selective gate: the input of token t0 + lane (every wave loads all 64)
   bf16x8 xq[!ELU && WITH_Q ? KS : 1];   // FAVOR+: token 16 w + l % 16, columns 32 ks + 8 (l / 16)
   bf16x8 xk[!ELU ? KS : 1];
   bf16x8 v[EV / 8];
@@ -254,6 +261,7 @@ struct RawChunk {
   // unconditionally.
   __device__ __forceinline__ void load(const CausalArgs& a, long long tok0, int t0, int row_end, int lane, int w) {
     const int g4 = lane >> 4, c16 = lane & 15;
+    if constexpr (GATE == GT_SEL) sg = a.g[tok0 + min(t0 + lane, row_end - 1)];
     if constexpr (ROWMAJOR) {
       const long long row = tok0 + min(t0 + TPW * w + lane / LPT, row_end - 1);
 #pragma unroll
@@ -310,7 +318,7 @@ template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SW
 __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>& raw,
                                               const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
                                               int k_off, int kh_off, int v_off, int gam_off, int logg_off,
-                                              int lane, int w, int qd_off = 0, int kd_off = 0) {
+                                              int lane, int w, int qd_off = 0, int kd_off = 0, int bs_off = 0) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
   constexpr int LPT = Raw::LPT;
   using FT = FeatTile<R, SWZ>;
@@ -321,6 +329,18 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
     const bool valid = t < L;
     float decay_k = 1.f;
     if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(L - 1 - t) * lg2gam);
+    if constexpr (GATE == GT_SEL) {
+      // the chunk's inclusive cumulative log-gate b, lane = token (each wave
+      // scans all 64); keys are weighted e^{b_end - b_t} for the state
+      const float la = keep_if(lane < L, gla_log_alpha(to_f32(raw.sg), a.inv_tau));
+      const float b = wave_inclusive_scan(la);
+      const float bend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
+      decay_k = __expf(bend - __shfl(b, t));
+      if (w == 0) lds<float>(sm, bs_off + 4 * lane) = b;
+      if constexpr (!WITH_Q) {
+        if (64 * w + lane < R) lds<float>(sm, logg_off + 4 * (64 * w + lane)) += bend;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < R / (8 * LPT); ++j) {
       const int f0 = 8 * (lane % LPT + LPT * j);
@@ -338,7 +358,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       const bf16x8 kr = keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
       const bf16x8 khr =
           keep_if(valid, cat8(pack4(vkh[0], vkh[1], vkh[2], vkh[3]), pack4(vkh[4], vkh[5], vkh[6], vkh[7])));
-      if constexpr (GATE != GT_DECAY) {
+      if constexpr (!kScalarDecay<GATE>) {
         lds<bf16x8>(sm, k_off + fo) = kr;
       } else if constexpr (WITH_Q) {
         lds<bf16x8>(sm, k_off + fo) = kr;
@@ -470,7 +490,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
       f32x4 st = S[rt][eb];
-      if constexpr (GATE == GT_DECAY || (GATE == GT_GLA && PRE)) {
+      if constexpr (kScalarDecay<GATE> || (GATE == GT_GLA && PRE)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[i] *= gr[i];
       }
@@ -494,7 +514,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
 #pragma unroll
         for (int i = 0; i < 4; ++i) gr[i] = lds<float>(sm, gam_off + 4 * (16 * rt + 4 * g4 + i));
       }
-      if constexpr (GATE == GT_DECAY || (GATE == GT_GLA && PRE)) {
+      if constexpr (kScalarDecay<GATE> || (GATE == GT_GLA && PRE)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
@@ -588,11 +608,12 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
     const int L = min(kChunk, sv.len - (t_begin + ci * kChunk));
     chunk_prelude<R, E, DK, FMAP, GATE, false, NW, LY::SWZ>(rw, a, L, lg2gam, sm, 0, half * LY::HALF + LY::k_off, 0,
                                                    half * LY::HALF + LY::v_off, half * LY::HALF + LY::gam_off,
-                                                   LY::logg_off, lane, w);
+                                                   LY::logg_off, lane, w, 0, 0, LY::bs_off);
   };
   auto update = [&](int ci, int half) {
     const int L = min(kChunk, sv.len - (t_begin + ci * kChunk));
-    const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+    float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+    if constexpr (GATE == GT_SEL) gsc = __expf(lds<float>(sm, LY::bs_off + 4 * 63));
     state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, half * LY::HALF + LY::k_off, half * LY::HALF + LY::v_off,
                                  half * LY::HALF + LY::gam_off, gsc, lane, w);
   };
@@ -639,7 +660,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
 #pragma unroll
       for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
   z_store<R, NW>(Z, a.z_out + slot * R, lane, w);
-  if constexpr (GATE == GT_GLA) {
+  if constexpr (GATE == GT_GLA || GATE == GT_SEL) {
     if (tid < R) a.logG_out[slot * R + tid] = lds<float>(sm, LY::logg_off + 4 * tid);
   }
 }
@@ -717,7 +738,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
     const int L = min(kChunk, sv.len - t0);
     if (live)
       chunk_prelude<R, E, DK, FMAP, GATE, true, NW, LY::SWZ>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
-                                                    LY::v_off, LY::gam_off, 0, lane, w);
+                                                    LY::v_off, LY::gam_off, 0, lane, w, 0, 0, LY::bs_off);
     // the raw registers are free again: this refill flies during the next DEPTH chunks
     raw.load(a, tok0, t0 + DEPTH * kChunk, t_end, lane, w);
     if (!live) return;
@@ -754,6 +775,12 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
             v[i] = acc[i];
             if (c == qw && key > q) v[i] = 0.f;  // only the diagonal tile straddles the mask
             if constexpr (GATE == GT_DECAY) v[i] *= gbase * ginv[i];
+            if constexpr (GATE == GT_SEL) {
+              // e^{b_q - b_key} <= 1 below the diagonal; a select (not a
+              // product) above it, where the factor may overflow
+              const float f = __expf(lds<float>(sm, LY::bs_off + 4 * q) - lds<float>(sm, LY::bs_off + 4 * key));
+              v[i] = key <= q ? v[i] * f : 0.f;
+            }
           }
           // bf16 scores, and the row sum of exactly those rounded values
           const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
@@ -774,6 +801,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
             zd += to_f32(qop[ks][j]) * lds<float>(sm, LY::z_off + 4 * (32 * ks + 8 * g4 + j));
         zd = sum_over_groups(zd);
         if constexpr (GATE == GT_DECAY) zd *= exp2f(float(q + 1) * lg2gam);
+        if constexpr (GATE == GT_SEL) zd *= __expf(lds<float>(sm, LY::bs_off + 4 * q));
         if (g4 == 0) lds<float>(sm, LY::zd_off + 4 * q) = zd;
       }
     }
@@ -796,13 +824,14 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
         inv_den = 1.f / (lds<float>(sm, LY::rs_off + 4 * q) + lds<float>(sm, LY::zd_off + 4 * q) + a.eps);
       float isc = 1.f;
       if constexpr (GATE == GT_DECAY) isc = exp2f(float(q + 1) * lg2gam);
+      if constexpr (GATE == GT_SEL) isc = __expf(lds<float>(sm, LY::bs_off + 4 * q));
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
         const int e = ebase + 16 * eb;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < KP; ++p) acc = mfma16(Sop[p][eb], qb[p], acc);
-        if constexpr (GATE == GT_DECAY) {
+        if constexpr (kScalarDecay<GATE>) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[i] *= isc;
         }
@@ -818,8 +847,9 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
     }
 
     // ---- carry the state past this chunk
-    const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, GATE == GT_DECAY ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
+    float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+    if constexpr (GATE == GT_SEL) gsc = __expf(lds<float>(sm, LY::bs_off + 4 * 63));
+    state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, kScalarDecay<GATE> ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
                                  gsc, lane, w);
     z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
     lds_barrier();
@@ -865,7 +895,7 @@ la_status run_causal(const FwdPlan& p) {
   a.P = p.P;
   a.seg_len = p.seg_len;
   a.eps = p.eps;
-  a.inv_tau = GATE == GT_GLA ? 1.f / p.tau : 0.f;
+  a.inv_tau = (GATE == GT_GLA || GATE == GT_SEL) ? 1.f / p.tau : 0.f;
   const unsigned BH = unsigned(p.nseq) * unsigned(p.H);
 
   if (p.P > 1) {

@@ -54,9 +54,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   // back from one basic block (clamped indices, no branches): the prologue
   // below then waits only for the small loads while the whole state slice is
   // in flight.
-  const bool gla = a.gate == LA_GATE_GLA;
+  const bool gla = a.gate == LA_GATE_GLA, sel = a.gate == LA_GATE_SEL;
   const int iq = min(tid, DK - 1), iv = min(tid, E - 1), ir = min(tid, R - 1);
-  const InT* gp = gla ? static_cast<const InT*>(a.g) + bh * R + ir : q + bh * DK + iq;
+  // GLA: one gate input per feature; selective: one per head
+  const InT* gp = gla ? static_cast<const InT*>(a.g) + bh * R + ir
+                      : (sel ? static_cast<const InT*>(a.g) + bh : q + bh * DK + iq);
   const InT rq = q[bh * DK + iq], rk = k[bh * DK + iq], rv = v[bh * E + iv], rg = *gp;
   long long si = bh;  // this head's state
   if (a.slot != nullptr) {
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) st[p] = float4{0.f, 0.f, 0.f, 0.f};
   }
-  const float xq = to_f32(rq), xk = to_f32(rk), xv = to_f32(rv), xg = gla ? to_f32(rg) : 0.f, xz = rz;
+  const float xq = to_f32(rq), xk = to_f32(rk), xv = to_f32(rv), xg = (gla || sel) ? to_f32(rg) : 0.f, xz = rz;
 
   // features and gate of this token
   // unconditional (clamped) writes keep the loads above out of branches;
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     }
     float al = 1.f;
     if (a.gate == LA_GATE_DECAY) al = a.gamma[bh % a.H];
-    if (a.gate == LA_GATE_GLA) al = __expf(gla_log_alpha(xg, a.inv_tau));
+    if (a.gate == LA_GATE_GLA || a.gate == LA_GATE_SEL) al = __expf(gla_log_alpha(xg, a.inv_tau));
     spq[tid] = pq;
     spk[tid] = pk;
     sal[tid] = al;
@@ -172,7 +174,7 @@ template <int R, int E, int DK, int FMAP>
 static la_status run_decode(const DecodePlan& p) {
   DecodeArgs a{p.S,         p.z,          p.q,    p.k,    p.v,         p.g,
                p.omega,     p.gamma,      p.out,  p.H,    p.in_dtype,  p.out_dtype,
-               p.gate,      p.eps,        p.gate == LA_GATE_GLA ? 1.f / p.tau : 0.f,
+               p.gate,      p.eps,        (p.gate == LA_GATE_GLA || p.gate == LA_GATE_SEL) ? 1.f / p.tau : 0.f,
                p.slot,      p.nslot,      p.flags};
   if (p.in_dtype == LA_BF16)
     hipLaunchKernelGGL((decode_step_kernel<R, E, DK, FMAP, bf16>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256), 0,

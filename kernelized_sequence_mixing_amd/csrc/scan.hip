@@ -47,14 +47,14 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S
       const int s = min(s0 + j, P - 1);
       const int si = reverse ? P - 1 - s : s;
       d[j] = base[si * stride];
-      G[j] = gate == GT_GLA ? logG[(bh * P + si) * R + row] : 0.f;
+      G[j] = (gate == GT_GLA || gate == GT_SEL) ? logG[(bh * P + si) * R + row] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int s = s0 + j;
       if (s < P) {
         base[(reverse ? P - 1 - s : s) * stride] = cur;
-        const float g = gate == GT_GLA ? __expf(G[j]) : seg_decay;
+        const float g = (gate == GT_GLA || gate == GT_SEL) ? __expf(G[j]) : seg_decay;
         cur = g * cur + d[j];
       }
     }

@@ -20,8 +20,8 @@ def gpu_gate(inp):
     kind = inp["gate"]
     if kind == "decay":
         return ("decay", dev(inp["gamma"]))
-    if kind == "gla":
-        return ("gla", dev(inp["g"]), inp["tau"])
+    if kind in ("gla", "sel"):
+        return (kind, dev(inp["g"]), inp["tau"])
     return None
 
 
@@ -30,13 +30,13 @@ def oracle_gate(inp, heads=None, t_slice=None):
     if kind == "decay":
         gam = to_f64(inp["gamma"])
         return ("decay", gam)
-    if kind == "gla":
+    if kind in ("gla", "sel"):
         g = to_f64(inp["g"])
         if heads is not None:
             g = g[heads[0]:heads[0] + 1, heads[1]:heads[1] + 1]
         if t_slice is not None:
             g = g[:, :, t_slice]
-        return ("gla", g, inp["tau"])
+        return (kind, g, inp["tau"])
     return None
 
 
@@ -58,8 +58,8 @@ def oracle_forward(inp, head=None, eps=None, S0=None, z0=None):
     if head is not None:
         b, h = head
         Q, K, V = (x[b:b + 1, h:h + 1] for x in (Q, K, V))
-        if gate is not None and gate[0] == "gla":
-            gate = ("gla", gate[1][b:b + 1, h:h + 1], gate[2])
+        if gate is not None and gate[0] in ("gla", "sel"):
+            gate = (gate[0], gate[1][b:b + 1, h:h + 1], gate[2])
         if gate is not None and gate[0] == "decay":
             gate = ("decay", gate[1][h:h + 1])
     om = to_f64(inp["omega"]) if inp["fmap"] == "favor" else None

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     lib = N.lib()
-    assert lib.la_abi_version() == 4
+    assert lib.la_abi_version() == 5
     names = [lib.la_status_str(i).decode() for i in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_ALIAS",
                      "LA_ERR_HIP"]
@@ -143,6 +143,13 @@ def _forward(a):
 
 
 BAD_FORWARD = [
+    ("sel favor", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP, fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP),
+     N.LA_ERR_UNSUPPORTED),
+    ("sel no g", dict(gkind=N.LA_GATE_SEL), N.LA_ERR_INVALID_ARG),
+    ("sel tau 0", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP, tau=0.0), N.LA_ERR_INVALID_ARG),
+    ("sel noncausal", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP, causal=0, in_dt=N.LA_F32, out_dt=N.LA_F32),
+     N.LA_ERR_INVALID_ARG),
+    ("gate kind 4", dict(gkind=4), N.LA_ERR_INVALID_ARG),
     ("identity noncausal", dict(fkind=N.LA_FMAP_IDENTITY, causal=0, in_dt=N.LA_F32, out_dt=N.LA_F32),
      N.LA_ERR_UNSUPPORTED),
     ("identity r != d_k", dict(fkind=N.LA_FMAP_IDENTITY, r=32), N.LA_ERR_INVALID_ARG),
@@ -240,6 +247,7 @@ def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAK
 BAD_BACKWARD = [
     ("n=0", dict(n=0), {}, N.LA_ERR_INVALID_ARG),
     ("identity", dict(fkind=N.LA_FMAP_IDENTITY), {}, N.LA_ERR_UNSUPPORTED),
+    ("sel", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), {}, N.LA_ERR_UNSUPPORTED),
     ("noncausal", dict(causal=0), {}, N.LA_ERR_UNSUPPORTED),
     ("favor", dict(fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
     ("gla without dg", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),

@@ -34,11 +34,11 @@ def _gate64(inp, head=None):
     if inp["gate"] == "decay":
         gam = to_f64(inp["gamma"])
         return ("decay", gam if head is None else gam[head[1]:head[1] + 1])
-    if inp["gate"] == "gla":
+    if inp["gate"] in ("gla", "sel"):
         g = to_f64(inp["g"])
         if head is not None:
             g = g[head[0]:head[0] + 1, head[1]:head[1] + 1]
-        return ("gla", g, inp["tau"])
+        return (inp["gate"], g, inp["tau"])
     return None
 
 
@@ -72,7 +72,7 @@ def _case(gate, d, dv, B, H, n, seed=2):
     return wl, make_inputs(wl, seed=seed, B=B, H=H, n=n)
 
 
-CASES = [(g, d, dv, B, H, n) for g in ("none", "decay", "gla")
+CASES = [(g, d, dv, B, H, n) for g in ("none", "decay", "gla", "sel")
          for (d, dv, B, H, n) in ((64, 64, 2, 4, 777), (64, 128, 2, 4, 300), (128, 64, 2, 3, 300),
                                   (32, 64, 2, 2, 129), (128, 128, 1, 2, 200), (64, 64, 4, 16, 1285))]
 
@@ -89,16 +89,15 @@ def test_ssm_parity(gate, d, dv, B, H, n):
     assert e < TOL_TERMS
 
 
-@pytest.mark.parametrize("gate", ["none", "gla"])
+@pytest.mark.parametrize("gate", ["none", "gla", "sel"])
 def test_ssm_resumes_from_state(gate):
     """A carried-in state (the oracle's state after a 150-token prefix) and the
     final state: the continuation equals one pass over the whole sequence."""
     wl, inp = _case(gate, 64, 64, 2, 4, 700, seed=6)
     m = 150
-    first = {k: (v[:, :, :m].contiguous() if isinstance(v, torch.Tensor) and v.dim() == 4 else v)
-             for k, v in inp.items()}
-    second = {k: (v[:, :, m:].contiguous() if isinstance(v, torch.Tensor) and v.dim() == 4 else v)
-              for k, v in inp.items()}
+    seq = ("Q", "K", "V", "g")  # the per-token inputs (the selective gate's g is [B, H, n])
+    first = {k: (v[:, :, :m].contiguous() if k in seq else v) for k, v in inp.items()}
+    second = {k: (v[:, :, m:].contiguous() if k in seq else v) for k, v in inp.items()}
     _, _, S1, z1 = oracle_ssm(first)
     o, sc, Sr, zr = oracle_ssm(second, S0=S1, z0=z1)
     got, S, z = run(second, torch.from_numpy(S1.astype(np.float32)), torch.from_numpy(z1.astype(np.float32)),
@@ -124,7 +123,7 @@ def test_ssm_full_size_sampled_heads():
         assert e < TOL_TERMS
 
 
-@pytest.mark.parametrize("gate", ["none", "decay", "gla"])
+@pytest.mark.parametrize("gate", ["none", "decay", "gla", "sel"])
 def test_ssm_decode_step(gate):
     """The recurrent step with identity features (fp32 arithmetic): one step
     from a carried state equals the oracle's step."""
@@ -135,15 +134,15 @@ def test_ssm_decode_step(gate):
     g = None
     if gate == "decay":
         g = ("decay", dev(inp["gamma"]))
-    elif gate == "gla":
-        g = ("gla", dev(inp["g"]), wl.tau)
+    elif gate in ("gla", "sel"):
+        g = (gate, dev(inp["g"]), wl.tau)
     out = ksm.decode_step(S, z, dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), fmap="identity", gate=g, eps=wl.eps)
     torch.cuda.synchronize()
     og = None
     if gate == "decay":
         og = ("decay", to_f64(inp["gamma"]))
-    elif gate == "gla":
-        og = ("gla", to_f64(inp["g"]), wl.tau)
+    elif gate in ("gla", "sel"):
+        og = (gate, to_f64(inp["g"]), wl.tau)
     o, S1, z1 = orc.decode_step(to_f64(inp["S0"]), to_f64(inp["z0"]), to_f64(inp["q"]), to_f64(inp["k"]),
                                 to_f64(inp["v"]), "identity", None, og, eps=wl.eps)
     sc, _, _ = orc.decode_step(np.abs(to_f64(inp["S0"])), to_f64(inp["z0"]), np.abs(to_f64(inp["q"])),
@@ -182,4 +181,55 @@ def test_ssm_serving_batch():
         e2 = term_err(o2[b:b + 1], o[:, :, L:], sc[:, :, L:])
         print(f"  ssm batch seq {b}: prefill {e1:.2e} step {e2:.2e}", flush=True)
         assert e1 < TOL_TERMS and e2 < TOL_TERMS
+        off += L
+
+
+# ------------------------------------------------ the selective scalar gate, normalised
+
+SEL_CASES = [(64, 64, 2, 4, 777), (64, 128, 2, 4, 300), (128, 64, 2, 3, 300), (32, 64, 2, 2, 129),
+             (128, 128, 1, 2, 200), (64, 64, 4, 16, 1285), (64, 64, 2, 1, 1), (64, 64, 2, 1, 65)]
+
+
+@pytest.mark.parametrize("d,dv,B,H,n", SEL_CASES)
+def test_selective_gate_elu1_parity(d, dv, B, H, n):
+    """elu+1 attention under the scalar selective gate (the RetNet decay made
+    input-dependent), every built shape, several segments with ragged tails and
+    tiny n, every head, to the row-wise tolerance of the bf16 paths."""
+    from _helpers import TOL_BF16, check_close, oracle_forward, run_forward
+    wl = WORKLOADS["causal_elu1"].resized(d_k=d, d_v=dv, r=d, gate="sel", qk_scale=d ** -0.5, v_scale=dv ** -0.5)
+    inp = make_inputs(wl, seed=4, B=B, H=H, n=n)
+    out = run_forward(inp)
+    ref, _, _ = oracle_forward(inp)
+    check_close(out, ref, TOL_BF16, f"elu1 sel d{d}x{dv} B{B} H{H} n{n}")
+
+
+def test_selective_gate_serving_batch():
+    """A ragged prefill under the selective gate through la_forward_batch,
+    states into slots, then a one-token step (the decode kernel on the slots)."""
+    import kernelized_sequence_mixing_amd as ksm
+    from _helpers import TOL_BF16, check_close
+    wl = WORKLOADS["causal_elu1"].resized(gate="sel")
+    H = 4
+    lens = [130, 1, 64, 700]
+    full = [make_inputs(wl, seed=80 + b, B=1, H=H, n=L + 1) for b, L in enumerate(lens)]
+    pre = {k: torch.cat([f[k][:, :, :L] for f, L in zip(full, lens)], dim=2).contiguous() for k in ("Q", "K", "V", "g")}
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    ids = torch.tensor([1, 3, 0, 2], dtype=torch.int32, device="cuda")
+    S = torch.zeros((4, H, 64, 64), dtype=torch.float32, device="cuda")
+    z = torch.zeros((4, H, 64), dtype=torch.float32, device="cuda")
+    o1 = ksm.forward_batch(dev(pre["Q"]), dev(pre["K"]), dev(pre["V"]), cu_seqlens=cu, max_seqlen=max(lens),
+                           state=(S, z), slot_ids=ids, write=True, gate=("sel", dev(pre["g"]), wl.tau),
+                           eps=wl.eps).cpu()
+    step = {k: torch.cat([f[k][:, :, L:L + 1] for f, L in zip(full, lens)], dim=0).contiguous()
+            for k in ("Q", "K", "V", "g")}
+    o2 = ksm.forward_batch(dev(step["Q"]), dev(step["K"]), dev(step["V"]), state=(S, z), slot_ids=ids, read=True,
+                           write=True, gate=("sel", dev(step["g"]), wl.tau), eps=wl.eps).cpu()
+    torch.cuda.synchronize()
+    off = 0
+    for b, L in enumerate(lens):
+        f = full[b]
+        o = orc.causal_recurrent(to_f64(f["Q"]), to_f64(f["K"]), to_f64(f["V"]), "elu1", None,
+                                 ("sel", to_f64(f["g"]), wl.tau), eps=wl.eps)[0]
+        check_close(o1[:, :, off:off + L], o[:, :, :L], TOL_BF16, f"sel batch prefill seq {b}")
+        check_close(o2[b:b + 1], o[:, :, L:], TOL_BF16, f"sel batch step seq {b}")
         off += L

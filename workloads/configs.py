@@ -19,7 +19,7 @@ class Workload:
     r: int                 # feature dimension (d_k for elu1)
     fmap: str              # "elu1" | "favor" | "identity" (the state-space read-out)
     causal: bool
-    gate: str              # "none" | "decay" | "gla"
+    gate: str              # "none" | "decay" | "gla" | "sel" (scalar selective)
     dtype: str             # input dtype: "f32" | "bf16"
     qk_scale: float        # Q, K ~ N(0,1) * qk_scale
     v_scale: float         # V ~ N(0,1) * v_scale
@@ -60,6 +60,9 @@ WORKLOADS = {
     "ssm_selective": Workload(
         "ssm_selective", B=2, H=16, n=16384, d_k=64, d_v=64, r=64, fmap="identity",
         causal=True, gate="gla", dtype="bf16", qk_scale=64 ** -0.5, v_scale=1.0),
+    "ssm_scalar": Workload(
+        "ssm_scalar", B=2, H=16, n=16384, d_k=64, d_v=64, r=64, fmap="identity",
+        causal=True, gate="sel", dtype="bf16", qk_scale=64 ** -0.5, v_scale=1.0),
     "favor_causal": Workload(
         "favor_causal", B=1, H=8, n=32768, d_k=64, d_v=64, r=256, fmap="favor",
         causal=True, gate="none", dtype="bf16", qk_scale=64 ** -0.25, v_scale=1.0),

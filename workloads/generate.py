@@ -83,6 +83,8 @@ def make_inputs(wl, seed: int = 0, *, B=None, H=None, n=None, qk_scale=None,
     if wl.gate == "gla":
         g = rng.standard_normal((B, H, n, wl.r), dtype=f32)
         out["g"] = _cast(g, wl.dtype)
+    if wl.gate == "sel":
+        out["g"] = _cast(rng.standard_normal((B, H, n), dtype=f32), wl.dtype)
     if wl.gate == "decay":
         out["gamma"] = torch.from_numpy(retnet_gammas(H))
     if wl.fmap == "favor":
@@ -116,6 +118,8 @@ def _decode_inputs(wl: Workload, rng, B, H, qs, vs) -> dict:
          "q": _cast(q, wl.dtype), "k": _cast(k, wl.dtype), "v": _cast(v, wl.dtype)}
     if wl.gate == "gla":
         d["g"] = _cast(rng.standard_normal((B, H, r), dtype=f32), wl.dtype)
+    if wl.gate == "sel":
+        d["g"] = _cast(rng.standard_normal((B, H), dtype=f32), wl.dtype)
     if wl.gate == "decay":
         d["gamma"] = torch.from_numpy(retnet_gammas(H))
     if wl.fmap == "favor":
