@@ -77,7 +77,9 @@ struct FavorFwdLayout {
   static constexpr int bytes_dk = bytes;
 };
 
-// Segment-state pass: kh/kl hold the (decay-weighted) key features.
+// Segment-state pass: kh/kl hold the (decay-weighted) key features; omega
+// sits in LDS for the whole kernel when it is at most 32 KB (read per feature
+// block by every wave, it cost more from the cache than the state update).
 template <int R, int E>
 struct FavorSegLayout {
   using F = FavorBlock<R>;
@@ -85,9 +87,12 @@ struct FavorSegLayout {
   static constexpr int kh_off = 0;
   static constexpr int kl_off = kh_off + kChunk * F::ROW + 16;
   static constexpr int v_off = kl_off + kChunk * F::ROW + 16;
-  static constexpr int bytes = v_off + kChunk * EP * 2;
+  static constexpr int om_off = v_off + kChunk * EP * 2;
+  static constexpr int bytes = om_off;
   template <int DK>
-  static constexpr int bytes_dk = bytes;
+  static constexpr bool om_lds = R * DK <= 16384;
+  template <int DK>
+  static constexpr int bytes_dk = bytes + (om_lds<DK> ? R * DK * 2 : 0);
 };
 
 // Per-lane byte offsets of every LDS access pattern, built once per feature
@@ -192,6 +197,40 @@ __device__ __forceinline__ void favor_load_omega(bf16x8 (&om)[FavorBlock<R>::FT]
   for (int ft = 0; ft < FavorBlock<R>::FT; ++ft)
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) om[ft][ks] = *reinterpret_cast<const bf16x8*>(orow + 16 * ft * DK + 32 * ks);
+}
+
+// omega [R][DK] in LDS: 16-byte chunk k of row r at chunk k ^ favor_om_swz(r),
+// so that the projection's operand reads (rows c of a 16-row tile, chunks
+// 4 ks + g, lanes in groups of rows 0..7 x g in {0, 1}) reach all banks.
+template <int DK>
+__device__ __forceinline__ int favor_om_swz(int r) {
+  if constexpr (DK == 32) return 2 * ((r >> 2) & 1);
+  else if constexpr (DK == 64) return r & 6;
+  else return 2 * (r & 7);
+}
+
+template <int R, int DK>
+__device__ __forceinline__ void favor_stage_omega(const bf16* omega, char* sm, int om_off, int tid) {
+  constexpr int CPR = DK / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int c = tid; c < R * CPR; c += 256) {
+    const int r = c / CPR, k = c % CPR;
+    lds<bf16x8>(sm, om_off + r * DK * 2 + 16 * (k ^ favor_om_swz<DK>(r))) =
+        *reinterpret_cast<const bf16x8*>(omega + (long long)r * DK + 8 * k);
+  }
+}
+
+// favor_load_omega's operands, from the LDS copy.
+template <int R, int DK, class LN>
+__device__ __forceinline__ void favor_lds_omega(bf16x8 (&om)[FavorBlock<R>::FT][DK / 32], char* sm, int om_off,
+                                                int fb, const LN& ln) {
+#pragma unroll
+  for (int ft = 0; ft < FavorBlock<R>::FT; ++ft)
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const int r = fb * FavorBlock<R>::FB + 16 * ft + ln.c16;
+      om[ft][ks] = lds<bf16x8>(sm, om_off + r * DK * 2 + 16 * ((4 * ks + ln.g4) ^ favor_om_swz<DK>(r)));
+    }
 }
 
 // hi/lo tile chunks of eight features (two adjacent 16-feature tiles), zero
@@ -388,8 +427,15 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
 
   RawChunk<R, E, DK, FM_FAVOR, GT_NONE, false> raw;
   raw.load(a, tok0, t_begin, t_end, lane, w);
+  constexpr bool OM_LDS = LY::template om_lds<DK>;
   bf16x8 om[F::FT][DK / 32];
-  favor_load_omega<R, DK>(om, a.omega, 0, LN(lane));
+  if constexpr (OM_LDS) {
+    favor_stage_omega<R, DK>(a.omega, sm, LY::om_off, threadIdx.x);
+    lds_barrier();
+    favor_lds_omega<R, DK>(om, sm, LY::om_off, 0, LN(lane));
+  } else {
+    favor_load_omega<R, DK>(om, a.omega, 0, LN(lane));
+  }
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int L = min(kChunk, sv.len - t0);
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
@@ -404,7 +450,11 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
       // pass 1 keeps only the keys of the state update (decay-weighted for RetNet)
       favor_project<R, DK, true, GATE == GT_DECAY, GATE == GT_DECAY>(ln, xk, shk, om, L, lg2gam, sm, LY::kh_off,
                                                                      LY::kl_off, LY::kh_off, LY::kl_off, w);
-      favor_load_omega<R, DK>(om, a.omega, fb + 1 < F::NFB ? fb + 1 : 0, ln);  // next block (block 0 of the next chunk)
+      // next block (block 0 of the next chunk)
+      if constexpr (OM_LDS)
+        favor_lds_omega<R, DK>(om, sm, LY::om_off, fb + 1 < F::NFB ? fb + 1 : 0, ln);
+      else
+        favor_load_omega<R, DK>(om, a.omega, fb + 1 < F::NFB ? fb + 1 : 0, ln);
       lds_barrier();
       favor_state_block<R, E>(ln, S, Z[fb], fb, sm, LY::kh_off, LY::kl_off, LY::v_off, gsc, w);
       lds_barrier();
