@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .la_oracle import feature_map
+from .la_oracle import feature_map, normalised
 
 __all__ = ["feature_map_vjp", "forward_terms", "backward", "backward_gla"]
 
@@ -38,11 +38,14 @@ def feature_map_vjp(x, dphi, fmap="elu1", omega=None):
 
     elu+1: phi'(x) = 1 for x > 0 and exp(x) for x <= 0 (the derivative of
     elu(x) + 1 with slope parameter 1; both sides give 1 at x = 0).
+    identity (the state-space form): phi'(x) = 1.
     FAVOR+: phi_m = exp(w_m.x - |x|^2/2) / sqrt(r) has d phi_m / dx =
     phi_m (w_m - x), so dL/dx = sum_m dphi_m phi_m (w_m - x).
     """
     x = _f64(x)
     dphi = _f64(dphi)
+    if fmap == "identity":
+        return dphi
     if fmap == "elu1":
         return dphi * np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
     if fmap == "favor":
@@ -102,6 +105,8 @@ def forward_terms(Q, K, V, fmap="elu1", omega=None, causal=True, gate=None, eps=
         z0 = _f64(z0)
         num = num + c[None, :, :, None] * np.einsum("bhir,bhre->bhie", pq, S0)
         den = den + c[None] * np.einsum("bhir,bhr->bhi", pq, z0)
+    if not normalised(fmap):
+        den = np.ones_like(den)   # the state-space read-out o = num
     o = num / den[..., None]
     return pq, pk, D, c, W, num, den, o
 
@@ -112,6 +117,7 @@ def backward(Q, K, V, dO, fmap="elu1", omega=None, causal=True, gate=None, eps=1
     Chain rule through the forward of ``forward_terms``:
       o_i = num_i / den_i            => dnum_i = dO_i / den_i = g_i,
                                         dden_i = -(dO_i . o_i) / den_i = h_i
+      (the state-space read-out o_i = num_i has g_i = dO_i and h_i = 0)
       num_i, den_i linear in W_ij    => dW_ij = g_i . v_j + h_i,  dV_j = sum_i W_ij g_i
       W_ij = (phi_q_i . phi_k_j) D_ij => dM_ij = dW_ij D_ij,
                                         dphi_q_i = sum_j dM_ij phi_k_j + c_i (S0 g_i + h_i z0),
@@ -122,7 +128,7 @@ def backward(Q, K, V, dO, fmap="elu1", omega=None, causal=True, gate=None, eps=1
     dO = _f64(dO)
     pq, pk, D, c, W, num, den, o = forward_terms(Q, K, V, fmap, omega, causal, gate, eps, S0, z0)
     g = dO / den[..., None]
-    h = -np.sum(dO * o, axis=-1) / den
+    h = -np.sum(dO * o, axis=-1) / den if normalised(fmap) else np.zeros(den.shape)
     dW = np.einsum("bhie,bhje->bhij", g, V) + h[..., None]
     dV = np.einsum("bhij,bhie->bhje", W, g)
     dM = dW * D[None]
@@ -179,9 +185,11 @@ def backward_gla(Q, K, V, dO, g, tau, fmap="elu1", omega=None, eps=1e-6, S0=None
         z0 = _f64(z0)
         num = num + np.einsum("bhik,bhke->bhie", pq * c, S0)
         den = den + np.einsum("bhik,bhk->bhi", pq * c, z0)
+    if not normalised(fmap):
+        den = np.ones_like(den)   # the state-space read-out o = num
     o = num / den[..., None]
     gg = dO / den[..., None]
-    h = -np.sum(dO * o, axis=-1) / den
+    h = -np.sum(dO * o, axis=-1) / den if normalised(fmap) else np.zeros(den.shape)
     dW = (np.einsum("bhie,bhje->bhij", gg, V) + h[..., None]) * mask[None, None]
     dV = np.einsum("bhij,bhie->bhje", W, gg)
     dpq = np.einsum("bhij,bhjk,bhijk->bhik", dW, pk, D)

@@ -25,7 +25,8 @@ def _loss(Q, K, V, dO, fmap, omega, causal, gate, eps, S0=None, z0=None):
 
 CASES = [("elu1", False, "none", False), ("elu1", True, "none", False), ("elu1", True, "decay", False),
          ("elu1", True, "decay", True), ("elu1", True, "none", True), ("favor", False, "none", False),
-         ("favor", True, "none", True), ("favor", True, "decay", False)]
+         ("favor", True, "none", True), ("favor", True, "decay", False),
+         ("identity", True, "none", False), ("identity", True, "decay", True)]
 
 
 @pytest.mark.parametrize("fmap,causal,gate_kind,with_state", CASES)
@@ -95,8 +96,9 @@ def test_output_invariant_to_query_feature_scale(causal, gate_kind):
     assert np.max(np.abs(s)) < 1e-12 * np.max(np.abs(dQ))
 
 
-@pytest.mark.parametrize("with_state", [False, True])
-def test_gla_gradients_match_finite_differences(with_state):
+@pytest.mark.parametrize("fmap,with_state", [("elu1", False), ("elu1", True), ("identity", False),
+                                             ("identity", True)])
+def test_gla_gradients_match_finite_differences(fmap, with_state):
     """dQ, dK, dV and the gradient of the raw gate input g of the GLA form,
     against central differences of the recurrent oracle (which applies the gate
     step by step and is pinned against the explicit weights)."""
@@ -112,10 +114,10 @@ def test_gla_gradients_match_finite_differences(with_state):
         S0 = np.abs(RNG.standard_normal((B, H, d, e)))
         z0 = np.abs(RNG.standard_normal((B, H, d))) + 0.5
     eps = 1e-3
-    dQ, dK, dV, dg = bwd.backward_gla(Q, K, V, dO, G, tau, "elu1", None, eps, S0, z0)
+    dQ, dK, dV, dg = bwd.backward_gla(Q, K, V, dO, G, tau, fmap, None, eps, S0, z0)
 
     def loss(Q_, K_, V_, G_):
-        o, _, _ = orc.causal_recurrent(Q_, K_, V_, "elu1", None, ("gla", G_, tau), eps, S0=S0, z0=z0)
+        o, _, _ = orc.causal_recurrent(Q_, K_, V_, fmap, None, ("gla", G_, tau), eps, S0=S0, z0=z0)
         return float(np.sum(o * dO))
     step = 1e-6
     for idx, (X, Gr) in enumerate(((Q, dQ), (K, dK), (V, dV), (G, dg))):
@@ -144,3 +146,19 @@ def test_gla_unit_gates_reduce_to_ungated():
     for a, b in zip(got[:3], want):
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
     assert np.all(got[3] == 0.0)
+
+
+def test_identity_gradients_closed_form():
+    """The state-space read-out y = tril(Q K^T) V is bilinear: dV = tril(Q K^T)^T dO,
+    dQ = tril(dO V^T) K, dK = tril(dO V^T)^T Q (numpy matmuls)."""
+    B, H, n, d, e = 1, 1, 7, 4, 3
+    Q = RNG.standard_normal((B, H, n, d))
+    K = RNG.standard_normal((B, H, n, d))
+    V = RNG.standard_normal((B, H, n, e))
+    dO = RNG.standard_normal((B, H, n, e))
+    dQ, dK, dV = bwd.backward(Q, K, V, dO, "identity", None, True, None, 1e-6)
+    A = np.tril(Q[0, 0] @ K[0, 0].T)
+    M = np.tril(dO[0, 0] @ V[0, 0].T)
+    np.testing.assert_allclose(dV[0, 0], A.T @ dO[0, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dQ[0, 0], M @ K[0, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dK[0, 0], M.T @ Q[0, 0], rtol=1e-12, atol=1e-12)
