@@ -265,8 +265,9 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  *   workspace: device scratch of at least la_backward_workspace_size bytes,
  *   256-byte aligned (segment states of both directions, g and h per token;
  *   GLA: also dQ~ . Q~ per token and feature and per-segment summed log-gates).
- * Supported (else LA_ERR_UNSUPPORTED): causal == 1, ELU1, any gate,
- * (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
+ * Supported (else LA_ERR_UNSUPPORTED): causal == 1, ELU1 or IDENTITY (the
+ * state-space read-out: g_i = dO_i, h_i = 0, phi' = 1), gate NONE, DECAY or
+ * GLA, (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
  * inputs, each other or the workspace (LA_ERR_ALIAS). Numerics as la_forward:
  * bf16 MFMA operands (phi, values, g, the scores and dW), fp32 accumulation,
  * states, denominators and the sums behind dg.

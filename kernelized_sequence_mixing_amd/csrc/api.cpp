@@ -214,7 +214,8 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
   if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
   const int gk = gate_kind(g);
   if (!causal && gk != LA_GATE_NONE) return LA_ERR_INVALID_ARG;
-  if (!causal || f->kind != LA_FMAP_ELU1 || gk == LA_GATE_SEL) return LA_ERR_UNSUPPORTED;
+  if (!causal || (f->kind != LA_FMAP_ELU1 && f->kind != LA_FMAP_IDENTITY) || gk == LA_GATE_SEL)
+    return LA_ERR_UNSUPPORTED;
   if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   const int key = p->d_k * 1000 + p->d_v;
   if (key != 64064 && key != 64128 && key != 128064) return LA_ERR_UNSUPPORTED;

@@ -12,7 +12,7 @@ static la_status launch_with_lds(K kernel, dim3 grid, int lds, hipStream_t st, c
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
-template <int R, int E, int GATE>
+template <int R, int E, int GATE, int FMAP>
 static la_status run_backward(const BwdPlan& p) {
   static_assert(Waves<R, E>::NW == 4, "the backward kernels use four-wave workgroups");
   const unsigned BH = unsigned(p.B) * unsigned(p.H);
@@ -59,7 +59,7 @@ static la_status run_backward(const BwdPlan& p) {
     a1.g = b.gl;
     a1.inv_tau = b.inv_tau;
     a1.logG_out = p.ws_logG;
-    auto k1 = causal_segment_state<R, E, R, FM_ELU1, GATE>;
+    auto k1 = causal_segment_state<R, E, R, FMAP, GATE>;
     constexpr int lds1 = SegLayout<R, E, GATE>::bytes;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
         hipSuccess)
@@ -77,37 +77,48 @@ static la_status run_backward(const BwdPlan& p) {
     b.in_head = (long long)R * E;
     b.in_seg = 0;
   }
-  if ((st = launch_with_lds(bwd_pass_a<R, E, GATE>, dim3(p.P, BH), BwdALayout<R, E, GATE>::bytes, p.stream, b)) !=
+  if ((st = launch_with_lds(bwd_pass_a<R, E, GATE, FMAP>, dim3(p.P, BH), BwdALayout<R, E, GATE>::bytes, p.stream, b)) !=
       LA_OK)
     return st;
   if (p.P > 1) {
     if constexpr (GATE == GT_GLA)
-      st = launch_with_lds(bwd_rstate_gla<R, E>, dim3(p.P - 1, BH), BwdRGLayout<R, E>::bytes, p.stream, b);
+      st = launch_with_lds(bwd_rstate_gla<R, E, FMAP>, dim3(p.P - 1, BH), BwdRGLayout<R, E>::bytes, p.stream, b);
     else
-      st = launch_with_lds(bwd_rstate<R, E, GATE>, dim3(p.P - 1, BH), BwdRLayout<R, E, GATE>::bytes, p.stream, b);
+      st = launch_with_lds(bwd_rstate<R, E, GATE, FMAP>, dim3(p.P - 1, BH), BwdRLayout<R, E, GATE>::bytes, p.stream,
+                           b);
     if (st != LA_OK) return st;
     if ((st = launch_segment_scan_reverse(p, p.ws_R, p.ws_rh, GATE == GT_GLA ? p.ws_logG : nullptr)) != LA_OK)
       return st;
   }
-  return launch_with_lds(bwd_pass_b<R, E, GATE>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b);
+  return launch_with_lds(bwd_pass_b<R, E, GATE, FMAP>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b);
 }
 
-template <int R, int E>
+template <int R, int E, int FMAP>
 static la_status run_backward_gated(const BwdPlan& p) {
   switch (p.gate) {
-    case LA_GATE_NONE: return run_backward<R, E, GT_NONE>(p);
-    case LA_GATE_DECAY: return run_backward<R, E, GT_DECAY>(p);
-    case LA_GATE_GLA: return run_backward<R, E, GT_GLA>(p);
+    case LA_GATE_NONE: return run_backward<R, E, GT_NONE, FMAP>(p);
+    case LA_GATE_DECAY: return run_backward<R, E, GT_DECAY, FMAP>(p);
+    case LA_GATE_GLA: return run_backward<R, E, GT_GLA, FMAP>(p);
     default: return LA_ERR_UNSUPPORTED;
   }
 }
 
-// Built shapes: elu+1 with (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}; no gate, RetNet decay or GLA.
+template <int R, int E>
+static la_status run_backward_fmap(const BwdPlan& p) {
+  switch (p.fmap) {
+    case LA_FMAP_ELU1: return run_backward_gated<R, E, FM_ELU1>(p);
+    case LA_FMAP_IDENTITY: return run_backward_gated<R, E, FM_IDENT>(p);
+    default: return LA_ERR_UNSUPPORTED;
+  }
+}
+
+// Built shapes: elu+1 or the state-space form with (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}; no gate,
+// RetNet decay or GLA.
 la_status launch_backward(const BwdPlan& p) {
   switch (p.r * 1000 + p.dv) {
-    case 64064: return run_backward_gated<64, 64>(p);
-    case 64128: return run_backward_gated<64, 128>(p);
-    case 128064: return run_backward_gated<128, 64>(p);
+    case 64064: return run_backward_fmap<64, 64>(p);
+    case 64128: return run_backward_fmap<64, 128>(p);
+    case 128064: return run_backward_fmap<128, 64>(p);
     default: return LA_ERR_UNSUPPORTED;
   }
 }

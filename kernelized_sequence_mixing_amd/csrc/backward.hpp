@@ -1,4 +1,5 @@
-// Backward pass of the chunkwise causal kernel (elu+1 features; no gate, the
+// Backward pass of the chunkwise causal kernel (elu+1 features or the
+// state-space form's identity features without a normaliser; no gate, the
 // RetNet decay or the diagonal GLA gate), for training with the parallel form ("Recurrent
 // Reformulation", "Linear Attention Mechanisms" (dileepadev.github.io): the
 // layer is trained in parallel and served as an RNN).
@@ -172,7 +173,7 @@ __device__ __forceinline__ float bwd_h(char* sm, int hp_off, int i) {
   return -s;
 }
 
-template <int R, int E, int GATE>
+template <int R, int E, int GATE, int FMAP = FM_ELU1>
 __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = BwdALayout<R, E, GATE>;
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   ca.g = b.gl;
   ca.inv_tau = b.inv_tau;
 
-  using Raw = RawChunk<R, E, R, FM_ELU1, GATE, true, NW>;
+  using Raw = RawChunk<R, E, R, FMAP, GATE, true, NW>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
   RowsE<E> rdo;
@@ -225,12 +226,14 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   }
   z_load<R, NW>(Z, b.S_in != nullptr ? b.z_in + (bh * b.in_head + s * b.in_seg) / E : nullptr, lane, w);
   z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
+  // the state-space read-out: h = 0 (the partial sums stay zero)
+  if constexpr (FMAP == FM_IDENT) lds<float>(sm, LY::hp_off + 4 * threadIdx.x) = 0.f;
 
   for (int ci = 0; ci < nch; ++ci) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
     // ---- prelude: features, values, dO, and the bf16 image of S
-    chunk_prelude<R, E, R, FM_ELU1, GATE, true, NW, true, GATE == GT_GLA ? kPreQD : 0>(
+    chunk_prelude<R, E, R, FMAP, GATE, true, NW, true, GATE == GT_GLA ? kPreQD : 0>(
         raw, ca, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off, LY::v_off, LY::gam_off, 0, lane, w, LY::qd_off);
     rdo.store(sm, LY::g_off, L, lane, w);
     state_image<R, E>(S, sm, LY::sb_off, lane, w);
@@ -239,7 +242,9 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     lds_barrier();
 
     // ---- scores A (masked, RetNet-weighted) and their row sums; phi(q) . z
-    {
+    // (the state-space read-out has no normaliser: g = dO, h = 0, and neither
+    // the scores nor o are needed)
+    if constexpr (FMAP != FM_IDENT) {
       const int qw = w;
       const int q = 16 * qw + c16;
       bf16x8 qop[KP];
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     lds_barrier();
 
     // ---- o (fp32, not stored), g = dO / den (bf16) and the wave's share of g . o
-    {
+    if constexpr (FMAP != FM_IDENT) {
       bf16x8 Sop[KP][NEB];
       state_operand<R, E>(S, Sop);
 #pragma unroll
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
             dq[u2] = dphi * to_f32(qd[u2]);
             db[u2] = dphi * to_f32(ph[u2]);
           } else {
-            dq[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
+            dq[u2] = dphi * phi_ew_deriv<FMAP>(to_f32(ph[u2]));
           }
         }
         if (i < L) *reinterpret_cast<bf16x4*>(b.dQ + (tok0 + t0 + i) * R + f0) = pack4(dq[0], dq[1], dq[2], dq[3]);
@@ -428,7 +433,7 @@ struct BwdRLayout {
   static constexpr int bytes = logg_off + R * 4;
 };
 
-template <int R, int E, int GATE>
+template <int R, int E, int GATE, int FMAP = FM_ELU1>
 __global__ __launch_bounds__(256) void bwd_rstate(BwdArgs b) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = BwdRLayout<R, E, GATE>;
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(256) void bwd_rstate(BwdArgs b) {
   f32x4 Rz[ZTiles<R, NW>::ZT];
   z_load<R, NW>(Rz, nullptr, lane, w);
 
-  using Raw = RawChunk<R, E, R, FM_ELU1, GATE, false, NW>;
+  using Raw = RawChunk<R, E, R, FMAP, GATE, false, NW>;
   // reversed chunk u0: row t holds token t_end - 1 - (u0 + t) (clamped into the segment)
   auto load_rev = [&](Raw& rw, float& hv, int u0) {
     const int tt = t_end - 1 - (u0 + 16 * w + lane / 4);
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(256) void bwd_rstate(BwdArgs b) {
   load_rev(raw, hv, 0);
   for (int u0 = 0; u0 < seg; u0 += kChunk) {
     const int L = min(kChunk, seg - u0);
-    chunk_prelude<R, E, R, FM_ELU1, GATE, false, NW, true>(raw, ca, L, lg2gam, sm, 0, LY::k_off, 0, LY::v_off,
+    chunk_prelude<R, E, R, FMAP, GATE, false, NW, true>(raw, ca, L, lg2gam, sm, 0, LY::k_off, 0, LY::v_off,
                                                            LY::gam_off, LY::logg_off, lane, w);
     {
       const int t = 16 * w + lane / 4;
@@ -530,7 +535,7 @@ __device__ __forceinline__ float row_inclusive_scan(float x) {
   return x;
 }
 
-template <int R, int E, int GATE>
+template <int R, int E, int GATE, int FMAP = FM_ELU1>
 __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = BwdBLayout<R, E, GATE>;
@@ -606,7 +611,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   score_tiles(w, sqi, skj);
   float carry[FPW][4];  // GLA: d log alpha at the end of the chunk, for this lane's features
 
-  using Raw = RawChunk<R, E, R, FM_ELU1, PG, true, NW>;
+  using Raw = RawChunk<R, E, R, FMAP, PG, true, NW>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
   RowsE<E> rg;
@@ -622,7 +627,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
     // ---- prelude
-    chunk_prelude<R, E, R, FM_ELU1, PG, true, NW, true, GATE == GT_GLA ? kPreKD : 0>(
+    chunk_prelude<R, E, R, FMAP, PG, true, NW, true, GATE == GT_GLA ? kPreKD : 0>(
         raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0, LY::v_off, LY::gam_off, 0, lane, w, 0, LY::kd_off);
     if constexpr (GATE == GT_DECAY) {
       // gamma^t phi(q) for the reverse-state update
@@ -632,7 +637,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
       for (int j = 0; j < R / 32; ++j) {
         float f[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) f[u] = elu1(to_f32(raw.q[j][u])) * wt;
+        for (int u = 0; u < 8; ++u) f[u] = phi_ew<FMAP>(to_f32(raw.q[j][u])) * wt;
         lds<bf16x8>(sm, LY::qw_off + FT::at(t, lane % 4 + 4 * j)) =
             keep_if(t < L, cat8(pack4(f[0], f[1], f[2], f[3]), pack4(f[4], f[5], f[6], f[7])));
       }
@@ -788,7 +793,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
             dk[u2] = dphi * to_f32(kd[u2]);
             bk[u2] = dphi * to_f32(ph[u2]);
           } else {
-            dk[u2] = dphi * fminf(to_f32(ph[u2]), 1.f);
+            dk[u2] = dphi * phi_ew_deriv<FMAP>(to_f32(ph[u2]));
           }
         }
         if (j < L) *reinterpret_cast<bf16x4*>(b.dK + (tok0 + t0 + j) * R + f0) = pack4(dk[0], dk[1], dk[2], dk[3]);
@@ -844,7 +849,7 @@ struct BwdRGLayout {
   static constexpr int bytes = logg_off + R * 4;
 };
 
-template <int R, int E>
+template <int R, int E, int FMAP = FM_ELU1>
 __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = BwdRGLayout<R, E>;
@@ -873,7 +878,7 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   // the lane that accumulates feature w FR + lane in the prelude clears it
   if (lane < FR) lds<float>(sm, LY::logg_off + 4 * (w * FR + lane)) = 0.f;
 
-  using Raw = RawChunk<R, E, R, FM_ELU1, GT_GLA, false, NW>;
+  using Raw = RawChunk<R, E, R, FMAP, GT_GLA, false, NW>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
   float hv = 0.f;
@@ -886,7 +891,7 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, t_end - t0);
-    chunk_prelude<R, E, R, FM_ELU1, GT_GLA, false, NW, true, kPreKPos>(raw, ca, L, 0.f, sm, 0, LY::q_off, 0,
+    chunk_prelude<R, E, R, FMAP, GT_GLA, false, NW, true, kPreKPos>(raw, ca, L, 0.f, sm, 0, LY::q_off, 0,
                                                                        LY::v_off, LY::gam_off, LY::logg_off, lane, w);
     if (w == 0) lds<float>(sm, LY::hw_off + 4 * lane) = lane < L ? hv : 0.f;
     if (ci > 0) load(ci - 1);

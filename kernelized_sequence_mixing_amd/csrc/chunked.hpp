@@ -54,6 +54,13 @@ __device__ __forceinline__ float phi_ew(float x) {
   if constexpr (FMAP == FM_IDENT) return x;
   else return elu1(x);
 }
+// Its derivative from the feature value: min(phi, 1) for elu+1 (1 above zero,
+// exp(x) = phi below), 1 for the identity.
+template <int FMAP>
+__device__ __forceinline__ float phi_ew_deriv(float phi) {
+  if constexpr (FMAP == FM_IDENT) return 1.f;
+  else return fminf(phi, 1.f);
+}
 enum GateKind { GT_NONE = 0, GT_DECAY = 1, GT_GLA = 2, GT_SEL = 3 };
 // Gates that scale every feature of a step alike (RetNet's fixed gamma, the
 // selective scalar a_t): keys are weighted per token, one factor per step.
@@ -392,8 +399,8 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
           // the chunk total is uniform across the wave: a scalar read of lane 63
           const float bend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
           const float eb = __expf(b), emb = __expf((EXTRA & kPreKPos) != 0 ? b : -b);
-          if constexpr ((EXTRA & kPreQD) != 0) dq[u] = eb * fminf(pq, 1.f);
-          if constexpr ((EXTRA & kPreKD) != 0) dk[u] = emb * fminf(pk, 1.f);
+          if constexpr ((EXTRA & kPreQD) != 0) dq[u] = eb * phi_ew_deriv<FMAP>(pq);
+          if constexpr ((EXTRA & kPreKD) != 0) dk[u] = emb * phi_ew_deriv<FMAP>(pk);
           pq *= eb;
           pk *= emb;  // K^ = e^{b_end} K~: applied to the state row after the update
           my_bend = lane == 8 * j + u ? bend : my_bend;

@@ -246,7 +246,8 @@ def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAK
 
 BAD_BACKWARD = [
     ("n=0", dict(n=0), {}, N.LA_ERR_INVALID_ARG),
-    ("identity", dict(fkind=N.LA_FMAP_IDENTITY), {}, N.LA_ERR_UNSUPPORTED),
+    ("identity sel", dict(fkind=N.LA_FMAP_IDENTITY, gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), {},
+     N.LA_ERR_UNSUPPORTED),
     ("sel", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), {}, N.LA_ERR_UNSUPPORTED),
     ("noncausal", dict(causal=0), {}, N.LA_ERR_UNSUPPORTED),
     ("favor", dict(fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),

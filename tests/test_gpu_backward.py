@@ -41,10 +41,11 @@ def head_err(got, ref):
     return float(np.max(num / den))
 
 
-def term_scales(inp, dO, S0=None, z0=None, head=None):
+def term_scales(inp, dO, S0=None, z0=None, head=None, fmap="elu1"):
     """Per entry of dQ, dK, dV: the sum of the magnitudes of the terms it sums
     (with the feature map's derivative for dQ, dK), from the oracle's forward
-    quantities."""
+    quantities (features and weights taken in magnitude: the identity map's
+    may be negative)."""
     Q, K, V = (to_f64(inp[k]) for k in ("Q", "K", "V"))
     d = to_f64(dO)
     gate = oracle_gate(inp)
@@ -55,16 +56,20 @@ def term_scales(inp, dO, S0=None, z0=None, head=None):
         Q, K, V, d = (x[b:b + 1, h:h + 1] for x in (Q, K, V, d))
         if gate is not None:
             gate = ("decay", gate[1][h:h + 1])
-    pq, pk, D, c, W, num, den, o = obwd.forward_terms(Q, K, V, "elu1", None, True, gate, inp["eps"], S0, z0)
+    pq, pk, D, c, W, num, den, o = obwd.forward_terms(Q, K, V, fmap, None, True, gate, inp["eps"], S0, z0)
     g = d / den[..., None]
-    hh = -np.sum(d * o, axis=-1) / den
+    hh = -np.sum(d * o, axis=-1) / den if fmap != "identity" else np.zeros(den.shape)
+    pq, pk = np.abs(pq), np.abs(pk)
     T = (np.einsum("bhie,bhje->bhij", np.abs(g), np.abs(V)) + np.abs(hh)[..., None]) * D[None]
     sq = np.einsum("bhij,bhjf->bhif", T, pk)
     if S0 is not None:
         sq = sq + c[None, :, :, None] * (np.einsum("bhre,bhie->bhir", np.abs(S0), np.abs(g)) +
-                                         np.abs(hh)[..., None] * z0[:, :, None, :])
+                                         np.abs(hh)[..., None] * np.abs(z0)[:, :, None, :])
     sk = np.einsum("bhij,bhif->bhjf", T, pq)
-    sv = np.einsum("bhij,bhie->bhje", W, np.abs(g))
+    Wabs = np.einsum("bhir,bhjr->bhij", pq, pk) * D[None]
+    sv = np.einsum("bhij,bhie->bhje", Wabs, np.abs(g))
+    if fmap == "identity":
+        return sq, sk, sv
     dphi = lambda x: np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
     return sq * dphi(Q), sk * dphi(K), sv
 
@@ -82,15 +87,15 @@ def check_grads(got, ref, scales, what):
         assert e < TOL_GRAD, (what, nm, e)
 
 
-def run_backward(inp, dO, S0=None, z0=None):
+def run_backward(inp, dO, S0=None, z0=None, fmap="elu1"):
     import kernelized_sequence_mixing_amd as ksm
-    res = ksm.backward(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(dO), fmap="elu1", gate=gpu_gate(inp),
+    res = ksm.backward(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(dO), fmap=fmap, gate=gpu_gate(inp),
                        eps=inp["eps"], S0=dev(S0), z0=dev(z0))
     torch.cuda.synchronize()
     return tuple(x.cpu() for x in res)
 
 
-def oracle_backward(inp, dO, S0=None, z0=None, head=None):
+def oracle_backward(inp, dO, S0=None, z0=None, head=None, fmap="elu1"):
     Q, K, V = (to_f64(inp[k]) for k in ("Q", "K", "V"))
     d = to_f64(dO)
     gate = oracle_gate(inp)
@@ -99,7 +104,7 @@ def oracle_backward(inp, dO, S0=None, z0=None, head=None):
         Q, K, V, d = (x[b:b + 1, h:h + 1] for x in (Q, K, V, d))
         if gate is not None:
             gate = ("decay", gate[1][h:h + 1])
-    return obwd.backward(Q, K, V, d, "elu1", None, True, gate, inp["eps"],
+    return obwd.backward(Q, K, V, d, fmap, None, True, gate, inp["eps"],
                          None if S0 is None else to_f64(S0), None if z0 is None else to_f64(z0))
 
 

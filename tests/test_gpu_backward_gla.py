@@ -7,10 +7,11 @@ sum of the magnitudes of the terms each gradient entry sums, here with the
 per-feature decay factors inside the sums. d log alpha_u is the sum of the
 terms of the pairs (query i >= u, key j < u) whose weight alpha_u decays, plus
 the carried-in state's terms of the queries i >= u; dg_u is that times
-sigmoid(-g_u) / tau, and its scale is the magnitude sum of those terms. Where
-no pair crosses u (u = 0 without a carried state) the exact value is zero and
-the scale is the bound of what the kernel's suffix sum leaves over (see
-gla_scales). The oracle's explicit form holds an [n, n, r] decay tensor per
+sigmoid(-g_u) / tau, and its scale is the magnitude sum of those terms. The
+kernel's partial sums cancel pair terms that do not cross u, so the scale
+adds the bound of what that cancellation leaves over (see gla_scales); it
+decides where no pair crosses u (u = 0 without a carried state, exact value
+zero) or only small terms do. The oracle's explicit form holds an [n, n, r] decay tensor per
 head, so the oracle runs head by head on sampled heads.
 """
 import numpy as np
@@ -40,30 +41,37 @@ def _head(inp, dO, head, S0=None, z0=None):
     return (sl(inp["Q"]), sl(inp["K"]), sl(inp["V"]), sl(dO), sl(inp["g"]), sl(S0), sl(z0))
 
 
-def gla_scales(Q, K, V, dO, g, tau, eps, S0=None, z0=None):
-    """Magnitude sums of the terms behind dQ, dK, dV and dg (one head)."""
-    pq = feature_map(Q, "elu1")
-    pk = feature_map(K, "elu1")
+def gla_scales(Q, K, V, dO, g, tau, eps, S0=None, z0=None, fmap="elu1"):
+    """Magnitude sums of the terms behind dQ, dK, dV and dg (one head);
+    features in magnitude (the identity map's may be negative)."""
+    norm = fmap != "identity"
+    pq = np.abs(feature_map(Q, fmap))
+    pk = np.abs(feature_map(K, fmap))
     n = Q.shape[2]
     la = -np.logaddexp(0.0, -g) / tau
     Bc = np.cumsum(la, axis=2)
     mask = np.tril(np.ones((n, n), dtype=bool))
     D = np.where(mask[None, None, :, :, None],
                  np.exp(np.minimum(Bc[:, :, :, None, :] - Bc[:, :, None, :, :], 0.0)), 0.0)
-    W = np.einsum("bhik,bhjk,bhijk->bhij", pq, pk, D)
+    sq_ = np.sign(feature_map(Q, fmap))
+    sk_ = np.sign(feature_map(K, fmap))
+    W = np.einsum("bhik,bhjk,bhijk->bhij", pq * sq_, pk * sk_, D)      # the signed weights
     num = W @ V
     den = W.sum(axis=-1) + eps
     c = np.exp(Bc)
     if S0 is not None:
-        num = num + (pq * c) @ S0
-        den = den + np.einsum("bhik,bhk->bhi", pq * c, z0)
+        num = num + (pq * sq_ * c) @ S0
+        den = den + np.einsum("bhik,bhk->bhi", pq * sq_ * c, z0)
+    if not norm:
+        den = np.ones_like(den)
     o = num / den[..., None]
     gg = dO / den[..., None]
-    hh = -np.sum(dO * o, axis=-1) / den
+    hh = -np.sum(dO * o, axis=-1) / den if norm else np.zeros(den.shape)
+    W = np.einsum("bhik,bhjk,bhijk->bhij", pq, pk, D)                  # in magnitude from here on
     T = (np.abs(gg) @ np.abs(np.swapaxes(V, -1, -2)) + np.abs(hh)[..., None]) * mask
     sq = np.einsum("bhij,bhjk,bhijk->bhik", T, pk, D)
     if S0 is not None:
-        sq = sq + c * (np.abs(gg) @ np.abs(np.swapaxes(S0, -1, -2)) + np.abs(hh)[..., None] * z0[:, :, None, :])
+        sq = sq + c * (np.abs(gg) @ np.abs(np.swapaxes(S0, -1, -2)) + np.abs(hh)[..., None] * np.abs(z0)[:, :, None, :])
     sk = np.einsum("bhij,bhik,bhijk->bhjk", T, pq, D)
     sv = np.einsum("bhij,bhie->bhje", W, np.abs(gg))
     # d log alpha_u sums the terms of the pairs (i >= u, j < u) that alpha_u
@@ -74,42 +82,55 @@ def gla_scales(Q, K, V, dO, g, tau, eps, S0=None, z0=None):
     P = np.where((i >= i.T)[None, None, :, :, None], P, 0.0)
     cross = P.sum(axis=2)                                                        # [b, h, u, k]
     if S0 is not None:
-        st = c * pq * (np.abs(gg) @ np.abs(np.swapaxes(S0, -1, -2)) + np.abs(hh)[..., None] * z0[:, :, None, :])
+        st = c * pq * (np.abs(gg) @ np.abs(np.swapaxes(S0, -1, -2)) + np.abs(hh)[..., None] * np.abs(z0)[:, :, None, :])
         cross = cross + np.flip(np.cumsum(np.flip(st, axis=2), axis=2), axis=2)
-    # where no pair crosses (u = 0 without a carried state) d log alpha_u is
-    # exactly zero; the kernel sums dB_t over the whole suffix, whose pair
-    # terms cancel up to one bf16 rounding of the state each side reads them
-    # through: 2^-8 of the suffix's magnitude sum bounds what is left
-    suffix = np.flip(np.cumsum(np.flip(sq * pq + sk * pk, axis=2), axis=2), axis=2)
-    sdg = np.where(cross > 0, cross, suffix * 2.0 ** -8) / (1.0 + np.exp(g)) / tau
+    # the kernel sums dB_t from u to the end of u's 64-token chunk and takes
+    # the terms that cross the chunk's end directly; the pair terms with both
+    # ends inside that range cancel up to one bf16 rounding of the operands
+    # each side reads them through, so 2^-8 of the magnitude sum of what it
+    # adds (the in-chunk suffix of |dB_t| and the crossing terms at the
+    # chunk's end) bounds what the cancellation leaves. That floor matters
+    # where few or small terms cross u: at u = 0 without a carried state
+    # (exact value zero) and, for the identity map, next to features near 0.
+    mag = sq * pq + sk * pk
+    floor = np.zeros_like(mag)
+    for c0 in range(0, n, 64):
+        c1 = min(n, c0 + 64)
+        part = np.flip(np.cumsum(np.flip(mag[:, :, c0:c1], axis=2), axis=2), axis=2)
+        floor[:, :, c0:c1] = part + (cross[:, :, c1:c1 + 1] if c1 < n else 0.0)
+    sdg = (cross + floor * 2.0 ** -8) / (1.0 + np.exp(g)) / tau
+    if not norm:
+        return sq, sk, sv, sdg
     dphi = lambda x: np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
     return sq * dphi(Q), sk * dphi(K), sv, sdg
 
 
-def run_backward_gla(inp, dO, S0=None, z0=None):
+def run_backward_gla(inp, dO, S0=None, z0=None, fmap="elu1"):
     import kernelized_sequence_mixing_amd as ksm
-    res = ksm.backward(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(dO), fmap="elu1", gate=gpu_gate(inp),
+    res = ksm.backward(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), dev(dO), fmap=fmap, gate=gpu_gate(inp),
                        eps=inp["eps"], S0=dev(S0), z0=dev(z0))
     torch.cuda.synchronize()
     assert len(res) == 4
     return tuple(x.cpu() for x in res)
 
 
-def check_heads(got, inp, dO, heads, what, S0=None, z0=None):
+def check_heads(got, inp, dO, heads, what, S0=None, z0=None, fmap="elu1"):
     for head in heads:
         b, h = head
         Q, K, V, d, g, s0, z = _head(inp, dO, head, S0, z0)
         z = None if z is None else z
-        ref = obwd.backward_gla(Q, K, V, d, g, inp["tau"], "elu1", None, inp["eps"], s0, z)
-        scales = gla_scales(Q, K, V, d, g, inp["tau"], inp["eps"], s0, z)
+        ref = obwd.backward_gla(Q, K, V, d, g, inp["tau"], fmap, None, inp["eps"], s0, z)
+        scales = gla_scales(Q, K, V, d, g, inp["tau"], inp["eps"], s0, z, fmap)
         errs = []
         for x, r, sc in zip(got, ref, scales):
             xg = to_f64(x[b:b + 1, h:h + 1])
             assert np.isfinite(xg).all()
-            errs.append(float(np.max(np.abs(xg - r) / (sc + 1e-30))))
+            rel = np.abs(xg - r) / (sc + 1e-30)
+            errs.append(float(np.max(rel)))
+        worst_u = int(np.unravel_index(np.argmax(rel), rel.shape)[2])
         dgh = float(np.max(np.abs(to_f64(got[3][b:b + 1, h:h + 1]) - ref[3])) / (np.max(np.abs(ref[3])) + 1e-30))
         print(f"  {what} head {head}: term-relative dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e} "
-              f"dg {errs[3]:.2e}; dg of the head max {dgh:.2e}", flush=True)
+              f"dg {errs[3]:.2e} (at step {worst_u}); dg of the head max {dgh:.2e}", flush=True)
         for nm, e in zip(("dQ", "dK", "dV", "dg"), errs):
             assert e < TOL_GRAD, (what, head, nm, e)
 
