@@ -15,8 +15,8 @@ of ``la_oracle`` (W_ij = phi(q_i).phi(k_j) D_ij, o_i = sum_j W_ij v_j /
 chain rule written out step by step below; nothing is blocked or reordered.
 
 Gates covered: none, the RetNet decay (gamma is a fixed per-head constant, so
-it has no gradient) and the diagonal GLA gate, whose raw input g also gets a
-gradient (``backward_gla``).
+it has no gradient), the diagonal GLA gate, whose raw input g also gets a
+gradient (``backward_gla``), and the selective scalar gate (``backward_sel``).
 Pinned by ``tests/test_oracle_backward_pins.py`` against central finite differences of
 the pinned forward oracle and against closed forms.
 """
@@ -26,7 +26,7 @@ import numpy as np
 
 from .la_oracle import feature_map, normalised
 
-__all__ = ["feature_map_vjp", "forward_terms", "backward", "backward_gla"]
+__all__ = ["feature_map_vjp", "forward_terms", "backward", "backward_gla", "backward_sel"]
 
 
 def _f64(a):
@@ -204,3 +204,21 @@ def backward_gla(Q, K, V, dO, g, tau, fmap="elu1", omega=None, eps=1e-6, S0=None
     dQ = feature_map_vjp(Q, dpq, fmap, omega)
     dK = feature_map_vjp(K, dpk, fmap, omega)
     return dQ, dK, dV, dg
+
+
+def backward_sel(Q, K, V, dO, g, tau, fmap="elu1", omega=None, eps=1e-6, S0=None, z0=None):
+    """(dQ, dK, dV, dg) for the selective scalar gate: one input-dependent
+    decay a_t = sigmoid(g_t)^(1/tau) per step and head, g of shape [B, H, n].
+
+    The recurrence is S_t = a_t S_{t-1} + phi(k_t) v_t^T: the diagonal gate of
+    ``backward_gla`` with alpha_tk = a_t on every feature k (the selective
+    recurrence with A_t = a_t I, dileepadev page, "Gating and Selective State
+    Updates"). dQ, dK, dV are therefore those of the GLA form with g repeated
+    over the features, and since every alpha_tk is the same function of g_t,
+    dL/dg_t = sum_k dL/dg_tk (the chain rule for a shared input).
+    """
+    g = _f64(g)
+    r = feature_map(Q[..., :1, :], fmap, omega).shape[-1]
+    G = np.repeat(g[..., None], r, axis=-1)
+    dQ, dK, dV, dG = backward_gla(Q, K, V, dO, G, tau, fmap, omega, eps, S0, z0)
+    return dQ, dK, dV, dG.sum(axis=-1)

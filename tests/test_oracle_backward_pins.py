@@ -162,3 +162,63 @@ def test_identity_gradients_closed_form():
     np.testing.assert_allclose(dV[0, 0], A.T @ dO[0, 0], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(dQ[0, 0], M @ K[0, 0], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(dK[0, 0], M.T @ Q[0, 0], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("fmap,with_state", [("elu1", False), ("elu1", True), ("identity", True)])
+def test_sel_gradients_match_finite_differences(fmap, with_state):
+    """The selective scalar gate: dQ, dK, dV and the gradient of its raw
+    per-step input g [B, H, n], against central differences of the recurrent
+    oracle, which applies a_t = sigmoid(g_t)^(1/tau) step by step."""
+    B, H, n, d, e = 1, 2, 9, 4, 3
+    tau = 2.0
+    Q = RNG.standard_normal((B, H, n, d)) * 0.7
+    K = RNG.standard_normal((B, H, n, d)) * 0.7
+    V = RNG.standard_normal((B, H, n, e))
+    G = RNG.standard_normal((B, H, n))
+    dO = RNG.standard_normal((B, H, n, e))
+    S0 = z0 = None
+    if with_state:
+        S0 = np.abs(RNG.standard_normal((B, H, d, e)))
+        z0 = np.abs(RNG.standard_normal((B, H, d))) + 0.5
+    eps = 1e-3
+    dQ, dK, dV, dg = bwd.backward_sel(Q, K, V, dO, G, tau, fmap, None, eps, S0, z0)
+    assert dg.shape == G.shape
+
+    def loss(Q_, K_, V_, G_):
+        o, _, _ = orc.causal_recurrent(Q_, K_, V_, fmap, None, ("sel", G_, tau), eps, S0=S0, z0=z0)
+        return float(np.sum(o * dO))
+    step = 1e-6
+    for idx, (X, Gr) in enumerate(((Q, dQ), (K, dK), (V, dV), (G, dg))):
+        U = RNG.standard_normal(X.shape)
+        args = [Q, K, V, G]
+        args[idx] = X + step * U
+        lp = loss(*args)
+        args[idx] = X - step * U
+        lm = loss(*args)
+        fd = (lp - lm) / (2 * step)
+        an = float(np.sum(Gr * U))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (idx, fd, an)
+
+
+def test_sel_single_step_gate_gradient_closed_form():
+    """One step after a carried state: o = (a phi(q)^T S0 + phi(q)^T phi(k) v) /
+    (a phi(q).z0 + phi(q).phi(k) + eps) with a = sigmoid(g)^(1/tau), so
+    dL/dg = dL/da * a sigmoid(-g) / tau, with dL/da by the quotient rule."""
+    d, e, tau, eps = 3, 2, 4.0, 1e-3
+    q = RNG.standard_normal(d)
+    k = RNG.standard_normal(d)
+    v = RNG.standard_normal(e)
+    dO = RNG.standard_normal(e)
+    S0 = np.abs(RNG.standard_normal((d, e)))
+    z0 = np.abs(RNG.standard_normal(d)) + 0.5
+    gv = 0.3
+    pq, pk = orc.feature_map(q, "elu1"), orc.feature_map(k, "elu1")
+    a = (1.0 / (1.0 + np.exp(-gv))) ** (1.0 / tau)
+    num = a * (pq @ S0) + (pq @ pk) * v
+    den = a * (pq @ z0) + pq @ pk + eps
+    dL_da = float(dO @ ((pq @ S0) * den - num * (pq @ z0)) / den ** 2)
+    want = dL_da * a * (1.0 / (1.0 + np.exp(gv))) / tau
+    sh = lambda x: x.reshape((1, 1) + x.shape)
+    got = bwd.backward_sel(sh(q[None]), sh(k[None]), sh(v[None]), sh(dO[None]), np.array([[[gv]]]), tau, "elu1",
+                           None, eps, sh(S0), sh(z0))[3]
+    assert abs(float(got[0, 0, 0]) - want) <= 1e-12 * max(1.0, abs(want))
