@@ -256,18 +256,23 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  * also gets its gradient: with B_t = sum_{u<=t} log alpha_u,
  *   dB_t = dphi(q_t) * phi(q_t) - dphi(k_t) * phi(k_t)   (per feature),
  *   dg_u = (sum_{t>=u} dB_t) * sigmoid(-g_u) / tau.
+ * The selective scalar gate is that gate with alpha_t = a_t on every feature,
+ * so its dg_t is the sum over features of the per-feature dg_t (the library
+ * runs the GLA passes on g repeated over features and sums their dg).
  *   Q, K, dQ, dK [B][H][n][d_k]; V, dO, dV [B][H][n][d_v]; all BF16 (in_dtype and
  *   out_dtype must be BF16). S0, z0: the optional carried-in state of the forward
  *   (both or neither; fp32). gamma and tau are constants: no gradient is returned
  *   for them, nor for S0, z0.
- *   dg: [B][H][n][r] BF16, the gradient of gate->g; required (non-NULL) with the
- *   GLA gate and must be NULL otherwise (else LA_ERR_INVALID_ARG).
+ *   dg: the gradient of gate->g, BF16 in its shape ([B][H][n][r] for GLA,
+ *   [B][H][n] for SEL); required (non-NULL) with those gates and must be NULL
+ *   otherwise (else LA_ERR_INVALID_ARG).
  *   workspace: device scratch of at least la_backward_workspace_size bytes,
  *   256-byte aligned (segment states of both directions, g and h per token;
- *   GLA: also dQ~ . Q~ per token and feature and per-segment summed log-gates).
+ *   GLA and SEL: also dQ~ . Q~ per token and feature and per-segment summed
+ *   log-gates; SEL: also g repeated over features and its per-feature dg).
  * Supported (else LA_ERR_UNSUPPORTED): causal == 1, ELU1 or IDENTITY (the
- * state-space read-out: g_i = dO_i, h_i = 0, phi' = 1), gate NONE, DECAY or
- * GLA, (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
+ * state-space read-out: g_i = dO_i, h_i = 0, phi' = 1), gate NONE, DECAY, GLA
+ * or SEL, (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
  * inputs, each other or the workspace (LA_ERR_ALIAS). Numerics as la_forward:
  * bf16 MFMA operands (phi, values, g, the scores and dW), fp32 accumulation,
  * states, denominators and the sums behind dg.

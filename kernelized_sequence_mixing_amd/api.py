@@ -291,7 +291,7 @@ class PreparedForwardBatch:
 
 def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream):
     """Validate and marshal one la_backward call: (ctypes arguments, keep-alive objects, gradients), the
-    gradients being (dQ, dK, dV), plus dg with the GLA gate."""
+    gradients being (dQ, dK, dV), plus dg with a gate input (GLA, selective)."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (dO, "dO")):
         _dev(t, nm)
     if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3] or dO.shape != V.shape:
@@ -309,13 +309,13 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
             _dev(t, nm)
             if tuple(t.shape) != shp or t.dtype != torch.float32:
                 raise ValueError(f"{nm} must be float32 {shp}")
-    gla = g.kind == N.LA_GATE_GLA
+    gla = g.kind in (N.LA_GATE_GLA, N.LA_GATE_SEL)  # gates with an input, whose gradient dg is returned
     if grads is None:
         grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
         if gla:
             grads = grads + (torch.empty_like(gate[1]),)
     if len(grads) != (4 if gla else 3):
-        raise ValueError("grads must be (dQ, dK, dV)" + (" plus dg with the GLA gate" if gla else ""))
+        raise ValueError("grads must be (dQ, dK, dV)" + (" plus dg with a gate input" if gla else ""))
     dQ, dK, dV = grads[:3]
     dg = grads[3] if gla else None
     for t, ref, nm in ((dQ, Q, "dQ"), (dK, K, "dK"), (dV, V, "dV")) + (((dg, gate[1], "dg"),) if gla else ()):
@@ -337,10 +337,11 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
 def backward(Q, K, V, dO, *, fmap="elu1", gate=None, eps=1e-6, S0=None, z0=None, grads=None, workspace=None,
              stream=None):
     """(dQ, dK, dV) of the causal forward for an incoming gradient dO, through la_backward;
-    (dQ, dK, dV, dg) with the GLA gate, dg the gradient of its raw input g.
+    (dQ, dK, dV, dg) with the GLA or the selective gate, dg the gradient of its raw input g.
 
     Q, K [B, H, n, d_k]; V, dO [B, H, n, d_v] (bf16); gate None | ("decay", gamma[H]) |
-    ("gla", g[B, H, n, d_k] bf16, tau); S0, z0: the forward's carried-in state, if any."""
+    ("gla", g[B, H, n, d_k] bf16, tau) | ("sel", g[B, H, n] bf16, tau); S0, z0: the forward's
+    carried-in state, if any."""
     args, _keep, grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream)
     N.check(N.lib().la_backward(*args), "la_backward")
     return grads

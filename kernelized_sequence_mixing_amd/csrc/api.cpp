@@ -214,8 +214,7 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
   if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
   const int gk = gate_kind(g);
   if (!causal && gk != LA_GATE_NONE) return LA_ERR_INVALID_ARG;
-  if (!causal || (f->kind != LA_FMAP_ELU1 && f->kind != LA_FMAP_IDENTITY) || gk == LA_GATE_SEL)
-    return LA_ERR_UNSUPPORTED;
+  if (!causal || (f->kind != LA_FMAP_ELU1 && f->kind != LA_FMAP_IDENTITY)) return LA_ERR_UNSUPPORTED;
   if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   const int key = p->d_k * 1000 + p->d_v;
   if (key != 64064 && key != 64128 && key != 128064) return LA_ERR_UNSUPPORTED;
@@ -223,15 +222,19 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
 }
 
 struct BwdWsLayout {
-  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, bytes;
+  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, gx_off, dgx_off, bytes;
   int P, L;
 };
 
 // Forward segment states, reverse segment states, g (bf16) and h per token;
-// GLA adds dQ~ . Q~ per token and feature and the segments' summed log-gates.
+// GLA adds dQ~ . Q~ per token and feature and the segments' summed log-gates;
+// the selective scalar gate runs the GLA passes and adds its input repeated
+// over features and the per-feature gradient of that (bf16 [B][H][n][r] each).
 BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, int gate) {
   BwdWsLayout w{};
-  plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate, &w.P, &w.L);
+  // the selective gate runs the GLA passes, on their segment plan
+  plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate == LA_GATE_SEL ? LA_GATE_GLA : gate, &w.P,
+                &w.L);
   const size_t BH = (size_t)p->B * p->H, r = (size_t)f->r, dv = (size_t)p->d_v, n = (size_t)p->n;
   const size_t states = BH * w.P * r * dv * 4, zs = BH * w.P * r * 4;
   w.S_off = 0;
@@ -241,13 +244,17 @@ BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, i
   w.G_off = round_up(w.rh_off + zs, kAlign);
   w.h_off = round_up(w.G_off + BH * n * dv * 2, kAlign);
   w.dB_off = round_up(w.h_off + BH * n * 4, kAlign);
-  if (gate != LA_GATE_GLA) {
-    w.logG_off = w.bytes = w.dB_off;
+  if (gate != LA_GATE_GLA && gate != LA_GATE_SEL) {
+    w.logG_off = w.gx_off = w.dgx_off = w.bytes = w.dB_off;
     return w;
   }
   const size_t n64 = (n + 63) / 64 * 64;  // dQ~ . Q~ is stored by whole chunks
   w.logG_off = round_up(w.dB_off + BH * n64 * r * 4, kAlign);
-  w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
+  w.gx_off = w.dgx_off = w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
+  if (gate == LA_GATE_SEL) {
+    w.dgx_off = round_up(w.gx_off + BH * n * r * 2, kAlign);
+    w.bytes = round_up(w.dgx_off + BH * n * r * 2, kAlign);
+  }
   return w;
 }
 
@@ -613,16 +620,17 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   if (Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || dQ == nullptr || dK == nullptr ||
       dV == nullptr)
     return LA_ERR_INVALID_ARG;
-  if ((dg != nullptr) != (gk == LA_GATE_GLA)) return LA_ERR_INVALID_ARG;
+  const bool sel = gk == LA_GATE_SEL;
+  if ((dg != nullptr) != (gk == LA_GATE_GLA || sel)) return LA_ERR_INVALID_ARG;
   if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_INVALID_ARG;
   for (const void* ptr : {Q, K, V, dO, (const void*)S0, (const void*)z0, (const void*)dQ, (const void*)dK,
                           (const void*)dV, (const void*)dg})
     if (ptr != nullptr && !aligned16(ptr)) return LA_ERR_INVALID_ARG;
   const size_t BH = (size_t)p->B * p->H, n = (size_t)p->n, r = (size_t)fmap->r;
-  const size_t qk = BH * n * p->d_k * 2, vv = BH * n * p->d_v * 2, gg = BH * n * r * 2;
+  const size_t qk = BH * n * p->d_k * 2, vv = BH * n * p->d_v * 2, gg = BH * n * (sel ? 1 : r) * 2;
   const Range rq = range_of(Q, qk), rk = range_of(K, qk), rv = range_of(V, vv), rdo = range_of(dO, vv);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
-  const Range rgl = range_of(gk == LA_GATE_GLA ? gate->g : nullptr, gg);
+  const Range rgl = range_of(gate_has_input(gk) ? gate->g : nullptr, gg);
   const Range rs0 = range_of(S0, BH * r * p->d_v * 4), rz0 = range_of(z0, BH * r * 4);
   const Range rdq = range_of(dQ, qk), rdk = range_of(dK, qk), rdv = range_of(dV, vv), rdg = range_of(dg, gg);
   const BwdWsLayout wl = bwd_workspace_layout(p, fmap, gk);
@@ -647,7 +655,7 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.out_dtype = p->out_dtype;
   plan.eps = p->eps;
   plan.fmap = fmap->kind;
-  plan.gate = gk;
+  plan.gate = sel ? LA_GATE_GLA : gk;  // the selective gate: the GLA passes on its repeated input
   plan.causal = 1;
   plan.Q = Q;
   plan.K = K;
@@ -668,16 +676,22 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.ws_rh = reinterpret_cast<float*>(ws + wl.rh_off);
   plan.ws_G = ws + wl.G_off;
   plan.ws_h = reinterpret_cast<float*>(ws + wl.h_off);
-  if (gk == LA_GATE_GLA) {
+  if (gk == LA_GATE_GLA || sel) {
     plan.ws_dB = reinterpret_cast<float*>(ws + wl.dB_off);
     plan.ws_logG = reinterpret_cast<float*>(ws + wl.logG_off);
-    plan.dg = dg;
+    plan.dg = sel ? static_cast<void*>(ws + wl.dgx_off) : dg;
   }
   plan.dO = dO;
   plan.dQ = dQ;
   plan.dK = dK;
   plan.dV = dV;
-  return launch_backward(plan);
+  if (sel) {
+    plan.g = ws + wl.gx_off;
+    if ((st = launch_gate_repeat(gate->g, ws + wl.gx_off, (long long)(BH * n), fmap->r, plan.stream)) != LA_OK)
+      return st;
+  }
+  if ((st = launch_backward(plan)) != LA_OK) return st;
+  return sel ? launch_gate_feature_sum(ws + wl.dgx_off, dg, (long long)(BH * n), fmap->r, plan.stream) : LA_OK;
 }
 
 la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t d_k, int32_t in_dtype,

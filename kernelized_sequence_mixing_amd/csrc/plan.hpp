@@ -114,5 +114,9 @@ la_status launch_backward(const BwdPlan& p);
 la_status launch_noncausal(const FwdPlan& p);
 la_status launch_decode(const DecodePlan& p);
 la_status launch_feature_map(const FmapPlan& p);
+// The selective scalar gate's backward: repeat g [rows] over r features, and
+// sum the per-feature gradient [rows][r] back to [rows].
+la_status launch_gate_repeat(const void* g, void* gx, long long rows, int r, hipStream_t stream);
+la_status launch_gate_feature_sum(const void* dgx, void* dg, long long rows, int r, hipStream_t stream);
 
 }  // namespace la

@@ -246,9 +246,14 @@ def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAK
 
 BAD_BACKWARD = [
     ("n=0", dict(n=0), {}, N.LA_ERR_INVALID_ARG),
-    ("identity sel", dict(fkind=N.LA_FMAP_IDENTITY, gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), {},
-     N.LA_ERR_UNSUPPORTED),
-    ("sel", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), {}, N.LA_ERR_UNSUPPORTED),
+    ("identity sel without dg", dict(fkind=N.LA_FMAP_IDENTITY, gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), {},
+     N.LA_ERR_INVALID_ARG),
+    ("sel without dg", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),
+    ("sel favor", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP, fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP),
+     dict(dg=FAKE + 14 * SP), N.LA_ERR_UNSUPPORTED),
+    ("sel dg aliases g", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), dict(dg=FAKE + 6 * SP + 1024), N.LA_ERR_ALIAS),
+    ("sel dg in workspace", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), dict(dg=FAKE + 4 * SP + 4096),
+     N.LA_ERR_ALIAS),
     ("noncausal", dict(causal=0), {}, N.LA_ERR_UNSUPPORTED),
     ("favor", dict(fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
     ("gla without dg", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),
@@ -310,6 +315,9 @@ def test_backward_workspace_size():
     assert size(4, 16, n, 64, 64, N.LA_GATE_DECAY) == size(4, 16, n, 64, 64)
     # GLA adds dQ~ . Q~ per token and feature (fp32) and the segments' summed log-gates
     assert size(4, 16, n, 64, 64, N.LA_GATE_GLA) == size(4, 16, n, 64, 64) + BH * n * 64 * 4 + zs
+    # the selective gate runs the GLA passes on g repeated over features: that copy and its
+    # per-feature gradient (bf16 each) come on top
+    assert size(4, 16, n, 64, 64, N.LA_GATE_SEL) == size(4, 16, n, 64, 64, N.LA_GATE_GLA) + 2 * BH * n * 64 * 2
 
 
 # ------------------------------------------------------------------ serving batch (validation, no launch)
