@@ -253,7 +253,7 @@ def backward_algorithmic_per_token(wl):
     """(bytes, matrix-core flops) per head-token of the causal backward pass.
 
     Bytes: read q, k, v, dO once, write dq, dk, dv once (GLA: also read g and
-    write dg). Flops (chunk C, masked upper triangle excluded): the scores, the
+    write dg, r per token each; the selective gate: one of each per token). Flops (chunk C, masked upper triangle excluded): the scores, the
     numerator of o, dW, and the intra-chunk parts of dq, dk, dv ((C+1)/2 * 2 r
     or 2 d_v each), plus six r x d_v products per token (o's inter-chunk read,
     dq's S g, dk's R v, dv's R phi(k), and the forward and reverse state
@@ -262,14 +262,16 @@ def backward_algorithmic_per_token(wl):
     nbytes = 2 * (2 * wl.d_k + 2 * wl.d_v) + 2 * (2 * wl.d_k + wl.d_v)
     if wl.gate == "gla":
         nbytes += 2 * (2 * wl.r)
+    elif wl.gate == "sel":
+        nbytes += 2 * 2
     half = (CHUNK + 1) / 2
     flops = half * 2 * wl.r * 3 + half * 2 * wl.d_v * 3 + 6 * 2 * wl.r * wl.d_v
     return nbytes, flops
 
 
 def bench_backward(wl, steps, warmup):
-    """la_backward on workload wl (causal elu+1): one step is one full backward pass
-    (with the GLA gate it includes dg)."""
+    """la_backward on workload wl (causal, elu+1 or identity features): one step is one
+    full backward pass (with a gate input it includes dg)."""
     import kernelized_sequence_mixing_amd as ksm
     from workloads import incoming_gradient
     inp = make_inputs(wl, seed=0)
@@ -278,12 +280,12 @@ def bench_backward(wl, steps, warmup):
     per_set = wl.head_tokens * nb_tok
     sets = _device_sets(inp, ["Q", "K", "V", "dO", "gamma", "g"], per_set)
     gate_of = {"none": lambda s: None, "decay": lambda s: ("decay", s["gamma"]),
-               "gla": lambda s: ("gla", s["g"], wl.tau)}[wl.gate]
+               "gla": lambda s: ("gla", s["g"], wl.tau), "sel": lambda s: ("sel", s["g"], wl.tau)}[wl.gate]
     grads = [(torch.empty_like(s["Q"]), torch.empty_like(s["K"]), torch.empty_like(s["V"])) +
-             ((torch.empty_like(s["g"]),) if wl.gate == "gla" else ()) for s in sets]
+             ((torch.empty_like(s["g"]),) if wl.gate in ("gla", "sel") else ()) for s in sets]
     stream = torch.cuda.current_stream()
-    calls = [ksm.PreparedBackward(s["Q"], s["K"], s["V"], s["dO"], gate=gate_of(s), eps=wl.eps, grads=grads[i],
-                                  stream=stream) for i, s in enumerate(sets)]
+    calls = [ksm.PreparedBackward(s["Q"], s["K"], s["V"], s["dO"], fmap=wl.fmap, gate=gate_of(s), eps=wl.eps,
+                                  grads=grads[i], stream=stream) for i, s in enumerate(sets)]
 
     def step(i):
         calls[i]()
@@ -296,7 +298,8 @@ def bench_backward(wl, steps, warmup):
             "hbm_alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "mfma_alg_TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4),
             "alg_bytes_per_token": nb_tok, "alg_flops_per_token": fl_tok,
-            "shape": {"B": wl.B, "H": wl.H, "n": wl.n, "d_k": wl.d_k, "d_v": wl.d_v, "gate": wl.gate}}
+            "shape": {"B": wl.B, "H": wl.H, "n": wl.n, "d_k": wl.d_k, "d_v": wl.d_v, "gate": wl.gate,
+                      "fmap": wl.fmap}}
 
 
 def cpu_baseline(wl, min_seconds=10.0):
@@ -396,6 +399,8 @@ def main():
         extra.append(bench_backward(WORKLOADS["gla_gate"].resized(name="gla_gate_d64", d_k=64, d_v=64, r=64,
                                                                   qk_scale=64 ** -0.5, v_scale=64 ** -0.5),
                                     args.steps, args.warmup))
+        for name in ("ssm_selective", "ssm_scalar"):  # the state-space form under both selective gates
+            extra.append(bench_backward(WORKLOADS[name], args.steps, args.warmup))
         line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
