@@ -70,6 +70,7 @@ static int elu_lds(int dv, int gate) {
     case GT_NONE: return elu_lds_gate<R, GT_NONE>(dv);
     case GT_DECAY: return elu_lds_gate<R, GT_DECAY>(dv);
     case GT_GLA: return elu_lds_gate<R, GT_GLA>(dv);
+    case GT_SEL: return elu_lds_gate<R, GT_SEL>(dv);
   }
   return 0;
 }
