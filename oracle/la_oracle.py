@@ -26,7 +26,7 @@ from __future__ import annotations
 import numpy as np
 
 FMAPS = ("elu1", "favor", "identity")
-GATES = ("none", "decay", "gla", "sel")
+GATES = ("none", "decay", "gla", "sel", "outer")
 
 
 def _f64(a):
@@ -152,7 +152,32 @@ def _gate_factor(gate, t, B, H):
     if kind == "sel":
         g, tau = gate[1], gate[2]
         return sel_alpha(np.asarray(g)[:, :, t], tau)[:, :, None]
+    if kind == "outer":
+        g, tau = gate[1], gate[3]
+        return gla_alpha(np.asarray(g)[:, :, t, :], tau)
     raise ValueError(f"unknown gate {kind!r}")
+
+
+def outer_beta(gv, tau):
+    """Value-side factor of the outer-product gate, beta_t = sigmoid(gv_t) ** (1 / tau).
+
+    [LAM-d] "Gating and Selective State Updates" gives the gate as a matrix
+    G_t in (0, 1)^{d x d} applied elementwise to the state. Reading: the
+    outer-product gate G_t = alpha_t beta_t^T, a key-side factor alpha_t (the
+    diagonal GLA gate) times a value-side factor beta_t per value column, both
+    from raw inputs through the GLA gate's sigmoid and 1/tau. Beta = 1 is the
+    GLA gate. The normaliser z, S's column for a constant value of 1, takes
+    the key side only (that constant is not a value column with a gate).
+    """
+    return gla_alpha(gv, tau)
+
+
+def _gate_factor_v(gate, t):
+    """Value-side multiplier of the previous state before step t ([B, H, d_v]),
+    or None (every gate but the outer-product one)."""
+    if gate is None or gate[0] != "outer":
+        return None
+    return outer_beta(np.asarray(gate[2])[:, :, t, :], gate[3])
 
 
 # ---------------------------------------------------------------------------
@@ -238,8 +263,35 @@ def attention_from_weights(W, V, eps=1e-6, normalise=True):
 def brute(Q, K, V, fmap="elu1", omega=None, causal=False, gate=None, eps=1e-6):
     """Quadratic reference: explicit weight matrix, then the mix (normalised
     unless ``fmap`` is the state-space "identity")."""
+    if gate is not None and gate[0] == "outer":
+        return brute_outer(Q, K, V, fmap, omega, gate, eps)
     W = kernel_weights(Q, K, fmap, omega, causal, gate)
     return attention_from_weights(W, V, eps, normalised(fmap))
+
+
+def brute_outer(Q, K, V, fmap, omega, gate, eps=1e-6):
+    """Explicit form of the causal outer-product gate ("outer", g, gv, tau).
+
+    Unrolling S_t = (alpha_t beta_t^T) * S_{t-1} + phi(k_t) v_t^T, key j reaches
+    query i >= j with the factor prod_{u=j+1..i} alpha_uk beta_ue on state
+    entry (k, e): o_ie = sum_j W_ij D_ije v_je / (sum_j W_ij + eps), where W are
+    the GLA weights of the key side (``kernel_weights`` with ("gla", g, tau))
+    and D_ije = prod_{u=j+1..i} beta_ue; the denominator has no value-side
+    factor (z takes the key side only, see ``outer_beta``).
+    """
+    V = _f64(V)
+    W = kernel_weights(Q, K, fmap, omega, True, ("gla", gate[1], gate[3]))
+    beta = outer_beta(gate[2], gate[3])  # [B, H, n, d_v]
+    B, H, n, dv = V.shape
+    num = np.zeros((B, H, n, dv))
+    for i in range(n):
+        for j in range(i + 1):
+            D = np.prod(beta[:, :, j + 1:i + 1, :], axis=2)  # empty product = 1
+            num[:, :, i, :] += W[:, :, i, j, None] * D * V[:, :, j, :]
+    if not normalised(fmap):
+        return num
+    den = W.sum(axis=-1) + eps
+    return num / den[..., None]
 
 
 # ---------------------------------------------------------------------------
@@ -261,8 +313,10 @@ def causal_recurrent(Q, K, V, fmap="elu1", omega=None, gate=None, eps=1e-6,
     value of constant 1), which keeps the weights of each output summing to
     one; eps is added to the denominator as in [LAM-s]'s routine; the page
     calls z's update "scalar" but z has r entries (it is summed elementwise).
-    ``gate`` is None, ("decay", gamma[H]), ("gla", g[B,H,n,r], tau) or
-    ("sel", g[B,H,n], tau). With the "identity" feature map the read-out is o_t = q_t^T S_t, the
+    ``gate`` is None, ("decay", gamma[H]), ("gla", g[B,H,n,r], tau),
+    ("sel", g[B,H,n], tau) or ("outer", g[B,H,n,r], gv[B,H,n,d_v], tau) (the
+    state entry (k, e) scaled by alpha_{t,k} beta_{t,e}, z by alpha_t; see
+    ``outer_beta``). With the "identity" feature map the read-out is o_t = q_t^T S_t, the
     state-space y_t = C_t^T h_t (z is still carried, unused).
     """
     V = _f64(V)
@@ -279,6 +333,9 @@ def causal_recurrent(Q, K, V, fmap="elu1", omega=None, gate=None, eps=1e-6,
         if G is not None:
             S = S * G[..., None]
             z = z * G
+        Gv = _gate_factor_v(gate, t)
+        if Gv is not None:
+            S = S * Gv[:, :, None, :]
         S = S + pk[:, :, t, :, None] * V[:, :, t, None, :]
         z = z + pk[:, :, t, :]
         num = np.einsum("bhr,bhre->bhe", pq[:, :, t, :], S)
@@ -296,8 +353,8 @@ def decode_step(S, z, q, k, v, fmap="elu1", omega=None, gate=None, eps=1e-6):
     [LAM-d] "Recurrent Reformulation" (rank-1 update of S, update of z, then
     the read-out); [AFA] "The recurrent form (causal)" (constant cost per
     token). q, k, v (and g for GLA) are [B, H, d] for the single new token;
-    ``gate`` is None, ("decay", gamma[H]), ("gla", g[B,H,r], tau) or
-    ("sel", g[B,H], tau).
+    ``gate`` is None, ("decay", gamma[H]), ("gla", g[B,H,r], tau),
+    ("sel", g[B,H], tau) or ("outer", g[B,H,r], gv[B,H,d_v], tau).
     """
     q4 = _f64(q)[:, :, None, :]
     k4 = _f64(k)[:, :, None, :]
@@ -307,6 +364,8 @@ def decode_step(S, z, q, k, v, fmap="elu1", omega=None, gate=None, eps=1e-6):
         g4 = ("gla", _f64(gate[1])[:, :, None, :], gate[2])
     if gate is not None and gate[0] == "sel":
         g4 = ("sel", _f64(gate[1])[:, :, None], gate[2])
+    if gate is not None and gate[0] == "outer":
+        g4 = ("outer", _f64(gate[1])[:, :, None, :], _f64(gate[2])[:, :, None, :], gate[3])
     o, S1, z1 = causal_recurrent(q4, k4, v4, fmap, omega, g4, eps, S0=S, z0=z)
     return o[:, :, 0, :], S1, z1
 

@@ -454,3 +454,82 @@ def test_selective_gate_is_gla_shared_by_features():
     a = orc.causal_recurrent(Q, K, V, "elu1", None, ("sel", g, 3.0))[0]
     b = orc.causal_recurrent(Q, K, V, "elu1", None, ("gla", np.repeat(g[..., None], d, axis=-1), 3.0))[0]
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------- outer-product gate
+
+def _outer_inputs(rng, B=2, H=2, n=13, d=4, dv=3):
+    Q, K = rng.standard_normal((B, H, n, d)), rng.standard_normal((B, H, n, d))
+    V = rng.standard_normal((B, H, n, dv))
+    g, gv = rng.standard_normal((B, H, n, d)) * 2.0, rng.standard_normal((B, H, n, dv)) * 2.0
+    return Q, K, V, g, gv
+
+
+def test_outer_gate_with_unit_value_side_is_gla():
+    """beta = 1 (gv -> +inf) leaves the diagonal GLA gate: outputs and states."""
+    rng = np.random.default_rng(41)
+    Q, K, V, g, gv = _outer_inputs(rng)
+    gv = np.full_like(gv, np.inf)
+    for fmap in ("elu1", "identity"):
+        a = orc.causal_recurrent(Q, K, V, fmap, None, ("outer", g, gv, 3.0))
+        b = orc.causal_recurrent(Q, K, V, fmap, None, ("gla", g, 3.0))
+        for x, y in zip(a, b):
+            np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(orc.brute(Q, K, V, fmap, None, True, ("outer", g, gv, 3.0)), b[0],
+                                   rtol=1e-10, atol=1e-12)
+
+
+def test_outer_gate_explicit_equals_recurrent():
+    """The explicit per-entry products of alpha and beta equal the step-by-step
+    recurrence, for both elementwise feature maps."""
+    rng = np.random.default_rng(42)
+    Q, K, V, g, gv = _outer_inputs(rng)
+    for fmap in ("elu1", "identity"):
+        gate = ("outer", g, gv, 2.0)
+        a = orc.causal_recurrent(Q, K, V, fmap, None, gate)[0]
+        b = orc.brute(Q, K, V, fmap, None, True, gate)
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_outer_gate_value_side_is_an_iir_filter_per_column():
+    """One key feature with alpha = 1 and a value-side gate constant in time:
+    column e of the state is h_t = beta_e h_{t-1} + k_t v_te, a first-order IIR
+    filter (scipy.signal.lfilter), and y_t = q_t h_t."""
+    rng = np.random.default_rng(43)
+    n, dv, tau = 40, 3, 2.0
+    q, k, V = rng.standard_normal(n), rng.standard_normal(n), rng.standard_normal((n, dv))
+    gvc = np.array([-2.0, 0.3, 4.0])
+    beta = scipy.special.expit(gvc) ** (1.0 / tau)
+    sh = lambda x: x.reshape((1, 1) + x.shape)
+    gate = ("outer", sh(np.full((n, 1), np.inf)), sh(np.broadcast_to(gvc, (n, dv)).copy()), tau)
+    got = orc.causal_recurrent(sh(q[:, None]), sh(k[:, None]), sh(V), "identity", None, gate)[0][0, 0]
+    for e in range(dv):
+        h = scipy.signal.lfilter([1.0], [1.0, -beta[e]], k * V[:, e])
+        np.testing.assert_allclose(got[:, e], q * h, rtol=1e-12, atol=1e-12)
+
+
+def test_outer_gate_normaliser_takes_the_key_side_only():
+    """z evolves as under the GLA gate whatever beta is, and with identical
+    value columns of one gate the output columns stay identical."""
+    rng = np.random.default_rng(44)
+    Q, K, V, g, gv = _outer_inputs(rng)
+    a = orc.causal_recurrent(Q, K, V, "elu1", None, ("outer", g, gv, 3.0))
+    b = orc.causal_recurrent(Q, K, V, "elu1", None, ("gla", g, 3.0))
+    np.testing.assert_allclose(a[2], b[2], rtol=1e-12)
+    Vs = np.repeat(V[..., :1], 3, axis=-1)
+    gvs = np.repeat(gv[..., :1], 3, axis=-1)
+    o = orc.causal_recurrent(Q, K, Vs, "elu1", None, ("outer", g, gvs, 3.0))[0]
+    np.testing.assert_allclose(o[..., 1], o[..., 0], rtol=1e-13)
+    np.testing.assert_allclose(o[..., 2], o[..., 0], rtol=1e-13)
+
+
+def test_outer_gate_decode_steps_equal_recurrence():
+    rng = np.random.default_rng(45)
+    Q, K, V, g, gv = _outer_inputs(rng, n=6)
+    o, S, z = orc.causal_recurrent(Q, K, V, "elu1", None, ("outer", g, gv, 3.0))
+    S1, z1 = np.zeros_like(S), np.zeros_like(z)
+    for t in range(Q.shape[2]):
+        ot, S1, z1 = orc.decode_step(S1, z1, Q[:, :, t], K[:, :, t], V[:, :, t], "elu1", None,
+                                     ("outer", g[:, :, t], gv[:, :, t], 3.0))
+        np.testing.assert_allclose(ot, o[:, :, t], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S1, S, rtol=1e-12)
