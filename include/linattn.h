@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 5
+#define LA_ABI_VERSION 6
 
 typedef enum la_status {
   LA_OK = 0,
@@ -78,7 +78,10 @@ typedef enum la_fmap_kind { LA_FMAP_ELU1 = 0, LA_FMAP_FAVOR = 1, LA_FMAP_IDENTIT
  *   NONE  : S_t = S_{t-1} + phi(k_t) v_t^T.
  *   DECAY : S_t = gamma_h S_{t-1} + phi(k_t) v_t^T (RetNet fixed decay).
  *   GLA   : S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T with
- *           alpha_t = sigmoid(g_t)^(1/tau) per feature row (diagonal GLA gate). */
+ *           alpha_t = sigmoid(g_t)^(1/tau) per feature row (diagonal GLA gate).
+ *   OUTER : S_t = (alpha_t beta_t^T) * S_{t-1} + phi(k_t) v_t^T (elementwise),
+ *           alpha_t as GLA, beta_t = sigmoid(gv_t)^(1/tau) per value column;
+ *           z_t = alpha_t * z_{t-1} + phi(k_t). */
 /*
  * Gates of the causal forms (the multiplier of the previous state at each
  * step). DECAY: RetNet's fixed gamma_h. GLA: a per-feature, input-dependent
@@ -88,9 +91,19 @@ typedef enum la_fmap_kind { LA_FMAP_ELU1 = 0, LA_FMAP_FAVOR = 1, LA_FMAP_IDENTIT
  * features, g [B][H][n] (decode: [B][H]); the RetNet decay made
  * input-dependent, the selective recurrence of Mamba's kind ("State Space
  * Models as Linear Attention", dileepadev page; "Evolution: add
- * decay/gating", vguerra page). GLA and SEL: elementwise feature maps only.
+ * decay/gating", vguerra page). OUTER: the gate matrix G_t in (0, 1)^{d x d}
+ * of "Gating and Selective State Updates" as the outer product of a key-side
+ * alpha_t (the GLA gate, input g) and a value-side beta_t (input gv
+ * [B][H][n][d_v], decode [B][H][d_v]); the normaliser z takes the key side
+ * only. GLA, SEL and OUTER: elementwise feature maps only.
  */
-typedef enum la_gate_kind { LA_GATE_NONE = 0, LA_GATE_DECAY = 1, LA_GATE_GLA = 2, LA_GATE_SEL = 3 } la_gate_kind;
+typedef enum la_gate_kind {
+  LA_GATE_NONE = 0,
+  LA_GATE_DECAY = 1,
+  LA_GATE_GLA = 2,
+  LA_GATE_SEL = 3,
+  LA_GATE_OUTER = 4
+} la_gate_kind;
 
 typedef struct la_problem {
   int32_t B, H;      /* batch, heads: >= 1 */
@@ -109,11 +122,13 @@ typedef struct la_feature_map {
 
 typedef struct la_gate {
   int32_t kind;       /* la_gate_kind */
-  float tau;          /* GLA temperature, > 0 (ignored otherwise) */
+  float tau;          /* GLA, SEL, OUTER temperature, > 0 (ignored otherwise) */
   const float* gamma; /* DECAY: device [H] fp32, each in (0, 1] -- a documented
                          precondition, not checked (the values live on the device) */
-  const void* g;      /* GLA: device [B][H][n][r] in in_dtype (decode: [B][H][r]);
+  const void* g;      /* GLA, OUTER: device [B][H][n][r] in in_dtype (decode: [B][H][r]);
                          SEL: [B][H][n] (decode: [B][H]) */
+  const void* gv;     /* OUTER: device [B][H][n][d_v] in in_dtype (decode: [B][H][d_v]);
+                         must be NULL for every other gate (else LA_ERR_INVALID_ARG) */
 } la_gate;
 
 /* Flags of la_batch.flags. */
@@ -179,8 +194,9 @@ la_status la_forward_segments(const la_problem* p, const la_feature_map* fmap,
  *   workspace     device scratch of at least la_forward_workspace_size bytes
  *                 (may be NULL when that size is 0), 256-byte aligned.
  * Supported (else LA_ERR_UNSUPPORTED):
- *   causal: in_dtype BF16, out_dtype BF16; ELU1 or IDENTITY with d_k in {32,64,128};
- *           FAVOR with d_k in {32,64,128}, r in {64,128,256}, gate NONE or DECAY;
+ *   causal: in_dtype BF16, out_dtype BF16; ELU1 or IDENTITY with d_k in {32,64,128}
+ *           and any gate; FAVOR with d_k in {32,64,128}, r in {64,128,256}, gate
+ *           NONE or DECAY;
  *           d_v in {32,64,128}; r * d_v <= 16384.
  *   non-causal: in/out dtype F32 or BF16 (any mix); same d_k, d_v, r sets.
  * Numerics: bf16 MFMA products with fp32 accumulation; the state, normaliser,
@@ -207,7 +223,7 @@ la_status la_forward_batch_workspace_size(const la_problem* p, const la_batch* b
  * la_forward(causal = 1) on that sequence alone with S0 = its slot's state
  * (LA_SLOT_READ) and S_final = its slot (LA_SLOT_WRITE); the slots are updated
  * in place, after every read of them.
- *   Q, K, out, gate->g as la_forward on the [B][H][n][.] tensors (B = 1 with
+ *   Q, K, out, gate->g, gate->gv as la_forward on the [B][H][n][.] tensors (B = 1 with
  *   cu_seqlens); fmap, gate as la_forward; out: tokens no sequence covers are
  *   left untouched.
  * Device-side contents are not validated on the host; the kernels clamp them
@@ -272,7 +288,7 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  *   log-gates; SEL: also g repeated over features and its per-feature dg).
  * Supported (else LA_ERR_UNSUPPORTED): causal == 1, ELU1 or IDENTITY (the
  * state-space read-out: g_i = dO_i, h_i = 0, phi' = 1), gate NONE, DECAY, GLA
- * or SEL, (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
+ * or SEL (not OUTER), (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
  * inputs, each other or the workspace (LA_ERR_ALIAS). Numerics as la_forward:
  * bf16 MFMA operands (phi, values, g, the scores and dW), fp32 accumulation,
  * states, denominators and the sums behind dg.

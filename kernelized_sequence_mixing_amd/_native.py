@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_ALIAS, LA_ERR_HIP = range(6)
 LA_F32, LA_BF16 = 0, 1
 LA_FMAP_ELU1, LA_FMAP_FAVOR, LA_FMAP_IDENTITY = 0, 1, 2
-LA_GATE_NONE, LA_GATE_DECAY, LA_GATE_GLA, LA_GATE_SEL = 0, 1, 2, 3
+LA_GATE_NONE, LA_GATE_DECAY, LA_GATE_GLA, LA_GATE_SEL, LA_GATE_OUTER = 0, 1, 2, 3, 4
 LA_SLOT_READ, LA_SLOT_WRITE = 1, 2
 
 EXPORTED = ("la_abi_version", "la_status_str", "la_forward_workspace_size", "la_forward_segments",
@@ -33,7 +33,7 @@ class LaFeatureMap(ctypes.Structure):
 
 
 class LaGate(ctypes.Structure):
-    _fields_ = [("kind", c_int32), ("tau", c_float), ("gamma", c_void_p), ("g", c_void_p)]
+    _fields_ = [("kind", c_int32), ("tau", c_float), ("gamma", c_void_p), ("g", c_void_p), ("gv", c_void_p)]
 
 
 class LaBatch(ctypes.Structure):

@@ -57,10 +57,11 @@ def _fmap_struct(fmap: str, omega, d_k: int):
     return N.LaFeatureMap(_FMAP[fmap], d_k, None), d_k
 
 
-def _gate_struct(gate, expect_g_shape):
-    """gate: None | ("decay", gamma[H] fp32) | ("gla", g, tau) | ("sel", g, tau); g has shape
-    expect_g_shape for GLA and expect_g_shape without its last (feature) axis for the
-    selective scalar gate."""
+def _gate_struct(gate, expect_g_shape, d_v=None):
+    """gate: None | ("decay", gamma[H] fp32) | ("gla", g, tau) | ("sel", g, tau) |
+    ("outer", g, gv, tau); g has shape expect_g_shape for GLA and the outer-product gate,
+    and expect_g_shape without its last (feature) axis for the selective scalar gate; gv
+    (the outer-product gate's value side) has d_v on that last axis."""
     if gate is None or gate == "none" or (isinstance(gate, tuple) and gate[0] == "none"):
         return N.LaGate(N.LA_GATE_NONE, 1.0, None, None)
     kind = gate[0]
@@ -79,6 +80,15 @@ def _gate_struct(gate, expect_g_shape):
         if tuple(g.shape) != tuple(expect_g_shape[:-1]):
             raise ValueError(f"g must be {tuple(expect_g_shape[:-1])}, got {tuple(g.shape)}")
         return N.LaGate(N.LA_GATE_SEL, float(gate[2]), None, g.data_ptr())
+    if kind == "outer":
+        g, gv = _dev(gate[1], "g"), _dev(gate[2], "gv")
+        want_v = tuple(expect_g_shape[:-1]) + (d_v,)
+        if tuple(g.shape) != tuple(expect_g_shape) or tuple(gv.shape) != want_v:
+            raise ValueError(f"g must be {tuple(expect_g_shape)} and gv {want_v}, got {tuple(g.shape)}, "
+                             f"{tuple(gv.shape)}")
+        if gv.dtype != g.dtype:
+            raise TypeError("g and gv must share a dtype")
+        return N.LaGate(N.LA_GATE_OUTER, float(gate[3]), None, g.data_ptr(), gv.data_ptr())
     raise ValueError(f"unknown gate {kind!r}")
 
 
@@ -93,7 +103,8 @@ def workspace_size(B, H, n, d_k, d_v, *, fmap="elu1", r=None, causal=True, gate_
     out_dtype = dtype if out_dtype is None else out_dtype
     p = _problem(B, H, n, d_k, d_v, _DT[dtype], _DT[out_dtype], 1e-6)
     f = N.LaFeatureMap(_FMAP[fmap], r, 16 if fmap == "favor" else None)
-    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA, "sel": N.LA_GATE_SEL}[gate_kind]
+    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA, "sel": N.LA_GATE_SEL,
+          "outer": N.LA_GATE_OUTER}[gate_kind]
     g = N.LaGate(gk, 16.0, None, None)
     out = ctypes.c_size_t(0)
     N.check(N.lib().la_forward_workspace_size(ctypes.byref(p), ctypes.byref(f), int(causal), ctypes.byref(g),
@@ -107,7 +118,8 @@ def segments(B, H, n, d_k, d_v, *, fmap="elu1", r=None, causal=True, gate_kind="
     r = d_k if r is None else r
     p = _problem(B, H, n, d_k, d_v, _DT[dtype], _DT[dtype], 1e-6)
     f = N.LaFeatureMap(_FMAP[fmap], r, 16 if fmap == "favor" else None)
-    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA, "sel": N.LA_GATE_SEL}[gate_kind]
+    gk = {"none": N.LA_GATE_NONE, "decay": N.LA_GATE_DECAY, "gla": N.LA_GATE_GLA, "sel": N.LA_GATE_SEL,
+          "outer": N.LA_GATE_OUTER}[gate_kind]
     g = N.LaGate(gk, 16.0, None, None)
     P, L = ctypes.c_int32(0), ctypes.c_int32(0)
     N.check(N.lib().la_forward_segments(ctypes.byref(p), ctypes.byref(f), int(causal), ctypes.byref(g),
@@ -130,8 +142,8 @@ def _forward_args(Q, K, V, fmap, omega, causal, gate, eps, S0, z0, return_state,
     f, r = _fmap_struct(fmap, omega, d_k)
     if omega is not None and omega.dtype != Q.dtype:
         raise TypeError("omega must have the input dtype")
-    g = _gate_struct(gate, (B, H, n, r))
-    if g.kind == N.LA_GATE_GLA and gate[1].dtype != Q.dtype:
+    g = _gate_struct(gate, (B, H, n, r), d_v)
+    if g.kind in (N.LA_GATE_GLA, N.LA_GATE_OUTER) and gate[1].dtype != Q.dtype:
         raise TypeError("g must have the input dtype")
     p = _problem(B, H, n, d_k, d_v, in_dt, _DT[out_dtype], eps)
     if out is None:
@@ -207,7 +219,7 @@ def _batch_args(Q, K, V, cu_seqlens, max_seqlen, state, slot_ids, read, write, f
     B, H, n, d_k = Q.shape
     d_v = V.shape[3]
     f, r = _fmap_struct(fmap, omega, d_k)
-    g = _gate_struct(gate, (B, H, n, r))
+    g = _gate_struct(gate, (B, H, n, r), d_v)
     p = _problem(B, H, n, d_k, d_v, _dt(Q), _dt(Q), eps)
     if cu_seqlens is not None:
         _dev(cu_seqlens, "cu_seqlens")
@@ -302,7 +314,7 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
     B, H, n, d_k = Q.shape
     d_v = V.shape[3]
     f, r = _fmap_struct(fmap, None, d_k)
-    g = _gate_struct(gate, (B, H, n, r))
+    g = _gate_struct(gate, (B, H, n, r), d_v)
     p = _problem(B, H, n, d_k, d_v, _dt(Q), _dt(Q), eps)
     for t, nm, shp in ((S0, "S0", (B, H, r, d_v)), (z0, "z0", (B, H, r))):
         if t is not None:
@@ -378,7 +390,7 @@ def _decode_args(S, z, q, k, v, fmap, omega, gate, eps, out_dtype, out, stream):
         raise ValueError(f"S must be float32 {(B, H, r, d_v)}")
     if tuple(z.shape) != (B, H, r) or z.dtype != torch.float32:
         raise ValueError(f"z must be float32 {(B, H, r)}")
-    g = _gate_struct(gate, (B, H, r))
+    g = _gate_struct(gate, (B, H, r), d_v)
     p = _problem(B, H, 1, d_k, d_v, _dt(q), _DT[out_dtype], eps)
     if out is None:
         out = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)

@@ -61,14 +61,18 @@ la_status check_fmap(const la_feature_map* f, int dk) {
 
 // gate may be NULL (= NONE). `check_ptrs` is false for the size queries.
 la_status check_gate(const la_gate* g, bool check_ptrs) {
-  if (g == nullptr || g->kind == LA_GATE_NONE) return LA_OK;
+  if (g == nullptr) return LA_OK;
+  if (check_ptrs && g->gv != nullptr && g->kind != LA_GATE_OUTER) return LA_ERR_INVALID_ARG;
+  if (g->kind == LA_GATE_NONE) return LA_OK;
   if (g->kind == LA_GATE_DECAY) {
     if (check_ptrs && (g->gamma == nullptr || !aligned16(g->gamma))) return LA_ERR_INVALID_ARG;
     return LA_OK;
   }
-  if (g->kind == LA_GATE_GLA || g->kind == LA_GATE_SEL) {
+  if (g->kind == LA_GATE_GLA || g->kind == LA_GATE_SEL || g->kind == LA_GATE_OUTER) {
     if (!(g->tau > 0.f) || !isfinite(g->tau)) return LA_ERR_INVALID_ARG;
     if (check_ptrs && (g->g == nullptr || !aligned16(g->g))) return LA_ERR_INVALID_ARG;
+    if (check_ptrs && g->kind == LA_GATE_OUTER && (g->gv == nullptr || !aligned16(g->gv))) return LA_ERR_INVALID_ARG;
+    if (check_ptrs && g->kind != LA_GATE_OUTER && g->gv != nullptr) return LA_ERR_INVALID_ARG;
     return LA_OK;
   }
   return LA_ERR_INVALID_ARG;
@@ -78,8 +82,13 @@ int gate_kind(const la_gate* g) { return g == nullptr ? LA_GATE_NONE : g->kind; 
 
 // Gates driven by a raw input g (GLA: one value per feature and token; the
 // selective scalar gate: one per token), and that input's elements per token.
-bool gate_has_input(int gk) { return gk == LA_GATE_GLA || gk == LA_GATE_SEL; }
-size_t gate_input_per_token(int gk, size_t r) { return gk == LA_GATE_GLA ? r : (gk == LA_GATE_SEL ? 1 : 0); }
+bool gate_has_input(int gk) { return gk == LA_GATE_GLA || gk == LA_GATE_SEL || gk == LA_GATE_OUTER; }
+size_t gate_input_per_token(int gk, size_t r) {
+  return (gk == LA_GATE_GLA || gk == LA_GATE_OUTER) ? r : (gk == LA_GATE_SEL ? 1 : 0);
+}
+// The outer-product gate's value-side input gv: d_v elements per token.
+size_t gate_vinput_per_token(int gk, size_t dv) { return gk == LA_GATE_OUTER ? dv : 0; }
+const void* gate_vinput(const la_gate* g) { return gate_kind(g) == LA_GATE_OUTER ? g->gv : nullptr; }
 
 // The built set of (d_k, r, d_v) shapes; see the header.
 bool shapes_built(const la_feature_map* f, int dk, int dv, bool causal) {
@@ -147,16 +156,17 @@ void plan_splits(int B, int H, int n, int* splits, int* split_len) {
 }
 
 struct WsLayout {
-  size_t S_off, z_off, logG_off, bytes;
+  size_t S_off, z_off, logG_off, logGv_off, bytes;
 };
 
 // Segment states (and GLA log-gates) of BH sequences cut into `pieces`.
-WsLayout workspace_pieces(size_t BH, size_t pieces, size_t r, size_t dv, bool gla) {
-  WsLayout w{0, 0, 0, 0};
+WsLayout workspace_pieces(size_t BH, size_t pieces, size_t r, size_t dv, bool gla, bool outer = false) {
+  WsLayout w{0, 0, 0, 0, 0};
   w.S_off = 0;
   w.z_off = round_up(BH * pieces * r * dv * 4, kAlign);
   w.logG_off = round_up(w.z_off + BH * pieces * r * 4, kAlign);
-  w.bytes = gla ? round_up(w.logG_off + BH * pieces * r * 4, kAlign) : w.logG_off;
+  w.logGv_off = w.bytes = gla ? round_up(w.logG_off + BH * pieces * r * 4, kAlign) : w.logG_off;
+  if (gla && outer) w.bytes = round_up(w.logGv_off + BH * pieces * dv * 4, kAlign);
   return w;
 }
 
@@ -166,14 +176,14 @@ WsLayout workspace_layout(const la_problem* p, const la_feature_map* f, int caus
   if (causal) {
     int P, L;
     plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate, &P, &L);
-    if (P <= 1) return WsLayout{0, 0, 0, 0};
+    if (P <= 1) return WsLayout{0, 0, 0, 0, 0};
     pieces = (size_t)P;
   } else {
     int sp, L;
     plan_splits(p->B, p->H, p->n, &sp, &L);
     pieces = (size_t)sp;
   }
-  return workspace_pieces(BH, pieces, f->r, p->d_v, causal && gate_has_input(gate));
+  return workspace_pieces(BH, pieces, f->r, p->d_v, causal && gate_has_input(gate), gate == LA_GATE_OUTER);
 }
 
 // The causal kernels of the plan's feature map.
@@ -215,6 +225,7 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
   const int gk = gate_kind(g);
   if (!causal && gk != LA_GATE_NONE) return LA_ERR_INVALID_ARG;
   if (!causal || (f->kind != LA_FMAP_ELU1 && f->kind != LA_FMAP_IDENTITY)) return LA_ERR_UNSUPPORTED;
+  if (gk == LA_GATE_OUTER) return LA_ERR_UNSUPPORTED;
   if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   const int key = p->d_k * 1000 + p->d_v;
   if (key != 64064 && key != 64128 && key != 128064) return LA_ERR_UNSUPPORTED;
@@ -326,6 +337,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   const Range rq = range_of(Q, BH * n * p->d_k * isz), rk = range_of(K, BH * n * p->d_k * isz),
               rv = range_of(V, BH * n * p->d_v * isz);
   const Range rg = range_of(gate_has_input(gk) ? gate->g : nullptr, BH * n * gate_input_per_token(gk, r) * isz);
+  const Range rgv = range_of(gate_vinput(gate), BH * n * gate_vinput_per_token(gk, p->d_v) * isz);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
   const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
   const Range rs0 = range_of(S0, BH * r * p->d_v * 4), rz0 = range_of(z0, BH * r * 4);
@@ -334,7 +346,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   const WsLayout wl = workspace_layout(p, fmap, causal, gk);
   const Range rws = range_of(wl.bytes ? workspace : nullptr, wl.bytes);
   for (Range o : {ro, rsf, rzf, rws}) {
-    for (Range i : {rq, rk, rv, rg, rgam, rom, rs0, rz0})
+    for (Range i : {rq, rk, rv, rg, rgv, rgam, rom, rs0, rz0})
       if (overlaps(o, i)) return LA_ERR_ALIAS;
   }
   if (overlaps(ro, rsf) || overlaps(ro, rzf) || overlaps(rsf, rzf) || overlaps(rws, ro) || overlaps(rws, rsf) ||
@@ -363,6 +375,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   plan.K = K;
   plan.V = V;
   plan.g = gate_has_input(gk) ? gate->g : nullptr;
+  plan.gv = gate_vinput(gate);
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
   plan.omega = fmap->omega;
   plan.S0 = S0;
@@ -376,6 +389,7 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   plan.ws_S = wl.bytes ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
   plan.ws_z = wl.bytes ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
   plan.ws_logG = (wl.bytes && causal && gate_has_input(gk)) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
+  plan.ws_logGv = (wl.bytes && causal && gk == LA_GATE_OUTER) ? reinterpret_cast<float*>(ws + wl.logGv_off) : nullptr;
   if (causal) {
     plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, p->d_v, p->d_k, gk, &plan.P, &plan.seg_len);
     return launch_causal(plan);
@@ -414,8 +428,9 @@ WsLayout batch_plan(const la_problem* p, const la_batch* b, const la_problem& ef
     plan_segments_ragged(eff.B, p->H, p->n, eff.n, f->kind, f->r, p->d_v, p->d_k, gate, P, seg_len);
   else
     plan_segments(eff.B, p->H, eff.n, f->kind, f->r, p->d_v, p->d_k, gate, P, seg_len);
-  if (*P <= 1) return WsLayout{0, 0, 0, 0};
-  return workspace_pieces((size_t)eff.B * p->H, (size_t)*P, f->r, p->d_v, gate_has_input(gate));
+  if (*P <= 1) return WsLayout{0, 0, 0, 0, 0};
+  return workspace_pieces((size_t)eff.B * p->H, (size_t)*P, f->r, p->d_v, gate_has_input(gate),
+                          gate == LA_GATE_OUTER);
 }
 }  // namespace
 
@@ -453,6 +468,7 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   const Range rq = range_of(Q, BH * n * p->d_k * isz), rk = range_of(K, BH * n * p->d_k * isz),
               rv = range_of(V, BH * n * p->d_v * isz);
   const Range rg = range_of(gate_has_input(gk) ? gate->g : nullptr, BH * n * gate_input_per_token(gk, r) * isz);
+  const Range rgv = range_of(gate_vinput(gate), BH * n * gate_vinput_per_token(gk, p->d_v) * isz);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
   const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
   const Range rcu = range_of(batch->cu_seqlens, ((size_t)batch->num_seqs + 1) * 4);
@@ -465,7 +481,7 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   const WsLayout wl = batch_plan(p, batch, eff, fmap, gk, &P, &seg_len);
   const Range rws = range_of(wl.bytes ? workspace : nullptr, wl.bytes);
   for (Range o : {ro, rS, rz, rws})
-    for (Range i : {rq, rk, rv, rg, rgam, rom, rcu, rsl})
+    for (Range i : {rq, rk, rv, rg, rgv, rgam, rom, rcu, rsl})
       if (overlaps(o, i)) return LA_ERR_ALIAS;
   if (overlaps(ro, rS) || overlaps(ro, rz) || overlaps(rS, rz) || overlaps(rws, ro) || overlaps(rws, rS) ||
       overlaps(rws, rz))
@@ -493,6 +509,7 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   plan.K = K;
   plan.V = V;
   plan.g = gate_has_input(gk) ? gate->g : nullptr;
+  plan.gv = gate_vinput(gate);
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
   plan.omega = fmap->omega;
   plan.nseq = eff.B;
@@ -513,6 +530,7 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   plan.ws_S = wl.bytes ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
   plan.ws_z = wl.bytes ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
   plan.ws_logG = (wl.bytes && gate_has_input(gk)) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
+  plan.ws_logGv = (wl.bytes && gk == LA_GATE_OUTER) ? reinterpret_cast<float*>(ws + wl.logGv_off) : nullptr;
   plan.P = P;
   plan.seg_len = seg_len;
   if (batch->cu_seqlens == nullptr && p->n == 1) {
@@ -535,6 +553,7 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
     dp.k = K;
     dp.v = V;
     dp.g = plan.g;
+    dp.gv = plan.gv;
     dp.gamma = plan.gamma;
     dp.omega = fmap->omega;
     dp.out = out;
@@ -566,11 +585,12 @@ la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
   const Range rq = range_of(q, BH * p->d_k * isz), rk = range_of(k, BH * p->d_k * isz),
               rv = range_of(v, BH * p->d_v * isz);
   const Range rg = range_of(gate_has_input(gk) ? gate->g : nullptr, BH * gate_input_per_token(gk, r) * isz);
+  const Range rgv = range_of(gate_vinput(gate), BH * gate_vinput_per_token(gk, p->d_v) * isz);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
   const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
   const Range ro = range_of(out, BH * p->d_v * dtype_size(p->out_dtype));
   for (Range o : {rS, rz, ro})
-    for (Range i : {rq, rk, rv, rg, rgam, rom})
+    for (Range i : {rq, rk, rv, rg, rgv, rgam, rom})
       if (overlaps(o, i)) return LA_ERR_ALIAS;
   if (overlaps(rS, rz) || overlaps(ro, rS) || overlaps(ro, rz)) return LA_ERR_ALIAS;
 
@@ -592,6 +612,7 @@ la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
   plan.k = k;
   plan.v = v;
   plan.g = gate_has_input(gk) ? gate->g : nullptr;
+  plan.gv = gate_vinput(gate);
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
   plan.omega = fmap->omega;
   plan.out = out;

@@ -61,7 +61,11 @@ __device__ __forceinline__ float phi_ew_deriv(float phi) {
   if constexpr (FMAP == FM_IDENT) return 1.f;
   else return fminf(phi, 1.f);
 }
-enum GateKind { GT_NONE = 0, GT_DECAY = 1, GT_GLA = 2, GT_SEL = 3 };
+enum GateKind { GT_NONE = 0, GT_DECAY = 1, GT_GLA = 2, GT_SEL = 3, GT_OUTER = 4 };
+// Gates with an input-dependent factor per key feature: GLA, and the
+// outer-product gate, which adds a factor per value column.
+template <int GATE>
+constexpr bool kKeyGate = GATE == GT_GLA || GATE == GT_OUTER;
 // Gates that scale every feature of a step alike (RetNet's fixed gamma, the
 // selective scalar a_t): keys are weighted per token, one factor per step.
 template <int GATE>
@@ -72,6 +76,7 @@ struct CausalArgs {
   const bf16* K;
   const bf16* V;
   const bf16* g;
+  const bf16* gv;          // the outer-product gate's value-side input [tok][E]
   const bf16* omega;
   const float* gamma;
   const float* S_in;       // pass 3: initial state per (head, segment); nullable
@@ -80,7 +85,8 @@ struct CausalArgs {
   long long in_seg;        // S_in element stride between segments
   float* S_out;            // pass 1: per-segment deltas; pass 3: final state (nullable)
   float* z_out;
-  float* logG_out;         // pass 1, GLA: per-segment summed log-gates
+  float* logG_out;         // pass 1, gates with an input: per-segment summed log-gates
+  float* logGv_out;        // pass 1, outer-product gate: per-segment summed value-side log-gates
   bf16* out;
   // A batch of independent sequences: with cu, blockIdx.y = b H + h and
   // sequence b is tokens cu[b] .. cu[b+1] of head h's n rows ([H][n][.]
@@ -177,7 +183,11 @@ struct FwdLayout {
   static constexpr int rs_off = gam_off + R * 4;   // [64] score row sums
   static constexpr int zd_off = rs_off + kChunk * 4;  // [64] Q^ . z_prev
   static constexpr int bs_off = zd_off + kChunk * 4;  // selective gate: [64] cumulative log-gate
-  static constexpr int bytes = bs_off + (GATE == GT_SEL ? kChunk * 4 : 0);
+  // outer-product gate: e^{c} per token and value column (fp32, rows of E + 4:
+  // 16-byte reads of 16 rows spread over the banks), e^{c_end} per column
+  static constexpr int ec_off = bs_off + (GATE == GT_SEL ? kChunk * 4 : 0);
+  static constexpr int gamv_off = ec_off + (GATE == GT_OUTER ? kChunk * (E + 4) * 4 : 0);
+  static constexpr int bytes = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
 };
 
 // Pass 1: one chunk (K^ rows, V rows, gate factors) per half, then the
@@ -186,14 +196,16 @@ struct FwdLayout {
 // whose preludes are short, run 2-5% slower pipelined).
 template <int R, int E, int GATE>
 struct SegLayout {
-  static constexpr bool PIPELINED = GATE == GT_GLA;
+  static constexpr bool PIPELINED = kKeyGate<GATE>;
   static constexpr bool SWZ = false;  // padded tiles (FeatTile)
   static constexpr int k_off = 0;     // K^ rows
   static constexpr int v_off = k_off + FeatTile<R, SWZ>::BYTES;
   static constexpr int gam_off = v_off + FeatTile<E, SWZ>::BYTES;
-  static constexpr int HALF = gam_off + R * 4;
+  static constexpr int gamv_off = gam_off + R * 4;  // outer-product gate: [E] e^{c_end}
+  static constexpr int HALF = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
   static constexpr int logg_off = (PIPELINED ? 2 : 1) * HALF;
-  static constexpr int bs_off = logg_off + R * 4;  // selective gate: [64] cumulative log-gate
+  static constexpr int loggv_off = logg_off + R * 4;  // outer-product gate: [E] summed value-side log-gates
+  static constexpr int bs_off = loggv_off + (GATE == GT_OUTER ? E * 4 : 0);  // selective gate: [64] cumulative log-gate
   static constexpr int bytes = bs_off + (GATE == GT_SEL ? kChunk * 4 : 0);
 };
 
@@ -250,11 +262,12 @@ struct RawChunk {
   static constexpr int TPW = kChunk / NW;  // tokens per wave (row-major layout)
   static constexpr int LPT = NW;           // lanes per token (row-major layout)
   static constexpr bool ELU = FMAP != FM_FAVOR;  // elementwise feature maps
-  static constexpr bool ROWMAJOR = ELU && GATE != GT_GLA;
+  static constexpr bool ROWMAJOR = ELU && !kKeyGate<GATE>;
   // row-major: R / (8 LPT) blocks of 8 features per lane per row (= FR / 8)
   bf16x8 q[ELU && WITH_Q ? FR / 8 : 1];
   bf16x8 k[ELU ? FR / 8 : 1];
-  bf16x8 g[GATE == GT_GLA ? FR / 8 : 1];
+  bf16x8 g[kKeyGate<GATE> ? FR / 8 : 1];
+  bf16x8 gv[GATE == GT_OUTER ? EV / 8 : 1];  // outer-product gate: value-side inputs, as v
   bf16 sg;  // selective gate: the input of token t0 + lane (every wave loads all 64)
   bf16x8 xq[!ELU && WITH_Q ? KS : 1];   // FAVOR+: token 16 w + l % 16, columns 32 ks + 8 (l / 16)
   bf16x8 xk[!ELU ? KS : 1];
@@ -291,12 +304,16 @@ struct RawChunk {
           k[j] = *reinterpret_cast<const bf16x8*>(a.K + row * R + w * FR + 8 * j);
         }
       }
-      if constexpr (GATE == GT_GLA) {
+      if constexpr (kKeyGate<GATE>) {
 #pragma unroll
         for (int j = 0; j < FR / 8; ++j) g[j] = *reinterpret_cast<const bf16x8*>(a.g + row * R + w * FR + 8 * j);
       }
 #pragma unroll
       for (int j = 0; j < EV / 8; ++j) v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * E + w * EV + 8 * j);
+      if constexpr (GATE == GT_OUTER) {
+#pragma unroll
+        for (int j = 0; j < EV / 8; ++j) gv[j] = *reinterpret_cast<const bf16x8*>(a.gv + row * E + w * EV + 8 * j);
+      }
     }
     if constexpr (!ELU) {
       const long long row = tok0 + min(t0 + 16 * w + c16, row_end - 1);
@@ -325,7 +342,8 @@ template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SW
 __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>& raw,
                                               const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
                                               int k_off, int kh_off, int v_off, int gam_off, int logg_off,
-                                              int lane, int w, int qd_off = 0, int kd_off = 0, int bs_off = 0) {
+                                              int lane, int w, int qd_off = 0, int kd_off = 0, int bs_off = 0,
+                                              int ec_off = 0, int gamv_off = 0, int loggv_off = 0) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
   constexpr int LPT = Raw::LPT;
   using FT = FeatTile<R, SWZ>;
@@ -393,7 +411,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       for (int u = 0; u < 8; ++u) {
         float pq = WITH_Q ? phi_ew<FMAP>(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
         float pk = phi_ew<FMAP>(to_f32(raw.k[j][u]));
-        if constexpr (GATE == GT_GLA) {
+        if constexpr (kKeyGate<GATE>) {
           float la = keep_if(valid, gla_log_alpha(to_f32(raw.g[j][u]), a.inv_tau));
           float b = wave_inclusive_scan(la);
           // the chunk total is uniform across the wave: a scalar read of lane 63
@@ -413,24 +431,56 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         lds<bf16x8>(sm, q_off + fo) = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
       lds<bf16x8>(sm, k_off + fo) =
           keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
-      if constexpr (GATE == GT_GLA && (EXTRA & kPreQD) != 0)
+      if constexpr (kKeyGate<GATE> && (EXTRA & kPreQD) != 0)
         lds<bf16x8>(sm, qd_off + fo) = cat8(pack4(dq[0], dq[1], dq[2], dq[3]), pack4(dq[4], dq[5], dq[6], dq[7]));
-      if constexpr (GATE == GT_GLA && (EXTRA & kPreKD) != 0)
+      if constexpr (kKeyGate<GATE> && (EXTRA & kPreKD) != 0)
         lds<bf16x8>(sm, kd_off + fo) = cat8(pack4(dk[0], dk[1], dk[2], dk[3]), pack4(dk[4], dk[5], dk[6], dk[7]));
     }
-    if constexpr (GATE == GT_GLA) {
+    if constexpr (kKeyGate<GATE>) {
       if (lane < Raw::FR) {
         lds<float>(sm, gam_off + 4 * (w * Raw::FR + lane)) = __expf(my_bend);
         if constexpr (!WITH_Q || (EXTRA & kPreLogG) != 0) lds<float>(sm, logg_off + 4 * (w * Raw::FR + lane)) += my_bend;
       }
     }
   }
-  // values (rows past the end are zero)
+  // values (rows past the end are zero). The outer-product gate's value side:
+  // c, the chunk's inclusive cumulative log-gate per value column (lane =
+  // token), gives V~ = e^{-c} v in the tile; WITH_Q also writes e^{c} (the
+  // outputs' factor), and every pass e^{c_end} per column (the state's
+  // column factor; pass 1 adds c_end to the segment's summed log-gates).
   {
     constexpr int EV = Raw::EV;
+    float my_cend = 0.f;
 #pragma unroll
-    for (int j = 0; j < EV / 8; ++j)
-      lds<bf16x8>(sm, v_off + VT::at(lane, w * EV / 8 + j)) = keep_if(valid, raw.v[j]);
+    for (int j = 0; j < EV / 8; ++j) {
+      if constexpr (GATE == GT_OUTER) {
+        float vs[8], ecs[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float la = keep_if(valid, gla_log_alpha(to_f32(raw.gv[j][u]), a.inv_tau));
+          const float c = wave_inclusive_scan(la);
+          const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
+          vs[u] = to_f32(raw.v[j][u]) * __expf(-c);
+          ecs[u] = __expf(c);
+          my_cend = lane == 8 * j + u ? cend : my_cend;
+        }
+        lds<bf16x8>(sm, v_off + VT::at(lane, w * EV / 8 + j)) =
+            keep_if(valid, cat8(pack4(vs[0], vs[1], vs[2], vs[3]), pack4(vs[4], vs[5], vs[6], vs[7])));
+        if constexpr (WITH_Q) {
+          const int eo = ec_off + 4 * (lane * (E + 4) + w * EV + 8 * j);
+          lds<f32x4>(sm, eo) = f32x4{ecs[0], ecs[1], ecs[2], ecs[3]};
+          lds<f32x4>(sm, eo + 16) = f32x4{ecs[4], ecs[5], ecs[6], ecs[7]};
+        }
+      } else {
+        lds<bf16x8>(sm, v_off + VT::at(lane, w * EV / 8 + j)) = keep_if(valid, raw.v[j]);
+      }
+    }
+    if constexpr (GATE == GT_OUTER) {
+      if (lane < EV) {
+        lds<float>(sm, gamv_off + 4 * (w * EV + lane)) = __expf(my_cend);
+        if constexpr (!WITH_Q) lds<float>(sm, loggv_off + 4 * (w * EV + lane)) += my_cend;
+      }
+    }
   }
 }
 
@@ -472,7 +522,7 @@ struct ZTiles {
 // state needs.
 template <int R, int E, int GATE, int NW, bool SWZ, bool ZW = false, bool PRE = false, class SArr, class ZArr>
 __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_off, int v_off, int gam_off,
-                                             float gscale, int lane, int w, int zw_off = 0) {
+                                             float gscale, int lane, int w, int zw_off = 0, int gamv_off = 0) {
   constexpr int ZT = ZTiles<R, NW>::ZT, NEB = E / (16 * NW);
   const int g4 = lane >> 4;
   const int ebase = w * (E / NW);
@@ -490,22 +540,25 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) ka[ks] = tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane);
     float gr[4] = {gscale, gscale, gscale, gscale};
-    if constexpr (GATE == GT_GLA) {
+    if constexpr (kKeyGate<GATE>) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) gr[i] = lds<float>(sm, gam_off + 4 * (16 * rt + 4 * g4 + i));
     }
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
       f32x4 st = S[rt][eb];
-      if constexpr (kScalarDecay<GATE> || (GATE == GT_GLA && PRE)) {
+      if constexpr (kScalarDecay<GATE> || (kKeyGate<GATE> && PRE)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[i] *= gr[i];
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vb[eb][ks], st);
-      if constexpr (GATE == GT_GLA && !PRE) {
+      if constexpr (kKeyGate<GATE> && !PRE) {
+        // the outer-product gate: also the column's value-side factor
+        float gc = 1.f;
+        if constexpr (GATE == GT_OUTER) gc = lds<float>(sm, gamv_off + 4 * (ebase + 16 * eb + (lane & 15)));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[i] *= gr[i];
+        for (int i = 0; i < 4; ++i) st[i] *= gr[i] * gc;
       }
       S[rt][eb] = st;
     }
@@ -517,11 +570,11 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
       const int rt = w * ZT + j;
       f32x4 zt = Z[j];
       float gr[4] = {gscale, gscale, gscale, gscale};
-      if constexpr (GATE == GT_GLA) {
+      if constexpr (kKeyGate<GATE>) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) gr[i] = lds<float>(sm, gam_off + 4 * (16 * rt + 4 * g4 + i));
       }
-      if constexpr (kScalarDecay<GATE> || (GATE == GT_GLA && PRE)) {
+      if constexpr (kScalarDecay<GATE> || (kKeyGate<GATE> && PRE)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
@@ -535,7 +588,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
         }
         zt = mfma16(tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane), zb, zt);
       }
-      if constexpr (GATE == GT_GLA && !PRE) {
+      if constexpr (kKeyGate<GATE> && !PRE) {  // z takes the key side only
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
@@ -597,6 +650,9 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
   f32x4 Z[ZTiles<R, NW>::ZT];
   z_load<R, NW>(Z, nullptr, lane, w);
   if (tid < R) lds<float>(sm, LY::logg_off + 4 * tid) = 0.f;
+  if constexpr (GATE == GT_OUTER) {
+    if (tid < E) lds<float>(sm, LY::loggv_off + 4 * tid) = 0.f;
+  }
   lds_barrier();
 
   // Two chunks of loads in flight: raw buffer b holds chunks of parity b;
@@ -615,14 +671,15 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
     const int L = min(kChunk, sv.len - (t_begin + ci * kChunk));
     chunk_prelude<R, E, DK, FMAP, GATE, false, NW, LY::SWZ>(rw, a, L, lg2gam, sm, 0, half * LY::HALF + LY::k_off, 0,
                                                    half * LY::HALF + LY::v_off, half * LY::HALF + LY::gam_off,
-                                                   LY::logg_off, lane, w, 0, 0, LY::bs_off);
+                                                   LY::logg_off, lane, w, 0, 0, LY::bs_off, 0,
+                                                   half * LY::HALF + LY::gamv_off, LY::loggv_off);
   };
   auto update = [&](int ci, int half) {
     const int L = min(kChunk, sv.len - (t_begin + ci * kChunk));
     float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
     if constexpr (GATE == GT_SEL) gsc = __expf(lds<float>(sm, LY::bs_off + 4 * 63));
     state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, half * LY::HALF + LY::k_off, half * LY::HALF + LY::v_off,
-                                 half * LY::HALF + LY::gam_off, gsc, lane, w);
+                                 half * LY::HALF + LY::gam_off, gsc, lane, w, 0, half * LY::HALF + LY::gamv_off);
   };
   if constexpr (LY::PIPELINED) {
     // while the state update of chunk ci reads half ci & 1, the prelude of
@@ -667,8 +724,11 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
 #pragma unroll
       for (int i = 0; i < 4; ++i) So[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = S[rt][eb][i];
   z_store<R, NW>(Z, a.z_out + slot * R, lane, w);
-  if constexpr (GATE == GT_GLA || GATE == GT_SEL) {
+  if constexpr (kKeyGate<GATE> || GATE == GT_SEL) {
     if (tid < R) a.logG_out[slot * R + tid] = lds<float>(sm, LY::logg_off + 4 * tid);
+  }
+  if constexpr (GATE == GT_OUTER) {
+    if (tid < E) a.logGv_out[slot * E + tid] = lds<float>(sm, LY::loggv_off + 4 * tid);
   }
 }
 
@@ -745,7 +805,8 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
     const int L = min(kChunk, sv.len - t0);
     if (live)
       chunk_prelude<R, E, DK, FMAP, GATE, true, NW, LY::SWZ>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
-                                                    LY::v_off, LY::gam_off, 0, lane, w, 0, 0, LY::bs_off);
+                                                    LY::v_off, LY::gam_off, 0, lane, w, 0, 0, LY::bs_off,
+                                                    LY::ec_off, LY::gamv_off);
     // the raw registers are free again: this refill flies during the next DEPTH chunks
     raw.load(a, tok0, t0 + DEPTH * kChunk, t_end, lane, w);
     if (!live) return;
@@ -846,6 +907,12 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
         for (int p2 = 0; p2 <= qt / 2; ++p2)
           acc = mfma16(tr_feat<E, LY::SWZ>(sm, LY::v_off, 32 * p2, e, lane),
                        lds<bf16x8>(sm, LY::a_off + AT::at(q, 4 * p2 + g4)), acc);
+        if constexpr (GATE == GT_OUTER) {
+          // both parts carry e^{-c} of the chunk start on the value side
+          const f32x4 ec = lds<f32x4>(sm, LY::ec_off + 4 * (q * (E + 4) + e + 4 * g4));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] *= ec[i];
+        }
         if (q < L) {
           bf16x4 o = pack4(acc[0] * inv_den, acc[1] * inv_den, acc[2] * inv_den, acc[3] * inv_den);
           *reinterpret_cast<bf16x4*>(a.out + (tok0 + t0 + q) * E + e + 4 * g4) = o;
@@ -857,7 +924,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
     float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
     if constexpr (GATE == GT_SEL) gsc = __expf(lds<float>(sm, LY::bs_off + 4 * 63));
     state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, kScalarDecay<GATE> ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
-                                 gsc, lane, w);
+                                 gsc, lane, w, 0, LY::gamv_off);
     z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
     lds_barrier();
   };
@@ -891,6 +958,7 @@ la_status run_causal(const FwdPlan& p) {
   a.K = static_cast<const bf16*>(p.K);
   a.V = static_cast<const bf16*>(p.V);
   a.g = static_cast<const bf16*>(p.g);
+  a.gv = static_cast<const bf16*>(p.gv);
   a.omega = static_cast<const bf16*>(p.omega);
   a.gamma = p.gamma;
   a.out = static_cast<bf16*>(p.out);
@@ -902,7 +970,7 @@ la_status run_causal(const FwdPlan& p) {
   a.P = p.P;
   a.seg_len = p.seg_len;
   a.eps = p.eps;
-  a.inv_tau = (GATE == GT_GLA || GATE == GT_SEL) ? 1.f / p.tau : 0.f;
+  a.inv_tau = (kKeyGate<GATE> || GATE == GT_SEL) ? 1.f / p.tau : 0.f;
   const unsigned BH = unsigned(p.nseq) * unsigned(p.H);
 
   if (p.P > 1) {
@@ -910,6 +978,7 @@ la_status run_causal(const FwdPlan& p) {
     a1.S_out = p.ws_S;
     a1.z_out = p.ws_z;
     a1.logG_out = p.ws_logG;
+    a1.logGv_out = p.ws_logGv;
     auto k1 = causal_segment_state<R, E, DK, FMAP, GATE>;
     constexpr int lds1 = SegLayout<R, E, GATE>::bytes;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=

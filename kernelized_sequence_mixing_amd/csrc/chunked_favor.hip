@@ -71,11 +71,14 @@ static int elu_lds(int dv, int gate) {
     case GT_DECAY: return elu_lds_gate<R, GT_DECAY>(dv);
     case GT_GLA: return elu_lds_gate<R, GT_GLA>(dv);
     case GT_SEL: return elu_lds_gate<R, GT_SEL>(dv);
+    case GT_OUTER: return elu_lds_gate<R, GT_OUTER>(dv);
   }
   return 0;
 }
 
-static_assert(GT_NONE == LA_GATE_NONE && GT_DECAY == LA_GATE_DECAY && GT_GLA == LA_GATE_GLA, "gate codes");
+static_assert(GT_NONE == LA_GATE_NONE && GT_DECAY == LA_GATE_DECAY && GT_GLA == LA_GATE_GLA &&
+                  GT_SEL == LA_GATE_SEL && GT_OUTER == LA_GATE_OUTER,
+              "gate codes");
 
 int causal_output_lds_bytes(int fmap, int r, int dv, int dk, int gate) {
   if (fmap == LA_FMAP_FAVOR) {

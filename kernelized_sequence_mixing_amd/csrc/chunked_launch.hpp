@@ -14,6 +14,7 @@ static la_status causal_by_gate(const FwdPlan& p) {
     case GT_DECAY: return run_causal<R, E, R, FMAP, GT_DECAY>(p);
     case GT_GLA: return run_causal<R, E, R, FMAP, GT_GLA>(p);
     case GT_SEL: return run_causal<R, E, R, FMAP, GT_SEL>(p);
+    case GT_OUTER: return run_causal<R, E, R, FMAP, GT_OUTER>(p);
   }
   return LA_ERR_UNSUPPORTED;
 }

@@ -5,6 +5,8 @@
 //
 //   S' = G S + phi(k) v^T,  z' = G z + phi(k),  o = phi(q)^T S' / (phi(q)^T z' + eps)
 //
+// (the outer-product gate scales entry (f, e) of S by alpha_f beta_e and z by
+// alpha),
 // The step streams each head's r x d_v fp32 state through once (read + write),
 // so it is bound by HBM bandwidth. One workgroup per (batch, head): thread
 // (row group, column quad) owns float4 column quads of R/(256/(E/4)) rows, all
@@ -24,6 +26,7 @@ struct DecodeArgs {
   const void* k;
   const void* v;
   const void* g;
+  const void* gv;  // the outer-product gate's value-side input [B][H][E]
   const void* omega;
   const float* gamma;
   void* out;
@@ -41,6 +44,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   __shared__ float sxq[DK], sxk[DK];
   __shared__ float spq[R], spk[R], sal[R];
   __shared__ __attribute__((aligned(16))) float sv[E];
+  __shared__ __attribute__((aligned(16))) float sbeta[E];  // value-side factors (1 without the outer-product gate)
   __shared__ __attribute__((aligned(16))) float sred[RPP * E];
   __shared__ float shalf[2], sden;
   const int tid = threadIdx.x;
@@ -54,12 +58,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   // back from one basic block (clamped indices, no branches): the prologue
   // below then waits only for the small loads while the whole state slice is
   // in flight.
-  const bool gla = a.gate == LA_GATE_GLA, sel = a.gate == LA_GATE_SEL;
+  const bool gla = a.gate == LA_GATE_GLA || a.gate == LA_GATE_OUTER, sel = a.gate == LA_GATE_SEL;
+  const bool outer = a.gate == LA_GATE_OUTER;
   const int iq = min(tid, DK - 1), iv = min(tid, E - 1), ir = min(tid, R - 1);
   // GLA: one gate input per feature; selective: one per head
   const InT* gp = gla ? static_cast<const InT*>(a.g) + bh * R + ir
                       : (sel ? static_cast<const InT*>(a.g) + bh : q + bh * DK + iq);
   const InT rq = q[bh * DK + iq], rk = k[bh * DK + iq], rv = v[bh * E + iv], rg = *gp;
+  const InT rgv = outer ? static_cast<const InT*>(a.gv)[bh * E + iv] : rv;
   long long si = bh;  // this head's state
   if (a.slot != nullptr) {
     const int sl = a.slot[bh / a.H];
@@ -85,6 +91,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   sxq[iq] = xq;
   sxk[iq] = xk;
   sv[iv] = xv;
+  sbeta[iv] = outer ? __expf(gla_log_alpha(to_f32(rgv), a.inv_tau)) : 1.f;
   __syncthreads();
   if constexpr (FMAP == 1) {
     if (tid < 2) {
@@ -118,7 +125,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     }
     float al = 1.f;
     if (a.gate == LA_GATE_DECAY) al = a.gamma[bh % a.H];
-    if (a.gate == LA_GATE_GLA || a.gate == LA_GATE_SEL) al = __expf(gla_log_alpha(xg, a.inv_tau));
+    if (gla || sel) al = __expf(gla_log_alpha(xg, a.inv_tau));
     spq[tid] = pq;
     spk[tid] = pk;
     sal[tid] = al;
@@ -144,16 +151,17 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
 
   // rank-1 update in place and partial read-out over this thread's rows
   const float4 vv = reinterpret_cast<const float4*>(sv)[col4];
+  const float4 bt = reinterpret_cast<const float4*>(sbeta)[col4];
   float4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int r = r0 + RPP * p;
     const float al = sal[r], pk = spk[r], pq = spq[r];
     float4 s = st[p];
-    s.x = al * s.x + pk * vv.x;
-    s.y = al * s.y + pk * vv.y;
-    s.z = al * s.z + pk * vv.z;
-    s.w = al * s.w + pk * vv.w;
+    s.x = al * bt.x * s.x + pk * vv.x;
+    s.y = al * bt.y * s.y + pk * vv.y;
+    s.z = al * bt.z * s.z + pk * vv.z;
+    s.w = al * bt.w * s.w + pk * vv.w;
     if (wr) Sh[r * CG + col4] = s;
     o.x += pq * s.x;
     o.y += pq * s.y;
@@ -172,10 +180,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
 
 template <int R, int E, int DK, int FMAP>
 static la_status run_decode(const DecodePlan& p) {
-  DecodeArgs a{p.S,         p.z,          p.q,    p.k,    p.v,         p.g,
-               p.omega,     p.gamma,      p.out,  p.H,    p.in_dtype,  p.out_dtype,
-               p.gate,      p.eps,        (p.gate == LA_GATE_GLA || p.gate == LA_GATE_SEL) ? 1.f / p.tau : 0.f,
-               p.slot,      p.nslot,      p.flags};
+  const bool inp = p.gate == LA_GATE_GLA || p.gate == LA_GATE_SEL || p.gate == LA_GATE_OUTER;
+  DecodeArgs a{p.S,     p.z,      p.q,        p.k,          p.v,    p.g,   p.gv,
+               p.omega, p.gamma,  p.out,      p.H,          p.in_dtype,   p.out_dtype,
+               p.gate,  p.eps,    inp ? 1.f / p.tau : 0.f,  p.slot, p.nslot, p.flags};
   if (p.in_dtype == LA_BF16)
     hipLaunchKernelGGL((decode_step_kernel<R, E, DK, FMAP, bf16>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256), 0,
                        p.stream, a);

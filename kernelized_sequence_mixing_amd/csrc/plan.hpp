@@ -31,6 +31,7 @@ struct FwdPlan {
   const void* K;
   const void* V;
   const void* g;
+  const void* gv;  // value-side gate input (the outer-product gate only)
   const void* omega;
   const float* gamma;
   const float* S0;
@@ -52,7 +53,8 @@ struct FwdPlan {
   // workspace carve (device)
   float* ws_S;     // [BH][P or splits][r][dv]
   float* ws_z;     // [BH][P or splits][r]
-  float* ws_logG;  // [BH][P][r]  (GLA only)
+  float* ws_logG;  // [BH][P][r]  (gates with an input)
+  float* ws_logGv; // [BH][P][dv] (the outer-product gate's value side)
   hipStream_t stream;
 };
 
@@ -85,6 +87,7 @@ struct DecodePlan {
   const void* k;
   const void* v;
   const void* g;
+  const void* gv;  // value-side gate input (the outer-product gate only)
   const void* omega;
   const float* gamma;
   void* out;

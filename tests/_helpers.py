@@ -22,6 +22,8 @@ def gpu_gate(inp):
         return ("decay", dev(inp["gamma"]))
     if kind in ("gla", "sel"):
         return (kind, dev(inp["g"]), inp["tau"])
+    if kind == "outer":
+        return ("outer", dev(inp["g"]), dev(inp["gv"]), inp["tau"])
     return None
 
 
@@ -37,6 +39,13 @@ def oracle_gate(inp, heads=None, t_slice=None):
         if t_slice is not None:
             g = g[:, :, t_slice]
         return (kind, g, inp["tau"])
+    if kind == "outer":
+        g, gv = to_f64(inp["g"]), to_f64(inp["gv"])
+        if heads is not None:
+            g, gv = (x[heads[0]:heads[0] + 1, heads[1]:heads[1] + 1] for x in (g, gv))
+        if t_slice is not None:
+            g, gv = g[:, :, t_slice], gv[:, :, t_slice]
+        return ("outer", g, gv, inp["tau"])
     return None
 
 
@@ -60,6 +69,8 @@ def oracle_forward(inp, head=None, eps=None, S0=None, z0=None):
         Q, K, V = (x[b:b + 1, h:h + 1] for x in (Q, K, V))
         if gate is not None and gate[0] in ("gla", "sel"):
             gate = (gate[0], gate[1][b:b + 1, h:h + 1], gate[2])
+        if gate is not None and gate[0] == "outer":
+            gate = ("outer", gate[1][b:b + 1, h:h + 1], gate[2][b:b + 1, h:h + 1], gate[3])
         if gate is not None and gate[0] == "decay":
             gate = ("decay", gate[1][h:h + 1])
     om = to_f64(inp["omega"]) if inp["fmap"] == "favor" else None

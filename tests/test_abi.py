@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     lib = N.lib()
-    assert lib.la_abi_version() == 5
+    assert lib.la_abi_version() == 6
     names = [lib.la_status_str(i).decode() for i in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_ALIAS",
                      "LA_ERR_HIP"]
@@ -62,7 +62,8 @@ def test_struct_layouts_match_the_header(tmp_path):
 int main(void) {{
   printf("%zu %zu %zu\\n", sizeof(la_problem), offsetof(la_problem, eps), offsetof(la_problem, out_dtype));
   printf("%zu %zu %zu\\n", sizeof(la_feature_map), offsetof(la_feature_map, r), offsetof(la_feature_map, omega));
-  printf("%zu %zu %zu %zu\\n", sizeof(la_gate), offsetof(la_gate, tau), offsetof(la_gate, gamma), offsetof(la_gate, g));
+  printf("%zu %zu %zu %zu %zu\\n", sizeof(la_gate), offsetof(la_gate, tau), offsetof(la_gate, gamma), offsetof(la_gate, g),
+         offsetof(la_gate, gv));
   printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(la_batch), offsetof(la_batch, cu_seqlens),
          offsetof(la_batch, num_seqs), offsetof(la_batch, max_seqlen), offsetof(la_batch, S), offsetof(la_batch, z),
          offsetof(la_batch, slot_ids), offsetof(la_batch, num_slots), offsetof(la_batch, flags));
@@ -74,7 +75,8 @@ int main(void) {{
     c = [list(map(int, ln.split())) for ln in lines if ln.strip()]
     assert c[0] == [ctypes.sizeof(N.LaProblem), N.LaProblem.eps.offset, N.LaProblem.out_dtype.offset]
     assert c[1] == [ctypes.sizeof(N.LaFeatureMap), N.LaFeatureMap.r.offset, N.LaFeatureMap.omega.offset]
-    assert c[2] == [ctypes.sizeof(N.LaGate), N.LaGate.tau.offset, N.LaGate.gamma.offset, N.LaGate.g.offset]
+    assert c[2] == [ctypes.sizeof(N.LaGate), N.LaGate.tau.offset, N.LaGate.gamma.offset, N.LaGate.g.offset,
+                    N.LaGate.gv.offset]
     B = N.LaBatch
     assert c[3] == [ctypes.sizeof(B), B.cu_seqlens.offset, B.num_seqs.offset, B.max_seqlen.offset, B.S.offset,
                     B.z.offset, B.slot_ids.offset, B.num_slots.offset, B.flags.offset]
@@ -127,6 +129,7 @@ SP = 1 << 32           # spacing of the fake buffers: far apart, so only planted
 def _args(**over):
     d = dict(B=2, H=3, n=100, d_k=64, d_v=64, in_dt=N.LA_BF16, out_dt=N.LA_BF16, eps=1e-6,
              fkind=N.LA_FMAP_ELU1, r=64, omega=None, causal=1, gkind=N.LA_GATE_NONE, tau=16.0, gamma=None, g=None,
+             gv=None,
              Q=FAKE, K=FAKE + SP, V=FAKE + 2 * SP, S0=None, z0=None, Sf=None, zf=None,
              out=FAKE + 3 * SP, ws=FAKE + 4 * SP, ws_bytes=1 << 30)
     d.update(over)
@@ -136,7 +139,7 @@ def _args(**over):
 def _forward(a):
     p = N.LaProblem(a["B"], a["H"], a["n"], a["d_k"], a["d_v"], a["in_dt"], a["out_dt"], a["eps"])
     f = N.LaFeatureMap(a["fkind"], a["r"], a["omega"])
-    g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"])
+    g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"], a["gv"])
     return N.lib().la_forward(ctypes.byref(p), a["Q"], a["K"], a["V"], ctypes.byref(f), a["causal"],
                               ctypes.byref(g), a["S0"], a["z0"], a["Sf"], a["zf"], a["out"], a["ws"],
                               a["ws_bytes"], None)
@@ -149,7 +152,18 @@ BAD_FORWARD = [
     ("sel tau 0", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP, tau=0.0), N.LA_ERR_INVALID_ARG),
     ("sel noncausal", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP, causal=0, in_dt=N.LA_F32, out_dt=N.LA_F32),
      N.LA_ERR_INVALID_ARG),
-    ("gate kind 4", dict(gkind=4), N.LA_ERR_INVALID_ARG),
+    ("gate kind 5", dict(gkind=5), N.LA_ERR_INVALID_ARG),
+    ("outer no g", dict(gkind=N.LA_GATE_OUTER, gv=FAKE + 7 * SP), N.LA_ERR_INVALID_ARG),
+    ("outer no gv", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP), N.LA_ERR_INVALID_ARG),
+    ("outer gv misaligned", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP + 8), N.LA_ERR_INVALID_ARG),
+    ("gv with gla", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP, gv=FAKE + 7 * SP), N.LA_ERR_INVALID_ARG),
+    ("gv without gate", dict(gv=FAKE + 7 * SP), N.LA_ERR_INVALID_ARG),
+    ("outer tau 0", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP, tau=0.0), N.LA_ERR_INVALID_ARG),
+    ("outer favor", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP, fkind=N.LA_FMAP_FAVOR, r=256,
+                         omega=FAKE + 5 * SP), N.LA_ERR_UNSUPPORTED),
+    ("outer noncausal", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP, causal=0, in_dt=N.LA_F32,
+                             out_dt=N.LA_F32), N.LA_ERR_INVALID_ARG),
+    ("outer gv under out", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 3 * SP + 256), N.LA_ERR_ALIAS),
     ("identity noncausal", dict(fkind=N.LA_FMAP_IDENTITY, causal=0, in_dt=N.LA_F32, out_dt=N.LA_F32),
      N.LA_ERR_UNSUPPORTED),
     ("identity r != d_k", dict(fkind=N.LA_FMAP_IDENTITY, r=32), N.LA_ERR_INVALID_ARG),
@@ -239,7 +253,7 @@ def test_feature_map_rejects():
 def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAKE + 13 * SP, dg=None):
     p = N.LaProblem(a["B"], a["H"], a["n"], a["d_k"], a["d_v"], a["in_dt"], a["out_dt"], a["eps"])
     f = N.LaFeatureMap(a["fkind"], a["r"], a["omega"])
-    g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"])
+    g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"], a["gv"])
     return N.lib().la_backward(ctypes.byref(p), a["Q"], a["K"], a["V"], dO, ctypes.byref(f), a["causal"],
                                ctypes.byref(g), a["S0"], a["z0"], dQ, dK, dV, dg, a["ws"], a["ws_bytes"], None)
 
@@ -251,6 +265,8 @@ BAD_BACKWARD = [
     ("sel without dg", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),
     ("sel favor", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP, fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP),
      dict(dg=FAKE + 14 * SP), N.LA_ERR_UNSUPPORTED),
+    ("outer", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP), dict(dg=FAKE + 14 * SP),
+     N.LA_ERR_UNSUPPORTED),
     ("sel dg aliases g", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), dict(dg=FAKE + 6 * SP + 1024), N.LA_ERR_ALIAS),
     ("sel dg in workspace", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), dict(dg=FAKE + 4 * SP + 4096),
      N.LA_ERR_ALIAS),
@@ -326,7 +342,7 @@ def _batch_call(a, cu=None, num_seqs=None, max_seqlen=None, S=FAKE + 20 * SP, z=
                 slot_ids=FAKE + 22 * SP, num_slots=8, flags=3, out=None):
     p = N.LaProblem(a["B"], a["H"], a["n"], a["d_k"], a["d_v"], a["in_dt"], a["out_dt"], a["eps"])
     f = N.LaFeatureMap(a["fkind"], a["r"], a["omega"])
-    g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"])
+    g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"], a["gv"])
     b = N.LaBatch(cu, a["B"] if num_seqs is None else num_seqs, a["n"] if max_seqlen is None else max_seqlen, S, z,
                   slot_ids, num_slots, flags)
     return N.lib().la_forward_batch(ctypes.byref(p), ctypes.byref(b), a["Q"], a["K"], a["V"], ctypes.byref(f),

@@ -19,7 +19,7 @@ class Workload:
     r: int                 # feature dimension (d_k for elu1)
     fmap: str              # "elu1" | "favor" | "identity" (the state-space read-out)
     causal: bool
-    gate: str              # "none" | "decay" | "gla" | "sel" (scalar selective)
+    gate: str              # "none" | "decay" | "gla" | "sel" (scalar selective) | "outer" (alpha beta^T)
     dtype: str             # input dtype: "f32" | "bf16"
     qk_scale: float        # Q, K ~ N(0,1) * qk_scale
     v_scale: float         # V ~ N(0,1) * v_scale

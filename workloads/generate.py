@@ -85,6 +85,9 @@ def make_inputs(wl, seed: int = 0, *, B=None, H=None, n=None, qk_scale=None,
         out["g"] = _cast(g, wl.dtype)
     if wl.gate == "sel":
         out["g"] = _cast(rng.standard_normal((B, H, n), dtype=f32), wl.dtype)
+    if wl.gate == "outer":  # key side as GLA, then the value side per value column
+        out["g"] = _cast(rng.standard_normal((B, H, n, wl.r), dtype=f32), wl.dtype)
+        out["gv"] = _cast(rng.standard_normal((B, H, n, wl.d_v), dtype=f32), wl.dtype)
     if wl.gate == "decay":
         out["gamma"] = torch.from_numpy(retnet_gammas(H))
     if wl.fmap == "favor":
@@ -120,6 +123,9 @@ def _decode_inputs(wl: Workload, rng, B, H, qs, vs) -> dict:
         d["g"] = _cast(rng.standard_normal((B, H, r), dtype=f32), wl.dtype)
     if wl.gate == "sel":
         d["g"] = _cast(rng.standard_normal((B, H), dtype=f32), wl.dtype)
+    if wl.gate == "outer":
+        d["g"] = _cast(rng.standard_normal((B, H, r), dtype=f32), wl.dtype)
+        d["gv"] = _cast(rng.standard_normal((B, H, dv), dtype=f32), wl.dtype)
     if wl.gate == "decay":
         d["gamma"] = torch.from_numpy(retnet_gammas(H))
     if wl.fmap == "favor":
