@@ -45,7 +45,7 @@ CHUNK = 64
 def algorithmic_per_token(wl):
     """(bytes, matrix-core flops) per head-token that the method must move/do.
 
-    Bytes: read q, k, v (and g) once, write o once. Flops (chunk C = 64, masked
+    Bytes: read q, k, v (and g; the outer-product gate also gv) once, write o once. Flops (chunk C = 64, masked
     upper triangle excluded): scores (C+1)/2 * 2r, intra A.V (C+1)/2 * 2 d_v,
     inter-chunk read 2 r d_v, state update 2 r d_v, FAVOR+ projection 2 * 2 d_k r.
     """
@@ -55,6 +55,8 @@ def algorithmic_per_token(wl):
         nbytes += isz * wl.r
     if wl.gate == "sel":
         nbytes += isz
+    if wl.gate == "outer":
+        nbytes += isz * (wl.r + wl.d_v)
     half = (CHUNK + 1) / 2
     flops = half * 2 * wl.r + half * 2 * wl.d_v + 4 * wl.r * wl.d_v
     if wl.fmap == "favor":
@@ -127,7 +129,7 @@ def time_steps(fn, n_sets, steps, warmup, stream):
 def bench_forward(wl, steps, warmup):
     import kernelized_sequence_mixing_amd as ksm
     inp = make_inputs(wl, seed=0)
-    keys = ["Q", "K", "V", "g", "gamma", "omega"]
+    keys = ["Q", "K", "V", "g", "gv", "gamma", "omega"]
     nb_tok, fl_tok = algorithmic_per_token(wl)
     per_set = wl.head_tokens * nb_tok
     sets = _device_sets(inp, keys, per_set)
@@ -136,6 +138,7 @@ def bench_forward(wl, steps, warmup):
         "decay": lambda s: ("decay", s["gamma"]),
         "gla": lambda s: ("gla", s["g"], wl.tau),
         "sel": lambda s: ("sel", s["g"], wl.tau),
+        "outer": lambda s: ("outer", s["g"], s["gv"], wl.tau),
     }[wl.gate]
     outs = [torch.empty((wl.B, wl.H, wl.n, wl.d_v), dtype=sets[0]["V"].dtype, device="cuda") for _ in sets]
     nws = ksm.workspace_size(wl.B, wl.H, wl.n, wl.d_k, wl.d_v, fmap=wl.fmap, r=wl.r, causal=wl.causal,
@@ -388,7 +391,8 @@ def main():
     }
     if not args.no_extra:
         extra = []
-        for name in ("noncausal_elu1_f32", "retnet_decay", "gla_gate", "ssm_selective", "ssm_scalar", "favor_causal"):
+        for name in ("noncausal_elu1_f32", "retnet_decay", "gla_gate", "outer_gate", "ssm_selective", "ssm_scalar",
+                     "favor_causal"):
             extra.append(bench_forward(WORKLOADS[name], args.steps, args.warmup))
         extra.append(bench_decode(WORKLOADS["gla_decode"], args.steps, args.warmup))
         extra.append(bench_serve_prefill(args.steps, args.warmup))

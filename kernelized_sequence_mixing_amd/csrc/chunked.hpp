@@ -187,7 +187,9 @@ struct FwdLayout {
   // 16-byte reads of 16 rows spread over the banks), e^{c_end} per column
   static constexpr int ec_off = bs_off + (GATE == GT_SEL ? kChunk * 4 : 0);
   static constexpr int gamv_off = ec_off + (GATE == GT_OUTER ? kChunk * (E + 4) * 4 : 0);
-  static constexpr int bytes = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
+  // outer-product gate: the low bf16 half of V~ (V~ = hi + lo, hi in the v tile)
+  static constexpr int vl_off = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
+  static constexpr int bytes = vl_off + (GATE == GT_OUTER ? FeatTile<E, SWZ>::BYTES : 0);
 };
 
 // Pass 1: one chunk (K^ rows, V rows, gate factors) per half, then the
@@ -202,7 +204,8 @@ struct SegLayout {
   static constexpr int v_off = k_off + FeatTile<R, SWZ>::BYTES;
   static constexpr int gam_off = v_off + FeatTile<E, SWZ>::BYTES;
   static constexpr int gamv_off = gam_off + R * 4;  // outer-product gate: [E] e^{c_end}
-  static constexpr int HALF = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
+  static constexpr int vl_off = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);  // outer-product gate: lo half of V~
+  static constexpr int HALF = vl_off + (GATE == GT_OUTER ? FeatTile<E, SWZ>::BYTES : 0);
   static constexpr int logg_off = (PIPELINED ? 2 : 1) * HALF;
   static constexpr int loggv_off = logg_off + R * 4;  // outer-product gate: [E] summed value-side log-gates
   static constexpr int bs_off = loggv_off + (GATE == GT_OUTER ? E * 4 : 0);  // selective gate: [64] cumulative log-gate
@@ -343,7 +346,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
                                               const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
                                               int k_off, int kh_off, int v_off, int gam_off, int logg_off,
                                               int lane, int w, int qd_off = 0, int kd_off = 0, int bs_off = 0,
-                                              int ec_off = 0, int gamv_off = 0, int loggv_off = 0) {
+                                              int ec_off = 0, int gamv_off = 0, int loggv_off = 0, int vl_off = 0) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
   constexpr int LPT = Raw::LPT;
   using FT = FeatTile<R, SWZ>;
@@ -445,7 +448,8 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
   }
   // values (rows past the end are zero). The outer-product gate's value side:
   // c, the chunk's inclusive cumulative log-gate per value column (lane =
-  // token), gives V~ = e^{-c} v in the tile; WITH_Q also writes e^{c} (the
+  // token), gives V~ = e^{-c} v as a hi + lo bf16 pair (v tile and vl tile:
+  // unlike v, V~ is not exact in bf16); WITH_Q also writes e^{c} (the
   // outputs' factor), and every pass e^{c_end} per column (the state's
   // column factor; pass 1 adds c_end to the segment's summed log-gates).
   {
@@ -464,8 +468,13 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
           ecs[u] = __expf(c);
           my_cend = lane == 8 * j + u ? cend : my_cend;
         }
-        lds<bf16x8>(sm, v_off + VT::at(lane, w * EV / 8 + j)) =
-            keep_if(valid, cat8(pack4(vs[0], vs[1], vs[2], vs[3]), pack4(vs[4], vs[5], vs[6], vs[7])));
+        const bf16x8 hi = cat8(pack4(vs[0], vs[1], vs[2], vs[3]), pack4(vs[4], vs[5], vs[6], vs[7]));
+        float lo[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) lo[u] = vs[u] - to_f32(hi[u]);
+        lds<bf16x8>(sm, v_off + VT::at(lane, w * EV / 8 + j)) = keep_if(valid, hi);
+        lds<bf16x8>(sm, vl_off + VT::at(lane, w * EV / 8 + j)) =
+            keep_if(valid, cat8(pack4(lo[0], lo[1], lo[2], lo[3]), pack4(lo[4], lo[5], lo[6], lo[7])));
         if constexpr (WITH_Q) {
           const int eo = ec_off + 4 * (lane * (E + 4) + w * EV + 8 * j);
           lds<f32x4>(sm, eo) = f32x4{ecs[0], ecs[1], ecs[2], ecs[3]};
@@ -522,7 +531,8 @@ struct ZTiles {
 // state needs.
 template <int R, int E, int GATE, int NW, bool SWZ, bool ZW = false, bool PRE = false, class SArr, class ZArr>
 __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_off, int v_off, int gam_off,
-                                             float gscale, int lane, int w, int zw_off = 0, int gamv_off = 0) {
+                                             float gscale, int lane, int w, int zw_off = 0, int gamv_off = 0,
+                                             int vl_off = 0) {
   constexpr int ZT = ZTiles<R, NW>::ZT, NEB = E / (16 * NW);
   const int g4 = lane >> 4;
   const int ebase = w * (E / NW);
@@ -534,6 +544,13 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
   for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_feat<E, SWZ>(sm, v_off, 32 * ks, ebase + 16 * eb, lane);
+  bf16x8 vbl[GATE == GT_OUTER ? NEB : 1][2];  // the outer-product gate: lo half of V~
+  if constexpr (GATE == GT_OUTER) {
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) vbl[eb][ks] = tr_feat<E, SWZ>(sm, vl_off, 32 * ks, ebase + 16 * eb, lane);
+  }
 #pragma unroll
   for (int rt = 0; rt < R / 16; ++rt) {
     bf16x8 ka[2];
@@ -553,6 +570,10 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vb[eb][ks], st);
+      if constexpr (GATE == GT_OUTER) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vbl[eb][ks], st);
+      }
       if constexpr (kKeyGate<GATE> && !PRE) {
         // the outer-product gate: also the column's value-side factor
         float gc = 1.f;
@@ -672,14 +693,16 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
     chunk_prelude<R, E, DK, FMAP, GATE, false, NW, LY::SWZ>(rw, a, L, lg2gam, sm, 0, half * LY::HALF + LY::k_off, 0,
                                                    half * LY::HALF + LY::v_off, half * LY::HALF + LY::gam_off,
                                                    LY::logg_off, lane, w, 0, 0, LY::bs_off, 0,
-                                                   half * LY::HALF + LY::gamv_off, LY::loggv_off);
+                                                   half * LY::HALF + LY::gamv_off, LY::loggv_off,
+                                                   half * LY::HALF + LY::vl_off);
   };
   auto update = [&](int ci, int half) {
     const int L = min(kChunk, sv.len - (t_begin + ci * kChunk));
     float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
     if constexpr (GATE == GT_SEL) gsc = __expf(lds<float>(sm, LY::bs_off + 4 * 63));
     state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, half * LY::HALF + LY::k_off, half * LY::HALF + LY::v_off,
-                                 half * LY::HALF + LY::gam_off, gsc, lane, w, 0, half * LY::HALF + LY::gamv_off);
+                                 half * LY::HALF + LY::gam_off, gsc, lane, w, 0, half * LY::HALF + LY::gamv_off,
+                                 half * LY::HALF + LY::vl_off);
   };
   if constexpr (LY::PIPELINED) {
     // while the state update of chunk ci reads half ci & 1, the prelude of
@@ -806,7 +829,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
     if (live)
       chunk_prelude<R, E, DK, FMAP, GATE, true, NW, LY::SWZ>(raw, a, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off,
                                                     LY::v_off, LY::gam_off, 0, lane, w, 0, 0, LY::bs_off,
-                                                    LY::ec_off, LY::gamv_off);
+                                                    LY::ec_off, LY::gamv_off, 0, LY::vl_off);
     // the raw registers are free again: this refill flies during the next DEPTH chunks
     raw.load(a, tok0, t0 + DEPTH * kChunk, t_end, lane, w);
     if (!live) return;
@@ -904,9 +927,11 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
           for (int i = 0; i < 4; ++i) acc[i] *= isc;
         }
 #pragma unroll
-        for (int p2 = 0; p2 <= qt / 2; ++p2)
-          acc = mfma16(tr_feat<E, LY::SWZ>(sm, LY::v_off, 32 * p2, e, lane),
-                       lds<bf16x8>(sm, LY::a_off + AT::at(q, 4 * p2 + g4)), acc);
+        for (int p2 = 0; p2 <= qt / 2; ++p2) {
+          const bf16x8 ab = lds<bf16x8>(sm, LY::a_off + AT::at(q, 4 * p2 + g4));
+          acc = mfma16(tr_feat<E, LY::SWZ>(sm, LY::v_off, 32 * p2, e, lane), ab, acc);
+          if constexpr (GATE == GT_OUTER) acc = mfma16(tr_feat<E, LY::SWZ>(sm, LY::vl_off, 32 * p2, e, lane), ab, acc);
+        }
         if constexpr (GATE == GT_OUTER) {
           // both parts carry e^{-c} of the chunk start on the value side
           const f32x4 ec = lds<f32x4>(sm, LY::ec_off + 4 * (q * (E + 4) + e + 4 * g4));
@@ -924,7 +949,7 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
     float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
     if constexpr (GATE == GT_SEL) gsc = __expf(lds<float>(sm, LY::bs_off + 4 * 63));
     state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, kScalarDecay<GATE> ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
-                                 gsc, lane, w, 0, LY::gamv_off);
+                                 gsc, lane, w, 0, LY::gamv_off, LY::vl_off);
     z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
     lds_barrier();
   };

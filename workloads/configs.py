@@ -53,6 +53,11 @@ WORKLOADS = {
     "gla_gate": Workload(
         "gla_gate", B=2, H=16, n=16384, d_k=128, d_v=128, r=128, fmap="elu1",
         causal=True, gate="gla", dtype="bf16", qk_scale=128 ** -0.5, v_scale=128 ** -0.5),
+    # the GLA workload's shape under the outer-product gate (value-side gate input gv
+    # ~ N(0,1) per value column, same tau)
+    "outer_gate": Workload(
+        "outer_gate", B=2, H=16, n=16384, d_k=128, d_v=128, r=128, fmap="elu1",
+        causal=True, gate="outer", dtype="bf16", qk_scale=128 ** -0.5, v_scale=128 ** -0.5),
     "gla_decode": Workload(
         "gla_decode", B=256, H=16, n=1, d_k=128, d_v=128, r=128, fmap="elu1",
         causal=True, gate="gla", dtype="bf16", qk_scale=128 ** -0.5, v_scale=128 ** -0.5,
