@@ -139,3 +139,16 @@ def test_outer_gate_serving_batch():
         check_close(o1[:, :, off:off + L], o[:, :, :L], TOL_BF16, f"outer batch prefill seq {b}")
         check_close(o2[b:b + 1], o[:, :, L:], TOL_BF16, f"outer batch step seq {b}")
         off += L
+
+
+def test_outer_gate_full_size_sampled_heads():
+    """The benchmark's outer-gate shape (B2 H16 n16384 d128, several segments),
+    two heads against the oracle's recurrence."""
+    wl = WORKLOADS["outer_gate"]
+    inp = make_inputs(wl, seed=0)
+    out = run_forward(inp)
+    assert torch.isfinite(out.float()).all()
+    for head in [(0, 0), (wl.B - 1, wl.H - 1)]:
+        ref, _, _ = oracle_forward(inp, head=head)
+        b, h = head
+        check_close(out[b:b + 1, h:h + 1], ref, TOL_BF16, f"outer full size head {head}")
