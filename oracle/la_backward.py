@@ -26,7 +26,8 @@ import numpy as np
 
 from .la_oracle import feature_map, normalised
 
-__all__ = ["feature_map_vjp", "forward_terms", "backward", "backward_gla", "backward_sel"]
+__all__ = ["feature_map_vjp", "forward_terms", "backward", "backward_gla", "backward_sel", "backward_gla_rows",
+           "backward_sel_rows"]
 
 
 def _f64(a):
@@ -222,3 +223,86 @@ def backward_sel(Q, K, V, dO, g, tau, fmap="elu1", omega=None, eps=1e-6, S0=None
     G = np.repeat(g[..., None], r, axis=-1)
     dQ, dK, dV, dG = backward_gla(Q, K, V, dO, G, tau, fmap, omega, eps, S0, z0)
     return dQ, dK, dV, dG.sum(axis=-1)
+
+
+def backward_gla_rows(Q, K, V, dO, g, tau, fmap="elu1", eps=1e-6, rows=(), tail=0, return_forward=False):
+    """Sampled entries of ``backward_gla`` for ONE head at any sequence length.
+
+    Q, K [n, d_k]; V, dO [n, d_v]; g [n, r] (no carried state). Returns
+    (dQ[rows], dK[rows], dV[rows], dg[n - tail:]). ``backward_gla`` holds an
+    [n, n, r] decay tensor; here each sampled row sums over its own partners
+    with the decays of that row only, so memory is O(n r):
+      forward: z_t = alpha_t * z_{t-1} + phi(k_t), S_t = diag(alpha_t) S_{t-1}
+               + phi(k_t) v_t^T (the recurrence of "Gating and Selective State
+               Updates", dileepadev page), den_t = phi(q_t).z_t + eps, o_t;
+      g_t = dO_t / den_t, h_t = -(dO_t . o_t) / den_t (state-space: dO_t, 0);
+      key row j:   D_ij = exp(B_i - B_j) for i >= j, W_ij = sum_k phi(q_i)_k
+                   phi(k_j)_k D_ijk, dV_j = sum_i W_ij g_i, dphi(k_j) =
+                   sum_i (g_i . v_j + h_i) phi(q_i) D_ij;
+      query row i: dphi(q_i) = sum_{j <= i} (g_i . v_j + h_i) phi(k_j) D_ij;
+      tail u:      d log alpha_u = sum_{t >= u} (dphi(q_t) phi(q_t) -
+                   dphi(k_t) phi(k_t)), dg_u = d log alpha_u sigmoid(-g_u) / tau;
+    then the feature map's vjp, as in ``backward_gla``. With return_forward,
+    also (den, o) of every token.
+    """
+    Q, K, V, dO, g = (_f64(x) for x in (Q, K, V, dO, g))
+    pq = feature_map(Q, fmap)
+    pk = feature_map(K, fmap)
+    n, r = pq.shape
+    dv = V.shape[1]
+    with np.errstate(over="ignore"):
+        la = -np.logaddexp(0.0, -g) / float(tau)
+    Bc = np.cumsum(la, axis=0)
+    al = np.exp(la)
+    S = np.zeros((r, dv))
+    z = np.zeros(r)
+    o = np.empty((n, dv))
+    den = np.ones(n)
+    norm = normalised(fmap)
+    for t in range(n):
+        S = al[t][:, None] * S + np.outer(pk[t], V[t])
+        z = al[t] * z + pk[t]
+        o[t] = pq[t] @ S
+        if norm:
+            den[t] = pq[t] @ z + eps
+            o[t] /= den[t]
+    gg = dO / den[:, None]
+    h = -np.sum(dO * o, axis=1) / den if norm else np.zeros(n)
+
+    def dphi_k(j):
+        D = np.exp(Bc[j:] - Bc[j])                       # [n - j, r], i >= j
+        dW = gg[j:] @ V[j] + h[j:]
+        W = (pq[j:] * D) @ pk[j]
+        return (dW[:, None] * pq[j:] * D).sum(axis=0), W @ gg[j:]
+
+    def dphi_q(i):
+        D = np.exp(Bc[i] - Bc[:i + 1])                   # [i + 1, r], j <= i
+        dW = V[:i + 1] @ gg[i] + h[i]
+        return (dW[:, None] * pk[:i + 1] * D).sum(axis=0)
+
+    rows = list(rows)
+    dQ = np.array([feature_map_vjp(Q[i], dphi_q(i), fmap) for i in rows]).reshape(len(rows), -1)
+    dK, dV = [], []
+    for j in rows:
+        dpk, dvj = dphi_k(j)
+        dK.append(feature_map_vjp(K[j], dpk, fmap))
+        dV.append(dvj)
+    dK = np.array(dK).reshape(len(rows), -1)
+    dV = np.array(dV).reshape(len(rows), dv)
+    dB = np.array([dphi_q(t) * pq[t] - dphi_k(t)[0] * pk[t] for t in range(n - tail, n)]).reshape(tail, r)
+    dlog = np.flip(np.cumsum(np.flip(dB, axis=0), axis=0), axis=0)
+    with np.errstate(over="ignore"):
+        dg = dlog / (1.0 + np.exp(g[n - tail:])) / float(tau)
+    if return_forward:
+        return dQ, dK, dV, dg, den, o
+    return dQ, dK, dV, dg
+
+
+def backward_sel_rows(Q, K, V, dO, g, tau, fmap="elu1", eps=1e-6, rows=(), tail=0):
+    """``backward_gla_rows`` for the selective scalar gate (g [n]): the GLA
+    form with g repeated over the features, dg summed over them (as in
+    ``backward_sel``)."""
+    g = _f64(g)
+    r = feature_map(_f64(Q)[:1], fmap).shape[-1]
+    dQ, dK, dV, dG = backward_gla_rows(Q, K, V, dO, np.repeat(g[:, None], r, axis=1), tau, fmap, eps, rows, tail)
+    return dQ, dK, dV, dG.sum(axis=1)

@@ -222,3 +222,39 @@ def test_sel_single_step_gate_gradient_closed_form():
     got = bwd.backward_sel(sh(q[None]), sh(k[None]), sh(v[None]), sh(dO[None]), np.array([[[gv]]]), tau, "elu1",
                            None, eps, sh(S0), sh(z0))[3]
     assert abs(float(got[0, 0, 0]) - want) <= 1e-12 * max(1.0, abs(want))
+
+
+@pytest.mark.parametrize("fmap", ["elu1", "identity"])
+def test_gla_sampled_rows_equal_the_explicit_form(fmap):
+    """backward_gla_rows (per-row sums, O(n r) memory, for full-length
+    sequences) equals backward_gla (the explicit [n, n, r] form) at every row
+    and every tail step."""
+    n, d, e, tau = 23, 4, 3, 5.0
+    Q = RNG.standard_normal((n, d)) * 0.7
+    K = RNG.standard_normal((n, d)) * 0.7
+    V = RNG.standard_normal((n, e))
+    G = RNG.standard_normal((n, d))
+    dO = RNG.standard_normal((n, e))
+    sh = lambda x: x[None, None]
+    want = bwd.backward_gla(sh(Q), sh(K), sh(V), sh(dO), sh(G), tau, fmap, None, 1e-3)
+    rows = [0, 1, 7, n - 1]
+    got = bwd.backward_gla_rows(Q, K, V, dO, G, tau, fmap, 1e-3, rows=rows, tail=n)
+    for a, b in zip(got[:3], want[:3]):
+        np.testing.assert_allclose(a, b[0, 0][rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got[3], want[3][0, 0], rtol=1e-10, atol=1e-12)
+
+
+def test_sel_sampled_rows_equal_the_explicit_form():
+    n, d, e, tau = 19, 4, 3, 3.0
+    Q = RNG.standard_normal((n, d)) * 0.7
+    K = RNG.standard_normal((n, d)) * 0.7
+    V = RNG.standard_normal((n, e))
+    G = RNG.standard_normal(n)
+    dO = RNG.standard_normal((n, e))
+    sh = lambda x: x[None, None]
+    want = bwd.backward_sel(sh(Q), sh(K), sh(V), sh(dO), sh(G), tau, "elu1", None, 1e-3)
+    rows = [0, 5, n - 1]
+    got = bwd.backward_sel_rows(Q, K, V, dO, G, tau, "elu1", 1e-3, rows=rows, tail=n)
+    for a, b in zip(got[:3], want[:3]):
+        np.testing.assert_allclose(a, b[0, 0][rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got[3], want[3][0, 0], rtol=1e-10, atol=1e-12)
