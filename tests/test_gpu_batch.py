@@ -229,3 +229,61 @@ def test_prefill_then_multi_token_decode(gate):
         sl = int(ids[b])
         _close_state(S[sl:sl + 1].cpu(), z[sl:sl + 1].cpu(), Sr, zr, f"{gate} seq {b} final")
         off += L
+
+
+# ------------------------------------------------ the benchmark's serving configurations
+
+def test_serving_prefill_bench_config_sampled():
+    """The ragged prefill bench.py times (32 sequences, seeded log-uniform
+    lengths 64 .. 8192, H16 d64 elu+1, states into slots): the shortest, the
+    longest and the last sequence on two heads against the oracle, with their
+    stored states."""
+    import kernelized_sequence_mixing_amd as ksm
+    from workloads import serving_lengths
+    lens = serving_lengths(32, seed=7)
+    T, H = int(lens.sum()), 16
+    wl = WORKLOADS["causal_elu1"].resized(name="serve_prefill", B=1, H=H, n=T, d_k=64, d_v=64, r=64)
+    inp = make_inputs(wl, seed=0)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    S = torch.zeros((32, H, 64, 64), dtype=torch.float32, device="cuda")
+    z = torch.zeros((32, H, 64), dtype=torch.float32, device="cuda")
+    out = ksm.forward_batch(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), cu_seqlens=torch.from_numpy(cu).cuda(),
+                            max_seqlen=int(lens.max()), state=(S, z),
+                            slot_ids=torch.arange(32, dtype=torch.int32, device="cuda"), write=True,
+                            eps=wl.eps).cpu()
+    torch.cuda.synchronize()
+    Sc, zc = S.cpu(), z.cpu()
+    for b in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 31}):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        for h in (0, H - 1):
+            Q, K, V = (to_f64(inp[k])[:, h:h + 1, lo:hi] for k in ("Q", "K", "V"))
+            o, Sr, zr = orc.causal_recurrent(Q, K, V, "elu1", None, None, eps=wl.eps)
+            check_close(out[:, h:h + 1, lo:hi], o, TOL_BF16, f"serve prefill seq {b} (len {hi - lo}) head {h}")
+            assert np.max(np.abs(to_f64(Sc[b, h]) - Sr[0, 0])) / np.max(np.abs(Sr)) < 1e-2
+            assert np.max(np.abs(to_f64(zc[b, h]) - zr[0, 0]) / zr[0, 0]) < 1e-2
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_serving_decode_bench_config_sampled(m):
+    """The decode steps bench.py times (B256 H16, 128 x 128 GLA states read
+    and written in their slots, m tokens per sequence): sampled sequences on
+    every head against the oracle's steps from the same states."""
+    import kernelized_sequence_mixing_amd as ksm
+    dwl = WORKLOADS["gla_decode"]
+    B, H = dwl.B, dwl.H
+    base = WORKLOADS["gla_gate"].resized(B=B, H=H, n=m)
+    inp = make_inputs(base, seed=0)
+    dec = make_inputs(dwl, seed=0)
+    S, z = dev(dec["S0"]), dev(dec["z0"])
+    out = ksm.forward_batch(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), state=(S, z),
+                            slot_ids=torch.arange(B, dtype=torch.int32, device="cuda"), read=True, write=True,
+                            gate=("gla", dev(inp["g"]), dwl.tau), eps=dwl.eps).cpu()
+    torch.cuda.synchronize()
+    Sc = S.cpu()
+    for b in (0, 97, B - 1):
+        sl = lambda x: to_f64(x)[b:b + 1]
+        o, Sr, _ = orc.causal_recurrent(sl(inp["Q"]), sl(inp["K"]), sl(inp["V"]), "elu1", None,
+                                        ("gla", sl(inp["g"]), dwl.tau), eps=dwl.eps, S0=sl(dec["S0"]),
+                                        z0=sl(dec["z0"]))
+        check_close(out[b:b + 1], o, TOL_BF16, f"serve decode m{m} seq {b}")
+        assert np.max(np.abs(to_f64(Sc[b]) - Sr[0])) / np.max(np.abs(Sr)) < 1e-2

@@ -108,10 +108,11 @@ def test_ssm_resumes_from_state(gate):
     assert np.max(np.abs(to_f64(S) - Sr)) / (np.max(np.abs(Sr)) + 1e-30) < 2e-2
 
 
-def test_ssm_full_size_sampled_heads():
-    """The benchmark's shape (B2 H16 n16384 d64, GLA gate, several segments),
-    two heads against the oracle's recurrence."""
-    wl = WORKLOADS["ssm_selective"]
+@pytest.mark.parametrize("name", ["ssm_selective", "ssm_scalar"])
+def test_ssm_full_size_sampled_heads(name):
+    """The benchmark's shapes (B2 H16 n16384 d64 under the GLA and the
+    selective gate, several segments), two heads against the oracle's recurrence."""
+    wl = WORKLOADS[name]
     inp = make_inputs(wl, seed=0)
     got = run(inp)
     assert torch.isfinite(got.float()).all()
@@ -119,7 +120,7 @@ def test_ssm_full_size_sampled_heads():
         o, sc, _, _ = oracle_ssm(inp, head=head)
         b, h = head
         e = term_err(got[b:b + 1, h:h + 1], o, sc)
-        print(f"  ssm full size head {head}: term-relative err {e:.2e}", flush=True)
+        print(f"  {name} full size head {head}: term-relative err {e:.2e}", flush=True)
         assert e < TOL_TERMS
 
 
