@@ -152,3 +152,11 @@ def test_outer_gate_full_size_sampled_heads():
         ref, _, _ = oracle_forward(inp, head=head)
         b, h = head
         check_close(out[b:b + 1, h:h + 1], ref, TOL_BF16, f"outer full size head {head}")
+
+
+def test_outer_gate_deterministic():
+    wl, inp = _elu_case(64, 64, 4, 16, 1285, seed=8)
+    a = run_forward(inp, return_state=True)
+    b = run_forward(inp, return_state=True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -109,7 +109,7 @@ def test_causal_workload_full_size(name):
 
 # ------------------------------------------------------------------ exact structure (bit-exact)
 
-@pytest.mark.parametrize("name", ["causal_elu1", "retnet_decay", "gla_gate", "favor_causal"])
+@pytest.mark.parametrize("name", ["causal_elu1", "retnet_decay", "gla_gate", "favor_causal", "outer_gate"])
 def test_exact_zero_probe(name):
     """V = 0 except a single 1 at (p, c): every output before p is exactly
     0.0, no other column is ever nonzero, and o_p[c] > 0. Sweeps p over chunk
