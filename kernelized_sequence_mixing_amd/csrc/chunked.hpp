@@ -415,11 +415,12 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         float pq = WITH_Q ? phi_ew<FMAP>(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
         float pk = phi_ew<FMAP>(to_f32(raw.k[j][u]));
         if constexpr (kKeyGate<GATE>) {
-          float la = keep_if(valid, gla_log_alpha(to_f32(raw.g[j][u]), a.inv_tau));
+          // base 2: b is the chunk's inclusive cumulative log2-gate
+          float la = keep_if(valid, gla_log2_alpha(to_f32(raw.g[j][u]), a.inv_tau));
           float b = wave_inclusive_scan(la);
           // the chunk total is uniform across the wave: a scalar read of lane 63
           const float bend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
-          const float eb = __expf(b), emb = __expf((EXTRA & kPreKPos) != 0 ? b : -b);
+          const float eb = __builtin_amdgcn_exp2f(b), emb = __builtin_amdgcn_exp2f((EXTRA & kPreKPos) != 0 ? b : -b);
           if constexpr ((EXTRA & kPreQD) != 0) dq[u] = eb * phi_ew_deriv<FMAP>(pq);
           if constexpr ((EXTRA & kPreKD) != 0) dk[u] = emb * phi_ew_deriv<FMAP>(pk);
           pq *= eb;
@@ -441,14 +442,15 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
     }
     if constexpr (kKeyGate<GATE>) {
       if (lane < Raw::FR) {
-        lds<float>(sm, gam_off + 4 * (w * Raw::FR + lane)) = __expf(my_bend);
-        if constexpr (!WITH_Q || (EXTRA & kPreLogG) != 0) lds<float>(sm, logg_off + 4 * (w * Raw::FR + lane)) += my_bend;
+        lds<float>(sm, gam_off + 4 * (w * Raw::FR + lane)) = __builtin_amdgcn_exp2f(my_bend);
+        if constexpr (!WITH_Q || (EXTRA & kPreLogG) != 0)
+          lds<float>(sm, logg_off + 4 * (w * Raw::FR + lane)) += my_bend * kLn2;  // natural log for the scan
       }
     }
   }
   // values (rows past the end are zero). The outer-product gate's value side:
   // c, the chunk's inclusive cumulative log-gate per value column (lane =
-  // token), gives V~ = e^{-c} v as a hi + lo bf16 pair (v tile and vl tile:
+  // token; scanned in base 2 like the key side), gives V~ = e^{-c} v as a hi + lo bf16 pair (v tile and vl tile:
   // unlike v, V~ is not exact in bf16); WITH_Q also writes e^{c} (the
   // outputs' factor), and every pass e^{c_end} per column (the state's
   // column factor; pass 1 adds c_end to the segment's summed log-gates).
@@ -461,11 +463,11 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         float vs[8], ecs[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float la = keep_if(valid, gla_log_alpha(to_f32(raw.gv[j][u]), a.inv_tau));
+          const float la = keep_if(valid, gla_log2_alpha(to_f32(raw.gv[j][u]), a.inv_tau));  // base 2
           const float c = wave_inclusive_scan(la);
           const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
-          vs[u] = to_f32(raw.v[j][u]) * __expf(-c);
-          ecs[u] = __expf(c);
+          vs[u] = to_f32(raw.v[j][u]) * __builtin_amdgcn_exp2f(-c);
+          ecs[u] = __builtin_amdgcn_exp2f(c);
           my_cend = lane == 8 * j + u ? cend : my_cend;
         }
         const bf16x8 hi = cat8(pack4(vs[0], vs[1], vs[2], vs[3]), pack4(vs[4], vs[5], vs[6], vs[7]));
@@ -486,8 +488,8 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
     }
     if constexpr (GATE == GT_OUTER) {
       if (lane < EV) {
-        lds<float>(sm, gamv_off + 4 * (w * EV + lane)) = __expf(my_cend);
-        if constexpr (!WITH_Q) lds<float>(sm, loggv_off + 4 * (w * EV + lane)) += my_cend;
+        lds<float>(sm, gamv_off + 4 * (w * EV + lane)) = __builtin_amdgcn_exp2f(my_cend);
+        if constexpr (!WITH_Q) lds<float>(sm, loggv_off + 4 * (w * EV + lane)) += my_cend * kLn2;
       }
     }
   }

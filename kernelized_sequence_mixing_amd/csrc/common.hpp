@@ -125,4 +125,15 @@ __device__ __forceinline__ float gla_log_alpha(float g, float inv_tau) {
   return -sp * inv_tau;
 }
 
+// The same quantity in base 2, log2(alpha) = -softplus(-g) / (tau ln 2), with
+// softplus / ln 2 = max(y, 0) + log2(1 + 2^-|y|) for y = -g log2(e): the chunk
+// preludes scan it and exponentiate with the hardware's base-2 exp directly.
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
+__device__ __forceinline__ float gla_log2_alpha(float g, float inv_tau) {
+  const float y = -g * kLog2e;
+  const float sp2 = fmaxf(y, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(y)));
+  return -sp2 * inv_tau;
+}
+
 }  // namespace la
