@@ -410,14 +410,19 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
     for (int j = 0; j < Raw::FR / 8; ++j) {
       const int f0 = w * Raw::FR + 8 * j;
       float vq[8], vk[8], dq[8], dk[8];
+      // base 2: bs[u] is the chunk's inclusive cumulative log2-gate of feature f0 + u
+      float bs[8];
+      if constexpr (kKeyGate<GATE>) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) bs[u] = keep_if(valid, gla_log2_alpha(to_f32(raw.g[j][u]), a.inv_tau));
+        wave_inclusive_scan_n(bs);
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         float pq = WITH_Q ? phi_ew<FMAP>(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
         float pk = phi_ew<FMAP>(to_f32(raw.k[j][u]));
         if constexpr (kKeyGate<GATE>) {
-          // base 2: b is the chunk's inclusive cumulative log2-gate
-          float la = keep_if(valid, gla_log2_alpha(to_f32(raw.g[j][u]), a.inv_tau));
-          float b = wave_inclusive_scan(la);
+          const float b = bs[u];
           // the chunk total is uniform across the wave: a scalar read of lane 63
           const float bend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
           const float eb = __builtin_amdgcn_exp2f(b), emb = __builtin_amdgcn_exp2f((EXTRA & kPreKPos) != 0 ? b : -b);
@@ -460,11 +465,13 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
 #pragma unroll
     for (int j = 0; j < EV / 8; ++j) {
       if constexpr (GATE == GT_OUTER) {
-        float vs[8], ecs[8];
+        float vs[8], ecs[8], cs[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cs[u] = keep_if(valid, gla_log2_alpha(to_f32(raw.gv[j][u]), a.inv_tau));  // base 2
+        wave_inclusive_scan_n(cs);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float la = keep_if(valid, gla_log2_alpha(to_f32(raw.gv[j][u]), a.inv_tau));  // base 2
-          const float c = wave_inclusive_scan(la);
+          const float c = cs[u];
           const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
           vs[u] = to_f32(raw.v[j][u]) * __builtin_amdgcn_exp2f(-c);
           ecs[u] = __builtin_amdgcn_exp2f(c);

@@ -88,6 +88,28 @@ __device__ __forceinline__ float dpp_or_zero(float x) {
 // Hillis-Steele within each row of 16 lanes (row_shr 1, 2, 4, 8), then the row
 // totals are carried with the row broadcasts of lane 15 (into rows 1, 3) and
 // lane 31 (into rows 2, 3).
+template <int CTRL, int ROW_MASK, int N>
+__device__ __forceinline__ void scan_step(float (&x)[N]) {
+  float t[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) t[u] = dpp_or_zero<CTRL, ROW_MASK>(x[u]);
+#pragma unroll
+  for (int u = 0; u < N; ++u) x[u] += t[u];
+}
+
+// N independent scans of wave_inclusive_scan, taken step by step across the
+// N values, so that no DPP read of a register follows right after its write
+// (a back-to-back chain needs wait states between the two).
+template <int N>
+__device__ __forceinline__ void wave_inclusive_scan_n(float (&x)[N]) {
+  scan_step<0x111, 0xf>(x);
+  scan_step<0x112, 0xf>(x);
+  scan_step<0x114, 0xf>(x);
+  scan_step<0x118, 0xf>(x);
+  scan_step<0x142, 0xa>(x);
+  scan_step<0x143, 0xc>(x);
+}
+
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
   x += dpp_or_zero<0x111, 0xf>(x);
   x += dpp_or_zero<0x112, 0xf>(x);
