@@ -126,9 +126,13 @@ typedef struct la_gate {
   const float* gamma; /* DECAY: device [H] fp32, each in (0, 1] -- a documented
                          precondition, not checked (the values live on the device) */
   const void* g;      /* GLA, OUTER: device [B][H][n][r] in in_dtype (decode: [B][H][r]);
-                         SEL: [B][H][n] (decode: [B][H]) */
-  const void* gv;     /* OUTER: device [B][H][n][d_v] in in_dtype (decode: [B][H][d_v]);
-                         must be NULL for every other gate (else LA_ERR_INVALID_ARG) */
+                         SEL: [B][H][n] (decode: [B][H]). Precondition of the causal
+                         kernels for GLA and OUTER, not checked: over any 64 aligned
+                         tokens the summed log alpha of each feature stays above -80
+                         (the factors e^{+-b} are referenced to the chunk start) */
+  const void* gv;     /* OUTER: device [B][H][n][d_v] in in_dtype (decode: [B][H][d_v]),
+                         with the same precondition per value column; must be NULL
+                         for every other gate (else LA_ERR_INVALID_ARG) */
 } la_gate;
 
 /* Flags of la_batch.flags. */
