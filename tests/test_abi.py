@@ -116,6 +116,11 @@ def test_workspace_sizes():
     gla = workspace_size(2, 16, 16384, 128, 128, gate_kind="gla")
     plain = workspace_size(2, 16, 16384, 128, 128)
     assert gla == plain + 32 * 8 * 128 * 4  # 8 segments: one summed log-gate row per (head, segment)
+    # the outer-product gate adds one summed value-side log-gate row (d_v) per (head, segment)
+    from kernelized_sequence_mixing_amd import segments
+    P, _ = segments(2, 16, 16384, 128, 128, gate_kind="outer")
+    outer = workspace_size(2, 16, 16384, 128, 128, gate_kind="outer")
+    assert outer == 32 * P * (128 * 128 + 128 + 128 + 128) * 4
     # non-causal partial sums always need workspace
     assert workspace_size(1, 1, 256, 32, 32, causal=False, dtype=torch.float32) > 0
 
