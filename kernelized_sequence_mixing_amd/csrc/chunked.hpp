@@ -15,7 +15,11 @@
 // reads the carried state. For the per-feature GLA gate with chunk-local
 // cumulative log-gate b_t, Q~ = phi(Q) e^{b}, K~ = phi(K) e^{-b},
 // K^ = phi(K) e^{b_end - b} and Gamma = e^{b_end}; for RetNet the chunk-local
-// weights gamma^(i-j), gamma^(i+1) and gamma^(L-1-j) are applied directly.
+// weights gamma^(i-j), gamma^(i+1) and gamma^(L-1-j) are applied directly, and
+// the selective scalar gate applies e^{b_i - b_j} from its per-token b. The
+// outer-product gate adds the value side: V~ = V e^{-c} per value column, the
+// outputs times e^{c}, the state's columns times e^{c_end} (z keeps the key
+// side only).
 //
 // To fill 256 compute units with few heads, each head's sequence is split into
 // P segments of whole chunks: pass 1 computes each segment's own state
@@ -193,7 +197,7 @@ struct FwdLayout {
 };
 
 // Pass 1: one chunk (K^ rows, V rows, gate factors) per half, then the
-// segment's summed log-gates. With the GLA gate the pass is software-pipelined
+// segment's summed log-gates. With a per-feature gate (GLA, outer) the pass is software-pipelined
 // over two halves (measured: 6% faster there; the ungated and RetNet passes,
 // whose preludes are short, run 2-5% slower pipelined).
 template <int R, int E, int GATE>
@@ -532,6 +536,8 @@ struct ZTiles {
 //   no gate   S <- S + K~^T V                    z <- z + K~^T 1
 //   RetNet    S <- gamma^L S + K^^T V            (kh_off holds K^ rows)
 //   GLA       S <- Gamma (S + K~^T V)            Gamma = diag(e^{b_end}) from gam_off
+//   outer     S <- Gamma (S + K~^T V~) Gamma_v   Gamma_v = diag(e^{c_end}) from gamv_off,
+//             V~ as hi + lo (vl_off holds lo)
 // Both operands come from [token][column] tiles by transpose reads.
 // S is f32x4[R / 16][E / (16 NW)], Z is f32x4[ZTiles<R, NW>::ZT].
 // With ZW the z column uses per-token weights (fp32 [64] at zw_off) instead of
