@@ -262,7 +262,7 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
                                      int32_t causal, const la_gate* gate, size_t* bytes);
 
 /*
- * Gradients of the causal forward pass, for training with the parallel form
+ * Gradients of the forward pass, for training with the parallel form
  * ("Recurrent Reformulation", dileepadev page: trained in parallel, run as an
  * RNN). For a loss L with dL/dout = dO, writes dQ = dL/dQ, dK = dL/dK and
  * dV = dL/dV of la_forward(p, Q, K, V, fmap, 1, gate, S0, z0, ...):
@@ -290,7 +290,12 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  *   256-byte aligned (segment states of both directions, g and h per token;
  *   GLA and SEL: also dQ~ . Q~ per token and feature and per-segment summed
  *   log-gates; SEL: also g repeated over features and its per-feature dg).
- * Supported (else LA_ERR_UNSUPPORTED): causal == 1, ELU1 or IDENTITY (the
+ * causal == 0 (the non-causal form, "The linear attention trick", sadullah
+ * page: dphi(q_i) = S g_i + z h_i, dphi(k_j) = G v_j + hq, dv_j = G^T phi(k_j)
+ * with G = sum_i phi(q_i) g_i^T, hq = sum_i phi(q_i) h_i): ELU1, no gate, no
+ * S0/z0 (else LA_ERR_INVALID_ARG), in_dtype == out_dtype in {F32, BF16} with
+ * the gradients in that dtype, the forward's (d_k, d_v) set; fp32 arithmetic.
+ * Supported (else LA_ERR_UNSUPPORTED) for causal == 1: ELU1 or IDENTITY (the
  * state-space read-out: g_i = dO_i, h_i = 0, phi' = 1), gate NONE, DECAY, GLA
  * or SEL (not OUTER), (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
  * inputs, each other or the workspace (LA_ERR_ALIAS). Numerics as la_forward:

@@ -301,7 +301,7 @@ class PreparedForwardBatch:
         return self.out
 
 
-def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream):
+def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream, causal=True):
     """Validate and marshal one la_backward call: (ctypes arguments, keep-alive objects, gradients), the
     gradients being (dQ, dK, dV), plus dg with a gate input (GLA, selective)."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (dO, "dO")):
@@ -335,26 +335,28 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
         if t.shape != ref.shape or t.dtype != ref.dtype:
             raise ValueError(f"{nm} has the wrong shape or dtype")
     ws_bytes = ctypes.c_size_t(0)
-    N.check(N.lib().la_backward_workspace_size(ctypes.byref(p), ctypes.byref(f), 1, ctypes.byref(g),
+    N.check(N.lib().la_backward_workspace_size(ctypes.byref(p), ctypes.byref(f), int(bool(causal)), ctypes.byref(g),
                                                ctypes.byref(ws_bytes)), "la_backward_workspace_size")
     need = ws_bytes.value
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    args = (ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), ctypes.byref(f), 1, ctypes.byref(g), _ptr(S0),
+    args = (ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), ctypes.byref(f), int(bool(causal)), ctypes.byref(g),
+            _ptr(S0),
             _ptr(z0), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dg), _ptr(workspace), need, _stream(Q, stream))
     keep = (p, f, g, Q, K, V, dO, gate, S0, z0, workspace)
     return args, keep, tuple(grads)
 
 
 def backward(Q, K, V, dO, *, fmap="elu1", gate=None, eps=1e-6, S0=None, z0=None, grads=None, workspace=None,
-             stream=None):
+             stream=None, causal=True):
     """(dQ, dK, dV) of the causal forward for an incoming gradient dO, through la_backward;
     (dQ, dK, dV, dg) with the GLA or the selective gate, dg the gradient of its raw input g.
 
     Q, K [B, H, n, d_k]; V, dO [B, H, n, d_v] (bf16); gate None | ("decay", gamma[H]) |
     ("gla", g[B, H, n, d_k] bf16, tau) | ("sel", g[B, H, n] bf16, tau); S0, z0: the forward's
-    carried-in state, if any."""
-    args, _keep, grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream)
+    carried-in state, if any. causal=False: the non-causal form (elu+1, no gate, no state;
+    fp32 or bf16, gradients in the input dtype)."""
+    args, _keep, grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream, causal)
     N.check(N.lib().la_backward(*args), "la_backward")
     return grads
 

@@ -224,7 +224,12 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
   if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
   const int gk = gate_kind(g);
   if (!causal && gk != LA_GATE_NONE) return LA_ERR_INVALID_ARG;
-  if (!causal || (f->kind != LA_FMAP_ELU1 && f->kind != LA_FMAP_IDENTITY)) return LA_ERR_UNSUPPORTED;
+  if (!causal) {
+    // the non-causal form: elu+1, fp32 vector-ALU kernels, gradients in the input dtype
+    if (f->kind != LA_FMAP_ELU1 || p->in_dtype != p->out_dtype) return LA_ERR_UNSUPPORTED;
+    return shapes_built(f, p->d_k, p->d_v, false) ? LA_OK : LA_ERR_UNSUPPORTED;
+  }
+  if (f->kind != LA_FMAP_ELU1 && f->kind != LA_FMAP_IDENTITY) return LA_ERR_UNSUPPORTED;
   if (gk == LA_GATE_OUTER) return LA_ERR_UNSUPPORTED;
   if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   const int key = p->d_k * 1000 + p->d_v;
@@ -241,7 +246,21 @@ struct BwdWsLayout {
 // GLA adds dQ~ . Q~ per token and feature and the segments' summed log-gates;
 // the selective scalar gate runs the GLA passes and adds its input repeated
 // over features and the per-feature gradient of that (bf16 [B][H][n][r] each).
-BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, int gate) {
+// The non-causal form: the splits' partial S, z (forward sums) and G, hq.
+BwdWsLayout nc_bwd_workspace_layout(const la_problem* p, const la_feature_map* f) {
+  BwdWsLayout w{};
+  plan_splits(p->B, p->H, p->n, &w.P, &w.L);
+  const size_t pieces = (size_t)p->B * p->H * w.P, r = (size_t)f->r, dv = (size_t)p->d_v;
+  w.S_off = 0;
+  w.z_off = round_up(pieces * r * dv * 4, kAlign);
+  w.R_off = round_up(w.z_off + pieces * r * 4, kAlign);
+  w.rh_off = round_up(w.R_off + pieces * r * dv * 4, kAlign);
+  w.bytes = round_up(w.rh_off + pieces * r * 4, kAlign);
+  return w;
+}
+
+BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, int gate, int causal = 1) {
+  if (!causal) return nc_bwd_workspace_layout(p, f);
   BwdWsLayout w{};
   // the selective gate runs the GLA passes, on their segment plan
   plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate == LA_GATE_SEL ? LA_GATE_GLA : gate, &w.P,
@@ -626,7 +645,7 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
   if (bytes == nullptr) return LA_ERR_INVALID_ARG;
   la_status st = check_backward_shape(p, fmap, causal, gate);
   if (st != LA_OK) return st;
-  *bytes = bwd_workspace_layout(p, fmap, gate_kind(gate)).bytes;
+  *bytes = bwd_workspace_layout(p, fmap, gate_kind(gate), causal).bytes;
   return LA_OK;
 }
 
@@ -644,17 +663,18 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   const bool sel = gk == LA_GATE_SEL;
   if ((dg != nullptr) != (gk == LA_GATE_GLA || sel)) return LA_ERR_INVALID_ARG;
   if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_INVALID_ARG;
+  if (!causal && S0 != nullptr) return LA_ERR_INVALID_ARG;  // the non-causal form has no carried state
   for (const void* ptr : {Q, K, V, dO, (const void*)S0, (const void*)z0, (const void*)dQ, (const void*)dK,
                           (const void*)dV, (const void*)dg})
     if (ptr != nullptr && !aligned16(ptr)) return LA_ERR_INVALID_ARG;
-  const size_t BH = (size_t)p->B * p->H, n = (size_t)p->n, r = (size_t)fmap->r;
-  const size_t qk = BH * n * p->d_k * 2, vv = BH * n * p->d_v * 2, gg = BH * n * (sel ? 1 : r) * 2;
+  const size_t BH = (size_t)p->B * p->H, n = (size_t)p->n, r = (size_t)fmap->r, isz = dtype_size(p->in_dtype);
+  const size_t qk = BH * n * p->d_k * isz, vv = BH * n * p->d_v * isz, gg = BH * n * (sel ? 1 : r) * 2;
   const Range rq = range_of(Q, qk), rk = range_of(K, qk), rv = range_of(V, vv), rdo = range_of(dO, vv);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
   const Range rgl = range_of(gate_has_input(gk) ? gate->g : nullptr, gg);
   const Range rs0 = range_of(S0, BH * r * p->d_v * 4), rz0 = range_of(z0, BH * r * 4);
   const Range rdq = range_of(dQ, qk), rdk = range_of(dK, qk), rdv = range_of(dV, vv), rdg = range_of(dg, gg);
-  const BwdWsLayout wl = bwd_workspace_layout(p, fmap, gk);
+  const BwdWsLayout wl = bwd_workspace_layout(p, fmap, gk, causal);
   const Range rws = range_of(workspace, wl.bytes);
   for (Range o : {rdq, rdk, rdv, rdg, rws})
     for (Range i : {rq, rk, rv, rdo, rgam, rgl, rs0, rz0})
@@ -706,6 +726,12 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.dQ = dQ;
   plan.dK = dK;
   plan.dV = dV;
+  if (!causal) {  // splits of the sequence: wl.P of wl.L tokens
+    plan.causal = 0;
+    plan.splits = wl.P;
+    plan.split_len = wl.L;
+    return launch_noncausal_backward(plan);
+  }
   if (sel) {
     plan.g = ws + wl.gx_off;
     if ((st = launch_gate_repeat(gate->g, ws + wl.gx_off, (long long)(BH * n), fmap->r, plan.stream)) != LA_OK)

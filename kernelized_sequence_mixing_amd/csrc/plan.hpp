@@ -114,6 +114,7 @@ la_status launch_causal_favor(const FwdPlan& p);
 la_status launch_segment_scan(const FwdPlan& p);
 la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG);
 la_status launch_backward(const BwdPlan& p);
+la_status launch_noncausal_backward(const BwdPlan& p);  // ws_S, ws_z: partial S, z; ws_R, ws_rh: partial G, hq
 la_status launch_noncausal(const FwdPlan& p);
 la_status launch_decode(const DecodePlan& p);
 la_status launch_feature_map(const FmapPlan& p);

@@ -275,7 +275,12 @@ BAD_BACKWARD = [
     ("sel dg aliases g", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), dict(dg=FAKE + 6 * SP + 1024), N.LA_ERR_ALIAS),
     ("sel dg in workspace", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), dict(dg=FAKE + 4 * SP + 4096),
      N.LA_ERR_ALIAS),
-    ("noncausal", dict(causal=0), {}, N.LA_ERR_UNSUPPORTED),
+    ("noncausal favor", dict(causal=0, fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
+    ("noncausal identity", dict(causal=0, fkind=N.LA_FMAP_IDENTITY), {}, N.LA_ERR_UNSUPPORTED),
+    ("noncausal dtype mix", dict(causal=0, in_dt=N.LA_F32), {}, N.LA_ERR_UNSUPPORTED),
+    ("noncausal with S0", dict(causal=0, S0=FAKE + 7 * SP, z0=FAKE + 8 * SP), {}, N.LA_ERR_INVALID_ARG),
+    ("noncausal d_v 96", dict(causal=0, d_v=96), {}, N.LA_ERR_UNSUPPORTED),
+    ("noncausal gated", dict(causal=0, gkind=N.LA_GATE_DECAY, gamma=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),
     ("favor", dict(fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
     ("gla without dg", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),
     ("dg without gla", {}, dict(dg=FAKE + 14 * SP), N.LA_ERR_INVALID_ARG),
