@@ -253,7 +253,7 @@ def bench_serve_decode(wl, m, steps, warmup):
 
 
 def backward_algorithmic_per_token(wl):
-    """(bytes, matrix-core flops) per head-token of the causal backward pass.
+    """(bytes, matrix-core flops) per head-token of the backward pass (causal unless wl.causal is False).
 
     Bytes: read q, k, v, dO once, write dq, dk, dv once (GLA: also read g and
     write dg, r per token each; the selective gate: one of each per token). Flops (chunk C, masked upper triangle excluded): the scores, the
@@ -262,13 +262,16 @@ def backward_algorithmic_per_token(wl):
     dq's S g, dk's R v, dv's R phi(k), and the forward and reverse state
     updates).
     """
-    nbytes = 2 * (2 * wl.d_k + 2 * wl.d_v) + 2 * (2 * wl.d_k + wl.d_v)
+    isz = 4 if wl.dtype == "f32" else 2
+    nbytes = isz * (2 * wl.d_k + 2 * wl.d_v) + isz * (2 * wl.d_k + wl.d_v)
     if wl.gate == "gla":
         nbytes += 2 * (2 * wl.r)
     elif wl.gate == "sel":
         nbytes += 2 * 2
     half = (CHUNK + 1) / 2
     flops = half * 2 * wl.r * 3 + half * 2 * wl.d_v * 3 + 6 * 2 * wl.r * wl.d_v
+    if not wl.causal:  # the non-causal form: S, G and the per-token products, no scores
+        flops = 6 * 2 * wl.r * wl.d_v
     return nbytes, flops
 
 
@@ -278,7 +281,7 @@ def bench_backward(wl, steps, warmup):
     import kernelized_sequence_mixing_amd as ksm
     from workloads import incoming_gradient
     inp = make_inputs(wl, seed=0)
-    inp["dO"] = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1)
+    inp["dO"] = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1, dtype=wl.dtype)
     nb_tok, fl_tok = backward_algorithmic_per_token(wl)
     per_set = wl.head_tokens * nb_tok
     sets = _device_sets(inp, ["Q", "K", "V", "dO", "gamma", "g"], per_set)
@@ -288,7 +291,7 @@ def bench_backward(wl, steps, warmup):
              ((torch.empty_like(s["g"]),) if wl.gate in ("gla", "sel") else ()) for s in sets]
     stream = torch.cuda.current_stream()
     calls = [ksm.PreparedBackward(s["Q"], s["K"], s["V"], s["dO"], fmap=wl.fmap, gate=gate_of(s), eps=wl.eps,
-                                  grads=grads[i], stream=stream) for i, s in enumerate(sets)]
+                                  grads=grads[i], stream=stream, causal=wl.causal) for i, s in enumerate(sets)]
 
     def step(i):
         calls[i]()
@@ -405,6 +408,7 @@ def main():
                                     args.steps, args.warmup))
         for name in ("ssm_selective", "ssm_scalar"):  # the state-space form under both selective gates
             extra.append(bench_backward(WORKLOADS[name], args.steps, args.warmup))
+        extra.append(bench_backward(WORKLOADS["noncausal_elu1_f32"], args.steps, args.warmup))
         line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)

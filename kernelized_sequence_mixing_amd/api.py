@@ -366,9 +366,9 @@ class PreparedBackward:
     calling the object launches it again on the same buffers and stream."""
 
     def __init__(self, Q, K, V, dO, *, fmap="elu1", gate=None, eps=1e-6, S0=None, z0=None, grads=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, causal=True):
         self._args, self._keep, self.grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace,
-                                                            stream)
+                                                            stream, causal)
         self._fn = N.lib().la_backward
 
     def __call__(self):
