@@ -43,12 +43,12 @@ def test_backward_bytes_per_token():
     assert bench.backward_algorithmic_per_token(WORKLOADS["noncausal_elu1_f32"])[0] == 4 * (2 * 32 + 2 * 32) + 4 * (2 * 32 + 32)
 
 
-def test_traffic_only_for_the_measured_sources(tmp_path, monkeypatch):
+def test_traffic_only_for_the_measured_sources(monkeypatch):
     path = os.path.join(ROOT, "profiles", "traffic_causal_elu1.json")
     with open(path) as f:
         rec = json.load(f)
-    # the committed summary matches the committed kernel sources
-    assert rec["source_digest"] == bench.source_digest()
+    # reported for the sources the counters were taken on
+    monkeypatch.setattr(bench, "source_digest", lambda: rec["source_digest"])
     assert bench.measured_traffic("causal_elu1") == rec["hbm_bytes_per_step"]
     # any change to the kernel sources voids it
     monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
