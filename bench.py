@@ -1,19 +1,25 @@
 """Benchmark: causal kernelized linear attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline] [--only NAME]
 
-A step is one full forward pass of the hot path (feature map, segment states,
-segment chaining, chunked outputs) over one batch of the headline workload:
-causal elu+1, B=4 H=16 n=4096 d_k=d_v=64, bf16 inputs, fp32 state, 64-token
-chunks. Inputs are seeded synthetic tensors already resident in HBM; several
-copies at different addresses are rotated so that consecutive steps do not
-find their inputs in the 256 MB last-level (MALL) cache. Timing uses HIP events
-on the stream the library launches on. Rank 0 prints one JSON line.
+A step is one full forward pass of the hot path (feature map, gate prelude,
+segment states, segment chaining, chunked outputs) over one batch of the
+headline workload: GLA-gated causal elu+1 linear attention, B=2 H=16 n=16384
+d_k=d_v=128, bf16 inputs and outputs, fp32 state, 64-token chunks (the largest
+of the measured configurations). Inputs are seeded synthetic tensors already
+resident in HBM; several copies at different addresses are rotated so that
+consecutive steps do not find their inputs in the 256 MB last-level (MALL)
+cache. Timing uses HIP events on the stream the library launches on; a second
+run of the same steps brackets every kernel launch with events
+(la_timing_begin / la_timing_end) for the per-kernel durations behind the
+roofline. Rank 0 prints one JSON line.
 
 The same line carries, under "extra", the other workloads (non-causal fp32,
-RetNet decay, GLA gate, FAVOR+, the GLA decode step, and the backward pass on
-the headline shape), and the fp64 CPU oracle timed on the host on a bounded
-sample of the headline workload.
+causal elu+1, RetNet decay, the outer-product gate, the state-space forms,
+FAVOR+, the GLA decode step, the serving batch and the backward passes), and
+the fp64 CPU oracle (blocked form) timed on the host's cores on a bounded
+sample of the headline workload. ``--only NAME`` runs one workload and prints
+its record alone (for per-workload profiles).
 """
 from __future__ import annotations
 
@@ -76,9 +82,10 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per step from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, calibrated on a plain
+    copy), if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -86,7 +93,8 @@ def measured_traffic(workload):
         t = json.load(f)
     if t.get("source_digest") != source_digest():
         return None
-    return t.get("hbm_bytes_per_step")
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def _device_sets(inp, keys, per_set_bytes):
@@ -126,6 +134,26 @@ def time_steps(fn, n_sets, steps, warmup, stream):
     return total_ms / steps, step_ms[len(step_ms) // 2]
 
 
+def forward_kernel_names(wl, P):
+    """Kernel names of one la_forward call, in launch order."""
+    if not wl.causal:
+        return ["nc_partial", "nc_readout"]
+    pre = "favor" if wl.fmap == "favor" else "causal"
+    return [f"{pre}_segment_state", "segment_scan_kernel", f"{pre}_chunk_forward"] if P > 1 else \
+        [f"{pre}_chunk_forward"]
+
+
+def kernel_table(times, names):
+    """Average ms per launch index over the timed calls, labelled with `names`."""
+    n = len(times[0])
+    if any(len(t) != n for t in times):
+        raise RuntimeError("calls made different numbers of launches")
+    if len(names) != n:
+        names = [f"launch{i}" for i in range(n)]
+    return [{"name": names[i], "avg_ms": round(sum(t[i] for t in times) / len(times), 5),
+             "min_ms": round(min(t[i] for t in times), 5)} for i in range(n)]
+
+
 def bench_forward(wl, steps, warmup):
     import kernelized_sequence_mixing_amd as ksm
     inp = make_inputs(wl, seed=0)
@@ -155,9 +183,14 @@ def bench_forward(wl, steps, warmup):
         calls[i]()
 
     ms, med = time_steps(step, len(sets), steps, warmup, stream)
+    order = iter(range(steps))
+    times = ksm.launch_times(lambda: calls[next(order) % len(calls)](), steps, stream)
+    P = ksm.segments(wl.B, wl.H, wl.n, wl.d_k, wl.d_v, fmap=wl.fmap, r=wl.r, causal=wl.causal,
+                     gate_kind=wl.gate, dtype=sets[0]["Q"].dtype)[0] if wl.causal else 1
     tok_s = wl.head_tokens / (ms * 1e-3)
     res = {"workload": wl.name, "ms_per_step": round(ms, 5), "median_ms": round(med, 5),
-           "value": tok_s, "unit": "head-tokens/s", "input_sets_rotated": len(sets)}
+           "value": tok_s, "unit": "head-tokens/s", "input_sets_rotated": len(sets),
+           "segments": P, "kernels": kernel_table(times, forward_kernel_names(wl, P))}
     gbs = per_set / (ms * 1e-3) / 1e9
     tfl = wl.head_tokens * fl_tok / (ms * 1e-3) / 1e12
     res["hbm_alg_GBs"] = round(gbs, 1)
@@ -308,30 +341,112 @@ def bench_backward(wl, steps, warmup):
                       "fmap": wl.fmap}}
 
 
-def cpu_baseline(wl, min_seconds=10.0):
-    """The fp64 oracle (recurrent form, numpy) on the host: whole passes over
-    all heads of the headline workload, repeated until about `min_seconds` of
-    CPU work has been timed."""
+def _host_info():
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001 - the vendor string is informational only
+        pass
+    return cpu, blas
+
+
+def cpu_baseline(wl, heads=16, block=64, max_threads=16):
+    """The fp64 oracle's blocked form (oracle.causal_blocked, numpy) on the
+    host: a bounded sample of `heads` whole heads of the workload (full
+    sequence length), one head per worker thread, every thread running its
+    BLAS single-threaded, so that all the host cores given to the process work
+    at once. 64-token blocks: with a per-feature gate the block's decay tensor
+    grows as block^2 r, and 64 is the fastest block on the host."""
     import oracle as orc
+    from concurrent.futures import ThreadPoolExecutor
     from workloads import to_f64
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover - installed in this image
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    threads = max(1, min(cores, max_threads, heads))
     inp = make_inputs(wl, seed=0)
-    Q, K, V = (to_f64(inp[k]) for k in ("Q", "K", "V"))
-    r0 = resource.getrusage(resource.RUSAGE_SELF)
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        orc.causal_recurrent(Q, K, V, wl.fmap, None, None, eps=wl.eps)
-        passes += 1
+    sel = [(i // wl.H, i % wl.H) for i in range(min(heads, wl.B * wl.H))]
+    gate = {"none": lambda b, h: None, "gla": lambda b, h: ("gla", to_f64(inp["g"][b:b + 1, h:h + 1]), wl.tau),
+            "decay": lambda b, h: ("decay", to_f64(inp["gamma"][h:h + 1]))}[wl.gate]
+    args = [(to_f64(inp["Q"][b:b + 1, h:h + 1]), to_f64(inp["K"][b:b + 1, h:h + 1]),
+             to_f64(inp["V"][b:b + 1, h:h + 1]), gate(b, h)) for b, h in sel]
+
+    def one(a):
+        return orc.causal_blocked(a[0], a[1], a[2], wl.fmap, None, a[3], eps=wl.eps, block=block)[0].shape
+
+    import contextlib
+    with (threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()):
+        r0 = resource.getrusage(resource.RUSAGE_SELF)
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, args))
         dt = time.perf_counter() - t0
-        if dt >= min_seconds or passes >= 20:
-            break
-    r1 = resource.getrusage(resource.RUSAGE_SELF)
-    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
-    return {"value": passes * wl.head_tokens / dt, "unit": "head-tokens/s", "cores": max(1, round(cpu / dt)),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"{wl.name}: {passes} full passes over all B*H={wl.B * wl.H} heads x n={wl.n} tokens, "
-                      "fp64 numpy recurrent form",
-            "host": platform.processor() or platform.machine()}
+        r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu_s = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    model, blas = _host_info()
+    toks = len(sel) * wl.n
+    return {"value": toks / dt, "unit": "head-tokens/s", "cores": threads, "kind": "oracle", "seconds": round(dt, 2),
+            "cpu_seconds": round(cpu_s, 1),
+            "sample": f"{wl.name}: {len(sel)} of the {wl.B * wl.H} heads, each the whole n={wl.n} sequence "
+                      f"(d_k=d_v={wl.d_k}, gate {wl.gate}), fp64 numpy blocked form in {block}-token blocks, "
+                      f"{threads} worker threads with single-threaded BLAS",
+            "host_cores_available": cores, "cpu_model": model, "blas": blas}
+
+
+def run_only(name, steps, warmup):
+    """One workload's record alone (for per-workload profiles)."""
+    if name in WORKLOADS and not WORKLOADS[name].decode:
+        return bench_forward(WORKLOADS[name], steps, warmup)
+    if name == "gla_decode":
+        return bench_decode(WORKLOADS[name], steps, warmup)
+    if name == "serve_prefill":
+        return bench_serve_prefill(steps, warmup)
+    if name in ("serve_decode_m1", "serve_decode_m4"):
+        return bench_serve_decode(WORKLOADS["gla_decode"], int(name[-1]), steps, warmup)
+    if name.endswith("_backward") and name[:-len("_backward")] in BACKWARD_WORKLOADS:
+        return bench_backward(BACKWARD_WORKLOADS[name[:-len("_backward")]], steps, warmup)
+    raise SystemExit(f"unknown workload {name!r}")
+
+
+# the backward lines: the headline shape of the ungated form, the GLA workload's sequence
+# shape at d_k = d_v = 64, the state-space form under both selective gates, non-causal
+BACKWARD_WORKLOADS = {
+    "causal_elu1": WORKLOADS["causal_elu1"],
+    "gla_gate_d64": WORKLOADS["gla_gate"].resized(name="gla_gate_d64", d_k=64, d_v=64, r=64, qk_scale=64 ** -0.5,
+                                                  v_scale=64 ** -0.5),
+    "ssm_selective": WORKLOADS["ssm_selective"],
+    "ssm_scalar": WORKLOADS["ssm_scalar"],
+    "noncausal_elu1_f32": WORKLOADS["noncausal_elu1_f32"],
+}
+
+
+def roofline(wl, res):
+    """The dominant kernel of a forward step against the HBM roofline:
+    algorithmic bytes of the whole step (every head-token's q, k, v, gate
+    inputs read once and o written once, all of them by the output pass) over
+    that kernel's average launch time from the per-launch events."""
+    nb_tok, _ = algorithmic_per_token(wl)
+    dom = max(res["kernels"], key=lambda k: k["avg_ms"])
+    alg = wl.head_tokens * nb_tok
+    gbs = alg / (dom["avg_ms"] * 1e-3) / 1e9
+    tr = measured_traffic(wl.name, dom["name"])
+    return {"bound": "hbm", "kernel": dom["name"], "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": tr, "alg_bytes_per_launch": alg,
+            "launch_ms": dom["avg_ms"],
+            "step": {"achieved": res["hbm_alg_GBs"], "frac": res["hbm_frac"], "ms": res["ms_per_step"]}}
 
 
 def main():
@@ -341,6 +456,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="run one workload and print its record alone")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -364,10 +480,14 @@ def main():
         return
     from kernelized_sequence_mixing_amd import _native
     _native.lib()  # fail loudly if the HIP library is missing
+    if args.only:
+        print(json.dumps(run_only(args.only, args.steps, args.warmup)), flush=True)
+        return
 
     wl = WORKLOADS[HEADLINE]
     head = bench_forward(wl, args.steps, args.warmup)
-    traffic = measured_traffic(wl.name)
+    print(f"headline {wl.name}: {head['ms_per_step']:.4f} ms/step, kernels {head['kernels']}", file=sys.stderr,
+          flush=True)
     line = {
         "metric": METRIC,
         "value": head["value"],
@@ -380,35 +500,33 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1)*d^-0.5 inputs, rotated copies in HBM)",
-        "config": {"workload": "causal elu+1 linear attention forward, B=4 H=16 n=4096 d_k=d_v=64, bf16 in/out, "
-                               "fp32 state, chunk 64", "B": wl.B, "H": wl.H, "n": wl.n, "d_k": wl.d_k,
-                   "d_v": wl.d_v, "feature_map": "elu+1", "gate": "none", "chunk": CHUNK},
-        "roofline": {"bound": "hbm", "kernel": "la_forward step (segment-state pass + scan + chunked output pass)",
-                     "achieved": head["hbm_alg_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["hbm_frac"], "traffic": traffic,
-                     "alg_bytes_per_launch": wl.head_tokens * head["alg_bytes_per_token"]},
-        "mfma": {"achieved_TFLOPs": head["mfma_alg_TFLOPs"], "peak_TFLOPs": BF16_PEAK_TFLOPS,
-                 "frac": head["mfma_frac"]},
+        "data": "synthetic (seeded N(0,1)*d^-0.5 inputs, N(0,1) gate inputs, rotated copies in HBM)",
+        "config": {"workload": "GLA-gated causal elu+1 linear attention forward, B=2 H=16 n=16384 d_k=d_v=128, "
+                               "bf16 in/out, fp32 state, chunk 64, tau 16", "B": wl.B, "H": wl.H, "n": wl.n,
+                   "d_k": wl.d_k, "d_v": wl.d_v, "feature_map": "elu+1", "gate": "gla", "chunk": CHUNK},
+        "kernels": head["kernels"],
+        "roofline": roofline(wl, head),
+        "mfma": {"alg_TFLOPs": head["mfma_alg_TFLOPs"], "peak_TFLOPs": BF16_PEAK_TFLOPS,
+                 "alg_frac": head["mfma_frac"], "note": "algorithmic flops over the step time; the counter-issued "
+                                                        "MFMA utilisation is in profiles/"},
         "context": {"softmax_score_matrix_n16384_fp16_bytes": 16384 * 16384 * 2},
     }
     if not args.no_extra:
         extra = []
-        for name in ("noncausal_elu1_f32", "retnet_decay", "gla_gate", "outer_gate", "ssm_selective", "ssm_scalar",
+        for name in ("noncausal_elu1_f32", "causal_elu1", "retnet_decay", "outer_gate", "ssm_selective", "ssm_scalar",
                      "favor_causal"):
-            extra.append(bench_forward(WORKLOADS[name], args.steps, args.warmup))
+            r = bench_forward(WORKLOADS[name], args.steps, args.warmup)
+            if WORKLOADS[name].causal:
+                r["roofline"] = roofline(WORKLOADS[name], r)
+            extra.append(r)
+            print(f"{name}: {r['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
         extra.append(bench_decode(WORKLOADS["gla_decode"], args.steps, args.warmup))
         extra.append(bench_serve_prefill(args.steps, args.warmup))
         for m in (1, 4):
             extra.append(bench_serve_decode(WORKLOADS["gla_decode"], m, args.steps, args.warmup))
-        extra.append(bench_backward(WORKLOADS["causal_elu1"], args.steps, args.warmup))
-        # the GLA workload's sequence shape at d_k = d_v = 64 (no backward build for 128 x 128 states)
-        extra.append(bench_backward(WORKLOADS["gla_gate"].resized(name="gla_gate_d64", d_k=64, d_v=64, r=64,
-                                                                  qk_scale=64 ** -0.5, v_scale=64 ** -0.5),
-                                    args.steps, args.warmup))
-        for name in ("ssm_selective", "ssm_scalar"):  # the state-space form under both selective gates
-            extra.append(bench_backward(WORKLOADS[name], args.steps, args.warmup))
-        extra.append(bench_backward(WORKLOADS["noncausal_elu1_f32"], args.steps, args.warmup))
+        for bw in BACKWARD_WORKLOADS.values():
+            extra.append(bench_backward(bw, args.steps, args.warmup))
+            print(f"{bw.name} backward: {extra[-1]['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
         line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)

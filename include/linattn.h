@@ -57,45 +57,42 @@ typedef enum la_status {
 
 typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
-/* Feature maps ("Choosing the Feature Map phi", dileepadev page):
- *   ELU1  : phi(x) = elu(x) + 1 elementwise (r == d_k).
- *   FAVOR : phi(x)_m = exp(w_m . x - |x|^2 / 2) / sqrt(r), m = 0..r-1, the
- *           positive random features whose inner product estimates exp(q.k);
- *           omega holds the r rows w_m. */
 /*
- * Feature maps. ELU1: phi(x) = elu(x) + 1; FAVOR: positive random features
- * exp(w.x - |x|^2/2) / sqrt(r) with omega [r][d_k]. IDENTITY: the state-space
- * form ("State Space Models as Linear Attention", dileepadev page: h_t =
- * A_t h_{t-1} + B_t x_t, y_t = C_t^T h_t): q = C and k = B enter unchanged
- * and the read-out is NOT normalised, o_i = q_i^T S_i (z is still carried as
- * the state's column of a constant-1 value and returned in z_final, but not
- * read); causal only, r = d_k, gates as for ELU1 (the GLA gate is the
- * selective, input-dependent diagonal A_t).
+ * Feature maps ("Choosing the Feature Map phi", dileepadev page):
+ *   ELU1     : phi(x) = elu(x) + 1 elementwise (r == d_k).
+ *   FAVOR    : phi(x)_m = exp(w_m . x - |x|^2 / 2) / sqrt(r), m = 0..r-1, the
+ *              positive random features whose inner product estimates
+ *              exp(q . k); omega [r][d_k] holds the rows w_m.
+ *   IDENTITY : the state-space form ("State Space Models as Linear Attention",
+ *              dileepadev page: h_t = A_t h_{t-1} + B_t x_t, y_t = C_t^T h_t):
+ *              q = C and k = B enter unchanged and the read-out is NOT
+ *              normalised, o_i = q_i^T S_i (z is still carried as the state's
+ *              column of a constant-1 value and returned in z_final, but not
+ *              read); causal only, r = d_k, gates as for ELU1 (the GLA gate is
+ *              the selective, input-dependent diagonal A_t).
  */
 typedef enum la_fmap_kind { LA_FMAP_ELU1 = 0, LA_FMAP_FAVOR = 1, LA_FMAP_IDENTITY = 2 } la_fmap_kind;
 
-/* State gates for the causal form ("Gating and Selective State Updates"):
- *   NONE  : S_t = S_{t-1} + phi(k_t) v_t^T.
- *   DECAY : S_t = gamma_h S_{t-1} + phi(k_t) v_t^T (RetNet fixed decay).
- *   GLA   : S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T with
- *           alpha_t = sigmoid(g_t)^(1/tau) per feature row (diagonal GLA gate).
- *   OUTER : S_t = (alpha_t beta_t^T) * S_{t-1} + phi(k_t) v_t^T (elementwise),
- *           alpha_t as GLA, beta_t = sigmoid(gv_t)^(1/tau) per value column;
- *           z_t = alpha_t * z_{t-1} + phi(k_t). */
 /*
- * Gates of the causal forms (the multiplier of the previous state at each
- * step). DECAY: RetNet's fixed gamma_h. GLA: a per-feature, input-dependent
- * alpha_t = sigmoid(g_t)^(1/tau), g [B][H][n][r] ("Gating and Selective State
- * Updates", dileepadev page). SEL: the scalar selective gate, one
- * input-dependent a_t = sigmoid(g_t)^(1/tau) per step and head shared by all
- * features, g [B][H][n] (decode: [B][H]); the RetNet decay made
- * input-dependent, the selective recurrence of Mamba's kind ("State Space
- * Models as Linear Attention", dileepadev page; "Evolution: add
- * decay/gating", vguerra page). OUTER: the gate matrix G_t in (0, 1)^{d x d}
- * of "Gating and Selective State Updates" as the outer product of a key-side
- * alpha_t (the GLA gate, input g) and a value-side beta_t (input gv
- * [B][H][n][d_v], decode [B][H][d_v]); the normaliser z takes the key side
- * only. GLA, SEL and OUTER: elementwise feature maps only.
+ * Gates of the causal forms: the multiplier of the previous state at each step
+ * ("Gating and Selective State Updates", dileepadev page; "Evolution: add
+ * decay/gating", vguerra page). z is gated exactly like S unless stated.
+ *   NONE  : S_t = S_{t-1} + phi(k_t) v_t^T.
+ *   DECAY : S_t = gamma_h S_{t-1} + phi(k_t) v_t^T (RetNet's fixed decay).
+ *   GLA   : S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T, a per-feature,
+ *           input-dependent alpha_t = sigmoid(g_t)^(1/tau), g [B][H][n][r].
+ *   SEL   : the scalar selective gate, one input-dependent
+ *           a_t = sigmoid(g_t)^(1/tau) per step and head shared by all
+ *           features, g [B][H][n] (decode: [B][H]): the RetNet decay made
+ *           input-dependent, the selective recurrence of Mamba's kind ("State
+ *           Space Models as Linear Attention", dileepadev page).
+ *   OUTER : S_t = (alpha_t beta_t^T) * S_{t-1} + phi(k_t) v_t^T (elementwise):
+ *           the gate matrix G_t in (0, 1)^{d x d} as the outer product of the
+ *           key-side alpha_t of GLA (input g) and a value-side
+ *           beta_t = sigmoid(gv_t)^(1/tau) per value column (input gv
+ *           [B][H][n][d_v], decode [B][H][d_v]); z_t = alpha_t * z_{t-1} +
+ *           phi(k_t) (the key side only).
+ * GLA, SEL and OUTER take elementwise feature maps only.
  */
 typedef enum la_gate_kind {
   LA_GATE_NONE = 0,
@@ -126,12 +123,20 @@ typedef struct la_gate {
   const float* gamma; /* DECAY: device [H] fp32, each in (0, 1] -- a documented
                          precondition, not checked (the values live on the device) */
   const void* g;      /* GLA, OUTER: device [B][H][n][r] in in_dtype (decode: [B][H][r]);
-                         SEL: [B][H][n] (decode: [B][H]). Precondition of the causal
-                         kernels for GLA and OUTER, not checked: over any 64 aligned
-                         tokens the summed log alpha of each feature stays above -80
-                         (the factors e^{+-b} are referenced to the chunk start) */
+                         SEL: [B][H][n] (decode: [B][H]). Precondition of the chunked
+                         causal kernels (la_forward, la_forward_batch with more than
+                         one token per sequence, la_backward) for GLA and OUTER, not
+                         checked since g lives on the device: within every 64-token
+                         chunk (tokens 64c .. 64c + 63 of each sequence) the summed
+                         log alpha of each feature stays at or above -80. The
+                         chunk's factors e^{+b}, e^{-b} are referenced to the chunk
+                         start and stay finite in fp32 and bf16 there; below it the
+                         outputs may be Inf or NaN. la_decode_step, one-token batch
+                         steps and SEL have no such limit (SEL forms each factor
+                         as e^{b_i - b_j} <= 1). */
   const void* gv;     /* OUTER: device [B][H][n][d_v] in in_dtype (decode: [B][H][d_v]),
-                         with the same precondition per value column; must be NULL
+                         with the same precondition per value column (summed
+                         log beta); must be NULL
                          for every other gate (else LA_ERR_INVALID_ARG) */
 } la_gate;
 
@@ -198,13 +203,16 @@ la_status la_forward_segments(const la_problem* p, const la_feature_map* fmap,
  *   workspace     device scratch of at least la_forward_workspace_size bytes
  *                 (may be NULL when that size is 0), 256-byte aligned.
  * Supported (else LA_ERR_UNSUPPORTED):
- *   causal: in_dtype BF16, out_dtype BF16; ELU1 or IDENTITY with d_k in {32,64,128}
- *           and any gate; FAVOR with d_k in {32,64,128}, r in {64,128,256}, gate
- *           NONE or DECAY;
- *           d_v in {32,64,128}; r * d_v <= 16384.
- *   non-causal: in/out dtype F32 or BF16 (any mix); same d_k, d_v, r sets.
+ *   causal: in_dtype BF16, out_dtype BF16; d_v in {64,128}; ELU1 or IDENTITY with
+ *           d_k in {32,64,128} and any gate; FAVOR with d_k in {32,64,128},
+ *           r in {64,128,256}, gate NONE or DECAY; r * d_v <= 16384.
+ *   non-causal: in/out dtype F32 or BF16 (any mix); d_k in {32,64,128},
+ *           d_v in {32,64,128}; FAVOR r in {64,128,256}; r * d_v <= 16384.
  * Numerics: bf16 MFMA products with fp32 accumulation; the state, normaliser,
- * gate factors and every denominator are fp32; the division is IEEE fp32.
+ * gate factors and every denominator are fp32. The causal kernels normalise
+ * each output row by one correctly rounded fp32 reciprocal of its denominator
+ * and a multiply, out = fl(num * fl(1 / den)); the non-causal kernels divide,
+ * out = fl(num / den) (IEEE fp32).
  */
 la_status la_forward(const la_problem* p, const void* Q, const void* K, const void* V,
                      const la_feature_map* fmap, int32_t causal, const la_gate* gate,
@@ -317,8 +325,9 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
  *   p->n must be 1; q, k [B][H][d_k], v [B][H][d_v], gate->g [B][H][r] (in_dtype);
  *   S [B][H][r][d_v] fp32 and z [B][H][r] fp32 are read and overwritten;
  *   out [B][H][d_v] in out_dtype.
- * Supported: in_dtype F32 or BF16, out_dtype F32 or BF16; ELU1 d_k in {32,64,128};
- * FAVOR d_k in {32,64,128}, r in {64,128,256}; any gate; d_v in {32,64,128}.
+ * Supported: in_dtype F32 or BF16, out_dtype F32 or BF16; ELU1 or IDENTITY with
+ * d_k in {32,64,128}; FAVOR d_k in {32,64,128}, r in {64,128,256}; any gate;
+ * d_v in {32,64,128}; r * d_v <= 16384. fp32 arithmetic; out = fl(num / den).
  */
 la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
                          const void* k, const void* v, const la_feature_map* fmap,
@@ -332,6 +341,23 @@ la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,
  */
 la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t d_k,
                                int32_t in_dtype, const void* X, float* out, void* stream);
+
+/*
+ * Launch timing, for profiling (computes nothing). la_timing_begin opens a
+ * bracket on the calling host thread; until la_timing_end on the same thread,
+ * every kernel launch the library makes first records events[i] on its stream
+ * (hipEventRecord; i counts the bracket's launches from 0). la_timing_end
+ * records events[launches] on `stream` and returns the number of launches in
+ * *launches (may be NULL), so hipEventElapsedTime(events[i], events[i + 1]) is
+ * the time of launch i on an otherwise idle stream. The events are the
+ * caller's hipEvent_t handles (created with timing enabled), at least
+ * launches + 1 of them; launches past n_events - 1 are counted, not recorded.
+ * Errors: LA_ERR_INVALID_ARG for a NULL event, n_events < 0, a bracket already
+ * open (begin) or none open (end); LA_ERR_HIP from la_timing_end if any record
+ * failed. The entry points called inside the bracket behave as always.
+ */
+la_status la_timing_begin(void* const* events, int32_t n_events);
+la_status la_timing_end(void* stream, int32_t* launches);
 
 #ifdef __cplusplus
 }

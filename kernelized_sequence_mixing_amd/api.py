@@ -42,12 +42,20 @@ def _stream(t: torch.Tensor, stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _fmap_struct(fmap: str, omega, d_k: int):
+def _same_dtype(t, in_dtype, name):
+    """The C ABI reads g, gv and omega with the element size of the input dtype,
+    so a tensor of another dtype would be misread (or read past its end)."""
+    if in_dtype is not None and isinstance(t, torch.Tensor) and t.dtype != in_dtype:
+        raise TypeError(f"{name} must have the input dtype {in_dtype}, got {t.dtype}")
+
+
+def _fmap_struct(fmap: str, omega, d_k: int, in_dtype=None):
     if fmap not in _FMAP:
         raise ValueError(f"unknown feature map {fmap!r}")
     if fmap == "favor":
         if omega is None:
             raise ValueError("favor needs omega [r, d_k]")
+        _same_dtype(omega, in_dtype, "omega")
         _dev(omega, "omega")
         if omega.dim() != 2 or omega.shape[1] != d_k:
             raise ValueError(f"omega must be [r, {d_k}], got {tuple(omega.shape)}")
@@ -57,14 +65,20 @@ def _fmap_struct(fmap: str, omega, d_k: int):
     return N.LaFeatureMap(_FMAP[fmap], d_k, None), d_k
 
 
-def _gate_struct(gate, expect_g_shape, d_v=None):
+def _gate_struct(gate, expect_g_shape, d_v=None, in_dtype=None):
     """gate: None | ("decay", gamma[H] fp32) | ("gla", g, tau) | ("sel", g, tau) |
     ("outer", g, gv, tau); g has shape expect_g_shape for GLA and the outer-product gate,
     and expect_g_shape without its last (feature) axis for the selective scalar gate; gv
-    (the outer-product gate's value side) has d_v on that last axis."""
+    (the outer-product gate's value side) has d_v on that last axis. g and gv must have
+    the input dtype in_dtype (checked before anything else)."""
     if gate is None or gate == "none" or (isinstance(gate, tuple) and gate[0] == "none"):
         return N.LaGate(N.LA_GATE_NONE, 1.0, None, None)
     kind = gate[0]
+    if kind in ("gla", "sel"):
+        _same_dtype(gate[1], in_dtype, "g")
+    if kind == "outer":
+        _same_dtype(gate[1], in_dtype, "g")
+        _same_dtype(gate[2], in_dtype, "gv")
     if kind == "decay":
         gam = _dev(gate[1], "gamma")
         if gam.dtype != torch.float32 or gam.shape != (expect_g_shape[1],):
@@ -139,12 +153,8 @@ def _forward_args(Q, K, V, fmap, omega, causal, gate, eps, S0, z0, return_state,
     d_v = V.shape[3]
     in_dt = _dt(Q)
     out_dtype = Q.dtype if out_dtype is None else out_dtype
-    f, r = _fmap_struct(fmap, omega, d_k)
-    if omega is not None and omega.dtype != Q.dtype:
-        raise TypeError("omega must have the input dtype")
-    g = _gate_struct(gate, (B, H, n, r), d_v)
-    if g.kind in (N.LA_GATE_GLA, N.LA_GATE_OUTER) and gate[1].dtype != Q.dtype:
-        raise TypeError("g must have the input dtype")
+    f, r = _fmap_struct(fmap, omega, d_k, Q.dtype)
+    g = _gate_struct(gate, (B, H, n, r), d_v, Q.dtype)
     p = _problem(B, H, n, d_k, d_v, in_dt, _DT[out_dtype], eps)
     if out is None:
         out = torch.empty((B, H, n, d_v), dtype=out_dtype, device=Q.device)
@@ -218,8 +228,8 @@ def _batch_args(Q, K, V, cu_seqlens, max_seqlen, state, slot_ids, read, write, f
         raise TypeError("Q, K, V must share a dtype")
     B, H, n, d_k = Q.shape
     d_v = V.shape[3]
-    f, r = _fmap_struct(fmap, omega, d_k)
-    g = _gate_struct(gate, (B, H, n, r), d_v)
+    f, r = _fmap_struct(fmap, omega, d_k, Q.dtype)
+    g = _gate_struct(gate, (B, H, n, r), d_v, Q.dtype)
     p = _problem(B, H, n, d_k, d_v, _dt(Q), _dt(Q), eps)
     if cu_seqlens is not None:
         _dev(cu_seqlens, "cu_seqlens")
@@ -313,8 +323,8 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
         raise TypeError("Q, K, V, dO must share a dtype")
     B, H, n, d_k = Q.shape
     d_v = V.shape[3]
-    f, r = _fmap_struct(fmap, None, d_k)
-    g = _gate_struct(gate, (B, H, n, r), d_v)
+    f, r = _fmap_struct(fmap, None, d_k, Q.dtype)
+    g = _gate_struct(gate, (B, H, n, r), d_v, Q.dtype)
     p = _problem(B, H, n, d_k, d_v, _dt(Q), _dt(Q), eps)
     for t, nm, shp in ((S0, "S0", (B, H, r, d_v)), (z0, "z0", (B, H, r))):
         if t is not None:
@@ -387,12 +397,12 @@ def _decode_args(S, z, q, k, v, fmap, omega, gate, eps, out_dtype, out, stream):
         raise TypeError("q, k, v must share a dtype")
     B, H, d_k = q.shape
     d_v = v.shape[2]
-    f, r = _fmap_struct(fmap, omega, d_k)
+    f, r = _fmap_struct(fmap, omega, d_k, q.dtype)
     if tuple(S.shape) != (B, H, r, d_v) or S.dtype != torch.float32:
         raise ValueError(f"S must be float32 {(B, H, r, d_v)}")
     if tuple(z.shape) != (B, H, r) or z.dtype != torch.float32:
         raise ValueError(f"z must be float32 {(B, H, r)}")
-    g = _gate_struct(gate, (B, H, r), d_v)
+    g = _gate_struct(gate, (B, H, r), d_v, q.dtype)
     p = _problem(B, H, 1, d_k, d_v, _dt(q), _DT[out_dtype], eps)
     if out is None:
         out = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
@@ -434,9 +444,40 @@ def feature_map(X, *, fmap="elu1", omega=None, stream=None):
     """phi(X) over the last axis in fp32 through la_feature_map_apply."""
     _dev(X, "X")
     d_k = X.shape[-1]
-    f, r = _fmap_struct(fmap, omega, d_k)
+    f, r = _fmap_struct(fmap, omega, d_k, X.dtype)
     rows = X.numel() // d_k
     out = torch.empty(X.shape[:-1] + (r,), dtype=torch.float32, device=X.device)
     N.check(N.lib().la_feature_map_apply(ctypes.byref(f), rows, d_k, _dt(X), _ptr(X), _ptr(out),
                                          _stream(X, stream)), "la_feature_map_apply")
     return out
+
+
+def launch_times(call, steps, stream, max_launches=8):
+    """GPU time of every kernel launch of `steps` calls of `call()` (a prepared
+    call on `stream`), through la_timing_begin / la_timing_end: each call runs
+    inside its own timing bracket with its own events, back to back. Returns a
+    list per call of the milliseconds of each launch, in launch order."""
+    L = N.lib()
+    evs = []
+    for _ in range(steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(max_launches + 1)]
+        for e in row:
+            e.record(stream)  # creates the event so that it has a handle
+        evs.append(row)
+    torch.cuda.synchronize()
+    handles = [(ctypes.c_void_p * len(row))(*[e.cuda_event for e in row]) for row in evs]
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    counts = []
+    for i in range(steps):
+        N.check(L.la_timing_begin(handles[i], len(evs[i])), "la_timing_begin")
+        try:
+            call()
+        finally:
+            nl = ctypes.c_int32(0)
+            st = L.la_timing_end(sp, ctypes.byref(nl))
+        N.check(st, "la_timing_end")
+        if nl.value > max_launches:
+            raise ValueError(f"{nl.value} launches per call; raise max_launches")
+        counts.append(nl.value)
+    torch.cuda.synchronize()
+    return [[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(counts[i])] for i in range(steps)]

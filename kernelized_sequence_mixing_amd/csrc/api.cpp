@@ -8,7 +8,12 @@
 #include "plan.hpp"
 
 namespace la {
+
+thread_local LaunchTimer* t_launch_timer = nullptr;
+
 namespace {
+
+thread_local LaunchTimer t_timer_slot;
 
 constexpr size_t kAlign = 256;
 
@@ -739,6 +744,25 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   }
   if ((st = launch_backward(plan)) != LA_OK) return st;
   return sel ? launch_gate_feature_sum(ws + wl.dgx_off, dg, (long long)(BH * n), fmap->r, plan.stream) : LA_OK;
+}
+
+la_status la_timing_begin(void* const* events, int32_t n_events) {
+  if (n_events < 0 || (n_events > 0 && events == nullptr)) return LA_ERR_INVALID_ARG;
+  if (t_launch_timer != nullptr) return LA_ERR_INVALID_ARG;  // brackets do not nest
+  for (int32_t i = 0; i < n_events; ++i)
+    if (events[i] == nullptr) return LA_ERR_INVALID_ARG;
+  t_timer_slot = LaunchTimer{events, n_events, 0, false};
+  t_launch_timer = &t_timer_slot;
+  return LA_OK;
+}
+
+la_status la_timing_end(void* stream, int32_t* launches) {
+  if (t_launch_timer == nullptr) return LA_ERR_INVALID_ARG;
+  LaunchTimer* t = t_launch_timer;
+  mark_launch(static_cast<hipStream_t>(stream));  // the end of the last launch
+  t_launch_timer = nullptr;
+  if (launches != nullptr) *launches = t->used - 1;
+  return t->failed ? LA_ERR_HIP : LA_OK;
 }
 
 la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t d_k, int32_t in_dtype,

@@ -8,7 +8,7 @@ static la_status launch_with_lds(K kernel, dim3 grid, int lds, hipStream_t st, c
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
       hipSuccess)
     return LA_ERR_HIP;
-  hipLaunchKernelGGL(kernel, grid, dim3(256), lds, st, b);
+  LA_LAUNCH(kernel, grid, dim3(256), lds, st, b);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
@@ -64,7 +64,7 @@ static la_status run_backward(const BwdPlan& p) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
         hipSuccess)
       return LA_ERR_HIP;
-    hipLaunchKernelGGL(k1, dim3(p.P - 1, BH), dim3(256), lds1, p.stream, a1);
+    LA_LAUNCH(k1, dim3(p.P - 1, BH), dim3(256), lds1, p.stream, a1);
     if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     if ((st = launch_segment_scan(p)) != LA_OK) return st;
     b.S_in = p.ws_S;

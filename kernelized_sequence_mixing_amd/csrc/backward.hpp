@@ -260,8 +260,9 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = 16 * c + 4 * g4 + i;
-          v[i] = key > q ? 0.f : acc[i];
-          if constexpr (GATE == GT_DECAY) v[i] *= exp2f(float(q - key) * lg2gam);
+          v[i] = acc[i];
+          if constexpr (GATE == GT_DECAY) v[i] *= exp2f(float(max(q - key, 0)) * lg2gam);
+          if (key > q) v[i] = 0.f;  // select after the factor (gamma^-15 overflows for a small gamma)
         }
         const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
         rs += (lo_bf16_f32(p01) + hi_bf16_f32(p01)) + (lo_bf16_f32(p23) + hi_bf16_f32(p23));
@@ -341,8 +342,9 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int j = 16 * jt + 4 * g4 + u;
-          v[u] = j > i ? 0.f : acc[u] + hi;
-          if constexpr (GATE == GT_DECAY) v[u] *= exp2f(float(i - j) * lg2gam);
+          v[u] = acc[u] + hi;
+          if constexpr (GATE == GT_DECAY) v[u] *= exp2f(float(max(i - j, 0)) * lg2gam);
+          if (j > i) v[u] = 0.f;
         }
         lds<bf16x4>(sm, LY::a_off + AT::at(i, 2 * jt + (g4 >> 1), 8 * (g4 & 1))) = pack4(v[0], v[1], v[2], v[3]);
       }
@@ -677,7 +679,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           const int i = 16 * it + 4 * g4 + u;
           const bool ok = i >= j;
           float dec = 1.f;
-          if constexpr (GATE == GT_DECAY) dec = exp2f(float(i - j) * lg2gam);
+          if constexpr (GATE == GT_DECAY) dec = exp2f(float(max(i - j, 0)) * lg2gam);
           vw[u] = ok ? aw[u] * dec : 0.f;
           vd[u] = ok ? (ad[u] + lds<float>(sm, LY::hw_off + 4 * i)) * dec : 0.f;
         }
@@ -721,7 +723,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
 #pragma unroll
         for (int p = 0; p < KP; ++p) kb[p] = feature_pairs<R>(sm, LY::k_off, j, p, g4);
         float sc = 1.f;
-        if constexpr (GATE == GT_DECAY) sc = exp2f(float(L - j) * lg2gam);
+        if constexpr (GATE == GT_DECAY) sc = exp2f(float(max(L - j, 0)) * lg2gam);
 #pragma unroll
         for (int eb = 0; eb < NEB; ++eb) {
           const int e = ebase + 16 * eb;
@@ -780,7 +782,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           a2 = mfma16(lds<bf16x8>(sm, LY::rb_off + VT::at(16 * ft + c16, 4 * ks + g4)),
                       lds<bf16x8>(sm, LY::v_off + VT::at(j, 4 * ks + g4)), a2);
         float sc = 1.f;
-        if constexpr (GATE == GT_DECAY) sc = exp2f(float(L - j) * lg2gam);
+        if constexpr (GATE == GT_DECAY) sc = exp2f(float(max(L - j, 0)) * lg2gam);
         const bf16x4 ph = lds<bf16x4>(sm, LY::k_off + FT::at(j, f0 / 8, 2 * (f0 % 8)));
         bf16x4 kd = ph;
         if constexpr (GATE == GT_GLA) kd = lds<bf16x4>(sm, LY::kd_off + FT::at(j, f0 / 8, 2 * (f0 % 8)));

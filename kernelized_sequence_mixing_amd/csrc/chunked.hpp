@@ -360,7 +360,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
     const int t = Raw::TPW * w + lane / LPT;
     const bool valid = t < L;
     float decay_k = 1.f;
-    if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(L - 1 - t) * lg2gam);
+    if constexpr (GATE == GT_DECAY) decay_k = exp2f(float(max(L - 1 - t, 0)) * lg2gam);  // rows past L are dropped
     if constexpr (GATE == GT_SEL) {
       // the chunk's inclusive cumulative log-gate b, lane = token (each wave
       // scans all 64); keys are weighted e^{b_end - b_t} for the state
@@ -861,26 +861,22 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
       const int q = 16 * qw + c16;
       if (scores) {
         float rs = 0.f;
-        float ginv[4] = {1.f, 1.f, 1.f, 1.f};  // gamma^(-i), i = 0..3
-        if constexpr (GATE == GT_DECAY) {
-#pragma unroll
-          for (int i = 1; i < 4; ++i) ginv[i] = exp2f(-float(i) * lg2gam);
-        }
         for (int c = 0; c <= qw; ++c) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KP; ++ks)
             acc = mfma16(lds<bf16x8>(sm, LY::k_off + FT::at(16 * c + c16, 4 * ks + g4)), qop[ks], acc);
           // acc[i] = A[q][key], key = 16c + 4g + i
-          float gbase = 1.f;
-          if constexpr (GATE == GT_DECAY) gbase = exp2f(float(q - 16 * c - 4 * g4) * lg2gam);
           float v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = 16 * c + 4 * g4 + i;
             v[i] = acc[i];
+            // RetNet: gamma^(q - key) <= 1 is formed only where key <= q, and
+            // the mask is a select, so no factor above the diagonal (gamma^-15
+            // there overflows for a small gamma) meets a product
+            if constexpr (GATE == GT_DECAY) v[i] *= exp2f(float(max(q - key, 0)) * lg2gam);
             if (c == qw && key > q) v[i] = 0.f;  // only the diagonal tile straddles the mask
-            if constexpr (GATE == GT_DECAY) v[i] *= gbase * ginv[i];
             if constexpr (GATE == GT_SEL) {
               // e^{b_q - b_key} <= 1 below the diagonal; a select (not a
               // product) above it, where the factor may overflow
@@ -1024,7 +1020,7 @@ la_status run_causal(const FwdPlan& p) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
         hipSuccess)
       return LA_ERR_HIP;
-    hipLaunchKernelGGL(k1, dim3(p.P - 1, BH), dim3(64 * Waves<R, E>::NW), lds1, p.stream, a1);
+    LA_LAUNCH(k1, dim3(p.P - 1, BH), dim3(64 * Waves<R, E>::NW), lds1, p.stream, a1);
     if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     la_status st = launch_segment_scan(p);
     if (st != LA_OK) return st;
@@ -1046,7 +1042,7 @@ la_status run_causal(const FwdPlan& p) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k3), hipFuncAttributeMaxDynamicSharedMemorySize, lds3) !=
       hipSuccess)
     return LA_ERR_HIP;
-  hipLaunchKernelGGL(k3, dim3(p.P, BH), dim3(64 * Waves<R, E>::NW), lds3, p.stream, a);
+  LA_LAUNCH(k3, dim3(p.P, BH), dim3(64 * Waves<R, E>::NW), lds3, p.stream, a);
   if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
   return LA_OK;
 }

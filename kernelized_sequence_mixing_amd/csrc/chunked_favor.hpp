@@ -259,7 +259,7 @@ __device__ __forceinline__ void favor_project(const LN& ln, const bf16x8 (&x)[DK
   const int t = 16 * w + ln.c16;
   const bool ok = !IS_K || t < L;
   float wt = 1.f;
-  if constexpr (WEIGHTED) wt = exp2f(float(L - 1 - t) * lg2gam);
+  if constexpr (WEIGHTED) wt = exp2f(float(max(L - 1 - t, 0)) * lg2gam);  // rows past L are dropped
 #pragma unroll
   for (int h = 0; h < F::FT / 2; ++h) {
     float f[2][4];
@@ -620,8 +620,9 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
             for (int i = 0; i < 4; ++i) {
               const int key = 16 * skj[sl] + 4 * ln.g4 + i;
               v[i] = sacc[sl][i];
+              // gamma^(q - key) only where key <= q; the mask selects after it
+              if constexpr (GATE == GT_DECAY) v[i] *= exp2f(float(max(q - key, 0)) * lg2gam);
               if (key > q) v[i] = 0.f;  // only the diagonal tiles straddle the mask
-              if constexpr (GATE == GT_DECAY) v[i] *= exp2f(float(q - key) * lg2gam);
             }
             const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
             typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -720,7 +721,7 @@ la_status run_causal_favor(const FwdPlan& p) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
         hipSuccess)
       return LA_ERR_HIP;
-    hipLaunchKernelGGL(k1, dim3(p.P - 1, BH), dim3(256), lds1, p.stream, a1);
+    LA_LAUNCH(k1, dim3(p.P - 1, BH), dim3(256), lds1, p.stream, a1);
     if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     la_status st = launch_segment_scan(p);
     if (st != LA_OK) return st;
@@ -742,7 +743,7 @@ la_status run_causal_favor(const FwdPlan& p) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k3), hipFuncAttributeMaxDynamicSharedMemorySize, lds3) !=
       hipSuccess)
     return LA_ERR_HIP;
-  hipLaunchKernelGGL(k3, dim3(p.P, BH), dim3(256), lds3, p.stream, a);
+  LA_LAUNCH(k3, dim3(p.P, BH), dim3(256), lds3, p.stream, a);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 

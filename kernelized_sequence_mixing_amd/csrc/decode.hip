@@ -185,10 +185,10 @@ static la_status run_decode(const DecodePlan& p) {
                p.omega, p.gamma,  p.out,      p.H,          p.in_dtype,   p.out_dtype,
                p.gate,  p.eps,    inp ? 1.f / p.tau : 0.f,  p.slot, p.nslot, p.flags};
   if (p.in_dtype == LA_BF16)
-    hipLaunchKernelGGL((decode_step_kernel<R, E, DK, FMAP, bf16>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256), 0,
+    LA_LAUNCH((decode_step_kernel<R, E, DK, FMAP, bf16>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256), 0,
                        p.stream, a);
   else
-    hipLaunchKernelGGL((decode_step_kernel<R, E, DK, FMAP, float>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256),
+    LA_LAUNCH((decode_step_kernel<R, E, DK, FMAP, float>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256),
                        0, p.stream, a);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

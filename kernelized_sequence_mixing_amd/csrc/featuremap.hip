@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void feature_map_kernel(const void* __restrict
 template <int R, int DK, int FMAP>
 static la_status run_fmap(const FmapPlan& p) {
   const long long blocks = (p.rows + 63) / 64;
-  hipLaunchKernelGGL((feature_map_kernel<R, DK, FMAP>), dim3(unsigned(blocks)), dim3(256), 0, p.stream, p.X,
+  LA_LAUNCH((feature_map_kernel<R, DK, FMAP>), dim3(unsigned(blocks)), dim3(256), 0, p.stream, p.X,
                      p.in_dtype, p.rows, p.omega, p.out);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

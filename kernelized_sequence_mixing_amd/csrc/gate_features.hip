@@ -51,7 +51,7 @@ la_status launch_gate_repeat(const void* g, void* gx, long long rows, int r, hip
   if (threads == 0) return LA_OK;
   const long long blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffffLL) return LA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(gate_repeat_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, static_cast<const bf16*>(g),
+  LA_LAUNCH(gate_repeat_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, static_cast<const bf16*>(g),
                      static_cast<bf16*>(gx), rows, r);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
@@ -64,9 +64,9 @@ la_status launch_gate_feature_sum(const void* dgx, void* dg, long long rows, int
   const bf16* src = static_cast<const bf16*>(dgx);
   bf16* dst = static_cast<bf16*>(dg);
   if (r == 64)
-    hipLaunchKernelGGL(gate_feature_sum_kernel<64>, dim3(unsigned(blocks)), dim3(256), 0, stream, src, dst, rows);
+    LA_LAUNCH(gate_feature_sum_kernel<64>, dim3(unsigned(blocks)), dim3(256), 0, stream, src, dst, rows);
   else if (r == 128)
-    hipLaunchKernelGGL(gate_feature_sum_kernel<128>, dim3(unsigned(blocks)), dim3(256), 0, stream, src, dst, rows);
+    LA_LAUNCH(gate_feature_sum_kernel<128>, dim3(unsigned(blocks)), dim3(256), 0, stream, src, dst, rows);
   else
     return LA_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void nc_readout(const void* __restrict__ Q, co
 template <int R, int E, int DK, int FMAP>
 static la_status run_nc(const FwdPlan& p) {
   const unsigned BH = unsigned(p.B) * unsigned(p.H);
-  hipLaunchKernelGGL((nc_partial<R, E, DK, FMAP>), dim3(p.splits, BH), dim3(256), 0, p.stream, p.K, p.V, p.omega,
+  LA_LAUNCH((nc_partial<R, E, DK, FMAP>), dim3(p.splits, BH), dim3(256), 0, p.stream, p.K, p.V, p.omega,
                      p.in_dtype, p.n, p.split_len, p.splits, p.ws_S, p.ws_z);
   if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
   constexpr int lds = (R * E + R + 16 * DK + 16 * R + 16) * 4;
@@ -78,7 +78,7 @@ static la_status run_nc(const FwdPlan& p) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k2), hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
       hipSuccess)
     return LA_ERR_HIP;
-  hipLaunchKernelGGL(k2, dim3((p.n + 63) / 64, BH), dim3(256), lds, p.stream, p.Q, p.omega, p.in_dtype,
+  LA_LAUNCH(k2, dim3((p.n + 63) / 64, BH), dim3(256), lds, p.stream, p.Q, p.omega, p.in_dtype,
                      p.out_dtype, p.n, p.splits, p.eps, p.ws_S, p.ws_z, p.out, p.S_final, p.z_final);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

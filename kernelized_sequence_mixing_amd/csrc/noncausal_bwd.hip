@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void ncb_key(const void* __restrict__ K, const
 template <int R, int E>
 la_status run_nc_backward(const BwdPlan& p) {
   const unsigned BH = unsigned(p.B) * unsigned(p.H);
-  hipLaunchKernelGGL((nc_partial<R, E, R, 0>), dim3(p.splits, BH), dim3(256), 0, p.stream, p.K, p.V, nullptr,
+  LA_LAUNCH((nc_partial<R, E, R, 0>), dim3(p.splits, BH), dim3(256), 0, p.stream, p.K, p.V, nullptr,
                      p.in_dtype, p.n, p.split_len, p.splits, p.ws_S, p.ws_z);
   if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
   constexpr int lds2 = (R * E + R + kTB * R + kTB * R + 2 * kTB * E + 2 * kTB) * 4;
@@ -184,7 +184,7 @@ la_status run_nc_backward(const BwdPlan& p) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k2), hipFuncAttributeMaxDynamicSharedMemorySize, lds2) !=
       hipSuccess)
     return LA_ERR_HIP;
-  hipLaunchKernelGGL(k2, dim3(p.splits, BH), dim3(256), lds2, p.stream, p.Q, p.dO, p.in_dtype, p.n, p.split_len,
+  LA_LAUNCH(k2, dim3(p.splits, BH), dim3(256), lds2, p.stream, p.Q, p.dO, p.in_dtype, p.n, p.split_len,
                      p.splits, p.eps, p.ws_S, p.ws_z, p.ws_R, p.ws_rh, p.dQ);
   if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
   constexpr int lds3 = (R * E + R + kTB * R + kTB * R + kTB * E) * 4;
@@ -192,7 +192,7 @@ la_status run_nc_backward(const BwdPlan& p) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k3), hipFuncAttributeMaxDynamicSharedMemorySize, lds3) !=
       hipSuccess)
     return LA_ERR_HIP;
-  hipLaunchKernelGGL(k3, dim3(p.splits, BH), dim3(256), lds3, p.stream, p.K, p.V, p.in_dtype, p.n, p.split_len,
+  LA_LAUNCH(k3, dim3(p.splits, BH), dim3(256), lds3, p.stream, p.K, p.V, p.in_dtype, p.n, p.split_len,
                      p.splits, p.ws_R, p.ws_rh, p.dK, p.dV);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

@@ -107,6 +107,29 @@ struct FmapPlan {
   hipStream_t stream;
 };
 
+// Launch timing (la_timing_begin / la_timing_end): while a bracket is open on
+// this host thread, every launch first records the next caller-owned event on
+// its stream. Launches past the events supplied are counted, not recorded.
+struct LaunchTimer {
+  void* const* ev;
+  int n;
+  int used;
+  bool failed;
+};
+extern thread_local LaunchTimer* t_launch_timer;
+inline void mark_launch(hipStream_t s) {
+  LaunchTimer* t = t_launch_timer;
+  if (t == nullptr) return;
+  if (t->used < t->n && hipEventRecord(static_cast<hipEvent_t>(t->ev[t->used]), s) != hipSuccess) t->failed = true;
+  t->used++;
+}
+// Every kernel launch of the library goes through this.
+#define LA_LAUNCH(kernel, grid, block, lds, stream, ...)          \
+  do {                                                            \
+    ::la::mark_launch(stream);                                    \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__); \
+  } while (0)
+
 // Launchers (each returns LA_OK or LA_ERR_HIP / LA_ERR_UNSUPPORTED).
 la_status launch_causal_elu1(const FwdPlan& p);
 la_status launch_causal_ssm(const FwdPlan& p);

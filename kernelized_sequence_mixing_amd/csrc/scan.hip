@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* __restrict__ S
 la_status launch_segment_scan(const FwdPlan& p) {
   const int items = p.r * p.dv + p.r;
   dim3 grid((items + 255) / 256, unsigned(p.nseq) * unsigned(p.H));
-  hipLaunchKernelGGL(segment_scan_kernel, grid, dim3(256), 0, p.stream, p.ws_S, p.ws_z, p.ws_logG, p.ws_logGv, p.S0, p.z0,
+  LA_LAUNCH(segment_scan_kernel, grid, dim3(256), 0, p.stream, p.ws_S, p.ws_z, p.ws_logG, p.ws_logGv, p.S0, p.z0,
                      p.gamma, p.slot, p.nslot, p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 0);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
@@ -78,7 +78,7 @@ la_status launch_segment_scan(const FwdPlan& p) {
 la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG) {
   const int items = p.r * p.dv + p.r;
   dim3 grid((items + 255) / 256, unsigned(p.nseq) * unsigned(p.H));
-  hipLaunchKernelGGL(segment_scan_kernel, grid, dim3(256), 0, p.stream, S, z, logG, nullptr, nullptr, nullptr, p.gamma,
+  LA_LAUNCH(segment_scan_kernel, grid, dim3(256), 0, p.stream, S, z, logG, nullptr, nullptr, nullptr, p.gamma,
                      nullptr, 0, p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 1);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

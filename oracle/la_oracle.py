@@ -185,23 +185,24 @@ def _gate_factor_v(gate, t):
 # ---------------------------------------------------------------------------
 
 def noncausal(Q, K, V, fmap="elu1", omega=None, eps=1e-6):
-    """o_i = phi(q_i)^T S / (phi(q_i)^T z + eps), S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j).
+    """Non-causal read-out o_i = phi(q_i).S / (phi(q_i).z + eps) over all keys.
 
-    [LAM-s] "The linear attention trick: drop or approximate the softmax" (the
-    reassociated routine with eps = 1e-6 added to the normaliser); [LAM-d]
-    "The Kernel Trick for Attention" (the S, z formula); [AFA] "Linear
-    Attention (the core trick)".
+    [LAM-d] "The Kernel Trick for Attention": S = sum_j phi(k_j) v_j^T and
+    z = sum_j phi(k_j), both formed once and shared by every query; [AFA]
+    "Linear Attention (the core trick)". The eps added to the denominator
+    follows [LAM-s] "The linear attention trick: drop or approximate the
+    softmax". Here z is kept as the last column of one augmented state: it is
+    the state column of a value that is the constant 1, so a single product
+    phi(q_i)^T [S | z] gives numerator and denominator together.
     """
     if not normalised(fmap):
         raise ValueError("the state-space read-out is defined for the causal form only")
     V = _f64(V)
-    pq = feature_map(Q, fmap, omega)
-    pk = feature_map(K, fmap, omega)
-    S = np.einsum("bhjr,bhje->bhre", pk, V)
-    z = pk.sum(axis=2)
-    num = np.einsum("bhir,bhre->bhie", pq, S)
-    den = np.einsum("bhir,bhr->bhi", pq, z) + eps
-    return num / den[..., None]
+    ones = np.ones(V.shape[:-1] + (1,))
+    Va = np.concatenate([V, ones], axis=-1)                           # [B, H, n, d_v + 1]
+    Sa = np.matmul(np.swapaxes(feature_map(K, fmap, omega), -1, -2), Va)  # [B, H, r, d_v + 1] = [S | z]
+    y = np.matmul(feature_map(Q, fmap, omega), Sa)                    # [B, H, n, d_v + 1]
+    return y[..., :-1] / (y[..., -1:] + eps)
 
 
 # ---------------------------------------------------------------------------
@@ -344,6 +345,91 @@ def causal_recurrent(Q, K, V, fmap="elu1", omega=None, gate=None, eps=1e-6,
             continue
         den = np.einsum("bhr,bhr->bh", pq[:, :, t, :], z) + eps
         out[:, :, t, :] = num / den[..., None]
+    return out, S, z
+
+
+def _step_log_gates(gate, B, H, n, dv):
+    """Per-step log of the state multiplier: (key side [B, H, n, r or 1], value
+    side [B, H, n, d_v] or None). The recurrence multiplies the previous state by
+    exp of these before adding step t (see ``causal_recurrent``)."""
+    kind = "none" if gate is None else gate[0]
+    if kind == "none":
+        return np.zeros((B, H, n, 1)), None
+    if kind == "decay":
+        return np.broadcast_to(np.log(_f64(gate[1])).reshape(1, H, 1, 1), (B, H, n, 1)), None
+    if kind == "gla":
+        return np.log(gla_alpha(gate[1], gate[2])), None
+    if kind == "sel":
+        return np.log(sel_alpha(gate[1], gate[2]))[..., None], None
+    if kind == "outer":
+        return np.log(gla_alpha(gate[1], gate[3])), np.log(outer_beta(gate[2], gate[3]))
+    raise ValueError(f"unknown gate {kind!r}")
+
+
+def causal_blocked(Q, K, V, fmap="elu1", omega=None, gate=None, eps=1e-6, S0=None, z0=None, block=256):
+    """The causal form evaluated block by block; returns (o, S_final, z_final).
+
+    The same quantities as ``causal_recurrent`` ([LAM-d] "Recurrent
+    Reformulation" with the gates of "Gating and Selective State Updates"),
+    grouped into blocks of ``block`` tokens: inside a block the explicit
+    weights W_ij = sum_k phi(q_i)_k phi(k_j)_k D_ijk of ``kernel_weights``
+    (j <= i, D the product of the gates of steps j+1 .. i, formed as the exp of
+    a difference of cumulative log-gates, which is <= 0), and from the blocks
+    before it the carried state, decayed by the gates of steps block start .. i.
+    At the block's end the state takes the block: S <- D_end S + sum_j
+    (phi(k_j) D_end,j) v_j^T (the outer-product gate also decays value column e
+    by its own factors; z takes the key side only). Nothing here is a kernel
+    optimisation: it is the sum of ``kernel_weights`` split at block edges, so
+    that long sequences need O(n block r) memory, and its products run on the
+    host's BLAS. Gates must be > 0 (their logs finite); a gate of exactly zero
+    is the recurrent form's case.
+    """
+    V = _f64(V)
+    norm = normalised(fmap)
+    pq = feature_map(Q, fmap, omega)
+    pk = feature_map(K, fmap, omega)
+    B, H, n, r = pq.shape
+    dv = V.shape[-1]
+    lk, lv = _step_log_gates(gate, B, H, n, dv)
+    S = np.zeros((B, H, r, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros((B, H, r)) if z0 is None else _f64(z0).copy()
+    out = np.empty((B, H, n, dv))
+    for t0 in range(0, n, block):
+        t1 = min(n, t0 + block)
+        L = t1 - t0
+        mask = np.tril(np.ones((L, L), dtype=bool))
+        bk = np.cumsum(lk[:, :, t0:t1], axis=2)                      # [B, H, L, r or 1], from the block start
+        dk = np.where(mask[None, None, :, :, None],
+                      np.exp(np.minimum(bk[:, :, :, None, :] - bk[:, :, None, :, :], 0.0)), 0.0)
+        q_, k_ = pq[:, :, t0:t1], pk[:, :, t0:t1]
+        if dk.shape[-1] == 1:
+            W = np.matmul(q_, np.swapaxes(k_, -1, -2)) * dk[..., 0]
+        else:
+            W = np.matmul(dk * k_[:, :, None, :, :], q_[..., None])[..., 0]   # sum over k, per (i, j)
+        qs = q_ * np.exp(bk)                                         # the carried state's decay to step i
+        v_ = V[:, :, t0:t1]
+        if lv is None:
+            num = np.matmul(W, v_) + np.matmul(qs, S)
+        else:
+            bv = np.cumsum(lv[:, :, t0:t1], axis=2)                  # [B, H, L, d_v]
+            dvv = np.where(mask[None, None, :, :, None],
+                           np.exp(np.minimum(bv[:, :, :, None, :] - bv[:, :, None, :, :], 0.0)), 0.0)
+            num = np.einsum("bhij,bhije,bhje->bhie", W, dvv, v_) + np.matmul(qs, S) * np.exp(bv)
+        if norm:
+            den = W.sum(axis=-1) + np.einsum("bhik,bhk->bhi", qs, z) + eps
+            out[:, :, t0:t1] = num / den[..., None]
+        else:
+            out[:, :, t0:t1] = num
+        # carry the state past the block
+        ek = np.exp(bk[:, :, -1:] - bk)                              # gates of steps j+1 .. block end
+        kd = k_ * ek
+        if lv is None:
+            S = S * np.exp(bk[:, :, -1])[..., None] + np.matmul(np.swapaxes(kd, -1, -2), v_)
+        else:
+            ev = np.exp(bv[:, :, -1:] - bv)
+            S = (S * np.exp(bk[:, :, -1])[..., None] * np.exp(bv[:, :, -1])[:, :, None, :]
+                 + np.matmul(np.swapaxes(kd, -1, -2), v_ * ev))
+        z = z * np.exp(bk[:, :, -1]) + kd.sum(axis=2)
     return out, S, z
 
 

@@ -31,12 +31,3 @@ def rowwise_rel_err(got, ref):
     if np.any(np.isnan(got)):
         return float("inf")
     return float(np.max(rel))
-
-
-def elementwise_max_rel_err(got, ref, floor=1e-30):
-    """Reported beside the gated metric, never gated on."""
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    if got.size == 0:
-        return 0.0
-    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), floor)))

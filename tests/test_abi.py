@@ -424,3 +424,52 @@ def test_batch_workspace_size():
     assert size(1, 40000, FAKE, 10, 4096) == ragged(40000, 10, 4096) == 10 * 16 * 4 * (64 * 64 + 64) * 4
     assert size(1, 8192, FAKE, 64, 4096) == ragged(8192, 64, 4096) > 0 == fwd(64, 4096)
     assert size(1, 40000, FAKE, 64, 128) == 0   # one segment per sequence: no workspace
+
+
+@needs_lib
+@no_gpu
+def test_valid_calls_without_a_device_return_hip_error():
+    """A well-formed call on a host with no GPU gets LA_ERR_HIP from the HIP
+    runtime's refusal, not a crash: every argument passes validation (fake,
+    aligned, non-overlapping device addresses that are never dereferenced),
+    so the first HIP call is the one that fails."""
+    lib = N.lib()
+    at = lambda i: ctypes.c_void_p(0x10000000 * (i + 1))  # 256 MB apart: no two ranges overlap
+    elu = N.LaFeatureMap(N.LA_FMAP_ELU1, 64, None)
+    none = N.LaGate(N.LA_GATE_NONE, 1.0, None, None)
+    for causal, n in ((1, 1000), (0, 1000)):
+        p = N.LaProblem(2, 4, n, 64, 64, N.LA_BF16, N.LA_BF16, 1e-6)
+        ws = ctypes.c_size_t(0)
+        assert lib.la_forward_workspace_size(ctypes.byref(p), ctypes.byref(elu), causal, ctypes.byref(none),
+                                             ctypes.byref(ws)) == N.LA_OK
+        st = lib.la_forward(ctypes.byref(p), at(0), at(1), at(2), ctypes.byref(elu), causal, ctypes.byref(none),
+                            None, None, None, None, at(3), at(4) if ws.value else None, ws.value, None)
+        assert st == N.LA_ERR_HIP, (causal, st)
+    p1 = N.LaProblem(2, 4, 1, 64, 64, N.LA_BF16, N.LA_F32, 1e-6)
+    assert lib.la_decode_step(ctypes.byref(p1), at(0), at(1), at(2), at(3), at(4), ctypes.byref(elu),
+                              ctypes.byref(none), at(5), None) == N.LA_ERR_HIP
+    p = N.LaProblem(2, 4, 1000, 64, 64, N.LA_BF16, N.LA_BF16, 1e-6)
+    ws = ctypes.c_size_t(0)
+    assert lib.la_backward_workspace_size(ctypes.byref(p), ctypes.byref(elu), 1, ctypes.byref(none),
+                                          ctypes.byref(ws)) == N.LA_OK
+    assert lib.la_backward(ctypes.byref(p), at(0), at(1), at(2), at(3), ctypes.byref(elu), 1, ctypes.byref(none),
+                           None, None, at(4), at(5), at(6), None, at(7), ws.value, None) == N.LA_ERR_HIP
+    assert lib.la_feature_map_apply(ctypes.byref(elu), 1000, 64, N.LA_BF16, at(0), at(1), None) == N.LA_ERR_HIP
+
+
+@needs_lib
+def test_timing_bracket_rules():
+    """la_timing_begin / la_timing_end: argument checks and nesting, without a
+    launch (an empty bracket records nothing when no events are given)."""
+    lib = N.lib()
+    n = ctypes.c_int32(-1)
+    assert lib.la_timing_end(None, ctypes.byref(n)) == N.LA_ERR_INVALID_ARG  # none open
+    assert lib.la_timing_begin(None, 2) == N.LA_ERR_INVALID_ARG
+    assert lib.la_timing_begin(None, -1) == N.LA_ERR_INVALID_ARG
+    nulls = (ctypes.c_void_p * 2)(None, None)
+    assert lib.la_timing_begin(nulls, 2) == N.LA_ERR_INVALID_ARG
+    assert lib.la_timing_begin(None, 0) == N.LA_OK
+    assert lib.la_timing_begin(None, 0) == N.LA_ERR_INVALID_ARG  # brackets do not nest
+    assert lib.la_timing_end(None, ctypes.byref(n)) == N.LA_OK
+    assert n.value == 0
+    assert lib.la_timing_end(None, None) == N.LA_ERR_INVALID_ARG

@@ -43,14 +43,41 @@ def test_backward_bytes_per_token():
     assert bench.backward_algorithmic_per_token(WORKLOADS["noncausal_elu1_f32"])[0] == 4 * (2 * 32 + 2 * 32) + 4 * (2 * 32 + 32)
 
 
-def test_traffic_only_for_the_measured_sources(monkeypatch):
-    path = os.path.join(ROOT, "profiles", "traffic_causal_elu1.json")
-    with open(path) as f:
-        rec = json.load(f)
-    # reported for the sources the counters were taken on
-    monkeypatch.setattr(bench, "source_digest", lambda: rec["source_digest"])
-    assert bench.measured_traffic("causal_elu1") == rec["hbm_bytes_per_step"]
+def test_traffic_only_for_the_measured_sources(monkeypatch, tmp_path):
+    """Counter traffic is reported per kernel, and only for the kernel sources
+    the counters were taken on."""
+    (tmp_path / "profiles").mkdir()
+    rec = {"workload": "gla_gate", "source_digest": "abcd" * 4,
+           "kernels": {"causal_chunk_forward": {"hbm_bytes_per_launch": 123456789}}}
+    (tmp_path / "profiles" / "traffic_gla_gate.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_digest", lambda: "abcd" * 4)
+    assert bench.measured_traffic("gla_gate", "causal_chunk_forward") == 123456789
+    assert bench.measured_traffic("gla_gate", "segment_scan_kernel") is None
+    assert bench.measured_traffic("no_such_workload", "causal_chunk_forward") is None
     # any change to the kernel sources voids it
     monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
-    assert bench.measured_traffic("causal_elu1") is None
-    assert bench.measured_traffic("no_such_workload") is None
+    assert bench.measured_traffic("gla_gate", "causal_chunk_forward") is None
+
+
+def test_roofline_takes_the_dominant_kernel(monkeypatch):
+    wl = WORKLOADS["gla_gate"]
+    monkeypatch.setattr(bench, "measured_traffic", lambda w, k: None)
+    res = {"kernels": [{"name": "causal_segment_state", "avg_ms": 0.1}, {"name": "segment_scan_kernel", "avg_ms": 0.01},
+                       {"name": "causal_chunk_forward", "avg_ms": 0.2}],
+           "hbm_alg_GBs": 1.0, "hbm_frac": 0.1, "ms_per_step": 0.31}
+    r = bench.roofline(wl, res)
+    assert r["kernel"] == "causal_chunk_forward"
+    alg = wl.head_tokens * 1280
+    assert r["alg_bytes_per_launch"] == alg
+    assert abs(r["achieved"] - alg / 0.2e-3 / 1e9) < 0.1
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
+
+
+def test_kernel_names_follow_the_plan():
+    assert bench.forward_kernel_names(WORKLOADS["gla_gate"], 8) == [
+        "causal_segment_state", "segment_scan_kernel", "causal_chunk_forward"]
+    assert bench.forward_kernel_names(WORKLOADS["favor_causal"], 1) == ["favor_chunk_forward"]
+    assert bench.forward_kernel_names(WORKLOADS["noncausal_elu1_f32"], 1) == ["nc_partial", "nc_readout"]
+    t = bench.kernel_table([[1.0, 2.0], [3.0, 4.0]], ["a", "b"])
+    assert t == [{"name": "a", "avg_ms": 2.0, "min_ms": 1.0}, {"name": "b", "avg_ms": 3.0, "min_ms": 2.0}]

@@ -533,3 +533,35 @@ def test_outer_gate_decode_steps_equal_recurrence():
                                      ("outer", g[:, :, t], gv[:, :, t], 3.0))
         np.testing.assert_allclose(ot, o[:, :, t], rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(S1, S, rtol=1e-12)
+
+
+# ------------------------------------------------------- blocked form
+
+@pytest.mark.parametrize("fmap", ["elu1", "favor", "identity"])
+@pytest.mark.parametrize("gate", ["none", "decay", "gla", "sel", "outer"])
+def test_blocked_form_equals_recurrent_and_explicit(fmap, gate):
+    """The blocked form (explicit weights inside a block, the carried state
+    across blocks) equals the token recurrence and, without a carried state,
+    the explicit n x n form, for block sizes that split the sequence at and
+    between chunk-like edges, with a ragged last block."""
+    rng = np.random.default_rng(21)
+    B, H, n, d, dv = 2, 3, 37, 8, 5
+    Q = rng.standard_normal((B, H, n, d)) * 0.5
+    K = rng.standard_normal((B, H, n, d)) * 0.5
+    V = rng.standard_normal((B, H, n, dv))
+    omega = rng.standard_normal((16, d)) if fmap == "favor" else None
+    r = 16 if fmap == "favor" else d
+    g = {"none": None, "decay": ("decay", np.array([0.9, 0.5, 0.99])),
+         "gla": ("gla", rng.standard_normal((B, H, n, r)), 2.0), "sel": ("sel", rng.standard_normal((B, H, n)), 2.0),
+         "outer": ("outer", rng.standard_normal((B, H, n, r)), rng.standard_normal((B, H, n, dv)), 2.0)}[gate]
+    S0 = rng.standard_normal((B, H, r, dv))
+    z0 = np.abs(rng.standard_normal((B, H, r))) + 1.0
+    a, Sa, za = orc.causal_recurrent(Q, K, V, fmap, omega, g, 1e-6, S0, z0)
+    ex = orc.brute(Q, K, V, fmap, omega, True, g, 1e-6)
+    for blk in (1, 4, 7, 36, 64):
+        b, Sb, zb = orc.causal_blocked(Q, K, V, fmap, omega, g, 1e-6, S0, z0, block=blk)
+        assert orc.rowwise_rel_err(b, a) < 1e-11
+        assert np.max(np.abs(Sb - Sa)) / np.max(np.abs(Sa)) < 1e-12
+        assert np.max(np.abs(zb - za)) / np.max(np.abs(za)) < 1e-12
+        c, _, _ = orc.causal_blocked(Q, K, V, fmap, omega, g, 1e-6, block=blk)
+        assert orc.rowwise_rel_err(c, ex) < 1e-11

@@ -73,8 +73,9 @@ WORKLOADS = {
         causal=True, gate="none", dtype="bf16", qk_scale=64 ** -0.25, v_scale=1.0),
 }
 
-# The measured headline workload (causal elu+1 forward, bf16, chunk 64).
-HEADLINE = "causal_elu1"
+# The measured headline workload: the largest configuration, the GLA-gated
+# causal elu+1 forward (B2 H16 n16384 d128, bf16, chunk 64).
+HEADLINE = "gla_gate"
 
 
 def describe(wl: Workload) -> str:

@@ -95,6 +95,22 @@ def make_inputs(wl, seed: int = 0, *, B=None, H=None, n=None, qk_scale=None,
     return out
 
 
+def strong_gate_input(shape, seed: int, dtype: str = "bf16", mean: float = -18.75, std: float = 0.25,
+                      period: int = 2, chunk: int = 64) -> torch.Tensor:
+    """A raw gate input of ``shape`` (time on axis 2: [B, H, n, r] or [B, H, n])
+    whose tokens in the chunk-sized blocks 0, period, 2 period, ... of the time
+    axis are N(mean, std^2) and whose other tokens are N(0, 1); period 1 makes
+    every block strong. Both draws are taken in full, in that order, from one
+    seeded generator, then cast like every other input."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    g = rng.standard_normal(shape, dtype=f32)
+    s = rng.standard_normal(shape, dtype=f32) * f32(std) + f32(mean)
+    blk = (np.arange(shape[2]) // chunk) % period == 0
+    sel = blk.reshape((1, 1, -1) + (1,) * (len(shape) - 3))
+    return _cast(np.where(sel, s, g), dtype)
+
+
 def incoming_gradient(shape, seed: int, dtype: str = "bf16", scale: float = 1.0) -> torch.Tensor:
     """A seeded dL/d(out) for the backward pass: N(0,1) * scale, cast like the inputs."""
     rng = np.random.default_rng(seed)
