@@ -10,8 +10,8 @@ work runs in the HIP kernels of ``liblinattn.so`` behind the C ABI declared in
 from ._native import LinattnError, LIB_PATH  # noqa: F401
 from .api import forward, decode_step, feature_map, workspace_size, segments  # noqa: F401
 from .api import PreparedForward, PreparedDecode, backward, PreparedBackward  # noqa: F401
-from .api import forward_batch, PreparedForwardBatch  # noqa: F401
+from .api import forward_batch, PreparedForwardBatch, launch_times  # noqa: F401
 
 __all__ = ["forward", "forward_batch", "PreparedForwardBatch", "backward", "decode_step", "feature_map", "workspace_size", "segments", "PreparedForward",
-           "PreparedBackward", "PreparedDecode",
+           "PreparedBackward", "PreparedDecode", "launch_times",
            "LinattnError", "LIB_PATH"]

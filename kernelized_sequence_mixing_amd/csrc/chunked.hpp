@@ -181,7 +181,9 @@ struct FwdLayout {
   static constexpr int k_off = q_off + FTB;
   static constexpr int v_off = k_off + FTB;
   static constexpr int kh_off = v_off + FeatTile<E, SWZ>::BYTES;
-  static constexpr int a_off = kh_off + (kScalarDecay<GATE> ? FTB : 0);
+  // K^ rows of the state update: RetNet and the selective gate weight each key
+  // row; the outer-product gate references its keys to the chunk end
+  static constexpr int a_off = kh_off + (kScalarDecay<GATE> || GATE == GT_OUTER ? FTB : 0);
   static constexpr int z_off = a_off + FeatTile<kChunk, SWZ>::BYTES;
   static constexpr int gam_off = z_off + R * 4;
   static constexpr int rs_off = gam_off + R * 4;   // [64] score row sums
@@ -413,7 +415,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
 #pragma unroll
     for (int j = 0; j < Raw::FR / 8; ++j) {
       const int f0 = w * Raw::FR + 8 * j;
-      float vq[8], vk[8], dq[8], dk[8];
+      float vq[8], vk[8], vkh[8], dq[8], dk[8];
       // base 2: bs[u] is the chunk's inclusive cumulative log2-gate of feature f0 + u
       float bs[8];
       if constexpr (kKeyGate<GATE>) {
@@ -432,8 +434,11 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
           const float eb = __builtin_amdgcn_exp2f(b), emb = __builtin_amdgcn_exp2f((EXTRA & kPreKPos) != 0 ? b : -b);
           if constexpr ((EXTRA & kPreQD) != 0) dq[u] = eb * phi_ew_deriv<FMAP>(pq);
           if constexpr ((EXTRA & kPreKD) != 0) dk[u] = emb * phi_ew_deriv<FMAP>(pk);
+          // the outer-product gate's state update takes K^ = e^{b_end - b} phi(k) <= 1
+          // (with its value side e^{-c} on top, e^{-b} would overflow first)
+          if constexpr (GATE == GT_OUTER) vkh[u] = pk * __builtin_amdgcn_exp2f(bend - b);
           pq *= eb;
-          pk *= emb;  // K^ = e^{b_end} K~: applied to the state row after the update
+          pk *= emb;  // K^ = e^{b_end} K~: applied to the state row after the update (GLA)
           my_bend = lane == 8 * j + u ? bend : my_bend;
         }
         vq[u] = pq;
@@ -442,8 +447,15 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       const int fo = FT::at(t, f0 / 8);
       if constexpr (WITH_Q)
         lds<bf16x8>(sm, q_off + fo) = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
-      lds<bf16x8>(sm, k_off + fo) =
-          keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
+      if constexpr (GATE == GT_OUTER) {
+        // pass 3: K~ for the scores and K^ for the state; pass 1: K^ only
+        const bf16x8 khr =
+            keep_if(valid, cat8(pack4(vkh[0], vkh[1], vkh[2], vkh[3]), pack4(vkh[4], vkh[5], vkh[6], vkh[7])));
+        lds<bf16x8>(sm, (WITH_Q ? kh_off : k_off) + fo) = khr;
+      }
+      if (GATE != GT_OUTER || WITH_Q)
+        lds<bf16x8>(sm, k_off + fo) =
+            keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
       if constexpr (kKeyGate<GATE> && (EXTRA & kPreQD) != 0)
         lds<bf16x8>(sm, qd_off + fo) = cat8(pack4(dq[0], dq[1], dq[2], dq[3]), pack4(dq[4], dq[5], dq[6], dq[7]));
       if constexpr (kKeyGate<GATE> && (EXTRA & kPreKD) != 0)
@@ -536,8 +548,8 @@ struct ZTiles {
 //   no gate   S <- S + K~^T V                    z <- z + K~^T 1
 //   RetNet    S <- gamma^L S + K^^T V            (kh_off holds K^ rows)
 //   GLA       S <- Gamma (S + K~^T V)            Gamma = diag(e^{b_end}) from gam_off
-//   outer     S <- Gamma (S + K~^T V~) Gamma_v   Gamma_v = diag(e^{c_end}) from gamv_off,
-//             V~ as hi + lo (vl_off holds lo)
+//   outer     S <- (Gamma S + K^^T V~) Gamma_v   Gamma_v = diag(e^{c_end}) from gamv_off,
+//             K^ = Gamma K~ (kh_off), V~ as hi + lo (vl_off holds lo)
 // Both operands come from [token][column] tiles by transpose reads.
 // S is f32x4[R / 16][E / (16 NW)], Z is f32x4[ZTiles<R, NW>::ZT].
 // With ZW the z column uses per-token weights (fp32 [64] at zw_off) instead of
@@ -579,7 +591,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
       f32x4 st = S[rt][eb];
-      if constexpr (kScalarDecay<GATE> || (kKeyGate<GATE> && PRE)) {
+      if constexpr (kScalarDecay<GATE> || (kKeyGate<GATE> && PRE) || GATE == GT_OUTER) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[i] *= gr[i];
       }
@@ -588,13 +600,13 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
       if constexpr (GATE == GT_OUTER) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vbl[eb][ks], st);
-      }
-      if constexpr (kKeyGate<GATE> && !PRE) {
-        // the outer-product gate: also the column's value-side factor
-        float gc = 1.f;
-        if constexpr (GATE == GT_OUTER) gc = lds<float>(sm, gamv_off + 4 * (ebase + 16 * eb + (lane & 15)));
+        // the column's value-side factor
+        const float gc = lds<float>(sm, gamv_off + 4 * (ebase + 16 * eb + (lane & 15)));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[i] *= gr[i] * gc;
+        for (int i = 0; i < 4; ++i) st[i] *= gc;
+      } else if constexpr (kKeyGate<GATE> && !PRE) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[i] *= gr[i];
       }
       S[rt][eb] = st;
     }
@@ -610,7 +622,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
 #pragma unroll
         for (int i = 0; i < 4; ++i) gr[i] = lds<float>(sm, gam_off + 4 * (16 * rt + 4 * g4 + i));
       }
-      if constexpr (kScalarDecay<GATE> || (kKeyGate<GATE> && PRE)) {
+      if constexpr (kScalarDecay<GATE> || (kKeyGate<GATE> && PRE) || GATE == GT_OUTER) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
@@ -624,7 +636,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
         }
         zt = mfma16(tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane), zb, zt);
       }
-      if constexpr (kKeyGate<GATE> && !PRE) {  // z takes the key side only
+      if constexpr (GATE == GT_GLA && !PRE) {  // z takes the key side only
 #pragma unroll
         for (int i = 0; i < 4; ++i) zt[i] *= gr[i];
       }
@@ -959,7 +971,8 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_chunk_forward(C
     // ---- carry the state past this chunk
     float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
     if constexpr (GATE == GT_SEL) gsc = __expf(lds<float>(sm, LY::bs_off + 4 * 63));
-    state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, kScalarDecay<GATE> ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
+    state_update<R, E, GATE, NW, LY::SWZ>(S, Z, sm, kScalarDecay<GATE> || GATE == GT_OUTER ? LY::kh_off : LY::k_off,
+                                 LY::v_off, LY::gam_off,
                                  gsc, lane, w, 0, LY::gamv_off, LY::vl_off);
     z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);  // old z no longer read this chunk
     lds_barrier();
