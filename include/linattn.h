@@ -343,6 +343,26 @@ la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t
                                int32_t in_dtype, const void* X, float* out, void* stream);
 
 /*
+ * la_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation). Arguments, results and errors are those of
+ * la_forward; the scratch memory la_forward would take as `workspace` is a
+ * fixed device array of LA_NOALLOC_SCRATCH_BYTES inside the library instead,
+ * one per GPU, held until the process ends. A problem whose
+ * la_forward_workspace_size exceeds that size returns LA_ERR_WORKSPACE (use
+ * la_forward with a workspace). Nothing is allocated, not even on the first
+ * call on a device (which only looks up the array's address). Every call on
+ * one GPU uses the same array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and give undefined results; calls in
+ * stream order are safe (no part of the array needs to be cleared).
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (32u << 20)
+la_status la_forward_noalloc(const la_problem* p, const void* Q, const void* K, const void* V,
+                             const la_feature_map* fmap, int32_t causal, const la_gate* gate,
+                             const float* S0, const float* z0, float* S_final, float* z_final,
+                             void* out, void* stream);
+
+/*
  * Launch timing, for profiling (computes nothing). la_timing_begin opens a
  * bracket on the calling host thread; until la_timing_end on the same thread,
  * every kernel launch the library makes first records events[i] on its stream

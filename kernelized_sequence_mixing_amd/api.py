@@ -141,8 +141,10 @@ def segments(B, H, n, d_k, d_v, *, fmap="elu1", r=None, causal=True, gate_kind="
     return P.value, L.value
 
 
-def _forward_args(Q, K, V, fmap, omega, causal, gate, eps, S0, z0, return_state, out_dtype, out, workspace, stream):
-    """Validate and marshal one la_forward call: (ctypes argument tuple, keep-alive objects, out, S_final, z_final)."""
+def _forward_args(Q, K, V, fmap, omega, causal, gate, eps, S0, z0, return_state, out_dtype, out, workspace, stream,
+                  noalloc=False):
+    """Validate and marshal one la_forward call: (ctypes argument tuple, keep-alive objects, out, S_final, z_final).
+    noalloc: the arguments of la_forward_noalloc instead (no workspace)."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
         _dev(t, nm)
     if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
@@ -171,6 +173,10 @@ def _forward_args(Q, K, V, fmap, omega, causal, gate, eps, S0, z0, return_state,
     if return_state:
         Sf = torch.empty((B, H, r, d_v), dtype=torch.float32, device=Q.device)
         zf = torch.empty((B, H, r), dtype=torch.float32, device=Q.device)
+    if noalloc:
+        args = (ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(f), int(bool(causal)), ctypes.byref(g),
+                _ptr(S0), _ptr(z0), _ptr(Sf), _ptr(zf), _ptr(out), _stream(Q, stream))
+        return args, (p, f, g, Q, K, V, omega, gate, S0, z0), out, Sf, zf
     ws_bytes = ctypes.c_size_t(0)
     N.check(N.lib().la_forward_workspace_size(ctypes.byref(p), ctypes.byref(f), int(bool(causal)), ctypes.byref(g),
                                               ctypes.byref(ws_bytes)), "la_forward_workspace_size")
@@ -195,6 +201,23 @@ def forward(Q, K, V, *, fmap="elu1", omega=None, causal=True, gate=None, eps=1e-
                                              out_dtype, out, workspace, stream)
     N.check(N.lib().la_forward(*args), "la_forward")
     return (out, Sf, zf) if return_state else out
+
+
+def forward_noalloc(Q, K, V, *, fmap="elu1", omega=None, causal=True, gate=None, eps=1e-6, S0=None, z0=None,
+                    out=None, S_final=None, z_final=None, stream=None):
+    """forward() through la_forward_noalloc: the library's own fixed scratch
+    array instead of a workspace. `out` (and S_final, z_final, to receive the
+    final state) must be given: this call allocates nothing."""
+    if out is None:
+        raise ValueError("forward_noalloc allocates nothing: pass out")
+    if (S_final is None) != (z_final is None):
+        raise ValueError("S_final and z_final go together")
+    args, _keep, out, _, _ = _forward_args(Q, K, V, fmap, omega, causal, gate, eps, S0, z0, False, out.dtype, out,
+                                           None, stream, noalloc=True)
+    if S_final is not None:
+        args = args[:9] + (_ptr(S_final), _ptr(z_final)) + args[11:]
+    N.check(N.lib().la_forward_noalloc(*args), "la_forward_noalloc")
+    return out
 
 
 class PreparedForward:
