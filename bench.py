@@ -406,6 +406,49 @@ def cpu_baseline(wl, heads=16, block=64, max_threads=16):
             "host_cores_available": cores, "cpu_model": model, "blas": blas}
 
 
+CROSSOVER_N = (1024, 2048, 4096, 8192, 16384, 32768)
+
+
+def bench_softmax(n, steps, warmup, B=4, H=16, d=64):
+    """The softmax-attention baseline (la_softmax_attention, causal, bf16) at
+    B4 H16 d64 and sequence length n: the quadratic form linear attention
+    replaces. Flops per head: 2 n^2 d (the scores and the weighted values, each
+    2 n^2 d / 2 over the causal triangle)."""
+    import kernelized_sequence_mixing_amd as ksm
+    wl = WORKLOADS["causal_elu1"].resized(name=f"softmax_n{n}", B=B, H=H, n=n, qk_scale=1.0, v_scale=1.0)
+    inp = make_inputs(wl, seed=0)
+    per_set = B * H * n * 4 * d * 2
+    sets = _device_sets(inp, ["Q", "K", "V"], per_set)
+    outs = [torch.empty_like(s["V"]) for s in sets]
+    stream = torch.cuda.current_stream()
+    calls = [ksm.PreparedSoftmax(s["Q"], s["K"], s["V"], causal=True, out=outs[i], stream=stream)
+             for i, s in enumerate(sets)]
+    ms, med = time_steps(lambda i: calls[i](), len(sets), steps, warmup, stream)
+    flops = 2.0 * n * n * d * B * H
+    tfl = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"softmax_causal_n{n}", "ms_per_step": round(ms, 5), "median_ms": round(med, 5),
+            "value": B * H * n / (ms * 1e-3), "unit": "head-tokens/s", "input_sets_rotated": len(sets),
+            "mfma_alg_TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4),
+            "score_matrix_fp16_bytes_per_head": n * n * 2,
+            "shape": {"B": B, "H": H, "n": n, "d": d, "causal": True}}
+
+
+def bench_crossover(steps, warmup):
+    """Softmax attention and causal elu+1 linear attention at the same B4 H16
+    d64 for each n of CROSSOVER_N: head-tokens/s of both, and the ratio."""
+    rows = []
+    for n in CROSSOVER_N:
+        st = max(3, steps // (n // 4096 + 1)) if n > 4096 else steps
+        sm = bench_softmax(n, st, min(warmup, 2), d=64)
+        lin = bench_forward(WORKLOADS["causal_elu1"].resized(name=f"causal_elu1_n{n}", n=n), st, min(warmup, 2))
+        rows.append({"n": n, "softmax_head_tokens_per_s": sm["value"], "softmax_ms": sm["ms_per_step"],
+                     "softmax_mfma_frac": sm["mfma_frac"], "linear_head_tokens_per_s": lin["value"],
+                     "linear_ms": lin["ms_per_step"], "linear_over_softmax": round(lin["value"] / sm["value"], 3)})
+        print(f"crossover n={n}: softmax {sm['ms_per_step']:.4f} ms ({sm['mfma_frac']:.3f} of MFMA peak), "
+              f"linear {lin['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
+    return {"workload": "crossover_softmax_vs_linear_B4_H16_d64", "rows": rows}
+
+
 def run_only(name, steps, warmup):
     """One workload's record alone (for per-workload profiles)."""
     if name in WORKLOADS and not WORKLOADS[name].decode:
@@ -416,6 +459,10 @@ def run_only(name, steps, warmup):
         return bench_serve_prefill(steps, warmup)
     if name in ("serve_decode_m1", "serve_decode_m4"):
         return bench_serve_decode(WORKLOADS["gla_decode"], int(name[-1]), steps, warmup)
+    if name.startswith("softmax_n"):
+        return bench_softmax(int(name[len("softmax_n"):]), steps, warmup)
+    if name == "crossover":
+        return bench_crossover(steps, warmup)
     if name.endswith("_backward") and name[:-len("_backward")] in BACKWARD_WORKLOADS:
         return bench_backward(BACKWARD_WORKLOADS[name[:-len("_backward")]], steps, warmup)
     raise SystemExit(f"unknown workload {name!r}")
@@ -527,6 +574,7 @@ def main():
         for bw in BACKWARD_WORKLOADS.values():
             extra.append(bench_backward(bw, args.steps, args.warmup))
             print(f"{bw.name} backward: {extra[-1]['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+        extra.append(bench_crossover(args.steps, args.warmup))
         line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -343,6 +343,24 @@ la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t
                                int32_t in_dtype, const void* X, float* out, void* stream);
 
 /*
+ * Softmax attention, the quadratic baseline that linear attention replaces
+ * ("Standard Self-Attention: The Quadratic Baseline", dileepadev page: every
+ * query scores every key and a row softmax of the n x n scores weights the
+ * values), for measuring where the linear forms overtake it ("When to Use
+ * Linear Attention", same page):
+ *   o_i = sum_j softmax_j(scale q_i . k_j) v_j  over j <= i (causal) or all j.
+ *   Q, K, V, out [B][H][n][d] BF16 (in_dtype and out_dtype BF16, d = d_k = d_v
+ *   in {64, 128}, else LA_ERR_UNSUPPORTED); scale > 0 and finite (1/sqrt(d) is
+ *   the usual temperature); eps is not used.
+ * The n x n scores are never stored: they are formed block by block (64 keys
+ * at a time) on bf16 MFMA with fp32 accumulation, with the online softmax's
+ * running maximum and row sums in fp32 and the weights rounded to bf16 for the
+ * weighted sum. out must not overlap the inputs (LA_ERR_ALIAS). No workspace.
+ */
+la_status la_softmax_attention(const la_problem* p, const void* Q, const void* K, const void* V,
+                               int32_t causal, float scale, void* out, void* stream);
+
+/*
  * la_forward without a caller workspace, for callers that cannot allocate
  * device memory (code under graph capture, tight serving loops, harnesses
  * that forbid allocation). Arguments, results and errors are those of

@@ -11,8 +11,8 @@ from ._native import LinattnError, LIB_PATH  # noqa: F401
 from .api import forward, decode_step, feature_map, workspace_size, segments  # noqa: F401
 from .api import PreparedForward, PreparedDecode, backward, PreparedBackward  # noqa: F401
 from .api import forward_batch, PreparedForwardBatch, launch_times  # noqa: F401
-from .api import forward_noalloc  # noqa: F401
+from .api import forward_noalloc, softmax_attention, PreparedSoftmax  # noqa: F401
 
 __all__ = ["forward", "forward_batch", "PreparedForwardBatch", "backward", "decode_step", "feature_map", "workspace_size", "segments", "PreparedForward",
-           "PreparedBackward", "PreparedDecode", "launch_times", "forward_noalloc",
+           "PreparedBackward", "PreparedDecode", "launch_times", "forward_noalloc", "softmax_attention", "PreparedSoftmax",
            "LinattnError", "LIB_PATH"]

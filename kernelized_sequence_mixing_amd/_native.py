@@ -21,7 +21,7 @@ LA_SLOT_READ, LA_SLOT_WRITE = 1, 2
 EXPORTED = ("la_abi_version", "la_status_str", "la_forward_workspace_size", "la_forward_segments",
             "la_forward", "la_forward_batch_workspace_size", "la_forward_batch", "la_backward_workspace_size",
             "la_backward", "la_decode_step", "la_feature_map_apply", "la_timing_begin", "la_timing_end",
-            "la_forward_noalloc")
+            "la_forward_noalloc", "la_softmax_attention")
 LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -98,6 +98,9 @@ def lib():
     L.la_forward_noalloc.argtypes = [POINTER(LaProblem), c_void_p, c_void_p, c_void_p, POINTER(LaFeatureMap),
                                      c_int32, POINTER(LaGate), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p]
+    L.la_softmax_attention.restype = c_int32
+    L.la_softmax_attention.argtypes = [POINTER(LaProblem), c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
+                                       c_void_p]
     L.la_timing_begin.restype = c_int32
     L.la_timing_begin.argtypes = [POINTER(c_void_p), c_int32]
     L.la_timing_end.restype = c_int32

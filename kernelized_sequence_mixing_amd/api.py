@@ -475,6 +475,51 @@ def feature_map(X, *, fmap="elu1", omega=None, stream=None):
     return out
 
 
+def _softmax_args(Q, K, V, causal, scale, out, stream):
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
+        _dev(t, nm)
+    if Q.dim() != 4 or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError(f"Q, K, V must share one [B, H, n, d] shape, got {tuple(Q.shape)} {tuple(K.shape)} "
+                         f"{tuple(V.shape)}")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K, V must share a dtype")
+    B, H, n, d = Q.shape
+    scale = d ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(V)
+    else:
+        _dev(out, "out")
+        if out.shape != V.shape or out.dtype != V.dtype:
+            raise ValueError("out has the wrong shape or dtype")
+    p = _problem(B, H, n, d, d, _dt(Q), _dt(out), 0.0)
+    args = (ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), int(bool(causal)), scale, _ptr(out), _stream(Q, stream))
+    return args, (p, Q, K, V), out
+
+
+def softmax_attention(Q, K, V, *, causal=True, scale=None, out=None, stream=None):
+    """Softmax attention (the quadratic baseline) through la_softmax_attention:
+    o_i = sum_j softmax_j(scale q_i . k_j) v_j, bf16 [B, H, n, d], d in {64, 128};
+    scale defaults to 1/sqrt(d)."""
+    args, _keep, out = _softmax_args(Q, K, V, causal, scale, out, stream)
+    N.check(N.lib().la_softmax_attention(*args), "la_softmax_attention")
+    return out
+
+
+class PreparedSoftmax:
+    """One la_softmax_attention call marshalled once (same arguments as
+    softmax_attention); calling the object launches it again."""
+
+    def __init__(self, Q, K, V, *, causal=True, scale=None, out=None, stream=None):
+        self._args, self._keep, self.out = _softmax_args(Q, K, V, causal, scale, out, stream)
+        self._fn = N.lib().la_softmax_attention
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            N.check(st, "la_softmax_attention")
+        return self.out
+
+
 def launch_times(call, steps, stream, max_launches=8):
     """GPU time of every kernel launch of `steps` calls of `call()` (a prepared
     call on `stream`), through la_timing_begin / la_timing_end: each call runs

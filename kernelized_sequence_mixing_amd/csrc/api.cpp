@@ -746,6 +746,26 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   return sel ? launch_gate_feature_sum(ws + wl.dgx_off, dg, (long long)(BH * n), fmap->r, plan.stream) : LA_OK;
 }
 
+la_status la_softmax_attention(const la_problem* p, const void* Q, const void* K, const void* V, int32_t causal,
+                               float scale, void* out, void* stream) {
+  la_status st = check_problem(p);
+  if (st != LA_OK) return st;
+  if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return LA_ERR_INVALID_ARG;
+  if (Q == nullptr || K == nullptr || V == nullptr || out == nullptr) return LA_ERR_INVALID_ARG;
+  for (const void* ptr : {Q, K, V, (const void*)out})
+    if (!aligned16(ptr)) return LA_ERR_INVALID_ARG;
+  if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (p->d_k != p->d_v || !in_set(p->d_k, {64, 128})) return LA_ERR_UNSUPPORTED;
+  const size_t bytes = (size_t)p->B * p->H * p->n * p->d_k * 2;
+  const Range ro = range_of(out, bytes);
+  for (Range i : {range_of(Q, bytes), range_of(K, bytes), range_of(V, bytes)})
+    if (overlaps(ro, i)) return LA_ERR_ALIAS;
+  if ((long long)p->B * p->H * ((p->n + 127) / 128) > 0x7fffffffLL) return LA_ERR_UNSUPPORTED;
+  SoftmaxPlan plan{p->B, p->H, p->n, p->d_k, causal, scale, Q, K, V, out, static_cast<hipStream_t>(stream)};
+  return launch_softmax(plan);
+}
+
 la_status la_timing_begin(void* const* events, int32_t n_events) {
   if (n_events < 0 || (n_events > 0 && events == nullptr)) return LA_ERR_INVALID_ARG;
   if (t_launch_timer != nullptr) return LA_ERR_INVALID_ARG;  // brackets do not nest

@@ -107,6 +107,17 @@ struct FmapPlan {
   hipStream_t stream;
 };
 
+// Softmax attention (the quadratic baseline): bf16 [B][H][n][d] in and out.
+struct SoftmaxPlan {
+  int B, H, n, d, causal;
+  float scale;
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* out;
+  hipStream_t stream;
+};
+
 // Launch timing (la_timing_begin / la_timing_end): while a bracket is open on
 // this host thread, every launch first records the next caller-owned event on
 // its stream. Launches past the events supplied are counted, not recorded.
@@ -141,6 +152,7 @@ la_status launch_noncausal_backward(const BwdPlan& p);  // ws_S, ws_z: partial S
 la_status launch_noncausal(const FwdPlan& p);
 la_status launch_decode(const DecodePlan& p);
 la_status launch_feature_map(const FmapPlan& p);
+la_status launch_softmax(const SoftmaxPlan& p);
 // The selective scalar gate's backward: repeat g [rows] over r features, and
 // sum the per-feature gradient [rows][r] back to [rows].
 la_status launch_gate_repeat(const void* g, void* gx, long long rows, int r, hipStream_t stream);
