@@ -58,6 +58,22 @@ __device__ __forceinline__ float phi_ew(float x) {
   if constexpr (FMAP == FM_IDENT) return x;
   else return elu1(x);
 }
+// phi(x) 2^s in one exponential, and the factor e = phi'(x) 2^s: for elu+1,
+// (x + 1) 2^s above zero and 2^(x log2(e) + s) below (phi' = 1 above, e^x
+// below, so e is the exponential itself); for the identity, x 2^s and 2^s.
+// The gated preludes need phi(q) e^{b}, phi(k) e^{-b} and e^{b} phi'(q), ...:
+// one transcendental each instead of one for phi and one for the gate.
+template <int FMAP>
+__device__ __forceinline__ float phi_times_exp2(float x, float s, float& e) {
+  if constexpr (FMAP == FM_IDENT) {
+    e = __builtin_amdgcn_exp2f(s);
+    return x * e;
+  } else {
+    const bool pos = x > 0.f;
+    e = __builtin_amdgcn_exp2f(pos ? s : __builtin_fmaf(x, kLog2e, s));
+    return pos ? (x + 1.f) * e : e;
+  }
+}
 // Its derivative from the feature value: min(phi, 1) for elu+1 (1 above zero,
 // exp(x) = phi below), 1 for the identity.
 template <int FMAP>
@@ -425,21 +441,30 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        float pq = WITH_Q ? phi_ew<FMAP>(to_f32(raw.q[WITH_Q ? j : 0][u])) : 0.f;
-        float pk = phi_ew<FMAP>(to_f32(raw.k[j][u]));
+        const float xq = WITH_Q ? to_f32(raw.q[WITH_Q ? j : 0][u]) : 0.f;
+        const float xk = to_f32(raw.k[j][u]);
+        float pq, pk;
         if constexpr (kKeyGate<GATE>) {
           const float b = bs[u];
           // the chunk total is uniform across the wave: a scalar read of lane 63
           const float bend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b), 63));
-          const float eb = __builtin_amdgcn_exp2f(b), emb = __builtin_amdgcn_exp2f((EXTRA & kPreKPos) != 0 ? b : -b);
-          if constexpr ((EXTRA & kPreQD) != 0) dq[u] = eb * phi_ew_deriv<FMAP>(pq);
-          if constexpr ((EXTRA & kPreKD) != 0) dk[u] = emb * phi_ew_deriv<FMAP>(pk);
+          // Q~ = phi(q) e^{b}, K~ = phi(k) e^{-b} (K^ = e^{b_end} K~ is applied to
+          // the state row after the update for GLA); eq = e^{b} phi'(q), ek = e^{-b} phi'(k)
+          float eq = 0.f, ek;
+          pq = WITH_Q ? phi_times_exp2<FMAP>(xq, b, eq) : 0.f;
+          pk = phi_times_exp2<FMAP>(xk, (EXTRA & kPreKPos) != 0 ? b : -b, ek);
+          if constexpr ((EXTRA & kPreQD) != 0) dq[u] = eq;
+          if constexpr ((EXTRA & kPreKD) != 0) dk[u] = ek;
           // the outer-product gate's state update takes K^ = e^{b_end - b} phi(k) <= 1
           // (with its value side e^{-c} on top, e^{-b} would overflow first)
-          if constexpr (GATE == GT_OUTER) vkh[u] = pk * __builtin_amdgcn_exp2f(bend - b);
-          pq *= eb;
-          pk *= emb;  // K^ = e^{b_end} K~: applied to the state row after the update (GLA)
+          if constexpr (GATE == GT_OUTER) {
+            float unused;
+            vkh[u] = phi_times_exp2<FMAP>(xk, bend - b, unused);
+          }
           my_bend = lane == 8 * j + u ? bend : my_bend;
+        } else {
+          pq = WITH_Q ? phi_ew<FMAP>(xq) : 0.f;
+          pk = phi_ew<FMAP>(xk);
         }
         vq[u] = pq;
         vk[u] = pk;
