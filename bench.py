@@ -361,7 +361,7 @@ def _host_info():
     return cpu, blas
 
 
-def cpu_baseline(wl, heads=16, block=64, max_threads=16):
+def cpu_baseline(wl, heads=32, block=64, max_threads=16):
     """The fp64 oracle's blocked form (oracle.causal_blocked, numpy) on the
     host: a bounded sample of `heads` whole heads of the workload (full
     sequence length), one head per worker thread, every thread running its
@@ -468,9 +468,12 @@ def run_only(name, steps, warmup):
     raise SystemExit(f"unknown workload {name!r}")
 
 
-# the backward lines: the headline shape of the ungated form, the GLA workload's sequence
-# shape at d_k = d_v = 64, the state-space form under both selective gates, non-causal
+# the backward lines: the GLA and RetNet workloads at their own shapes (128 x 128 states, two
+# value-column halves), the ungated elu+1 shape, the GLA sequence shape at d_k = d_v = 64, the
+# state-space form under both selective gates, non-causal
 BACKWARD_WORKLOADS = {
+    "gla_gate": WORKLOADS["gla_gate"],
+    "retnet_decay": WORKLOADS["retnet_decay"],
     "causal_elu1": WORKLOADS["causal_elu1"],
     "gla_gate_d64": WORKLOADS["gla_gate"].resized(name="gla_gate_d64", d_k=64, d_v=64, r=64, qk_scale=64 ** -0.5,
                                                   v_scale=64 ** -0.5),

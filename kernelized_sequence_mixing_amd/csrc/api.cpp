@@ -17,6 +17,8 @@ thread_local LaunchTimer t_timer_slot;
 
 constexpr size_t kAlign = 256;
 
+typedef uint16_t bf16_bits;  // element type for pointer offsets into bf16 arrays
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -238,12 +240,18 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
   if (gk == LA_GATE_OUTER) return LA_ERR_UNSUPPORTED;
   if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   const int key = p->d_k * 1000 + p->d_v;
-  if (key != 64064 && key != 64128 && key != 128064) return LA_ERR_UNSUPPORTED;
+  if (key != 64064 && key != 64128 && key != 128064 && key != 128128) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 
+// (d_k, d_v) = (128, 128) runs the (128, 64) kernels on the two halves of the
+// value columns: every gradient is linear in g = dO / den and h = -(dO . o) /
+// den, and both split into per-half sums (h = h_1 + h_2), so dQ, dK and dg are
+// the sums of the halves' and dV their concatenation.
+bool backward_in_halves(const la_problem* p) { return p->d_k == 128 && p->d_v == 128; }
+
 struct BwdWsLayout {
-  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, gx_off, dgx_off, bytes;
+  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, gx_off, dgx_off, s0h_off, bytes;
   int P, L;
 };
 
@@ -264,8 +272,11 @@ BwdWsLayout nc_bwd_workspace_layout(const la_problem* p, const la_feature_map* f
   return w;
 }
 
-BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, int gate, int causal = 1) {
-  if (!causal) return nc_bwd_workspace_layout(p, f);
+BwdWsLayout bwd_workspace_layout(const la_problem* p_in, const la_feature_map* f, int gate, int causal = 1) {
+  if (!causal) return nc_bwd_workspace_layout(p_in, f);
+  la_problem half = *p_in;
+  if (backward_in_halves(p_in)) half.d_v = p_in->d_v / 2;  // the halves run one after the other
+  const la_problem* p = &half;
   BwdWsLayout w{};
   // the selective gate runs the GLA passes, on their segment plan
   plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate == LA_GATE_SEL ? LA_GATE_GLA : gate, &w.P,
@@ -281,15 +292,18 @@ BwdWsLayout bwd_workspace_layout(const la_problem* p, const la_feature_map* f, i
   w.dB_off = round_up(w.h_off + BH * n * 4, kAlign);
   if (gate != LA_GATE_GLA && gate != LA_GATE_SEL) {
     w.logG_off = w.gx_off = w.dgx_off = w.bytes = w.dB_off;
-    return w;
+  } else {
+    const size_t n64 = (n + 63) / 64 * 64;  // dQ~ . Q~ is stored by whole chunks
+    w.logG_off = round_up(w.dB_off + BH * n64 * r * 4, kAlign);
+    w.gx_off = w.dgx_off = w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
+    if (gate == LA_GATE_SEL) {
+      w.dgx_off = round_up(w.gx_off + BH * n * r * 2, kAlign);
+      w.bytes = round_up(w.dgx_off + BH * n * r * 2, kAlign);
+    }
   }
-  const size_t n64 = (n + 63) / 64 * 64;  // dQ~ . Q~ is stored by whole chunks
-  w.logG_off = round_up(w.dB_off + BH * n64 * r * 4, kAlign);
-  w.gx_off = w.dgx_off = w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
-  if (gate == LA_GATE_SEL) {
-    w.dgx_off = round_up(w.gx_off + BH * n * r * 2, kAlign);
-    w.bytes = round_up(w.dgx_off + BH * n * r * 2, kAlign);
-  }
+  // value-column halves: one half of a carried-in state at a time, dense
+  w.s0h_off = w.bytes;
+  if (backward_in_halves(p_in)) w.bytes = round_up(w.s0h_off + BH * r * dv * 4, kAlign);
   return w;
 }
 
@@ -742,7 +756,28 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
     if ((st = launch_gate_repeat(gate->g, ws + wl.gx_off, (long long)(BH * n), fmap->r, plan.stream)) != LA_OK)
       return st;
   }
-  if ((st = launch_backward(plan)) != LA_OK) return st;
+  if (backward_in_halves(p)) {
+    const int half = p->d_v / 2;
+    BwdPlan hp = plan;
+    hp.dv = half;
+    hp.ldv = p->d_v;
+    float* s0h = reinterpret_cast<float*>(ws + wl.s0h_off);
+    for (int k = 0; k < 2; ++k) {
+      hp.V = static_cast<const bf16_bits*>(V) + k * half;
+      hp.dO = static_cast<const bf16_bits*>(dO) + k * half;
+      hp.dV = static_cast<bf16_bits*>(dV) + k * half;
+      hp.accum = k;
+      if (S0 != nullptr) {  // this half's columns of the carried-in state, dense ([BH][r][half]); z0 is shared
+        if (hipMemcpy2DAsync(s0h, half * sizeof(float), S0 + k * half, p->d_v * sizeof(float), half * sizeof(float),
+                             BH * r, hipMemcpyDeviceToDevice, plan.stream) != hipSuccess)
+          return LA_ERR_HIP;
+        hp.S0 = s0h;
+      }
+      if ((st = launch_backward(hp)) != LA_OK) return st;
+    }
+  } else if ((st = launch_backward(plan)) != LA_OK) {
+    return st;
+  }
   return sel ? launch_gate_feature_sum(ws + wl.dgx_off, dg, (long long)(BH * n), fmap->r, plan.stream) : LA_OK;
 }
 

@@ -29,6 +29,8 @@ static la_status run_backward(const BwdPlan& p) {
   b.dQ = static_cast<bf16*>(p.dQ);
   b.dK = static_cast<bf16*>(p.dK);
   b.dV = static_cast<bf16*>(p.dV);
+  b.ldv = p.ldv > 0 ? p.ldv : E;
+  b.accum = p.accum;
   b.H = p.H;
   b.n = p.n;
   b.P = p.P;
@@ -48,6 +50,7 @@ static la_status run_backward(const BwdPlan& p) {
     a1.Q = b.Q;
     a1.K = b.K;
     a1.V = b.V;
+    a1.ldv = b.ldv;
     a1.gamma = p.gamma;
     a1.H = p.H;
     a1.n = p.n;
@@ -113,7 +116,8 @@ static la_status run_backward_fmap(const BwdPlan& p) {
 }
 
 // Built shapes: elu+1 or the state-space form with (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}; no gate,
-// RetNet decay or GLA.
+// RetNet decay or GLA. (128, 128) runs as two (128, 64) halves of the value
+// columns (la_backward).
 la_status launch_backward(const BwdPlan& p) {
   switch (p.r * 1000 + p.dv) {
     case 64064: return run_backward_fmap<64, 64>(p);

@@ -64,9 +64,23 @@ struct BwdArgs {
   float* dB;       // dQ~ . Q~ (pass A, read by pass B), in the order of dbq_at
   float* logG;     // [B H P R] summed log-gate of each segment (bwd_rstate_gla)
   bf16* dg;        // [B H n R]
+  int ldv;         // elements between rows of V, dO and dV (a value-column half of a wider V)
+  int accum;       // add dQ, dK, dg to what the arrays hold (the second value-column half)
   int H, n, P, seg_len;
   float eps, inv_tau;
 };
+
+// Four gradient entries stored as bf16, or added to the stored ones (the
+// gradients are sums over value columns; a wide V runs in column halves).
+__device__ __forceinline__ void store_grad4(bf16* p, const float (&x)[4], bool accum) {
+  float y[4] = {x[0], x[1], x[2], x[3]};
+  if (accum) {
+    const bf16x4 o = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) y[u] += to_f32(o[u]);
+  }
+  *reinterpret_cast<bf16x4*>(p) = pack4(y[0], y[1], y[2], y[3]);
+}
 
 // Index (floats) of the four features 16 ft + 4 g .. + 3 of token 16 it + c of
 // chunk ch (chunks counted from the head's first token) in the GLA workspace of
@@ -85,10 +99,11 @@ __device__ __forceinline__ long long dbq_at(long long bh, int n, int ch, int ft,
 template <int E>
 struct RowsE {
   bf16x8 v[E / 32];
-  __device__ __forceinline__ void load(const bf16* X, long long tok0, int t0, int row_end, int lane, int w) {
+  __device__ __forceinline__ void load(const bf16* X, long long ld, long long tok0, int t0, int row_end, int lane,
+                                       int w) {
     const long long row = tok0 + min(t0 + 16 * w + lane / 4, row_end - 1);
 #pragma unroll
-    for (int j = 0; j < E / 32; ++j) v[j] = *reinterpret_cast<const bf16x8*>(X + row * E + 8 * (lane % 4 + 4 * j));
+    for (int j = 0; j < E / 32; ++j) v[j] = *reinterpret_cast<const bf16x8*>(X + row * ld + 8 * (lane % 4 + 4 * j));
   }
   // into a FeatTile<E> tile; rows >= L are zero
   __device__ __forceinline__ void store(char* sm, int off, int L, int lane, int w) const {
@@ -197,6 +212,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   ca.Q = b.Q;
   ca.K = b.K;
   ca.V = b.V;
+  ca.ldv = b.ldv;
   ca.g = b.gl;
   ca.inv_tau = b.inv_tau;
 
@@ -205,7 +221,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   Raw raw;
   RowsE<E> rdo;
   raw.load(ca, tok0, t_begin, t_end, lane, w);
-  rdo.load(b.dO, tok0, t_begin, t_end, lane, w);
+  rdo.load(b.dO, b.ldv, tok0, t_begin, t_end, lane, w);
 
   // ---- forward state entering the segment
   f32x4 S[R / 16][NEB];
@@ -238,7 +254,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     rdo.store(sm, LY::g_off, L, lane, w);
     state_image<R, E>(S, sm, LY::sb_off, lane, w);
     raw.load(ca, tok0, t0 + kChunk, t_end, lane, w);
-    rdo.load(b.dO, tok0, t0 + kChunk, t_end, lane, w);
+    rdo.load(b.dO, b.ldv, tok0, t0 + kChunk, t_end, lane, w);
     lds_barrier();
 
     // ---- scores A (masked, RetNet-weighted) and their row sums; phi(q) . z
@@ -390,7 +406,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
             dq[u2] = dphi * phi_ew_deriv<FMAP>(to_f32(ph[u2]));
           }
         }
-        if (i < L) *reinterpret_cast<bf16x4*>(b.dQ + (tok0 + t0 + i) * R + f0) = pack4(dq[0], dq[1], dq[2], dq[3]);
+        if (i < L) store_grad4(b.dQ + (tok0 + t0 + i) * R + f0, dq, b.accum != 0);
         if constexpr (GATE == GT_GLA)
           *reinterpret_cast<f32x4*>(b.dB + dbq_at<R>(bh, b.n, t0 / kChunk, ft, it, lane)) = db;
       }
@@ -561,6 +577,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   ca.Q = b.Q;
   ca.K = b.K;
   ca.V = b.V;
+  ca.ldv = b.ldv;
   ca.g = b.gl;
   ca.inv_tau = b.inv_tau;
   // the chunk's tiles: plain features (RetNet weights are applied per product)
@@ -621,7 +638,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   auto load = [&](int ci) {
     const int t0 = t_begin + ci * kChunk;
     raw.load(ca, tok0, t0, t_end, lane, w);
-    rg.load(b.G, tok0, t0, t_end, lane, w);
+    rg.load(b.G, E, tok0, t0, t_end, lane, w);
     hv = b.h[tok0 + min(t0 + lane, t_end - 1)];
   };
   load(nch - 1);
@@ -737,7 +754,8 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
             acc = mfma16(tr_feat<E, true>(sm, LY::g_off, 32 * p, e, lane),
                          lds<bf16x8>(sm, LY::w_off + AT::at(j, 4 * p + g4)), acc);
           if (j < L)
-            *reinterpret_cast<bf16x4*>(b.dV + (tok0 + t0 + j) * E + e + 4 * g4) = pack4(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<bf16x4*>(b.dV + (tok0 + t0 + j) * b.ldv + e + 4 * g4) =
+                pack4(acc[0], acc[1], acc[2], acc[3]);
         }
       }
     }
@@ -798,7 +816,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
             dk[u2] = dphi * phi_ew_deriv<FMAP>(to_f32(ph[u2]));
           }
         }
-        if (j < L) *reinterpret_cast<bf16x4*>(b.dK + (tok0 + t0 + j) * R + f0) = pack4(dk[0], dk[1], dk[2], dk[3]);
+        if (j < L) store_grad4(b.dK + (tok0 + t0 + j) * R + f0, dk, b.accum != 0);
         if constexpr (GATE == GT_GLA) {
           // ---- dg: d log alpha_t = (d log alpha after the tile) + sum of dB over
           // the tile's tokens t' >= t (the row of 16 lanes holds tokens 16 jt + c
@@ -814,7 +832,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
             o[u2] = (carry[u][u2] + ((tot - pre) + x)) * b.inv_tau * __builtin_amdgcn_rcpf(1.f + __expf(to_f32(gv[u2])));
             carry[u][u2] += tot;
           }
-          if (j < L) *reinterpret_cast<bf16x4*>(b.dg + (tok0 + t0 + j) * R + f0) = pack4(o[0], o[1], o[2], o[3]);
+          if (j < L) store_grad4(b.dg + (tok0 + t0 + j) * R + f0, o, b.accum != 0);
         }
       }
     }

@@ -117,6 +117,7 @@ struct CausalArgs {
   const int* slot;
   int nslot;
   int in_is_state;         // S_in is the caller's carried state (indexed like S_out), not the segment workspace
+  int ldv;                 // elements between rows of V (0: d_v, dense); the backward's value-column halves
   int H, n, P, seg_len;
   float eps, inv_tau;
 };
@@ -306,6 +307,7 @@ struct RawChunk {
   // unconditionally.
   __device__ __forceinline__ void load(const CausalArgs& a, long long tok0, int t0, int row_end, int lane, int w) {
     const int g4 = lane >> 4, c16 = lane & 15;
+    const long long ldv = a.ldv > 0 ? a.ldv : E;
     if constexpr (GATE == GT_SEL) sg = a.g[tok0 + min(t0 + lane, row_end - 1)];
     if constexpr (ROWMAJOR) {
       const long long row = tok0 + min(t0 + TPW * w + lane / LPT, row_end - 1);
@@ -317,7 +319,7 @@ struct RawChunk {
       }
 #pragma unroll
       for (int j = 0; j < E / (8 * LPT); ++j)
-        v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * E + 8 * (lane % LPT + LPT * j));
+        v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * ldv + 8 * (lane % LPT + LPT * j));
       return;
     }
     {
@@ -334,7 +336,7 @@ struct RawChunk {
         for (int j = 0; j < FR / 8; ++j) g[j] = *reinterpret_cast<const bf16x8*>(a.g + row * R + w * FR + 8 * j);
       }
 #pragma unroll
-      for (int j = 0; j < EV / 8; ++j) v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * E + w * EV + 8 * j);
+      for (int j = 0; j < EV / 8; ++j) v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * ldv + w * EV + 8 * j);
       if constexpr (GATE == GT_OUTER) {
 #pragma unroll
         for (int j = 0; j < EV / 8; ++j) gv[j] = *reinterpret_cast<const bf16x8*>(a.gv + row * E + w * EV + 8 * j);

@@ -73,6 +73,9 @@ struct BwdPlan : FwdPlan {
   // GLA gate
   void* dg;      // [BH][n][r] out_dtype
   float* ws_dB;  // [BH][ceil(n / 64) * 64][r] in the kernels' own order
+  // a value-column half of a wider V: elements between rows of V, dO and dV
+  // (0: dv), and whether dQ, dK, dg are added to (the second half) or stored
+  int ldv, accum;
 };
 
 struct DecodePlan {

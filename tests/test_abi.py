@@ -297,7 +297,7 @@ BAD_BACKWARD = [
      N.LA_ERR_ALIAS),
     ("gla favor", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP, fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP),
      dict(dg=FAKE + 14 * SP), N.LA_ERR_UNSUPPORTED),
-    ("d 128x128", dict(d_k=128, r=128, d_v=128), {}, N.LA_ERR_UNSUPPORTED),
+    ("d_v 32", dict(d_v=32), {}, N.LA_ERR_UNSUPPORTED),
     ("d_k 32", dict(d_k=32, r=32), {}, N.LA_ERR_UNSUPPORTED),
     ("fp32", dict(in_dt=N.LA_F32, out_dt=N.LA_F32), {}, N.LA_ERR_UNSUPPORTED),
     ("decay no gamma", dict(gkind=N.LA_GATE_DECAY), {}, N.LA_ERR_INVALID_ARG),
@@ -344,6 +344,19 @@ def test_backward_workspace_size():
     # the selective gate runs the GLA passes on g repeated over features: that copy and its
     # per-feature gradient (bf16 each) come on top
     assert size(4, 16, n, 64, 64, N.LA_GATE_SEL) == size(4, 16, n, 64, 64, N.LA_GATE_GLA) + 2 * BH * n * 64 * 2
+
+    def size128(B, H, n, dv, gk=N.LA_GATE_NONE):
+        p = N.LaProblem(B, H, n, 128, dv, N.LA_BF16, N.LA_BF16, 1e-6)
+        f = N.LaFeatureMap(N.LA_FMAP_ELU1, 128, None)
+        g = N.LaGate(gk, 16.0, None, None)
+        out = ctypes.c_size_t(0)
+        assert lib.la_backward_workspace_size(ctypes.byref(p), ctypes.byref(f), 1, ctypes.byref(g),
+                                              ctypes.byref(out)) == N.LA_OK
+        return out.value
+    # 128 x 128 states run as two (128, 64) halves of the value columns, one after the other, on
+    # the halves' workspace, plus one half of a carried-in state (fp32 [BH][128][64])
+    for gk in (N.LA_GATE_NONE, N.LA_GATE_GLA):
+        assert size128(2, 16, 16384, 128, gk) == size128(2, 16, 16384, 64, gk) + 32 * 128 * 64 * 4
 
 
 # ------------------------------------------------------------------ serving batch (validation, no launch)

@@ -118,7 +118,8 @@ def _case(gate, d, dv, B, H, n, seed=3):
 CASES = [("none", 64, 64, 2, 4, 200), ("none", 64, 64, 2, 4, 777), ("decay", 64, 64, 2, 4, 777),
          ("none", 64, 64, 4, 16, 1285), ("decay", 64, 64, 4, 16, 1285), ("none", 128, 64, 2, 4, 300),
          ("decay", 64, 128, 2, 4, 300), ("none", 64, 64, 1, 1, 1), ("none", 64, 64, 2, 1, 63),
-         ("decay", 64, 64, 2, 1, 65)]
+         ("decay", 64, 64, 2, 1, 65), ("none", 128, 128, 2, 4, 777), ("decay", 128, 128, 2, 8, 1285),
+         ("none", 128, 128, 1, 1, 65)]
 
 
 @pytest.mark.parametrize("gate,d,dv,B,H,n", CASES)
@@ -130,15 +131,16 @@ def test_backward_parity_small(gate, d, dv, B, H, n):
     check_grads(got, oracle_backward(inp, dO), term_scales(inp, dO), f"{gate} d{d}x{dv} B{B} H{H} n{n}")
 
 
-@pytest.mark.parametrize("gate", ["none", "decay"])
-def test_backward_with_carried_state(gate):
-    """The forward's carried-in state enters dQ (and g, h, hence every gradient)."""
-    wl, inp, dO = _case(gate, 64, 64, 4, 16, 700, seed=9)
+@pytest.mark.parametrize("gate,d", [("none", 64), ("decay", 64), ("decay", 128)])
+def test_backward_with_carried_state(gate, d):
+    """The forward's carried-in state enters dQ (and g, h, hence every gradient);
+    at 128 x 128 each value-column half takes its own half of it."""
+    wl, inp, dO = _case(gate, d, d, 4, 16, 700, seed=9)
     rng = np.random.default_rng(77)
-    S0 = torch.from_numpy((rng.standard_normal((4, 16, 64, 64)) * 2.0).astype(np.float32))
-    z0 = torch.from_numpy((20.0 + 2.0 * np.abs(rng.standard_normal((4, 16, 64)))).astype(np.float32))
+    S0 = torch.from_numpy((rng.standard_normal((4, 16, d, d)) * 2.0).astype(np.float32))
+    z0 = torch.from_numpy((20.0 + 2.0 * np.abs(rng.standard_normal((4, 16, d)))).astype(np.float32))
     got = run_backward(inp, dO, S0, z0)
-    check_grads(got, oracle_backward(inp, dO, S0, z0), term_scales(inp, dO, S0, z0), f"carried state {gate}")
+    check_grads(got, oracle_backward(inp, dO, S0, z0), term_scales(inp, dO, S0, z0), f"carried state {gate} d{d}")
 
 
 def test_backward_headline_full_size():

@@ -1,5 +1,6 @@
-"""Full-size parity of the gated backward pass, in the launch configuration
-the benchmark times (B2 H16 n16384 d64): sampled gradient entries of two heads
+"""Full-size parity of the gated backward pass, in the launch configurations
+the benchmark times (B2 H16 n16384 at d64 and at the GLA workload's own
+d128, which runs as two value-column halves): sampled gradient entries of two heads
 against the fp64 oracle's per-row form (oracle.la_backward.backward_gla_rows,
 pinned against the explicit form), for the GLA gate with elu+1, and the
 state-space form under the GLA and the selective scalar gate.
@@ -69,7 +70,8 @@ def sampled_scales(Q, K, V, dO, G, tau, fmap, den, o, rows, tail):
     return s_q, s_k, s_v, s_g
 
 
-CASES = [("gla_gate_d64", "elu1", "gla"), ("ssm_selective", "identity", "gla"), ("ssm_scalar", "identity", "sel")]
+CASES = [("gla_gate_d64", "elu1", "gla"), ("ssm_selective", "identity", "gla"), ("ssm_scalar", "identity", "sel"),
+         ("gla_gate", "elu1", "gla")]
 
 
 @pytest.mark.parametrize("name,fmap,gate", CASES)

@@ -143,7 +143,7 @@ def _case(d, dv, B, H, n, seed=3):
 
 
 CASES = [(64, 64, 2, 4, 777), (64, 64, 4, 16, 1285), (128, 64, 2, 4, 300), (64, 128, 2, 4, 300),
-         (64, 64, 2, 4, 200), (64, 64, 1, 1, 1), (64, 64, 2, 1, 65)]
+         (64, 64, 2, 4, 200), (64, 64, 1, 1, 1), (64, 64, 2, 1, 65), (128, 128, 2, 4, 777), (128, 128, 4, 16, 300)]
 
 
 @pytest.mark.parametrize("d,dv,B,H,n", CASES)
@@ -164,6 +164,16 @@ def test_backward_gla_with_carried_state():
     z0 = torch.from_numpy((20.0 + 2.0 * np.abs(rng.standard_normal((4, 16, 64)))).astype(np.float32))
     got = run_backward_gla(inp, dO, S0, z0)
     check_heads(got, inp, dO, [(0, 0), (3, 15)], "gla carried state", S0, z0)
+
+
+def test_backward_gla_128_with_carried_state():
+    """128 x 128 states (two value-column halves, each with its half of the carried state)."""
+    wl, inp, dO = _case(128, 128, 2, 4, 500, seed=10)
+    rng = np.random.default_rng(78)
+    S0 = torch.from_numpy((rng.standard_normal((2, 4, 128, 128)) * 2.0).astype(np.float32))
+    z0 = torch.from_numpy((20.0 + 2.0 * np.abs(rng.standard_normal((2, 4, 128)))).astype(np.float32))
+    got = run_backward_gla(inp, dO, S0, z0)
+    check_heads(got, inp, dO, [(0, 0), (1, 3)], "gla 128x128 carried state", S0, z0)
 
 
 def test_backward_gla_deterministic():

@@ -71,7 +71,7 @@ def check_heads(got, inp, dO, heads, what, fmap, S0=None, z0=None):
 
 CASES = [(f, d, dv, B, H, n) for f in ("elu1", "identity")
          for (d, dv, B, H, n) in ((64, 64, 2, 4, 777), (64, 64, 2, 4, 1285), (128, 64, 2, 2, 300),
-                                  (64, 128, 2, 2, 300), (64, 64, 2, 1, 65))]
+                                  (64, 128, 2, 2, 300), (64, 64, 2, 1, 65), (128, 128, 2, 2, 300))]
 
 
 @pytest.mark.parametrize("fmap,d,dv,B,H,n", CASES)

@@ -31,7 +31,7 @@ def _case(gate, d, dv, B, H, n, seed=3):
 
 CASES = [(g, d, dv, B, H, n) for g in ("none", "decay")
          for (d, dv, B, H, n) in ((64, 64, 2, 4, 777), (64, 128, 2, 4, 300), (128, 64, 2, 4, 300),
-                                  (64, 64, 4, 16, 1285), (64, 64, 2, 1, 65))]
+                                  (64, 64, 4, 16, 1285), (64, 64, 2, 1, 65), (128, 128, 2, 4, 777))]
 
 
 @pytest.mark.parametrize("gate,d,dv,B,H,n", CASES)
@@ -53,7 +53,7 @@ def test_ssm_backward_carried_state():
 
 
 GLA_CASES = [(64, 64, 2, 4, 777), (64, 64, 4, 16, 1285), (128, 64, 2, 4, 300), (64, 128, 2, 4, 300),
-             (64, 64, 2, 1, 65)]
+             (64, 64, 2, 1, 65), (128, 128, 2, 4, 300)]
 
 
 @pytest.mark.parametrize("d,dv,B,H,n", GLA_CASES)
