@@ -305,26 +305,30 @@ def backward_algorithmic_per_token(wl):
     flops = half * 2 * wl.r * 3 + half * 2 * wl.d_v * 3 + 6 * 2 * wl.r * wl.d_v
     if not wl.causal:  # the non-causal form: S, G and the per-token products, no scores
         flops = 6 * 2 * wl.r * wl.d_v
+    if wl.fmap == "favor":  # phi(q), phi(k) and their pullbacks: four r x d_k products per token
+        flops += 4 * 2 * wl.r * wl.d_k
     return nbytes, flops
 
 
 def bench_backward(wl, steps, warmup):
-    """la_backward on workload wl (causal, elu+1 or identity features): one step is one
-    full backward pass (with a gate input it includes dg)."""
+    """la_backward on workload wl (causal; elu+1, FAVOR+ or identity features): one step is
+    one full backward pass (with a gate input it includes dg; with FAVOR+ the feature
+    materialisation and the pass back through the map)."""
     import kernelized_sequence_mixing_amd as ksm
     from workloads import incoming_gradient
     inp = make_inputs(wl, seed=0)
     inp["dO"] = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1, dtype=wl.dtype)
     nb_tok, fl_tok = backward_algorithmic_per_token(wl)
     per_set = wl.head_tokens * nb_tok
-    sets = _device_sets(inp, ["Q", "K", "V", "dO", "gamma", "g"], per_set)
+    sets = _device_sets(inp, ["Q", "K", "V", "dO", "gamma", "g", "omega"], per_set)
     gate_of = {"none": lambda s: None, "decay": lambda s: ("decay", s["gamma"]),
                "gla": lambda s: ("gla", s["g"], wl.tau), "sel": lambda s: ("sel", s["g"], wl.tau)}[wl.gate]
     grads = [(torch.empty_like(s["Q"]), torch.empty_like(s["K"]), torch.empty_like(s["V"])) +
              ((torch.empty_like(s["g"]),) if wl.gate in ("gla", "sel") else ()) for s in sets]
     stream = torch.cuda.current_stream()
-    calls = [ksm.PreparedBackward(s["Q"], s["K"], s["V"], s["dO"], fmap=wl.fmap, gate=gate_of(s), eps=wl.eps,
-                                  grads=grads[i], stream=stream, causal=wl.causal) for i, s in enumerate(sets)]
+    calls = [ksm.PreparedBackward(s["Q"], s["K"], s["V"], s["dO"], fmap=wl.fmap, omega=s.get("omega"),
+                                  gate=gate_of(s), eps=wl.eps, grads=grads[i], stream=stream, causal=wl.causal)
+             for i, s in enumerate(sets)]
 
     def step(i):
         calls[i]()
@@ -470,7 +474,8 @@ def run_only(name, steps, warmup):
 
 # the backward lines: the GLA and RetNet workloads at their own shapes (128 x 128 states, two
 # value-column halves), the ungated elu+1 shape, the GLA sequence shape at d_k = d_v = 64, the
-# state-space form under both selective gates, non-causal
+# state-space form under both selective gates, non-causal, FAVOR+ at the causal FAVOR+ shape with
+# r = 128 (the widest feature count the backward builds)
 BACKWARD_WORKLOADS = {
     "gla_gate": WORKLOADS["gla_gate"],
     "retnet_decay": WORKLOADS["retnet_decay"],
@@ -480,6 +485,7 @@ BACKWARD_WORKLOADS = {
     "ssm_selective": WORKLOADS["ssm_selective"],
     "ssm_scalar": WORKLOADS["ssm_scalar"],
     "noncausal_elu1_f32": WORKLOADS["noncausal_elu1_f32"],
+    "favor_r128": WORKLOADS["favor_causal"].resized(name="favor_r128", r=128),
 }
 
 

@@ -305,7 +305,13 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  * the gradients in that dtype, the forward's (d_k, d_v) set; fp32 arithmetic.
  * Supported (else LA_ERR_UNSUPPORTED) for causal == 1: ELU1 or IDENTITY (the
  * state-space read-out: g_i = dO_i, h_i = 0, phi' = 1), gate NONE, DECAY, GLA
- * or SEL (not OUTER), (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}. Outputs must not overlap the
+ * or SEL (not OUTER), (d_k, d_v) in {(64, 64), (64, 128), (128, 64), (128, 128)}
+ * (128 x 128 runs as two 64-column value halves); FAVOR ("Choosing the Feature
+ * Map phi", dileepadev page) with gate NONE or DECAY, d_k in {32, 64, 128},
+ * r in {64, 128}, (r, d_v) in the same set: phi(Q), phi(K) are materialised in
+ * bf16 in the workspace, the passes above give dphi, and
+ *   dx = sum_m dphi_m phi_m (w_m - x)
+ * takes it back through the map (fp32, omega as given). Outputs must not overlap the
  * inputs, each other or the workspace (LA_ERR_ALIAS). Numerics as la_forward:
  * bf16 MFMA operands (phi, values, g, the scores and dW), fp32 accumulation,
  * states, denominators and the sums behind dg.

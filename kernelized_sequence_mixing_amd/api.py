@@ -334,7 +334,7 @@ class PreparedForwardBatch:
         return self.out
 
 
-def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream, causal=True):
+def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream, causal=True, omega=None):
     """Validate and marshal one la_backward call: (ctypes arguments, keep-alive objects, gradients), the
     gradients being (dQ, dK, dV), plus dg with a gate input (GLA, selective)."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (dO, "dO")):
@@ -346,7 +346,7 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
         raise TypeError("Q, K, V, dO must share a dtype")
     B, H, n, d_k = Q.shape
     d_v = V.shape[3]
-    f, r = _fmap_struct(fmap, None, d_k, Q.dtype)
+    f, r = _fmap_struct(fmap, omega, d_k, Q.dtype)
     g = _gate_struct(gate, (B, H, n, r), d_v, Q.dtype)
     p = _problem(B, H, n, d_k, d_v, _dt(Q), _dt(Q), eps)
     for t, nm, shp in ((S0, "S0", (B, H, r, d_v)), (z0, "z0", (B, H, r))):
@@ -376,20 +376,22 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
     args = (ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), ctypes.byref(f), int(bool(causal)), ctypes.byref(g),
             _ptr(S0),
             _ptr(z0), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dg), _ptr(workspace), need, _stream(Q, stream))
-    keep = (p, f, g, Q, K, V, dO, gate, S0, z0, workspace)
+    keep = (p, f, g, Q, K, V, dO, gate, S0, z0, workspace, omega)
     return args, keep, tuple(grads)
 
 
-def backward(Q, K, V, dO, *, fmap="elu1", gate=None, eps=1e-6, S0=None, z0=None, grads=None, workspace=None,
-             stream=None, causal=True):
+def backward(Q, K, V, dO, *, fmap="elu1", omega=None, gate=None, eps=1e-6, S0=None, z0=None, grads=None,
+             workspace=None, stream=None, causal=True):
     """(dQ, dK, dV) of the causal forward for an incoming gradient dO, through la_backward;
     (dQ, dK, dV, dg) with the GLA or the selective gate, dg the gradient of its raw input g.
 
     Q, K [B, H, n, d_k]; V, dO [B, H, n, d_v] (bf16); gate None | ("decay", gamma[H]) |
     ("gla", g[B, H, n, d_k] bf16, tau) | ("sel", g[B, H, n] bf16, tau); S0, z0: the forward's
-    carried-in state, if any. causal=False: the non-causal form (elu+1, no gate, no state;
-    fp32 or bf16, gradients in the input dtype)."""
-    args, _keep, grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream, causal)
+    carried-in state, if any. fmap="favor" with omega [r, d_k] (r 64 or 128; no gate or the
+    decay). causal=False: the non-causal form (elu+1, no gate, no state; fp32 or bf16,
+    gradients in the input dtype)."""
+    args, _keep, grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream, causal,
+                                        omega)
     N.check(N.lib().la_backward(*args), "la_backward")
     return grads
 
@@ -398,10 +400,10 @@ class PreparedBackward:
     """One la_backward call marshalled once (same arguments as backward);
     calling the object launches it again on the same buffers and stream."""
 
-    def __init__(self, Q, K, V, dO, *, fmap="elu1", gate=None, eps=1e-6, S0=None, z0=None, grads=None,
+    def __init__(self, Q, K, V, dO, *, fmap="elu1", omega=None, gate=None, eps=1e-6, S0=None, z0=None, grads=None,
                  workspace=None, stream=None, causal=True):
         self._args, self._keep, self.grads = _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace,
-                                                            stream, causal)
+                                                            stream, causal, omega)
         self._fn = N.lib().la_backward
 
     def __call__(self):

@@ -236,22 +236,28 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
     if (f->kind != LA_FMAP_ELU1 || p->in_dtype != p->out_dtype) return LA_ERR_UNSUPPORTED;
     return shapes_built(f, p->d_k, p->d_v, false) ? LA_OK : LA_ERR_UNSUPPORTED;
   }
-  if (f->kind != LA_FMAP_ELU1 && f->kind != LA_FMAP_IDENTITY) return LA_ERR_UNSUPPORTED;
   if (gk == LA_GATE_OUTER) return LA_ERR_UNSUPPORTED;
   if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
-  const int key = p->d_k * 1000 + p->d_v;
+  if (f->kind == LA_FMAP_FAVOR) {
+    // the chunked kernels on the materialised features (r wide), then back through the map
+    if (gk != LA_GATE_NONE && gk != LA_GATE_DECAY) return LA_ERR_UNSUPPORTED;
+    if (!in_set(p->d_k, {32, 64, 128})) return LA_ERR_UNSUPPORTED;
+  } else if (f->kind != LA_FMAP_ELU1 && f->kind != LA_FMAP_IDENTITY) {
+    return LA_ERR_UNSUPPORTED;
+  }
+  const int key = f->r * 1000 + p->d_v;
   if (key != 64064 && key != 64128 && key != 128064 && key != 128128) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 
-// (d_k, d_v) = (128, 128) runs the (128, 64) kernels on the two halves of the
+// (r, d_v) = (128, 128) runs the (128, 64) kernels on the two halves of the
 // value columns: every gradient is linear in g = dO / den and h = -(dO . o) /
 // den, and both split into per-half sums (h = h_1 + h_2), so dQ, dK and dg are
 // the sums of the halves' and dV their concatenation.
-bool backward_in_halves(const la_problem* p) { return p->d_k == 128 && p->d_v == 128; }
+bool backward_in_halves(const la_problem* p, int r) { return r == 128 && p->d_v == 128; }
 
 struct BwdWsLayout {
-  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, gx_off, dgx_off, s0h_off, bytes;
+  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, gx_off, dgx_off, s0h_off, fv_off, bytes;
   int P, L;
 };
 
@@ -275,7 +281,7 @@ BwdWsLayout nc_bwd_workspace_layout(const la_problem* p, const la_feature_map* f
 BwdWsLayout bwd_workspace_layout(const la_problem* p_in, const la_feature_map* f, int gate, int causal = 1) {
   if (!causal) return nc_bwd_workspace_layout(p_in, f);
   la_problem half = *p_in;
-  if (backward_in_halves(p_in)) half.d_v = p_in->d_v / 2;  // the halves run one after the other
+  if (backward_in_halves(p_in, f->r)) half.d_v = p_in->d_v / 2;  // the halves run one after the other
   const la_problem* p = &half;
   BwdWsLayout w{};
   // the selective gate runs the GLA passes, on their segment plan
@@ -303,7 +309,10 @@ BwdWsLayout bwd_workspace_layout(const la_problem* p_in, const la_feature_map* f
   }
   // value-column halves: one half of a carried-in state at a time, dense
   w.s0h_off = w.bytes;
-  if (backward_in_halves(p_in)) w.bytes = round_up(w.s0h_off + BH * r * dv * 4, kAlign);
+  if (backward_in_halves(p_in, f->r)) w.bytes = round_up(w.s0h_off + BH * r * dv * 4, kAlign);
+  // FAVOR+: phi(Q), phi(K) and their gradients, bf16 [BH][n][r] each
+  w.fv_off = w.bytes;
+  if (f->kind == LA_FMAP_FAVOR) w.bytes = round_up(w.fv_off + 4 * BH * n * r * 2, kAlign);
   return w;
 }
 
@@ -692,11 +701,12 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
   const Range rgl = range_of(gate_has_input(gk) ? gate->g : nullptr, gg);
   const Range rs0 = range_of(S0, BH * r * p->d_v * 4), rz0 = range_of(z0, BH * r * 4);
+  const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
   const Range rdq = range_of(dQ, qk), rdk = range_of(dK, qk), rdv = range_of(dV, vv), rdg = range_of(dg, gg);
   const BwdWsLayout wl = bwd_workspace_layout(p, fmap, gk, causal);
   const Range rws = range_of(workspace, wl.bytes);
   for (Range o : {rdq, rdk, rdv, rdg, rws})
-    for (Range i : {rq, rk, rv, rdo, rgam, rgl, rs0, rz0})
+    for (Range i : {rq, rk, rv, rdo, rgam, rgl, rs0, rz0, rom})
       if (overlaps(o, i)) return LA_ERR_ALIAS;
   if (overlaps(rdq, rdk) || overlaps(rdq, rdv) || overlaps(rdk, rdv) || overlaps(rws, rdq) || overlaps(rws, rdk) ||
       overlaps(rws, rdv) || overlaps(rdg, rdq) || overlaps(rdg, rdk) || overlaps(rdg, rdv) || overlaps(rdg, rws))
@@ -756,7 +766,25 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
     if ((st = launch_gate_repeat(gate->g, ws + wl.gx_off, (long long)(BH * n), fmap->r, plan.stream)) != LA_OK)
       return st;
   }
-  if (backward_in_halves(p)) {
+  // FAVOR+: the kernels run on the materialised features phi(Q), phi(K) and
+  // write d phi, which favor_vjp takes back through the map into dQ, dK
+  const bool favor = fmap->kind == LA_FMAP_FAVOR;
+  bf16_bits* fv = reinterpret_cast<bf16_bits*>(ws + wl.fv_off);
+  const size_t fsz = BH * n * r;
+  if (favor) {
+    if ((st = launch_favor_features(Q, p->in_dtype, (long long)(BH * n), p->d_k, fmap->r, fmap->omega, fv,
+                                    plan.stream)) != LA_OK ||
+        (st = launch_favor_features(K, p->in_dtype, (long long)(BH * n), p->d_k, fmap->r, fmap->omega, fv + fsz,
+                                    plan.stream)) != LA_OK)
+      return st;
+    plan.Q = fv;
+    plan.K = fv + fsz;
+    plan.dQ = fv + 2 * fsz;
+    plan.dK = fv + 3 * fsz;
+    plan.fmap = kFmapPrecomputed;
+    plan.dk = fmap->r;
+  }
+  if (backward_in_halves(p, fmap->r)) {
     const int half = p->d_v / 2;
     BwdPlan hp = plan;
     hp.dv = half;
@@ -777,6 +805,13 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
     }
   } else if ((st = launch_backward(plan)) != LA_OK) {
     return st;
+  }
+  if (favor) {
+    if ((st = launch_favor_vjp(fv + 2 * fsz, fv, Q, p->in_dtype, (long long)(BH * n), p->d_k, fmap->r, fmap->omega, dQ,
+                               p->out_dtype, plan.stream)) != LA_OK)
+      return st;
+    return launch_favor_vjp(fv + 3 * fsz, fv + fsz, K, p->in_dtype, (long long)(BH * n), p->d_k, fmap->r, fmap->omega,
+                            dK, p->out_dtype, plan.stream);
   }
   return sel ? launch_gate_feature_sum(ws + wl.dgx_off, dg, (long long)(BH * n), fmap->r, plan.stream) : LA_OK;
 }

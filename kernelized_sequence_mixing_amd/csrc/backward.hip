@@ -111,6 +111,10 @@ static la_status run_backward_fmap(const BwdPlan& p) {
   switch (p.fmap) {
     case LA_FMAP_ELU1: return run_backward_gated<R, E, FM_ELU1>(p);
     case LA_FMAP_IDENTITY: return run_backward_gated<R, E, FM_IDENT>(p);
+    case kFmapPrecomputed:  // FAVOR+'s materialised features: no gate or the RetNet decay
+      if (p.gate == LA_GATE_NONE) return run_backward<R, E, GT_NONE, FM_PRE>(p);
+      if (p.gate == LA_GATE_DECAY) return run_backward<R, E, GT_DECAY, FM_PRE>(p);
+      return LA_ERR_UNSUPPORTED;
     default: return LA_ERR_UNSUPPORTED;
   }
 }

@@ -49,13 +49,16 @@
 
 namespace la {
 
-enum FmapKind { FM_ELU1 = 0, FM_FAVOR = 1, FM_IDENT = 2 };
+// FM_PRE: features computed beforehand and passed in place of q and k (the
+// FAVOR+ backward runs the elementwise kernels on its materialised features):
+// taken as they are, like the identity, but with the normalised read-out.
+enum FmapKind { FM_ELU1 = 0, FM_FAVOR = 1, FM_IDENT = 2, FM_PRE = 3 };
 
 // Elementwise feature maps of the chunk prelude: elu+1, or the identity of the
-// state-space form (whose read-out is not normalised).
+// state-space form (whose read-out is not normalised) and of precomputed features.
 template <int FMAP>
 __device__ __forceinline__ float phi_ew(float x) {
-  if constexpr (FMAP == FM_IDENT) return x;
+  if constexpr (FMAP == FM_IDENT || FMAP == FM_PRE) return x;
   else return elu1(x);
 }
 // phi(x) 2^s in one exponential, and the factor e = phi'(x) 2^s: for elu+1,
@@ -65,7 +68,7 @@ __device__ __forceinline__ float phi_ew(float x) {
 // one transcendental each instead of one for phi and one for the gate.
 template <int FMAP>
 __device__ __forceinline__ float phi_times_exp2(float x, float s, float& e) {
-  if constexpr (FMAP == FM_IDENT) {
+  if constexpr (FMAP == FM_IDENT || FMAP == FM_PRE) {
     e = __builtin_amdgcn_exp2f(s);
     return x * e;
   } else {
@@ -75,10 +78,10 @@ __device__ __forceinline__ float phi_times_exp2(float x, float s, float& e) {
   }
 }
 // Its derivative from the feature value: min(phi, 1) for elu+1 (1 above zero,
-// exp(x) = phi below), 1 for the identity.
+// exp(x) = phi below), 1 for the identity and precomputed features.
 template <int FMAP>
 __device__ __forceinline__ float phi_ew_deriv(float phi) {
-  if constexpr (FMAP == FM_IDENT) return 1.f;
+  if constexpr (FMAP == FM_IDENT || FMAP == FM_PRE) return 1.f;
   else return fminf(phi, 1.f);
 }
 enum GateKind { GT_NONE = 0, GT_DECAY = 1, GT_GLA = 2, GT_SEL = 3, GT_OUTER = 4 };

@@ -156,6 +156,14 @@ la_status launch_noncausal(const FwdPlan& p);
 la_status launch_decode(const DecodePlan& p);
 la_status launch_feature_map(const FmapPlan& p);
 la_status launch_softmax(const SoftmaxPlan& p);
+// FAVOR+ backward: its features materialised (bf16 [rows][r]) and the
+// gradient through the feature map, dX = sum_m dphi_m phi_m (w_m - x).
+la_status launch_favor_features(const void* X, int in_dt, long long rows, int dk, int r, const void* omega, void* out,
+                                hipStream_t st);
+la_status launch_favor_vjp(const void* dphi, const void* phi, const void* X, int in_dt, long long rows, int dk, int r,
+                           const void* omega, void* dX, int out_dt, hipStream_t st);
+// BwdPlan::fmap value for features computed beforehand (not a public feature map).
+constexpr int kFmapPrecomputed = 3;
 // The selective scalar gate's backward: repeat g [rows] over r features, and
 // sum the per-feature gradient [rows][r] back to [rows].
 la_status launch_gate_repeat(const void* g, void* gx, long long rows, int r, hipStream_t stream);

@@ -281,7 +281,11 @@ BAD_BACKWARD = [
     ("noncausal with S0", dict(causal=0, S0=FAKE + 7 * SP, z0=FAKE + 8 * SP), {}, N.LA_ERR_INVALID_ARG),
     ("noncausal d_v 96", dict(causal=0, d_v=96), {}, N.LA_ERR_UNSUPPORTED),
     ("noncausal gated", dict(causal=0, gkind=N.LA_GATE_DECAY, gamma=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),
-    ("favor", dict(fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
+    ("favor r 256", dict(fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
+    ("favor r 32", dict(fkind=N.LA_FMAP_FAVOR, r=32, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
+    ("favor r 128 d_v 32", dict(fkind=N.LA_FMAP_FAVOR, r=128, d_v=32, omega=FAKE + 5 * SP), {},
+     N.LA_ERR_UNSUPPORTED),
+    ("favor no omega", dict(fkind=N.LA_FMAP_FAVOR, r=128), {}, N.LA_ERR_INVALID_ARG),
     ("gla without dg", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),
     ("dg without gla", {}, dict(dg=FAKE + 14 * SP), N.LA_ERR_INVALID_ARG),
     ("gla no g", dict(gkind=N.LA_GATE_GLA), dict(dg=FAKE + 14 * SP), N.LA_ERR_INVALID_ARG),
@@ -357,6 +361,19 @@ def test_backward_workspace_size():
     # the halves' workspace, plus one half of a carried-in state (fp32 [BH][128][64])
     for gk in (N.LA_GATE_NONE, N.LA_GATE_GLA):
         assert size128(2, 16, 16384, 128, gk) == size128(2, 16, 16384, 64, gk) + 32 * 128 * 64 * 4
+
+    def size_favor(B, H, n, d, r, dv):
+        p = N.LaProblem(B, H, n, d, dv, N.LA_BF16, N.LA_BF16, 1e-6)
+        f = N.LaFeatureMap(N.LA_FMAP_FAVOR, r, ctypes.c_void_p(FAKE))
+        g = N.LaGate(N.LA_GATE_NONE, 16.0, None, None)
+        out = ctypes.c_size_t(0)
+        assert lib.la_backward_workspace_size(ctypes.byref(p), ctypes.byref(f), 1, ctypes.byref(g),
+                                              ctypes.byref(out)) == N.LA_OK
+        return out.value
+    # FAVOR+ runs the passes at width r on phi(Q), phi(K) and their gradients (bf16 [BH][n][r] each)
+    assert size_favor(1, 8, 32768, 64, 128, 64) == size128(1, 8, 32768, 64) + 4 * 8 * 32768 * 128 * 2
+    assert size_favor(2, 2, 300, 128, 128, 128) == size128(2, 2, 300, 128) + 4 * 4 * 300 * 128 * 2
+    assert size_favor(1, 1, 65, 32, 64, 64) == size(1, 1, 65, 64, 64) + 4 * 65 * 64 * 2
 
 
 # ------------------------------------------------------------------ serving batch (validation, no launch)
