@@ -310,6 +310,27 @@ def backward_algorithmic_per_token(wl):
     return nbytes, flops
 
 
+def backward_kernel_names(wl, count):
+    """Labels of la_backward's launches, in order: with several segments the forward's
+    segment-state pass and scan, pass A, the reverse state pass and reverse scan, pass B
+    (one segment: A and B only); 128 x 128 states repeat them per value-column half;
+    FAVOR+ adds the feature kernels before and the pullbacks through the map after."""
+    favor = wl.fmap == "favor"
+    halves = 2 if (wl.r if favor else wl.d_k) == 128 and wl.d_v == 128 else 1
+    core = count - (4 if favor else 0)
+    if not wl.causal or core % halves:
+        return []
+    per = core // halves
+    one = {6: ["segment_state", "segment_scan", "bwd_pass_a", "bwd_rstate", "segment_scan_reverse", "bwd_pass_b"],
+           2: ["bwd_pass_a", "bwd_pass_b"]}.get(per)
+    if one is None:
+        return []
+    names = one if halves == 1 else [f"{k}_h{h}" for h in range(2) for k in one]
+    if favor:
+        names = ["favor_features_q", "favor_features_k"] + names + ["favor_vjp_q", "favor_vjp_k"]
+    return names
+
+
 def bench_backward(wl, steps, warmup):
     """la_backward on workload wl (causal; elu+1, FAVOR+ or identity features): one step is
     one full backward pass (with a gate input it includes dg; with FAVOR+ the feature
@@ -334,10 +355,13 @@ def bench_backward(wl, steps, warmup):
         calls[i]()
 
     ms, med = time_steps(step, len(sets), steps, warmup, stream)
+    order = iter(range(10 ** 9))
+    times = ksm.launch_times(lambda: calls[next(order) % len(calls)](), min(steps, 20), stream, max_launches=24)
     gbs = per_set / (ms * 1e-3) / 1e9
     tfl = wl.head_tokens * fl_tok / (ms * 1e-3) / 1e12
     return {"workload": wl.name + "_backward", "ms_per_step": round(ms, 5), "median_ms": round(med, 5),
             "value": wl.head_tokens / (ms * 1e-3), "unit": "head-tokens/s", "input_sets_rotated": len(sets),
+            "kernels": kernel_table(times, backward_kernel_names(wl, len(times[0]))),
             "hbm_alg_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "mfma_alg_TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4),
             "alg_bytes_per_token": nb_tok, "alg_flops_per_token": fl_tok,
