@@ -62,13 +62,7 @@ static la_status run_backward(const BwdPlan& p) {
     a1.g = b.gl;
     a1.inv_tau = b.inv_tau;
     a1.logG_out = p.ws_logG;
-    auto k1 = causal_segment_state<R, E, R, FMAP, GATE>;
-    constexpr int lds1 = SegLayout<R, E, GATE>::bytes;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
-        hipSuccess)
-      return LA_ERR_HIP;
-    LA_LAUNCH(k1, dim3(p.P - 1, BH), dim3(256), lds1, p.stream, a1);
-    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    if ((st = launch_segment_pass<R, E, R, FMAP, GATE>(a1, p.P, BH, p.stream)) != LA_OK) return st;
     if ((st = launch_segment_scan(p)) != LA_OK) return st;
     b.S_in = p.ws_S;
     b.z_in = p.ws_z;

@@ -44,6 +44,8 @@
 // and keeps K^ in a tile of its own (pass 1 stores only K^, in the k tile).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -72,9 +74,12 @@ __device__ __forceinline__ float phi_times_exp2(float x, float s, float& e) {
     e = __builtin_amdgcn_exp2f(s);
     return x * e;
   } else {
-    const bool pos = x > 0.f;
-    e = __builtin_amdgcn_exp2f(pos ? s : __builtin_fmaf(x, kLog2e, s));
-    return pos ? (x + 1.f) * e : e;
+    // with m = min(x, 0): e = 2^(m log2(e) + s) and phi 2^s = (x - m + 1) e,
+    // the two branches' values without a compare or select (x - m is the
+    // positive part and keeps a NaN input a NaN)
+    const float m = fminf(x, 0.f);
+    e = __builtin_amdgcn_exp2f(__builtin_fmaf(m, kLog2e, s));
+    return __builtin_fmaf(x - m, e, e);
   }
 }
 // Its derivative from the feature value: min(phi, 1) for elu+1 (1 above zero,
@@ -122,6 +127,7 @@ struct CausalArgs {
   int in_is_state;         // S_in is the caller's carried state (indexed like S_out), not the segment workspace
   int ldv;                 // elements between rows of V (0: d_v, dense); the backward's value-column halves
   int H, n, P, seg_len;
+  int nbh;                 // sequences x heads (set by launchers whose grid is not [.][nbh])
   float eps, inv_tau;
 };
 
@@ -813,6 +819,232 @@ __global__ __launch_bounds__((64 * Waves<R, E>::NW)) void causal_segment_state(C
 }
 
 // ---------------------------------------------------------------------------
+// Pass 1 for the GLA gate, feature-major ("Gating and Selective State
+// Updates": S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T). Per chunk the
+// segment's state takes S <- diag(Gamma) S + K^T V with
+// K^_t = e^{b_end - b_t} phi(k_t) (b the chunk's inclusive cumulative
+// log-gate, Gamma = e^{b_end}; every factor <= 1), and z likewise.
+//
+// The feature rows of the state are independent under this gate, so each
+// segment is split over R / 64 workgroups of 64 features (four waves, one
+// 16-feature tile each, every value column). The chunk's k and g columns of
+// the block and its v rows are staged in LDS as they load (coalesced); each
+// lane then reads its feature's column for eight consecutive tokens per
+// 32-token block by transpose reads, which is also the A-operand layout of
+// the state update (contraction over tokens). So the cumulative log-gate is a
+// running sum inside the lane plus a two-step prefix over the four lane
+// groups, and K^ goes from registers to the matrix cores without an LDS round
+// trip; z is the state column of a constant-1 value. LDS holds two chunks
+// (one barrier per chunk).
+// ---------------------------------------------------------------------------
+constexpr int kGlaSegFeatures = 64;  // features per workgroup of the feature-major pass
+
+template <int E>
+struct GlaSegLayout {
+  using FTR = FeatTile<kGlaSegFeatures, false>;
+  using FTE = FeatTile<E, false>;
+  static constexpr int k_off = 0;
+  static constexpr int g_off = k_off + FTR::BYTES;
+  static constexpr int v_off = g_off + FTR::BYTES;
+  static constexpr int HALF = v_off + FTE::BYTES;
+  static constexpr int bytes = 2 * HALF;
+};
+
+// Built for the GLA gate with 64 or 128 features.
+template <int R, int GATE>
+constexpr bool kGlaFeatureMajorSeg = GATE == GT_GLA && R % kGlaSegFeatures == 0;
+
+template <int R, int E, int DK, int FMAP>
+__global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char sm[];
+  using LY = GlaSegLayout<E>;
+  constexpr int FB = kGlaSegFeatures, NFB = R / FB, ET = E / 16;
+  constexpr int VR = FB / 8, VE = E / 8;              // 16-byte pieces per row of the k (g) block and of v
+  constexpr int PK = 64 * VR / 256, PV = 64 * VE / 256;  // pieces per thread
+  using FTR = typename LY::FTR;
+  using FTE = typename LY::FTE;
+  const int lane = lane_id(), w = wave_id<4>(), tid = threadIdx.x;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  // 1D grid: workgroup i runs on XCD i % 8, so the feature blocks of one
+  // (head, segment), which read the same value rows, take ids 8 apart (same
+  // XCD and L2, dispatched back to back)
+  const int nseg = a.P - 1;
+  const int grp = blockIdx.x / (8 * NFB), r8 = blockIdx.x % (8 * NFB);
+  const int fb = r8 / 8;
+  const long long idx = 8ll * grp + r8 % 8;
+  if (idx >= (long long)nseg * a.nbh) return;
+  const int s = int(idx % nseg);
+  const long long bh = idx / nseg;
+  const SeqView sv = seq_view(a, bh);
+  const int t_begin = s * a.seg_len;
+  if (t_begin + a.seg_len >= sv.len) return;  // only segments that a later one follows
+  const int t_end = min(sv.len, t_begin + a.seg_len);
+  const long long tok0 = sv.tok0;
+  const long long ldv = a.ldv > 0 ? a.ldv : E;
+  const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
+  const int f_lane = FB * fb + 16 * w + c16;  // this lane's feature
+
+  f32x4 S[ET], Z = {0.f, 0.f, 0.f, 0.f};  // state rows 16 w + 4 g4 + i of the block; z of the same rows
+#pragma unroll
+  for (int eb = 0; eb < ET; ++eb) S[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lg = 0.f;  // summed log2-gates of feature f_lane
+  bf16x8 ones;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ones[u] = (bf16)1.f;
+
+  // raw rows of one chunk in registers: piece i of thread tid is piece
+  // tid + 256 i of the block's tile in row-major order (rows clamped to the segment)
+  bf16x8 rk[PK], rg[PK], rv[PV];
+  auto load = [&](int ci) {
+    const int t0 = t_begin + ci * kChunk;
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+      const int pc = tid + 256 * i;
+      const long long at = (tok0 + min(t0 + pc / VR, t_end - 1)) * R + FB * fb + 8 * (pc % VR);
+      rk[i] = *reinterpret_cast<const bf16x8*>(a.K + at);
+      rg[i] = *reinterpret_cast<const bf16x8*>(a.g + at);
+    }
+#pragma unroll
+    for (int i = 0; i < PV; ++i) {
+      const int pc = tid + 256 * i;
+      const long long row = tok0 + min(t0 + pc / VE, t_end - 1);
+      rv[i] = *reinterpret_cast<const bf16x8*>(a.V + row * ldv + 8 * (pc % VE));
+    }
+  };
+  auto stage = [&](int half) {
+    char* base = sm + half * LY::HALF;
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+      const int pc = tid + 256 * i;
+      lds<bf16x8>(base, LY::k_off + FTR::at(pc / VR, pc % VR)) = rk[i];
+      lds<bf16x8>(base, LY::g_off + FTR::at(pc / VR, pc % VR)) = rg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PV; ++i) {
+      const int pc = tid + 256 * i;
+      lds<bf16x8>(base, LY::v_off + FTE::at(pc / VE, pc % VE)) = rv[i];
+    }
+  };
+
+  load(0);
+  stage(0);
+  load(1);
+  lds_barrier();
+  for (int ci = 0; ci < nch; ++ci) {
+    const int half = ci & 1;
+    if (ci + 1 < nch) stage(half ^ 1);
+    load(ci + 2);  // unconditional: past the segment it re-reads its last row
+    const int L = min(kChunk, sv.len - (t_begin + ci * kChunk));
+    char* base = sm + half * LY::HALF;
+    // MASKED: a chunk shorter than 64 tokens (the sequence's last); rows past
+    // L get a zero log-gate and a zero key
+    auto chunk = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+      // lane (c16, g4): feature f_lane, tokens 32 ks + 8 g4 + j
+      float b[2][8];
+      bf16x8 kk[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 gg = tr_feat<FB, false>(base, LY::g_off, 32 * ks, 16 * w, lane);
+        kk[ks] = tr_feat<FB, false>(base, LY::k_off, 32 * ks, 16 * w, lane);
+        float run = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float la = gla_log2_alpha(to_f32(gg[j]), a.inv_tau);
+          run += MASKED ? keep_if(32 * ks + 8 * g4 + j < L, la) : la;
+          b[ks][j] = run;
+        }
+      }
+      // prefix of the lane totals over the four lane groups, both blocks at once
+      float inc0 = b[0][7], inc1 = b[1][7];
+      {
+        const float u0 = __shfl_up(inc0, 16), u1 = __shfl_up(inc1, 16);
+        inc0 += g4 >= 1 ? u0 : 0.f;
+        inc1 += g4 >= 1 ? u1 : 0.f;
+        const float v0 = __shfl_up(inc0, 32), v1 = __shfl_up(inc1, 32);
+        inc0 += g4 >= 2 ? v0 : 0.f;
+        inc1 += g4 >= 2 ? v1 : 0.f;
+      }
+      const float tot0 = __shfl(inc0, 48 + c16), tot1 = __shfl(inc1, 48 + c16);
+      const float bend = tot0 + tot1;
+      // exponent of K^ for token (ks, j): bend - (b[ks][j] + offset of the lane's run)
+      const float r0 = bend - (inc0 - b[0][7]), r1 = bend - (tot0 + inc1 - b[1][7]);
+      bf16x8 kh[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float unused;
+          e[j] = phi_times_exp2<FMAP>(to_f32(kk[ks][j]), (ks == 0 ? r0 : r1) - b[ks][j], unused);
+          if constexpr (MASKED) e[j] = keep_if(32 * ks + 8 * g4 + j < L, e[j]);
+        }
+        kh[ks] = cat8(pack4(e[0], e[1], e[2], e[3]), pack4(e[4], e[5], e[6], e[7]));
+      }
+      const float gam = __builtin_amdgcn_exp2f(bend);
+      lg += bend;
+      float gr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gr[i] = __shfl(gam, 4 * g4 + i);  // Gamma of state row 16 w + 4 g4 + i
+#pragma unroll
+      for (int eb = 0; eb < ET; ++eb) {
+        f32x4 st = S[eb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[i] *= gr[i];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) st = mfma16(kh[ks], tr_feat<E, false>(base, LY::v_off, 32 * ks, 16 * eb, lane), st);
+        S[eb] = st;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Z[i] *= gr[i];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) Z = mfma16(kh[ks], ones, Z);
+    };
+    if (L == kChunk)
+      chunk(std::false_type{});
+    else
+      chunk(std::true_type{});
+    lds_barrier();
+  }
+  const long long slot = bh * a.P + s;
+  const int row0 = FB * fb + 16 * w + 4 * g4;
+  float* So = a.S_out + slot * R * E;
+#pragma unroll
+  for (int eb = 0; eb < ET; ++eb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) So[(row0 + i) * E + 16 * eb + c16] = S[eb][i];
+  if (c16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a.z_out[slot * R + row0 + i] = Z[i];
+  }
+  if (g4 == 0) a.logG_out[slot * R + f_lane] = lg * kLn2;  // natural log for the scan
+}
+
+// Pass 1 launch: the feature-major GLA pass where it is built, else causal_segment_state.
+template <int R, int E, int DK, int FMAP, int GATE>
+la_status launch_segment_pass(const CausalArgs& a1, int P, unsigned BH, hipStream_t stream) {
+  if constexpr (kGlaFeatureMajorSeg<R, GATE> && FMAP != FM_FAVOR) {
+    auto k1 = gla_segment_state<R, E, DK, FMAP>;
+    constexpr int lds1 = GlaSegLayout<E>::bytes;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
+        hipSuccess)
+      return LA_ERR_HIP;
+    CausalArgs a2 = a1;
+    a2.nbh = int(BH);
+    const unsigned groups = (unsigned(P - 1) * BH + 7) / 8;
+    LA_LAUNCH(k1, dim3(groups * 8 * (R / kGlaSegFeatures)), dim3(256), lds1, stream, a2);
+  } else {
+    auto k1 = causal_segment_state<R, E, DK, FMAP, GATE>;
+    constexpr int lds1 = SegLayout<R, E, GATE>::bytes;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
+        hipSuccess)
+      return LA_ERR_HIP;
+    LA_LAUNCH(k1, dim3(P - 1, BH), dim3(64 * Waves<R, E>::NW), lds1, stream, a1);
+  }
+  return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
 // Pass 3: outputs of one segment, starting from its chained state.
 // ---------------------------------------------------------------------------
 template <int R, int E, int DK, int FMAP, int GATE>
@@ -1058,14 +1290,9 @@ la_status run_causal(const FwdPlan& p) {
     a1.z_out = p.ws_z;
     a1.logG_out = p.ws_logG;
     a1.logGv_out = p.ws_logGv;
-    auto k1 = causal_segment_state<R, E, DK, FMAP, GATE>;
-    constexpr int lds1 = SegLayout<R, E, GATE>::bytes;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
-        hipSuccess)
-      return LA_ERR_HIP;
-    LA_LAUNCH(k1, dim3(p.P - 1, BH), dim3(64 * Waves<R, E>::NW), lds1, p.stream, a1);
-    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
-    la_status st = launch_segment_scan(p);
+    la_status st = launch_segment_pass<R, E, DK, FMAP, GATE>(a1, p.P, BH, p.stream);
+    if (st != LA_OK) return st;
+    st = launch_segment_scan(p);
     if (st != LA_OK) return st;
     a.S_in = p.ws_S;
     a.z_in = p.ws_z;
