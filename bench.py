@@ -82,10 +82,10 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, calibrated on a plain
-    copy), if it was taken on the current kernel sources; else None."""
+def _profile_entry(workload, kernel):
+    """The committed rocprofv3 summary of `kernel` on `workload`
+    (profiles/traffic_<workload>.json), if it was taken on the current kernel
+    sources; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -93,8 +93,28 @@ def measured_traffic(workload, kernel):
         t = json.load(f)
     if t.get("source_digest") != source_digest():
         return None
-    k = t.get("kernels", {}).get(kernel)
+    return t.get("kernels", {}).get(kernel)
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, calibrated on a plain
+    copy), if it was taken on the current kernel sources; else None."""
+    k = _profile_entry(workload, kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def measured_mfma(workload, kernel):
+    """Counter-measured matrix-core use of `kernel` on `workload` from the same
+    summary: issued bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) per
+    launch and over its traced duration, and the MFMA-busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs); else None."""
+    k = _profile_entry(workload, kernel)
+    if k is None or k.get("mfma_flops") is None:
+        return None
+    return {"kernel": k.get("kernel"), "issued_flops_per_launch": k["mfma_flops"],
+            "issued_TFLOPs": k.get("mfma_tflops"), "issued_frac": k.get("mfma_frac"),
+            "busy_frac": k.get("mfma_busy"), "traced_us": k.get("avg_us")}
 
 
 def _device_sets(inp, keys, per_set_bytes):
@@ -139,8 +159,10 @@ def forward_kernel_names(wl, P):
     if not wl.causal:
         return ["nc_partial", "nc_readout"]
     pre = "favor" if wl.fmap == "favor" else "causal"
-    return [f"{pre}_segment_state", "segment_scan_kernel", f"{pre}_chunk_forward"] if P > 1 else \
-        [f"{pre}_chunk_forward"]
+    # the GLA gate's segment pass is the feature-major kernel where it is built (64 or 128 features)
+    seg = "gla_segment_state" if (wl.gate == "gla" and wl.fmap != "favor" and wl.d_k % 64 == 0) \
+        else f"{pre}_segment_state"
+    return [seg, "segment_scan_kernel", f"{pre}_chunk_forward"] if P > 1 else [f"{pre}_chunk_forward"]
 
 
 def kernel_table(times, names):
@@ -587,8 +609,10 @@ def main():
         "kernels": head["kernels"],
         "roofline": roofline(wl, head),
         "mfma": {"alg_TFLOPs": head["mfma_alg_TFLOPs"], "peak_TFLOPs": BF16_PEAK_TFLOPS,
-                 "alg_frac": head["mfma_frac"], "note": "algorithmic flops over the step time; the counter-issued "
-                                                        "MFMA utilisation is in profiles/"},
+                 "alg_frac": head["mfma_frac"],
+                 "counter": measured_mfma(wl.name, max(head["kernels"], key=lambda k: k["avg_ms"])["name"]),
+                 "note": "alg_*: algorithmic flops over the step time; counter: the dominant kernel's rocprofv3 "
+                         "summary in profiles/ (null if taken on other kernel sources)"},
         "context": {"softmax_score_matrix_n16384_fp16_bytes": 16384 * 16384 * 2},
     }
     if not args.no_extra:

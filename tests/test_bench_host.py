@@ -55,9 +55,18 @@ def test_traffic_only_for_the_measured_sources(monkeypatch, tmp_path):
     assert bench.measured_traffic("gla_gate", "causal_chunk_forward") == 123456789
     assert bench.measured_traffic("gla_gate", "segment_scan_kernel") is None
     assert bench.measured_traffic("no_such_workload", "causal_chunk_forward") is None
+    # the matrix-core counters ride in the same record
+    assert bench.measured_mfma("gla_gate", "causal_chunk_forward") is None
+    rec["kernels"]["causal_chunk_forward"].update(kernel="causal_chunk_forward<128, 128, 128, 0, 2>",
+                                                 mfma_flops=4.8e10, mfma_tflops=240.0, mfma_frac=0.0954,
+                                                 mfma_busy=0.0977, avg_us=200.0)
+    (tmp_path / "profiles" / "traffic_gla_gate.json").write_text(json.dumps(rec))
+    m = bench.measured_mfma("gla_gate", "causal_chunk_forward")
+    assert m["issued_flops_per_launch"] == 4.8e10 and m["busy_frac"] == 0.0977 and m["issued_frac"] == 0.0954
     # any change to the kernel sources voids it
     monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
     assert bench.measured_traffic("gla_gate", "causal_chunk_forward") is None
+    assert bench.measured_mfma("gla_gate", "causal_chunk_forward") is None
 
 
 def test_roofline_takes_the_dominant_kernel(monkeypatch):
@@ -76,7 +85,10 @@ def test_roofline_takes_the_dominant_kernel(monkeypatch):
 
 def test_kernel_names_follow_the_plan():
     assert bench.forward_kernel_names(WORKLOADS["gla_gate"], 8) == [
+        "gla_segment_state", "segment_scan_kernel", "causal_chunk_forward"]
+    assert bench.forward_kernel_names(WORKLOADS["causal_elu1"], 8) == [
         "causal_segment_state", "segment_scan_kernel", "causal_chunk_forward"]
+    assert bench.forward_kernel_names(WORKLOADS["gla_gate"].resized(d_k=32, r=32), 8)[0] == "causal_segment_state"
     assert bench.forward_kernel_names(WORKLOADS["favor_causal"], 1) == ["favor_chunk_forward"]
     assert bench.forward_kernel_names(WORKLOADS["noncausal_elu1_f32"], 1) == ["nc_partial", "nc_readout"]
     t = bench.kernel_table([[1.0, 2.0], [3.0, 4.0]], ["a", "b"])
