@@ -203,9 +203,14 @@ la_status la_forward_segments(const la_problem* p, const la_feature_map* fmap,
  *   workspace     device scratch of at least la_forward_workspace_size bytes
  *                 (may be NULL when that size is 0), 256-byte aligned.
  * Supported (else LA_ERR_UNSUPPORTED):
- *   causal: in_dtype BF16, out_dtype BF16; d_v in {64,128}; ELU1 or IDENTITY with
+ *   causal: in_dtype BF16, out_dtype BF16; d_v in {32,64,128}; ELU1 or IDENTITY with
  *           d_k in {32,64,128} and any gate; FAVOR with d_k in {32,64,128},
  *           r in {64,128,256}, gate NONE or DECAY; r * d_v <= 16384.
+ *           d_v = 32 runs the 64-column kernels on copies whose rows are 64
+ *           wide (columns 32..63 zero) of V, gate->gv, out, S0 and S_final, held
+ *           in the workspace (counted by la_forward_workspace_size), and
+ *           copies the 32 real columns back: results equal the d_v = 64
+ *           problem with zero-padded values, column for column.
  *   non-causal: in/out dtype F32 or BF16 (any mix); d_k in {32,64,128},
  *           d_v in {32,64,128}; FAVOR r in {64,128,256}; r * d_v <= 16384.
  * Numerics: bf16 MFMA products with fp32 accumulation; the state, normaliser,
@@ -253,7 +258,8 @@ la_status la_forward_batch_workspace_size(const la_problem* p, const la_batch* b
  * A ragged batch is planned from p->n and max_seqlen (the lengths stay on the
  * device): segments sized for about one round of workgroups over all
  * sequences, as many as the longest sequence needs.
- * Supported: as la_forward with causal == 1. Errors: LA_ERR_INVALID_ARG for a
+ * Supported: as la_forward with causal == 1, except d_v = 32, which only the
+ * one-token step takes (LA_ERR_UNSUPPORTED otherwise). Errors: LA_ERR_INVALID_ARG for a
  * malformed batch (num_seqs, max_seqlen, flags, B != 1 with cu_seqlens, NULL
  * pool pointers with flags set); LA_ERR_ALIAS when out, the pool or the
  * workspace overlap an input or each other. The library allocates nothing.

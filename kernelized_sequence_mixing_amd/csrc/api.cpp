@@ -99,8 +99,9 @@ const void* gate_vinput(const la_gate* g) { return gate_kind(g) == LA_GATE_OUTER
 
 // The built set of (d_k, r, d_v) shapes; see the header.
 bool shapes_built(const la_feature_map* f, int dk, int dv, bool causal) {
+  (void)causal;  // causal d_v = 32 runs the 64-column kernels on padded copies (padded_dv)
   if (!in_set(dk, {32, 64, 128})) return false;
-  if (causal ? !in_set(dv, {64, 128}) : !in_set(dv, {32, 64, 128})) return false;
+  if (!in_set(dv, {32, 64, 128})) return false;
   if (f->kind == LA_FMAP_FAVOR && !in_set(f->r, {64, 128, 256})) return false;
   return (long long)f->r * dv <= 16384;
 }
@@ -164,7 +165,15 @@ void plan_splits(int B, int H, int n, int* splits, int* split_len) {
 
 struct WsLayout {
   size_t S_off, z_off, logG_off, logGv_off, bytes;
+  // causal d_v = 32: 64-column copies of V (and gv), the output, S0 and S_final
+  size_t vpad_off = 0, gvpad_off = 0, opad_off = 0, s0pad_off = 0, sfpad_off = 0;
 };
+
+// The causal chunk kernels tile the value columns 64 wide: la_forward runs d_v
+// = 32 on copies of V, gv, out, S0 and S_final whose rows are kPadDv wide
+// (columns 32 .. 63 zero), held in its workspace (columns.hip).
+constexpr int kPadDv = 64;
+bool padded_dv(int causal, int dv) { return causal != 0 && dv == 32; }
 
 // Segment states (and GLA log-gates) of BH sequences cut into `pieces`.
 WsLayout workspace_pieces(size_t BH, size_t pieces, size_t r, size_t dv, bool gla, bool outer = false) {
@@ -179,18 +188,36 @@ WsLayout workspace_pieces(size_t BH, size_t pieces, size_t r, size_t dv, bool gl
 
 WsLayout workspace_layout(const la_problem* p, const la_feature_map* f, int causal, int gate) {
   const size_t BH = (size_t)p->B * p->H;
-  size_t pieces;
+  const bool pad = padded_dv(causal, p->d_v);
+  const int dv = pad ? kPadDv : p->d_v;
+  WsLayout w{0, 0, 0, 0, 0};
   if (causal) {
     int P, L;
-    plan_segments(p->B, p->H, p->n, f->kind, f->r, p->d_v, p->d_k, gate, &P, &L);
-    if (P <= 1) return WsLayout{0, 0, 0, 0, 0};
-    pieces = (size_t)P;
+    plan_segments(p->B, p->H, p->n, f->kind, f->r, dv, p->d_k, gate, &P, &L);
+    if (P > 1) w = workspace_pieces(BH, (size_t)P, f->r, dv, gate_has_input(gate), gate == LA_GATE_OUTER);
   } else {
     int sp, L;
     plan_splits(p->B, p->H, p->n, &sp, &L);
-    pieces = (size_t)sp;
+    w = workspace_pieces(BH, (size_t)sp, f->r, dv, false, false);
   }
-  return workspace_pieces(BH, pieces, f->r, p->d_v, causal && gate_has_input(gate), gate == LA_GATE_OUTER);
+  if (pad) {
+    const size_t rows = BH * (size_t)p->n, r = (size_t)f->r;
+    size_t off = round_up(w.bytes, kAlign);
+    w.vpad_off = off;
+    off = round_up(off + rows * kPadDv * 2, kAlign);  // bf16 (causal inputs are bf16)
+    if (gate == LA_GATE_OUTER) {
+      w.gvpad_off = off;
+      off = round_up(off + rows * kPadDv * 2, kAlign);
+    }
+    w.opad_off = off;
+    off = round_up(off + rows * kPadDv * 2, kAlign);  // bf16 out
+    w.s0pad_off = off;
+    off = round_up(off + BH * r * kPadDv * 4, kAlign);
+    w.sfpad_off = off;
+    off = round_up(off + BH * r * kPadDv * 4, kAlign);
+    w.bytes = off;
+  }
+  return w;
 }
 
 // The causal kernels of the plan's feature map.
@@ -433,10 +460,37 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   plan.nseq = p->B;
   plan.stream = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  plan.ws_S = wl.bytes ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
-  plan.ws_z = wl.bytes ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
-  plan.ws_logG = (wl.bytes && causal && gate_has_input(gk)) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
-  plan.ws_logGv = (wl.bytes && causal && gk == LA_GATE_OUTER) ? reinterpret_cast<float*>(ws + wl.logGv_off) : nullptr;
+  // the segment states live at the workspace's start (the padded copies, if any, after them)
+  const bool seg_ws = wl.S_off != wl.z_off;
+  plan.ws_S = seg_ws ? reinterpret_cast<float*>(ws + wl.S_off) : nullptr;
+  plan.ws_z = seg_ws ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
+  plan.ws_logG = (seg_ws && causal && gate_has_input(gk)) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
+  plan.ws_logGv = (seg_ws && causal && gk == LA_GATE_OUTER) ? reinterpret_cast<float*>(ws + wl.logGv_off) : nullptr;
+  if (causal && padded_dv(causal, p->d_v)) {
+    // d_v = 32: the 64-column kernels on zero-padded copies, then the real columns back
+    const long long rows = (long long)BH * (long long)n, srows = (long long)BH * (long long)r;
+    const hipStream_t hs = plan.stream;
+    plan.dv = kPadDv;
+    if ((st = launch_copy_columns(V, ws + wl.vpad_off, rows, 32, kPadDv, 32, kPadDv, 2, hs)) != LA_OK) return st;
+    plan.V = ws + wl.vpad_off;
+    if (gk == LA_GATE_OUTER) {
+      if ((st = launch_copy_columns(plan.gv, ws + wl.gvpad_off, rows, 32, kPadDv, 32, kPadDv, 2, hs)) != LA_OK)
+        return st;
+      plan.gv = ws + wl.gvpad_off;
+    }
+    if (S0 != nullptr) {
+      if ((st = launch_copy_columns(S0, ws + wl.s0pad_off, srows, 32, kPadDv, 32, kPadDv, 4, hs)) != LA_OK) return st;
+      plan.S0 = reinterpret_cast<const float*>(ws + wl.s0pad_off);
+    }
+    if (S_final != nullptr) plan.S_final = reinterpret_cast<float*>(ws + wl.sfpad_off);
+    plan.out = ws + wl.opad_off;
+    plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, plan.dv, p->d_k, gk, &plan.P, &plan.seg_len);
+    if ((st = launch_causal(plan)) != LA_OK) return st;
+    if ((st = launch_copy_columns(ws + wl.opad_off, out, rows, kPadDv, 32, 32, 32, 2, hs)) != LA_OK) return st;
+    if (S_final != nullptr)
+      return launch_copy_columns(ws + wl.sfpad_off, S_final, srows, kPadDv, 32, 32, 32, 4, hs);
+    return LA_OK;
+  }
   if (causal) {
     plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, p->d_v, p->d_k, gk, &plan.P, &plan.seg_len);
     return launch_causal(plan);
@@ -465,6 +519,9 @@ la_status check_batch(const la_problem* p, const la_batch* b, const la_feature_m
     return LA_ERR_INVALID_ARG;
   }
   if (b->flags != 0 && b->num_slots < 1) return LA_ERR_INVALID_ARG;
+  // d_v = 32 only on the one-token step (the recurrent kernel); the chunk
+  // kernels' padded copies are a la_forward workspace feature
+  if (p->d_v == 32 && !(b->cu_seqlens == nullptr && p->n == 1)) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 

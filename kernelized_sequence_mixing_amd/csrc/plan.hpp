@@ -153,6 +153,9 @@ la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, cons
 la_status launch_backward(const BwdPlan& p);
 la_status launch_noncausal_backward(const BwdPlan& p);  // ws_S, ws_z: partial S, z; ws_R, ws_rh: partial G, hq
 la_status launch_noncausal(const FwdPlan& p);
+// dst[row][c] = src[row][c] for c < cols, 0 for cols <= c < width (rows of src_ld / dst_ld elements, esz bytes)
+la_status launch_copy_columns(const void* src, void* dst, long long rows, int src_ld, int dst_ld, int cols, int width,
+                              int esz, hipStream_t st);
 la_status launch_decode(const DecodePlan& p);
 la_status launch_feature_map(const FmapPlan& p);
 la_status launch_softmax(const SoftmaxPlan& p);

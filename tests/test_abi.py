@@ -194,7 +194,8 @@ BAD_FORWARD = [
     ("noncausal gated", dict(causal=0, gkind=N.LA_GATE_DECAY, gamma=FAKE + 6 * SP), N.LA_ERR_INVALID_ARG),
     ("causal flag 2", dict(causal=2), N.LA_ERR_INVALID_ARG),
     ("d_k 48", dict(d_k=48, r=48), N.LA_ERR_UNSUPPORTED),
-    ("causal d_v 32", dict(d_v=32), N.LA_ERR_UNSUPPORTED),
+    ("causal d_v 96", dict(d_v=96), N.LA_ERR_UNSUPPORTED),
+    ("causal d_v 32 ws small", dict(d_v=32, ws_bytes=1 << 16), N.LA_ERR_WORKSPACE),
     ("causal fp32", dict(in_dt=N.LA_F32, out_dt=N.LA_F32), N.LA_ERR_UNSUPPORTED),
     ("causal fp32 out", dict(out_dt=N.LA_F32), N.LA_ERR_UNSUPPORTED),
     ("r*d_v too big", dict(fkind=N.LA_FMAP_FAVOR, r=256, d_v=128, omega=FAKE + 5 * SP), N.LA_ERR_UNSUPPORTED),
@@ -408,6 +409,8 @@ BAD_BATCH = [
     ("out over cu", dict(B=1), dict(cu=FAKE + 3 * SP, num_seqs=4, max_seqlen=50), N.LA_ERR_ALIAS),
     ("pool over slot ids", {}, dict(slot_ids=FAKE + 20 * SP + 64), N.LA_ERR_ALIAS),
     ("ws small", dict(ws_bytes=16), {}, N.LA_ERR_WORKSPACE),
+    ("d_v 32 multi-token", dict(d_v=32), {}, N.LA_ERR_UNSUPPORTED),
+    ("d_v 32 ragged", dict(B=1, d_v=32), dict(cu=FAKE + 23 * SP, num_seqs=4, max_seqlen=50), N.LA_ERR_UNSUPPORTED),
 ]
 
 
@@ -454,6 +457,31 @@ def test_batch_workspace_size():
     assert size(1, 40000, FAKE, 10, 4096) == ragged(40000, 10, 4096) == 10 * 16 * 4 * (64 * 64 + 64) * 4
     assert size(1, 8192, FAKE, 64, 4096) == ragged(8192, 64, 4096) > 0 == fwd(64, 4096)
     assert size(1, 40000, FAKE, 64, 128) == 0   # one segment per sequence: no workspace
+
+
+@needs_lib
+def test_causal_dv32_workspace():
+    """Causal d_v = 32 runs the 64-column kernels on padded copies in the
+    workspace: the 64-column problem's segment states, then bf16 V and out
+    copies [B H n 64] and fp32 S0 and S_final copies [B H r 64], each region
+    256-byte aligned (the outer-product gate adds a bf16 copy of gv)."""
+    lib = N.lib()
+    up = lambda x: -(-x // 256) * 256
+
+    def size(dv, gk=N.LA_GATE_NONE, B=2, H=3, n=1000, d=64):
+        p = N.LaProblem(B, H, n, d, dv, N.LA_BF16, N.LA_BF16, 1e-6)
+        f = N.LaFeatureMap(N.LA_FMAP_ELU1, d, None)
+        g = N.LaGate(gk, 16.0, None, None)
+        out = ctypes.c_size_t(0)
+        assert lib.la_forward_workspace_size(ctypes.byref(p), ctypes.byref(f), 1, ctypes.byref(g),
+                                             ctypes.byref(out)) == N.LA_OK
+        return out.value
+    for gk, copies in ((N.LA_GATE_NONE, 2), (N.LA_GATE_GLA, 2), (N.LA_GATE_OUTER, 3)):
+        B, H, n, d = 2, 3, 1000, 64
+        pads = copies * up(B * H * n * 64 * 2) + 2 * up(B * H * d * 64 * 4)
+        assert size(32, gk) == up(size(64, gk)) + pads
+    # one segment: only the copies
+    assert size(32, B=1, H=1, n=64) == 2 * up(64 * 64 * 2) + 2 * up(64 * 64 * 4)
 
 
 @needs_lib
