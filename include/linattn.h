@@ -205,14 +205,18 @@ la_status la_forward_segments(const la_problem* p, const la_feature_map* fmap,
  * Supported (else LA_ERR_UNSUPPORTED):
  *   causal: in_dtype BF16, out_dtype BF16; d_v in {32,64,128}; ELU1 or IDENTITY with
  *           d_k in {32,64,128} and any gate; FAVOR with d_k in {32,64,128},
- *           r in {64,128,256}, gate NONE or DECAY; r * d_v <= 16384.
+ *           r in {32,64,128,256}, gate NONE or DECAY; r * d_v <= 16384.
  *           d_v = 32 runs the 64-column kernels on copies whose rows are 64
  *           wide (columns 32..63 zero) of V, gate->gv, out, S0 and S_final, held
  *           in the workspace (counted by la_forward_workspace_size), and
  *           copies the 32 real columns back: results equal the d_v = 64
- *           problem with zero-padded values, column for column.
+ *           problem with zero-padded values, column for column. FAVOR r = 32
+ *           likewise runs the 64-feature kernels on omega zero-padded to 64
+ *           rows, the features past 32 masked to zero and the map's 1/sqrt(r)
+ *           taken at r = 32, with S0, z0, S_final, z_final padded and copied
+ *           back alike: the result is the r = 32 map's.
  *   non-causal: in/out dtype F32 or BF16 (any mix); d_k in {32,64,128},
- *           d_v in {32,64,128}; FAVOR r in {64,128,256}; r * d_v <= 16384.
+ *           d_v in {32,64,128}; FAVOR r in {32,64,128,256}; r * d_v <= 16384.
  * Numerics: bf16 MFMA products with fp32 accumulation; the state, normaliser,
  * gate factors and every denominator are fp32. The causal kernels normalise
  * each output row by one correctly rounded fp32 reciprocal of its denominator
@@ -258,8 +262,8 @@ la_status la_forward_batch_workspace_size(const la_problem* p, const la_batch* b
  * A ragged batch is planned from p->n and max_seqlen (the lengths stay on the
  * device): segments sized for about one round of workgroups over all
  * sequences, as many as the longest sequence needs.
- * Supported: as la_forward with causal == 1, except d_v = 32, which only the
- * one-token step takes (LA_ERR_UNSUPPORTED otherwise). Errors: LA_ERR_INVALID_ARG for a
+ * Supported: as la_forward with causal == 1, except d_v = 32 and FAVOR r = 32,
+ * which only the one-token step takes (LA_ERR_UNSUPPORTED otherwise). Errors: LA_ERR_INVALID_ARG for a
  * malformed batch (num_seqs, max_seqlen, flags, B != 1 with cu_seqlens, NULL
  * pool pointers with flags set); LA_ERR_ALIAS when out, the pool or the
  * workspace overlap an input or each other. The library allocates nothing.
@@ -338,7 +342,7 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
  *   S [B][H][r][d_v] fp32 and z [B][H][r] fp32 are read and overwritten;
  *   out [B][H][d_v] in out_dtype.
  * Supported: in_dtype F32 or BF16, out_dtype F32 or BF16; ELU1 or IDENTITY with
- * d_k in {32,64,128}; FAVOR d_k in {32,64,128}, r in {64,128,256}; any gate;
+ * d_k in {32,64,128}; FAVOR d_k in {32,64,128}, r in {32,64,128,256}; any gate;
  * d_v in {32,64,128}; r * d_v <= 16384. fp32 arithmetic; out = fl(num / den).
  */
 la_status la_decode_step(const la_problem* p, float* S, float* z, const void* q,

@@ -102,7 +102,7 @@ bool shapes_built(const la_feature_map* f, int dk, int dv, bool causal) {
   (void)causal;  // causal d_v = 32 runs the 64-column kernels on padded copies (padded_dv)
   if (!in_set(dk, {32, 64, 128})) return false;
   if (!in_set(dv, {32, 64, 128})) return false;
-  if (f->kind == LA_FMAP_FAVOR && !in_set(f->r, {64, 128, 256})) return false;
+  if (f->kind == LA_FMAP_FAVOR && !in_set(f->r, {32, 64, 128, 256})) return false;
   return (long long)f->r * dv <= 16384;
 }
 
@@ -165,15 +165,20 @@ void plan_splits(int B, int H, int n, int* splits, int* split_len) {
 
 struct WsLayout {
   size_t S_off, z_off, logG_off, logGv_off, bytes;
-  // causal d_v = 32: 64-column copies of V (and gv), the output, S0 and S_final
-  size_t vpad_off = 0, gvpad_off = 0, opad_off = 0, s0pad_off = 0, sfpad_off = 0;
+  // causal d_v = 32 / FAVOR+ r = 32: zero-padded copies of V (and gv), the
+  // output, omega, S0, z0, S_final and z_final
+  size_t vpad_off = 0, gvpad_off = 0, opad_off = 0, ompad_off = 0, s0pad_off = 0, sfpad_off = 0, z0pad_off = 0,
+         zfpad_off = 0;
 };
 
-// The causal chunk kernels tile the value columns 64 wide: la_forward runs d_v
-// = 32 on copies of V, gv, out, S0 and S_final whose rows are kPadDv wide
-// (columns 32 .. 63 zero), held in its workspace (columns.hip).
-constexpr int kPadDv = 64;
+// The causal chunk kernels tile the value columns and the FAVOR+ features 64
+// wide: la_forward runs d_v = 32 and FAVOR+ r = 32 on zero-padded copies held
+// in its workspace (columns.hip): V, gv and out with rows of kPadDv columns;
+// omega with kPadR rows, the kernel masking features past r to zero; the
+// states with rows and columns padded alike.
+constexpr int kPadDv = 64, kPadR = 64;
 bool padded_dv(int causal, int dv) { return causal != 0 && dv == 32; }
+bool padded_r(int causal, const la_feature_map* f) { return causal != 0 && f->kind == LA_FMAP_FAVOR && f->r == 32; }
 
 // Segment states (and GLA log-gates) of BH sequences cut into `pieces`.
 WsLayout workspace_pieces(size_t BH, size_t pieces, size_t r, size_t dv, bool gla, bool outer = false) {
@@ -188,33 +193,37 @@ WsLayout workspace_pieces(size_t BH, size_t pieces, size_t r, size_t dv, bool gl
 
 WsLayout workspace_layout(const la_problem* p, const la_feature_map* f, int causal, int gate) {
   const size_t BH = (size_t)p->B * p->H;
-  const bool pad = padded_dv(causal, p->d_v);
-  const int dv = pad ? kPadDv : p->d_v;
+  const bool pad_dv = padded_dv(causal, p->d_v), pad_r = padded_r(causal, f);
+  const int dv = pad_dv ? kPadDv : p->d_v, rk = pad_r ? kPadR : f->r;
   WsLayout w{0, 0, 0, 0, 0};
   if (causal) {
     int P, L;
-    plan_segments(p->B, p->H, p->n, f->kind, f->r, dv, p->d_k, gate, &P, &L);
-    if (P > 1) w = workspace_pieces(BH, (size_t)P, f->r, dv, gate_has_input(gate), gate == LA_GATE_OUTER);
+    plan_segments(p->B, p->H, p->n, f->kind, rk, dv, p->d_k, gate, &P, &L);
+    if (P > 1) w = workspace_pieces(BH, (size_t)P, rk, dv, gate_has_input(gate), gate == LA_GATE_OUTER);
   } else {
     int sp, L;
     plan_splits(p->B, p->H, p->n, &sp, &L);
     w = workspace_pieces(BH, (size_t)sp, f->r, dv, false, false);
   }
-  if (pad) {
-    const size_t rows = BH * (size_t)p->n, r = (size_t)f->r;
+  if (pad_dv || pad_r) {
+    const size_t rows = BH * (size_t)p->n;
     size_t off = round_up(w.bytes, kAlign);
-    w.vpad_off = off;
-    off = round_up(off + rows * kPadDv * 2, kAlign);  // bf16 (causal inputs are bf16)
-    if (gate == LA_GATE_OUTER) {
-      w.gvpad_off = off;
-      off = round_up(off + rows * kPadDv * 2, kAlign);
+    auto take = [&](size_t& at, size_t bytes) {
+      at = off;
+      off = round_up(off + bytes, kAlign);
+    };
+    if (pad_dv) {
+      take(w.vpad_off, rows * kPadDv * 2);  // bf16 (causal inputs and outputs are bf16)
+      if (gate == LA_GATE_OUTER) take(w.gvpad_off, rows * kPadDv * 2);
+      take(w.opad_off, rows * kPadDv * 2);
     }
-    w.opad_off = off;
-    off = round_up(off + rows * kPadDv * 2, kAlign);  // bf16 out
-    w.s0pad_off = off;
-    off = round_up(off + BH * r * kPadDv * 4, kAlign);
-    w.sfpad_off = off;
-    off = round_up(off + BH * r * kPadDv * 4, kAlign);
+    if (pad_r) take(w.ompad_off, (size_t)kPadR * p->d_k * 2);
+    take(w.s0pad_off, BH * rk * dv * 4);
+    take(w.sfpad_off, BH * rk * dv * 4);
+    if (pad_r) {
+      take(w.z0pad_off, BH * rk * 4);
+      take(w.zfpad_off, BH * rk * 4);
+    }
     w.bytes = off;
   }
   return w;
@@ -384,7 +393,9 @@ la_status la_forward_segments(const la_problem* p, const la_feature_map* fmap, i
     return LA_OK;
   }
   int P, L;
-  plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, p->d_v, p->d_k, gate_kind(gate), &P, &L);
+  // the plan of the kernels that run (64-wide copies for d_v = 32 and FAVOR+ r = 32)
+  const int dv = padded_dv(causal, p->d_v) ? kPadDv : p->d_v, rk = padded_r(causal, fmap) ? kPadR : fmap->r;
+  plan_segments(p->B, p->H, p->n, fmap->kind, rk, dv, p->d_k, gate_kind(gate), &P, &L);
   *segments = P;
   *segment_len = L;
   return LA_OK;
@@ -466,29 +477,51 @@ la_status la_forward(const la_problem* p, const void* Q, const void* K, const vo
   plan.ws_z = seg_ws ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
   plan.ws_logG = (seg_ws && causal && gate_has_input(gk)) ? reinterpret_cast<float*>(ws + wl.logG_off) : nullptr;
   plan.ws_logGv = (seg_ws && causal && gk == LA_GATE_OUTER) ? reinterpret_cast<float*>(ws + wl.logGv_off) : nullptr;
-  if (causal && padded_dv(causal, p->d_v)) {
-    // d_v = 32: the 64-column kernels on zero-padded copies, then the real columns back
-    const long long rows = (long long)BH * (long long)n, srows = (long long)BH * (long long)r;
+  const bool pad_dv = padded_dv(causal, p->d_v), pad_r = padded_r(causal, fmap);
+  if (pad_dv || pad_r) {
+    // the 64-wide kernels on zero-padded copies, then the real part back
+    const long long heads = (long long)BH;
+    const int rr = int(r), dv = p->d_v, rk = pad_r ? kPadR : rr, dvk = pad_dv ? kPadDv : dv;
     const hipStream_t hs = plan.stream;
-    plan.dv = kPadDv;
-    if ((st = launch_copy_columns(V, ws + wl.vpad_off, rows, 32, kPadDv, 32, kPadDv, 2, hs)) != LA_OK) return st;
-    plan.V = ws + wl.vpad_off;
-    if (gk == LA_GATE_OUTER) {
-      if ((st = launch_copy_columns(plan.gv, ws + wl.gvpad_off, rows, 32, kPadDv, 32, kPadDv, 2, hs)) != LA_OK)
+    plan.dv = dvk;
+    plan.r = rk;
+    plan.r_valid = pad_r ? rr : 0;
+    if (pad_dv) {
+      const int nn = p->n;
+      if ((st = launch_copy_block(V, ws + wl.vpad_off, heads, nn, dv, nn, dvk, 2, hs)) != LA_OK) return st;
+      plan.V = ws + wl.vpad_off;
+      if (gk == LA_GATE_OUTER) {
+        if ((st = launch_copy_block(plan.gv, ws + wl.gvpad_off, heads, nn, dv, nn, dvk, 2, hs)) != LA_OK) return st;
+        plan.gv = ws + wl.gvpad_off;
+      }
+      plan.out = ws + wl.opad_off;
+    }
+    if (pad_r) {
+      if ((st = launch_copy_block(fmap->omega, ws + wl.ompad_off, 1, rr, p->d_k, rk, p->d_k, 2, hs)) != LA_OK)
         return st;
-      plan.gv = ws + wl.gvpad_off;
+      plan.omega = ws + wl.ompad_off;
     }
     if (S0 != nullptr) {
-      if ((st = launch_copy_columns(S0, ws + wl.s0pad_off, srows, 32, kPadDv, 32, kPadDv, 4, hs)) != LA_OK) return st;
+      if ((st = launch_copy_block(S0, ws + wl.s0pad_off, heads, rr, dv, rk, dvk, 4, hs)) != LA_OK) return st;
       plan.S0 = reinterpret_cast<const float*>(ws + wl.s0pad_off);
+      if (pad_r) {
+        if ((st = launch_copy_block(z0, ws + wl.z0pad_off, heads, 1, rr, 1, rk, 4, hs)) != LA_OK) return st;
+        plan.z0 = reinterpret_cast<const float*>(ws + wl.z0pad_off);
+      }
     }
-    if (S_final != nullptr) plan.S_final = reinterpret_cast<float*>(ws + wl.sfpad_off);
-    plan.out = ws + wl.opad_off;
-    plan_segments(p->B, p->H, p->n, fmap->kind, fmap->r, plan.dv, p->d_k, gk, &plan.P, &plan.seg_len);
+    if (S_final != nullptr) {
+      plan.S_final = reinterpret_cast<float*>(ws + wl.sfpad_off);
+      if (pad_r) plan.z_final = reinterpret_cast<float*>(ws + wl.zfpad_off);
+    }
+    plan_segments(p->B, p->H, p->n, fmap->kind, rk, dvk, p->d_k, gk, &plan.P, &plan.seg_len);
     if ((st = launch_causal(plan)) != LA_OK) return st;
-    if ((st = launch_copy_columns(ws + wl.opad_off, out, rows, kPadDv, 32, 32, 32, 2, hs)) != LA_OK) return st;
-    if (S_final != nullptr)
-      return launch_copy_columns(ws + wl.sfpad_off, S_final, srows, kPadDv, 32, 32, 32, 4, hs);
+    if (pad_dv && (st = launch_copy_block(ws + wl.opad_off, out, heads, p->n, dvk, p->n, dv, 2, hs)) != LA_OK)
+      return st;
+    if (S_final != nullptr) {
+      if ((st = launch_copy_block(ws + wl.sfpad_off, S_final, heads, rk, dvk, rr, dv, 4, hs)) != LA_OK) return st;
+      if (pad_r && (st = launch_copy_block(ws + wl.zfpad_off, z_final, heads, 1, rk, 1, rr, 4, hs)) != LA_OK)
+        return st;
+    }
     return LA_OK;
   }
   if (causal) {
@@ -521,7 +554,8 @@ la_status check_batch(const la_problem* p, const la_batch* b, const la_feature_m
   if (b->flags != 0 && b->num_slots < 1) return LA_ERR_INVALID_ARG;
   // d_v = 32 only on the one-token step (the recurrent kernel); the chunk
   // kernels' padded copies are a la_forward workspace feature
-  if (p->d_v == 32 && !(b->cu_seqlens == nullptr && p->n == 1)) return LA_ERR_UNSUPPORTED;
+  if ((p->d_v == 32 || (f->kind == LA_FMAP_FAVOR && f->r == 32)) && !(b->cu_seqlens == nullptr && p->n == 1))
+    return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 
@@ -920,7 +954,7 @@ la_status la_feature_map_apply(const la_feature_map* fmap, int64_t rows, int32_t
   if (X == nullptr || out == nullptr || !aligned16(X) || !aligned16(out)) return LA_ERR_INVALID_ARG;
   if (fmap->kind == LA_FMAP_IDENTITY) return LA_ERR_UNSUPPORTED;  // nothing to apply
   if (!in_set(d_k, {32, 64, 128})) return LA_ERR_UNSUPPORTED;
-  if (fmap->kind == LA_FMAP_FAVOR && !in_set(fmap->r, {64, 128, 256})) return LA_ERR_UNSUPPORTED;
+  if (fmap->kind == LA_FMAP_FAVOR && !in_set(fmap->r, {32, 64, 128, 256})) return LA_ERR_UNSUPPORTED;
   if ((rows + 63) / 64 > 0x7fffffffLL) return LA_ERR_UNSUPPORTED;
   const size_t isz = dtype_size(in_dtype);
   const Range rx = range_of(X, (size_t)rows * d_k * isz), ro = range_of(out, (size_t)rows * fmap->r * 4);

@@ -128,6 +128,7 @@ struct CausalArgs {
   int ldv;                 // elements between rows of V (0: d_v, dense); the backward's value-column halves
   int H, n, P, seg_len;
   int nbh;                 // sequences x heads (set by launchers whose grid is not [.][nbh])
+  int r_valid;             // FAVOR+: the map's feature count when below R (features past it are zero); 0 = R
   float eps, inv_tau;
 };
 

@@ -135,9 +135,10 @@ __device__ __forceinline__ bf16x8 tr_pair(char* sm, int addr, int gap) {
 
 // The raw rows of this wave's tokens (16 w + c) as projection B operands,
 // copied out of the prefetch registers, and each token's shift in base 2,
-// (|x|^2/2 + ln(r)/2) log2(e).
+// (|x|^2/2 + ln(r)/2) log2(e), r = rv the map's feature count (R, or fewer
+// when the kernel runs a narrower map with its extra features masked).
 template <int R, int DK>
-__device__ __forceinline__ float favor_take_x(const bf16x8 (&raw)[DK / 32], bf16x8 (&x)[DK / 32]) {
+__device__ __forceinline__ float favor_take_x(const bf16x8 (&raw)[DK / 32], bf16x8 (&x)[DK / 32], int rv = R) {
   float ss = 0.f;
 #pragma unroll
   for (int ks = 0; ks < DK / 32; ++ks) {
@@ -148,7 +149,7 @@ __device__ __forceinline__ float favor_take_x(const bf16x8 (&raw)[DK / 32], bf16
       ss += xv * xv;
     }
   }
-  return (0.5f * sum_over_groups(ss) + 0.5f * __logf(float(R))) * 1.44269504f;
+  return (0.5f * sum_over_groups(ss) + 0.5f * __logf(float(rv))) * 1.44269504f;
 }
 
 // hi/lo bf16 pairs of four floats (packed two per dword).
@@ -250,10 +251,13 @@ __device__ __forceinline__ void favor_store_pair(char* sm, int hi_at, int lo_at,
 // rows, omega rows from the cache). Keys past the chunk's valid rows are zero.
 // With WEIGHTED, keys are also written multiplied by gamma^(L-1-t) (RetNet
 // state update) into (wh_off, wl_off); with ONLY_WEIGHTED that is the only copy.
+// Features at or past rv (a narrower map run on these R-wide kernels, its
+// omega zero-padded to R rows) are zero.
 template <int R, int DK, bool IS_K, bool WEIGHTED, bool ONLY_WEIGHTED, class LN>
 __device__ __forceinline__ void favor_project(const LN& ln, const bf16x8 (&x)[DK / 32], float shift2,
                                               const bf16x8 (&om)[FavorBlock<R>::FT][DK / 32], int L, float lg2gam,
-                                              char* sm, int hi_off, int lo_off, int wh_off, int wl_off, int w) {
+                                              char* sm, int hi_off, int lo_off, int wh_off, int wl_off, int w,
+                                              int fb = 0, int rv = R) {
   using F = FavorBlock<R>;
   constexpr int KS = DK / 32;
   const int t = 16 * w + ln.c16;
@@ -271,6 +275,11 @@ __device__ __forceinline__ void favor_project(const LN& ln, const bf16x8 (&x)[DK
       // acc[i] = P[token t][block feature 16 (2 h + u) + 4 g + i]
 #pragma unroll
       for (int i = 0; i < 4; ++i) f[u][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], 1.44269504f, -shift2));
+      if (R == F::FB && rv < R) {  // only the one-block kernels serve narrower maps
+        const int f0 = F::FB * fb + 16 * (2 * h + u) + 4 * ln.g4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[u][i] = f0 + i < rv ? f[u][i] : 0.f;
+      }
     }
     // logical chunk 4 h + g of row t
     const int at = F::TILE16 * w + ln.row[h];
@@ -408,6 +417,7 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
   const SeqView sv = seq_view(a, bh);
+  const int rvalid = a.r_valid > 0 ? a.r_valid : R;  // features of the map (the rest are masked)
   const int t_begin = s * a.seg_len;
   // only segments that a later segment of the same sequence follows
   if (t_begin + a.seg_len >= sv.len) return;
@@ -440,7 +450,7 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
     const int L = min(kChunk, sv.len - t0);
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
     bf16x8 xk[DK / 32];
-    const float shk = favor_take_x<R, DK>(raw.xk, xk);
+    const float shk = favor_take_x<R, DK>(raw.xk, xk, rvalid);
     favor_write_v<E>(raw.v, sm, LY::v_off, lane, w);
     // the raw registers are free: the next chunk's loads fly during this one
     raw.load(a, tok0, t0 + kChunk, t_end, lane, w);
@@ -449,7 +459,8 @@ __global__ __launch_bounds__(256) void favor_segment_state(CausalArgs a) {
       const LN ln(opaque_lane(lane));
       // pass 1 keeps only the keys of the state update (decay-weighted for RetNet)
       favor_project<R, DK, true, GATE == GT_DECAY, GATE == GT_DECAY>(ln, xk, shk, om, L, lg2gam, sm, LY::kh_off,
-                                                                     LY::kl_off, LY::kh_off, LY::kl_off, w);
+                                                                     LY::kl_off, LY::kh_off, LY::kl_off, w, fb,
+                                                                     rvalid);
       // next block (block 0 of the next chunk)
       if constexpr (OM_LDS)
         favor_lds_omega<R, DK>(om, sm, LY::om_off, fb + 1 < F::NFB ? fb + 1 : 0, ln);
@@ -487,6 +498,7 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   const long long bh = blockIdx.y;
   const int h = int(bh % a.H);
   const SeqView sv = seq_view(a, bh);
+  const int rvalid = a.r_valid > 0 ? a.r_valid : R;  // features of the map (the rest are masked)
   const int t_begin = s * a.seg_len;
   if (s > 0 && t_begin >= sv.len) return;  // past the end of this sequence
   const int t_end = min(sv.len, t_begin + a.seg_len);
@@ -530,7 +542,7 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
   for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int L = min(kChunk, sv.len - t0);
     bf16x8 xq[DK / 32], xk[DK / 32];
-    const float shq = favor_take_x<R, DK>(raw.xq, xq), shk = favor_take_x<R, DK>(raw.xk, xk);
+    const float shq = favor_take_x<R, DK>(raw.xq, xq, rvalid), shk = favor_take_x<R, DK>(raw.xk, xk, rvalid);
     favor_write_v<E>(raw.v, sm, LY::v_off, lane, w);
     // the raw registers are free: the next chunk's loads fly during this one
     raw.load(a, tok0, t0 + kChunk, t_end, lane, w);
@@ -548,9 +560,10 @@ __global__ __launch_bounds__(256, 2) void favor_chunk_forward(CausalArgs a) {
     for (int fb = 0; fb < F::NFB; ++fb) {
       const LN ln(opaque_lane(lane));
       const bool last = fb == F::NFB - 1;
-      favor_project<R, DK, false, false, false>(ln, xq, shq, om, L, lg2gam, sm, LY::qh_off, LY::ql_off, 0, 0, w);
+      favor_project<R, DK, false, false, false>(ln, xq, shq, om, L, lg2gam, sm, LY::qh_off, LY::ql_off, 0, 0, w, fb,
+                                                rvalid);
       favor_project<R, DK, true, GATE == GT_DECAY, false>(ln, xk, shk, om, L, lg2gam, sm, LY::kh_off, LY::kl_off,
-                                                          LY::kwh_off, LY::kwl_off, w);
+                                                          LY::kwh_off, LY::kwl_off, w, fb, rvalid);
       favor_load_omega<R, DK>(om, a.omega, fb + 1 < F::NFB ? fb + 1 : 0, ln);  // next block (block 0 of the next chunk)
       lds_barrier();
 
@@ -702,6 +715,7 @@ la_status run_causal_favor(const FwdPlan& p) {
   a.V = static_cast<const bf16*>(p.V);
   a.omega = static_cast<const bf16*>(p.omega);
   a.gamma = p.gamma;
+  a.r_valid = p.r_valid;
   a.out = static_cast<bf16*>(p.out);
   a.cu = p.cu;
   a.slot = p.slot;

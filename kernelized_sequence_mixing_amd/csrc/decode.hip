@@ -233,6 +233,7 @@ la_status launch_decode(const DecodePlan& p) {
     return LA_ERR_UNSUPPORTED;
   }
   switch (p.r) {
+    case 32: return dec_favor_by_dk<32>(p);
     case 64: return dec_favor_by_dk<64>(p);
     case 128: return dec_favor_by_dk<128>(p);
     case 256: return dec_favor_by_dk<256>(p);

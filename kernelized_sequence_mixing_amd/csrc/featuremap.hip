@@ -64,6 +64,7 @@ la_status launch_feature_map(const FmapPlan& p) {
     return LA_ERR_UNSUPPORTED;
   }
   switch (p.r) {
+    case 32: return fm_favor_by_dk<32>(p);
     case 64: return fm_favor_by_dk<64>(p);
     case 128: return fm_favor_by_dk<128>(p);
     case 256: return fm_favor_by_dk<256>(p);

@@ -115,6 +115,7 @@ la_status launch_noncausal(const FwdPlan& p) {
     return LA_ERR_UNSUPPORTED;
   }
   switch (p.r) {
+    case 32: return nc_favor_by_dk<32>(p);
     case 64: return nc_favor_by_dk<64>(p);
     case 128: return nc_favor_by_dk<128>(p);
     case 256: return nc_favor_by_dk<256>(p);

@@ -23,6 +23,7 @@ int causal_output_lds_bytes(int fmap, int r, int dv, int dk, int gate);
 
 struct FwdPlan {
   int B, H, n, dk, dv, r;
+  int r_valid;  // FAVOR+ run on kernels wider than its map: the map's feature count (0 = r)
   int in_dtype, out_dtype;
   float eps;
   int fmap, gate, causal;
@@ -153,9 +154,10 @@ la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, cons
 la_status launch_backward(const BwdPlan& p);
 la_status launch_noncausal_backward(const BwdPlan& p);  // ws_S, ws_z: partial S, z; ws_R, ws_rh: partial G, hq
 la_status launch_noncausal(const FwdPlan& p);
-// dst[row][c] = src[row][c] for c < cols, 0 for cols <= c < width (rows of src_ld / dst_ld elements, esz bytes)
-la_status launch_copy_columns(const void* src, void* dst, long long rows, int src_ld, int dst_ld, int cols, int width,
-                              int esz, hipStream_t st);
+// dst[h][i][j] = src[h][i][j] inside src's [src_rows][src_cols], 0 elsewhere in dst's [dst_rows][dst_cols]
+// (heads of each, contiguous, esz bytes per element): zero-padded or cropped copies
+la_status launch_copy_block(const void* src, void* dst, long long heads, int src_rows, int src_cols, int dst_rows,
+                            int dst_cols, int esz, hipStream_t st);
 la_status launch_decode(const DecodePlan& p);
 la_status launch_feature_map(const FmapPlan& p);
 la_status launch_softmax(const SoftmaxPlan& p);

@@ -411,6 +411,7 @@ BAD_BATCH = [
     ("ws small", dict(ws_bytes=16), {}, N.LA_ERR_WORKSPACE),
     ("d_v 32 multi-token", dict(d_v=32), {}, N.LA_ERR_UNSUPPORTED),
     ("d_v 32 ragged", dict(B=1, d_v=32), dict(cu=FAKE + 23 * SP, num_seqs=4, max_seqlen=50), N.LA_ERR_UNSUPPORTED),
+    ("favor r 32 multi-token", dict(fkind=N.LA_FMAP_FAVOR, r=32, omega=FAKE + 5 * SP), {}, N.LA_ERR_UNSUPPORTED),
 ]
 
 
@@ -482,6 +483,22 @@ def test_causal_dv32_workspace():
         assert size(32, gk) == up(size(64, gk)) + pads
     # one segment: only the copies
     assert size(32, B=1, H=1, n=64) == 2 * up(64 * 64 * 2) + 2 * up(64 * 64 * 4)
+
+    # FAVOR+ r = 32: the 64-feature problem's segment states, omega padded to 64 rows (bf16),
+    # S0 / S_final copies [B H 64 d_v] and z0 / z_final copies [B H 64] (fp32)
+    def fsize(r, dv, B=2, H=3, n=3000, d=64):
+        p = N.LaProblem(B, H, n, d, dv, N.LA_BF16, N.LA_BF16, 1e-6)
+        f = N.LaFeatureMap(N.LA_FMAP_FAVOR, r, ctypes.c_void_p(FAKE))
+        g = N.LaGate(N.LA_GATE_NONE, 16.0, None, None)
+        out = ctypes.c_size_t(0)
+        assert lib.la_forward_workspace_size(ctypes.byref(p), ctypes.byref(f), 1, ctypes.byref(g),
+                                             ctypes.byref(out)) == N.LA_OK
+        return out.value
+    BH = 6
+    assert fsize(32, 64) == up(fsize(64, 64)) + up(64 * 64 * 2) + 2 * up(BH * 64 * 64 * 4) + 2 * up(BH * 64 * 4)
+    # both at once: r = 32 and d_v = 32
+    assert fsize(32, 32) == (up(fsize(64, 64)) + 2 * up(BH * 3000 * 64 * 2) + up(64 * 64 * 2) +
+                             2 * up(BH * 64 * 64 * 4) + 2 * up(BH * 64 * 4))
 
 
 @needs_lib
