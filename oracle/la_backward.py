@@ -16,7 +16,9 @@ chain rule written out step by step below; nothing is blocked or reordered.
 
 Gates covered: none, the RetNet decay (gamma is a fixed per-head constant, so
 it has no gradient), the diagonal GLA gate, whose raw input g also gets a
-gradient (``backward_gla``), and the selective scalar gate (``backward_sel``).
+gradient (``backward_gla``), the selective scalar gate (``backward_sel``) and
+the outer-product gate, with gradients of both raw inputs g and gv
+(``backward_outer``).
 Pinned by ``tests/test_oracle_backward_pins.py`` against central finite differences of
 the pinned forward oracle and against closed forms.
 """
@@ -26,8 +28,8 @@ import numpy as np
 
 from .la_oracle import feature_map, normalised
 
-__all__ = ["feature_map_vjp", "forward_terms", "backward", "backward_gla", "backward_sel", "backward_gla_rows",
-           "backward_sel_rows"]
+__all__ = ["feature_map_vjp", "forward_terms", "backward", "backward_gla", "backward_sel", "backward_outer",
+           "backward_gla_rows", "backward_sel_rows"]
 
 
 def _f64(a):
@@ -223,6 +225,81 @@ def backward_sel(Q, K, V, dO, g, tau, fmap="elu1", omega=None, eps=1e-6, S0=None
     G = np.repeat(g[..., None], r, axis=-1)
     dQ, dK, dV, dG = backward_gla(Q, K, V, dO, G, tau, fmap, omega, eps, S0, z0)
     return dQ, dK, dV, dG.sum(axis=-1)
+
+
+def backward_outer(Q, K, V, dO, g, gv, tau, fmap="elu1", omega=None, eps=1e-6, S0=None, z0=None):
+    """(dQ, dK, dV, dg, dgv) of L = sum_i dO_i . o_i for the causal form with
+    the outer-product gate G_t = alpha_t beta_t^T, all float64.
+
+    Forward (the dileepadev page, "Gating and Selective State Updates", a gate
+    matrix applied elementwise to the state; read as a key-side factor
+    alpha_t = sigmoid(g_t)^(1/tau) per feature times a value-side factor
+    beta_t = sigmoid(gv_t)^(1/tau) per value column, z gated by alpha only):
+    with A_t = sum_{u<=t} log alpha_u and C_t = sum_{u<=t} log beta_u,
+      W_ij   = sum_k phi(q_i)_k phi(k_j)_k exp(A_ik - A_jk)          (j <= i)
+      num_ie = sum_{j<=i} W_ij v_je exp(C_ie - C_je) + exp(C_ie) sum_k phi(q_i)_k exp(A_ik) S0_ke
+      den_i  = sum_{j<=i} W_ij + sum_k phi(q_i)_k exp(A_ik) z0_k + eps,   o_i = num_i / den_i.
+    Chain rule, written out:
+      g_i = dO_i / den_i,  h_i = -(dO_i . o_i) / den_i
+      dW_ij = sum_e g_ie v_je exp(C_ie - C_je) + h_i      (num and den through W_ij)
+      dv_je = sum_{i>=j} W_ij g_ie exp(C_ie - C_je)
+      dphi_q, dphi_k and dA_t = dphi_q_t phi_q_t - dphi_k_t phi_k_t as in
+        ``backward_gla`` with this dW (the carried state adds
+        exp(A_ik) (sum_e S0_ke exp(C_ie) g_ie + z0_k h_i) to dphi_q_ik)
+      dC_te = g_te num_te - dv_te v_te   (C_t enters num_t with + and every
+        later query's pair with key t with -)
+      d log alpha_u = sum_{t>=u} dA_t,  d log beta_u = sum_{t>=u} dC_t
+      dg = d log alpha sigmoid(-g) / tau,  dgv = d log beta sigmoid(-gv) / tau.
+    """
+    V = _f64(V)
+    dO = _f64(dO)
+    g = _f64(g)
+    gv = _f64(gv)
+    pq = feature_map(Q, fmap, omega)
+    pk = feature_map(K, fmap, omega)
+    B, H, n, r = pq.shape
+    with np.errstate(over="ignore"):
+        loga = -np.logaddexp(0.0, -g) / float(tau)
+        logb = -np.logaddexp(0.0, -gv) / float(tau)
+    Ac = np.cumsum(loga, axis=2)                                  # [B, H, n, r]
+    Cc = np.cumsum(logb, axis=2)                                  # [B, H, n, d_v]
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    mask = (j <= i)
+    Dk = np.where(mask[None, None, :, :, None], np.exp(np.minimum(Ac[:, :, :, None, :] - Ac[:, :, None, :, :], 0.0)),
+                  0.0)                                            # [B, H, i, j, r]
+    Dv = np.where(mask[None, None, :, :, None], np.exp(np.minimum(Cc[:, :, :, None, :] - Cc[:, :, None, :, :], 0.0)),
+                  0.0)                                            # [B, H, i, j, d_v]
+    W = np.einsum("bhik,bhjk,bhijk->bhij", pq, pk, Dk)
+    num = np.einsum("bhij,bhije,bhje->bhie", W, Dv, V)
+    den = W.sum(axis=-1) + eps
+    ca = np.exp(Ac)
+    cb = np.exp(Cc)
+    if S0 is not None:
+        S0 = _f64(S0)
+        z0 = _f64(z0)
+        num = num + cb * np.einsum("bhik,bhke->bhie", pq * ca, S0)
+        den = den + np.einsum("bhik,bhk->bhi", pq * ca, z0)
+    if not normalised(fmap):
+        den = np.ones_like(den)   # the state-space read-out o = num
+    o = num / den[..., None]
+    gg = dO / den[..., None]
+    h = -np.sum(dO * o, axis=-1) / den if normalised(fmap) else np.zeros(den.shape)
+    dW = (np.einsum("bhie,bhije,bhje->bhij", gg, Dv, V) + h[..., None]) * mask[None, None]
+    dV = np.einsum("bhij,bhije,bhie->bhje", W, Dv, gg)
+    dpq = np.einsum("bhij,bhjk,bhijk->bhik", dW, pk, Dk)
+    dpk = np.einsum("bhij,bhik,bhijk->bhjk", dW, pq, Dk)
+    if S0 is not None:
+        dpq = dpq + ca * (np.einsum("bhke,bhie->bhik", S0, gg * cb) + h[..., None] * z0[:, :, None, :])
+    dA = dpq * pq - dpk * pk
+    dC = gg * num - dV * V
+    suffix = lambda x: np.flip(np.cumsum(np.flip(x, axis=2), axis=2), axis=2)
+    with np.errstate(over="ignore"):
+        dg = suffix(dA) / (1.0 + np.exp(g)) / float(tau)
+        dgv = suffix(dC) / (1.0 + np.exp(gv)) / float(tau)
+    dQ = feature_map_vjp(Q, dpq, fmap, omega)
+    dK = feature_map_vjp(K, dpk, fmap, omega)
+    return dQ, dK, dV, dg, dgv
 
 
 def backward_gla_rows(Q, K, V, dO, g, tau, fmap="elu1", eps=1e-6, rows=(), tail=0, return_forward=False):

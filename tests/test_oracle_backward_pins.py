@@ -148,6 +148,85 @@ def test_gla_unit_gates_reduce_to_ungated():
     assert np.all(got[3] == 0.0)
 
 
+@pytest.mark.parametrize("fmap,with_state", [("elu1", False), ("elu1", True), ("identity", True)])
+def test_outer_gradients_match_finite_differences(fmap, with_state):
+    """The outer-product gate: dQ, dK, dV and the gradients of both raw gate
+    inputs (g per feature, gv per value column) against central differences of
+    the recurrent oracle, which applies (alpha_t beta_t^T) * S step by step."""
+    B, H, n, d, e = 1, 2, 8, 4, 3
+    tau = 3.0
+    Q = RNG.standard_normal((B, H, n, d)) * 0.7
+    K = RNG.standard_normal((B, H, n, d)) * 0.7
+    V = RNG.standard_normal((B, H, n, e))
+    G = RNG.standard_normal((B, H, n, d))
+    GV = RNG.standard_normal((B, H, n, e))
+    dO = RNG.standard_normal((B, H, n, e))
+    S0 = z0 = None
+    if with_state:
+        S0 = RNG.standard_normal((B, H, d, e))
+        z0 = np.abs(RNG.standard_normal((B, H, d))) + 0.5
+    eps = 1e-3
+    grads = bwd.backward_outer(Q, K, V, dO, G, GV, tau, fmap, None, eps, S0, z0)
+    assert grads[3].shape == G.shape and grads[4].shape == GV.shape
+
+    def loss(Q_, K_, V_, G_, GV_):
+        o, _, _ = orc.causal_recurrent(Q_, K_, V_, fmap, None, ("outer", G_, GV_, tau), eps, S0=S0, z0=z0)
+        return float(np.sum(o * dO))
+    step = 1e-6
+    for idx, (X, Gr) in enumerate(zip((Q, K, V, G, GV), grads)):
+        U = RNG.standard_normal(X.shape)
+        args = [Q, K, V, G, GV]
+        args[idx] = X + step * U
+        lp = loss(*args)
+        args[idx] = X - step * U
+        lm = loss(*args)
+        fd = (lp - lm) / (2 * step)
+        an = float(np.sum(Gr * U))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (idx, fd, an)
+
+
+def test_outer_unit_value_gate_reduces_to_gla():
+    """beta = 1 (gv = +inf) is the GLA gate: the same dQ, dK, dV, dg as
+    backward_gla, and dgv = 0."""
+    B, H, n, d, e = 1, 2, 7, 4, 3
+    Q = RNG.standard_normal((B, H, n, d))
+    K = RNG.standard_normal((B, H, n, d))
+    V = RNG.standard_normal((B, H, n, e))
+    G = RNG.standard_normal((B, H, n, d))
+    dO = RNG.standard_normal((B, H, n, e))
+    S0 = RNG.standard_normal((B, H, d, e))
+    z0 = np.abs(RNG.standard_normal((B, H, d))) + 0.5
+    GV = np.full((B, H, n, e), np.inf)
+    got = bwd.backward_outer(Q, K, V, dO, G, GV, 2.0, "elu1", None, 1e-3, S0, z0)
+    want = bwd.backward_gla(Q, K, V, dO, G, 2.0, "elu1", None, 1e-3, S0, z0)
+    for a, b in zip(got[:4], want):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    assert np.all(got[4] == 0.0)
+
+
+def test_outer_single_step_value_gate_closed_form():
+    """One step after a carried state: o_e = (beta_e phi(q)^T S0[:, e] + w v_e) /
+    (phi(q).z0 + w + eps) with w = phi(q).phi(k) (alpha = 1, beta_e =
+    sigmoid(gv_e)^(1/tau)); dL/dgv_e = dO_e phi(q)^T S0[:, e] / den *
+    beta_e sigmoid(-gv_e) / tau."""
+    d, e, tau, eps = 3, 2, 4.0, 1e-3
+    q = RNG.standard_normal(d)
+    k = RNG.standard_normal(d)
+    v = RNG.standard_normal(e)
+    dO = RNG.standard_normal(e)
+    S0 = RNG.standard_normal((d, e))
+    z0 = np.abs(RNG.standard_normal(d)) + 0.5
+    gv = np.array([0.3, -1.1])
+    pq, pk = orc.feature_map(q, "elu1"), orc.feature_map(k, "elu1")
+    beta = (1.0 / (1.0 + np.exp(-gv))) ** (1.0 / tau)
+    den = pq @ z0 + pq @ pk + eps
+    want = dO * (pq @ S0) / den * beta * (1.0 / (1.0 + np.exp(gv))) / tau
+    sh = lambda x: x.reshape((1, 1) + x.shape)
+    got = bwd.backward_outer(sh(q[None]), sh(k[None]), sh(v[None]), sh(dO[None]), np.full((1, 1, 1, d), np.inf),
+                             sh(gv[None]), tau, "elu1", None, eps, sh(S0), sh(z0))[4]
+    np.testing.assert_allclose(got[0, 0, 0], want, rtol=1e-12, atol=1e-15)
+
+
 def test_identity_gradients_closed_form():
     """The state-space read-out y = tril(Q K^T) V is bilinear: dV = tril(Q K^T)^T dO,
     dQ = tril(dO V^T) K, dK = tril(dO V^T)^T Q (numpy matmuls)."""
