@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 6
+#define LA_ABI_VERSION 7
 
 typedef enum la_status {
   LA_OK = 0,
@@ -297,25 +297,35 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  * The selective scalar gate is that gate with alpha_t = a_t on every feature,
  * so its dg_t is the sum over features of the per-feature dg_t (the library
  * runs the GLA passes on g repeated over features and sums their dg).
+ * The outer-product gate G_t = alpha_t beta_t^T adds a value-side factor
+ * beta_t = sigmoid(gv_t)^(1/tau) per column (z takes the key side only):
+ * with C_t = sum_{u<=t} log beta_u, the pairs carry exp(C_i - C_j) per value
+ * column, dg follows the GLA rule, and
+ *   dC_t = dO_t * o_t - dV_t * v_t   (per column),
+ *   dgv_u = (sum_{t>=u} dC_t) * sigmoid(-gv_u) / tau.
  *   Q, K, dQ, dK [B][H][n][d_k]; V, dO, dV [B][H][n][d_v]; all BF16 (in_dtype and
  *   out_dtype must be BF16). S0, z0: the optional carried-in state of the forward
  *   (both or neither; fp32). gamma and tau are constants: no gradient is returned
  *   for them, nor for S0, z0.
- *   dg: the gradient of gate->g, BF16 in its shape ([B][H][n][r] for GLA,
- *   [B][H][n] for SEL); required (non-NULL) with those gates and must be NULL
- *   otherwise (else LA_ERR_INVALID_ARG).
+ *   dg: the gradient of gate->g, BF16 in its shape ([B][H][n][r] for GLA and
+ *   OUTER, [B][H][n] for SEL); required (non-NULL) with those gates and must be
+ *   NULL otherwise (else LA_ERR_INVALID_ARG).
+ *   dgv: the gradient of gate->gv, BF16 [B][H][n][d_v]; required with OUTER and
+ *   must be NULL otherwise (else LA_ERR_INVALID_ARG).
  *   workspace: device scratch of at least la_backward_workspace_size bytes,
  *   256-byte aligned (segment states of both directions, g and h per token;
- *   GLA and SEL: also dQ~ . Q~ per token and feature and per-segment summed
- *   log-gates; SEL: also g repeated over features and its per-feature dg).
+ *   GLA, SEL and OUTER: also dQ~ . Q~ per token and feature and per-segment
+ *   summed log-gates; SEL: also g repeated over features and its per-feature
+ *   dg; OUTER: also dO * o per token and value column (fp32) and per-segment
+ *   summed value-side log-gates).
  * causal == 0 (the non-causal form, "The linear attention trick", sadullah
  * page: dphi(q_i) = S g_i + z h_i, dphi(k_j) = G v_j + hq, dv_j = G^T phi(k_j)
  * with G = sum_i phi(q_i) g_i^T, hq = sum_i phi(q_i) h_i): ELU1, no gate, no
  * S0/z0 (else LA_ERR_INVALID_ARG), in_dtype == out_dtype in {F32, BF16} with
  * the gradients in that dtype, the forward's (d_k, d_v) set; fp32 arithmetic.
  * Supported (else LA_ERR_UNSUPPORTED) for causal == 1: ELU1 or IDENTITY (the
- * state-space read-out: g_i = dO_i, h_i = 0, phi' = 1), gate NONE, DECAY, GLA
- * or SEL (not OUTER), (d_k, d_v) in {(64, 64), (64, 128), (128, 64), (128, 128)}
+ * state-space read-out: g_i = dO_i, h_i = 0, phi' = 1), gate NONE, DECAY, GLA,
+ * SEL or OUTER, (d_k, d_v) in {(64, 64), (64, 128), (128, 64), (128, 128)}
  * (128 x 128 runs as two 64-column value halves); FAVOR ("Choosing the Feature
  * Map phi", dileepadev page) with gate NONE or DECAY, d_k in {32, 64, 128},
  * r in {64, 128}, (r, d_v) in the same set: phi(Q), phi(K) are materialised in
@@ -324,13 +334,15 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  * takes it back through the map (fp32, omega as given). Outputs must not overlap the
  * inputs, each other or the workspace (LA_ERR_ALIAS). Numerics as la_forward:
  * bf16 MFMA operands (phi, values, g, the scores and dW), fp32 accumulation,
- * states, denominators and the sums behind dg.
+ * states, denominators and the sums behind dg and dgv. OUTER has the forward's
+ * gate-input precondition (the summed log alpha and log beta of every 64-token
+ * chunk at or above -80).
  */
 la_status la_backward(const la_problem* p, const void* Q, const void* K, const void* V,
                       const void* dO, const la_feature_map* fmap, int32_t causal,
                       const la_gate* gate, const float* S0, const float* z0, void* dQ,
-                      void* dK, void* dV, void* dg, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      void* dK, void* dV, void* dg, void* dgv, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent step for a batch of carried states, updated IN PLACE

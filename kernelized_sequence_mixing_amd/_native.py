@@ -87,7 +87,7 @@ def lib():
     L.la_backward.restype = c_int32
     L.la_backward.argtypes = [POINTER(LaProblem), c_void_p, c_void_p, c_void_p, c_void_p, POINTER(LaFeatureMap),
                               c_int32, POINTER(LaGate), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                              c_void_p, c_size_t, c_void_p]
+                              c_void_p, c_void_p, c_size_t, c_void_p]
     L.la_decode_step.restype = c_int32
     L.la_decode_step.argtypes = [POINTER(LaProblem), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  POINTER(LaFeatureMap), POINTER(LaGate), c_void_p, c_void_p]

@@ -336,7 +336,8 @@ class PreparedForwardBatch:
 
 def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, stream, causal=True, omega=None):
     """Validate and marshal one la_backward call: (ctypes arguments, keep-alive objects, gradients), the
-    gradients being (dQ, dK, dV), plus dg with a gate input (GLA, selective)."""
+    gradients being (dQ, dK, dV), plus dg with a gate input (GLA, selective, outer-product) and dgv with
+    the outer-product gate's value side."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (dO, "dO")):
         _dev(t, nm)
     if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3] or dO.shape != V.shape:
@@ -354,16 +355,24 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
             _dev(t, nm)
             if tuple(t.shape) != shp or t.dtype != torch.float32:
                 raise ValueError(f"{nm} must be float32 {shp}")
-    gla = g.kind in (N.LA_GATE_GLA, N.LA_GATE_SEL)  # gates with an input, whose gradient dg is returned
+    # gates with an input, whose gradient dg is returned; the outer-product gate adds dgv
+    gla = g.kind in (N.LA_GATE_GLA, N.LA_GATE_SEL, N.LA_GATE_OUTER)
+    outer = g.kind == N.LA_GATE_OUTER
     if grads is None:
         grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
         if gla:
             grads = grads + (torch.empty_like(gate[1]),)
-    if len(grads) != (4 if gla else 3):
-        raise ValueError("grads must be (dQ, dK, dV)" + (" plus dg with a gate input" if gla else ""))
+        if outer:
+            grads = grads + (torch.empty_like(gate[2]),)
+    if len(grads) != 3 + int(gla) + int(outer):
+        raise ValueError("grads must be (dQ, dK, dV)" + (" plus dg with a gate input" if gla else "") +
+                         (" and dgv" if outer else ""))
     dQ, dK, dV = grads[:3]
     dg = grads[3] if gla else None
-    for t, ref, nm in ((dQ, Q, "dQ"), (dK, K, "dK"), (dV, V, "dV")) + (((dg, gate[1], "dg"),) if gla else ()):
+    dgv = grads[4] if outer else None
+    checks = ((dQ, Q, "dQ"), (dK, K, "dK"), (dV, V, "dV")) + (((dg, gate[1], "dg"),) if gla else ()) + \
+        (((dgv, gate[2], "dgv"),) if outer else ())
+    for t, ref, nm in checks:
         _dev(t, nm)
         if t.shape != ref.shape or t.dtype != ref.dtype:
             raise ValueError(f"{nm} has the wrong shape or dtype")
@@ -375,7 +384,7 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     args = (ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), ctypes.byref(f), int(bool(causal)), ctypes.byref(g),
             _ptr(S0),
-            _ptr(z0), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dg), _ptr(workspace), need, _stream(Q, stream))
+            _ptr(z0), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dg), _ptr(dgv), _ptr(workspace), need, _stream(Q, stream))
     keep = (p, f, g, Q, K, V, dO, gate, S0, z0, workspace, omega)
     return args, keep, tuple(grads)
 
@@ -383,10 +392,12 @@ def _backward_args(Q, K, V, dO, fmap, gate, eps, S0, z0, grads, workspace, strea
 def backward(Q, K, V, dO, *, fmap="elu1", omega=None, gate=None, eps=1e-6, S0=None, z0=None, grads=None,
              workspace=None, stream=None, causal=True):
     """(dQ, dK, dV) of the causal forward for an incoming gradient dO, through la_backward;
-    (dQ, dK, dV, dg) with the GLA or the selective gate, dg the gradient of its raw input g.
+    (dQ, dK, dV, dg) with the GLA or the selective gate, dg the gradient of its raw input g;
+    (dQ, dK, dV, dg, dgv) with the outer-product gate, dgv the gradient of its value-side input gv.
 
     Q, K [B, H, n, d_k]; V, dO [B, H, n, d_v] (bf16); gate None | ("decay", gamma[H]) |
-    ("gla", g[B, H, n, d_k] bf16, tau) | ("sel", g[B, H, n] bf16, tau); S0, z0: the forward's
+    ("gla", g[B, H, n, d_k] bf16, tau) | ("sel", g[B, H, n] bf16, tau) |
+    ("outer", g[B, H, n, d_k], gv[B, H, n, d_v] bf16, tau); S0, z0: the forward's
     carried-in state, if any. fmap="favor" with omega [r, d_k] (r 64 or 128; no gate or the
     decay). causal=False: the non-causal form (elu+1, no gate, no state; fp32 or bf16,
     gradients in the input dtype)."""

@@ -257,8 +257,9 @@ la_status check_forward_shape(const la_problem* p, const la_feature_map* f, int 
   return LA_OK;
 }
 
-// The backward pass: causal elu+1, bf16 in and out, any gate,
-// (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}.
+// The backward pass: causal elu+1 or identity features with any gate, or
+// FAVOR+ without a gate input; bf16 in and out; (d_k, d_v) in {(64, 64),
+// (64, 128), (128, 64), (128, 128)}.
 la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int causal, const la_gate* g) {
   la_status st = check_problem(p);
   if (st != LA_OK) return st;
@@ -272,7 +273,6 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
     if (f->kind != LA_FMAP_ELU1 || p->in_dtype != p->out_dtype) return LA_ERR_UNSUPPORTED;
     return shapes_built(f, p->d_k, p->d_v, false) ? LA_OK : LA_ERR_UNSUPPORTED;
   }
-  if (gk == LA_GATE_OUTER) return LA_ERR_UNSUPPORTED;
   if (p->in_dtype != LA_BF16 || p->out_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   if (f->kind == LA_FMAP_FAVOR) {
     // the chunked kernels on the materialised features (r wide), then back through the map
@@ -293,14 +293,17 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
 bool backward_in_halves(const la_problem* p, int r) { return r == 128 && p->d_v == 128; }
 
 struct BwdWsLayout {
-  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, gx_off, dgx_off, s0h_off, fv_off, bytes;
+  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, gx_off, dgx_off, Pw_off, logGv_off, s0h_off,
+      fv_off, bytes;
   int P, L;
 };
 
 // Forward segment states, reverse segment states, g (bf16) and h per token;
 // GLA adds dQ~ . Q~ per token and feature and the segments' summed log-gates;
 // the selective scalar gate runs the GLA passes and adds its input repeated
-// over features and the per-feature gradient of that (bf16 [B][H][n][r] each).
+// over features and the per-feature gradient of that (bf16 [B][H][n][r] each);
+// the outer-product gate adds dO * o per token and value column (fp32) and
+// the segments' summed value-side log-gates.
 // The non-causal form: the splits' partial S, z (forward sums) and G, hq.
 BwdWsLayout nc_bwd_workspace_layout(const la_problem* p, const la_feature_map* f) {
   BwdWsLayout w{};
@@ -332,15 +335,19 @@ BwdWsLayout bwd_workspace_layout(const la_problem* p_in, const la_feature_map* f
   w.G_off = round_up(w.rh_off + zs, kAlign);
   w.h_off = round_up(w.G_off + BH * n * dv * 2, kAlign);
   w.dB_off = round_up(w.h_off + BH * n * 4, kAlign);
-  if (gate != LA_GATE_GLA && gate != LA_GATE_SEL) {
-    w.logG_off = w.gx_off = w.dgx_off = w.bytes = w.dB_off;
+  if (gate != LA_GATE_GLA && gate != LA_GATE_SEL && gate != LA_GATE_OUTER) {
+    w.logG_off = w.gx_off = w.dgx_off = w.Pw_off = w.logGv_off = w.bytes = w.dB_off;
   } else {
     const size_t n64 = (n + 63) / 64 * 64;  // dQ~ . Q~ is stored by whole chunks
     w.logG_off = round_up(w.dB_off + BH * n64 * r * 4, kAlign);
-    w.gx_off = w.dgx_off = w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
+    w.gx_off = w.dgx_off = w.Pw_off = w.logGv_off = w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
     if (gate == LA_GATE_SEL) {
       w.dgx_off = round_up(w.gx_off + BH * n * r * 2, kAlign);
       w.bytes = round_up(w.dgx_off + BH * n * r * 2, kAlign);
+    }
+    if (gate == LA_GATE_OUTER) {
+      w.logGv_off = round_up(w.Pw_off + BH * n * dv * 4, kAlign);
+      w.bytes = round_up(w.logGv_off + BH * w.P * dv * 4, kAlign);
     }
   }
   // value-column halves: one half of a carried-in state at a time, dense
@@ -770,7 +777,7 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
 
 la_status la_backward(const la_problem* p, const void* Q, const void* K, const void* V, const void* dO,
                       const la_feature_map* fmap, int32_t causal, const la_gate* gate, const float* S0,
-                      const float* z0, void* dQ, void* dK, void* dV, void* dg, void* workspace,
+                      const float* z0, void* dQ, void* dK, void* dV, void* dg, void* dgv, void* workspace,
                       size_t workspace_bytes, void* stream) {
   la_status st = check_backward_shape(p, fmap, causal, gate);
   if (st != LA_OK) return st;
@@ -779,29 +786,33 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   if (Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || dQ == nullptr || dK == nullptr ||
       dV == nullptr)
     return LA_ERR_INVALID_ARG;
-  const bool sel = gk == LA_GATE_SEL;
-  if ((dg != nullptr) != (gk == LA_GATE_GLA || sel)) return LA_ERR_INVALID_ARG;
+  const bool sel = gk == LA_GATE_SEL, outer = gk == LA_GATE_OUTER;
+  if ((dg != nullptr) != (gk == LA_GATE_GLA || sel || outer)) return LA_ERR_INVALID_ARG;
+  if ((dgv != nullptr) != outer) return LA_ERR_INVALID_ARG;
   if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_INVALID_ARG;
   if (!causal && S0 != nullptr) return LA_ERR_INVALID_ARG;  // the non-causal form has no carried state
   for (const void* ptr : {Q, K, V, dO, (const void*)S0, (const void*)z0, (const void*)dQ, (const void*)dK,
-                          (const void*)dV, (const void*)dg})
+                          (const void*)dV, (const void*)dg, (const void*)dgv})
     if (ptr != nullptr && !aligned16(ptr)) return LA_ERR_INVALID_ARG;
   const size_t BH = (size_t)p->B * p->H, n = (size_t)p->n, r = (size_t)fmap->r, isz = dtype_size(p->in_dtype);
   const size_t qk = BH * n * p->d_k * isz, vv = BH * n * p->d_v * isz, gg = BH * n * (sel ? 1 : r) * 2;
   const Range rq = range_of(Q, qk), rk = range_of(K, qk), rv = range_of(V, vv), rdo = range_of(dO, vv);
   const Range rgam = range_of(gk == LA_GATE_DECAY ? gate->gamma : nullptr, (size_t)p->H * 4);
   const Range rgl = range_of(gate_has_input(gk) ? gate->g : nullptr, gg);
+  const Range rgv = range_of(outer ? gate->gv : nullptr, vv);
   const Range rs0 = range_of(S0, BH * r * p->d_v * 4), rz0 = range_of(z0, BH * r * 4);
   const Range rom = range_of(fmap->kind == LA_FMAP_FAVOR ? fmap->omega : nullptr, r * p->d_k * isz);
   const Range rdq = range_of(dQ, qk), rdk = range_of(dK, qk), rdv = range_of(dV, vv), rdg = range_of(dg, gg);
+  const Range rdgv = range_of(dgv, vv);
   const BwdWsLayout wl = bwd_workspace_layout(p, fmap, gk, causal);
   const Range rws = range_of(workspace, wl.bytes);
-  for (Range o : {rdq, rdk, rdv, rdg, rws})
-    for (Range i : {rq, rk, rv, rdo, rgam, rgl, rs0, rz0, rom})
+  const Range outs[] = {rdq, rdk, rdv, rdg, rdgv, rws};
+  for (Range o : outs)
+    for (Range i : {rq, rk, rv, rdo, rgam, rgl, rgv, rs0, rz0, rom})
       if (overlaps(o, i)) return LA_ERR_ALIAS;
-  if (overlaps(rdq, rdk) || overlaps(rdq, rdv) || overlaps(rdk, rdv) || overlaps(rws, rdq) || overlaps(rws, rdk) ||
-      overlaps(rws, rdv) || overlaps(rdg, rdq) || overlaps(rdg, rdk) || overlaps(rdg, rdv) || overlaps(rdg, rws))
-    return LA_ERR_ALIAS;
+  for (size_t a = 0; a < 6; ++a)
+    for (size_t c = a + 1; c < 6; ++c)
+      if (overlaps(outs[a], outs[c])) return LA_ERR_ALIAS;
   if (workspace == nullptr || workspace_bytes < wl.bytes) return LA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return LA_ERR_WORKSPACE;
 
@@ -823,6 +834,7 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.V = V;
   plan.gamma = gk == LA_GATE_DECAY ? gate->gamma : nullptr;
   plan.g = gate_has_input(gk) ? gate->g : nullptr;
+  plan.gv = outer ? gate->gv : nullptr;
   plan.tau = gate_has_input(gk) ? gate->tau : 1.f;
   plan.S0 = S0;
   plan.z0 = z0;
@@ -837,10 +849,15 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.ws_rh = reinterpret_cast<float*>(ws + wl.rh_off);
   plan.ws_G = ws + wl.G_off;
   plan.ws_h = reinterpret_cast<float*>(ws + wl.h_off);
-  if (gk == LA_GATE_GLA || sel) {
+  if (gk == LA_GATE_GLA || sel || outer) {
     plan.ws_dB = reinterpret_cast<float*>(ws + wl.dB_off);
     plan.ws_logG = reinterpret_cast<float*>(ws + wl.logG_off);
     plan.dg = sel ? static_cast<void*>(ws + wl.dgx_off) : dg;
+  }
+  if (outer) {
+    plan.ws_P = reinterpret_cast<float*>(ws + wl.Pw_off);
+    plan.ws_logGv = reinterpret_cast<float*>(ws + wl.logGv_off);
+    plan.dgv = dgv;
   }
   plan.dO = dO;
   plan.dQ = dQ;
@@ -885,6 +902,10 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
       hp.V = static_cast<const bf16_bits*>(V) + k * half;
       hp.dO = static_cast<const bf16_bits*>(dO) + k * half;
       hp.dV = static_cast<bf16_bits*>(dV) + k * half;
+      if (outer) {  // this half's value columns of gv and dgv (row stride d_v)
+        hp.gv = static_cast<const bf16_bits*>(gate->gv) + k * half;
+        hp.dgv = static_cast<bf16_bits*>(dgv) + k * half;
+      }
       hp.accum = k;
       if (S0 != nullptr) {  // this half's columns of the carried-in state, dense ([BH][r][half]); z0 is shared
         if (hipMemcpy2DAsync(s0h, half * sizeof(float), S0 + k * half, p->d_v * sizeof(float), half * sizeof(float),

@@ -36,12 +36,18 @@ static la_status run_backward(const BwdPlan& p) {
   b.P = p.P;
   b.seg_len = p.seg_len;
   b.eps = p.eps;
-  if constexpr (GATE == GT_GLA) {
+  if constexpr (kKeyGate<GATE>) {
     b.gl = static_cast<const bf16*>(p.g);
     b.inv_tau = 1.f / p.tau;
     b.dB = p.ws_dB;
     b.logG = p.ws_logG;
     b.dg = static_cast<bf16*>(p.dg);
+  }
+  if constexpr (GATE == GT_OUTER) {
+    b.gvl = static_cast<const bf16*>(p.gv);
+    b.Pw = p.ws_P;
+    b.logGv = p.ws_logGv;
+    b.dgv = static_cast<bf16*>(p.dgv);
   }
   la_status st;
   // forward state entering each segment: the forward's segment pass and scan
@@ -60,8 +66,11 @@ static la_status run_backward(const BwdPlan& p) {
     a1.S_out = p.ws_S;
     a1.z_out = p.ws_z;
     a1.g = b.gl;
+    a1.gv = b.gvl;
+    a1.ldgv = b.ldv;
     a1.inv_tau = b.inv_tau;
     a1.logG_out = p.ws_logG;
+    a1.logGv_out = p.ws_logGv;
     if ((st = launch_segment_pass<R, E, R, FMAP, GATE>(a1, p.P, BH, p.stream)) != LA_OK) return st;
     if ((st = launch_segment_scan(p)) != LA_OK) return st;
     b.S_in = p.ws_S;
@@ -78,13 +87,15 @@ static la_status run_backward(const BwdPlan& p) {
       LA_OK)
     return st;
   if (p.P > 1) {
-    if constexpr (GATE == GT_GLA)
-      st = launch_with_lds(bwd_rstate_gla<R, E, FMAP>, dim3(p.P - 1, BH), BwdRGLayout<R, E>::bytes, p.stream, b);
+    if constexpr (kKeyGate<GATE>)
+      st = launch_with_lds(bwd_rstate_gla<R, E, GATE, FMAP>, dim3(p.P - 1, BH), BwdRGLayout<R, E, GATE>::bytes,
+                           p.stream, b);
     else
       st = launch_with_lds(bwd_rstate<R, E, GATE, FMAP>, dim3(p.P - 1, BH), BwdRLayout<R, E, GATE>::bytes, p.stream,
                            b);
     if (st != LA_OK) return st;
-    if ((st = launch_segment_scan_reverse(p, p.ws_R, p.ws_rh, GATE == GT_GLA ? p.ws_logG : nullptr)) != LA_OK)
+    if ((st = launch_segment_scan_reverse(p, p.ws_R, p.ws_rh, kKeyGate<GATE> ? p.ws_logG : nullptr,
+                                          GATE == GT_OUTER ? p.ws_logGv : nullptr)) != LA_OK)
       return st;
   }
   return launch_with_lds(bwd_pass_b<R, E, GATE, FMAP>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b);
@@ -96,6 +107,7 @@ static la_status run_backward_gated(const BwdPlan& p) {
     case LA_GATE_NONE: return run_backward<R, E, GT_NONE, FMAP>(p);
     case LA_GATE_DECAY: return run_backward<R, E, GT_DECAY, FMAP>(p);
     case LA_GATE_GLA: return run_backward<R, E, GT_GLA, FMAP>(p);
+    case LA_GATE_OUTER: return run_backward<R, E, GT_OUTER, FMAP>(p);
     default: return LA_ERR_UNSUPPORTED;
   }
 }
@@ -114,7 +126,7 @@ static la_status run_backward_fmap(const BwdPlan& p) {
 }
 
 // Built shapes: elu+1 or the state-space form with (d_k, d_v) in {(64, 64), (64, 128), (128, 64)}; no gate,
-// RetNet decay or GLA. (128, 128) runs as two (128, 64) halves of the value
+// RetNet decay, GLA or the outer-product gate. (128, 128) runs as two (128, 64) halves of the value
 // columns (la_backward).
 la_status launch_backward(const BwdPlan& p) {
   switch (p.r * 1000 + p.dv) {

@@ -64,7 +64,12 @@ struct BwdArgs {
   float* dB;       // dQ~ . Q~ (pass A, read by pass B), in the order of dbq_at
   float* logG;     // [B H P R] summed log-gate of each segment (bwd_rstate_gla)
   bf16* dg;        // [B H n R]
-  int ldv;         // elements between rows of V, dO and dV (a value-column half of a wider V)
+  // outer-product gate (per value column: beta = sigmoid(gv)^(1/tau))
+  const bf16* gvl;  // [B H n ldv] raw value-side gate input
+  float* Pw;        // [B H n E] g * num (= dO * o) per token and column (pass A), read by pass B
+  float* logGv;     // [B H P E] summed value-side log-gate of each segment
+  bf16* dgv;        // [B H n ldv]
+  int ldv;         // elements between rows of V, dO, dV, gv and dgv (a value-column half of a wider V)
   int accum;       // add dQ, dK, dg to what the arrays hold (the second value-column half)
   int H, n, P, seg_len;
   float eps, inv_tau;
@@ -114,9 +119,11 @@ struct RowsE {
 };
 
 // bf16 image of a wave's state slab (rows all R, value columns [w E/4, (w+1) E/4))
-// into an [R][E] tile (FeatTile<E> rows), for products that contract over E.
+// into an [R][E] tile (FeatTile<E> rows), for products that contract over E;
+// with colscale_off >= 0 each column is first scaled by the fp32 factor there.
 template <int R, int E, class SArr>
-__device__ __forceinline__ void state_image(const SArr& S, char* sm, int off, int lane, int w) {
+__device__ __forceinline__ void state_image(const SArr& S, char* sm, int off, int lane, int w,
+                                            int colscale_off = -1) {
   constexpr int NEB = E / 64;
   const int g4 = lane >> 4, c16 = lane & 15, ebase = w * (E / 4);
 #pragma unroll
@@ -124,9 +131,10 @@ __device__ __forceinline__ void state_image(const SArr& S, char* sm, int off, in
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
       const int e = ebase + 16 * eb + c16;
+      const float cs = colscale_off >= 0 ? lds<float>(sm, colscale_off + 4 * e) : 1.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        lds<bf16>(sm, off + FeatTile<E>::at(16 * rt + 4 * g4 + i, e / 8, 2 * (e % 8))) = (bf16)S[rt][eb][i];
+        lds<bf16>(sm, off + FeatTile<E>::at(16 * rt + 4 * g4 + i, e / 8, 2 * (e % 8))) = (bf16)(S[rt][eb][i] * cs);
     }
 }
 
@@ -161,9 +169,9 @@ struct BwdALayout {
   static constexpr int k_off = q_off + FTB;            // phi(k)
   static constexpr int v_off = k_off + FTB;            // v
   static constexpr int g_off = v_off + VTB;            // dO, then g = dO / den
-  static constexpr int kh_off = g_off + VTB;           // RetNet: gamma^(L-1-t) phi(k)
-  static constexpr int qd_off = kh_off + (GATE == GT_DECAY ? FTB : 0);  // GLA: e^{b} phi'(q)
-  static constexpr int a_off = qd_off + (GATE == GT_GLA ? FTB : 0);     // scores A, then dW
+  static constexpr int kh_off = g_off + VTB;           // RetNet: gamma^(L-1-t) phi(k); outer: K^
+  static constexpr int qd_off = kh_off + (GATE == GT_DECAY || GATE == GT_OUTER ? FTB : 0);  // e^{b} phi'(q)
+  static constexpr int a_off = qd_off + (kKeyGate<GATE> ? FTB : 0);     // scores A, then dW
   static constexpr int sb_off = a_off + ATB;           // bf16 [R][E] image of S entering the chunk
   static constexpr int z_off = sb_off + R * 2 * E;     // [R] z entering the chunk
   static constexpr int rs_off = z_off + R * 4;         // [64] score row sums
@@ -171,7 +179,12 @@ struct BwdALayout {
   static constexpr int inv_off = zd_off + kChunk * 4;  // [64] 1 / den
   static constexpr int hp_off = inv_off + kChunk * 4;  // [4][64] partial g . o per wave
   static constexpr int gam_off = hp_off + 4 * kChunk * 4;
-  static constexpr int bytes = gam_off + R * 4;
+  // outer-product gate: e^{c} per token and value column (rows of E + 4),
+  // e^{c_end} per column, the lo half of V~ = e^{-c} v (the v tile holds hi)
+  static constexpr int ec_off = gam_off + R * 4;
+  static constexpr int gamv_off = ec_off + (GATE == GT_OUTER ? kChunk * (E + 4) * 4 : 0);
+  static constexpr int vl_off = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
+  static constexpr int bytes = vl_off + (GATE == GT_OUTER ? VTB : 0);
 };
 
 // h_i = -g_i . o_i from the four waves' partial dot products (fixed order).
@@ -214,6 +227,8 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   ca.V = b.V;
   ca.ldv = b.ldv;
   ca.g = b.gl;
+  ca.gv = b.gvl;
+  ca.ldgv = b.ldv;
   ca.inv_tau = b.inv_tau;
 
   using Raw = RawChunk<R, E, R, FMAP, GATE, true, NW>;
@@ -249,8 +264,9 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
     // ---- prelude: features, values, dO, and the bf16 image of S
-    chunk_prelude<R, E, R, FMAP, GATE, true, NW, true, GATE == GT_GLA ? kPreQD : 0>(
-        raw, ca, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off, LY::v_off, LY::gam_off, 0, lane, w, LY::qd_off);
+    chunk_prelude<R, E, R, FMAP, GATE, true, NW, true, kKeyGate<GATE> ? kPreQD : 0>(
+        raw, ca, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off, LY::v_off, LY::gam_off, 0, lane, w, LY::qd_off, 0, 0,
+        LY::ec_off, LY::gamv_off, 0, LY::vl_off);
     rdo.store(sm, LY::g_off, L, lane, w);
     state_image<R, E>(S, sm, LY::sb_off, lane, w);
     raw.load(ca, tok0, t0 + kChunk, t_end, lane, w);
@@ -259,8 +275,10 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
 
     // ---- scores A (masked, RetNet-weighted) and their row sums; phi(q) . z
     // (the state-space read-out has no normaliser: g = dO, h = 0, and neither
-    // the scores nor o are needed)
-    if constexpr (FMAP != FM_IDENT) {
+    // the scores nor o are needed, except by the outer-product gate, whose
+    // G~ and dO * o take the output's value-side factors; there 1 / den = 1)
+    constexpr bool NEED_O = FMAP != FM_IDENT || GATE == GT_OUTER;
+    if constexpr (NEED_O) {
       const int qw = w;
       const int q = 16 * qw + c16;
       bf16x8 qop[KP];
@@ -297,13 +315,16 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
       if (g4 == 0) {
         lds<float>(sm, LY::rs_off + 4 * q) = rs;
         lds<float>(sm, LY::zd_off + 4 * q) = zd;
-        lds<float>(sm, LY::inv_off + 4 * q) = 1.f / (rs + zd + b.eps);
+        lds<float>(sm, LY::inv_off + 4 * q) = FMAP == FM_IDENT ? 1.f : 1.f / (rs + zd + b.eps);
       }
     }
     lds_barrier();
 
-    // ---- o (fp32, not stored), g = dO / den (bf16) and the wave's share of g . o
-    if constexpr (FMAP != FM_IDENT) {
+    // ---- o (fp32, not stored), g = dO / den (bf16) and the wave's share of g . o.
+    // The outer-product gate: the products give num e^{-c} (V~ = e^{-c} v as hi +
+    // lo); the tile takes G~ = e^{c} g, and h uses G~ . (num e^{-c}) / den (the
+    // same sum as g . o); dO * o goes to the workspace for the value-side gradient.
+    if constexpr (NEED_O) {
       bf16x8 Sop[KP][NEB];
       state_operand<R, E>(S, Sop);
 #pragma unroll
@@ -325,20 +346,36 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[i] *= isc;
 #pragma unroll
-          for (int p2 = 0; p2 <= qt / 2; ++p2)
-            acc = mfma16(tr_feat<E, true>(sm, LY::v_off, 32 * p2, e, lane),
-                         lds<bf16x8>(sm, LY::a_off + AT::at(q, 4 * p2 + g4)), acc);
-          // acc[i] = num[q][e + 4 g + i]
+          for (int p2 = 0; p2 <= qt / 2; ++p2) {
+            const bf16x8 ab = lds<bf16x8>(sm, LY::a_off + AT::at(q, 4 * p2 + g4));
+            acc = mfma16(tr_feat<E, true>(sm, LY::v_off, 32 * p2, e, lane), ab, acc);
+            if constexpr (GATE == GT_OUTER) acc = mfma16(tr_feat<E, true>(sm, LY::vl_off, 32 * p2, e, lane), ab, acc);
+          }
+          // acc[i] = num[q][e + 4 g + i] (outer: times e^{-c})
           const int go = LY::g_off + VT::at(q, (e + 4 * g4) / 8, 2 * ((e + 4 * g4) % 8));
           const bf16x4 dov = lds<bf16x4>(sm, go);
-          const bf16x4 gb = pack4(to_f32(dov[0]) * inv_den, to_f32(dov[1]) * inv_den, to_f32(dov[2]) * inv_den,
-                                  to_f32(dov[3]) * inv_den);
+          float gsc[4] = {inv_den, inv_den, inv_den, inv_den};
+          if constexpr (GATE == GT_OUTER) {
+            const f32x4 ec = lds<f32x4>(sm, LY::ec_off + 4 * (q * (E + 4) + e + 4 * g4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gsc[i] = inv_den * ec[i];
+          }
+          const bf16x4 gb = pack4(to_f32(dov[0]) * gsc[0], to_f32(dov[1]) * gsc[1], to_f32(dov[2]) * gsc[2],
+                                  to_f32(dov[3]) * gsc[3]);
+          if constexpr (GATE == GT_OUTER) {
+            // g * num = G~ * (num e^{-c}) with the rounded G~ that pass B's dV
+            // uses too, so the pairs inside a suffix cancel in dO * o - dV * v
+            f32x4 pw;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pw[i] = to_f32(gb[i]) * acc[i];
+            if (q < L) *reinterpret_cast<f32x4*>(b.Pw + (tok0 + t0 + q) * E + e + 4 * g4) = pw;
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) hp += to_f32(gb[i]) * (acc[i] * inv_den);
           lds<bf16x4>(sm, go) = gb;
         }
         hp = sum_over_groups(hp);
-        if (g4 == 0) lds<float>(sm, LY::hp_off + 256 * w + 4 * q) = hp;
+        if (FMAP != FM_IDENT && g4 == 0) lds<float>(sm, LY::hp_off + 256 * w + 4 * q) = hp;
       }
     }
     lds_barrier();
@@ -369,7 +406,8 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     lds_barrier();
 
     // ---- dphi(q)^T = Phi_k^T dW^T + gamma^(t+1) (S G^T + z h^T); dq = dphi(q) phi'(q).
-    // GLA: the tiles hold Q~ = e^{b} phi(q) and K~ = e^{-b} phi(k), so this is
+    // GLA and the outer-product gate: the tiles hold Q~ = e^{b} phi(q) and
+    // K~ = e^{-b} phi(k) (and G~ for the outer gate), so this is
     // dQ~ (with the state terms unweighted); dq = dQ~ e^{b} phi'(q), and
     // dQ~ . Q~ goes to dB (the log-gates' gradient, completed by pass B).
 #pragma unroll
@@ -393,13 +431,13 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
         if constexpr (GATE == GT_DECAY) sc = exp2f(float(i + 1) * lg2gam);
         const bf16x4 ph = lds<bf16x4>(sm, LY::q_off + FT::at(i, f0 / 8, 2 * (f0 % 8)));
         bf16x4 qd = ph;
-        if constexpr (GATE == GT_GLA) qd = lds<bf16x4>(sm, LY::qd_off + FT::at(i, f0 / 8, 2 * (f0 % 8)));
+        if constexpr (kKeyGate<GATE>) qd = lds<bf16x4>(sm, LY::qd_off + FT::at(i, f0 / 8, 2 * (f0 % 8)));
         float dq[4];
         f32x4 db;
 #pragma unroll
         for (int u2 = 0; u2 < 4; ++u2) {
           const float dphi = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::z_off + 4 * (f0 + u2)) * hi);
-          if constexpr (GATE == GT_GLA) {
+          if constexpr (kKeyGate<GATE>) {
             dq[u2] = dphi * to_f32(qd[u2]);
             db[u2] = dphi * to_f32(ph[u2]);
           } else {
@@ -407,7 +445,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
           }
         }
         if (i < L) store_grad4(b.dQ + (tok0 + t0 + i) * R + f0, dq, b.accum != 0);
-        if constexpr (GATE == GT_GLA)
+        if constexpr (kKeyGate<GATE>)
           *reinterpret_cast<f32x4*>(b.dB + dbq_at<R>(bh, b.n, t0 / kChunk, ft, it, lane)) = db;
       }
     }
@@ -427,8 +465,8 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
 
     // ---- carry the forward state past this chunk
     const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE, NW, true>(S, Z, sm, GATE == GT_DECAY ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off,
-                                       gsc, lane, w);
+    state_update<R, E, GATE, NW, true>(S, Z, sm, GATE == GT_DECAY || GATE == GT_OUTER ? LY::kh_off : LY::k_off,
+                                       LY::v_off, LY::gam_off, gsc, lane, w, 0, LY::gamv_off, LY::vl_off);
     z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
     lds_barrier();
   }
@@ -530,17 +568,20 @@ struct BwdBLayout {
   static constexpr int v_off = k_off + FTB;            // v
   static constexpr int g_off = v_off + VTB;            // g
   static constexpr int qw_off = g_off + VTB;           // RetNet: gamma^t phi(q)
-  static constexpr int kd_off = qw_off + (GATE == GT_DECAY ? FTB : 0);  // GLA: e^{-b} phi'(k)
-  static constexpr int gr_off = kd_off + (GATE == GT_GLA ? FTB : 0);    // GLA: the raw gate input g
-  static constexpr int w_off = gr_off + (GATE == GT_GLA ? FTB : 0);     // W^T [key][query]
+  static constexpr int kd_off = qw_off + (GATE == GT_DECAY ? FTB : 0);  // GLA, outer: e^{-b} phi'(k)
+  static constexpr int gr_off = kd_off + (kKeyGate<GATE> ? FTB : 0);    // GLA, outer: the raw gate input g
+  static constexpr int w_off = gr_off + (kKeyGate<GATE> ? FTB : 0);     // W^T [key][query]
   static constexpr int dw_off = w_off + ATB;           // dW^T [key][query]
   static constexpr int rb_off = dw_off + ATB;          // bf16 [R][E] image of R entering the chunk
   static constexpr int rh_off = rb_off + R * 2 * E;    // [R] r_h entering the chunk
   static constexpr int hw_off = rh_off + R * 4;        // [64] h
   static constexpr int gam_off = hw_off + kChunk * 4;  // GLA: e^{chunk's summed log-gate}
-  // GLA: [4][R] the waves' partial products of the states at the next segment's start
+  // GLA, outer: [4][R] the waves' partial products of the states at the next segment's start
   static constexpr int cpart_off = gam_off + R * 4;
-  static constexpr int bytes = cpart_off + (GATE == GT_GLA ? 4 * R * 4 : 0);
+  // outer: e^{c} per token and value column (rows of E + 4), e^{c_end} per column
+  static constexpr int ec_off = cpart_off + (kKeyGate<GATE> ? 4 * R * 4 : 0);
+  static constexpr int gamv_off = ec_off + (GATE == GT_OUTER ? kChunk * (E + 4) * 4 : 0);
+  static constexpr int bytes = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
 };
 
 // Inclusive prefix sum across each row of 16 lanes (lane c gets x_0 + ... + x_c
@@ -579,10 +620,14 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   ca.V = b.V;
   ca.ldv = b.ldv;
   ca.g = b.gl;
+  ca.gv = b.gvl;
+  ca.ldgv = b.ldv;
   ca.inv_tau = b.inv_tau;
   // the chunk's tiles: plain features (RetNet weights are applied per product)
-  // or, with the GLA gate, Q~ and K~ as in the forward
-  constexpr int PG = GATE == GT_GLA ? GT_GLA : GT_NONE;
+  // or, with the GLA and outer-product gates, Q~ and K~ as in the forward (and
+  // V~ = e^{-c} v, its bf16 hi part, for the outer gate)
+  constexpr int PG = kKeyGate<GATE> ? GATE : GT_NONE;
+  constexpr bool OUT = GATE == GT_OUTER;
 
   // ---- reverse state entering the segment from its end
   f32x4 Rs[R / 16][NEB];
@@ -603,10 +648,15 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   // sum_e S(t1)[f][e] R(t1)[f][e] + z(t1)[f] r_h(t1)[f], S(t1) the forward
   // state entering that segment and R(t1) the reverse state entering this one
   // from its end: the waves' partial sums over their value columns here, the
-  // z share in the first chunk
+  // z share in the first chunk. The outer-product gate's d log beta there is
+  // sum_f S(t1)[f][e] R(t1)[f][e] (z has no value-side factor): a column sum
+  // over the wave's own slab.
   const bool later = s + 1 < b.P;
-  if constexpr (GATE == GT_GLA) {
+  float cvt[NEB];  // outer: d log beta at t1 for column ebase + 16 eb + c16
+  if constexpr (kKeyGate<GATE>) {
     const float* Sn = later ? b.S_in + bh * b.in_head + (long long)(s + 1) * b.in_seg : nullptr;
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) cvt[eb] = 0.f;
 #pragma unroll
     for (int rt = 0; rt < R / 16; ++rt)
 #pragma unroll
@@ -615,7 +665,11 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
         float acc = 0.f;
         if (later) {
 #pragma unroll
-          for (int eb = 0; eb < NEB; ++eb) acc += Rs[rt][eb][i] * Sn[f * E + ebase + 16 * eb + c16];
+          for (int eb = 0; eb < NEB; ++eb) {
+            const float pr = Rs[rt][eb][i] * Sn[f * E + ebase + 16 * eb + c16];
+            acc += pr;
+            if constexpr (OUT) cvt[eb] += pr;
+          }
         }
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
@@ -623,6 +677,22 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
         acc += __shfl_xor(acc, 8);
         if (c16 == 0) lds<float>(sm, LY::cpart_off + 4 * (w * R + f)) = acc;
       }
+    if constexpr (OUT) {
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb) {
+        cvt[eb] += __shfl_xor(cvt[eb], 16);
+        cvt[eb] += __shfl_xor(cvt[eb], 32);
+      }
+    }
+  }
+  // outer: d log beta entering from the later tokens, for the columns
+  // e + 4 g + u this lane holds in the dV products below
+  float carryv[OUT ? NEB : 1][4];
+  if constexpr (OUT) {
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) carryv[eb][u] = __shfl(cvt[eb], 4 * g4 + u);
   }
 
   const int nslot = w < 2 ? 3 : 2;
@@ -646,8 +716,9 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
     // ---- prelude
-    chunk_prelude<R, E, R, FMAP, PG, true, NW, true, GATE == GT_GLA ? kPreKD : 0>(
-        raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0, LY::v_off, LY::gam_off, 0, lane, w, 0, LY::kd_off);
+    chunk_prelude<R, E, R, FMAP, PG, true, NW, true, kKeyGate<GATE> ? (kPreKD | (OUT ? kPreNoKH | kPreVHi : 0)) : 0>(
+        raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0, LY::v_off, LY::gam_off, 0, lane, w, 0, LY::kd_off, 0,
+        LY::ec_off, LY::gamv_off);
     if constexpr (GATE == GT_DECAY) {
       // gamma^t phi(q) for the reverse-state update
       const int t = 16 * w + lane / 4;
@@ -661,7 +732,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
             keep_if(t < L, cat8(pack4(f[0], f[1], f[2], f[3]), pack4(f[4], f[5], f[6], f[7])));
       }
     }
-    if constexpr (GATE == GT_GLA) {
+    if constexpr (kKeyGate<GATE>) {
       // the raw gate of this lane's token and the wave's features, for dg
 #pragma unroll
       for (int jg = 0; jg < R / 32; ++jg)
@@ -669,7 +740,8 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     }
     rg.store(sm, LY::g_off, L, lane, w);
     if (w == 0) lds<float>(sm, LY::hw_off + 4 * lane) = lane < L ? hv : 0.f;
-    state_image<R, E>(Rs, sm, LY::rb_off, lane, w);
+    // (outer: R scaled by e^{c_end} per column, for the dK~ product with V~)
+    state_image<R, E>(Rs, sm, LY::rb_off, lane, w, OUT ? LY::gamv_off : -1);
     z_store<R, NW>(Rz, reinterpret_cast<float*>(sm + LY::rh_off), lane, w);
     if (ci > 0) load(ci - 1);
     lds_barrier();
@@ -716,10 +788,16 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     // ---- dv^T = G^T W (intra) + gamma^(L-t) R'^T phi(k)^T (inter): the wave's value columns.
     // GLA: a key's share of the state reaches the chunk's end scaled by
     // Gamma = e^{chunk's summed log-gate} per feature, so the inter term is
-    // (Gamma R)^T K~^T.
+    // (Gamma R)^T K~^T. The outer-product gate: dv = e^{-c} ((Gamma R Gamma_v)^T K~^T
+    // + G~^T W), and the value-side log-gate's gradient dC = dO * o - dv * v,
+    // summed over the later tokens of each column (key tiles back to front),
+    // gives dgv = d log beta sigmoid(-gv) / tau.
     {
       bf16x8 Rop[KP][NEB];
-      if constexpr (GATE == GT_GLA) {
+      if constexpr (kKeyGate<GATE>) {
+        float gc[NEB];
+#pragma unroll
+        for (int eb = 0; eb < NEB; ++eb) gc[eb] = OUT ? lds<float>(sm, LY::gamv_off + 4 * (ebase + 16 * eb + c16)) : 1.f;
         f32x4 Rg[R / 16][NEB];
 #pragma unroll
         for (int rt = 0; rt < R / 16; ++rt)
@@ -727,14 +805,15 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           for (int i = 0; i < 4; ++i) {
             const float gm = lds<float>(sm, LY::gam_off + 4 * (16 * rt + 4 * g4 + i));
 #pragma unroll
-            for (int eb = 0; eb < NEB; ++eb) Rg[rt][eb][i] = Rs[rt][eb][i] * gm;
+            for (int eb = 0; eb < NEB; ++eb) Rg[rt][eb][i] = OUT ? Rs[rt][eb][i] * (gm * gc[eb]) : Rs[rt][eb][i] * gm;
           }
         state_operand<R, E>(Rg, Rop);
       } else {
         state_operand<R, E>(Rs, Rop);
       }
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
+      for (int jj = 0; jj < 4; ++jj) {
+        const int jt = OUT ? 3 - jj : jj;
         const int j = 16 * jt + c16;
         bf16x8 kb[KP];
 #pragma unroll
@@ -753,6 +832,28 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           for (int p = jt / 2; p < 2; ++p)
             acc = mfma16(tr_feat<E, true>(sm, LY::g_off, 32 * p, e, lane),
                          lds<bf16x8>(sm, LY::w_off + AT::at(j, 4 * p + g4)), acc);
+          if constexpr (OUT) {
+            const f32x4 ec = lds<f32x4>(sm, LY::ec_off + 4 * (j * (E + 4) + e + 4 * g4));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] *= __builtin_amdgcn_rcpf(ec[u]);
+            // rows past the chunk read the segment's last row (in bounds) and are masked
+            const long long row = tok0 + min(t0 + j, t_end - 1);
+            const f32x4 pw = *reinterpret_cast<const f32x4*>(b.Pw + row * E + e + 4 * g4);
+            const bf16x4 vr = *reinterpret_cast<const bf16x4*>(b.V + row * b.ldv + e + 4 * g4);
+            const bf16x4 gvr = *reinterpret_cast<const bf16x4*>(b.gvl + row * b.ldv + e + 4 * g4);
+            float o[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float x = j < L ? pw[u] - acc[u] * to_f32(vr[u]) : 0.f;
+              const float pre = row_inclusive_scan(x);
+              const float tot = __shfl(pre, (lane & 48) | 15);
+              o[u] = (carryv[eb][u] + ((tot - pre) + x)) * b.inv_tau *
+                     __builtin_amdgcn_rcpf(1.f + __expf(to_f32(gvr[u])));
+              carryv[eb][u] += tot;
+            }
+            if (j < L)
+              *reinterpret_cast<bf16x4*>(b.dgv + (tok0 + t0 + j) * b.ldv + e + 4 * g4) = pack4(o[0], o[1], o[2], o[3]);
+          }
           if (j < L)
             *reinterpret_cast<bf16x4*>(b.dV + (tok0 + t0 + j) * b.ldv + e + 4 * g4) =
                 pack4(acc[0], acc[1], acc[2], acc[3]);
@@ -761,7 +862,8 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     }
 
     // ---- dphi(k)^T = Phi_q^T dW (intra) + gamma^(L-t) (R v + r_h) (inter); dk = dphi(k) phi'(k).
-    // GLA: dK~ = Q~^T dW + Gamma (R v + r_h); dk = dK~ e^{-b} phi'(k), and
+    // GLA: dK~ = Q~^T dW + Gamma (R v + r_h); dk = dK~ e^{-b} phi'(k) (the
+    // outer-product gate: R Gamma_v V~ in place of R v), and
     // dB = dQ~ . Q~ - dK~ . K~, the gradient of the cumulative log-gate, whose
     // suffix sums give dg (below). A lane keeps the same features in every
     // chunk: 16 ft + 4 g + u2, tokens 16 jt + c.
@@ -769,7 +871,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     for (int u = 0; u < FPW; ++u) {
       const int ft = w * FPW + u;
       const int f0 = 16 * ft + 4 * g4;
-      if constexpr (GATE == GT_GLA) {
+      if constexpr (kKeyGate<GATE>) {
         if (ci == nch - 1) {
           // d log alpha entering from the later segments (see above)
 #pragma unroll
@@ -788,7 +890,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
       // GLA walks the key tiles back to front for the suffix sums of dB
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int jt = GATE == GT_GLA ? 3 - jj : jj;
+        const int jt = kKeyGate<GATE> ? 3 - jj : jj;
         const int j = 16 * jt + c16;
         f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -803,13 +905,13 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
         if constexpr (GATE == GT_DECAY) sc = exp2f(float(max(L - j, 0)) * lg2gam);
         const bf16x4 ph = lds<bf16x4>(sm, LY::k_off + FT::at(j, f0 / 8, 2 * (f0 % 8)));
         bf16x4 kd = ph;
-        if constexpr (GATE == GT_GLA) kd = lds<bf16x4>(sm, LY::kd_off + FT::at(j, f0 / 8, 2 * (f0 % 8)));
+        if constexpr (kKeyGate<GATE>) kd = lds<bf16x4>(sm, LY::kd_off + FT::at(j, f0 / 8, 2 * (f0 % 8)));
         float dk[4], bk[4];
 #pragma unroll
         for (int u2 = 0; u2 < 4; ++u2) {
-          if constexpr (GATE == GT_GLA) sc = lds<float>(sm, LY::gam_off + 4 * (f0 + u2));
+          if constexpr (kKeyGate<GATE>) sc = lds<float>(sm, LY::gam_off + 4 * (f0 + u2));
           const float dphi = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::rh_off + 4 * (f0 + u2)));
-          if constexpr (GATE == GT_GLA) {
+          if constexpr (kKeyGate<GATE>) {
             dk[u2] = dphi * to_f32(kd[u2]);
             bk[u2] = dphi * to_f32(ph[u2]);
           } else {
@@ -817,7 +919,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           }
         }
         if (j < L) store_grad4(b.dK + (tok0 + t0 + j) * R + f0, dk, b.accum != 0);
-        if constexpr (GATE == GT_GLA) {
+        if constexpr (kKeyGate<GATE>) {
           // ---- dg: d log alpha_t = (d log alpha after the tile) + sum of dB over
           // the tile's tokens t' >= t (the row of 16 lanes holds tokens 16 jt + c
           // of four features); dg = d log alpha sigmoid(-g) / tau
@@ -838,10 +940,10 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     }
 
     // ---- R <- gamma^L R + (gamma^t phi(q))^T [g, h]: the state entering the previous chunk
-    // (GLA: R <- Gamma R + Q~^T [g, h])
-    if constexpr (GATE == GT_GLA) {
-      state_update<R, E, GT_GLA, NW, true, true, true>(Rs, Rz, sm, LY::q_off, LY::g_off, LY::gam_off, 1.f, lane, w,
-                                                       LY::hw_off);
+    // (GLA: R <- Gamma R + Q~^T [g, h]; outer: R <- Gamma R Gamma_v + Q~^T [G~, h])
+    if constexpr (kKeyGate<GATE>) {
+      state_update<R, E, GATE, NW, true, true, true>(Rs, Rz, sm, LY::q_off, LY::g_off, LY::gam_off, 1.f, lane, w,
+                                                     LY::hw_off, LY::gamv_off);
     } else {
       const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
       state_update<R, E, GATE, NW, true, true>(Rs, Rz, sm, GATE == GT_DECAY ? LY::qw_off : LY::q_off, LY::g_off,
@@ -857,23 +959,28 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
 // R_c = Gamma_c R_{c+1} + Q~_c^T [g, h] (Q~ = e^{b} phi(q), b the chunk's
 // inclusive summed log-gate), so the segment's share starts from zero at its
 // end and runs its chunks back to front in natural row order. The segment's
-// summed log-gate goes to logG for the reverse scan.
+// summed log-gate goes to logG for the reverse scan. The outer-product gate
+// adds its value side: R_c = (Gamma_c Gamma_v,c^T) * R_{c+1} + Q~_c^T [G~, h]
+// with G~ = e^{c} g (pass A stores G~), and the segment's summed value-side
+// log-gates go to logGv.
 // ---------------------------------------------------------------------------
-template <int R, int E>
+template <int R, int E, int GATE>
 struct BwdRGLayout {
   static constexpr int q_off = 0;                           // Q~
-  static constexpr int v_off = q_off + FeatTile<R>::BYTES;  // g
+  static constexpr int v_off = q_off + FeatTile<R>::BYTES;  // g (outer: G~)
   static constexpr int hw_off = v_off + FeatTile<E>::BYTES;  // [64] h
   static constexpr int gam_off = hw_off + kChunk * 4;        // [R] e^{chunk's summed log-gate}
   static constexpr int logg_off = gam_off + R * 4;           // [R] segment's summed log-gate
-  static constexpr int bytes = logg_off + R * 4;
+  static constexpr int gamv_off = logg_off + R * 4;          // outer: [E] e^{chunk's summed value-side log-gate}
+  static constexpr int loggv_off = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);  // outer: [E] segment's sum
+  static constexpr int bytes = loggv_off + (GATE == GT_OUTER ? E * 4 : 0);
 };
 
-template <int R, int E, int FMAP = FM_ELU1>
+template <int R, int E, int GATE, int FMAP = FM_ELU1>
 __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  using LY = BwdRGLayout<R, E>;
-  constexpr int NW = 4, NEB = E / 64, FR = R / NW;
+  using LY = BwdRGLayout<R, E, GATE>;
+  constexpr int NW = 4, NEB = E / 64, FR = R / NW, EV = E / NW;
   const int lane = lane_id(), w = wave_id<NW>();
   const int g4 = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x + 1;
@@ -886,6 +993,8 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   ca.K = b.Q;  // the queries in the prelude's key slot, scaled by e^{+b}: Q~
   ca.V = b.G;
   ca.g = b.gl;
+  ca.gv = b.gvl;
+  ca.ldgv = b.ldv;
   ca.inv_tau = b.inv_tau;
 
   f32x4 Rs[R / 16][NEB];
@@ -897,8 +1006,11 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   z_load<R, NW>(Rz, nullptr, lane, w);
   // the lane that accumulates feature w FR + lane in the prelude clears it
   if (lane < FR) lds<float>(sm, LY::logg_off + 4 * (w * FR + lane)) = 0.f;
+  if constexpr (GATE == GT_OUTER) {
+    if (lane < EV) lds<float>(sm, LY::loggv_off + 4 * (w * EV + lane)) = 0.f;
+  }
 
-  using Raw = RawChunk<R, E, R, FMAP, GT_GLA, false, NW>;
+  using Raw = RawChunk<R, E, R, FMAP, GATE, false, NW>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
   float hv = 0.f;
@@ -911,13 +1023,14 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, t_end - t0);
-    chunk_prelude<R, E, R, FMAP, GT_GLA, false, NW, true, kPreKPos>(raw, ca, L, 0.f, sm, 0, LY::q_off, 0,
-                                                                       LY::v_off, LY::gam_off, LY::logg_off, lane, w);
+    chunk_prelude<R, E, R, FMAP, GATE, false, NW, true, kPreKPos | (GATE == GT_OUTER ? kPreVRaw : 0)>(
+        raw, ca, L, 0.f, sm, 0, LY::q_off, 0, LY::v_off, LY::gam_off, LY::logg_off, lane, w, 0, 0, 0, 0,
+        LY::gamv_off, LY::loggv_off);
     if (w == 0) lds<float>(sm, LY::hw_off + 4 * lane) = lane < L ? hv : 0.f;
     if (ci > 0) load(ci - 1);
     lds_barrier();
-    state_update<R, E, GT_GLA, NW, true, true, true>(Rs, Rz, sm, LY::q_off, LY::v_off, LY::gam_off, 1.f, lane, w,
-                                                     LY::hw_off);
+    state_update<R, E, GATE, NW, true, true, true>(Rs, Rz, sm, LY::q_off, LY::v_off, LY::gam_off, 1.f, lane, w,
+                                                   LY::hw_off, LY::gamv_off);
     lds_barrier();
   }
   const long long slot = bh * b.P + s;
@@ -930,6 +1043,9 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
       for (int i = 0; i < 4; ++i) Ro[(16 * rt + 4 * g4 + i) * E + ebase + 16 * eb + c16] = Rs[rt][eb][i];
   z_store<R, NW>(Rz, b.rh_ws + slot * R, lane, w);
   if (lane < FR) b.logG[slot * R + w * FR + lane] = lds<float>(sm, LY::logg_off + 4 * (w * FR + lane));
+  if constexpr (GATE == GT_OUTER) {
+    if (lane < EV) b.logGv[slot * E + w * EV + lane] = lds<float>(sm, LY::loggv_off + 4 * (w * EV + lane));
+  }
 }
 
 }  // namespace la

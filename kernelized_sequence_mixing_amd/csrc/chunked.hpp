@@ -126,6 +126,7 @@ struct CausalArgs {
   int nslot;
   int in_is_state;         // S_in is the caller's carried state (indexed like S_out), not the segment workspace
   int ldv;                 // elements between rows of V (0: d_v, dense); the backward's value-column halves
+  int ldgv;                // elements between rows of gv (0: d_v, dense)
   int H, n, P, seg_len;
   int nbh;                 // sequences x heads (set by launchers whose grid is not [.][nbh])
   int r_valid;             // FAVOR+: the map's feature count when below R (features past it are zero); 0 = R
@@ -318,6 +319,7 @@ struct RawChunk {
   __device__ __forceinline__ void load(const CausalArgs& a, long long tok0, int t0, int row_end, int lane, int w) {
     const int g4 = lane >> 4, c16 = lane & 15;
     const long long ldv = a.ldv > 0 ? a.ldv : E;
+    const long long ldgv = a.ldgv > 0 ? a.ldgv : E;
     if constexpr (GATE == GT_SEL) sg = a.g[tok0 + min(t0 + lane, row_end - 1)];
     if constexpr (ROWMAJOR) {
       const long long row = tok0 + min(t0 + TPW * w + lane / LPT, row_end - 1);
@@ -349,7 +351,7 @@ struct RawChunk {
       for (int j = 0; j < EV / 8; ++j) v[j] = *reinterpret_cast<const bf16x8*>(a.V + row * ldv + w * EV + 8 * j);
       if constexpr (GATE == GT_OUTER) {
 #pragma unroll
-        for (int j = 0; j < EV / 8; ++j) gv[j] = *reinterpret_cast<const bf16x8*>(a.gv + row * E + w * EV + 8 * j);
+        for (int j = 0; j < EV / 8; ++j) gv[j] = *reinterpret_cast<const bf16x8*>(a.gv + row * ldgv + w * EV + 8 * j);
       }
     }
     if constexpr (!ELU) {
@@ -373,8 +375,12 @@ struct RawChunk {
 // min(phi(x), 1) for elu+1), the factors that turn gradients with respect to
 // Q~ and K~ into gradients of q and k; kPreLogG adds the chunk's summed
 // log-gates to logg also when WITH_Q; kPreKPos scales the key slot by e^{+b}
-// (the Q~ of the reverse state, with the queries passed as keys).
-constexpr int kPreQD = 1, kPreKD = 2, kPreLogG = 4, kPreKPos = 8;
+// (the Q~ of the reverse state, with the queries passed as keys). For the
+// outer-product gate's backward: kPreVRaw stores the value slot as loaded
+// (the reverse state's G~ = e^{+c} g, already scaled) while still taking the
+// value-side totals; kPreNoKH skips the K^ tile and kPreVHi the lo half of V~
+// (the reverse pass needs neither).
+constexpr int kPreQD = 1, kPreKD = 2, kPreLogG = 4, kPreKPos = 8, kPreVRaw = 16, kPreNoKH = 32, kPreVHi = 64;
 template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SWZ, int EXTRA = 0>
 __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>& raw,
                                               const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
@@ -469,7 +475,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
           if constexpr ((EXTRA & kPreKD) != 0) dk[u] = ek;
           // the outer-product gate's state update takes K^ = e^{b_end - b} phi(k) <= 1
           // (with its value side e^{-c} on top, e^{-b} would overflow first)
-          if constexpr (GATE == GT_OUTER) {
+          if constexpr (GATE == GT_OUTER && (EXTRA & (kPreKPos | kPreNoKH)) == 0) {
             float unused;
             vkh[u] = phi_times_exp2<FMAP>(xk, bend - b, unused);
           }
@@ -484,13 +490,16 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       const int fo = FT::at(t, f0 / 8);
       if constexpr (WITH_Q)
         lds<bf16x8>(sm, q_off + fo) = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
-      if constexpr (GATE == GT_OUTER) {
-        // pass 3: K~ for the scores and K^ for the state; pass 1: K^ only
+      // the outer-product gate: pass 3 writes K~ for the scores and K^ for the
+      // state, pass 1 K^ only; the backward's reverse state (kPreKPos) the key
+      // slot alone
+      constexpr bool kh_tile = GATE == GT_OUTER && (EXTRA & (kPreKPos | kPreNoKH)) == 0;
+      if constexpr (kh_tile) {
         const bf16x8 khr =
             keep_if(valid, cat8(pack4(vkh[0], vkh[1], vkh[2], vkh[3]), pack4(vkh[4], vkh[5], vkh[6], vkh[7])));
         lds<bf16x8>(sm, (WITH_Q ? kh_off : k_off) + fo) = khr;
       }
-      if (GATE != GT_OUTER || WITH_Q)
+      if (!kh_tile || WITH_Q)
         lds<bf16x8>(sm, k_off + fo) =
             keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
       if constexpr (kKeyGate<GATE> && (EXTRA & kPreQD) != 0)
@@ -526,17 +535,23 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         for (int u = 0; u < 8; ++u) {
           const float c = cs[u];
           const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
-          vs[u] = to_f32(raw.v[j][u]) * __builtin_amdgcn_exp2f(-c);
+          if constexpr ((EXTRA & kPreVRaw) == 0) vs[u] = to_f32(raw.v[j][u]) * __builtin_amdgcn_exp2f(-c);
           ecs[u] = __builtin_amdgcn_exp2f(c);
           my_cend = lane == 8 * j + u ? cend : my_cend;
         }
-        const bf16x8 hi = cat8(pack4(vs[0], vs[1], vs[2], vs[3]), pack4(vs[4], vs[5], vs[6], vs[7]));
-        float lo[8];
+        if constexpr ((EXTRA & kPreVRaw) != 0) {
+          lds<bf16x8>(sm, v_off + VT::at(lane, w * EV / 8 + j)) = keep_if(valid, raw.v[j]);
+        } else {
+          const bf16x8 hi = cat8(pack4(vs[0], vs[1], vs[2], vs[3]), pack4(vs[4], vs[5], vs[6], vs[7]));
+          lds<bf16x8>(sm, v_off + VT::at(lane, w * EV / 8 + j)) = keep_if(valid, hi);
+          if constexpr ((EXTRA & kPreVHi) == 0) {
+            float lo[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) lo[u] = vs[u] - to_f32(hi[u]);
-        lds<bf16x8>(sm, v_off + VT::at(lane, w * EV / 8 + j)) = keep_if(valid, hi);
-        lds<bf16x8>(sm, vl_off + VT::at(lane, w * EV / 8 + j)) =
-            keep_if(valid, cat8(pack4(lo[0], lo[1], lo[2], lo[3]), pack4(lo[4], lo[5], lo[6], lo[7])));
+            for (int u = 0; u < 8; ++u) lo[u] = vs[u] - to_f32(hi[u]);
+            lds<bf16x8>(sm, vl_off + VT::at(lane, w * EV / 8 + j)) =
+                keep_if(valid, cat8(pack4(lo[0], lo[1], lo[2], lo[3]), pack4(lo[4], lo[5], lo[6], lo[7])));
+          }
+        }
         if constexpr (WITH_Q) {
           const int eo = ec_off + 4 * (lane * (E + 4) + w * EV + 8 * j);
           lds<f32x4>(sm, eo) = f32x4{ecs[0], ecs[1], ecs[2], ecs[3]};
@@ -592,7 +607,8 @@ struct ZTiles {
 // With ZW the z column uses per-token weights (fp32 [64] at zw_off) instead of
 // the constant-1 value: z <- Gamma z + K^^T w. With PRE the GLA gate scales
 // the old state only (S <- Gamma S + K~^T V), as the backward pass's reverse
-// state needs.
+// state needs; the outer-product gate with PRE likewise scales the old state
+// by both sides and adds one bf16 value tile: S <- (Gamma 1^T) * S * (1 Gamma_v^T) + K~^T V.
 template <int R, int E, int GATE, int NW, bool SWZ, bool ZW = false, bool PRE = false, class SArr, class ZArr>
 __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_off, int v_off, int gam_off,
                                              float gscale, int lane, int w, int zw_off = 0, int gamv_off = 0,
@@ -608,8 +624,9 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
   for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) vb[eb][ks] = tr_feat<E, SWZ>(sm, v_off, 32 * ks, ebase + 16 * eb, lane);
-  bf16x8 vbl[GATE == GT_OUTER ? NEB : 1][2];  // the outer-product gate: lo half of V~
-  if constexpr (GATE == GT_OUTER) {
+  constexpr bool VLO = GATE == GT_OUTER && !PRE;
+  bf16x8 vbl[VLO ? NEB : 1][2];  // the outer-product gate: lo half of V~
+  if constexpr (VLO) {
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
@@ -628,13 +645,17 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb) {
       f32x4 st = S[rt][eb];
-      if constexpr (kScalarDecay<GATE> || (kKeyGate<GATE> && PRE) || GATE == GT_OUTER) {
+      if constexpr (GATE == GT_OUTER && PRE) {
+        const float gc = lds<float>(sm, gamv_off + 4 * (ebase + 16 * eb + (lane & 15)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[i] *= gr[i] * gc;
+      } else if constexpr (kScalarDecay<GATE> || (kKeyGate<GATE> && PRE) || GATE == GT_OUTER) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[i] *= gr[i];
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vb[eb][ks], st);
-      if constexpr (GATE == GT_OUTER) {
+      if constexpr (VLO) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vbl[eb][ks], st);
         // the column's value-side factor

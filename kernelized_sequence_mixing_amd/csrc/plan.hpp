@@ -71,11 +71,14 @@ struct BwdPlan : FwdPlan {
   float* ws_rh;  // [BH][P][r]
   void* ws_G;    // [BH][n][dv] bf16
   float* ws_h;   // [BH][n]
-  // GLA gate
+  // GLA and outer-product gates
   void* dg;      // [BH][n][r] out_dtype
   float* ws_dB;  // [BH][ceil(n / 64) * 64][r] in the kernels' own order
-  // a value-column half of a wider V: elements between rows of V, dO and dV
-  // (0: dv), and whether dQ, dK, dg are added to (the second half) or stored
+  // outer-product gate: the gradient of gv, dO * o per token and column
+  void* dgv;     // [BH][n][ldv] out_dtype
+  float* ws_P;   // [BH][n][dv]
+  // a value-column half of a wider V: elements between rows of V, dO, dV, gv
+  // and dgv (0: dv), and whether dQ, dK, dg are added to (the second half) or stored
   int ldv, accum;
 };
 
@@ -150,7 +153,8 @@ la_status launch_causal_elu1(const FwdPlan& p);
 la_status launch_causal_ssm(const FwdPlan& p);
 la_status launch_causal_favor(const FwdPlan& p);
 la_status launch_segment_scan(const FwdPlan& p);
-la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG);
+la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG,
+                                      const float* logGv = nullptr);
 la_status launch_backward(const BwdPlan& p);
 la_status launch_noncausal_backward(const BwdPlan& p);  // ws_S, ws_z: partial S, z; ws_R, ws_rh: partial G, hq
 la_status launch_noncausal(const FwdPlan& p);

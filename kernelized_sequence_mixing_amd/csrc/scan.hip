@@ -75,10 +75,10 @@ la_status launch_segment_scan(const FwdPlan& p) {
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
-la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG) {
+la_status launch_segment_scan_reverse(const FwdPlan& p, float* S, float* z, const float* logG, const float* logGv) {
   const int items = p.r * p.dv + p.r;
   dim3 grid((items + 255) / 256, unsigned(p.nseq) * unsigned(p.H));
-  LA_LAUNCH(segment_scan_kernel, grid, dim3(256), 0, p.stream, S, z, logG, nullptr, nullptr, nullptr, p.gamma,
+  LA_LAUNCH(segment_scan_kernel, grid, dim3(256), 0, p.stream, S, z, logG, logGv, nullptr, nullptr, p.gamma,
                      nullptr, 0, p.H, p.P, p.r, p.dv, p.seg_len, p.gate, 1);
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     lib = N.lib()
-    assert lib.la_abi_version() == 6
+    assert lib.la_abi_version() == 7
     names = [lib.la_status_str(i).decode() for i in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_ALIAS",
                      "LA_ERR_HIP"]
@@ -256,12 +256,12 @@ def test_feature_map_rejects():
 
 # ------------------------------------------------------------------ backward (validation, no launch)
 
-def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAKE + 13 * SP, dg=None):
+def _backward(a, dO=FAKE + 10 * SP, dQ=FAKE + 11 * SP, dK=FAKE + 12 * SP, dV=FAKE + 13 * SP, dg=None, dgv=None):
     p = N.LaProblem(a["B"], a["H"], a["n"], a["d_k"], a["d_v"], a["in_dt"], a["out_dt"], a["eps"])
     f = N.LaFeatureMap(a["fkind"], a["r"], a["omega"])
     g = N.LaGate(a["gkind"], a["tau"], a["gamma"], a["g"], a["gv"])
     return N.lib().la_backward(ctypes.byref(p), a["Q"], a["K"], a["V"], dO, ctypes.byref(f), a["causal"],
-                               ctypes.byref(g), a["S0"], a["z0"], dQ, dK, dV, dg, a["ws"], a["ws_bytes"], None)
+                               ctypes.byref(g), a["S0"], a["z0"], dQ, dK, dV, dg, dgv, a["ws"], a["ws_bytes"], None)
 
 
 BAD_BACKWARD = [
@@ -271,8 +271,24 @@ BAD_BACKWARD = [
     ("sel without dg", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), {}, N.LA_ERR_INVALID_ARG),
     ("sel favor", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP, fkind=N.LA_FMAP_FAVOR, r=256, omega=FAKE + 5 * SP),
      dict(dg=FAKE + 14 * SP), N.LA_ERR_UNSUPPORTED),
-    ("outer", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP), dict(dg=FAKE + 14 * SP),
-     N.LA_ERR_UNSUPPORTED),
+    ("outer without dgv", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP), dict(dg=FAKE + 14 * SP),
+     N.LA_ERR_INVALID_ARG),
+    ("outer without dg", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP), dict(dgv=FAKE + 15 * SP),
+     N.LA_ERR_INVALID_ARG),
+    ("dgv without outer", dict(gkind=N.LA_GATE_GLA, g=FAKE + 6 * SP), dict(dg=FAKE + 14 * SP, dgv=FAKE + 15 * SP),
+     N.LA_ERR_INVALID_ARG),
+    ("outer no gv", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP), dict(dg=FAKE + 14 * SP, dgv=FAKE + 15 * SP),
+     N.LA_ERR_INVALID_ARG),
+    ("outer dgv misaligned", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP),
+     dict(dg=FAKE + 14 * SP, dgv=FAKE + 15 * SP + 8), N.LA_ERR_INVALID_ARG),
+    ("outer dgv aliases gv", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP),
+     dict(dg=FAKE + 14 * SP, dgv=FAKE + 7 * SP + 256), N.LA_ERR_ALIAS),
+    ("outer dgv aliases dg", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP),
+     dict(dg=FAKE + 14 * SP, dgv=FAKE + 14 * SP + 512), N.LA_ERR_ALIAS),
+    ("outer dV aliases gv", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP),
+     dict(dg=FAKE + 14 * SP, dgv=FAKE + 15 * SP, dV=FAKE + 7 * SP), N.LA_ERR_ALIAS),
+    ("outer favor", dict(gkind=N.LA_GATE_OUTER, g=FAKE + 6 * SP, gv=FAKE + 7 * SP, fkind=N.LA_FMAP_FAVOR, r=128,
+                         omega=FAKE + 5 * SP), dict(dg=FAKE + 14 * SP, dgv=FAKE + 15 * SP), N.LA_ERR_UNSUPPORTED),
     ("sel dg aliases g", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), dict(dg=FAKE + 6 * SP + 1024), N.LA_ERR_ALIAS),
     ("sel dg in workspace", dict(gkind=N.LA_GATE_SEL, g=FAKE + 6 * SP), dict(dg=FAKE + 4 * SP + 4096),
      N.LA_ERR_ALIAS),
@@ -349,6 +365,19 @@ def test_backward_workspace_size():
     # the selective gate runs the GLA passes on g repeated over features: that copy and its
     # per-feature gradient (bf16 each) come on top
     assert size(4, 16, n, 64, 64, N.LA_GATE_SEL) == size(4, 16, n, 64, 64, N.LA_GATE_GLA) + 2 * BH * n * 64 * 2
+    # the outer-product gate: the GLA regions on its own segment plan, plus dO * o per token and value
+    # column (fp32) and the segments' summed value-side log-gates
+    p = N.LaProblem(4, 16, n, 64, 64, N.LA_BF16, N.LA_BF16, 1e-6)
+    f = N.LaFeatureMap(N.LA_FMAP_ELU1, 64, None)
+    g = N.LaGate(N.LA_GATE_OUTER, 16.0, None, None)
+    segs, seg_len = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert lib.la_forward_segments(ctypes.byref(p), ctypes.byref(f), 1, ctypes.byref(g), ctypes.byref(segs),
+                                   ctypes.byref(seg_len)) == N.LA_OK
+    Po = segs.value
+    assert Po > 1
+    so, zo = BH * Po * 64 * 64 * 4, BH * Po * 64 * 4
+    assert size(4, 16, n, 64, 64, N.LA_GATE_OUTER) == (2 * so + 2 * zo + BH * n * 64 * 2 + BH * n * 4 +
+                                                       BH * n * 64 * 4 + zo + BH * n * 64 * 4 + BH * Po * 64 * 4)
 
     def size128(B, H, n, dv, gk=N.LA_GATE_NONE):
         p = N.LaProblem(B, H, n, 128, dv, N.LA_BF16, N.LA_BF16, 1e-6)
@@ -528,7 +557,7 @@ def test_valid_calls_without_a_device_return_hip_error():
     assert lib.la_backward_workspace_size(ctypes.byref(p), ctypes.byref(elu), 1, ctypes.byref(none),
                                           ctypes.byref(ws)) == N.LA_OK
     assert lib.la_backward(ctypes.byref(p), at(0), at(1), at(2), at(3), ctypes.byref(elu), 1, ctypes.byref(none),
-                           None, None, at(4), at(5), at(6), None, at(7), ws.value, None) == N.LA_ERR_HIP
+                           None, None, at(4), at(5), at(6), None, None, at(7), ws.value, None) == N.LA_ERR_HIP
     assert lib.la_feature_map_apply(ctypes.byref(elu), 1000, 64, N.LA_BF16, at(0), at(1), None) == N.LA_ERR_HIP
 
 
