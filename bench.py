@@ -311,7 +311,9 @@ def backward_algorithmic_per_token(wl):
     """(bytes, matrix-core flops) per head-token of the backward pass (causal unless wl.causal is False).
 
     Bytes: read q, k, v, dO once, write dq, dk, dv once (GLA: also read g and
-    write dg, r per token each; the selective gate: one of each per token). Flops (chunk C, masked upper triangle excluded): the scores, the
+    write dg, r per token each; the selective gate: one of each per token; the
+    outer-product gate: g and dg, plus gv and dgv, d_v per token each). Flops
+    (chunk C, masked upper triangle excluded): the scores, the
     numerator of o, dW, and the intra-chunk parts of dq, dk, dv ((C+1)/2 * 2 r
     or 2 d_v each), plus six r x d_v products per token (o's inter-chunk read,
     dq's S g, dk's R v, dv's R phi(k), and the forward and reverse state
@@ -323,6 +325,8 @@ def backward_algorithmic_per_token(wl):
         nbytes += 2 * (2 * wl.r)
     elif wl.gate == "sel":
         nbytes += 2 * 2
+    elif wl.gate == "outer":
+        nbytes += 2 * (2 * wl.r) + 2 * (2 * wl.d_v)
     half = (CHUNK + 1) / 2
     flops = half * 2 * wl.r * 3 + half * 2 * wl.d_v * 3 + 6 * 2 * wl.r * wl.d_v
     if not wl.causal:  # the non-causal form: S, G and the per-token products, no scores
@@ -355,19 +359,21 @@ def backward_kernel_names(wl, count):
 
 def bench_backward(wl, steps, warmup):
     """la_backward on workload wl (causal; elu+1, FAVOR+ or identity features): one step is
-    one full backward pass (with a gate input it includes dg; with FAVOR+ the feature
-    materialisation and the pass back through the map)."""
+    one full backward pass (with a gate input it includes dg, and dgv for the outer-product
+    gate; with FAVOR+ the feature materialisation and the pass back through the map)."""
     import kernelized_sequence_mixing_amd as ksm
     from workloads import incoming_gradient
     inp = make_inputs(wl, seed=0)
     inp["dO"] = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1, dtype=wl.dtype)
     nb_tok, fl_tok = backward_algorithmic_per_token(wl)
     per_set = wl.head_tokens * nb_tok
-    sets = _device_sets(inp, ["Q", "K", "V", "dO", "gamma", "g", "omega"], per_set)
+    sets = _device_sets(inp, ["Q", "K", "V", "dO", "gamma", "g", "gv", "omega"], per_set)
     gate_of = {"none": lambda s: None, "decay": lambda s: ("decay", s["gamma"]),
-               "gla": lambda s: ("gla", s["g"], wl.tau), "sel": lambda s: ("sel", s["g"], wl.tau)}[wl.gate]
+               "gla": lambda s: ("gla", s["g"], wl.tau), "sel": lambda s: ("sel", s["g"], wl.tau),
+               "outer": lambda s: ("outer", s["g"], s["gv"], wl.tau)}[wl.gate]
     grads = [(torch.empty_like(s["Q"]), torch.empty_like(s["K"]), torch.empty_like(s["V"])) +
-             ((torch.empty_like(s["g"]),) if wl.gate in ("gla", "sel") else ()) for s in sets]
+             ((torch.empty_like(s["g"]),) if wl.gate in ("gla", "sel", "outer") else ()) +
+             ((torch.empty_like(s["gv"]),) if wl.gate == "outer" else ()) for s in sets]
     stream = torch.cuda.current_stream()
     calls = [ksm.PreparedBackward(s["Q"], s["K"], s["V"], s["dO"], fmap=wl.fmap, omega=s.get("omega"),
                                   gate=gate_of(s), eps=wl.eps, grads=grads[i], stream=stream, causal=wl.causal)
@@ -518,12 +524,13 @@ def run_only(name, steps, warmup):
     raise SystemExit(f"unknown workload {name!r}")
 
 
-# the backward lines: the GLA and RetNet workloads at their own shapes (128 x 128 states, two
-# value-column halves), the ungated elu+1 shape, the GLA sequence shape at d_k = d_v = 64, the
-# state-space form under both selective gates, non-causal, FAVOR+ at the causal FAVOR+ shape with
+# the backward lines: the GLA, outer-product-gate and RetNet workloads at their own shapes (128 x 128
+# states, two value-column halves), the ungated elu+1 shape, the GLA sequence shape at d_k = d_v = 64,
+# the state-space form under both selective gates, non-causal, FAVOR+ at the causal FAVOR+ shape with
 # r = 128 (the widest feature count the backward builds)
 BACKWARD_WORKLOADS = {
     "gla_gate": WORKLOADS["gla_gate"],
+    "outer_gate": WORKLOADS["outer_gate"],
     "retnet_decay": WORKLOADS["retnet_decay"],
     "causal_elu1": WORKLOADS["causal_elu1"],
     "gla_gate_d64": WORKLOADS["gla_gate"].resized(name="gla_gate_d64", d_k=64, d_v=64, r=64, qk_scale=64 ** -0.5,

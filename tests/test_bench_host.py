@@ -40,6 +40,8 @@ def test_backward_bytes_per_token():
     gla64 = WORKLOADS["gla_gate"].resized(d_k=64, d_v=64, r=64)
     assert bench.backward_algorithmic_per_token(gla64)[0] == 1152
     assert bench.backward_algorithmic_per_token(WORKLOADS["ssm_scalar"])[0] == 900
+    # the outer-product gate: q, k, v, dO, dq, dk, dv, g, dg (d = 128) and gv, dgv (d_v = 128), bf16
+    assert bench.backward_algorithmic_per_token(WORKLOADS["outer_gate"])[0] == 2 * 128 * 11
     assert bench.backward_algorithmic_per_token(WORKLOADS["noncausal_elu1_f32"])[0] == 4 * (2 * 32 + 2 * 32) + 4 * (2 * 32 + 32)
 
 

@@ -21,7 +21,7 @@ import pytest
 import torch
 
 from oracle import la_backward as obwd
-from oracle.la_oracle import feature_map
+from oracle.la_oracle import causal_recurrent, feature_map
 from workloads import WORKLOADS, make_inputs, strong_gate_input, to_f64, incoming_gradient
 from _helpers import dev, gpu_gate
 
@@ -198,6 +198,42 @@ def test_backward_outer_at_the_domain_edge(side):
         inp["gv"] = strong_gate_input((2, 4, 700, 64), 71)
     got = run_backward_outer(inp, dO)
     check_heads(got, inp, dO, [(0, 0), (1, 3)], f"outer backward edge ({side})")
+
+
+def test_backward_outer_workload_full_size_tail():
+    """The outer-product gate's workload (B2 H16 n16384 d_k = d_v = 128: two
+    value-column halves, several segments) in one la_backward call. Every
+    gradient of a token depends only on that token, the later ones and the
+    forward state entering it, so on two sampled heads the last 320 tokens'
+    gradients are checked against the oracle run on those tokens from the
+    state the recurrent oracle carries into them; every entry is finite."""
+    wl = WORKLOADS["outer_gate"]
+    inp = make_inputs(wl, seed=0)
+    dO = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1)
+    print(f"  outer backward at B={wl.B} H={wl.H} n={wl.n} d_k={wl.d_k} d_v={wl.d_v}", flush=True)
+    got = run_backward_outer(inp, dO)
+    for x in got:
+        assert torch.isfinite(x).all()
+    m = 320
+    n0 = wl.n - m
+    for b, h in [(0, 0), (wl.B - 1, wl.H - 1)]:
+        sl = lambda x: to_f64(x[b:b + 1, h:h + 1])
+        Q, K, V, d, g, gv = (sl(inp["Q"]), sl(inp["K"]), sl(inp["V"]), sl(dO), sl(inp["g"]), sl(inp["gv"]))
+        pre = lambda x: x[:, :, :n0]
+        _, S0, z0 = causal_recurrent(pre(Q), pre(K), pre(V), "elu1", None, ("outer", pre(g), pre(gv), inp["tau"]),
+                                     inp["eps"])
+        tail = lambda x: x[:, :, n0:]
+        args = (tail(Q), tail(K), tail(V), tail(d), tail(g), tail(gv), inp["tau"])
+        ref = obwd.backward_outer(*args, "elu1", None, inp["eps"], S0, z0)
+        scales = outer_scales(*args, inp["eps"], S0, z0)
+        errs = []
+        for x, r, sc in zip(got, ref, scales):
+            xg = to_f64(x[b:b + 1, h:h + 1, n0:])
+            errs.append(float(np.max(np.abs(xg - r) / (sc + 1e-30))))
+        print(f"  full-size head ({b}, {h}), last {m} tokens: term-relative " +
+              " ".join(f"{nm} {e:.2e}" for nm, e in zip(NAMES, errs)), flush=True)
+        for nm, e in zip(NAMES, errs):
+            assert e < TOL_GRAD, ("full size", (b, h), nm, e)
 
 
 def test_backward_outer_deterministic():
