@@ -184,7 +184,12 @@ struct BwdALayout {
   static constexpr int ec_off = gam_off + R * 4;
   static constexpr int gamv_off = ec_off + (GATE == GT_OUTER ? kChunk * (E + 4) * 4 : 0);
   static constexpr int vl_off = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
-  static constexpr int bytes = vl_off + (GATE == GT_OUTER ? VTB : 0);
+  // the bf16 residuals of the key features (dq's product over keys) and of the
+  // scores (the numerator of o; then of dW for dq), which enter those products
+  // as hi + lo pairs
+  static constexpr int klo_off = vl_off + (GATE == GT_OUTER ? VTB : 0);
+  static constexpr int alo_off = klo_off + FTB;
+  static constexpr int bytes = alo_off + ATB;
 };
 
 // h_i = -g_i . o_i from the four waves' partial dot products (fixed order).
@@ -264,9 +269,9 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
     // ---- prelude: features, values, dO, and the bf16 image of S
-    chunk_prelude<R, E, R, FMAP, GATE, true, NW, true, kKeyGate<GATE> ? kPreQD : 0>(
+    chunk_prelude<R, E, R, FMAP, GATE, true, NW, true, (kKeyGate<GATE> ? kPreQD : 0) | kPreKLo>(
         raw, ca, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off, LY::v_off, LY::gam_off, 0, lane, w, LY::qd_off, 0, 0,
-        LY::ec_off, LY::gamv_off, 0, LY::vl_off);
+        LY::ec_off, LY::gamv_off, 0, LY::vl_off, LY::klo_off);
     rdo.store(sm, LY::g_off, L, lane, w);
     state_image<R, E>(S, sm, LY::sb_off, lane, w);
     raw.load(ca, tok0, t0 + kChunk, t_end, lane, w);
@@ -298,12 +303,21 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
           if constexpr (GATE == GT_DECAY) v[i] *= exp2f(float(max(q - key, 0)) * lg2gam);
           if (key > q) v[i] = 0.f;  // select after the factor (gamma^-15 overflows for a small gamma)
         }
+        // hi and lo bf16 parts; the row sum of exactly what the products read
         const unsigned p01 = pack2_bits(v[0], v[1]), p23 = pack2_bits(v[2], v[3]);
-        rs += (lo_bf16_f32(p01) + hi_bf16_f32(p01)) + (lo_bf16_f32(p23) + hi_bf16_f32(p23));
+        const float h0 = lo_bf16_f32(p01), h1 = hi_bf16_f32(p01), h2 = lo_bf16_f32(p23), h3 = hi_bf16_f32(p23);
+        const unsigned l01 = pack2_bits(v[0] - h0, v[1] - h1), l23 = pack2_bits(v[2] - h2, v[3] - h3);
+        rs += ((h0 + lo_bf16_f32(l01)) + (h1 + hi_bf16_f32(l01))) + ((h2 + lo_bf16_f32(l23)) + (h3 + hi_bf16_f32(l23)));
         typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        lds<u32x2>(sm, LY::a_off + AT::at(q, 2 * c + (g4 >> 1), 8 * (g4 & 1))) = u32x2{p01, p23};
+        const int ao = AT::at(q, 2 * c + (g4 >> 1), 8 * (g4 & 1));
+        lds<u32x2>(sm, LY::a_off + ao) = u32x2{p01, p23};
+        lds<u32x2>(sm, LY::alo_off + ao) = u32x2{l01, l23};
       }
-      if ((qw & 1) == 0) lds<bf16x4>(sm, LY::a_off + AT::at(q, 2 * (qw + 1) + (g4 >> 1), 8 * (g4 & 1))) = bf16x4{};
+      if ((qw & 1) == 0) {
+        const int ao = AT::at(q, 2 * (qw + 1) + (g4 >> 1), 8 * (g4 & 1));
+        lds<bf16x4>(sm, LY::a_off + ao) = bf16x4{};
+        lds<bf16x4>(sm, LY::alo_off + ao) = bf16x4{};
+      }
       rs = sum_over_groups(rs);
       float zd = 0.f;
 #pragma unroll
@@ -348,7 +362,10 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
 #pragma unroll
           for (int p2 = 0; p2 <= qt / 2; ++p2) {
             const bf16x8 ab = lds<bf16x8>(sm, LY::a_off + AT::at(q, 4 * p2 + g4));
-            acc = mfma16(tr_feat<E, true>(sm, LY::v_off, 32 * p2, e, lane), ab, acc);
+            const bf16x8 abl = lds<bf16x8>(sm, LY::alo_off + AT::at(q, 4 * p2 + g4));
+            const bf16x8 vt = tr_feat<E, true>(sm, LY::v_off, 32 * p2, e, lane);
+            acc = mfma16(vt, ab, acc);
+            acc = mfma16(vt, abl, acc);
             if constexpr (GATE == GT_OUTER) acc = mfma16(tr_feat<E, true>(sm, LY::vl_off, 32 * p2, e, lane), ab, acc);
           }
           // acc[i] = num[q][e + 4 g + i] (outer: times e^{-c})
@@ -388,9 +405,13 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
       for (int jt = 0; jt <= it; ++jt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KE; ++ks)
-          acc = mfma16(lds<bf16x8>(sm, LY::v_off + VT::at(16 * jt + c16, 4 * ks + g4)),
-                       lds<bf16x8>(sm, LY::g_off + VT::at(i, 4 * ks + g4)), acc);
+        for (int ks = 0; ks < KE; ++ks) {
+          const bf16x8 gb = lds<bf16x8>(sm, LY::g_off + VT::at(i, 4 * ks + g4));
+          acc = mfma16(lds<bf16x8>(sm, LY::v_off + VT::at(16 * jt + c16, 4 * ks + g4)), gb, acc);
+          // the outer-product gate: V~ as hi + lo (V~ = e^{-c} v is not exact in bf16)
+          if constexpr (GATE == GT_OUTER)
+            acc = mfma16(lds<bf16x8>(sm, LY::vl_off + VT::at(16 * jt + c16, 4 * ks + g4)), gb, acc);
+        }
         float v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -399,9 +420,17 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
           if constexpr (GATE == GT_DECAY) v[u] *= exp2f(float(max(i - j, 0)) * lg2gam);
           if (j > i) v[u] = 0.f;
         }
-        lds<bf16x4>(sm, LY::a_off + AT::at(i, 2 * jt + (g4 >> 1), 8 * (g4 & 1))) = pack4(v[0], v[1], v[2], v[3]);
+        const int ao = AT::at(i, 2 * jt + (g4 >> 1), 8 * (g4 & 1));
+        const bf16x4 dwh = pack4(v[0], v[1], v[2], v[3]);
+        lds<bf16x4>(sm, LY::a_off + ao) = dwh;
+        lds<bf16x4>(sm, LY::alo_off + ao) = pack4(v[0] - to_f32(dwh[0]), v[1] - to_f32(dwh[1]),
+                                                  v[2] - to_f32(dwh[2]), v[3] - to_f32(dwh[3]));
       }
-      if ((it & 1) == 0) lds<bf16x4>(sm, LY::a_off + AT::at(i, 2 * (it + 1) + (g4 >> 1), 8 * (g4 & 1))) = bf16x4{};
+      if ((it & 1) == 0) {
+        const int ao = AT::at(i, 2 * (it + 1) + (g4 >> 1), 8 * (g4 & 1));
+        lds<bf16x4>(sm, LY::a_off + ao) = bf16x4{};
+        lds<bf16x4>(sm, LY::alo_off + ao) = bf16x4{};
+      }
     }
     lds_barrier();
 
@@ -417,11 +446,19 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int i = 16 * it + c16;
-        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+        // a1: K^T dW^T on the bf16 parts, which pass B's dK~ . K~ mirrors (dg
+        // relies on the two cancelling pair by pair); a1c: the residual
+        // products (K_lo dW + K dW_lo) that dq adds
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a1c = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = 0; p <= it / 2; ++p)
-          a1 = mfma16(tr_feat<R, true>(sm, LY::k_off, 32 * p, 16 * ft, lane),
-                      lds<bf16x8>(sm, LY::a_off + AT::at(i, 4 * p + g4)), a1);
+        for (int p = 0; p <= it / 2; ++p) {
+          const bf16x8 dwb = lds<bf16x8>(sm, LY::a_off + AT::at(i, 4 * p + g4));
+          const bf16x8 dwl = lds<bf16x8>(sm, LY::alo_off + AT::at(i, 4 * p + g4));
+          const bf16x8 kt = tr_feat<R, true>(sm, LY::k_off, 32 * p, 16 * ft, lane);
+          a1 = mfma16(kt, dwb, a1);
+          a1c = mfma16(tr_feat<R, true>(sm, LY::klo_off, 32 * p, 16 * ft, lane), dwb, a1c);
+          a1c = mfma16(kt, dwl, a1c);
+        }
 #pragma unroll
         for (int ks = 0; ks < KE; ++ks)
           a2 = mfma16(lds<bf16x8>(sm, LY::sb_off + VT::at(16 * ft + c16, 4 * ks + g4)),
@@ -436,10 +473,11 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
         f32x4 db;
 #pragma unroll
         for (int u2 = 0; u2 < 4; ++u2) {
-          const float dphi = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::z_off + 4 * (f0 + u2)) * hi);
+          const float dphi_b = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::z_off + 4 * (f0 + u2)) * hi);
+          const float dphi = dphi_b + a1c[u2];
           if constexpr (kKeyGate<GATE>) {
             dq[u2] = dphi * to_f32(qd[u2]);
-            db[u2] = dphi * to_f32(ph[u2]);
+            db[u2] = dphi_b * to_f32(ph[u2]);
           } else {
             dq[u2] = dphi * phi_ew_deriv<FMAP>(to_f32(ph[u2]));
           }
@@ -581,7 +619,9 @@ struct BwdBLayout {
   // outer: e^{c} per token and value column (rows of E + 4), e^{c_end} per column
   static constexpr int ec_off = cpart_off + (kKeyGate<GATE> ? 4 * R * 4 : 0);
   static constexpr int gamv_off = ec_off + (GATE == GT_OUTER ? kChunk * (E + 4) * 4 : 0);
-  static constexpr int bytes = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
+  static constexpr int wlo_off = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);  // the bf16 residual of W^T (dv's product)
+  static constexpr int vl_off = wlo_off + ATB;  // outer: the lo half of V~
+  static constexpr int bytes = vl_off + (GATE == GT_OUTER ? VTB : 0);
 };
 
 // Inclusive prefix sum across each row of 16 lanes (lane c gets x_0 + ... + x_c
@@ -716,9 +756,9 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
     // ---- prelude
-    chunk_prelude<R, E, R, FMAP, PG, true, NW, true, kKeyGate<GATE> ? (kPreKD | (OUT ? kPreNoKH | kPreVHi : 0)) : 0>(
+    chunk_prelude<R, E, R, FMAP, PG, true, NW, true, kKeyGate<GATE> ? (kPreKD | (OUT ? kPreNoKH : 0)) : 0>(
         raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0, LY::v_off, LY::gam_off, 0, lane, w, 0, LY::kd_off, 0,
-        LY::ec_off, LY::gamv_off);
+        LY::ec_off, LY::gamv_off, 0, LY::vl_off);
     if constexpr (GATE == GT_DECAY) {
       // gamma^t phi(q) for the reverse-state update
       const int t = 16 * w + lane / 4;
@@ -758,9 +798,12 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           aw = mfma16(lds<bf16x8>(sm, LY::q_off + FT::at(16 * it + c16, 4 * ks + g4)),
                       lds<bf16x8>(sm, LY::k_off + FT::at(j, 4 * ks + g4)), aw);
 #pragma unroll
-        for (int ks = 0; ks < KE; ++ks)
-          ad = mfma16(lds<bf16x8>(sm, LY::g_off + VT::at(16 * it + c16, 4 * ks + g4)),
-                      lds<bf16x8>(sm, LY::v_off + VT::at(j, 4 * ks + g4)), ad);
+        for (int ks = 0; ks < KE; ++ks) {
+          const bf16x8 gb = lds<bf16x8>(sm, LY::g_off + VT::at(16 * it + c16, 4 * ks + g4));
+          ad = mfma16(gb, lds<bf16x8>(sm, LY::v_off + VT::at(j, 4 * ks + g4)), ad);
+          // the outer-product gate: V~ as hi + lo, as pass A forms dW
+          if constexpr (OUT) ad = mfma16(gb, lds<bf16x8>(sm, LY::vl_off + VT::at(j, 4 * ks + g4)), ad);
+        }
         // aw[u] = phi(q_i) . phi(k_j), ad[u] = g_i . v_j with i = 16 it + 4 g + u
         float vw[4], vd[4];
 #pragma unroll
@@ -773,7 +816,10 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           vd[u] = ok ? (ad[u] + lds<float>(sm, LY::hw_off + 4 * i)) * dec : 0.f;
         }
         const int o = AT::at(j, 2 * it + (g4 >> 1), 8 * (g4 & 1));
-        lds<bf16x4>(sm, LY::w_off + o) = pack4(vw[0], vw[1], vw[2], vw[3]);
+        const bf16x4 wh = pack4(vw[0], vw[1], vw[2], vw[3]);
+        lds<bf16x4>(sm, LY::w_off + o) = wh;
+        lds<bf16x4>(sm, LY::wlo_off + o) = pack4(vw[0] - to_f32(wh[0]), vw[1] - to_f32(wh[1]), vw[2] - to_f32(wh[2]),
+                                                 vw[3] - to_f32(wh[3]));
         lds<bf16x4>(sm, LY::dw_off + o) = pack4(vd[0], vd[1], vd[2], vd[3]);
       }
     }
@@ -781,6 +827,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     if (w >= 2) {
       const int o = AT::at(16 * (2 * w - 3) + c16, 2 * (2 * w - 4) + (g4 >> 1), 8 * (g4 & 1));
       lds<bf16x4>(sm, LY::w_off + o) = bf16x4{};
+      lds<bf16x4>(sm, LY::wlo_off + o) = bf16x4{};
       lds<bf16x4>(sm, LY::dw_off + o) = bf16x4{};
     }
     lds_barrier();
@@ -829,9 +876,11 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) acc[u] *= sc;
 #pragma unroll
-          for (int p = jt / 2; p < 2; ++p)
-            acc = mfma16(tr_feat<E, true>(sm, LY::g_off, 32 * p, e, lane),
-                         lds<bf16x8>(sm, LY::w_off + AT::at(j, 4 * p + g4)), acc);
+          for (int p = jt / 2; p < 2; ++p) {
+            const bf16x8 gt = tr_feat<E, true>(sm, LY::g_off, 32 * p, e, lane);
+            acc = mfma16(gt, lds<bf16x8>(sm, LY::w_off + AT::at(j, 4 * p + g4)), acc);
+            acc = mfma16(gt, lds<bf16x8>(sm, LY::wlo_off + AT::at(j, 4 * p + g4)), acc);
+          }
           if constexpr (OUT) {
             const f32x4 ec = lds<f32x4>(sm, LY::ec_off + 4 * (j * (E + 4) + e + 4 * g4));
 #pragma unroll

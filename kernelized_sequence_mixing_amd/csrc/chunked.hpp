@@ -379,14 +379,26 @@ struct RawChunk {
 // outer-product gate's backward: kPreVRaw stores the value slot as loaded
 // (the reverse state's G~ = e^{+c} g, already scaled) while still taking the
 // value-side totals; kPreNoKH skips the K^ tile and kPreVHi the lo half of V~
-// (the reverse pass needs neither).
-constexpr int kPreQD = 1, kPreKD = 2, kPreLogG = 4, kPreKPos = 8, kPreVRaw = 16, kPreNoKH = 32, kPreVHi = 64;
+// (the reverse pass needs neither). kPreKLo (WITH_Q) also writes the bf16
+// residual of the key slot (its fp32 value minus the stored bf16) at klo_off,
+// for products that take the keys as a hi + lo pair.
+constexpr int kPreQD = 1, kPreKD = 2, kPreLogG = 4, kPreKPos = 8, kPreVRaw = 16, kPreNoKH = 32, kPreVHi = 64,
+              kPreKLo = 128;
+
+// Eight floats as bf16 (hi) and their bf16 residuals x - hi (lo).
+__device__ __forceinline__ bf16x8 bf16_residual8(const float (&x)[8], const bf16x8& hi) {
+  float r[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) r[u] = x[u] - to_f32(hi[u]);
+  return cat8(pack4(r[0], r[1], r[2], r[3]), pack4(r[4], r[5], r[6], r[7]));
+}
 template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SWZ, int EXTRA = 0>
 __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>& raw,
                                               const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
                                               int k_off, int kh_off, int v_off, int gam_off, int logg_off,
                                               int lane, int w, int qd_off = 0, int kd_off = 0, int bs_off = 0,
-                                              int ec_off = 0, int gamv_off = 0, int loggv_off = 0, int vl_off = 0) {
+                                              int ec_off = 0, int gamv_off = 0, int loggv_off = 0, int vl_off = 0,
+                                              int klo_off = 0) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
   constexpr int LPT = Raw::LPT;
   using FT = FeatTile<R, SWZ>;
@@ -434,6 +446,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       } else {
         lds<bf16x8>(sm, k_off + fo) = khr;
       }
+      if constexpr (WITH_Q && (EXTRA & kPreKLo) != 0) lds<bf16x8>(sm, klo_off + fo) = keep_if(valid, bf16_residual8(vk, kr));
     }
 #pragma unroll
     for (int j = 0; j < E / (8 * LPT); ++j)
@@ -499,9 +512,12 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
             keep_if(valid, cat8(pack4(vkh[0], vkh[1], vkh[2], vkh[3]), pack4(vkh[4], vkh[5], vkh[6], vkh[7])));
         lds<bf16x8>(sm, (WITH_Q ? kh_off : k_off) + fo) = khr;
       }
-      if (!kh_tile || WITH_Q)
-        lds<bf16x8>(sm, k_off + fo) =
-            keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
+      if (!kh_tile || WITH_Q) {
+        const bf16x8 kr = cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7]));
+        lds<bf16x8>(sm, k_off + fo) = keep_if(valid, kr);
+        if constexpr (WITH_Q && (EXTRA & kPreKLo) != 0)
+          lds<bf16x8>(sm, klo_off + fo) = keep_if(valid, bf16_residual8(vk, kr));
+      }
       if constexpr (kKeyGate<GATE> && (EXTRA & kPreQD) != 0)
         lds<bf16x8>(sm, qd_off + fo) = cat8(pack4(dq[0], dq[1], dq[2], dq[3]), pack4(dq[4], dq[5], dq[6], dq[7]));
       if constexpr (kKeyGate<GATE> && (EXTRA & kPreKD) != 0)

@@ -128,9 +128,11 @@ def check_heads(got, inp, dO, heads, what, S0=None, z0=None, fmap="elu1"):
             rel = np.abs(xg - r) / (sc + 1e-30)
             errs.append(float(np.max(rel)))
         worst_u = int(np.unravel_index(np.argmax(rel), rel.shape)[2])
-        dgh = float(np.max(np.abs(to_f64(got[3][b:b + 1, h:h + 1]) - ref[3])) / (np.max(np.abs(ref[3])) + 1e-30))
+        hm = [float(np.max(np.abs(to_f64(x[b:b + 1, h:h + 1]) - r)) / (np.max(np.abs(r)) + 1e-30))
+              for x, r in zip(got, ref)]
         print(f"  {what} head {head}: term-relative dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e} "
-              f"dg {errs[3]:.2e} (at step {worst_u}); dg of the head max {dgh:.2e}", flush=True)
+              f"dg {errs[3]:.2e} (at step {worst_u}); of the head max dQ {hm[0]:.2e} dK {hm[1]:.2e} dV {hm[2]:.2e} "
+              f"dg {hm[3]:.2e}", flush=True)
         for nm, e in zip(("dQ", "dK", "dV", "dg"), errs):
             assert e < TOL_GRAD, (what, head, nm, e)
 
