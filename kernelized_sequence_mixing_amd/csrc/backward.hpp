@@ -619,9 +619,20 @@ struct BwdBLayout {
   // outer: e^{c} per token and value column (rows of E + 4), e^{c_end} per column
   static constexpr int ec_off = cpart_off + (kKeyGate<GATE> ? 4 * R * 4 : 0);
   static constexpr int gamv_off = ec_off + (GATE == GT_OUTER ? kChunk * (E + 4) * 4 : 0);
-  static constexpr int wlo_off = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);  // the bf16 residual of W^T (dv's product)
-  static constexpr int vl_off = wlo_off + ATB;  // outer: the lo half of V~
-  static constexpr int bytes = vl_off + (GATE == GT_OUTER ? VTB : 0);
+  // outer: the bf16 residual of W^T (dv's product, so that dO * o - dv * v
+  // cancels within a token's own pairs as pass A forms it)
+  static constexpr int wlo_off = gamv_off + (GATE == GT_OUTER ? E * 4 : 0);
+  static constexpr int vl_off = wlo_off + (GATE == GT_OUTER ? ATB : 0);  // outer: the lo half of V~
+  // the bf16 residuals of the query features and of dW^T, for dk's product over
+  // queries: not for the outer-product gate, whose tiles fill the LDS, nor where
+  // they would halve the workgroups a CU holds (two fit in 80 KB each)
+  static constexpr int base_end = vl_off + (GATE == GT_OUTER ? VTB : 0);
+  static constexpr int kTwoPerCu = 80 * 1024;
+  static constexpr bool DK_SPLIT =
+      GATE != GT_OUTER && (base_end + FTB + ATB <= kTwoPerCu || base_end > kTwoPerCu);
+  static constexpr int qlo_off = base_end;
+  static constexpr int dwlo_off = qlo_off + (DK_SPLIT ? FTB : 0);
+  static constexpr int bytes = dwlo_off + (DK_SPLIT ? ATB : 0);
 };
 
 // Inclusive prefix sum across each row of 16 lanes (lane c gets x_0 + ... + x_c
@@ -756,9 +767,10 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
     // ---- prelude
-    chunk_prelude<R, E, R, FMAP, PG, true, NW, true, kKeyGate<GATE> ? (kPreKD | (OUT ? kPreNoKH : 0)) : 0>(
+    chunk_prelude<R, E, R, FMAP, PG, true, NW, true,
+                  (kKeyGate<GATE> ? (kPreKD | (OUT ? kPreNoKH : 0)) : 0) | (LY::DK_SPLIT ? kPreQLo : 0)>(
         raw, ca, L, 0.f, sm, LY::q_off, LY::k_off, 0, LY::v_off, LY::gam_off, 0, lane, w, 0, LY::kd_off, 0,
-        LY::ec_off, LY::gamv_off, 0, LY::vl_off);
+        LY::ec_off, LY::gamv_off, 0, LY::vl_off, 0, LY::qlo_off);
     if constexpr (GATE == GT_DECAY) {
       // gamma^t phi(q) for the reverse-state update
       const int t = 16 * w + lane / 4;
@@ -818,17 +830,23 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
         const int o = AT::at(j, 2 * it + (g4 >> 1), 8 * (g4 & 1));
         const bf16x4 wh = pack4(vw[0], vw[1], vw[2], vw[3]);
         lds<bf16x4>(sm, LY::w_off + o) = wh;
-        lds<bf16x4>(sm, LY::wlo_off + o) = pack4(vw[0] - to_f32(wh[0]), vw[1] - to_f32(wh[1]), vw[2] - to_f32(wh[2]),
-                                                 vw[3] - to_f32(wh[3]));
-        lds<bf16x4>(sm, LY::dw_off + o) = pack4(vd[0], vd[1], vd[2], vd[3]);
+        if constexpr (OUT)
+          lds<bf16x4>(sm, LY::wlo_off + o) = pack4(vw[0] - to_f32(wh[0]), vw[1] - to_f32(wh[1]),
+                                                   vw[2] - to_f32(wh[2]), vw[3] - to_f32(wh[3]));
+        const bf16x4 dh = pack4(vd[0], vd[1], vd[2], vd[3]);
+        lds<bf16x4>(sm, LY::dw_off + o) = dh;
+        if constexpr (LY::DK_SPLIT)
+          lds<bf16x4>(sm, LY::dwlo_off + o) = pack4(vd[0] - to_f32(dh[0]), vd[1] - to_f32(dh[1]),
+                                                    vd[2] - to_f32(dh[2]), vd[3] - to_f32(dh[3]));
       }
     }
     // tiles below the diagonal read by the products over 32 queries: (key 1, query 0) and (3, 2)
     if (w >= 2) {
       const int o = AT::at(16 * (2 * w - 3) + c16, 2 * (2 * w - 4) + (g4 >> 1), 8 * (g4 & 1));
       lds<bf16x4>(sm, LY::w_off + o) = bf16x4{};
-      lds<bf16x4>(sm, LY::wlo_off + o) = bf16x4{};
+      if constexpr (OUT) lds<bf16x4>(sm, LY::wlo_off + o) = bf16x4{};
       lds<bf16x4>(sm, LY::dw_off + o) = bf16x4{};
+      if constexpr (LY::DK_SPLIT) lds<bf16x4>(sm, LY::dwlo_off + o) = bf16x4{};
     }
     lds_barrier();
 
@@ -879,7 +897,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
           for (int p = jt / 2; p < 2; ++p) {
             const bf16x8 gt = tr_feat<E, true>(sm, LY::g_off, 32 * p, e, lane);
             acc = mfma16(gt, lds<bf16x8>(sm, LY::w_off + AT::at(j, 4 * p + g4)), acc);
-            acc = mfma16(gt, lds<bf16x8>(sm, LY::wlo_off + AT::at(j, 4 * p + g4)), acc);
+            if constexpr (OUT) acc = mfma16(gt, lds<bf16x8>(sm, LY::wlo_off + AT::at(j, 4 * p + g4)), acc);
           }
           if constexpr (OUT) {
             const f32x4 ec = lds<f32x4>(sm, LY::ec_off + 4 * (j * (E + 4) + e + 4 * g4));
@@ -941,11 +959,19 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
       for (int jj = 0; jj < 4; ++jj) {
         const int jt = kKeyGate<GATE> ? 3 - jj : jj;
         const int j = 16 * jt + c16;
-        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+        // a1: Q^T dW on the bf16 parts, which pass A's dQ~ . Q~ mirrors (dg);
+        // a1c: the residual products (Q_lo dW + Q dW_lo) that dk adds
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a1c = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = jt / 2; p < 2; ++p)
-          a1 = mfma16(tr_feat<R, true>(sm, LY::q_off, 32 * p, 16 * ft, lane),
-                      lds<bf16x8>(sm, LY::dw_off + AT::at(j, 4 * p + g4)), a1);
+        for (int p = jt / 2; p < 2; ++p) {
+          const bf16x8 qt = tr_feat<R, true>(sm, LY::q_off, 32 * p, 16 * ft, lane);
+          const bf16x8 dwb = lds<bf16x8>(sm, LY::dw_off + AT::at(j, 4 * p + g4));
+          a1 = mfma16(qt, dwb, a1);
+          if constexpr (LY::DK_SPLIT) {
+            a1c = mfma16(tr_feat<R, true>(sm, LY::qlo_off, 32 * p, 16 * ft, lane), dwb, a1c);
+            a1c = mfma16(qt, lds<bf16x8>(sm, LY::dwlo_off + AT::at(j, 4 * p + g4)), a1c);
+          }
+        }
 #pragma unroll
         for (int ks = 0; ks < KE; ++ks)
           a2 = mfma16(lds<bf16x8>(sm, LY::rb_off + VT::at(16 * ft + c16, 4 * ks + g4)),
@@ -959,10 +985,11 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
 #pragma unroll
         for (int u2 = 0; u2 < 4; ++u2) {
           if constexpr (kKeyGate<GATE>) sc = lds<float>(sm, LY::gam_off + 4 * (f0 + u2));
-          const float dphi = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::rh_off + 4 * (f0 + u2)));
+          const float dphi_b = a1[u2] + sc * (a2[u2] + lds<float>(sm, LY::rh_off + 4 * (f0 + u2)));
+          const float dphi = dphi_b + a1c[u2];
           if constexpr (kKeyGate<GATE>) {
             dk[u2] = dphi * to_f32(kd[u2]);
-            bk[u2] = dphi * to_f32(ph[u2]);
+            bk[u2] = dphi_b * to_f32(ph[u2]);
           } else {
             dk[u2] = dphi * phi_ew_deriv<FMAP>(to_f32(ph[u2]));
           }

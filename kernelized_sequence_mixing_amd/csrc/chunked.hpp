@@ -381,9 +381,10 @@ struct RawChunk {
 // value-side totals; kPreNoKH skips the K^ tile and kPreVHi the lo half of V~
 // (the reverse pass needs neither). kPreKLo (WITH_Q) also writes the bf16
 // residual of the key slot (its fp32 value minus the stored bf16) at klo_off,
-// for products that take the keys as a hi + lo pair.
+// and kPreQLo that of the query slot at qlo_off, for products that take them
+// as hi + lo pairs.
 constexpr int kPreQD = 1, kPreKD = 2, kPreLogG = 4, kPreKPos = 8, kPreVRaw = 16, kPreNoKH = 32, kPreVHi = 64,
-              kPreKLo = 128;
+              kPreKLo = 128, kPreQLo = 256;
 
 // Eight floats as bf16 (hi) and their bf16 residuals x - hi (lo).
 __device__ __forceinline__ bf16x8 bf16_residual8(const float (&x)[8], const bf16x8& hi) {
@@ -398,7 +399,7 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
                                               int k_off, int kh_off, int v_off, int gam_off, int logg_off,
                                               int lane, int w, int qd_off = 0, int kd_off = 0, int bs_off = 0,
                                               int ec_off = 0, int gamv_off = 0, int loggv_off = 0, int vl_off = 0,
-                                              int klo_off = 0) {
+                                              int klo_off = 0, int qlo_off = 0) {
   using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
   constexpr int LPT = Raw::LPT;
   using FT = FeatTile<R, SWZ>;
@@ -432,8 +433,11 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         vkh[u] = vk[u] * decay_k;
       }
       const int fo = FT::at(t, f0 / 8);
-      if constexpr (WITH_Q)
-        lds<bf16x8>(sm, q_off + fo) = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
+      if constexpr (WITH_Q) {
+        const bf16x8 qr = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
+        lds<bf16x8>(sm, q_off + fo) = qr;
+        if constexpr ((EXTRA & kPreQLo) != 0) lds<bf16x8>(sm, qlo_off + fo) = bf16_residual8(vq, qr);
+      }
       // keys past the end are zeroed after packing (four masks per eight features)
       const bf16x8 kr = keep_if(valid, cat8(pack4(vk[0], vk[1], vk[2], vk[3]), pack4(vk[4], vk[5], vk[6], vk[7])));
       const bf16x8 khr =
@@ -501,8 +505,11 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
         vk[u] = pk;
       }
       const int fo = FT::at(t, f0 / 8);
-      if constexpr (WITH_Q)
-        lds<bf16x8>(sm, q_off + fo) = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
+      if constexpr (WITH_Q) {
+        const bf16x8 qr = cat8(pack4(vq[0], vq[1], vq[2], vq[3]), pack4(vq[4], vq[5], vq[6], vq[7]));
+        lds<bf16x8>(sm, q_off + fo) = qr;
+        if constexpr ((EXTRA & kPreQLo) != 0) lds<bf16x8>(sm, qlo_off + fo) = bf16_residual8(vq, qr);
+      }
       // the outer-product gate: pass 3 writes K~ for the scores and K^ for the
       // state, pass 1 K^ only; the backward's reverse state (kPreKPos) the key
       // slot alone
