@@ -78,13 +78,16 @@ def term_err(got, ref, scale):
     return float(np.max(np.abs(to_f64(got) - ref) / (scale + 1e-30)))
 
 
-def check_grads(got, ref, scales, what):
+def check_grads(got, ref, scales, what, tol_head=None):
     errs = [term_err(g, r, sc) for g, r, sc in zip(got, ref, scales)]
     heads = [head_err(g, r) for g, r in zip(got, ref)]
     print(f"  {what}: term-relative dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}; "
           f"of the head max dQ {heads[0]:.2e} dK {heads[1]:.2e} dV {heads[2]:.2e}", flush=True)
     for nm, e in zip(("dQ", "dK", "dV"), errs):
         assert e < TOL_GRAD, (what, nm, e)
+    if tol_head is not None:
+        for nm, e in zip(("dQ", "dK", "dV"), heads):
+            assert e < tol_head, (what, nm, "of the head max", e)
 
 
 def run_backward(inp, dO, S0=None, z0=None, fmap="elu1"):
@@ -144,7 +147,10 @@ def test_backward_with_carried_state(gate, d):
 
 
 def test_backward_headline_full_size():
-    """The benchmark's shape (B4 H16 n4096 d64, 8 segments), two sampled heads."""
+    """The benchmark's shape (B4 H16 n4096 d64, 8 segments), two sampled heads. Here
+    the errors are also bounded against each head's largest entry (1.5e-2: dq's
+    products take the keys, the scores and dW as hi + lo pairs; single bf16 operands
+    measured 2.8-3.1e-2)."""
     wl = WORKLOADS["causal_elu1"]
     inp = make_inputs(wl, seed=0)
     dO = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1)
@@ -154,7 +160,7 @@ def test_backward_headline_full_size():
     for head in [(0, 0), (wl.B - 1, wl.H - 1)]:
         b, h = head
         check_grads([g[b:b + 1, h:h + 1] for g in got], oracle_backward(inp, dO, head=head),
-                    term_scales(inp, dO, head=head), f"head {head}")
+                    term_scales(inp, dO, head=head), f"head {head}", tol_head=1.5e-2)
 
 
 def test_backward_deterministic():

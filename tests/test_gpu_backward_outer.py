@@ -168,13 +168,16 @@ def test_backward_outer_parity(d, dv, B, H, n):
     check_heads(got, inp, dO, [(0, 0), (B - 1, H - 1)], f"outer d{d} dv{dv} B{B} H{H} n{n}")
 
 
-def test_backward_outer_carried_state():
-    wl, inp, dO = _case(64, 64, 2, 4, 400, seed=5)
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_outer_carried_state(d):
+    """A carried-in state; at 128 x 128 each value-column half takes its own
+    columns of S0 (z0 is shared)."""
+    wl, inp, dO = _case(d, d, 2, 4, 400, seed=5)
     rng = np.random.default_rng(81)
-    S0 = torch.from_numpy((rng.standard_normal((2, 4, 64, 64)) * 2.0).astype(np.float32))
-    z0 = torch.from_numpy((20.0 + 2.0 * np.abs(rng.standard_normal((2, 4, 64)))).astype(np.float32))
+    S0 = torch.from_numpy((rng.standard_normal((2, 4, d, d)) * 2.0).astype(np.float32))
+    z0 = torch.from_numpy((20.0 + 2.0 * np.abs(rng.standard_normal((2, 4, d)))).astype(np.float32))
     got = run_backward_outer(inp, dO, S0, z0)
-    check_heads(got, inp, dO, [(0, 0), (1, 3)], "outer carried state", S0, z0)
+    check_heads(got, inp, dO, [(0, 0), (1, 3)], f"outer carried state d{d}", S0, z0)
 
 
 def test_backward_outer_state_space():
