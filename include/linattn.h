@@ -125,14 +125,14 @@ typedef struct la_gate {
   const void* g;      /* GLA, OUTER: device [B][H][n][r] in in_dtype (decode: [B][H][r]);
                          SEL: [B][H][n] (decode: [B][H]). Precondition of the chunked
                          causal kernels (la_forward, la_forward_batch with more than
-                         one token per sequence, la_backward) for GLA and OUTER, not
+                         16 tokens per sequence, la_backward) for GLA and OUTER, not
                          checked since g lives on the device: within every 64-token
                          chunk (tokens 64c .. 64c + 63 of each sequence) the summed
                          log alpha of each feature stays at or above -80. The
                          chunk's factors e^{+b}, e^{-b} are referenced to the chunk
                          start and stay finite in fp32 and bf16 there; below it the
-                         outputs may be Inf or NaN. la_decode_step, one-token batch
-                         steps and SEL have no such limit (SEL forms each factor
+                         outputs may be Inf or NaN. la_decode_step, batch steps of
+                         up to 16 tokens and SEL have no such limit (SEL forms each factor
                          as e^{b_i - b_j} <= 1). */
   const void* gv;     /* OUTER: device [B][H][n][d_v] in in_dtype (decode: [B][H][d_v]),
                          with the same precondition per value column (summed
@@ -256,14 +256,16 @@ la_status la_forward_batch_workspace_size(const la_problem* p, const la_batch* b
  * outputs for the shared tokens.
  * Slot ids must be distinct within a call when LA_SLOT_WRITE is set (two
  * sequences writing one slot race).
- * A batch of one token per sequence (no cu_seqlens, p->n == 1) runs the
- * recurrent step of la_decode_step (fp32 arithmetic, one read and one write of
- * each state) on the slots; longer steps and prefills run the chunked kernels.
+ * A step of up to 16 tokens per sequence (no cu_seqlens, p->n <= 16) runs the
+ * recurrent step of la_decode_step once per token, in order, on the slots (fp32
+ * arithmetic; each state is read and written once, held in registers across
+ * the tokens); longer steps and prefills run the chunked kernels.
  * A ragged batch is planned from p->n and max_seqlen (the lengths stay on the
  * device): segments sized for about one round of workgroups over all
  * sequences, as many as the longest sequence needs.
  * Supported: as la_forward with causal == 1, except d_v = 32 and FAVOR r = 32,
- * which only the one-token step takes (LA_ERR_UNSUPPORTED otherwise). Errors: LA_ERR_INVALID_ARG for a
+ * which only steps of up to 16 tokens take (LA_ERR_UNSUPPORTED otherwise).
+ * Errors: LA_ERR_INVALID_ARG for a
  * malformed batch (num_seqs, max_seqlen, flags, B != 1 with cu_seqlens, NULL
  * pool pointers with flags set); LA_ERR_ALIAS when out, the pool or the
  * workspace overlap an input or each other. The library allocates nothing.

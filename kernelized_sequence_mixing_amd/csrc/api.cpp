@@ -559,9 +559,10 @@ la_status check_batch(const la_problem* p, const la_batch* b, const la_feature_m
     return LA_ERR_INVALID_ARG;
   }
   if (b->flags != 0 && b->num_slots < 1) return LA_ERR_INVALID_ARG;
-  // d_v = 32 only on the one-token step (the recurrent kernel); the chunk
-  // kernels' padded copies are a la_forward workspace feature
-  if ((p->d_v == 32 || (f->kind == LA_FMAP_FAVOR && f->r == 32)) && !(b->cu_seqlens == nullptr && p->n == 1))
+  // d_v = 32 only on short steps (the recurrent kernel); the chunk kernels'
+  // padded copies are a la_forward workspace feature
+  if ((p->d_v == 32 || (f->kind == LA_FMAP_FAVOR && f->r == 32)) &&
+      !(b->cu_seqlens == nullptr && p->n <= kMaxStepTokens))
     return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
@@ -678,9 +679,11 @@ la_status la_forward_batch(const la_problem* p, const la_batch* batch, const voi
   plan.ws_logGv = (wl.bytes && gk == LA_GATE_OUTER) ? reinterpret_cast<float*>(ws + wl.logGv_off) : nullptr;
   plan.P = P;
   plan.seg_len = seg_len;
-  if (batch->cu_seqlens == nullptr && p->n == 1) {
-    // one token per sequence: the recurrent step kernel streams each state once
+  if (batch->cu_seqlens == nullptr && p->n <= kMaxStepTokens) {
+    // a few tokens per sequence: the recurrent step kernel streams each state
+    // once and takes the tokens in order with the state in registers
     DecodePlan dp{};
+    dp.m = p->n;
     dp.B = p->B;
     dp.H = p->H;
     dp.dk = p->d_k;

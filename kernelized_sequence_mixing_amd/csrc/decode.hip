@@ -12,9 +12,12 @@
 // (row group, column quad) owns float4 column quads of R/(256/(E/4)) rows, all
 // loads issued before the prologue so the whole state is in flight while the
 // features are computed; the read-out reduction over rows goes through LDS.
-// The states may live in a pool of slots (la_forward_batch with one token per
+// The states may live in a pool of slots (la_forward_batch with a few tokens per
 // sequence): then the head's state is slot[b] H + h, read and/or written as
 // the flags say, and a slot outside the pool means a zero state, not stored.
+// With m tokens per sequence the state stays in registers across the m steps,
+// taken in order (each read-out sees the state after its own token), and is
+// read and written once; the next token's small inputs load during a step.
 #include "vec_common.hpp"
 
 namespace la {
@@ -34,6 +37,7 @@ struct DecodeArgs {
   float eps, inv_tau;
   const int* slot;  // nullable: state index = b H + h
   int nslot, flags;  // flags: 1 read the state, 2 write it back
+  int m;             // tokens per sequence ([B][H][m][.] inputs and outputs), 1 .. kMaxStepTokens
 };
 
 template <int R, int E, int DK, int FMAP, typename InT>
@@ -54,18 +58,28 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const InT* k = static_cast<const InT*>(a.k);
   const InT* v = static_cast<const InT*>(a.v);
 
-  // Small per-head inputs first, then the state stream, all issued back to
-  // back from one basic block (clamped indices, no branches): the prologue
-  // below then waits only for the small loads while the whole state slice is
-  // in flight.
+  // Small per-head inputs of the first token, then the state stream, all
+  // issued back to back from one basic block (clamped indices, no branches):
+  // the prologue below then waits only for the small loads while the whole
+  // state slice is in flight.
   const bool gla = a.gate == LA_GATE_GLA || a.gate == LA_GATE_OUTER, sel = a.gate == LA_GATE_SEL;
   const bool outer = a.gate == LA_GATE_OUTER;
   const int iq = min(tid, DK - 1), iv = min(tid, E - 1), ir = min(tid, R - 1);
-  // GLA: one gate input per feature; selective: one per head
-  const InT* gp = gla ? static_cast<const InT*>(a.g) + bh * R + ir
-                      : (sel ? static_cast<const InT*>(a.g) + bh : q + bh * DK + iq);
-  const InT rq = q[bh * DK + iq], rk = k[bh * DK + iq], rv = v[bh * E + iv], rg = *gp;
-  const InT rgv = outer ? static_cast<const InT*>(a.gv)[bh * E + iv] : rv;
+  const int m = a.m;
+  // token t's small inputs: q, k, v, the gate input (GLA: one per feature;
+  // selective: one per head) and the outer-product gate's value side
+  InT rq, rk, rv, rg, rgv;
+  auto load_token = [&](int t) {
+    const long long tok = bh * m + t;
+    rq = q[tok * DK + iq];
+    rk = k[tok * DK + iq];
+    rv = v[tok * E + iv];
+    const InT* gp = gla ? static_cast<const InT*>(a.g) + tok * R + ir
+                        : (sel ? static_cast<const InT*>(a.g) + tok : q + tok * DK + iq);
+    rg = *gp;
+    rgv = outer ? static_cast<const InT*>(a.gv)[tok * E + iv] : rv;
+  };
+  load_token(0);
   long long si = bh;  // this head's state
   if (a.slot != nullptr) {
     const int sl = a.slot[bh / a.H];
@@ -83,98 +97,108 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) st[p] = float4{0.f, 0.f, 0.f, 0.f};
   }
-  const float xq = to_f32(rq), xk = to_f32(rk), xv = to_f32(rv), xg = (gla || sel) ? to_f32(rg) : 0.f, xz = rz;
 
-  // features and gate of this token
-  // unconditional (clamped) writes keep the loads above out of branches;
-  // threads past the end rewrite the last element with the same value
-  sxq[iq] = xq;
-  sxk[iq] = xk;
-  sv[iv] = xv;
-  sbeta[iv] = outer ? __expf(gla_log_alpha(to_f32(rgv), a.inv_tau)) : 1.f;
-  __syncthreads();
-  if constexpr (FMAP == 1) {
-    if (tid < 2) {
-      const float* x = tid == 0 ? sxq : sxk;
-      float s = 0.f;
-      for (int d = 0; d < DK; ++d) s += x[d] * x[d];
-      shalf[tid] = 0.5f * s;
+  for (int t = 0; t < m; ++t) {
+    const float xq = to_f32(rq), xk = to_f32(rk), xv = to_f32(rv), xg = (gla || sel) ? to_f32(rg) : 0.f;
+    const float xgv = to_f32(rgv);
+    if (t + 1 < m) load_token(t + 1);  // in flight during this step
+
+    // features and gate of this token
+    // unconditional (clamped) writes keep the loads above out of branches;
+    // threads past the end rewrite the last element with the same value
+    sxq[iq] = xq;
+    sxk[iq] = xk;
+    sv[iv] = xv;
+    sbeta[iv] = outer ? __expf(gla_log_alpha(xgv, a.inv_tau)) : 1.f;
+    __syncthreads();
+    if constexpr (FMAP == 1) {
+      if (tid < 2) {
+        const float* x = tid == 0 ? sxq : sxk;
+        float s = 0.f;
+        for (int d = 0; d < DK; ++d) s += x[d] * x[d];
+        shalf[tid] = 0.5f * s;
+      }
+      __syncthreads();
+    }
+    float zdot = 0.f;
+    if (tid < R) {
+      float pq, pk;
+      if constexpr (FMAP == 0) {
+        pq = elu1(xq);
+        pk = elu1(xk);
+      } else if constexpr (FMAP == 2) {  // the state-space form: C = q, B = k as they are
+        pq = xq;
+        pk = xk;
+      } else {
+        float aq = 0.f, ak = 0.f;
+        const InT* om = static_cast<const InT*>(a.omega) + (long long)tid * DK;
+        for (int d = 0; d < DK; ++d) {
+          const float w = to_f32(om[d]);
+          aq += w * sxq[d];
+          ak += w * sxk[d];
+        }
+        const float isr = rsqrtf(float(R));
+        pq = __expf(aq - shalf[0]) * isr;
+        pk = __expf(ak - shalf[1]) * isr;
+      }
+      float al = 1.f;
+      if (a.gate == LA_GATE_DECAY) al = a.gamma[bh % a.H];
+      if (gla || sel) al = __expf(gla_log_alpha(xg, a.inv_tau));
+      spq[tid] = pq;
+      spk[tid] = pk;
+      sal[tid] = al;
+      rz = al * rz + pk;
+      zdot = pq * rz;
+    }
+    // denominator: block reduction of phi(q) . z'
+    zdot += __shfl_xor(zdot, 1);
+    zdot += __shfl_xor(zdot, 2);
+    zdot += __shfl_xor(zdot, 4);
+    zdot += __shfl_xor(zdot, 8);
+    zdot += __shfl_xor(zdot, 16);
+    zdot += __shfl_xor(zdot, 32);
+    if ((tid & 63) == 0) sred[tid >> 6] = zdot;
+    __syncthreads();
+    if (tid == 0) {
+      float d = 0.f;
+      for (int w = 0; w < 4; ++w) d += sred[w];
+      sden = d + a.eps;
     }
     __syncthreads();
-  }
-  float zdot = 0.f;
-  if (tid < R) {
-    float pq, pk;
-    if constexpr (FMAP == 0) {
-      pq = elu1(xq);
-      pk = elu1(xk);
-    } else if constexpr (FMAP == 2) {  // the state-space form: C = q, B = k as they are
-      pq = xq;
-      pk = xk;
-    } else {
-      float aq = 0.f, ak = 0.f;
-      const InT* om = static_cast<const InT*>(a.omega) + (long long)tid * DK;
-      for (int d = 0; d < DK; ++d) {
-        const float w = to_f32(om[d]);
-        aq += w * sxq[d];
-        ak += w * sxk[d];
-      }
-      const float isr = rsqrtf(float(R));
-      pq = __expf(aq - shalf[0]) * isr;
-      pk = __expf(ak - shalf[1]) * isr;
-    }
-    float al = 1.f;
-    if (a.gate == LA_GATE_DECAY) al = a.gamma[bh % a.H];
-    if (gla || sel) al = __expf(gla_log_alpha(xg, a.inv_tau));
-    spq[tid] = pq;
-    spk[tid] = pk;
-    sal[tid] = al;
-    const float zn = al * xz + pk;
-    if (wr) a.z[si * R + tid] = zn;
-    zdot = pq * zn;
-  }
-  // denominator: block reduction of phi(q) . z'
-  zdot += __shfl_xor(zdot, 1);
-  zdot += __shfl_xor(zdot, 2);
-  zdot += __shfl_xor(zdot, 4);
-  zdot += __shfl_xor(zdot, 8);
-  zdot += __shfl_xor(zdot, 16);
-  zdot += __shfl_xor(zdot, 32);
-  if ((tid & 63) == 0) sred[tid >> 6] = zdot;
-  __syncthreads();
-  if (tid == 0) {
-    float d = 0.f;
-    for (int w = 0; w < 4; ++w) d += sred[w];
-    sden = d + a.eps;
-  }
-  __syncthreads();
 
-  // rank-1 update in place and partial read-out over this thread's rows
-  const float4 vv = reinterpret_cast<const float4*>(sv)[col4];
-  const float4 bt = reinterpret_cast<const float4*>(sbeta)[col4];
-  float4 o = {0.f, 0.f, 0.f, 0.f};
+    // rank-1 update (in registers) and partial read-out over this thread's rows
+    const float4 vv = reinterpret_cast<const float4*>(sv)[col4];
+    const float4 bt = reinterpret_cast<const float4*>(sbeta)[col4];
+    float4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int r = r0 + RPP * p;
-    const float al = sal[r], pk = spk[r], pq = spq[r];
-    float4 s = st[p];
-    s.x = al * bt.x * s.x + pk * vv.x;
-    s.y = al * bt.y * s.y + pk * vv.y;
-    s.z = al * bt.z * s.z + pk * vv.z;
-    s.w = al * bt.w * s.w + pk * vv.w;
-    if (wr) Sh[r * CG + col4] = s;
-    o.x += pq * s.x;
-    o.y += pq * s.y;
-    o.z += pq * s.z;
-    o.w += pq * s.w;
+    for (int p = 0; p < PASSES; ++p) {
+      const int r = r0 + RPP * p;
+      const float al = sal[r], pk = spk[r], pq = spq[r];
+      float4 s = st[p];
+      s.x = al * bt.x * s.x + pk * vv.x;
+      s.y = al * bt.y * s.y + pk * vv.y;
+      s.z = al * bt.z * s.z + pk * vv.z;
+      s.w = al * bt.w * s.w + pk * vv.w;
+      st[p] = s;
+      o.x += pq * s.x;
+      o.y += pq * s.y;
+      o.z += pq * s.z;
+      o.w += pq * s.w;
+    }
+    reinterpret_cast<float4*>(sred)[r0 * CG + col4] = o;
+    __syncthreads();
+    if (tid < E) {
+      float acc = 0.f;
+      for (int rg = 0; rg < RPP; ++rg) acc += sred[rg * E + tid];
+      // the state-space read-out y = C^T h is not normalised
+      st_elem(a.out, (bh * m + t) * E + tid, a.out_dt, FMAP == 2 ? acc : acc / sden);
+    }
+    if (t + 1 < m) __syncthreads();  // the next step rewrites the shared vectors and sred
   }
-  reinterpret_cast<float4*>(sred)[r0 * CG + col4] = o;
-  __syncthreads();
-  if (tid < E) {
-    float acc = 0.f;
-    for (int rg = 0; rg < RPP; ++rg) acc += sred[rg * E + tid];
-    // the state-space read-out y = C^T h is not normalised
-    st_elem(a.out, bh * E + tid, a.out_dt, FMAP == 2 ? acc : acc / sden);
+  if (wr) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) Sh[(r0 + RPP * p) * CG + col4] = st[p];
+    if (tid < R) a.z[si * R + tid] = rz;
   }
 }
 
@@ -183,7 +207,7 @@ static la_status run_decode(const DecodePlan& p) {
   const bool inp = p.gate == LA_GATE_GLA || p.gate == LA_GATE_SEL || p.gate == LA_GATE_OUTER;
   DecodeArgs a{p.S,     p.z,      p.q,        p.k,          p.v,    p.g,   p.gv,
                p.omega, p.gamma,  p.out,      p.H,          p.in_dtype,   p.out_dtype,
-               p.gate,  p.eps,    inp ? 1.f / p.tau : 0.f,  p.slot, p.nslot, p.flags};
+               p.gate,  p.eps,    inp ? 1.f / p.tau : 0.f,  p.slot, p.nslot, p.flags, p.m > 0 ? p.m : 1};
   if (p.in_dtype == LA_BF16)
     LA_LAUNCH((decode_step_kernel<R, E, DK, FMAP, bf16>), dim3(unsigned(p.B) * unsigned(p.H)), dim3(256), 0,
                        p.stream, a);

@@ -16,6 +16,9 @@ constexpr int kComputeUnits = 256;  // MI355X
 constexpr int kLdsPerCU = 160 * 1024;
 constexpr int kMaxGroupsPerCU = 2;  // measured: 2 beats 1 and 3 on the chunked passes (fewer segments, less state traffic)
 constexpr int kNonCausalGroups = 512;
+// la_forward_batch steps of at most this many tokens per sequence (no
+// cu_seqlens) run the recurrent step kernel, each state read and written once
+constexpr int kMaxStepTokens = 16;
 
 // LDS bytes of the causal output-pass workgroup for this shape (0 if not built);
 // pure host arithmetic over the kernels' own layout definitions.
@@ -98,11 +101,12 @@ struct DecodePlan {
   const void* omega;
   const float* gamma;
   void* out;
-  // state slots (la_forward_batch with one token per sequence): state index
+  // state slots (la_forward_batch with a few tokens per sequence): state index
   // slot[b] H + h; flags 1 read, 2 write (la_decode_step: no slots, both)
   const int* slot;
   int nslot, flags;
   hipStream_t stream;
+  int m;  // tokens per sequence (0 or 1: one step; at most kMaxStepTokens)
 };
 
 struct FmapPlan {

@@ -287,3 +287,100 @@ def test_serving_decode_bench_config_sampled(m):
                                         z0=sl(dec["z0"]))
         check_close(out[b:b + 1], o, TOL_BF16, f"serve decode m{m} seq {b}")
         assert np.max(np.abs(to_f64(Sc[b]) - Sr[0])) / np.max(np.abs(Sr)) < 1e-2
+
+
+# ------------------------------------------------ short steps on the recurrent step kernel
+
+def _step_wl(fmap, gate, d, dv, r=None):
+    if fmap == "favor":
+        return WORKLOADS["favor_causal"].resized(gate=gate, d_v=dv, r=r or 256)
+    if fmap == "identity":
+        return WORKLOADS["ssm_selective"].resized(gate=gate, d_k=d, d_v=dv, r=d)
+    base = WORKLOADS["outer_gate"] if gate == "outer" else WORKLOADS["gla_gate"]
+    return base.resized(gate=gate, d_k=d, d_v=dv, r=d, qk_scale=d ** -0.5, v_scale=dv ** -0.5)
+
+
+def _token_gate(inp, t, rows):
+    kind = inp["gate"]
+    if kind == "decay":
+        return ("decay", dev(inp["gamma"]))
+    if kind in ("gla", "sel"):
+        return (kind, dev(inp["g"])[rows, :, t].contiguous(), inp["tau"])
+    if kind == "outer":
+        return ("outer", dev(inp["g"])[rows, :, t].contiguous(), dev(inp["gv"])[rows, :, t].contiguous(), inp["tau"])
+    return None
+
+
+def _oracle_gate_row(inp, b):
+    kind = inp["gate"]
+    if kind == "decay":
+        return ("decay", to_f64(inp["gamma"]))
+    if kind in ("gla", "sel"):
+        return (kind, to_f64(inp["g"])[b:b + 1], inp["tau"])
+    if kind == "outer":
+        return ("outer", to_f64(inp["g"])[b:b + 1], to_f64(inp["gv"])[b:b + 1], inp["tau"])
+    return None
+
+
+STEP_CASES = [("elu1", "none", 64, 64, None, 2), ("elu1", "decay", 64, 64, None, 5),
+              ("elu1", "gla", 128, 128, None, 16), ("elu1", "sel", 64, 64, None, 7),
+              ("elu1", "outer", 64, 64, None, 4), ("favor", "none", 64, 64, None, 3),
+              ("favor", "decay", 64, 64, 32, 16), ("identity", "gla", 64, 64, None, 6),
+              ("elu1", "none", 64, 32, None, 4), ("elu1", "gla", 32, 64, None, 9)]
+
+
+@pytest.mark.parametrize("fmap,gate,d,dv,r,m", STEP_CASES)
+def test_short_steps_equal_successive_decode_steps(fmap, gate, d, dv, r, m):
+    """A batch step of m <= 16 tokens per sequence (no cu_seqlens) runs the
+    recurrent step kernel over its tokens with the state held in registers:
+    outputs and stored states equal m successive la_decode_step calls on the
+    gathered states bit for bit, a slot id outside the pool starts from zero
+    and stores nothing, other slots stay as they were, and the outputs follow
+    the oracle's recurrence. Includes d_v = 32 and FAVOR+ r = 32, which only
+    such steps take."""
+    import kernelized_sequence_mixing_amd as ksm
+    wl = _step_wl(fmap, gate, d, dv, r)
+    B, H, n_slots = 5, 3, 7
+    inp = make_inputs(wl, seed=60 + m, B=B, H=H, n=m)
+    rng = np.random.default_rng(61 + m)
+    S_init = rng.standard_normal((n_slots, H, wl.r, wl.d_v)).astype(np.float32)
+    z_init = (20.0 + rng.random((n_slots, H, wl.r))).astype(np.float32)
+    S, z = torch.from_numpy(S_init).to("cuda"), torch.from_numpy(z_init).to("cuda")
+    ids_np = np.array([3, 0, 6, 9, 1], dtype=np.int32)  # 9 is outside the pool
+    ids = torch.from_numpy(ids_np).to("cuda")
+    before_S, before_z = S.clone(), z.clone()
+    om = dev(inp.get("omega"))
+    out = ksm.forward_batch(dev(inp["Q"]), dev(inp["K"]), dev(inp["V"]), state=(S, z), slot_ids=ids, read=True,
+                            write=True, fmap=fmap, omega=om, gate=gpu_gate(inp), eps=inp["eps"])
+    # the same tokens as m successive decode steps on copies of the states (a zero state for slot 9)
+    rows = torch.arange(B, device="cuda")
+    S_ref = torch.stack([S_init_t if ok else torch.zeros_like(S_init_t) for S_init_t, ok in
+                         zip(before_S[torch.from_numpy(np.minimum(ids_np, n_slots - 1).astype(np.int64)).to("cuda")],
+                             ids_np < n_slots)]).contiguous()
+    z_ref = torch.stack([z_t if ok else torch.zeros_like(z_t) for z_t, ok in
+                         zip(before_z[torch.from_numpy(np.minimum(ids_np, n_slots - 1).astype(np.int64)).to("cuda")],
+                             ids_np < n_slots)]).contiguous()
+    refs = []
+    for t in range(m):
+        refs.append(ksm.decode_step(S_ref, z_ref, dev(inp["Q"])[:, :, t].contiguous(),
+                                    dev(inp["K"])[:, :, t].contiguous(), dev(inp["V"])[:, :, t].contiguous(),
+                                    fmap=fmap, omega=om, gate=_token_gate(inp, t, rows), eps=inp["eps"],
+                                    out_dtype=out.dtype))
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.stack(refs, dim=2)), f"{fmap} {gate} m{m}: outputs differ from the decode steps"
+    for b, sl in enumerate(ids_np):
+        if sl < n_slots:
+            assert torch.equal(S[sl], S_ref[b]) and torch.equal(z[sl], z_ref[b])
+    for sl in (2, 4, 5):
+        assert torch.equal(S[sl], before_S[sl]) and torch.equal(z[sl], before_z[sl])
+    oc = out.cpu()
+    for b in (0, 3):
+        sl = int(ids_np[b])
+        ok = sl < n_slots
+        o, _, _ = orc.causal_recurrent(to_f64(inp["Q"])[b:b + 1], to_f64(inp["K"])[b:b + 1],
+                                       to_f64(inp["V"])[b:b + 1], fmap,
+                                       to_f64(inp["omega"]) if fmap == "favor" else None, _oracle_gate_row(inp, b),
+                                       eps=inp["eps"], S0=S_init[sl:sl + 1] if ok else None,
+                                       z0=z_init[sl:sl + 1] if ok else None)
+        tol = TOL_BF16 if fmap != "identity" else 2e-2
+        check_close(oc[b:b + 1], o, tol, f"{fmap} {gate} d{d} dv{dv} m{m} seq {b} slot {sl}")
