@@ -298,7 +298,8 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  *   dg_u = (sum_{t>=u} dB_t) * sigmoid(-g_u) / tau.
  * The selective scalar gate is that gate with alpha_t = a_t on every feature,
  * so its dg_t is the sum over features of the per-feature dg_t (the library
- * runs the GLA passes on g repeated over features and sums their dg).
+ * runs the GLA passes with each token's one input used for every feature and
+ * sums their dg over features in a fixed order).
  * The outer-product gate G_t = alpha_t beta_t^T adds a value-side factor
  * beta_t = sigmoid(gv_t)^(1/tau) per column (z takes the key side only):
  * with C_t = sum_{u<=t} log beta_u, the pairs carry exp(C_i - C_j) per value
@@ -317,9 +318,8 @@ la_status la_backward_workspace_size(const la_problem* p, const la_feature_map* 
  *   workspace: device scratch of at least la_backward_workspace_size bytes,
  *   256-byte aligned (segment states of both directions, g and h per token;
  *   GLA, SEL and OUTER: also dQ~ . Q~ per token and feature and per-segment
- *   summed log-gates; SEL: also g repeated over features and its per-feature
- *   dg; OUTER: also dO * o per token and value column (fp32) and per-segment
- *   summed value-side log-gates).
+ *   summed log-gates; OUTER: also dO * o per token and value column (fp32)
+ *   and per-segment summed value-side log-gates).
  * causal == 0 (the non-causal form, "The linear attention trick", sadullah
  * page: dphi(q_i) = S g_i + z h_i, dphi(k_j) = G v_j + hq, dv_j = G^T phi(k_j)
  * with G = sum_i phi(q_i) g_i^T, hq = sum_i phi(q_i) h_i): ELU1, no gate, no

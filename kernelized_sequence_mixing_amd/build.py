@@ -27,7 +27,7 @@ LIB = os.path.join(PKG, "liblinattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "chunked_elu1.hip", "chunked_ssm.hip", "chunked_favor.hip", "scan.hip", "noncausal.hip", "decode.hip",
-           "featuremap.hip", "backward.hip", "gate_features.hip", "noncausal_bwd.hip", "noalloc.hip",
+           "featuremap.hip", "backward.hip", "noncausal_bwd.hip", "noalloc.hip",
            "softmax_attn.hip", "favor_backward.hip", "columns.hip"]
 
 HIPCC_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -293,15 +293,13 @@ la_status check_backward_shape(const la_problem* p, const la_feature_map* f, int
 bool backward_in_halves(const la_problem* p, int r) { return r == 128 && p->d_v == 128; }
 
 struct BwdWsLayout {
-  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, gx_off, dgx_off, Pw_off, logGv_off, s0h_off,
-      fv_off, bytes;
+  size_t S_off, z_off, R_off, rh_off, G_off, h_off, dB_off, logG_off, Pw_off, logGv_off, s0h_off, fv_off, bytes;
   int P, L;
 };
 
 // Forward segment states, reverse segment states, g (bf16) and h per token;
-// GLA adds dQ~ . Q~ per token and feature and the segments' summed log-gates;
-// the selective scalar gate runs the GLA passes and adds its input repeated
-// over features and the per-feature gradient of that (bf16 [B][H][n][r] each);
+// GLA adds dQ~ . Q~ per token and feature and the segments' summed log-gates
+// (the selective scalar gate runs the GLA passes on its one input per token);
 // the outer-product gate adds dO * o per token and value column (fp32) and
 // the segments' summed value-side log-gates.
 // The non-causal form: the splits' partial S, z (forward sums) and G, hq.
@@ -336,15 +334,11 @@ BwdWsLayout bwd_workspace_layout(const la_problem* p_in, const la_feature_map* f
   w.h_off = round_up(w.G_off + BH * n * dv * 2, kAlign);
   w.dB_off = round_up(w.h_off + BH * n * 4, kAlign);
   if (gate != LA_GATE_GLA && gate != LA_GATE_SEL && gate != LA_GATE_OUTER) {
-    w.logG_off = w.gx_off = w.dgx_off = w.Pw_off = w.logGv_off = w.bytes = w.dB_off;
+    w.logG_off = w.Pw_off = w.logGv_off = w.bytes = w.dB_off;
   } else {
     const size_t n64 = (n + 63) / 64 * 64;  // dQ~ . Q~ is stored by whole chunks
     w.logG_off = round_up(w.dB_off + BH * n64 * r * 4, kAlign);
-    w.gx_off = w.dgx_off = w.Pw_off = w.logGv_off = w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
-    if (gate == LA_GATE_SEL) {
-      w.dgx_off = round_up(w.gx_off + BH * n * r * 2, kAlign);
-      w.bytes = round_up(w.dgx_off + BH * n * r * 2, kAlign);
-    }
+    w.Pw_off = w.logGv_off = w.bytes = round_up(w.logG_off + BH * w.P * r * 4, kAlign);
     if (gate == LA_GATE_OUTER) {
       w.logGv_off = round_up(w.Pw_off + BH * n * dv * 4, kAlign);
       w.bytes = round_up(w.logGv_off + BH * w.P * dv * 4, kAlign);
@@ -830,7 +824,7 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   plan.out_dtype = p->out_dtype;
   plan.eps = p->eps;
   plan.fmap = fmap->kind;
-  plan.gate = sel ? LA_GATE_GLA : gk;  // the selective gate: the GLA passes on its repeated input
+  plan.gate = sel ? LA_GATE_GLA : gk;  // the selective gate: the GLA passes, its input broadcast over features
   plan.causal = 1;
   plan.Q = Q;
   plan.K = K;
@@ -855,7 +849,8 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
   if (gk == LA_GATE_GLA || sel || outer) {
     plan.ws_dB = reinterpret_cast<float*>(ws + wl.dB_off);
     plan.ws_logG = reinterpret_cast<float*>(ws + wl.logG_off);
-    plan.dg = sel ? static_cast<void*>(ws + wl.dgx_off) : dg;
+    plan.dg = dg;
+    plan.g_scalar = sel ? 1 : 0;  // the selective gate: one input per token, dg summed over features in pass B
   }
   if (outer) {
     plan.ws_P = reinterpret_cast<float*>(ws + wl.Pw_off);
@@ -871,11 +866,6 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
     plan.splits = wl.P;
     plan.split_len = wl.L;
     return launch_noncausal_backward(plan);
-  }
-  if (sel) {
-    plan.g = ws + wl.gx_off;
-    if ((st = launch_gate_repeat(gate->g, ws + wl.gx_off, (long long)(BH * n), fmap->r, plan.stream)) != LA_OK)
-      return st;
   }
   // FAVOR+: the kernels run on the materialised features phi(Q), phi(K) and
   // write d phi, which favor_vjp takes back through the map into dQ, dK
@@ -928,7 +918,7 @@ la_status la_backward(const la_problem* p, const void* Q, const void* K, const v
     return launch_favor_vjp(fv + 3 * fsz, fv + fsz, K, p->in_dtype, (long long)(BH * n), p->d_k, fmap->r, fmap->omega,
                             dK, p->out_dtype, plan.stream);
   }
-  return sel ? launch_gate_feature_sum(ws + wl.dgx_off, dg, (long long)(BH * n), fmap->r, plan.stream) : LA_OK;
+  return LA_OK;
 }
 
 la_status la_softmax_attention(const la_problem* p, const void* Q, const void* K, const void* V, int32_t causal,

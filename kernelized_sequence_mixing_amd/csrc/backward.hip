@@ -12,7 +12,8 @@ static la_status launch_with_lds(K kernel, dim3 grid, int lds, hipStream_t st, c
   return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
-template <int R, int E, int GATE, int FMAP>
+// SG: the GLA passes with one gate input per token (the selective gate).
+template <int R, int E, int GATE, int FMAP, bool SG = false>
 static la_status run_backward(const BwdPlan& p) {
   static_assert(Waves<R, E>::NW == 4, "the backward kernels use four-wave workgroups");
   const unsigned BH = unsigned(p.B) * unsigned(p.H);
@@ -71,7 +72,7 @@ static la_status run_backward(const BwdPlan& p) {
     a1.inv_tau = b.inv_tau;
     a1.logG_out = p.ws_logG;
     a1.logGv_out = p.ws_logGv;
-    if ((st = launch_segment_pass<R, E, R, FMAP, GATE>(a1, p.P, BH, p.stream)) != LA_OK) return st;
+    if ((st = launch_segment_pass<R, E, R, FMAP, GATE, SG>(a1, p.P, BH, p.stream)) != LA_OK) return st;
     if ((st = launch_segment_scan(p)) != LA_OK) return st;
     b.S_in = p.ws_S;
     b.z_in = p.ws_z;
@@ -83,12 +84,12 @@ static la_status run_backward(const BwdPlan& p) {
     b.in_head = (long long)R * E;
     b.in_seg = 0;
   }
-  if ((st = launch_with_lds(bwd_pass_a<R, E, GATE, FMAP>, dim3(p.P, BH), BwdALayout<R, E, GATE>::bytes, p.stream, b)) !=
-      LA_OK)
+  if ((st = launch_with_lds(bwd_pass_a<R, E, GATE, FMAP, SG>, dim3(p.P, BH), BwdALayout<R, E, GATE>::bytes, p.stream,
+                            b)) != LA_OK)
     return st;
   if (p.P > 1) {
     if constexpr (kKeyGate<GATE>)
-      st = launch_with_lds(bwd_rstate_gla<R, E, GATE, FMAP>, dim3(p.P - 1, BH), BwdRGLayout<R, E, GATE>::bytes,
+      st = launch_with_lds(bwd_rstate_gla<R, E, GATE, FMAP, SG>, dim3(p.P - 1, BH), BwdRGLayout<R, E, GATE>::bytes,
                            p.stream, b);
     else
       st = launch_with_lds(bwd_rstate<R, E, GATE, FMAP>, dim3(p.P - 1, BH), BwdRLayout<R, E, GATE>::bytes, p.stream,
@@ -98,7 +99,7 @@ static la_status run_backward(const BwdPlan& p) {
                                           GATE == GT_OUTER ? p.ws_logGv : nullptr)) != LA_OK)
       return st;
   }
-  return launch_with_lds(bwd_pass_b<R, E, GATE, FMAP>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b);
+  return launch_with_lds(bwd_pass_b<R, E, GATE, FMAP, SG>, dim3(p.P, BH), BwdBLayout<R, E, GATE>::bytes, p.stream, b);
 }
 
 template <int R, int E, int FMAP>
@@ -106,7 +107,8 @@ static la_status run_backward_gated(const BwdPlan& p) {
   switch (p.gate) {
     case LA_GATE_NONE: return run_backward<R, E, GT_NONE, FMAP>(p);
     case LA_GATE_DECAY: return run_backward<R, E, GT_DECAY, FMAP>(p);
-    case LA_GATE_GLA: return run_backward<R, E, GT_GLA, FMAP>(p);
+    case LA_GATE_GLA:
+      return p.g_scalar ? run_backward<R, E, GT_GLA, FMAP, true>(p) : run_backward<R, E, GT_GLA, FMAP, false>(p);
     case LA_GATE_OUTER: return run_backward<R, E, GT_OUTER, FMAP>(p);
     default: return LA_ERR_UNSUPPORTED;
   }

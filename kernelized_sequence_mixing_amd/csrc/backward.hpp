@@ -206,7 +206,8 @@ __device__ __forceinline__ float bwd_h(char* sm, int hp_off, int i) {
   return -s;
 }
 
-template <int R, int E, int GATE, int FMAP = FM_ELU1>
+// SG (GLA only): one gate input per token for every feature (the selective gate).
+template <int R, int E, int GATE, int FMAP = FM_ELU1, bool SG = false>
 __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = BwdALayout<R, E, GATE>;
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   ca.ldgv = b.ldv;
   ca.inv_tau = b.inv_tau;
 
-  using Raw = RawChunk<R, E, R, FMAP, GATE, true, NW>;
+  using Raw = RawChunk<R, E, R, FMAP, GATE, true, NW, SG>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
   RowsE<E> rdo;
@@ -616,8 +617,10 @@ struct BwdBLayout {
   static constexpr int gam_off = hw_off + kChunk * 4;  // GLA: e^{chunk's summed log-gate}
   // GLA, outer: [4][R] the waves' partial products of the states at the next segment's start
   static constexpr int cpart_off = gam_off + R * 4;
+  // GLA with one gate input per token: [4][64] the waves' sums of dg over their features
+  static constexpr int dgs_off = cpart_off + (kKeyGate<GATE> ? 4 * R * 4 : 0);
   // outer: e^{c} per token and value column (rows of E + 4), e^{c_end} per column
-  static constexpr int ec_off = cpart_off + (kKeyGate<GATE> ? 4 * R * 4 : 0);
+  static constexpr int ec_off = dgs_off + (GATE == GT_GLA ? 4 * kChunk * 4 : 0);
   static constexpr int gamv_off = ec_off + (GATE == GT_OUTER ? kChunk * (E + 4) * 4 : 0);
   // outer: the bf16 residual of W^T (dv's product, so that dO * o - dv * v
   // cancels within a token's own pairs as pass A forms it)
@@ -645,7 +648,9 @@ __device__ __forceinline__ float row_inclusive_scan(float x) {
   return x;
 }
 
-template <int R, int E, int GATE, int FMAP = FM_ELU1>
+// SG (GLA only): one gate input per token for every feature; dg [B H n] is its
+// gradient summed over features.
+template <int R, int E, int GATE, int FMAP = FM_ELU1, bool SG = false>
 __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = BwdBLayout<R, E, GATE>;
@@ -751,7 +756,7 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   score_tiles(w, sqi, skj);
   float carry[FPW][4];  // GLA: d log alpha at the end of the chunk, for this lane's features
 
-  using Raw = RawChunk<R, E, R, FMAP, PG, true, NW>;
+  using Raw = RawChunk<R, E, R, FMAP, PG, true, NW, SG>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
   RowsE<E> rg;
@@ -787,8 +792,16 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
     if constexpr (kKeyGate<GATE>) {
       // the raw gate of this lane's token and the wave's features, for dg
 #pragma unroll
-      for (int jg = 0; jg < R / 32; ++jg)
-        lds<bf16x8>(sm, LY::gr_off + FT::at(lane, (w * (R / 4) + 8 * jg) / 8)) = raw.g[jg];
+      for (int jg = 0; jg < R / 32; ++jg) {
+        bf16x8 gp;
+        if constexpr (SG) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) gp[u] = raw.gs;
+        } else {
+          gp = raw.g[jg];
+        }
+        lds<bf16x8>(sm, LY::gr_off + FT::at(lane, (w * (R / 4) + 8 * jg) / 8)) = gp;
+      }
     }
     rg.store(sm, LY::g_off, L, lane, w);
     if (w == 0) lds<float>(sm, LY::hw_off + 4 * lane) = lane < L ? hv : 0.f;
@@ -1010,7 +1023,19 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
             o[u2] = (carry[u][u2] + ((tot - pre) + x)) * b.inv_tau * __builtin_amdgcn_rcpf(1.f + __expf(to_f32(gv[u2])));
             carry[u][u2] += tot;
           }
-          if (j < L) store_grad4(b.dg + (tok0 + t0 + j) * R + f0, o, b.accum != 0);
+          if constexpr (SG) {
+            // the sum over this wave's features for token j: over the lane's
+            // four, its lane groups, then its feature tiles (kept in LDS by
+            // the lanes of group 0, in a fixed order)
+            float ts = (o[0] + o[1]) + (o[2] + o[3]);
+            ts += __shfl_xor(ts, 16);
+            ts += __shfl_xor(ts, 32);
+            if (g4 == 0) {
+              float& slot = lds<float>(sm, LY::dgs_off + 4 * (w * kChunk + j));
+              slot = u == 0 ? ts : slot + ts;
+            }
+          } else if (j < L)
+            store_grad4(b.dg + (tok0 + t0 + j) * R + f0, o, b.accum != 0);
         }
       }
     }
@@ -1026,6 +1051,18 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
                                                LY::gam_off, gsc, lane, w, LY::hw_off);
     }
     lds_barrier();
+    if constexpr (SG) {
+      // one gate input per token: its dg is the sum over all features (the four
+      // waves' partial sums, in a fixed order; the next chunk rewrites them only
+      // after its own barriers)
+      if (w == 0 && lane < L) {
+        const float sdg = (lds<float>(sm, LY::dgs_off + 4 * lane) + lds<float>(sm, LY::dgs_off + 4 * (kChunk + lane))) +
+                          (lds<float>(sm, LY::dgs_off + 4 * (2 * kChunk + lane)) +
+                           lds<float>(sm, LY::dgs_off + 4 * (3 * kChunk + lane)));
+        bf16* p = b.dg + tok0 + t0 + lane;
+        *p = (bf16)(b.accum != 0 ? sdg + to_f32(*p) : sdg);
+      }
+    }
   }
 }
 
@@ -1052,7 +1089,7 @@ struct BwdRGLayout {
   static constexpr int bytes = loggv_off + (GATE == GT_OUTER ? E * 4 : 0);
 };
 
-template <int R, int E, int GATE, int FMAP = FM_ELU1>
+template <int R, int E, int GATE, int FMAP = FM_ELU1, bool SG = false>
 __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = BwdRGLayout<R, E, GATE>;
@@ -1086,7 +1123,7 @@ __global__ __launch_bounds__(256) void bwd_rstate_gla(BwdArgs b) {
     if (lane < EV) lds<float>(sm, LY::loggv_off + 4 * (w * EV + lane)) = 0.f;
   }
 
-  using Raw = RawChunk<R, E, R, FMAP, GATE, false, NW>;
+  using Raw = RawChunk<R, E, R, FMAP, GATE, false, NW, SG>;
   const int nch = (t_end - t_begin + kChunk - 1) / kChunk;
   Raw raw;
   float hv = 0.f;

@@ -291,7 +291,9 @@ __device__ __forceinline__ bf16x8 tr_feat(char* sm, int tile_off, int k0, int co
 //    layout for FAVOR+ too.
 // FAVOR+ inputs X (projected inside the kernel): wave w holds tokens
 // [16w, 16w+16), lane l token 16 w + l % 16, columns 32 ks + 8 (l / 16) .. + 7.
-template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW = 4>
+// SG (the GLA passes serving the selective gate's backward): g holds one
+// input per token, used for every feature.
+template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW = 4, bool SG = false>
 struct RawChunk {
   static constexpr int FR = R / NW;      // features per wave (lane-per-token layout)
   static constexpr int EV = E / NW;      // value columns per wave
@@ -304,6 +306,7 @@ struct RawChunk {
   bf16x8 q[ELU && WITH_Q ? FR / 8 : 1];
   bf16x8 k[ELU ? FR / 8 : 1];
   bf16x8 g[kKeyGate<GATE> ? FR / 8 : 1];
+  bf16 gs;  // SG: the token's one gate input (used for every feature)
   bf16x8 gv[GATE == GT_OUTER ? EV / 8 : 1];  // outer-product gate: value-side inputs, as v
   bf16 sg;  // selective gate: the input of token t0 + lane (every wave loads all 64)
   bf16x8 xq[!ELU && WITH_Q ? KS : 1];   // FAVOR+: token 16 w + l % 16, columns 32 ks + 8 (l / 16)
@@ -343,7 +346,9 @@ struct RawChunk {
           k[j] = *reinterpret_cast<const bf16x8*>(a.K + row * R + w * FR + 8 * j);
         }
       }
-      if constexpr (kKeyGate<GATE>) {
+      if constexpr (kKeyGate<GATE> && SG) {
+        gs = a.g[row];
+      } else if constexpr (kKeyGate<GATE>) {
 #pragma unroll
         for (int j = 0; j < FR / 8; ++j) g[j] = *reinterpret_cast<const bf16x8*>(a.g + row * R + w * FR + 8 * j);
       }
@@ -393,14 +398,14 @@ __device__ __forceinline__ bf16x8 bf16_residual8(const float (&x)[8], const bf16
   for (int u = 0; u < 8; ++u) r[u] = x[u] - to_f32(hi[u]);
   return cat8(pack4(r[0], r[1], r[2], r[3]), pack4(r[4], r[5], r[6], r[7]));
 }
-template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SWZ, int EXTRA = 0>
-__device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>& raw,
+template <int R, int E, int DK, int FMAP, int GATE, bool WITH_Q, int NW, bool SWZ, int EXTRA = 0, bool SG = false>
+__device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW, SG>& raw,
                                               const CausalArgs& a, int L, float lg2gam, char* sm, int q_off,
                                               int k_off, int kh_off, int v_off, int gam_off, int logg_off,
                                               int lane, int w, int qd_off = 0, int kd_off = 0, int bs_off = 0,
                                               int ec_off = 0, int gamv_off = 0, int loggv_off = 0, int vl_off = 0,
                                               int klo_off = 0, int qlo_off = 0) {
-  using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW>;
+  using Raw = RawChunk<R, E, DK, FMAP, GATE, WITH_Q, NW, SG>;
   constexpr int LPT = Raw::LPT;
   using FT = FeatTile<R, SWZ>;
   using VT = FeatTile<E, SWZ>;
@@ -471,7 +476,14 @@ __device__ __forceinline__ void chunk_prelude(const RawChunk<R, E, DK, FMAP, GAT
       float bs[8];
       if constexpr (kKeyGate<GATE>) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) bs[u] = keep_if(valid, gla_log2_alpha(to_f32(raw.g[j][u]), a.inv_tau));
+        for (int u = 0; u < 8; ++u) {
+          float gin;
+          if constexpr (SG)
+            gin = to_f32(raw.gs);
+          else
+            gin = to_f32(raw.g[j][u]);
+          bs[u] = keep_if(valid, gla_log2_alpha(gin, a.inv_tau));
+        }
         wave_inclusive_scan_n(bs);
       }
 #pragma unroll
@@ -899,7 +911,7 @@ struct GlaSegLayout {
 template <int R, int GATE>
 constexpr bool kGlaFeatureMajorSeg = GATE == GT_GLA && R % kGlaSegFeatures == 0;
 
-template <int R, int E, int DK, int FMAP>
+template <int R, int E, int DK, int FMAP, bool SG = false>
 __global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = GlaSegLayout<E>;
@@ -940,14 +952,19 @@ __global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
   // raw rows of one chunk in registers: piece i of thread tid is piece
   // tid + 256 i of the block's tile in row-major order (rows clamped to the segment)
   bf16x8 rk[PK], rg[PK], rv[PV];
+  bf16 rgs[SG ? PK : 1];  // SG: the piece's token's one gate input
   auto load = [&](int ci) {
     const int t0 = t_begin + ci * kChunk;
 #pragma unroll
     for (int i = 0; i < PK; ++i) {
       const int pc = tid + 256 * i;
-      const long long at = (tok0 + min(t0 + pc / VR, t_end - 1)) * R + FB * fb + 8 * (pc % VR);
+      const long long rowi = tok0 + min(t0 + pc / VR, t_end - 1);
+      const long long at = rowi * R + FB * fb + 8 * (pc % VR);
       rk[i] = *reinterpret_cast<const bf16x8*>(a.K + at);
-      rg[i] = *reinterpret_cast<const bf16x8*>(a.g + at);
+      if constexpr (SG)
+        rgs[i] = a.g[rowi];
+      else
+        rg[i] = *reinterpret_cast<const bf16x8*>(a.g + at);
     }
 #pragma unroll
     for (int i = 0; i < PV; ++i) {
@@ -962,7 +979,14 @@ __global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
     for (int i = 0; i < PK; ++i) {
       const int pc = tid + 256 * i;
       lds<bf16x8>(base, LY::k_off + FTR::at(pc / VR, pc % VR)) = rk[i];
-      lds<bf16x8>(base, LY::g_off + FTR::at(pc / VR, pc % VR)) = rg[i];
+      bf16x8 gp;
+      if constexpr (SG) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) gp[u] = rgs[i];
+      } else {
+        gp = rg[i];
+      }
+      lds<bf16x8>(base, LY::g_off + FTR::at(pc / VR, pc % VR)) = gp;
     }
 #pragma unroll
     for (int i = 0; i < PV; ++i) {
@@ -1066,10 +1090,12 @@ __global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
 }
 
 // Pass 1 launch: the feature-major GLA pass where it is built, else causal_segment_state.
-template <int R, int E, int DK, int FMAP, int GATE>
+// SG: one gate input per token (the selective gate's backward on the GLA passes).
+template <int R, int E, int DK, int FMAP, int GATE, bool SG = false>
 la_status launch_segment_pass(const CausalArgs& a1, int P, unsigned BH, hipStream_t stream) {
+  static_assert(!SG || kGlaFeatureMajorSeg<R, GATE>, "one gate input per token: the GLA passes only");
   if constexpr (kGlaFeatureMajorSeg<R, GATE> && FMAP != FM_FAVOR) {
-    auto k1 = gla_segment_state<R, E, DK, FMAP>;
+    auto k1 = gla_segment_state<R, E, DK, FMAP, SG>;
     constexpr int lds1 = GlaSegLayout<E>::bytes;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
         hipSuccess)

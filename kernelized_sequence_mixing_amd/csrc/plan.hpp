@@ -30,6 +30,7 @@ struct FwdPlan {
   int in_dtype, out_dtype;
   float eps;
   int fmap, gate, causal;
+  int g_scalar;  // GLA passes with one gate input per token (the selective gate's backward)
   float tau;
   const void* Q;
   const void* K;
@@ -177,9 +178,5 @@ la_status launch_favor_vjp(const void* dphi, const void* phi, const void* X, int
                            const void* omega, void* dX, int out_dt, hipStream_t st);
 // BwdPlan::fmap value for features computed beforehand (not a public feature map).
 constexpr int kFmapPrecomputed = 3;
-// The selective scalar gate's backward: repeat g [rows] over r features, and
-// sum the per-feature gradient [rows][r] back to [rows].
-la_status launch_gate_repeat(const void* g, void* gx, long long rows, int r, hipStream_t stream);
-la_status launch_gate_feature_sum(const void* dgx, void* dg, long long rows, int r, hipStream_t stream);
 
 }  // namespace la

@@ -362,9 +362,8 @@ def test_backward_workspace_size():
     assert size(4, 16, n, 64, 64, N.LA_GATE_DECAY) == size(4, 16, n, 64, 64)
     # GLA adds dQ~ . Q~ per token and feature (fp32) and the segments' summed log-gates
     assert size(4, 16, n, 64, 64, N.LA_GATE_GLA) == size(4, 16, n, 64, 64) + BH * n * 64 * 4 + zs
-    # the selective gate runs the GLA passes on g repeated over features: that copy and its
-    # per-feature gradient (bf16 each) come on top
-    assert size(4, 16, n, 64, 64, N.LA_GATE_SEL) == size(4, 16, n, 64, 64, N.LA_GATE_GLA) + 2 * BH * n * 64 * 2
+    # the selective gate runs the GLA passes with its one input per token: the same regions
+    assert size(4, 16, n, 64, 64, N.LA_GATE_SEL) == size(4, 16, n, 64, 64, N.LA_GATE_GLA)
     # the outer-product gate: the GLA regions on its own segment plan, plus dO * o per token and value
     # column (fp32) and the segments' summed value-side log-gates
     p = N.LaProblem(4, 16, n, 64, 64, N.LA_BF16, N.LA_BF16, 1e-6)
