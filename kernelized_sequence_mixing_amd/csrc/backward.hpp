@@ -75,17 +75,28 @@ struct BwdArgs {
   float eps, inv_tau;
 };
 
-// Four gradient entries stored as bf16, or added to the stored ones (the
+// Four gradient entries stored as bf16, or added to the stored ones prev (the
 // gradients are sums over value columns; a wide V runs in column halves).
-__device__ __forceinline__ void store_grad4(bf16* p, const float (&x)[4], bool accum) {
+__device__ __forceinline__ void store_grad4(bf16* p, const float (&x)[4], bool accum, bf16x4 prev) {
   float y[4] = {x[0], x[1], x[2], x[3]};
   if (accum) {
-    const bf16x4 o = *reinterpret_cast<const bf16x4*>(p);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) y[u] += to_f32(o[u]);
+    for (int u = 0; u < 4; ++u) y[u] += to_f32(prev[u]);
   }
   *reinterpret_cast<bf16x4*>(p) = pack4(y[0], y[1], y[2], y[3]);
 }
+
+// The stored entries that the second value-column half adds to, loaded at the
+// start of a chunk so that their latency hides behind the chunk's work (a load
+// at the store would wait for every memory access in flight before it).
+__device__ __forceinline__ bf16x4 load_prev4(const bf16* p, bool accum, bool valid) {
+  return accum && valid ? *reinterpret_cast<const bf16x4*>(p) : bf16x4{};
+}
+
+// The (r, d_v) = (128, 64) kernels are the ones that run as the halves of a
+// 128 x 128 state; only they hold the prefetched entries in registers.
+template <int R, int E>
+constexpr bool kHalfCols = R == 128 && E == 64;
 
 // Index (floats) of the four features 16 ft + 4 g .. + 3 of token 16 it + c of
 // chunk ch (chunks counted from the head's first token) in the GLA workspace of
@@ -269,6 +280,16 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
   for (int ci = 0; ci < nch; ++ci) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
+    constexpr bool PF = kHalfCols<R, E>;
+    bf16x4 prevq[PF ? FPW : 1][4];
+    if constexpr (PF) {
+#pragma unroll
+      for (int u = 0; u < FPW; ++u)
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          prevq[u][it] = load_prev4(b.dQ + (tok0 + t0 + 16 * it + c16) * R + 16 * (w * FPW + u) + 4 * g4,
+                                    b.accum != 0, 16 * it + c16 < L);
+    }
     // ---- prelude: features, values, dO, and the bf16 image of S
     chunk_prelude<R, E, R, FMAP, GATE, true, NW, true, (kKeyGate<GATE> ? kPreQD : 0) | kPreKLo>(
         raw, ca, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off, LY::v_off, LY::gam_off, 0, lane, w, LY::qd_off, 0, 0,
@@ -483,7 +504,10 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
             dq[u2] = dphi * phi_ew_deriv<FMAP>(to_f32(ph[u2]));
           }
         }
-        if (i < L) store_grad4(b.dQ + (tok0 + t0 + i) * R + f0, dq, b.accum != 0);
+        if (i < L) {
+          bf16* at = b.dQ + (tok0 + t0 + i) * R + f0;
+          store_grad4(at, dq, b.accum != 0, PF ? prevq[PF ? u : 0][it] : load_prev4(at, b.accum != 0, true));
+        }
         if constexpr (kKeyGate<GATE>)
           *reinterpret_cast<f32x4*>(b.dB + dbq_at<R>(bh, b.n, t0 / kChunk, ft, it, lane)) = db;
       }
@@ -771,6 +795,23 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int t0 = t_begin + ci * kChunk;
     const int L = min(kChunk, b.n - t0);
+    constexpr bool PF = kHalfCols<R, E>;
+    constexpr bool DGF = kKeyGate<GATE> && !SG;  // dg per feature
+    bf16x4 prevk[PF ? FPW : 1][4], prevg[PF && DGF ? FPW : 1][4];
+    bf16 prevgs = bf16(0.f);
+    if constexpr (PF) {
+#pragma unroll
+      for (int u = 0; u < FPW; ++u)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const long long at = (tok0 + t0 + 16 * jt + c16) * R + 16 * (w * FPW + u) + 4 * g4;
+          prevk[u][jt] = load_prev4(b.dK + at, b.accum != 0, 16 * jt + c16 < L);
+          if constexpr (DGF) prevg[u][jt] = load_prev4(b.dg + at, b.accum != 0, 16 * jt + c16 < L);
+        }
+      if constexpr (SG) {
+        if (b.accum != 0 && w == 0 && lane < L) prevgs = b.dg[tok0 + t0 + lane];
+      }
+    }
     // ---- prelude
     chunk_prelude<R, E, R, FMAP, PG, true, NW, true,
                   (kKeyGate<GATE> ? (kPreKD | (OUT ? kPreNoKH : 0)) : 0) | (LY::DK_SPLIT ? kPreQLo : 0)>(
@@ -1007,7 +1048,10 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
             dk[u2] = dphi * phi_ew_deriv<FMAP>(to_f32(ph[u2]));
           }
         }
-        if (j < L) store_grad4(b.dK + (tok0 + t0 + j) * R + f0, dk, b.accum != 0);
+        if (j < L) {
+          bf16* at = b.dK + (tok0 + t0 + j) * R + f0;
+          store_grad4(at, dk, b.accum != 0, PF ? prevk[PF ? u : 0][jt] : load_prev4(at, b.accum != 0, true));
+        }
         if constexpr (kKeyGate<GATE>) {
           // ---- dg: d log alpha_t = (d log alpha after the tile) + sum of dB over
           // the tile's tokens t' >= t (the row of 16 lanes holds tokens 16 jt + c
@@ -1034,8 +1078,10 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
               float& slot = lds<float>(sm, LY::dgs_off + 4 * (w * kChunk + j));
               slot = u == 0 ? ts : slot + ts;
             }
-          } else if (j < L)
-            store_grad4(b.dg + (tok0 + t0 + j) * R + f0, o, b.accum != 0);
+          } else if (j < L) {
+            bf16* at = b.dg + (tok0 + t0 + j) * R + f0;
+            store_grad4(at, o, b.accum != 0, PF ? prevg[PF ? u : 0][jt] : load_prev4(at, b.accum != 0, true));
+          }
         }
       }
     }
@@ -1059,8 +1105,9 @@ __global__ __launch_bounds__(256) void bwd_pass_b(BwdArgs b) {
         const float sdg = (lds<float>(sm, LY::dgs_off + 4 * lane) + lds<float>(sm, LY::dgs_off + 4 * (kChunk + lane))) +
                           (lds<float>(sm, LY::dgs_off + 4 * (2 * kChunk + lane)) +
                            lds<float>(sm, LY::dgs_off + 4 * (3 * kChunk + lane)));
-        bf16* p = b.dg + tok0 + t0 + lane;
-        *p = (bf16)(b.accum != 0 ? sdg + to_f32(*p) : sdg);
+        bf16* at = b.dg + tok0 + t0 + lane;
+        if constexpr (!PF) prevgs = b.accum != 0 ? *at : bf16(0.f);
+        *at = (bf16)(b.accum != 0 ? sdg + to_f32(prevgs) : sdg);
       }
     }
   }
