@@ -1,7 +1,7 @@
 """Pins of the fp64 softmax-attention oracle (oracle/softmax.py) against a
 library routine and closed forms, so that a slip in it (a transposed operand,
 a missing temperature, a strict or missing mask, a softmax over the wrong
-axis) fails here before it could judge a kernel."""
+axis) fails here before a kernel is ever compared with it."""
 import numpy as np
 import pytest
 import torch
