@@ -134,7 +134,7 @@ struct RowsE {
 // with colscale_off >= 0 each column is first scaled by the fp32 factor there.
 template <int R, int E, class SArr>
 __device__ __forceinline__ void state_image(const SArr& S, char* sm, int off, int lane, int w,
-                                            int colscale_off = -1) {
+                                            int colscale_off = -1, int lo_off = -1) {
   constexpr int NEB = E / 64;
   const int g4 = lane >> 4, c16 = lane & 15, ebase = w * (E / 4);
 #pragma unroll
@@ -144,8 +144,14 @@ __device__ __forceinline__ void state_image(const SArr& S, char* sm, int off, in
       const int e = ebase + 16 * eb + c16;
       const float cs = colscale_off >= 0 ? lds<float>(sm, colscale_off + 4 * e) : 1.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        lds<bf16>(sm, off + FeatTile<E>::at(16 * rt + 4 * g4 + i, e / 8, 2 * (e % 8))) = (bf16)(S[rt][eb][i] * cs);
+      for (int i = 0; i < 4; ++i) {
+        const float x = S[rt][eb][i] * cs;
+        const bf16 hi = (bf16)x;
+        const int at = FeatTile<E>::at(16 * rt + 4 * g4 + i, e / 8, 2 * (e % 8));
+        lds<bf16>(sm, off + at) = hi;
+        // the residual x - hi as a second image (a hi + lo pair of the state)
+        if (lo_off >= 0) lds<bf16>(sm, lo_off + at) = (bf16)(x - to_f32(hi));
+      }
     }
 }
 
@@ -200,7 +206,16 @@ struct BwdALayout {
   // as hi + lo pairs
   static constexpr int klo_off = vl_off + (GATE == GT_OUTER ? VTB : 0);
   static constexpr int alo_off = klo_off + FTB;
-  static constexpr int bytes = alo_off + ATB;
+  // GLA: the bf16 residual of the state image, so that dq's state product takes
+  // S as a hi + lo pair (the largest of the remaining roundings in dq). With 64
+  // features it has the v tile's shape and takes its place once the state
+  // update has read v (SLO_V: the update moves ahead of dq), which keeps the
+  // 64 x 64 layout within the LDS of two workgroups per CU; otherwise it has a
+  // region of its own.
+  static constexpr bool SLO = GATE == GT_GLA;
+  static constexpr bool SLO_V = SLO && R == kChunk;
+  static constexpr int sblo_off = SLO_V ? v_off : alo_off + ATB;
+  static constexpr int bytes = alo_off + ATB + (SLO && !SLO_V ? R * 2 * E : 0);
 };
 
 // h_i = -g_i . o_i from the four waves' partial dot products (fixed order).
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
         raw, ca, L, lg2gam, sm, LY::q_off, LY::k_off, LY::kh_off, LY::v_off, LY::gam_off, 0, lane, w, LY::qd_off, 0, 0,
         LY::ec_off, LY::gamv_off, 0, LY::vl_off, LY::klo_off);
     rdo.store(sm, LY::g_off, L, lane, w);
-    state_image<R, E>(S, sm, LY::sb_off, lane, w);
+    state_image<R, E>(S, sm, LY::sb_off, lane, w, -1, LY::SLO && !LY::SLO_V ? LY::sblo_off : -1);
     raw.load(ca, tok0, t0 + kChunk, t_end, lane, w);
     rdo.load(b.dO, b.ldv, tok0, t0 + kChunk, t_end, lane, w);
     lds_barrier();
@@ -456,6 +471,31 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     }
     lds_barrier();
 
+    if constexpr (LY::SLO_V) {
+      // the state's residual image replaces v: the residual of S entering the
+      // chunk is kept in registers, the state moves past the chunk (its last
+      // read of v), and the residual is written over v once every wave is done
+      bf16 slo[R / 16][E / 64][4];
+#pragma unroll
+      for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+        for (int eb = 0; eb < E / 64; ++eb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) slo[rt][eb][i] = (bf16)(S[rt][eb][i] - to_f32((bf16)S[rt][eb][i]));
+      state_update<R, E, GATE, NW, true>(S, Z, sm, LY::k_off, LY::v_off, LY::gam_off, 1.f, lane, w);
+      lds_barrier();
+#pragma unroll
+      for (int rt = 0; rt < R / 16; ++rt)
+#pragma unroll
+        for (int eb = 0; eb < E / 64; ++eb) {
+          const int e = ebase + 16 * eb + c16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            lds<bf16>(sm, LY::sblo_off + FeatTile<E>::at(16 * rt + 4 * g4 + i, e / 8, 2 * (e % 8))) = slo[rt][eb][i];
+        }
+      lds_barrier();
+    }
+
     // ---- dphi(q)^T = Phi_k^T dW^T + gamma^(t+1) (S G^T + z h^T); dq = dphi(q) phi'(q).
     // GLA and the outer-product gate: the tiles hold Q~ = e^{b} phi(q) and
     // K~ = e^{-b} phi(k) (and G~ for the outer gate), so this is
@@ -482,9 +522,11 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
           a1c = mfma16(kt, dwl, a1c);
         }
 #pragma unroll
-        for (int ks = 0; ks < KE; ++ks)
-          a2 = mfma16(lds<bf16x8>(sm, LY::sb_off + VT::at(16 * ft + c16, 4 * ks + g4)),
-                      lds<bf16x8>(sm, LY::g_off + VT::at(i, 4 * ks + g4)), a2);
+        for (int ks = 0; ks < KE; ++ks) {
+          const bf16x8 gop = lds<bf16x8>(sm, LY::g_off + VT::at(i, 4 * ks + g4));
+          a2 = mfma16(lds<bf16x8>(sm, LY::sb_off + VT::at(16 * ft + c16, 4 * ks + g4)), gop, a2);
+          if constexpr (LY::SLO) a2 = mfma16(lds<bf16x8>(sm, LY::sblo_off + VT::at(16 * ft + c16, 4 * ks + g4)), gop, a2);
+        }
         const float hi = bwd_h(sm, LY::hp_off, i);
         float sc = 1.f;
         if constexpr (GATE == GT_DECAY) sc = exp2f(float(i + 1) * lg2gam);
@@ -526,10 +568,12 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     }
     lds_barrier();  // z, the S image and the tiles are read above; the update below rewrites z
 
-    // ---- carry the forward state past this chunk
-    const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-    state_update<R, E, GATE, NW, true>(S, Z, sm, GATE == GT_DECAY || GATE == GT_OUTER ? LY::kh_off : LY::k_off,
-                                       LY::v_off, LY::gam_off, gsc, lane, w, 0, LY::gamv_off, LY::vl_off);
+    // ---- carry the forward state past this chunk (SLO_V: done above)
+    if constexpr (!LY::SLO_V) {
+      const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
+      state_update<R, E, GATE, NW, true>(S, Z, sm, GATE == GT_DECAY || GATE == GT_OUTER ? LY::kh_off : LY::k_off,
+                                         LY::v_off, LY::gam_off, gsc, lane, w, 0, LY::gamv_off, LY::vl_off);
+    }
     z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
     lds_barrier();
   }

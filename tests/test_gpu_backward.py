@@ -148,9 +148,9 @@ def test_backward_with_carried_state(gate, d):
 
 def test_backward_headline_full_size():
     """The benchmark's shape (B4 H16 n4096 d64, 8 segments), two sampled heads. Here
-    the errors are also bounded against each head's largest entry (1.5e-2: dq's
+    the errors are also bounded against each head's largest entry (1e-2: dq's
     products take the keys, the scores and dW as hi + lo pairs; single bf16 operands
-    measured 2.8-3.1e-2)."""
+    measured 2.8-3.1e-2, the split ones 4.9e-3 and 6.3e-3)."""
     wl = WORKLOADS["causal_elu1"]
     inp = make_inputs(wl, seed=0)
     dO = incoming_gradient((wl.B, wl.H, wl.n, wl.d_v), 1)
@@ -160,7 +160,7 @@ def test_backward_headline_full_size():
     for head in [(0, 0), (wl.B - 1, wl.H - 1)]:
         b, h = head
         check_grads([g[b:b + 1, h:h + 1] for g in got], oracle_backward(inp, dO, head=head),
-                    term_scales(inp, dO, head=head), f"head {head}", tol_head=1.5e-2)
+                    term_scales(inp, dO, head=head), f"head {head}", tol_head=1e-2)
 
 
 def test_backward_deterministic():

@@ -114,7 +114,10 @@ def run_backward_gla(inp, dO, S0=None, z0=None, fmap="elu1"):
     return tuple(x.cpu() for x in res)
 
 
-def check_heads(got, inp, dO, heads, what, S0=None, z0=None, fmap="elu1"):
+def check_heads(got, inp, dO, heads, what, S0=None, z0=None, fmap="elu1", tol_head_dq=None):
+    """Term-relative bounds on every gradient; with tol_head_dq also dq's error over
+    the head's largest dq entry (dq's state product takes the state as a hi + lo
+    pair, as its key and dW products do)."""
     for head in heads:
         b, h = head
         Q, K, V, d, g, s0, z = _head(inp, dO, head, S0, z0)
@@ -135,6 +138,8 @@ def check_heads(got, inp, dO, heads, what, S0=None, z0=None, fmap="elu1"):
               f"dg {hm[3]:.2e}", flush=True)
         for nm, e in zip(("dQ", "dK", "dV", "dg"), errs):
             assert e < TOL_GRAD, (what, head, nm, e)
+        if tol_head_dq is not None:
+            assert hm[0] < tol_head_dq, (what, head, "dQ of the head max", hm[0])
 
 
 def _case(d, dv, B, H, n, seed=3):
@@ -155,7 +160,9 @@ def test_backward_gla_parity(d, dv, B, H, n):
     wl, inp, dO = _case(d, dv, B, H, n)
     got = run_backward_gla(inp, dO)
     heads = sorted({(0, 0), (B - 1, H - 1)} | ({(B // 2, H // 2)} if n < 1000 else set()))
-    check_heads(got, inp, dO, heads, f"gla d{d}x{dv} B{B} H{H} n{n}")
+    # dq over the head's largest entry too (measured 4.0e-3 to 9.0e-3), except at n = 1,
+    # where the true dq nearly vanishes and the ratio says nothing
+    check_heads(got, inp, dO, heads, f"gla d{d}x{dv} B{B} H{H} n{n}", tol_head_dq=1e-2 if n > 1 else None)
 
 
 def test_backward_gla_with_carried_state():
