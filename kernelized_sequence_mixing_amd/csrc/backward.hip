@@ -72,7 +72,7 @@ static la_status run_backward(const BwdPlan& p) {
     a1.inv_tau = b.inv_tau;
     a1.logG_out = p.ws_logG;
     a1.logGv_out = p.ws_logGv;
-    if ((st = launch_segment_pass<R, E, R, FMAP, GATE, SG>(a1, p.P, BH, p.stream)) != LA_OK) return st;
+    if ((st = launch_segment_pass<R, E, R, FMAP, GATE, SG, GATE == GT_GLA>(a1, p.P, BH, p.stream)) != LA_OK) return st;
     if ((st = launch_segment_scan(p)) != LA_OK) return st;
     b.S_in = p.ws_S;
     b.z_in = p.ws_z;

@@ -482,7 +482,8 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
         for (int eb = 0; eb < E / 64; ++eb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) slo[rt][eb][i] = (bf16)(S[rt][eb][i] - to_f32((bf16)S[rt][eb][i]));
-      state_update<R, E, GATE, NW, true>(S, Z, sm, LY::k_off, LY::v_off, LY::gam_off, 1.f, lane, w);
+      state_update<R, E, GATE, NW, true, false, false, true>(S, Z, sm, LY::k_off, LY::v_off, LY::gam_off, 1.f, lane,
+                                                             w, 0, 0, 0, LY::klo_off);
       lds_barrier();
 #pragma unroll
       for (int rt = 0; rt < R / 16; ++rt)
@@ -571,8 +572,11 @@ __global__ __launch_bounds__(256) void bwd_pass_a(BwdArgs b) {
     // ---- carry the forward state past this chunk (SLO_V: done above)
     if constexpr (!LY::SLO_V) {
       const float gsc = GATE == GT_DECAY ? exp2f(float(L) * lg2gam) : 1.f;
-      state_update<R, E, GATE, NW, true>(S, Z, sm, GATE == GT_DECAY || GATE == GT_OUTER ? LY::kh_off : LY::k_off,
-                                         LY::v_off, LY::gam_off, gsc, lane, w, 0, LY::gamv_off, LY::vl_off);
+      // GLA: the gated keys K~ as a hi + lo pair (their bf16 rounding in the state
+      // is the largest remaining term in dq)
+      state_update<R, E, GATE, NW, true, false, false, GATE == GT_GLA>(
+          S, Z, sm, GATE == GT_DECAY || GATE == GT_OUTER ? LY::kh_off : LY::k_off, LY::v_off, LY::gam_off, gsc, lane,
+          w, 0, LY::gamv_off, LY::vl_off, LY::klo_off);
     }
     z_store<R, NW>(Z, reinterpret_cast<float*>(sm + LY::z_off), lane, w);
     lds_barrier();

@@ -644,10 +644,13 @@ struct ZTiles {
 // the old state only (S <- Gamma S + K~^T V), as the backward pass's reverse
 // state needs; the outer-product gate with PRE likewise scales the old state
 // by both sides and adds one bf16 value tile: S <- (Gamma 1^T) * S * (1 Gamma_v^T) + K~^T V.
-template <int R, int E, int GATE, int NW, bool SWZ, bool ZW = false, bool PRE = false, class SArr, class ZArr>
+// With KLO the key rows also have a bf16 residual tile at klo_off, added as a
+// second product (the keys as a hi + lo pair).
+template <int R, int E, int GATE, int NW, bool SWZ, bool ZW = false, bool PRE = false, bool KLO = false, class SArr,
+          class ZArr>
 __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_off, int v_off, int gam_off,
                                              float gscale, int lane, int w, int zw_off = 0, int gamv_off = 0,
-                                             int vl_off = 0) {
+                                             int vl_off = 0, int klo_off = 0) {
   constexpr int ZT = ZTiles<R, NW>::ZT, NEB = E / (16 * NW);
   const int g4 = lane >> 4;
   const int ebase = w * (E / NW);
@@ -669,9 +672,13 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
   }
 #pragma unroll
   for (int rt = 0; rt < R / 16; ++rt) {
-    bf16x8 ka[2];
+    bf16x8 ka[2], kal[KLO ? 2 : 1];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) ka[ks] = tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane);
+    if constexpr (KLO) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) kal[ks] = tr_feat<R, SWZ>(sm, klo_off, 32 * ks, 16 * rt, lane);
+    }
     float gr[4] = {gscale, gscale, gscale, gscale};
     if constexpr (kKeyGate<GATE>) {
 #pragma unroll
@@ -690,6 +697,10 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vb[eb][ks], st);
+      if constexpr (KLO) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) st = mfma16(kal[ks], vb[eb][ks], st);
+      }
       if constexpr (VLO) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) st = mfma16(ka[ks], vbl[eb][ks], st);
@@ -728,6 +739,7 @@ __device__ __forceinline__ void state_update(SArr& S, ZArr& Z, char* sm, int kh_
           for (int jj = 0; jj < 8; ++jj) zb[jj] = (bf16)lds<float>(sm, zw_off + 4 * (32 * ks + 8 * g4 + jj));
         }
         zt = mfma16(tr_feat<R, SWZ>(sm, kh_off, 32 * ks, 16 * rt, lane), zb, zt);
+        if constexpr (KLO) zt = mfma16(tr_feat<R, SWZ>(sm, klo_off, 32 * ks, 16 * rt, lane), zb, zt);
       }
       if constexpr (GATE == GT_GLA && !PRE) {  // z takes the key side only
 #pragma unroll
@@ -911,7 +923,8 @@ struct GlaSegLayout {
 template <int R, int GATE>
 constexpr bool kGlaFeatureMajorSeg = GATE == GT_GLA && R % kGlaSegFeatures == 0;
 
-template <int R, int E, int DK, int FMAP, bool SG = false>
+// KLO (the backward's state recompute): K^ enters the state as a hi + lo pair.
+template <int R, int E, int DK, int FMAP, bool SG = false, bool KLO = false>
 __global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   using LY = GlaSegLayout<E>;
@@ -1038,7 +1051,7 @@ __global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
       const float bend = tot0 + tot1;
       // exponent of K^ for token (ks, j): bend - (b[ks][j] + offset of the lane's run)
       const float r0 = bend - (inc0 - b[0][7]), r1 = bend - (tot0 + inc1 - b[1][7]);
-      bf16x8 kh[2];
+      bf16x8 kh[2], kl[KLO ? 2 : 1];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         float e[8];
@@ -1049,6 +1062,7 @@ __global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
           if constexpr (MASKED) e[j] = keep_if(32 * ks + 8 * g4 + j < L, e[j]);
         }
         kh[ks] = cat8(pack4(e[0], e[1], e[2], e[3]), pack4(e[4], e[5], e[6], e[7]));
+        if constexpr (KLO) kl[ks] = bf16_residual8(e, kh[ks]);
       }
       const float gam = __builtin_amdgcn_exp2f(bend);
       lg += bend;
@@ -1061,13 +1075,20 @@ __global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[i] *= gr[i];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) st = mfma16(kh[ks], tr_feat<E, false>(base, LY::v_off, 32 * ks, 16 * eb, lane), st);
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 vt = tr_feat<E, false>(base, LY::v_off, 32 * ks, 16 * eb, lane);
+          st = mfma16(kh[ks], vt, st);
+          if constexpr (KLO) st = mfma16(kl[ks], vt, st);
+        }
         S[eb] = st;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) Z[i] *= gr[i];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) Z = mfma16(kh[ks], ones, Z);
+      for (int ks = 0; ks < 2; ++ks) {
+        Z = mfma16(kh[ks], ones, Z);
+        if constexpr (KLO) Z = mfma16(kl[ks], ones, Z);
+      }
     };
     if (L == kChunk)
       chunk(std::false_type{});
@@ -1091,11 +1112,11 @@ __global__ __launch_bounds__(256) void gla_segment_state(CausalArgs a) {
 
 // Pass 1 launch: the feature-major GLA pass where it is built, else causal_segment_state.
 // SG: one gate input per token (the selective gate's backward on the GLA passes).
-template <int R, int E, int DK, int FMAP, int GATE, bool SG = false>
+template <int R, int E, int DK, int FMAP, int GATE, bool SG = false, bool KLO = false>
 la_status launch_segment_pass(const CausalArgs& a1, int P, unsigned BH, hipStream_t stream) {
   static_assert(!SG || kGlaFeatureMajorSeg<R, GATE>, "one gate input per token: the GLA passes only");
   if constexpr (kGlaFeatureMajorSeg<R, GATE> && FMAP != FM_FAVOR) {
-    auto k1 = gla_segment_state<R, E, DK, FMAP, SG>;
+    auto k1 = gla_segment_state<R, E, DK, FMAP, SG, KLO>;
     constexpr int lds1 = GlaSegLayout<E>::bytes;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, lds1) !=
         hipSuccess)
